@@ -1,0 +1,150 @@
+"""Seeded synthetic inputs for the Erase-then-Delta Attention (EDA) forward.
+
+This module is shared by the HIP path's tests/bench and by the CPU oracle's
+tests.  It draws random tensors only: it contains none of the recurrence's
+arithmetic (no decay, erase or write step), so neither side can inherit a
+mistake in the method from it.
+
+Distributions follow the inputs the EDA paper's layer hands to its recurrence
+(paper Sec. 3.3 and the reading slides' frame "EDA preserves the delta write
+after cleanup"): q, k, e are L2-normalised directions, v is an unconstrained
+value, alpha is a per-key-channel retention in (0, 1], beta and gamma are
+scalar gates in (0, 1).  "N(mu, s)" below means mean mu and standard
+deviation s.
+
+Layouts (all contiguous, row-major):
+  q, k, e : [B, T, H, d_k]      v : [B, T, H, d_v]
+  alpha   : [B, T, H, d_k] fp32 beta, gamma : [B, T, H] fp32
+  S0      : [B, H, d_k, d_v] fp32 (None means zeros)
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    dtype: str  # "f32" or "bf16": storage type of q, k, e, v and o
+    alpha_mu: float = 2.0
+    gamma_mu: float = 0.0
+    s0_std: float = 0.0  # 0 => S0 is zeros
+    chunk: int = 64
+    seed: int = 0
+    steps: int = 0  # decode workloads: number of one-token steps (T == 1)
+
+    @property
+    def token_heads(self) -> int:
+        return self.B * self.T * self.H * max(self.steps, 1)
+
+
+# The workloads the forward is measured and checked on.  d_k = d_v = 128 and
+# 16 or 32 heads are the head shapes of the paper's Dense/MoE models
+# (paper Appendix A, Table 4); 2K, 32K and 128K contexts follow its 4K
+# pretraining, 32K midtraining and RULER 4K-128K evaluation lengths.
+WORKLOADS = {
+    "tiny": Workload("tiny", B=1, T=64, H=1, dk=16, dv=16, dtype="f32", seed=0),
+    "train": Workload("train", B=4, T=2048, H=16, dk=128, dv=128, dtype="bf16", seed=1),
+    "long": Workload("long", B=1, T=32768, H=32, dk=128, dv=128, dtype="bf16",
+                     s0_std=0.02, seed=2),
+    "long_h16": Workload("long_h16", B=1, T=32768, H=16, dk=128, dv=128, dtype="bf16",
+                         s0_std=0.02, seed=12),
+    "verylong": Workload("verylong", B=1, T=131072, H=16, dk=128, dv=128, dtype="bf16",
+                         alpha_mu=3.0, gamma_mu=-1.0, seed=3),
+    "decode": Workload("decode", B=256, T=1, H=32, dk=128, dv=128, dtype="bf16",
+                       s0_std=0.02, seed=4, steps=128),
+}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def _unit(g: torch.Generator, shape, device) -> torch.Tensor:
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def make_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16", *,
+                seed: int = 0, alpha_mu: float = 2.0, alpha_std: float = 0.5,
+                gamma_mu: float = 0.0, s0_std: float = 0.0,
+                device: str | torch.device = "cpu") -> dict:
+    """Draw one batch of inputs.
+
+    q, k, e ~ N(0, 1) per element, L2-normalised over the channel axis in
+    fp32, then stored in `dtype` (bf16 rounding is round-to-nearest-even, so
+    the stored vectors have norm 1 up to ~2^-9).  v ~ N(0, 1).
+    alpha = sigmoid(N(alpha_mu, alpha_std)) per key channel; beta =
+    sigmoid(N(0, 1)); gamma = sigmoid(N(gamma_mu, 1)); S0 ~ N(0, s0_std) or
+    None when s0_std == 0.  Draw order is fixed (q, k, e, v, alpha, beta,
+    gamma, S0) so a seed names one input set on a given device.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    td = torch_dtype(dtype)
+    q = _unit(g, (B, T, H, dk), device).to(td)
+    k = _unit(g, (B, T, H, dk), device).to(td)
+    e = _unit(g, (B, T, H, dk), device).to(td)
+    v = torch.randn((B, T, H, dv), generator=g, device=device).to(td)
+    alpha = torch.sigmoid(alpha_mu + alpha_std * torch.randn((B, T, H, dk), generator=g,
+                                                              device=device))
+    beta = torch.sigmoid(torch.randn((B, T, H), generator=g, device=device))
+    gamma = torch.sigmoid(gamma_mu + torch.randn((B, T, H), generator=g, device=device))
+    S0: Optional[torch.Tensor] = None
+    if s0_std > 0:
+        S0 = s0_std * torch.randn((B, H, dk, dv), generator=g, device=device)
+    return dict(q=q, k=k, e=e, v=v, alpha=alpha.contiguous(), beta=beta.contiguous(),
+                gamma=gamma.contiguous(), S0=S0)
+
+
+def make_workload(w: Workload, device: str | torch.device = "cpu", seed: Optional[int] = None) -> dict:
+    """Inputs for a named workload.  Decode workloads return per-step inputs
+    stacked on a leading step axis: q, k, e, v, alpha are [steps, N, H, d],
+    beta, gamma are [steps, N, H], and S0 is [N, H, d_k, d_v]."""
+    s = w.seed if seed is None else seed
+    if w.steps:
+        x = make_inputs(w.steps, w.B, w.H, w.dk, w.dv, w.dtype, seed=s,
+                        alpha_mu=w.alpha_mu, gamma_mu=w.gamma_mu, s0_std=0.0,
+                        device=device)
+        g = torch.Generator(device=device)
+        g.manual_seed(s + 1_000_003)
+        x["S0"] = w.s0_std * torch.randn((w.B, w.H, w.dk, w.dv), generator=g, device=device)
+        return x
+    return make_inputs(w.B, w.T, w.H, w.dk, w.dv, w.dtype, seed=s, alpha_mu=w.alpha_mu,
+                       gamma_mu=w.gamma_mu, s0_std=w.s0_std, device=device)
+
+
+def hand_example() -> dict:
+    """The two-dimensional teaching example of the reading slides (frame "A
+    two-dimensional example isolates the new capability") and the Chinese
+    reading notes (method part 3): d_k = 2, d_v = 1, S_{t-1} = (3, 5)^T,
+    e = (1, 0), k = (0, 1), v = 7, D = I, beta = gamma = 1.  q is not given
+    on the pages; q = (1, 1) reads the sum of both rows.  fp32 storage."""
+    f = torch.float32
+    return dict(
+        q=torch.tensor([1.0, 1.0], dtype=f).view(1, 1, 1, 2),
+        k=torch.tensor([0.0, 1.0], dtype=f).view(1, 1, 1, 2),
+        e=torch.tensor([1.0, 0.0], dtype=f).view(1, 1, 1, 2),
+        v=torch.tensor([7.0], dtype=f).view(1, 1, 1, 1),
+        alpha=torch.ones((1, 1, 1, 2), dtype=f),
+        beta=torch.ones((1, 1, 1), dtype=f),
+        gamma=torch.ones((1, 1, 1), dtype=f),
+        S0=torch.tensor([[3.0], [5.0]], dtype=f).view(1, 1, 2, 1),
+    )
+
+
+def random_pair_abs_cos_mean(d: int) -> float:
+    """E|u.r| for independent uniform unit vectors in R^d:
+    Gamma(d/2) / (sqrt(pi) * Gamma((d+1)/2)).  For d = 128 this is the
+    ~0.0707 random-direction reference the paper's address-geometry probe
+    compares against (paper Sec. 4.5; slides frame on |cos(e, k)|)."""
+    return math.exp(math.lgamma(d / 2) - math.lgamma((d + 1) / 2)) / math.sqrt(math.pi)

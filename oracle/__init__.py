@@ -1,0 +1,123 @@
+"""fp64 CPU oracle for the Erase-then-Delta Attention (EDA) recurrence forward.
+
+TEST INFRASTRUCTURE ONLY: imported by `tests/`, by `__graft_entry__.smoke()`
+and by the benchmark's CPU-baseline leg, never by the GPU library or its
+Python binding.  It shares no code with the GPU path.
+
+`eda_ref.c` implements the paper's three ordered stages token by token
+(EDA paper Sec. 3.3, Eqs. (8)-(13)) in IEEE fp64; this module compiles it
+with the system C compiler and passes numpy arrays to it.  Inputs of any
+float type are widened to fp64 exactly (bf16 and fp32 values are exactly
+representable in fp64).
+
+Every function here is pinned by the `-m "not gpu"` tests in
+`tests/test_oracle_pins.py` (hand-worked example, readout identity, expanded
+operator, KDA reduction, explicit-matrix and exact-rational brute force,
+doubled-sequence form, special cases and invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "eda_ref.c")
+_LIB_PATH = os.path.join(_HERE, "libeda_ref.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile eda_ref.c into liboracle (plain gcc, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                        "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.eda_ref_fwd.argtypes = [dp] * 10 + [ctypes.c_long] * 5 + [ctypes.c_int]
+        lib.eda_ref_fwd.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor -> numpy (bf16 widened exactly via fp32)
+        import torch
+        x = x.detach().to("cpu")
+        if x.dtype == torch.bfloat16:
+            x = x.float()
+        x = x.numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def eda_ref_fwd(q, k, e, v, alpha, beta, gamma, S0=None, *, nthreads: Optional[int] = None,
+                want_state: bool = True):
+    """Token-by-token fp64 EDA forward.
+
+    q, k, e, alpha: [B, T, H, d_k]; v: [B, T, H, d_v]; beta, gamma: [B, T, H];
+    S0: [B, H, d_k, d_v] or None (zeros).  Returns (o [B, T, H, d_v],
+    S_final [B, H, d_k, d_v] or None), both fp64 numpy arrays.
+    """
+    q, k, e, v, alpha, beta, gamma, S0 = map(_f64, (q, k, e, v, alpha, beta, gamma, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, a, shp in (("k", k, (B, T, H, dk)), ("e", e, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("alpha", alpha, (B, T, H, dk)),
+                         ("beta", beta, (B, T, H)), ("gamma", gamma, (B, T, H))):
+        if a.shape != shp:
+            raise ValueError(f"oracle: {name} has shape {a.shape}, expected {shp}")
+    if S0 is not None and S0.shape != (B, H, dk, dv):
+        raise ValueError(f"oracle: S0 has shape {S0.shape}, expected {(B, H, dk, dv)}")
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    S_final = np.zeros((B, H, dk, dv), dtype=np.float64) if want_state else None
+    nt = nthreads or default_threads()
+    rc = _load().eda_ref_fwd(_ptr(q), _ptr(k), _ptr(e), _ptr(v), _ptr(alpha), _ptr(beta),
+                             _ptr(gamma), _ptr(S0), _ptr(o), _ptr(S_final),
+                             B, T, H, dk, dv, int(nt))
+    if rc != 0:
+        raise RuntimeError("oracle: eda_ref_fwd failed")
+    return o, S_final
+
+
+def eda_ref_decode(q, k, e, v, alpha, beta, gamma, S0, *, nthreads: Optional[int] = None):
+    """A sequence of one-token steps with the state carried between them.
+
+    Inputs are stacked per step: q, k, e, alpha: [steps, N, H, d_k]; v:
+    [steps, N, H, d_v]; beta, gamma: [steps, N, H]; S0: [N, H, d_k, d_v] or
+    None.  Each (n, h) is one head run over `steps` tokens, so this is the
+    same recurrence with the step axis as time; the arrays are only
+    re-ordered (no arithmetic).  Returns (o [steps, N, H, d_v], S_final).
+    """
+    sw = lambda x: None if x is None else np.swapaxes(_f64(x), 0, 1)
+    o, S = eda_ref_fwd(sw(q), sw(k), sw(e), sw(v), sw(alpha), sw(beta), sw(gamma),
+                       _f64(S0), nthreads=nthreads)
+    return np.ascontiguousarray(np.swapaxes(o, 0, 1)), S
