@@ -1,0 +1,165 @@
+/*
+ * eda.h -- C ABI of the MI355X (gfx950) Erase-then-Delta Attention forward.
+ *
+ * The operation (EDA paper, Sec. 3.3, Eq. (8); reading slides, frame "EDA
+ * preserves the delta write after cleanup"): every head keeps a state
+ * S in R^{d_k x d_v} (rows are key channels, fp32) and for each token t
+ *
+ *     S_t = (I - beta_t k_t k_t^T)(I - gamma_t e_t e_t^T) Diag(alpha_t) S_{t-1}
+ *           + beta_t k_t v_t^T,                 o_t = S_t^T q_t,
+ *
+ * i.e. decay the retained key channels, erase along the cleanup address
+ * e_t, then the delta-rule corrected write along k_t (Eqs. (9)-(13)); the
+ * readout uses the post-update state and no query scale.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor arguments are DEVICE pointers to contiguous row-major
+ *    arrays owned by the caller.  q, k, e, v, alpha, beta, gamma need only
+ *    their element alignment (2 or 4 bytes); states and the chunked path's
+ *    o must be 16-byte aligned (decode's o: element alignment).
+ *  - Token inputs use the layout [B, T, H, d] (batch, time, head, channel);
+ *    per-token scalars [B, T, H]; states [B, H, d_k, d_v].
+ *  - q, k, e, v and o share one storage type (`eda_dtype_t`); alpha, beta,
+ *    gamma and the states are always fp32.  Arithmetic on the state is fp32.
+ *  - Inputs are not range-checked (they are device data): the results are
+ *    defined for alpha in (0, 1], beta and gamma in [0, 1] and finite
+ *    values; q, k, e are used exactly as given (the layer normalises them,
+ *    paper Fig. 1).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *    enqueued; no call synchronises, allocates memory or keeps state between
+ *    calls, so concurrent calls on different streams are safe.
+ *  - Every check below happens before anything is enqueued; a call that
+ *    returns an error has touched no memory.  A failed kernel launch
+ *    returns EDA_ERR_HIP.  Nothing is printed and no exception crosses the
+ *    ABI.
+ */
+#ifndef EDA_H
+#define EDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EDA_OK = 0,
+    EDA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    EDA_ERR_SHAPE = 2,       /* a size is <= 0 or too large                       */
+    EDA_ERR_DTYPE = 3,       /* unknown eda_dtype_t                               */
+    EDA_ERR_ALIGN = 4,       /* a pointer is misaligned (see conventions)          */
+    EDA_ERR_UNSUPPORTED = 5, /* head dims or chunk size outside the supported set */
+    EDA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required        */
+    EDA_ERR_ALIAS = 7,       /* an output overlaps an input it may not overlap     */
+    EDA_ERR_HIP = 8          /* a HIP launch failed                               */
+} eda_status_t;
+
+typedef enum { EDA_F32 = 0, EDA_BF16 = 1 } eda_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *eda_status_string(eda_status_t s);
+
+/*
+ * Bytes of device workspace eda_fwd_chunked needs for these sizes (0 for an
+ * unsupported combination).  `chunk` is the number of tokens per chunk
+ * (0 selects the default, 32).
+ */
+size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v,
+                                      eda_dtype_t dtype, int chunk);
+
+/*
+ * Chunk-parallel (prefill) forward over a whole sequence.
+ *
+ * Computes, for all B*H heads, o_t for t = 0..T-1 and the final state,
+ * exactly the recurrence above up to floating-point rounding.  The sequence
+ * is cut into chunks of `chunk` tokens; each token is treated as two rank-1
+ * sub-steps, an erase (key e_t, gate gamma_t, decay alpha_t, no write) then
+ * a delta write (key k_t, gate beta_t, no decay, value v_t), which is the
+ * doubled-sequence form of the paper's Sec. 3.4 (Eqs. (17)-(18); slides
+ * frame "Two virtual steps recover a standard delta recurrence").  Within a
+ * chunk the sub-steps are solved with a triangular (UT/WY-type) transform
+ * and dense bf16/fp32 matrix-core products; the state is carried across
+ * chunks in fp32.  The chunk size does not change the exact result.
+ *
+ *   q, k, e : [B, T, H, d_k]  dtype          v : [B, T, H, d_v]  dtype
+ *   alpha   : [B, T, H, d_k]  fp32 retention per key channel
+ *   beta, gamma : [B, T, H]   fp32 write gate and erase gate
+ *   S0      : [B, H, d_k, d_v] fp32 initial state, or NULL for zeros
+ *   o       : [B, T, H, d_v]  dtype, written (fp32 accumulation, then
+ *             round-to-nearest-even for bf16)
+ *   S_final : [B, H, d_k, d_v] fp32 final state, or NULL (not written);
+ *             may be the same pointer as S0 (updated in place)
+ *   workspace : device scratch of at least
+ *             eda_fwd_chunked_workspace_size(...) bytes, 256-byte aligned;
+ *             its contents on entry are ignored and on return undefined
+ *
+ * Supported: 1 <= d_k, d_v <= 128; chunk in {0, 16, 32}; B, T, H >= 1 with
+ * B*T*H*max(d_k, d_v) < 2^31.  o may not overlap any input; S_final may
+ * overlap S0 only as the identical pointer.
+ */
+eda_status_t eda_fwd_chunked(const void *q, const void *k, const void *e, const void *v,
+                             const float *alpha, const float *beta, const float *gamma,
+                             const float *S0, void *o, float *S_final,
+                             int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
+                             int chunk, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * The two halves of eda_fwd_chunked, for callers that want to schedule them
+ * separately (for example, prepare the next batch's chunk factors while the
+ * state pass of this one runs, or time the two phases).  Calling prepare and
+ * then finish with the same sizes, dtype, chunk and workspace (on one stream,
+ * or with the ordering made explicit) is exactly eda_fwd_chunked.
+ *
+ * eda_fwd_chunked_prepare: from q, k, e, alpha, beta, gamma alone, fills the
+ *   workspace with every per-chunk factor that does not depend on the state
+ *   (the decayed sub-step Gram's triangular inverse applied to the erase and
+ *   write keys, the query products and the chunk's total decay).  Chunks are
+ *   independent, so this phase is fully parallel.
+ * eda_fwd_chunked_finish: carries the fp32 state through the chunks in order
+ *   (serial over chunks, parallel over heads and value columns), reading v,
+ *   beta and the prepared workspace, and writes o and S_final.
+ *
+ * Arguments, layouts and checks are those of eda_fwd_chunked; a phase
+ * ignores the pointers it does not use.  The workspace contents between the
+ * two calls are opaque and valid only for the same sizes, dtype and chunk.
+ */
+eda_status_t eda_fwd_chunked_prepare(const void *q, const void *k, const void *e,
+                                     const float *alpha, const float *beta, const float *gamma,
+                                     int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
+                                     int chunk, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+eda_status_t eda_fwd_chunked_finish(const void *v, const float *beta, const float *S0, void *o,
+                                    float *S_final, int B, int T, int H, int d_k, int d_v,
+                                    eda_dtype_t dtype, int chunk, const void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
+ * One token of the recurrence for N independent sequences (decode).
+ *
+ * For each (n, h): reads S_in once, applies decay, erase and corrected write
+ * for one token and writes S_out and o.  The three reductions S^T e, S^T k,
+ * S^T q are taken in the same pass over S (the paper's Sec. 3.5 notes that
+ * decoding is dominated by reading and writing the state).
+ *
+ *   q, k, e : [N, H, d_k] dtype   v : [N, H, d_v] dtype
+ *   alpha   : [N, H, d_k] fp32    beta, gamma : [N, H] fp32
+ *   S_in    : [N, H, d_k, d_v] fp32, or NULL for zeros
+ *   S_out   : [N, H, d_k, d_v] fp32, required; may equal S_in (in place)
+ *   o       : [N, H, d_v] dtype
+ *
+ * Supported: 1 <= d_k, d_v <= 128, N, H >= 1.  S_out may overlap S_in only
+ * as the identical pointer; o may not overlap any input.
+ */
+eda_status_t eda_fwd_recurrent_step(const void *q, const void *k, const void *e, const void *v,
+                                    const float *alpha, const float *beta, const float *gamma,
+                                    const float *S_in, float *S_out, void *o,
+                                    int N, int H, int d_k, int d_v, eda_dtype_t dtype,
+                                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EDA_H */

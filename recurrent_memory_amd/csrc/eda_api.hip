@@ -1,0 +1,232 @@
+// eda_api.hip -- the C ABI declared in include/eda.h: argument checks, then
+// kernel launches.  Every check runs before anything is enqueued.
+#include <stdint.h>
+
+#include "../../include/eda.h"
+#include "eda_common.h"
+
+namespace eda {
+template <typename Tin>
+hipError_t launch_decode(const void *, const void *, const void *, const void *, const float *,
+                         const float *, const float *, const float *, float *, void *, int, int,
+                         int, int, hipStream_t);
+template <typename T>
+size_t chunked_ws_t(int, int, int, int, int, int);
+template <typename T>
+hipError_t launch_chunked(int, const void *, const void *, const void *, const void *,
+                          const float *, const float *, const float *, const float *, void *,
+                          float *, int, int, int, int, int, int, void *, hipStream_t);
+}  // namespace eda
+
+namespace {
+
+constexpr int kDefaultChunk = 32;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+    bool set;
+};
+
+Range range_of(const void *p, size_t bytes) {
+    Range r;
+    r.lo = (uintptr_t)p;
+    r.hi = r.lo + bytes;
+    r.set = p != nullptr && bytes > 0;
+    return r;
+}
+
+bool overlap(const Range &a, const Range &b) { return a.set && b.set && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+size_t elem_size(eda_dtype_t dt) { return dt == EDA_BF16 ? 2 : 4; }
+
+bool dtype_ok(eda_dtype_t dt) { return dt == EDA_F32 || dt == EDA_BF16; }
+
+bool dims_ok(long a, long b, long c, int dk, int dv) {
+    if (a <= 0 || b <= 0 || c <= 0 || dk <= 0 || dv <= 0) return false;
+    const long dmax = dk > dv ? dk : dv;
+    return a * b * c * dmax < (1L << 31);
+}
+
+bool head_dims_supported(int dk, int dv) { return dk >= 1 && dk <= 128 && dv >= 1 && dv <= 128; }
+
+int resolve_chunk(int chunk) { return chunk == 0 ? kDefaultChunk : chunk; }
+
+bool chunk_supported(int chunk) { return chunk == 16 || chunk == 32; }
+
+}  // namespace
+
+extern "C" {
+
+const char *eda_status_string(eda_status_t s) {
+    switch (s) {
+        case EDA_OK: return "ok";
+        case EDA_ERR_NULL: return "required pointer is NULL";
+        case EDA_ERR_SHAPE: return "size out of range";
+        case EDA_ERR_DTYPE: return "unknown dtype";
+        case EDA_ERR_ALIGN: return "pointer misaligned (see eda.h)";
+        case EDA_ERR_UNSUPPORTED: return "head dims or chunk size not supported";
+        case EDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case EDA_ERR_ALIAS: return "output overlaps an input";
+        case EDA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
+                                      int chunk) {
+    chunk = resolve_chunk(chunk);
+    if (!dtype_ok(dtype) || !dims_ok(B, T, H, d_k, d_v) || !head_dims_supported(d_k, d_v) ||
+        !chunk_supported(chunk))
+        return 0;
+    return dtype == EDA_BF16 ? eda::chunked_ws_t<eda::bf16>(B, T, H, d_k, d_v, chunk)
+                             : eda::chunked_ws_t<float>(B, T, H, d_k, d_v, chunk);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks and launch for the chunked family.  phase 1 = prepare
+// (needs q, k, e, alpha, beta, gamma), 2 = finish (needs v, beta, o),
+// 3 = both.  Pointers a phase does not use may be NULL and are ignored.
+eda_status_t chunked_call(int phase, const void *q, const void *k, const void *e, const void *v,
+                          const float *alpha, const float *beta, const float *gamma,
+                          const float *S0, void *o, float *S_final, int B, int T, int H, int d_k,
+                          int d_v, eda_dtype_t dtype, int chunk, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    if (phase & 1) {
+        if (!q || !k || !e || !alpha || !beta || !gamma) return EDA_ERR_NULL;
+    } else {
+        q = k = e = nullptr;
+        alpha = gamma = nullptr;
+    }
+    if (phase & 2) {
+        if (!v || !beta || !o) return EDA_ERR_NULL;
+    } else {
+        v = nullptr;
+        S0 = nullptr;
+        o = nullptr;
+        S_final = nullptr;
+    }
+    if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
+    if (!dims_ok(B, T, H, d_k, d_v)) return EDA_ERR_SHAPE;
+    chunk = resolve_chunk(chunk);
+    if (!head_dims_supported(d_k, d_v) || !chunk_supported(chunk)) return EDA_ERR_UNSUPPORTED;
+    // Element alignment for arrays read element-wise; 16 bytes where the
+    // kernels use vector accesses (o, states).
+    const size_t es = elem_size(dtype);
+    const void *elem_ptrs[] = {q, k, e, v};
+    for (const void *p : elem_ptrs)
+        if (p && !aligned(p, es)) return EDA_ERR_ALIGN;
+    const void *f32_ptrs[] = {alpha, beta, gamma};
+    for (const void *p : f32_ptrs)
+        if (p && !aligned(p, 4)) return EDA_ERR_ALIGN;
+    const void *vec_ptrs[] = {S0, o, S_final};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned(p, 16)) return EDA_ERR_ALIGN;
+    const size_t need = eda_fwd_chunked_workspace_size(B, T, H, d_k, d_v, dtype, chunk);
+    if (need == 0) return EDA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < need) return EDA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return EDA_ERR_ALIGN;
+
+    const size_t btH = (size_t)B * T * H;
+    const Range in[] = {range_of(q, btH * d_k * es), range_of(k, btH * d_k * es),
+                        range_of(e, btH * d_k * es), range_of(v, btH * d_v * es),
+                        range_of(alpha, btH * d_k * 4), range_of(beta, btH * 4),
+                        range_of(gamma, btH * 4)};
+    const Range rS0 = range_of(S0, (size_t)B * H * d_k * d_v * 4);
+    const Range rSf = range_of(S_final, (size_t)B * H * d_k * d_v * 4);
+    const Range rO = range_of(o, btH * d_v * es);
+    const Range rW = range_of(workspace, need);
+    for (const Range &r : in) {
+        if (overlap(rO, r) || overlap(rSf, r) || overlap(rW, r)) return EDA_ERR_ALIAS;
+    }
+    if (overlap(rO, rS0) || overlap(rO, rSf) || overlap(rO, rW)) return EDA_ERR_ALIAS;
+    if (overlap(rW, rS0) || overlap(rW, rSf)) return EDA_ERR_ALIAS;
+    if (overlap(rSf, rS0) && S_final != S0) return EDA_ERR_ALIAS;
+
+    hipError_t err =
+        dtype == EDA_BF16
+            ? eda::launch_chunked<eda::bf16>(phase, q, k, e, v, alpha, beta, gamma, S0, o, S_final,
+                                             B, T, H, d_k, d_v, chunk, workspace,
+                                             (hipStream_t)stream)
+            : eda::launch_chunked<float>(phase, q, k, e, v, alpha, beta, gamma, S0, o, S_final, B,
+                                         T, H, d_k, d_v, chunk, workspace, (hipStream_t)stream);
+    return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+eda_status_t eda_fwd_chunked(const void *q, const void *k, const void *e, const void *v,
+                             const float *alpha, const float *beta, const float *gamma,
+                             const float *S0, void *o, float *S_final, int B, int T, int H,
+                             int d_k, int d_v, eda_dtype_t dtype, int chunk, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    return chunked_call(3, q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v,
+                        dtype, chunk, workspace, workspace_bytes, stream);
+}
+
+eda_status_t eda_fwd_chunked_prepare(const void *q, const void *k, const void *e,
+                                     const float *alpha, const float *beta, const float *gamma,
+                                     int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
+                                     int chunk, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    return chunked_call(1, q, k, e, nullptr, alpha, beta, gamma, nullptr, nullptr, nullptr, B, T,
+                        H, d_k, d_v, dtype, chunk, workspace, workspace_bytes, stream);
+}
+
+eda_status_t eda_fwd_chunked_finish(const void *v, const float *beta, const float *S0, void *o,
+                                    float *S_final, int B, int T, int H, int d_k, int d_v,
+                                    eda_dtype_t dtype, int chunk, const void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    return chunked_call(2, nullptr, nullptr, nullptr, v, nullptr, beta, nullptr, S0, o, S_final,
+                        B, T, H, d_k, d_v, dtype, chunk, const_cast<void *>(workspace),
+                        workspace_bytes, stream);
+}
+
+eda_status_t eda_fwd_recurrent_step(const void *q, const void *k, const void *e, const void *v,
+                                    const float *alpha, const float *beta, const float *gamma,
+                                    const float *S_in, float *S_out, void *o, int N, int H,
+                                    int d_k, int d_v, eda_dtype_t dtype, void *stream) {
+    if (!q || !k || !e || !v || !alpha || !beta || !gamma || !S_out || !o) return EDA_ERR_NULL;
+    if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
+    if (!dims_ok(N, 1, H, d_k, d_v)) return EDA_ERR_SHAPE;
+    if (!head_dims_supported(d_k, d_v)) return EDA_ERR_UNSUPPORTED;
+    const size_t es0 = elem_size(dtype);
+    const void *elem_ptrs[] = {q, k, e, v, o};
+    for (const void *p : elem_ptrs)
+        if (!aligned(p, es0)) return EDA_ERR_ALIGN;
+    const void *f32_ptrs[] = {alpha, beta, gamma};
+    for (const void *p : f32_ptrs)
+        if (!aligned(p, 4)) return EDA_ERR_ALIGN;
+    const void *vec_ptrs[] = {S_in, S_out};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned(p, 16)) return EDA_ERR_ALIGN;
+
+    const size_t es = elem_size(dtype), nH = (size_t)N * H;
+    const Range in[] = {range_of(q, nH * d_k * es), range_of(k, nH * d_k * es),
+                        range_of(e, nH * d_k * es), range_of(v, nH * d_v * es),
+                        range_of(alpha, nH * d_k * 4), range_of(beta, nH * 4),
+                        range_of(gamma, nH * 4)};
+    const Range rSi = range_of(S_in, nH * d_k * d_v * 4);
+    const Range rSo = range_of(S_out, nH * d_k * d_v * 4);
+    const Range rO = range_of(o, nH * d_v * es);
+    for (const Range &r : in)
+        if (overlap(rO, r) || overlap(rSo, r)) return EDA_ERR_ALIAS;
+    if (overlap(rO, rSi) || overlap(rO, rSo)) return EDA_ERR_ALIAS;
+    if (overlap(rSo, rSi) && S_out != S_in) return EDA_ERR_ALIAS;
+
+    hipError_t err =
+        dtype == EDA_BF16
+            ? eda::launch_decode<eda::bf16>(q, k, e, v, alpha, beta, gamma, S_in, S_out, o, N, H,
+                                            d_k, d_v, (hipStream_t)stream)
+            : eda::launch_decode<float>(q, k, e, v, alpha, beta, gamma, S_in, S_out, o, N, H, d_k,
+                                        d_v, (hipStream_t)stream);
+    return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
+}
+
+}  // extern "C"

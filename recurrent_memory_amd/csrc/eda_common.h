@@ -1,0 +1,139 @@
+// eda_common.h -- device helpers shared by the EDA kernels (gfx950 only).
+//
+// Storage types: `bf16` is the raw 16-bit pattern of a bfloat16 (round to
+// nearest even on conversion); fp32 is plain float.  Matrix-core products use
+// the "NT" convention throughout:
+//
+//     C[m][n] += sum_k X[m][k] * Y[n][k]
+//
+// with both X and Y stored row-major with k contiguous.  One 16x16 output
+// tile is accumulated by one wavefront (64 lanes).  For lane l the operand
+// fragments are X[m0 + l%16][k0 + KPL*(l/16) + 0..KPL-1] and the same for Y
+// (KPL = 8 for the bf16 16x16x32 instruction, 1 for fp32 16x16x4); since the
+// same k-to-lane map is used for both operands, the sum over k is exact
+// whatever order the hardware reduces k in.  The 16x16 fp32 accumulator of
+// lane l holds C[4*(l/16) + i][l%16], i = 0..3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eda {
+
+typedef uint16_t bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);                                         // nearest even
+    return (bf16)(u >> 16);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// Matrix-core traits.  KB = k consumed per instruction, KPL = k per lane.
+// ---------------------------------------------------------------------------
+template <typename T> struct MM;
+
+template <> struct MM<bf16> {
+    static constexpr int KB = 32, KPL = 8;
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ frag load(const bf16 *p) {
+        return *reinterpret_cast<const bf16x8 *>(p);
+    }
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // k = 16 remainder: 16x16x16 instruction, 4 k per lane.
+    static __device__ __forceinline__ f32x4 mma16(const bf16 *x, const bf16 *y, f32x4 c) {
+        s16x4 a = *reinterpret_cast<const s16x4 *>(x);
+        s16x4 b = *reinterpret_cast<const s16x4 *>(y);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct MM<float> {
+    static constexpr int KB = 4, KPL = 1;
+    typedef float frag;
+    static __device__ __forceinline__ frag load(const float *p) { return *p; }
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// acc += X[0:16][0:K] * Y[0:16][0:K]^T for the wave's 16x16 tile.
+// X, Y point at the tile's first row; ldx, ldy are row strides (elements).
+template <typename T, int K>
+__device__ __forceinline__ f32x4 tile_nt(const T *X, int ldx, const T *Y, int ldy, f32x4 acc,
+                                         int lane) {
+    static_assert(K % 16 == 0, "tile depth must be a multiple of 16");
+    const int r = lane & 15, g = lane >> 4;
+    if constexpr (sizeof(T) == 2) {
+        constexpr int KF = K / 32 * 32;
+        const T *xp = X + r * ldx + 8 * g;
+        const T *yp = Y + r * ldy + 8 * g;
+#pragma unroll
+        for (int k0 = 0; k0 < KF; k0 += 32)
+            acc = MM<T>::mma(MM<T>::load(xp + k0), MM<T>::load(yp + k0), acc);
+        if constexpr (K % 32 == 16)
+            acc = MM<T>::mma16(X + r * ldx + KF + 4 * g, Y + r * ldy + KF + 4 * g, acc);
+    } else {
+        const T *xp = X + r * ldx + g;
+        const T *yp = Y + r * ldy + g;
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += 4)
+            acc = MM<T>::mma(xp[k0], yp[k0], acc);
+    }
+    return acc;
+}
+
+// Same, with a run-time depth (multiple of 16 for bf16, of 4 for fp32).
+template <typename T>
+__device__ __forceinline__ f32x4 tile_nt_dyn(const T *X, int ldx, const T *Y, int ldy, int K,
+                                             f32x4 acc, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    if constexpr (sizeof(T) == 2) {
+        int k0 = 0;
+        const T *xp = X + r * ldx + 8 * g;
+        const T *yp = Y + r * ldy + 8 * g;
+        for (; k0 + 32 <= K; k0 += 32)
+            acc = MM<T>::mma(MM<T>::load(xp + k0), MM<T>::load(yp + k0), acc);
+        if (k0 < K)
+            acc = MM<T>::mma16(X + r * ldx + k0 + 4 * g, Y + r * ldy + k0 + 4 * g, acc);
+    } else {
+        const T *xp = X + r * ldx + g;
+        const T *yp = Y + r * ldy + g;
+        for (int k0 = 0; k0 < K; k0 += 4) acc = MM<T>::mma(xp[k0], yp[k0], acc);
+    }
+    return acc;
+}
+
+// Store 4 consecutive values (one accumulator's column run) as T.
+template <typename T> __device__ __forceinline__ void store4(T *p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, float a, float b, float c, float d) {
+    s16x4 v;
+    v[0] = (short)from_f32<bf16>(a);
+    v[1] = (short)from_f32<bf16>(b);
+    v[2] = (short)from_f32<bf16>(c);
+    v[3] = (short)from_f32<bf16>(d);
+    *reinterpret_cast<s16x4 *>(p) = v;
+}
+template <> __device__ __forceinline__ void store4<float>(float *p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{a, b, c, d};
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+}  // namespace eda

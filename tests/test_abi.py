@@ -1,0 +1,139 @@
+"""C-ABI contract tests that need the built library but no GPU.
+
+Every argument check in libeda.so runs before any HIP call, so invalid
+calls can be made with fake (never dereferenced) device addresses.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import recurrent_memory_amd as eda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "eda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(eda.library_path()),
+                                reason="libeda.so not built")
+
+
+def declared_functions():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(eda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("eda_fwd_chunked", "eda_fwd_recurrent_step", "eda_fwd_chunked_workspace_size",
+              "eda_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(eda.library_path())
+    for n in declared_functions():
+        assert hasattr(lib, n), f"libeda.so does not export {n}"
+
+
+def test_status_strings():
+    lib = eda.load_library()
+    for code in range(9):
+        s = lib.eda_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.eda_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_size():
+    lib = eda.load_library()
+    ws = lib.eda_fwd_chunked_workspace_size
+    big = ws(4, 2048, 16, 128, 128, 1, 32)
+    assert big > 0
+    assert ws(4, 2048, 16, 128, 128, 1, 0) == big            # 0 selects the default chunk
+    assert ws(4, 4096, 16, 128, 128, 1, 32) == 2 * big        # linear in the chunk count
+    assert ws(4, 2048, 16, 128, 128, 0, 32) > big             # fp32 factors are larger
+    assert ws(1, 1, 1, 2, 1, 0, 16) > 0
+    assert ws(4, 2048, 16, 129, 128, 1, 32) == 0              # unsupported head dim
+    assert ws(4, 2048, 16, 128, 128, 1, 48) == 0              # unsupported chunk
+    assert ws(4, 2048, 16, 128, 128, 7, 32) == 0              # bad dtype
+    assert ws(0, 2048, 16, 128, 128, 1, 32) == 0
+
+
+# Fake device addresses: distinct, 256-byte aligned, far apart, never dereferenced.
+BASE = 1 << 40
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(BASE + (i << 32) + off)
+
+
+def chunked_args(**kw):
+    B, T, H, dk, dv, dt, chunk = 2, 64, 2, 64, 64, 1, 32
+    a = dict(q=fake(1), k=fake(2), e=fake(3), v=fake(4), alpha=fake(5), beta=fake(6),
+             gamma=fake(7), S0=fake(8), o=fake(9), S_final=fake(10), B=B, T=T, H=H, dk=dk, dv=dv,
+             dt=dt, chunk=chunk, ws=fake(11), wsb=1 << 30, stream=None)
+    a.update(kw)
+    return a
+
+
+def call_chunked(a):
+    lib = eda.load_library()
+    return lib.eda_fwd_chunked(a["q"], a["k"], a["e"], a["v"], a["alpha"], a["beta"], a["gamma"],
+                               a["S0"], a["o"], a["S_final"], a["B"], a["T"], a["H"], a["dk"],
+                               a["dv"], a["dt"], a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("field,val,code", [
+    ("q", None, 1), ("v", None, 1), ("alpha", None, 1), ("o", None, 1),
+    ("dt", 5, 3),
+    ("B", 0, 2), ("T", -1, 2), ("dk", 0, 2),
+    ("dk", 129, 5), ("dv", 200, 5), ("chunk", 64, 5), ("chunk", 7, 5),
+    ("q", fake(1, 1), 4), ("alpha", fake(5, 2), 4), ("S0", fake(8, 4), 4), ("o", fake(9, 8), 4),
+    ("ws", fake(11, 128), 4),
+    ("ws", None, 6), ("wsb", 1024, 6),
+    ("o", fake(1, 256), 7),           # o inside q
+    ("S_final", fake(8, 256), 7),     # partial overlap with S0
+    ("o", fake(11, 512), 7),          # o inside the workspace
+])
+def test_chunked_rejects(field, val, code):
+    assert call_chunked(chunked_args(**{field: val})) == code
+
+
+def test_scalar_inputs_need_only_element_alignment():
+    # per-token gates sliced out of a stacked tensor sit at 4-byte offsets
+    assert call_chunked(chunked_args(beta=fake(6, 4), gamma=fake(7, 12), alpha=fake(5, 4),
+                                     q=fake(1, 2), dt=1, wsb=16)) == 6  # reaches the workspace check
+
+
+def test_chunked_too_large_shape():
+    assert call_chunked(chunked_args(B=1 << 12, T=1 << 12, H=1 << 4, dk=128, dv=128)) == 2
+
+
+def call_step(**kw):
+    a = dict(q=fake(1), k=fake(2), e=fake(3), v=fake(4), alpha=fake(5), beta=fake(6), gamma=fake(7),
+             S_in=fake(8), S_out=fake(9), o=fake(10), N=4, H=2, dk=128, dv=128, dt=1, stream=None)
+    a.update(kw)
+    lib = eda.load_library()
+    return lib.eda_fwd_recurrent_step(a["q"], a["k"], a["e"], a["v"], a["alpha"], a["beta"],
+                                      a["gamma"], a["S_in"], a["S_out"], a["o"], a["N"], a["H"],
+                                      a["dk"], a["dv"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S_out=None), 1), (dict(o=None), 1), (dict(k=None), 1),
+    (dict(dt=2), 3), (dict(N=0), 2), (dict(dv=0), 2), (dict(dk=130), 5),
+    (dict(e=fake(3, 1)), 4), (dict(beta=fake(6, 2)), 4), (dict(S_in=fake(8, 8)), 4),
+    (dict(S_out=fake(8, 1024)), 7),    # partial overlap with S_in
+    (dict(o=fake(1, 64)), 7),          # o inside q
+    (dict(S_out=fake(5)), 7),          # state written over alpha
+])
+def test_step_rejects(kw, code):
+    assert call_step(**kw) == code
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 4, 1, 8))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        eda.fwd_chunked(x, x, x, x, x, x[..., 0], x[..., 0])

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every element; full-size workloads compare every output
+of a seeded sample of heads (heads are independent, so each sampled head's
+oracle run is exact).  Tolerances: fp32 inputs max-abs <= 1e-4; bf16 inputs
+relative Frobenius <= 5e-3 on o and on the final state.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import recurrent_memory_amd as eda
+import oracle
+from eda_inputs import WORKLOADS, hand_example, make_inputs, make_workload
+from _helpers import check, oracle_heads, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(x):
+    return {n: (None if t is None else t.to(DEV)) for n, t in x.items()}
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def run_chunked(x, chunk=0, **kw):
+    o, S = eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"],
+                           x["S0"], chunk=chunk, **kw)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def full_oracle(x):
+    return oracle.eda_ref_fwd(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"],
+                              x["S0"])
+
+
+# ---------------------------------------------------------------------------
+# the hand-worked example, exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_hand_example_chunked(dtype, chunk):
+    say(f"hand example chunked {dtype} chunk={chunk}")
+    x = hand_example()
+    for n in ("q", "k", "e", "v"):
+        x[n] = x[n].to(dtype)
+    o, S = run_chunked(dev(x), chunk=chunk)
+    assert S.cpu().flatten().tolist() == [0.0, 7.0]
+    assert float(o.float().cpu()) == 7.0
+    x["gamma"] = torch.zeros_like(x["gamma"])
+    o, S = run_chunked(dev(x), chunk=chunk)
+    assert S.cpu().flatten().tolist() == [3.0, 7.0]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_hand_example_decode(dtype):
+    say(f"hand example decode {dtype}")
+    x = hand_example()
+    d = {n: t[:, 0] for n, t in x.items() if n != "S0"}
+    for n in ("q", "k", "e", "v"):
+        d[n] = d[n].to(dtype)
+    d = dev(d)
+    o, S = eda.recurrent_step(d["q"], d["k"], d["e"], d["v"], d["alpha"], d["beta"], d["gamma"],
+                              x["S0"].to(DEV))
+    torch.cuda.synchronize()
+    assert S.cpu().flatten().tolist() == [0.0, 7.0]
+    assert float(o.float().cpu()) == 7.0
+
+
+# ---------------------------------------------------------------------------
+# small and ragged cases, every element
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_tiny_workload_fp32(chunk):
+    w = WORKLOADS["tiny"]
+    say(f"tiny fp32 chunk={chunk}")
+    x = make_workload(w)
+    ro, rS = full_oracle(x)
+    o, S = run_chunked(dev(x), chunk=chunk)
+    check(to64(o), to64(S), ro, rS, "f32", f"tiny chunk={chunk}")
+
+
+def test_tiny_workload_fp32_decode():
+    w = WORKLOADS["tiny"]
+    say("tiny fp32 decode over T=64 steps")
+    x = make_workload(w)
+    ro, rS = full_oracle(x)
+    xd = dev(x)
+    S = torch.zeros((1, 1, 16, 16), device=DEV)
+    outs = []
+    for t in range(w.T):
+        o, S = eda.recurrent_step(*(xd[n][:, t].contiguous() for n in
+                                    ("q", "k", "e", "v", "alpha", "beta", "gamma")), S, inplace=True)
+        outs.append(o.clone())
+    torch.cuda.synchronize()
+    got = torch.stack(outs, 1)
+    check(to64(got), to64(S), ro, rS, "f32", "tiny decode")
+
+
+RAGGED = [(1, 1, 1, 16), (1, 1, 1, 32), (2, 15, 3, 16), (1, 33, 2, 32), (2, 100, 2, 16),
+          (1, 64, 1, 32), (1, 65, 1, 32), (3, 47, 1, 16)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,H,chunk", RAGGED)
+def test_ragged(dtype, B, T, H, chunk):
+    dk, dv = (48, 80) if dtype == "f32" else (128, 128)
+    say(f"ragged {dtype} B={B} T={T} H={H} chunk={chunk} dk={dk} dv={dv}")
+    x = make_inputs(B, T, H, dk, dv, dtype, seed=100 + T, s0_std=0.5)
+    ro, rS = full_oracle(x)
+    o, S = run_chunked(dev(x), chunk=chunk)
+    check(to64(o), to64(S), ro, rS, dtype, f"ragged T={T}")
+
+
+@pytest.mark.parametrize("dk,dv", [(2, 1), (16, 16), (31, 7), (48, 80), (64, 64), (100, 128),
+                                   (128, 33), (128, 128)])
+def test_head_dims_fp32(dk, dv):
+    say(f"head dims fp32 dk={dk} dv={dv}")
+    x = make_inputs(2, 40, 2, dk, dv, "f32", seed=dk * 1000 + dv, s0_std=0.3)
+    ro, rS = full_oracle(x)
+    o, S = run_chunked(dev(x))
+    check(to64(o), to64(S), ro, rS, "f32", f"dims {dk}x{dv}")
+    xs = {n: t[:, 0].contiguous() for n, t in x.items() if n != "S0"}
+    xs = dev(xs)
+    od, Sd = eda.recurrent_step(xs["q"], xs["k"], xs["e"], xs["v"], xs["alpha"], xs["beta"],
+                                xs["gamma"], x["S0"].to(DEV))
+    ro1, rS1 = oracle.eda_ref_fwd(*(x[n][:, :1] for n in ("q", "k", "e", "v", "alpha", "beta", "gamma")),
+                                  x["S0"])
+    torch.cuda.synchronize()
+    check(to64(od), to64(Sd), ro1[:, 0], rS1, "f32", f"decode dims {dk}x{dv}")
+
+
+def test_chunk_sizes_agree_bf16():
+    say("chunk 16 vs 32 bf16")
+    x = dev(make_inputs(2, 300, 4, 128, 128, "bf16", seed=5, s0_std=0.02))
+    o16, S16 = run_chunked(x, chunk=16)
+    o32, S32 = run_chunked(x, chunk=32)
+    xo = {n: (None if t is None else t.cpu()) for n, t in x.items()}
+    ro, rS = full_oracle(xo)
+    check(to64(o16), to64(S16), ro, rS, "bf16", "chunk16")
+    check(to64(o32), to64(S32), ro, rS, "bf16", "chunk32")
+
+
+def test_resume_and_inplace_state():
+    """chunked(T1) -> S; chunked(T2, S0=S) continues the same recurrence
+    (the state is the whole checkpoint); S_final may be S0 itself."""
+    say("resume T1=200 + T2=137, in-place state")
+    x = make_inputs(2, 337, 3, 128, 128, "bf16", seed=9, s0_std=0.02)
+    ro, rS = full_oracle(x)
+    xd = dev(x)
+    part = lambda a, b_: {n: (t[:, a:b_].contiguous() if n != "S0" else t) for n, t in xd.items()}
+    x1 = part(0, 200)
+    o1, S1 = run_chunked(x1)
+    x2 = part(200, 337)
+    x2["S0"] = S1
+    o2, S2 = eda.fwd_chunked(*(x2[n].contiguous() for n in ("q", "k", "e", "v", "alpha", "beta", "gamma")),
+                             S1, S_final=S1)  # in place
+    torch.cuda.synchronize()
+    assert S2.data_ptr() == S1.data_ptr()
+    got_o = torch.cat([o1, o2], 1)
+    check(to64(got_o), to64(S2), ro, rS, "bf16", "resume")
+
+
+def test_prefill_then_decode_handoff():
+    say("prefill 150 tokens then 20 decode steps")
+    x = make_inputs(2, 170, 4, 128, 128, "bf16", seed=21, s0_std=0.02)
+    ro, rS = full_oracle(x)
+    xd = dev(x)
+    pre = {n: (t[:, :150].contiguous() if n != "S0" else t) for n, t in xd.items()}
+    o1, S = run_chunked(pre)
+    outs = [o1]
+    for t in range(150, 170):
+        o, S = eda.recurrent_step(*(xd[n][:, t].contiguous() for n in
+                                    ("q", "k", "e", "v", "alpha", "beta", "gamma")), S, inplace=True)
+        outs.append(o[:, None])
+    torch.cuda.synchronize()
+    check(to64(torch.cat(outs, 1)), to64(S), ro, rS, "bf16", "handoff")
+
+
+@pytest.mark.parametrize("kind", ["floor", "one"])
+def test_stress_decay_extremes(kind):
+    """alpha at the safe gate's floor e^-5 on every channel (the chunk's decay
+    leaves fp32 range, exercising the exact wide-decay path) and alpha = 1."""
+    say(f"stress alpha={kind}")
+    x = make_inputs(1, 4096, 2, 128, 128, "bf16", seed=5)
+    x["alpha"] = torch.full_like(x["alpha"], math.exp(-5.0) if kind == "floor" else 1.0)
+    ro, rS = full_oracle(x)
+    o, S = run_chunked(dev(x))
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    check(to64(o), to64(S), ro, rS, "bf16", f"stress {kind}")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled heads
+# ---------------------------------------------------------------------------
+def sampled_check(name, n_heads, seed=0):
+    w = WORKLOADS[name]
+    say(f"{name} full size B={w.B} T={w.T} H={w.H}, {n_heads} sampled heads")
+    x = make_workload(w, device=DEV)
+    o, S = run_chunked(x, chunk=0)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    rng = np.random.default_rng(seed)
+    heads = sorted({(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(n_heads)})
+    xc = {n: (None if t is None else t.cpu()) for n, t in x.items()}
+    refs = oracle_heads(xc, heads)
+    go = np.concatenate([to64(o[b, :, h]) for b, h in heads])
+    gs = np.concatenate([to64(S[b, h]) for b, h in heads])
+    ro = np.concatenate([r[0] for r in refs])
+    rs = np.concatenate([r[1] for r in refs])
+    return check(go, gs, ro, rs, "bf16", f"{name} heads={heads}")
+
+
+def test_train_workload_sampled():
+    sampled_check("train", 8)
+
+
+@pytest.mark.slow
+def test_long_workload_sampled():
+    sampled_check("long", 3)
+
+
+@pytest.mark.slow
+def test_verylong_workload_sampled():
+    sampled_check("verylong", 2)
+
+
+def test_decode_workload_sampled():
+    """256 sequences x 32 heads, 128 one-token steps updating the state in
+    place; the oracle runs the sampled (n, h) heads over the same 128 steps."""
+    w = WORKLOADS["decode"]
+    say(f"decode N={w.B} H={w.H} steps={w.steps}")
+    x = make_workload(w, device=DEV)
+    S = x["S0"].clone()
+    outs = []
+    for t in range(w.steps):
+        o, S = eda.recurrent_step(*(x[n][t] for n in ("q", "k", "e", "v", "alpha", "beta", "gamma")),
+                                  S, inplace=True)
+        outs.append(o)
+    torch.cuda.synchronize()
+    got = torch.stack(outs)  # [steps, N, H, dv]
+    rng = np.random.default_rng(1)
+    heads = sorted({(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(24)})
+    xc = {n: t.cpu() for n, t in x.items()}
+    go, gs, ro, rs = [], [], [], []
+    for n_, h in heads:
+        sel = {n: xc[n][:, n_:n_ + 1, h:h + 1] for n in ("q", "k", "e", "v", "alpha", "beta", "gamma")}
+        o_ref, S_ref = oracle.eda_ref_decode(**sel, S0=xc["S0"][n_:n_ + 1, h:h + 1])
+        go.append(to64(got[:, n_, h])); ro.append(o_ref[:, 0, 0])
+        gs.append(to64(S[n_, h])); rs.append(S_ref[0, 0])
+    check(np.concatenate(go), np.concatenate(gs), np.concatenate(ro), np.concatenate(rs), "bf16",
+          f"decode heads={len(heads)}")
