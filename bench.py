@@ -1,0 +1,257 @@
+"""Throughput of the Erase-then-Delta Attention (EDA) forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
+
+A step is one chunked forward (`eda_fwd_chunked`: intra-chunk factors, then
+the state pass) over one batch of synthetic inputs already resident in HBM.
+The default workload is the training shape B=4, H=16, T=2048,
+d_k=d_v=128, bf16 q/k/e/v, fp32 gates and state.  One JSON line is printed:
+tokens/s of the whole batch, the roofline of the dominant kernel (its
+average duration measured with HIP events on the launch stream), the fp64
+CPU oracle timed on the host on a bounded sample of the same workload, and a
+decode section (256 sequences x 32 heads, one token per step, state updated
+in place) with its own HBM roofline.
+
+Algorithmic work used for the rooflines (d_k = d_v = d, C tokens per chunk,
+L = 2C sub-steps; each token is an erase sub-step and a delta sub-step):
+  intra-chunk kernel, multiply-adds per chunk-head:
+      L^2 d (decayed Gram) + L^3/6 (triangular inverse) + L^2 d (W factor)
+      + C L d (query-key products)
+  state-pass kernel, multiply-adds per chunk-head:
+      L d^2 (W S) + L C d (value part of U) + C d^2 (query-state product)
+      + C L d (intra-chunk output) + L d^2 (state update)
+  compulsory HBM bytes per token-head: q, k, e, v and o in the storage type,
+  alpha fp32 per key channel, beta and gamma fp32; decode adds the fp32
+  state read and written once (2 d_k d_v 4 bytes).
+Peaks: MI355X dense bf16 matrix 2.5 PFLOP/s, fp32 matrix 157.3 TFLOP/s,
+HBM3E 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "EDA fwd tokens/sec (H=16,d=128, T=2K/32K) + % MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+def intra_macs_per_chunk_head(C: int, d: int) -> float:
+    L = 2 * C
+    return L * L * d + L ** 3 / 6.0 + L * L * d + C * L * d
+
+
+def state_macs_per_chunk_head(C: int, d: int) -> float:
+    L = 2 * C
+    return L * d * d + L * C * d + C * d * d + C * L * d + L * d * d
+
+
+def token_bytes(dk: int, dv: int, es: int) -> dict:
+    """Compulsory bytes per token-head, split by the kernel that moves them."""
+    intra = 3 * dk * es + dk * 4 + 2 * 4          # q, k, e, alpha, beta, gamma
+    state = dv * es + 4 + dv * es                 # v, beta (re-read), o
+    return dict(intra=intra, state=state, chunked=3 * dk * es + dv * es + dk * 4 + 8 + dv * es)
+
+
+def decode_bytes_per_head(dk: int, dv: int, es: int) -> int:
+    return 2 * dk * dv * 4 + (3 * dk + dv) * es + dk * 4 + 8 + dv * es
+
+
+# ---------------------------------------------------------------------------
+# timing helpers (events on the stream the library launches on)
+# ---------------------------------------------------------------------------
+def time_events(torch, fn, reps: int) -> float:
+    """Average milliseconds of `fn` over `reps` back-to-back calls, measured
+    with HIP events recorded on the current stream (the launch stream)."""
+    s = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(s)
+    for _ in range(reps):
+        fn()
+    end.record(s)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train", choices=["train", "long", "long_h16", "verylong"])
+    ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library default)")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the EDA forward is independent per (batch, head), "
+              "so more GPUs would each run this same kernel on their own share of heads; "
+              "run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import recurrent_memory_amd as eda
+    from eda_inputs import WORKLOADS, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (the EDA path has no CPU implementation)", file=sys.stderr)
+        return 1
+    eda.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = WORKLOADS[args.workload]
+    chunk = args.chunk or eda.DEFAULT_CHUNK
+    x = make_workload(w, device=dev)
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    es = 2 if w.dtype == "bf16" else 4
+    o = torch.empty((B, T, H, dv), dtype=x["q"].dtype, device=dev)
+    S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(eda.workspace_size(B, T, H, dk, dv, x["q"].dtype, chunk), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
+                        chunk=chunk, out=o, S_final=S_final, workspace=ws)
+
+    def prepare():
+        eda.fwd_chunked_prepare(x["q"], x["k"], x["e"], x["alpha"], x["beta"], x["gamma"], ws,
+                                dv=dv, chunk=chunk)
+
+    def finish():
+        eda.fwd_chunked_finish(x["v"], x["beta"], x["S0"], o, S_final, ws, dk=dk, chunk=chunk)
+
+    print(f"[bench] workload {w.name}: B={B} T={T} H={H} d_k={dk} d_v={dv} {w.dtype} chunk={chunk}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = B * T
+    value = tokens * args.steps / wall
+    print(f"[bench] {ms_per_step:.4f} ms/step, {value:.4g} tokens/s", file=sys.stderr, flush=True)
+
+    # per-kernel durations (each half launched alone, events on the launch stream)
+    prepare(); finish(); torch.cuda.synchronize()
+    ms_intra = time_events(torch, prepare, args.kernel_reps)
+    prepare(); torch.cuda.synchronize()
+    ms_state = time_events(torch, finish, args.kernel_reps)
+    d = dk  # d_k = d_v on every measured workload
+    NC = (T + chunk - 1) // chunk
+    n_ch = B * H * NC
+    tb = token_bytes(dk, dv, es)
+    peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    kern = {}
+    for name, ms, macs, byts in (
+            ("eda_chunk_intra", ms_intra, intra_macs_per_chunk_head(chunk, d) * n_ch,
+             tb["intra"] * B * T * H),
+            ("eda_chunk_state", ms_state, state_macs_per_chunk_head(chunk, d) * n_ch,
+             tb["state"] * B * T * H + (2 if x["S0"] is not None else 1) * B * H * dk * dv * 4)):
+        tflops = 2 * macs / (ms * 1e-3) / 1e12
+        gbs = byts / (ms * 1e-3) / 1e9
+        # the binding roofline at the algorithmic level is the one whose floor is larger
+        bound = "mfma" if 2 * macs / (peak_mm * 1e12) >= byts / (PEAK_HBM_GBS * 1e9) else "hbm"
+        kern[name] = dict(ms=round(ms, 5), flop=2 * macs, bytes=byts, tflops=round(tflops, 3),
+                          gbs=round(gbs, 2), bound=bound,
+                          frac_mfma=round(tflops / peak_mm, 5), frac_hbm=round(gbs / PEAK_HBM_GBS, 5))
+    dom = max(kern, key=lambda n: kern[n]["ms"])
+    kd = kern[dom]
+    if kd["bound"] == "mfma":
+        roof = dict(kernel=dom, bound="mfma", achieved=kd["tflops"], peak=peak_mm, unit="TFLOP/s",
+                    frac=kd["frac_mfma"], traffic=None)
+    else:
+        roof = dict(kernel=dom, bound="hbm", achieved=kd["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=kd["frac_hbm"], traffic=None)
+    total_flop = kern["eda_chunk_intra"]["flop"] + kern["eda_chunk_state"]["flop"]
+    path = dict(mfma_frac=round(total_flop / (ms_per_step * 1e-3) / 1e12 / peak_mm, 5),
+                hbm_frac=round(tb["chunked"] * B * T * H / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                canonical_flop_per_token_head=total_flop / (B * T * H),
+                compulsory_bytes_per_token_head=tb["chunked"])
+    print(f"[bench] kernels: {json.dumps(kern)}", file=sys.stderr, flush=True)
+
+    # decode: N sequences x H heads, one token per step, state in place
+    decode = None
+    if not args.no_decode:
+        wd = WORKLOADS["decode"]
+        xd = make_workload(wd, device=dev)
+        Sd = xd["S0"].clone()
+        od = torch.empty((wd.B, wd.H, wd.dv), dtype=xd["q"].dtype, device=dev)
+        nsteps = min(args.decode_steps, wd.steps)
+        per = [tuple(xd[n][t] for n in ("q", "k", "e", "v", "alpha", "beta", "gamma"))
+               for t in range(nsteps)]
+
+        def decode_run():
+            for t in range(nsteps):
+                eda.recurrent_step(*per[t], Sd, S_out=Sd, o=od)
+
+        decode_run(); torch.cuda.synchronize()
+        ms_run = time_events(torch, decode_run, 3)
+        ms_tok = ms_run / nsteps
+        dbytes = decode_bytes_per_head(wd.dk, wd.dv, 2 if wd.dtype == "bf16" else 4) * wd.B * wd.H
+        gbs = dbytes / (ms_tok * 1e-3) / 1e9
+        decode = dict(workload=f"decode: N={wd.B} H={wd.H} d_k=d_v={wd.dk} {wd.dtype}, "
+                               f"{nsteps} steps in place",
+                      value=round(wd.B / (ms_tok * 1e-3), 1), unit="tokens/s",
+                      ms_per_token_step=round(ms_tok, 5),
+                      roofline=dict(kernel="eda_decode_kernel", bound="hbm", achieved=round(gbs, 2),
+                                    peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 5),
+                                    traffic=None))
+        print(f"[bench] decode {ms_tok * 1e3:.2f} us/step, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+        del xd, per
+
+    # fp64 CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from eda_inputs import make_inputs
+        threads = min(oracle.default_threads(), 16)
+        Tc = min(T, 2048)
+        Bc = 1 if w.B * Tc * w.H > 4 * 2048 * 16 else w.B
+        xc = make_inputs(Bc, Tc, w.H, dk, dv, w.dtype, seed=w.seed, alpha_mu=w.alpha_mu,
+                         gamma_mu=w.gamma_mu, s0_std=w.s0_std)
+        t1 = time.perf_counter()
+        oracle.eda_ref_fwd(xc["q"], xc["k"], xc["e"], xc["v"], xc["alpha"], xc["beta"], xc["gamma"],
+                           xc["S0"], nthreads=threads)
+        dt = time.perf_counter() - t1
+        cpu = dict(value=round(Bc * Tc / dt, 2), unit="tokens/s", cores=threads, kind="oracle",
+                   sample=f"B={Bc} T={Tc} H={w.H} d_k=d_v={dk} (all heads), fp64 token recurrence, "
+                          f"{dt:.2f} s")
+        print(f"[bench] cpu oracle {cpu}", file=sys.stderr, flush=True)
+
+    line = dict(
+        metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(ms_per_step, 5), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype=w.dtype, data="synthetic",
+        config=dict(workload=f"{w.name}: EDA chunked forward B={B} T={T} H={H} d_k={dk} d_v={dv} "
+                             f"{w.dtype} inputs, fp32 gates and state, chunk={chunk}",
+                    B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, tokens_per_step=tokens,
+                    parallelism="single GPU"),
+        roofline=roof, cpu_baseline=cpu, kernels=kern, chunked_path=path, decode=decode)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
