@@ -2,11 +2,13 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
 
-A step is one chunked forward (`eda_fwd_chunked`: intra-chunk factors, then
-the state pass) over one batch of synthetic inputs already resident in HBM.
+A step is one chunked forward (`eda_fwd_chunked`; for bf16 inputs a single
+kernel that computes each chunk's factors on chip and carries the state
+through the chunks) over one batch of synthetic inputs already resident in
+HBM.
 The default workload is the training shape B=4, H=16, T=2048,
 d_k=d_v=128, bf16 q/k/e/v, fp32 gates and state.  One JSON line is printed:
-tokens/s of the whole batch, the roofline of the dominant kernel (its
+tokens/s of the whole batch, the roofline of the chunked kernel (its
 average duration measured with HIP events on the launch stream), the fp64
 CPU oracle timed on the host on a bounded sample of the same workload, and a
 decode section (256 sequences x 32 heads, one token per step, state updated
@@ -14,12 +16,13 @@ in place) with its own HBM roofline.
 
 Algorithmic work used for the rooflines (d_k = d_v = d, C tokens per chunk,
 L = 2C sub-steps; each token is an erase sub-step and a delta sub-step):
-  intra-chunk kernel, multiply-adds per chunk-head:
+  canonical chunk-form multiply-adds per chunk-head, state independent:
       L^2 d (decayed Gram) + L^3/6 (triangular inverse) + L^2 d (W factor)
       + C L d (query-key products)
-  state-pass kernel, multiply-adds per chunk-head:
+  and state dependent:
       L d^2 (W S) + L C d (value part of U) + C d^2 (query-state product)
       + C L d (intra-chunk output) + L d^2 (state update)
+  (counted once per chunk-head, however often the kernel recomputes them)
   compulsory HBM bytes per token-head: q, k, e, v and o in the storage type,
   alpha fp32 per key channel, beta and gamma fp32; decode adds the fp32
   state read and written once (2 d_k d_v 4 bytes).
@@ -91,7 +94,6 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train", choices=["train", "long", "long_h16", "verylong"])
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library default)")
-    ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -124,72 +126,61 @@ def main() -> int:
     es = 2 if w.dtype == "bf16" else 4
     o = torch.empty((B, T, H, dv), dtype=x["q"].dtype, device=dev)
     S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    ws = torch.empty(eda.workspace_size(B, T, H, dk, dv, x["q"].dtype, chunk), dtype=torch.uint8,
-                     device=dev)
+    need = eda.workspace_size(B, T, H, dk, dv, x["q"].dtype, chunk)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
 
     def step():
         eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
                         chunk=chunk, out=o, S_final=S_final, workspace=ws)
-
-    def prepare():
-        eda.fwd_chunked_prepare(x["q"], x["k"], x["e"], x["alpha"], x["beta"], x["gamma"], ws,
-                                dv=dv, chunk=chunk)
-
-    def finish():
-        eda.fwd_chunked_finish(x["v"], x["beta"], x["S0"], o, S_final, ws, dk=dk, chunk=chunk)
 
     print(f"[bench] workload {w.name}: B={B} T={T} H={H} d_k={dk} d_v={dv} {w.dtype} chunk={chunk}",
           file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # timed region: wall clock around K steps, and HIP events on the launch
+    # stream (bf16 runs one kernel per step, so event time / K is the average
+    # duration of that kernel)
+    s = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(s)
     for _ in range(args.steps):
         step()
+    ev1.record(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_kernel = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     tokens = B * T
     value = tokens * args.steps / wall
-    print(f"[bench] {ms_per_step:.4f} ms/step, {value:.4g} tokens/s", file=sys.stderr, flush=True)
+    print(f"[bench] {ms_per_step:.4f} ms/step (events {ms_kernel:.4f} ms), {value:.4g} tokens/s",
+          file=sys.stderr, flush=True)
 
-    # per-kernel durations (each half launched alone, events on the launch stream)
-    prepare(); finish(); torch.cuda.synchronize()
-    ms_intra = time_events(torch, prepare, args.kernel_reps)
-    prepare(); torch.cuda.synchronize()
-    ms_state = time_events(torch, finish, args.kernel_reps)
     d = dk  # d_k = d_v on every measured workload
     NC = (T + chunk - 1) // chunk
     n_ch = B * H * NC
     tb = token_bytes(dk, dv, es)
     peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    kern = {}
-    for name, ms, macs, byts in (
-            ("eda_chunk_intra", ms_intra, intra_macs_per_chunk_head(chunk, d) * n_ch,
-             tb["intra"] * B * T * H),
-            ("eda_chunk_state", ms_state, state_macs_per_chunk_head(chunk, d) * n_ch,
-             tb["state"] * B * T * H + (2 if x["S0"] is not None else 1) * B * H * dk * dv * 4)):
-        tflops = 2 * macs / (ms * 1e-3) / 1e12
-        gbs = byts / (ms * 1e-3) / 1e9
-        # the binding roofline at the algorithmic level is the one whose floor is larger
-        bound = "mfma" if 2 * macs / (peak_mm * 1e12) >= byts / (PEAK_HBM_GBS * 1e9) else "hbm"
-        kern[name] = dict(ms=round(ms, 5), flop=2 * macs, bytes=byts, tflops=round(tflops, 3),
-                          gbs=round(gbs, 2), bound=bound,
-                          frac_mfma=round(tflops / peak_mm, 5), frac_hbm=round(gbs / PEAK_HBM_GBS, 5))
-    dom = max(kern, key=lambda n: kern[n]["ms"])
-    kd = kern[dom]
-    if kd["bound"] == "mfma":
-        roof = dict(kernel=dom, bound="mfma", achieved=kd["tflops"], peak=peak_mm, unit="TFLOP/s",
-                    frac=kd["frac_mfma"], traffic=None)
+    flop = 2 * (intra_macs_per_chunk_head(chunk, d) + state_macs_per_chunk_head(chunk, d)) * n_ch
+    byts = tb["chunked"] * B * T * H + (2 if x["S0"] is not None else 1) * B * H * dk * dv * 4
+    tflops = flop / (ms_kernel * 1e-3) / 1e12
+    gbs = byts / (ms_kernel * 1e-3) / 1e9
+    # the binding roofline at the algorithmic level is the one with the larger floor
+    mfma_bound = flop / (peak_mm * 1e12) >= byts / (PEAK_HBM_GBS * 1e9)
+    kname = "eda_chunk_fused"
+    if mfma_bound:
+        roof = dict(kernel=kname, bound="mfma", achieved=round(tflops, 3), peak=peak_mm,
+                    unit="TFLOP/s", frac=round(tflops / peak_mm, 5), traffic=None)
     else:
-        roof = dict(kernel=dom, bound="hbm", achieved=kd["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=kd["frac_hbm"], traffic=None)
-    total_flop = kern["eda_chunk_intra"]["flop"] + kern["eda_chunk_state"]["flop"]
-    path = dict(mfma_frac=round(total_flop / (ms_per_step * 1e-3) / 1e12 / peak_mm, 5),
-                hbm_frac=round(tb["chunked"] * B * T * H / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
-                canonical_flop_per_token_head=total_flop / (B * T * H),
+        roof = dict(kernel=kname, bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS,
+                    unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 5), traffic=None)
+    path = dict(kernel_ms=round(ms_kernel, 5), canonical_flop=flop, compulsory_bytes=byts,
+                mfma_tflops=round(tflops, 3), mfma_frac=round(tflops / peak_mm, 5),
+                hbm_gbs=round(gbs, 2), hbm_frac=round(gbs / PEAK_HBM_GBS, 5),
+                canonical_flop_per_token_head=flop / (B * T * H),
                 compulsory_bytes_per_token_head=tb["chunked"])
-    print(f"[bench] kernels: {json.dumps(kern)}", file=sys.stderr, flush=True)
+    print(f"[bench] chunked path: {json.dumps(path)}", file=sys.stderr, flush=True)
 
     # decode: N sequences x H heads, one token per step, state in place
     decode = None
@@ -248,7 +239,7 @@ def main() -> int:
                              f"{w.dtype} inputs, fp32 gates and state, chunk={chunk}",
                     B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, tokens_per_step=tokens,
                     parallelism="single GPU"),
-        roofline=roof, cpu_baseline=cpu, kernels=kern, chunked_path=path, decode=decode)
+        roofline=roof, cpu_baseline=cpu, chunked_path=path, decode=decode)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -60,9 +60,13 @@ typedef enum { EDA_F32 = 0, EDA_BF16 = 1 } eda_dtype_t;
 const char *eda_status_string(eda_status_t s);
 
 /*
- * Bytes of device workspace eda_fwd_chunked needs for these sizes (0 for an
- * unsupported combination).  `chunk` is the number of tokens per chunk
- * (0 selects the default, 32).
+ * Bytes of device workspace eda_fwd_chunked needs for these sizes.  `chunk`
+ * is the number of tokens per chunk (0 selects the default, 32).  bf16 inputs
+ * need none (the whole chunk computation stays on chip): the result is 0, and
+ * the workspace arguments of eda_fwd_chunked are then ignored.  fp32 inputs
+ * stage each chunk's state-independent factors in the workspace.  The result
+ * is also 0 for an unsupported combination, which eda_fwd_chunked reports as
+ * EDA_ERR_UNSUPPORTED.
  */
 size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v,
                                       eda_dtype_t dtype, int chunk);
@@ -90,8 +94,9 @@ size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v,
  *   S_final : [B, H, d_k, d_v] fp32 final state, or NULL (not written);
  *             may be the same pointer as S0 (updated in place)
  *   workspace : device scratch of at least
- *             eda_fwd_chunked_workspace_size(...) bytes, 256-byte aligned;
- *             its contents on entry are ignored and on return undefined
+ *             eda_fwd_chunked_workspace_size(...) bytes, 256-byte aligned
+ *             (NULL allowed when that size is 0); its contents on entry are
+ *             ignored and on return undefined
  *
  * Supported: 1 <= d_k, d_v <= 128; chunk in {0, 16, 32}; B, T, H >= 1 with
  * B*T*H*max(d_k, d_v) < 2^31.  o may not overlap any input; S_final may
@@ -103,37 +108,6 @@ eda_status_t eda_fwd_chunked(const void *q, const void *k, const void *e, const 
                              int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
                              int chunk, void *workspace, size_t workspace_bytes,
                              void *stream);
-
-/*
- * The two halves of eda_fwd_chunked, for callers that want to schedule them
- * separately (for example, prepare the next batch's chunk factors while the
- * state pass of this one runs, or time the two phases).  Calling prepare and
- * then finish with the same sizes, dtype, chunk and workspace (on one stream,
- * or with the ordering made explicit) is exactly eda_fwd_chunked.
- *
- * eda_fwd_chunked_prepare: from q, k, e, alpha, beta, gamma alone, fills the
- *   workspace with every per-chunk factor that does not depend on the state
- *   (the decayed sub-step Gram's triangular inverse applied to the erase and
- *   write keys, the query products and the chunk's total decay).  Chunks are
- *   independent, so this phase is fully parallel.
- * eda_fwd_chunked_finish: carries the fp32 state through the chunks in order
- *   (serial over chunks, parallel over heads and value columns), reading v,
- *   beta and the prepared workspace, and writes o and S_final.
- *
- * Arguments, layouts and checks are those of eda_fwd_chunked; a phase
- * ignores the pointers it does not use.  The workspace contents between the
- * two calls are opaque and valid only for the same sizes, dtype and chunk.
- */
-eda_status_t eda_fwd_chunked_prepare(const void *q, const void *k, const void *e,
-                                     const float *alpha, const float *beta, const float *gamma,
-                                     int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
-                                     int chunk, void *workspace, size_t workspace_bytes,
-                                     void *stream);
-
-eda_status_t eda_fwd_chunked_finish(const void *v, const float *beta, const float *S0, void *o,
-                                    float *S_final, int B, int T, int H, int d_k, int d_v,
-                                    eda_dtype_t dtype, int chunk, const void *workspace,
-                                    size_t workspace_bytes, void *stream);
 
 /*
  * One token of the recurrence for N independent sequences (decode).

@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd_chunked", "fwd_chunked_prepare", "fwd_chunked_finish", "recurrent_step", "workspace_size", "library_path", "load_library",
+__all__ = ["fwd_chunked", "recurrent_step", "workspace_size", "library_path", "load_library",
            "EdaError", "STATUS", "DEFAULT_CHUNK"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,10 +63,6 @@ def load_library():
     lib.eda_fwd_chunked.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, vp, fp,
                                     i, i, i, i, i, i, i, vp, sz, vp]
     lib.eda_fwd_chunked.restype = i
-    lib.eda_fwd_chunked_prepare.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i, vp, sz, vp]
-    lib.eda_fwd_chunked_prepare.restype = i
-    lib.eda_fwd_chunked_finish.argtypes = [vp, fp, fp, vp, fp, i, i, i, i, i, i, i, vp, sz, vp]
-    lib.eda_fwd_chunked_finish.restype = i
     lib.eda_fwd_recurrent_step.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp, vp,
                                            i, i, i, i, i, vp]
     lib.eda_fwd_recurrent_step.restype = i
@@ -124,46 +120,17 @@ def fwd_chunked(q, k, e, v, alpha, beta, gamma, S0=None, *, chunk: int = 0,
     if S_final is None and want_state:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     need = int(lib.eda_fwd_chunked_workspace_size(B, T, H, dk, dv, dt, chunk))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     code = lib.eda_fwd_chunked(
         _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(e, "e", q.dtype), _ptr(v, "v", q.dtype),
         _ptr(alpha, "alpha", torch.float32), _ptr(beta, "beta", torch.float32),
         _ptr(gamma, "gamma", torch.float32), _ptr(S0, "S0", torch.float32),
         _ptr(out, "o", q.dtype), _ptr(S_final, "S_final", torch.float32),
-        B, T, H, dk, dv, dt, chunk, _ptr(workspace, "workspace"), workspace.numel(),
-        _stream(q.device))
+        B, T, H, dk, dv, dt, chunk, _ptr(workspace, "workspace"),
+        0 if workspace is None else workspace.numel(), _stream(q.device))
     _check("eda_fwd_chunked", code)
     return out, S_final
-
-
-def fwd_chunked_prepare(q, k, e, alpha, beta, gamma, workspace: torch.Tensor, *, dv: int,
-                        chunk: int = 0) -> None:
-    """First half of fwd_chunked: fill `workspace` with the per-chunk factors
-    that do not depend on the state (see eda_fwd_chunked_prepare)."""
-    lib = load_library()
-    B, T, H, dk = q.shape
-    dt = _dtype_code(q)
-    code = lib.eda_fwd_chunked_prepare(
-        _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(e, "e", q.dtype),
-        _ptr(alpha, "alpha", torch.float32), _ptr(beta, "beta", torch.float32),
-        _ptr(gamma, "gamma", torch.float32), B, T, H, dk, dv, dt, chunk,
-        _ptr(workspace, "workspace"), workspace.numel(), _stream(q.device))
-    _check("eda_fwd_chunked_prepare", code)
-
-
-def fwd_chunked_finish(v, beta, S0, out: torch.Tensor, S_final: Optional[torch.Tensor],
-                       workspace: torch.Tensor, *, dk: int, chunk: int = 0) -> None:
-    """Second half of fwd_chunked: the state pass over a workspace filled by
-    fwd_chunked_prepare with the same sizes; writes `out` and `S_final`."""
-    lib = load_library()
-    B, T, H, dv = v.shape
-    dt = _dtype_code(v)
-    code = lib.eda_fwd_chunked_finish(
-        _ptr(v, "v", v.dtype), _ptr(beta, "beta", torch.float32), _ptr(S0, "S0", torch.float32),
-        _ptr(out, "o", v.dtype), _ptr(S_final, "S_final", torch.float32), B, T, H, dk, dv, dt,
-        chunk, _ptr(workspace, "workspace"), workspace.numel(), _stream(v.device))
-    _check("eda_fwd_chunked_finish", code)
 
 
 def recurrent_step(q, k, e, v, alpha, beta, gamma, S_in=None, *, S_out: Optional[torch.Tensor] = None,

@@ -16,6 +16,9 @@ template <typename T>
 hipError_t launch_chunked(int, const void *, const void *, const void *, const void *,
                           const float *, const float *, const float *, const float *, void *,
                           float *, int, int, int, int, int, int, void *, hipStream_t);
+hipError_t launch_fused(const void *, const void *, const void *, const void *, const float *,
+                        const float *, const float *, const float *, void *, float *, int, int,
+                        int, int, int, int, hipStream_t);
 }  // namespace eda
 
 namespace {
@@ -80,36 +83,23 @@ size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v, eda
     if (!dtype_ok(dtype) || !dims_ok(B, T, H, d_k, d_v) || !head_dims_supported(d_k, d_v) ||
         !chunk_supported(chunk))
         return 0;
-    return dtype == EDA_BF16 ? eda::chunked_ws_t<eda::bf16>(B, T, H, d_k, d_v, chunk)
-                             : eda::chunked_ws_t<float>(B, T, H, d_k, d_v, chunk);
+    // bf16: the single-pass kernel keeps every intermediate on chip
+    return dtype == EDA_BF16 ? 0 : eda::chunked_ws_t<float>(B, T, H, d_k, d_v, chunk);
 }
 
 }  // extern "C"
 
 namespace {
 
-// Shared checks and launch for the chunked family.  phase 1 = prepare
-// (needs q, k, e, alpha, beta, gamma), 2 = finish (needs v, beta, o),
-// 3 = both.  Pointers a phase does not use may be NULL and are ignored.
-eda_status_t chunked_call(int phase, const void *q, const void *k, const void *e, const void *v,
+// Checks, then the launch.  bf16 runs the single-pass kernel (no workspace);
+// fp32 runs the two-kernel form (chunk factors to the workspace, then the
+// state pass).
+eda_status_t chunked_call(const void *q, const void *k, const void *e, const void *v,
                           const float *alpha, const float *beta, const float *gamma,
                           const float *S0, void *o, float *S_final, int B, int T, int H, int d_k,
                           int d_v, eda_dtype_t dtype, int chunk, void *workspace,
                           size_t workspace_bytes, void *stream) {
-    if (phase & 1) {
-        if (!q || !k || !e || !alpha || !beta || !gamma) return EDA_ERR_NULL;
-    } else {
-        q = k = e = nullptr;
-        alpha = gamma = nullptr;
-    }
-    if (phase & 2) {
-        if (!v || !beta || !o) return EDA_ERR_NULL;
-    } else {
-        v = nullptr;
-        S0 = nullptr;
-        o = nullptr;
-        S_final = nullptr;
-    }
+    if (!q || !k || !e || !v || !alpha || !beta || !gamma || !o) return EDA_ERR_NULL;
     if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
     if (!dims_ok(B, T, H, d_k, d_v)) return EDA_ERR_SHAPE;
     chunk = resolve_chunk(chunk);
@@ -119,17 +109,18 @@ eda_status_t chunked_call(int phase, const void *q, const void *k, const void *e
     const size_t es = elem_size(dtype);
     const void *elem_ptrs[] = {q, k, e, v};
     for (const void *p : elem_ptrs)
-        if (p && !aligned(p, es)) return EDA_ERR_ALIGN;
+        if (!aligned(p, es)) return EDA_ERR_ALIGN;
     const void *f32_ptrs[] = {alpha, beta, gamma};
     for (const void *p : f32_ptrs)
-        if (p && !aligned(p, 4)) return EDA_ERR_ALIGN;
+        if (!aligned(p, 4)) return EDA_ERR_ALIGN;
     const void *vec_ptrs[] = {S0, o, S_final};
     for (const void *p : vec_ptrs)
         if (p && !aligned(p, 16)) return EDA_ERR_ALIGN;
     const size_t need = eda_fwd_chunked_workspace_size(B, T, H, d_k, d_v, dtype, chunk);
-    if (need == 0) return EDA_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < need) return EDA_ERR_WORKSPACE;
-    if (((uintptr_t)workspace & 255u) != 0) return EDA_ERR_ALIGN;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return EDA_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return EDA_ERR_ALIGN;
+    }
 
     const size_t btH = (size_t)B * T * H;
     const Range in[] = {range_of(q, btH * d_k * es), range_of(k, btH * d_k * es),
@@ -139,7 +130,7 @@ eda_status_t chunked_call(int phase, const void *q, const void *k, const void *e
     const Range rS0 = range_of(S0, (size_t)B * H * d_k * d_v * 4);
     const Range rSf = range_of(S_final, (size_t)B * H * d_k * d_v * 4);
     const Range rO = range_of(o, btH * d_v * es);
-    const Range rW = range_of(workspace, need);
+    const Range rW = range_of(need > 0 ? workspace : nullptr, need);
     for (const Range &r : in) {
         if (overlap(rO, r) || overlap(rSf, r) || overlap(rW, r)) return EDA_ERR_ALIAS;
     }
@@ -149,10 +140,9 @@ eda_status_t chunked_call(int phase, const void *q, const void *k, const void *e
 
     hipError_t err =
         dtype == EDA_BF16
-            ? eda::launch_chunked<eda::bf16>(phase, q, k, e, v, alpha, beta, gamma, S0, o, S_final,
-                                             B, T, H, d_k, d_v, chunk, workspace,
-                                             (hipStream_t)stream)
-            : eda::launch_chunked<float>(phase, q, k, e, v, alpha, beta, gamma, S0, o, S_final, B,
+            ? eda::launch_fused(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v,
+                                chunk, (hipStream_t)stream)
+            : eda::launch_chunked<float>(3, q, k, e, v, alpha, beta, gamma, S0, o, S_final, B,
                                          T, H, d_k, d_v, chunk, workspace, (hipStream_t)stream);
     return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
 }
@@ -166,26 +156,8 @@ eda_status_t eda_fwd_chunked(const void *q, const void *k, const void *e, const 
                              const float *S0, void *o, float *S_final, int B, int T, int H,
                              int d_k, int d_v, eda_dtype_t dtype, int chunk, void *workspace,
                              size_t workspace_bytes, void *stream) {
-    return chunked_call(3, q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v,
-                        dtype, chunk, workspace, workspace_bytes, stream);
-}
-
-eda_status_t eda_fwd_chunked_prepare(const void *q, const void *k, const void *e,
-                                     const float *alpha, const float *beta, const float *gamma,
-                                     int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
-                                     int chunk, void *workspace, size_t workspace_bytes,
-                                     void *stream) {
-    return chunked_call(1, q, k, e, nullptr, alpha, beta, gamma, nullptr, nullptr, nullptr, B, T,
-                        H, d_k, d_v, dtype, chunk, workspace, workspace_bytes, stream);
-}
-
-eda_status_t eda_fwd_chunked_finish(const void *v, const float *beta, const float *S0, void *o,
-                                    float *S_final, int B, int T, int H, int d_k, int d_v,
-                                    eda_dtype_t dtype, int chunk, const void *workspace,
-                                    size_t workspace_bytes, void *stream) {
-    return chunked_call(2, nullptr, nullptr, nullptr, v, nullptr, beta, nullptr, S0, o, S_final,
-                        B, T, H, d_k, d_v, dtype, chunk, const_cast<void *>(workspace),
-                        workspace_bytes, stream);
+    return chunked_call(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v, dtype,
+                        chunk, workspace, workspace_bytes, stream);
 }
 
 eda_status_t eda_fwd_recurrent_step(const void *q, const void *k, const void *e, const void *v,

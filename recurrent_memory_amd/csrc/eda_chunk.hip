@@ -1,5 +1,8 @@
-// eda_chunk.hip -- chunk-parallel EDA forward (prefill): intra-chunk kernel
-// and inter-chunk state-pass kernel.
+// eda_chunk.hip -- chunk-parallel EDA forward (prefill) in two kernels: an
+// intra-chunk kernel writes each chunk's state-independent factors to a
+// workspace, then a state-pass kernel carries the state through the chunks.
+// This is the fp32-input path (fp32 matrix-core products throughout); bf16
+// inputs take the single-pass kernel in eda_fused.hip.
 //
 // Sub-step form.  Each token t becomes two rank-1 sub-steps of the gated
 // delta recurrence S_j = (I - b'_j kap_j kap_j^T) D_j S_{j-1} + b'_j kap_j nu_j^T
@@ -566,12 +569,7 @@ hipError_t launch_chunked(int phase, const void *q, const void *k, const void *e
     return hipErrorInvalidValue;
 }
 
-template size_t chunked_ws_t<bf16>(int, int, int, int, int, int);
 template size_t chunked_ws_t<float>(int, int, int, int, int, int);
-template hipError_t launch_chunked<bf16>(int, const void *, const void *, const void *,
-                                         const void *, const float *, const float *, const float *,
-                                         const float *, void *, float *, int, int, int, int, int,
-                                         int, void *, hipStream_t);
 template hipError_t launch_chunked<float>(int, const void *, const void *, const void *,
                                           const void *, const float *, const float *, const float *,
                                           const float *, void *, float *, int, int, int, int, int,

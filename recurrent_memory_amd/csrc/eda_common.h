@@ -24,19 +24,29 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
+// Two fp32 -> two bf16 packed in 32 bits (round to nearest even; gfx950 has a
+// single instruction for it), low half = a.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2 r = __builtin_convertvector((f32x2{a, b}), bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(((uint32_t)x) << 16); }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                                         // nearest even
-    return (bf16)(u >> 16);
+    return (bf16)(__builtin_bit_cast(uint16_t, (__bf16)x));  // round to nearest even
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+
 
 // ---------------------------------------------------------------------------
 // Matrix-core traits.  KB = k consumed per instruction, KPL = k per lane.
@@ -119,12 +129,7 @@ __device__ __forceinline__ f32x4 tile_nt_dyn(const T *X, int ldx, const T *Y, in
 // Store 4 consecutive values (one accumulator's column run) as T.
 template <typename T> __device__ __forceinline__ void store4(T *p, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, float a, float b, float c, float d) {
-    s16x4 v;
-    v[0] = (short)from_f32<bf16>(a);
-    v[1] = (short)from_f32<bf16>(b);
-    v[2] = (short)from_f32<bf16>(c);
-    v[3] = (short)from_f32<bf16>(d);
-    *reinterpret_cast<s16x4 *>(p) = v;
+    *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16(a, b), pack_bf16(c, d));
 }
 template <> __device__ __forceinline__ void store4<float>(float *p, float a, float b, float c, float d) {
     *reinterpret_cast<f32x4 *>(p) = f32x4{a, b, c, d};

@@ -48,16 +48,16 @@ def test_status_strings():
 def test_workspace_size():
     lib = eda.load_library()
     ws = lib.eda_fwd_chunked_workspace_size
-    big = ws(4, 2048, 16, 128, 128, 1, 32)
+    assert ws(4, 2048, 16, 128, 128, 1, 32) == 0              # bf16: everything stays on chip
+    big = ws(4, 2048, 16, 128, 128, 0, 32)                    # fp32: staged chunk factors
     assert big > 0
-    assert ws(4, 2048, 16, 128, 128, 1, 0) == big            # 0 selects the default chunk
-    assert ws(4, 4096, 16, 128, 128, 1, 32) == 2 * big        # linear in the chunk count
-    assert ws(4, 2048, 16, 128, 128, 0, 32) > big             # fp32 factors are larger
+    assert ws(4, 2048, 16, 128, 128, 0, 0) == big            # 0 selects the default chunk
+    assert ws(4, 4096, 16, 128, 128, 0, 32) == 2 * big        # linear in the chunk count
     assert ws(1, 1, 1, 2, 1, 0, 16) > 0
-    assert ws(4, 2048, 16, 129, 128, 1, 32) == 0              # unsupported head dim
-    assert ws(4, 2048, 16, 128, 128, 1, 48) == 0              # unsupported chunk
+    assert ws(4, 2048, 16, 129, 128, 0, 32) == 0              # unsupported head dim
+    assert ws(4, 2048, 16, 128, 128, 0, 48) == 0              # unsupported chunk
     assert ws(4, 2048, 16, 128, 128, 7, 32) == 0              # bad dtype
-    assert ws(0, 2048, 16, 128, 128, 1, 32) == 0
+    assert ws(0, 2048, 16, 128, 128, 0, 32) == 0
 
 
 # Fake device addresses: distinct, 256-byte aligned, far apart, never dereferenced.
@@ -69,7 +69,9 @@ def fake(i, off=0):
 
 
 def chunked_args(**kw):
-    B, T, H, dk, dv, dt, chunk = 2, 64, 2, 64, 64, 1, 32
+    # fp32 (dt=0): the path that needs a workspace, so every rejection below is
+    # decided by a check before any launch
+    B, T, H, dk, dv, dt, chunk = 2, 64, 2, 64, 64, 0, 32
     a = dict(q=fake(1), k=fake(2), e=fake(3), v=fake(4), alpha=fake(5), beta=fake(6),
              gamma=fake(7), S0=fake(8), o=fake(9), S_final=fake(10), B=B, T=T, H=H, dk=dk, dv=dv,
              dt=dt, chunk=chunk, ws=fake(11), wsb=1 << 30, stream=None)
@@ -89,7 +91,7 @@ def call_chunked(a):
     ("dt", 5, 3),
     ("B", 0, 2), ("T", -1, 2), ("dk", 0, 2),
     ("dk", 129, 5), ("dv", 200, 5), ("chunk", 64, 5), ("chunk", 7, 5),
-    ("q", fake(1, 1), 4), ("alpha", fake(5, 2), 4), ("S0", fake(8, 4), 4), ("o", fake(9, 8), 4),
+    ("q", fake(1, 2), 4), ("alpha", fake(5, 2), 4), ("S0", fake(8, 4), 4), ("o", fake(9, 8), 4),
     ("ws", fake(11, 128), 4),
     ("ws", None, 6), ("wsb", 1024, 6),
     ("o", fake(1, 256), 7),           # o inside q
@@ -103,7 +105,11 @@ def test_chunked_rejects(field, val, code):
 def test_scalar_inputs_need_only_element_alignment():
     # per-token gates sliced out of a stacked tensor sit at 4-byte offsets
     assert call_chunked(chunked_args(beta=fake(6, 4), gamma=fake(7, 12), alpha=fake(5, 4),
-                                     q=fake(1, 2), dt=1, wsb=16)) == 6  # reaches the workspace check
+                                     q=fake(1, 4), wsb=16)) == 6  # reaches the workspace check
+
+
+def test_bf16_misaligned_input_rejected():
+    assert call_chunked(chunked_args(q=fake(1, 1), dt=1)) == 4
 
 
 def test_chunked_too_large_shape():
