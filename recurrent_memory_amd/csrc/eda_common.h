@@ -126,6 +126,33 @@ __device__ __forceinline__ f32x4 tile_nt_dyn(const T *X, int ldx, const T *Y, in
     return acc;
 }
 
+// acc += A B^T for the wave's 16x16 tile where A is stored TRANSPOSED:
+// A[m][k] = M[k][m] with M row-major (k rows, m contiguous).  M points at
+// M[k0][m0], Y at Y[n0][k0] (k contiguous).  The gfx950 transposing LDS read
+// gives, within each group of 16 lanes where lane i addresses row i/4 and
+// columns 4(i%4)..4(i%4)+3 of a 4x16 block, lane n the 4 values of column n
+// -- i.e. the A operand of the matrix instruction for 4 consecutive k.
+// M must be in LDS.
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+template <int K>
+__device__ __forceinline__ f32x4 tile_tn_bf16(const uint16_t *M, int ldm, const uint16_t *Y, int ldy,
+                                              f32x4 acc, int lane) {
+    static_assert(K % 32 == 0, "tile depth must be a multiple of 32");
+    const int g = lane >> 4, i = lane & 15, n = lane & 15;
+    const uint16_t *mp = M + (8 * g + (i >> 2)) * ldm + 4 * (i & 3);
+    const uint16_t *yp = Y + n * ldy + 8 * g;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(mp + k0 * ldm));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(mp + (k0 + 4) * ldm));
+        typedef __attribute__((ext_vector_type(8))) short s16x8;
+        const s16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8),
+                                                      *reinterpret_cast<const bf16x8 *>(yp + k0), acc, 0, 0, 0);
+    }
+    return acc;
+}
+
 // Store 4 consecutive values (one accumulator's column run) as T.
 template <typename T> __device__ __forceinline__ void store4(T *p, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, float a, float b, float c, float d) {

@@ -42,6 +42,8 @@
 //
 // The workgroups of one head's slices get ids congruent mod 8, so they are
 // dispatched to the same XCD and read the head's inputs through one L2.
+#include <type_traits>
+
 #include "eda_common.h"
 
 namespace eda {
@@ -74,6 +76,17 @@ __device__ __forceinline__ float scan_group(float x, int seg) {
     return x;
 }
 
+// Value of the last lane of each group of N consecutive lanes.
+template <int N>
+__device__ __forceinline__ float group_last(float x) {
+    if constexpr (N == 16) {
+        // ds_swizzle bit mode: lane' = (lane & 0x10) | 0xF within each 32 lanes
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F0));
+    } else {
+        return __shfl(x, N - 1, N);
+    }
+}
+
 __host__ __device__ constexpr int imax(int a, int b) { return a > b ? a : b; }
 __host__ __device__ constexpr int imin(int a, int b) { return a < b ? a : b; }
 __host__ __device__ constexpr int align16(int x) { return (x + 15) / 16 * 16; }
@@ -81,7 +94,7 @@ __host__ __device__ constexpr int align16(int x) { return (x + 15) / 16 * 16; }
 template <int C, int D, int BV, int NW>
 struct FusedGeom {
     static constexpr int L = 2 * C, NB = L / 16, NT = 64 * NW;
-    static constexpr int LDA = D + 8, LDL = L + 8, ZW = 16 + 8;  // +16 bytes per row
+    static constexpr int LDA = D + 8, LDL = L + 8;  // +16 bytes per row
     // element-wise role: 4 consecutive key channels x a run of TPT tokens
     static constexpr int NQ = D / 4;
     static constexpr int TPC = imin(NT / NQ, C);       // threads per channel quad
@@ -94,19 +107,27 @@ struct FusedGeom {
     static constexpr int YPW = (NYT + NW - 1) / NW;
     // LDS layout (bytes)
     static constexpr int szKl = align16(L * LDA * 2), szQl = align16(C * LDA * 2);
-    static constexpr int szKrT = align16(D * LDL * 2), szP = align16(C * LDL * 2);
-    static constexpr int szAbf = align16(L * LDL * 2), szAd = NB * 16 * 17 * 4;
-    static constexpr int szMI = align16(L * LDL * 2), szZd = align16(NB * 16 * ZW * 2);
-    static constexpr int szGs = C * D * 4;             // element-wise path only, aliases MI..Zd
-    static constexpr int szInv = imax(2 * szMI + szZd, szGs);
+    static constexpr int szP = align16(C * LDL * 2);
+    static constexpr int ADS = 20;                     // Ad row stride (floats): conflict-free writes, 16-byte rows
+    static constexpr int szAbf = align16(L * LDL * 2), szAd = NB * 16 * ADS * 4;
+    static constexpr int szMI = align16(L * LDL * 2);
+    static constexpr int szGs = C * D * 4;             // element-wise path only, aliases MI, MT
+    static constexpr int szInv = imax(2 * szMI, szGs);
     static constexpr int szSt = align16(BV * LDA * 2), szVs = align16(C * BV * 2);
     static constexpr int szZt = align16(BV * LDL * 2);
+    static constexpr int LDO = BV + 8, szOs = align16(C * LDO * 2);   // output staging
     static constexpr int szMisc = (L + 2 * C + 4 * D) * 4;
-    static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oQraw = oQl + szQl;
-    static constexpr int oKrT = oQraw + szQl, oP = oKrT + szKrT, oAbf = oP + szP;
+    // staging of one chunk's raw inputs (written late in the previous chunk)
+    static constexpr int ASD = D + 8;                  // alpha staging row stride (floats)
+    static constexpr int szQs = align16(C * LDA * 2), szAs = align16(C * ASD * 4);
+    static constexpr int LPR = D / 8, RPP = NT / LPR, PQ = (C + RPP - 1) / RPP;   // 16-byte loads of bf16 rows
+    static constexpr int LPA = D / 4, RPA = NT / LPA, PA = (C + RPA - 1) / RPA;   // 16-byte loads of alpha rows
+    static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oQs = oQl + szQl;
+    static constexpr int oKs = oQs + szQs, oEs = oKs + szQs, oAs = oEs + szQs;
+    static constexpr int oP = oAs + szAs, oAbf = oP + szP;
     static constexpr int oAd = oAbf + szAbf, oInv = oAd + szAd, oSt = oInv + szInv;
     static constexpr int oVs = oSt + szSt, oZt = oVs + szVs, oUt = oZt + szZt;
-    static constexpr int oMisc = oUt + szZt;
+    static constexpr int oOs = oUt + szZt, oMisc = oOs + szOs;
     static constexpr int LDS = oMisc + szMisc;
     static_assert(LDS <= 160 * 1024, "LDS budget exceeded");
 };
@@ -120,27 +141,31 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
                 int dk, int dv, int NC, int R, int vec) {
     using G = FusedGeom<C, D, BV, NW>;
     using T = bf16;
-    constexpr int L = G::L, NB = G::NB, NT = G::NT, LDA = G::LDA, LDL = G::LDL, ZW = G::ZW;
+    constexpr int L = G::L, NB = G::NB, NT = G::NT, LDA = G::LDA, LDL = G::LDL;
     constexpr int TPC = G::TPC, TPT = G::TPT, VPT = G::VPT, NYT = G::NYT, YPW = G::YPW;
+    constexpr int ADS = G::ADS, ASD = G::ASD;
+    constexpr int LPR = G::LPR, RPP = G::RPP, PQ = G::PQ, LPA = G::LPA, RPA = G::RPA, PA = G::PA;
     constexpr int NST = (D / 16) * (BV / 16);          // state tiles
     constexpr int SPW = (NST + NW - 1) / NW;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Kl = (T *)(smem + G::oKl);       // kap o exp(G - r)                 [L][LDA]
-    T *Kr = (T *)(smem + G::oKr);       // kap o exp(r - G); raw kap (wide) [L][LDA]
+    T *Kr = (T *)(smem + G::oKr);       // kap o exp(r - G); wide: raw kap, then Khat [L][LDA]
     T *Ql = (T *)(smem + G::oQl);       // q o exp(G - r)                   [C][LDA]
-    T *Qraw = (T *)(smem + G::oQraw);   // raw q (wide)                     [C][LDA]
-    T *KrT = (T *)(smem + G::oKrT);     // Kr^T (wide: Khat^T)              [D][LDL]
+    T *Qs = (T *)(smem + G::oQs);       // raw q, k, e of the chunk          [C][LDA]
+    T *Ks = (T *)(smem + G::oKs);
+    T *Es = (T *)(smem + G::oEs);
+    float *As = (float *)(smem + G::oAs);  // raw alpha of the chunk        [C][ASD]
     T *Pm = (T *)(smem + G::oP);        // P, causal                        [C][LDL]
     T *Abf = (T *)(smem + G::oAbf);     // A, off-diagonal 16-blocks        [L][LDL]
-    float *Ad = (float *)(smem + G::oAd);  // A, diagonal 16-blocks (fp32)  [NB][16][17]
+    float *Ad = (float *)(smem + G::oAd);  // A, diagonal 16-blocks (fp32)  [NB][16][ADS]
     T *MI = (T *)(smem + G::oInv);      // (I + A)^{-1}                     [L][LDL]
-    T *MT = MI + L * LDL;               // its transpose                    [L][LDL]
-    T *Zd = MT + L * LDL;               // column-sweep scratch per wave    [NB][16][ZW]
+    T *MT = MI + L * LDL;               // its transpose (diagonal blocks)  [L][LDL]
     float *Gs = (float *)(smem + G::oInv);  // G (wide)                     [C][D]
     T *St = (T *)(smem + G::oSt);       // S'^T (bf16 operand)              [BV][LDA]
     T *Vs = (T *)(smem + G::oVs);       // values of the slice              [C][BV]
     T *Zt = (T *)(smem + G::oZt);       // Z^T (bf16)                       [BV][LDL]
     T *Ut = (T *)(smem + G::oUt);       // U^T (bf16)                       [BV][LDL]
+    T *Os = (T *)(smem + G::oOs);       // previous chunk's outputs          [C][LDO]
     float *bp = (float *)(smem + G::oMisc);   // b' per sub-step            [L]
     float *sb = bp + L, *sg = sb + C;         // beta, gamma per token      [C]
     float *glc = sg + C;                      // G_C per channel (log2)     [D]
@@ -161,56 +186,116 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
     const bf16 *vh = v + hrow * dv + n0;
     const int HK = H * dk, HV = H * dv;
 
-    // ---- prefetch registers for one chunk ----------------------------------------
-    uint2 pq[TPT], pk[TPT], pe[TPT];
-    f32x4 pa[TPT];
+    // ---- prefetch of one chunk: whole-row 16-byte loads into registers, ---------------
+    // ---- written to the LDS staging buffers later (stage_chunk) ----------------------
+    uint4 rq[PQ], rk[PQ], re[PQ];
+    f32x4 ra[PA];
     bf16 pv[VPT];
     float pb = 0.f, pg = 0.f;
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {  // threads without an element-wise role keep these
-        pq[i] = pk[i] = pe[i] = make_uint2(0, 0);
-        pa[i] = f32x4{1.f, 1.f, 1.f, 1.f};
-    }
     auto load_chunk = [&](int cidx, int tid) {
         const int t0 = cidx * C, nval = min(C, Tlen - t0);
-        const int qd = tid / TPC, seg = tid % TPC, c0 = 4 * qd;
-        if (tid < G::ACT) {
+        if (vec && nval == C) {
+            // whole chunk, d_k == D, aligned rows: no masking
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) {
-                const int tau = seg * TPT + i;
-                const int off = (t0 + tau) * HK + c0;
-                if (vec) {
-                    const bool ok = tau < nval && c0 < dk;
-                    pq[i] = ok ? *(const uint2 *)(qh + off) : make_uint2(0, 0);
-                    pk[i] = ok ? *(const uint2 *)(kh + off) : make_uint2(0, 0);
-                    pe[i] = ok ? *(const uint2 *)(eh + off) : make_uint2(0, 0);
-                    pa[i] = ok ? *(const f32x4 *)(ah + off) : f32x4{1.f, 1.f, 1.f, 1.f};
-                } else {
-                    uint32_t xq[4], xk[4], xe[4];
+            for (int p = 0; p < PQ; ++p) {
+                const int r = tid / LPR + RPP * p, blk = tid % LPR;
+                if (RPP * PQ == C || r < C) {
+                    const int off = (t0 + r) * HK + 8 * blk;
+                    rq[p] = *(const uint4 *)(qh + off);
+                    rk[p] = *(const uint4 *)(kh + off);
+                    re[p] = *(const uint4 *)(eh + off);
+                }
+            }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const bool ok = tau < nval && c0 + j < dk;
-                        xq[j] = ok ? qh[off + j] : 0u;
-                        xk[j] = ok ? kh[off + j] : 0u;
-                        xe[j] = ok ? eh[off + j] : 0u;
-                        pa[i][j] = ok ? ah[off + j] : 1.f;
-                    }
-                    pq[i] = make_uint2(xq[0] | (xq[1] << 16), xq[2] | (xq[3] << 16));
-                    pk[i] = make_uint2(xk[0] | (xk[1] << 16), xk[2] | (xk[3] << 16));
-                    pe[i] = make_uint2(xe[0] | (xe[1] << 16), xe[2] | (xe[3] << 16));
+            for (int p = 0; p < PA; ++p) {
+                const int r = tid / LPA + RPA * p, blk = tid % LPA;
+                if (RPA * PA == C || r < C) ra[p] = *(const f32x4 *)(ah + (t0 + r) * HK + 4 * blk);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < PQ; ++p) {
+                const int r = tid / LPR + RPP * p, c8 = 8 * (tid % LPR);
+                uint32_t xq[8], xk[8], xe[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const bool ok = r < nval && c8 + j < dk;
+                    const int off = (t0 + r) * HK + c8 + j;
+                    xq[j] = ok ? qh[off] : 0u;
+                    xk[j] = ok ? kh[off] : 0u;
+                    xe[j] = ok ? eh[off] : 0u;
+                }
+                rq[p] = make_uint4(xq[0] | (xq[1] << 16), xq[2] | (xq[3] << 16), xq[4] | (xq[5] << 16), xq[6] | (xq[7] << 16));
+                rk[p] = make_uint4(xk[0] | (xk[1] << 16), xk[2] | (xk[3] << 16), xk[4] | (xk[5] << 16), xk[6] | (xk[7] << 16));
+                re[p] = make_uint4(xe[0] | (xe[1] << 16), xe[2] | (xe[3] << 16), xe[4] | (xe[5] << 16), xe[6] | (xe[7] << 16));
+            }
+#pragma unroll
+            for (int p = 0; p < PA; ++p) {
+                const int r = tid / LPA + RPA * p, c4 = 4 * (tid % LPA);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = r < nval && c4 + j < dk;
+                    ra[p][j] = ok ? ah[(t0 + r) * HK + c4 + j] : 1.f;
                 }
             }
         }
+        if (nval == C && n0 + BV <= dv && C * BV == NT * VPT) {
 #pragma unroll
-        for (int m = 0; m < VPT; ++m) {
-            const int idx = tid + NT * m, tau = idx / BV, n = idx % BV;
-            const bool ok = idx < C * BV && tau < nval && n0 + n < dv;
-            pv[m] = ok ? vh[(t0 + tau) * HV + n] : (bf16)0;
+            for (int m = 0; m < VPT; ++m) {
+                const int idx = tid + NT * m;
+                pv[m] = vh[(t0 + idx / BV) * HV + idx % BV];
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < VPT; ++m) {
+                const int idx = tid + NT * m, tau = idx / BV, n = idx % BV;
+                const bool ok = idx < C * BV && tau < nval && n0 + n < dv;
+                pv[m] = ok ? vh[(t0 + tau) * HV + n] : (bf16)0;
+            }
         }
         if (tid < C) {
             const bool ok = tid < nval;
             pb = ok ? bh_[(t0 + tid) * H] : 0.f;
             pg = ok ? gh[(t0 + tid) * H] : 0.f;
+        }
+    };
+    auto stage_chunk = [&](int tid) {
+#pragma unroll
+        for (int p = 0; p < PQ; ++p) {
+            const int r = tid / LPR + RPP * p, blk = tid % LPR;
+            if (RPP * PQ == C || r < C) {
+                *(uint4 *)(Qs + r * LDA + 8 * blk) = rq[p];
+                *(uint4 *)(Ks + r * LDA + 8 * blk) = rk[p];
+                *(uint4 *)(Es + r * LDA + 8 * blk) = re[p];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PA; ++p) {
+            const int r = tid / LPA + RPA * p, blk = tid % LPA;
+            if (RPA * PA == C || r < C) *(f32x4 *)(As + r * ASD + 4 * blk) = ra[p];
+        }
+    };
+
+    // ---- outputs: staged in LDS, written one chunk later ----------------------------
+    // Loads and stores share one completion counter, so a wait for the next
+    // chunk's inputs would also wait for stores issued just before it; writing
+    // a chunk's outputs right before the following prefetch keeps every wait
+    // on operations issued a whole chunk earlier.
+    constexpr int LDO = G::LDO;
+    auto flush_outputs = [&](int cprev, int tid) {
+        const int tp0 = cprev * C, nv = min(C, Tlen - tp0);
+        for (int idx = tid; idx < C * (BV / 4); idx += NT) {
+            const int tau = idx / (BV / 4), n = 4 * (idx % (BV / 4));
+            if (tau >= nv) continue;
+            const uint2 val = *(const uint2 *)(Os + tau * LDO + n);
+            T *op = o + row(tp0 + tau) * dv + n0 + n;
+            if ((dv & 3) == 0 && n0 + n + 3 < dv) {
+                *(uint2 *)op = val;
+            } else {
+                const T vv[4] = {(T)(val.x & 0xffffu), (T)(val.x >> 16), (T)(val.y & 0xffffu), (T)(val.y >> 16)};
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    if (n0 + n + rr < dv) op[rr] = vv[rr];
+            }
         }
     };
 
@@ -234,7 +319,9 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
             }
         }
         load_chunk(0, tid);
+        stage_chunk(tid);
     }
+    __syncthreads();
 
     for (int cidx = 0; cidx < NC; ++cidx) {
         const int t0 = cidx * C, nvalid = min(C, Tlen - t0);
@@ -259,27 +346,24 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
         float g[TPT][4];
         bool wide_here = false;
         {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            // tokens seg + TPC i: one group scan per i, offset by the earlier runs' totals
+            float base[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < TPT; ++i)
+            for (int i = 0; i < TPT; ++i) {
+                const f32x4 pa = act ? *(const f32x4 *)(As + (seg + TPC * i) * ASD + c0)
+                                     : f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    acc[j] += __builtin_amdgcn_logf(pa[i][j]);
-                    g[i][j] = acc[j];
+                    g[i][j] = base[j] + scan_group<TPC>(__builtin_amdgcn_logf(pa[j]), seg);
+                    base[j] = group_last<TPC>(g[i][j]);
                 }
-            float incl[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) incl[j] = scan_group<TPC>(acc[j], seg);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < TPT; ++i) g[i][j] += incl[j] - acc[j];
+            }
             if (act && seg == TPC - 1) {
-                *(f32x4 *)(glc + c0) = f32x4{incl[0], incl[1], incl[2], incl[3]};
-                *(f32x4 *)(erL + c0) = f32x4{exp2f_(0.5f * incl[0]), exp2f_(0.5f * incl[1]),
-                                             exp2f_(0.5f * incl[2]), exp2f_(0.5f * incl[3])};
+                *(f32x4 *)(glc + c0) = f32x4{base[0], base[1], base[2], base[3]};
+                *(f32x4 *)(erL + c0) = f32x4{exp2f_(0.5f * base[0]), exp2f_(0.5f * base[1]),
+                                             exp2f_(0.5f * base[2]), exp2f_(0.5f * base[3])};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wide_here |= incl[j] < -WIDE_G2;
+                for (int j = 0; j < 4; ++j) wide_here |= base[j] < -WIDE_G2;
             }
         }
         // also the barrier after the previous chunk's last reads
@@ -291,54 +375,51 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
             float r[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) r[j] = wide ? 0.f : 0.5f * gl[j];
-            uint32_t kt[4][TPT];  // Kr^T pairs (erase, delta) per channel and token
+            auto token_ops = [&](auto WIDE) {
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) {
-                const int tau = seg * TPT + i;
-                float ev[4], kv[4], qv[4];
-                ev[0] = lo_bf16(pe[i].x); ev[1] = hi_bf16(pe[i].x);
-                ev[2] = lo_bf16(pe[i].y); ev[3] = hi_bf16(pe[i].y);
-                kv[0] = lo_bf16(pk[i].x); kv[1] = hi_bf16(pk[i].x);
-                kv[2] = lo_bf16(pk[i].y); kv[3] = hi_bf16(pk[i].y);
-                qv[0] = lo_bf16(pq[i].x); qv[1] = hi_bf16(pq[i].x);
-                qv[2] = lo_bf16(pq[i].y); qv[3] = hi_bf16(pq[i].y);
-                float f[4], fi[4];
-                if (!wide) {
+                for (int i = 0; i < TPT; ++i) {
+                    const int tau = seg + TPC * i;
+                    const uint2 pq = *(const uint2 *)(Qs + tau * LDA + c0);
+                    const uint2 pk = *(const uint2 *)(Ks + tau * LDA + c0);
+                    const uint2 pe = *(const uint2 *)(Es + tau * LDA + c0);
+                    float ev[4], kv[4], qv[4];
+                    ev[0] = lo_bf16(pe.x); ev[1] = hi_bf16(pe.x);
+                    ev[2] = lo_bf16(pe.y); ev[3] = hi_bf16(pe.y);
+                    kv[0] = lo_bf16(pk.x); kv[1] = hi_bf16(pk.x);
+                    kv[2] = lo_bf16(pk.y); kv[3] = hi_bf16(pk.y);
+                    qv[0] = lo_bf16(pq.x); qv[1] = hi_bf16(pq.x);
+                    qv[2] = lo_bf16(pq.y); qv[3] = hi_bf16(pq.y);
+                    float f[4];
+                    if constexpr (!decltype(WIDE)::value) {
+                        float fi[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        f[j] = exp2f_(g[i][j] - r[j]);
-                        fi[j] = exp2f_(r[j] - g[i][j]);
+                        for (int j = 0; j < 4; ++j) {
+                            f[j] = exp2f_(g[i][j] - r[j]);
+                            fi[j] = exp2f_(r[j] - g[i][j]);
+                        }
+                        *(uint2 *)(Kr + (2 * tau) * LDA + c0) =
+                            make_uint2(pack_bf16(ev[0] * fi[0], ev[1] * fi[1]), pack_bf16(ev[2] * fi[2], ev[3] * fi[3]));
+                        *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) =
+                            make_uint2(pack_bf16(kv[0] * fi[0], kv[1] * fi[1]), pack_bf16(kv[2] * fi[2], kv[3] * fi[3]));
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            f[j] = exp2f_(g[i][j]);
+                            Gs[tau * D + c0 + j] = g[i][j];
+                        }
+                        *(uint2 *)(Kr + (2 * tau) * LDA + c0) = pe;
+                        *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = pk;
                     }
-                    *(uint2 *)(Kr + (2 * tau) * LDA + c0) =
-                        make_uint2(pack_bf16(ev[0] * fi[0], ev[1] * fi[1]), pack_bf16(ev[2] * fi[2], ev[3] * fi[3]));
-                    *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) =
-                        make_uint2(pack_bf16(kv[0] * fi[0], kv[1] * fi[1]), pack_bf16(kv[2] * fi[2], kv[3] * fi[3]));
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        f[j] = exp2f_(g[i][j]);
-                        fi[j] = exp2f_(gl[j] - g[i][j]);  // Khat factor, <= 1
-                        Gs[tau * D + c0 + j] = g[i][j];
-                    }
-                    *(uint2 *)(Kr + (2 * tau) * LDA + c0) = pe[i];
-                    *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = pk[i];
-                    *(uint2 *)(Qraw + tau * LDA + c0) = pq[i];
+                    *(uint2 *)(Kl + (2 * tau) * LDA + c0) =
+                        make_uint2(pack_bf16(ev[0] * f[0], ev[1] * f[1]), pack_bf16(ev[2] * f[2], ev[3] * f[3]));
+                    *(uint2 *)(Kl + (2 * tau + 1) * LDA + c0) =
+                        make_uint2(pack_bf16(kv[0] * f[0], kv[1] * f[1]), pack_bf16(kv[2] * f[2], kv[3] * f[3]));
+                    *(uint2 *)(Ql + tau * LDA + c0) =
+                        make_uint2(pack_bf16(qv[0] * f[0], qv[1] * f[1]), pack_bf16(qv[2] * f[2], qv[3] * f[3]));
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kt[j][i] = pack_bf16(ev[j] * fi[j], kv[j] * fi[j]);
-                *(uint2 *)(Kl + (2 * tau) * LDA + c0) =
-                    make_uint2(pack_bf16(ev[0] * f[0], ev[1] * f[1]), pack_bf16(ev[2] * f[2], ev[3] * f[3]));
-                *(uint2 *)(Kl + (2 * tau + 1) * LDA + c0) =
-                    make_uint2(pack_bf16(kv[0] * f[0], kv[1] * f[1]), pack_bf16(kv[2] * f[2], kv[3] * f[3]));
-                *(uint2 *)(Ql + tau * LDA + c0) =
-                    make_uint2(pack_bf16(qv[0] * f[0], qv[1] * f[1]), pack_bf16(qv[2] * f[2], qv[3] * f[3]));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                T *dst = KrT + (c0 + j) * LDL + 2 * seg * TPT;
-                if constexpr (TPT == 2) *(uint2 *)dst = make_uint2(kt[j][0], kt[j][1]);
-                else *(uint32_t *)dst = kt[j][0];
-            }
+            };
+            if (!wide) token_ops(std::false_type{});
+            else token_ops(std::true_type{});
             if (seg == 0) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -366,6 +447,7 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
             const int idx = tid + NT * m;
             if (idx < C * BV) Vs[idx] = pv[m];
         }
+        if (cidx > 0) flush_outputs(cidx - 1, tid);
         if (cidx + 1 < NC) load_chunk(cidx + 1, tid);
         __syncthreads();
 
@@ -399,9 +481,14 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
                 float x[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
+                    const f32x4 *arow = (const f32x4 *)(Ad + (J * 16 + i) * ADS);
+                    f32x4 av[4];
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4)
+                        if (4 * v4 < i) av[v4] = arow[v4];
                     float sum = (i == col) ? 1.f : 0.f;
 #pragma unroll
-                    for (int p = 0; p < i; ++p) sum -= Ad[(J * 16 + i) * 17 + p] * x[p];
+                    for (int p = 0; p < i; ++p) sum -= av[p >> 2][p & 3] * x[p];
                     x[i] = sum;
                 }
 #pragma unroll
@@ -420,7 +507,7 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int jl = g4 + rr;
-                    Ad[(J * 16 + jl) * 17 + l16] = (jl > l16) ? bp[16 * J + jl] * a[rr] : 0.f;
+                    Ad[(J * 16 + jl) * ADS + l16] = (jl > l16) ? bp[16 * J + jl] * a[rr] : 0.f;
                 }
                 wave_lds_sync();
                 invert_diag(J);
@@ -465,7 +552,7 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
                              exp2f_(Gs[tj * D + cc] - Gs[ti * D + cc]);
                     s *= bp[j];
                 }
-                if ((j >> 4) == (ii >> 4)) Ad[((j >> 4) * 16 + (j & 15)) * 17 + (ii & 15)] = s;
+                if ((j >> 4) == (ii >> 4)) Ad[((j >> 4) * 16 + (j & 15)) * ADS + (ii & 15)] = s;
                 else if (ii < j) Abf[j * LDL + ii] = from_f32<T>(s);
             }
             for (int idx = tid; idx < C * L; idx += NT) {
@@ -475,10 +562,16 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
                     const int ti = ii >> 1;
 #pragma unroll 2
                     for (int cc = 0; cc < D; ++cc)
-                        s += to_f32(Qraw[tau * LDA + cc]) * to_f32(Kr[ii * LDA + cc]) *
+                        s += to_f32(Qs[tau * LDA + cc]) * to_f32(Kr[ii * LDA + cc]) *
                              exp2f_(Gs[tau * D + cc] - Gs[ti * D + cc]);
                 }
                 Pm[tau * LDL + ii] = from_f32<T>(s);
+            }
+            __syncthreads();
+            // the state update reads Kr: turn the raw keys into Khat = kap 2^(G_C - G)
+            for (int idx = tid; idx < L * D; idx += NT) {
+                const int j = idx / D, cc = idx % D;
+                Kr[j * LDA + cc] = from_f32<T>(to_f32(Kr[j * LDA + cc]) * exp2f_(glc[cc] - Gs[(j >> 1) * D + cc]));
             }
             __syncthreads();
             if (wave < NB) invert_diag(wave);
@@ -487,25 +580,45 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
 
         // ---- 1d. off-diagonal blocks of (I + A)^{-1}, one column block per wave:
         //      X_JI = -X_JJ sum_{I <= K < J} A_JK X_KI, for J = I+1, I+2, ...
+        // A 16x16 accumulator (lane: rows 4g..4g+3 of column l%16) is exactly the
+        // B operand of the 16x16x16 instruction, so the X_KI stay in registers.
         if (wave < NB - 1) {
             const int I = wave;
-            T *Zw = Zd + wave * 16 * ZW;
-            for (int J = I + 1; J < NB; ++J) {
-                f32x4 a = tile_nt_dyn<T>(Abf + 16 * J * LDL + 16 * I, LDL, MT + 16 * I * LDL + 16 * I,
-                                         LDL, 16 * (J - I), zero4(), lane);
-                store4<T>(Zw + l16 * ZW + g4, a[0], a[1], a[2], a[3]);
-                wave_lds_sync();
-                f32x4 x = tile_nt<T, 16>(MI + 16 * J * LDL + 16 * J, LDL, Zw, ZW, zero4(), lane);
-                const int a0 = 16 * J + g4, ncol = 16 * I + l16;
+            s16x4 xb[NB];   // X_KI as bf16 B operands (K >= I)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) MI[(a0 + rr) * LDL + ncol] = from_f32<T>(-x[rr]);
-                store4<T>(MT + ncol * LDL + a0, -x[0], -x[1], -x[2], -x[3]);
-                wave_lds_sync();
+            for (int K = 0; K < NB - 1; ++K)
+                if (K == I) xb[K] = *(const s16x4 *)(MT + (16 * K + l16) * LDL + 16 * K + g4);
+#pragma unroll
+            for (int J = 1; J < NB; ++J) {
+                if (J <= I) continue;
+                f32x4 t = zero4();
+#pragma unroll
+                for (int K = 0; K < J; ++K) {
+                    if (K < I) continue;
+                    const s16x4 a = *(const s16x4 *)(Abf + (16 * J + l16) * LDL + 16 * K + g4);
+                    t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, xb[K], t, 0, 0, 0);
+                }
+                const uint32_t t01 = pack_bf16(t[0], t[1]), t23 = pack_bf16(t[2], t[3]);
+                const s16x4 tb = __builtin_bit_cast(s16x4, make_uint2(t01, t23));
+                const s16x4 m = *(const s16x4 *)(MI + (16 * J + l16) * LDL + 16 * J + g4);
+                const f32x4 x = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(m, tb, zero4(), 0, 0, 0);
+                const uint32_t x01 = pack_bf16(-x[0], -x[1]), x23 = pack_bf16(-x[2], -x[3]);
+                xb[J] = __builtin_bit_cast(s16x4, make_uint2(x01, x23));
+                const int a0 = 16 * J + g4, ncol = 16 * I + l16;
+                MI[(a0 + 0) * LDL + ncol] = (T)(x01 & 0xffffu);
+                MI[(a0 + 1) * LDL + ncol] = (T)(x01 >> 16);
+                MI[(a0 + 2) * LDL + ncol] = (T)(x23 & 0xffffu);
+                MI[(a0 + 3) * LDL + ncol] = (T)(x23 >> 16);
             }
         }
         __syncthreads();
 
         // ---- 2a. U = (I + A)^{-1} Z  (Z's rounding residual added in fp32) --------
+        // First the next chunk's raw inputs go to the staging buffers: their last
+        // readers in this chunk (1a, 1b, the element-wise path of 1c) are behind
+        // the barriers above, and the barrier below orders them before the next
+        // chunk's reads.
+        if (cidx + 1 < NC) stage_chunk(tid);
 #pragma unroll
         for (int m = 0; m < YPW; ++m) {
             const int t = wave + NW * m;
@@ -525,17 +638,7 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
             f32x4 a = tile_nt<T, D>(St + 16 * nb * LDA, LDA, Ql + 16 * tb * LDA, LDA, zero4(), lane);
             a = tile_nt_dyn<T>(Ut + 16 * nb * LDL, LDL, Pm + 16 * tb * LDL, LDL,
                                min(L, 32 * (tb + 1)), a, lane);
-            const int tau = 16 * tb + l16, n = n0 + 16 * nb + g4;
-            if (tau < nvalid) {
-                T *op = o + row(t0 + tau) * dv;
-                if ((dv & 3) == 0 && n + 3 < dv) {
-                    store4<T>(op + n, a[0], a[1], a[2], a[3]);
-                } else {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        if (n + rr < dv) op[n + rr] = from_f32<T>(a[rr]);
-                }
-            }
+            store4<T>(Os + (16 * tb + l16) * LDO + 16 * nb + g4, a[0], a[1], a[2], a[3]);
         }
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
@@ -545,13 +648,15 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
                 f32x4 a;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) a[rr] = lam1[16 * rb + g4 + rr] * S[m][rr];
-                a = tile_nt<T, L>(KrT + 16 * rb * LDL, LDL, Ut + 16 * cb * LDL, LDL, a, lane);
+                a = tile_tn_bf16<L>(Kr + 16 * rb, LDA, Ut + 16 * cb * LDL, LDL, a, lane);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) S[m][rr] = sK[16 * rb + g4 + rr] * a[rr];
             }
         }
     }
 
+    __syncthreads();
+    flush_outputs(NC - 1, threadIdx.x);
     if (S_final) {
         // every read of S0 happened before the chunk loop, so S_final may be S0
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -588,10 +693,11 @@ hipError_t launch_fused_t(const void *q, const void *k, const void *e, const voi
     const int NC = (Tlen + C - 1) / C, BH = B * H;
     const int R = (dv + BV - 1) / BV;
     const int grid = 8 * ((BH + 7) / 8) * R;
-    // 8-byte loads of 4 bf16 channels and 16-byte loads of 4 alphas need
-    // d_k % 4 == 0 and aligned bases; otherwise element loads are used
-    const int vec = (dk % 4 == 0) && ((uintptr_t)q % 8 == 0) && ((uintptr_t)k % 8 == 0) &&
-                    ((uintptr_t)e % 8 == 0) && ((uintptr_t)alpha % 16 == 0);
+    // 16-byte loads of whole token rows need d_k == D and 16-byte aligned
+    // bases (D is a multiple of 8, so every row start stays aligned);
+    // otherwise element loads are used
+    const int vec = (dk == D) && ((uintptr_t)q % 16 == 0) && ((uintptr_t)k % 16 == 0) &&
+                    ((uintptr_t)e % 16 == 0) && ((uintptr_t)alpha % 16 == 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(G::NT), G::LDS, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)e, (const bf16 *)v, alpha, beta, gamma, S0,
                        S_final, (bf16 *)o, Tlen, H, BH, dk, dv, NC, R, vec);
