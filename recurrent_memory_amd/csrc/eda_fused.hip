@@ -103,8 +103,15 @@ struct FusedGeom {
     static_assert((TPC & (TPC - 1)) == 0 && TPC <= 64 && C % TPC == 0 && ACT <= NT, "split");
     static_assert(TPT == 1 || TPT == 2, "token run");
     static constexpr int VPT = (C * BV + NT - 1) / NT; // value elements per thread
+    // waves 0..NB-1 invert the diagonal blocks of A and sweep the inverse; the
+    // other NZW "matrix" waves own the Z/U tiles, A and P tiles and the
+    // state-independent half of the outputs
+    static constexpr int NZW = NW - NB;
+    static_assert(NZW >= 1, "too few waves for this chunk size");
     static constexpr int NYT = NB * (BV / 16);         // Z / U tiles
-    static constexpr int YPW = (NYT + NW - 1) / NW;
+    static constexpr int YPW = (NYT + NZW - 1) / NZW;
+    static constexpr int NOT = (BV / 16) * (C / 16);   // output tiles
+    static constexpr int OPW = (NOT + NZW - 1) / NZW;
     // LDS layout (bytes)
     static constexpr int szKl = align16(L * LDA * 2), szQl = align16(C * LDA * 2);
     static constexpr int szP = align16(C * LDL * 2);
@@ -143,6 +150,7 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
     using T = bf16;
     constexpr int L = G::L, NB = G::NB, NT = G::NT, LDA = G::LDA, LDL = G::LDL;
     constexpr int TPC = G::TPC, TPT = G::TPT, VPT = G::VPT, NYT = G::NYT, YPW = G::YPW;
+    constexpr int NZW = G::NZW, NOT = G::NOT, OPW = G::OPW;
     constexpr int ADS = G::ADS, ASD = G::ASD;
     constexpr int LPR = G::LPR, RPP = G::RPP, PQ = G::PQ, LPA = G::LPA, RPA = G::RPA, PA = G::PA;
     constexpr int NST = (D / 16) * (BV / 16);          // state tiles
@@ -452,12 +460,13 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
         __syncthreads();
 
         // ---- 1c. Z = Diag(b') (N - Kl S') ; A (strictly lower) ; P (causal) -------
+        const int mw = wave - NB;  // matrix-wave index (< 0 on the inverse waves)
         f32x4 ZR[YPW];  // fp32 rounding residual of Z, kept for the U product
 #pragma unroll
         for (int m = 0; m < YPW; ++m) {
-            const int t = wave + NW * m;
+            const int t = mw + NZW * m;
             ZR[m] = zero4();
-            if (t < NYT) {
+            if (mw >= 0 && t < NYT) {
                 const int jb = t / (BV / 16), nb = t % (BV / 16);
                 f32x4 y = tile_nt<T, D>(Kl + 16 * jb * LDA, LDA, St + 16 * nb * LDA, LDA, zero4(), lane);
                 float z[4];
@@ -512,12 +521,10 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
                 wave_lds_sync();
                 invert_diag(J);
             }
-            // off-diagonal A tiles, then P^T tiles; waves that own a diagonal
-            // block take the last ranks
+            // off-diagonal A tiles, then P^T tiles, on the matrix waves
             constexpr int NOD = NB * (NB - 1) / 2;
             constexpr int NPT = NB * (C / 16);
-            const int rank = (wave + NW - NB) % NW;
-            for (int t = rank; t < NOD + NPT; t += NW) {
+            for (int t = mw; mw >= 0 && t < NOD + NPT; t += NZW) {
                 if (t < NOD) {
                     int J = 1, I = t;
                     while (I >= J) { I -= J; ++J; }
@@ -578,6 +585,17 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
         }
         __syncthreads();
 
+        // ---- 1d (matrix waves): the state-independent half of the outputs, Ql S'
+        f32x4 OA[OPW];
+#pragma unroll
+        for (int m = 0; m < OPW; ++m) {
+            const int t = mw + NZW * m;
+            OA[m] = zero4();
+            if (mw >= 0 && t < NOT) {
+                const int nb = t / (C / 16), tb = t % (C / 16);
+                OA[m] = tile_nt<T, D>(St + 16 * nb * LDA, LDA, Ql + 16 * tb * LDA, LDA, zero4(), lane);
+            }
+        }
         // ---- 1d. off-diagonal blocks of (I + A)^{-1}, one column block per wave:
         //      X_JI = -X_JJ sum_{I <= K < J} A_JK X_KI, for J = I+1, I+2, ...
         // A 16x16 accumulator (lane: rows 4g..4g+3 of column l%16) is exactly the
@@ -621,8 +639,8 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
         if (cidx + 1 < NC) stage_chunk(tid);
 #pragma unroll
         for (int m = 0; m < YPW; ++m) {
-            const int t = wave + NW * m;
-            if (t < NYT) {
+            const int t = mw + NZW * m;
+            if (mw >= 0 && t < NYT) {
                 const int jb = t / (BV / 16), nb = t % (BV / 16);
                 f32x4 u = tile_nt_dyn<T>(MI + 16 * jb * LDL, LDL, Zt + 16 * nb * LDL, LDL,
                                          16 * (jb + 1), ZR[m], lane);
@@ -632,13 +650,15 @@ eda_chunk_fused(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf
         __syncthreads();
 
         // ---- 2b. outputs o^T = S'^T Ql^T + U^T P^T ; S <- e^r (e^r S + Kr^T U) ------
-        constexpr int NOT = (BV / 16) * (C / 16);
-        for (int t = wave; t < NOT; t += NW) {
-            const int nb = t / (C / 16), tb = t % (C / 16);
-            f32x4 a = tile_nt<T, D>(St + 16 * nb * LDA, LDA, Ql + 16 * tb * LDA, LDA, zero4(), lane);
-            a = tile_nt_dyn<T>(Ut + 16 * nb * LDL, LDL, Pm + 16 * tb * LDL, LDL,
-                               min(L, 32 * (tb + 1)), a, lane);
-            store4<T>(Os + (16 * tb + l16) * LDO + 16 * nb + g4, a[0], a[1], a[2], a[3]);
+#pragma unroll
+        for (int m = 0; m < OPW; ++m) {
+            const int t = mw + NZW * m;
+            if (mw >= 0 && t < NOT) {
+                const int nb = t / (C / 16), tb = t % (C / 16);
+                const f32x4 a = tile_nt_dyn<T>(Ut + 16 * nb * LDL, LDL, Pm + 16 * tb * LDL, LDL,
+                                               min(L, 32 * (tb + 1)), OA[m], lane);
+                store4<T>(Os + (16 * tb + l16) * LDO + 16 * nb + g4, a[0], a[1], a[2], a[3]);
+            }
         }
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
