@@ -60,13 +60,12 @@ typedef enum { EDA_F32 = 0, EDA_BF16 = 1 } eda_dtype_t;
 const char *eda_status_string(eda_status_t s);
 
 /*
- * Bytes of device workspace eda_fwd_chunked needs for these sizes.  `chunk`
- * is the number of tokens per chunk (0 selects the default, 32).  bf16 inputs
- * need none (the whole chunk computation stays on chip): the result is 0, and
- * the workspace arguments of eda_fwd_chunked are then ignored.  fp32 inputs
- * stage each chunk's state-independent factors in the workspace.  The result
- * is also 0 for an unsupported combination, which eda_fwd_chunked reports as
- * EDA_ERR_UNSUPPORTED.
+ * Bytes of device workspace eda_fwd_chunked needs for these sizes (0 for an
+ * unsupported combination).  `chunk` is the number of tokens per chunk (0
+ * selects the default, 32).  The workspace holds every chunk's
+ * state-independent factors between the two kernels of the chunked forward:
+ * for bf16 inputs with d_k = d_v = 128 and 32-token chunks that is 59136
+ * bytes per chunk and head (about 1.8 KB per token and head).
  */
 size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v,
                                       eda_dtype_t dtype, int chunk);
@@ -94,9 +93,8 @@ size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v,
  *   S_final : [B, H, d_k, d_v] fp32 final state, or NULL (not written);
  *             may be the same pointer as S0 (updated in place)
  *   workspace : device scratch of at least
- *             eda_fwd_chunked_workspace_size(...) bytes, 256-byte aligned
- *             (NULL allowed when that size is 0); its contents on entry are
- *             ignored and on return undefined
+ *             eda_fwd_chunked_workspace_size(...) bytes, 256-byte aligned;
+ *             its contents on entry are ignored and on return undefined
  *
  * Supported: 1 <= d_k, d_v <= 128; chunk in {0, 16, 32}; B, T, H >= 1 with
  * B*T*H*max(d_k, d_v) < 2^31.  o may not overlap any input; S_final may

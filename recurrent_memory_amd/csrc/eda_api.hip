@@ -16,9 +16,10 @@ template <typename T>
 hipError_t launch_chunked(int, const void *, const void *, const void *, const void *,
                           const float *, const float *, const float *, const float *, void *,
                           float *, int, int, int, int, int, int, void *, hipStream_t);
-hipError_t launch_fused(const void *, const void *, const void *, const void *, const float *,
-                        const float *, const float *, const float *, void *, float *, int, int,
-                        int, int, int, int, hipStream_t);
+size_t bf16_ws_bytes(int, int, int, int, int, int);
+hipError_t launch_bf16(const void *, const void *, const void *, const void *, const float *,
+                       const float *, const float *, const float *, void *, float *, int, int, int,
+                       int, int, int, void *, hipStream_t);
 }  // namespace eda
 
 namespace {
@@ -83,17 +84,17 @@ size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v, eda
     if (!dtype_ok(dtype) || !dims_ok(B, T, H, d_k, d_v) || !head_dims_supported(d_k, d_v) ||
         !chunk_supported(chunk))
         return 0;
-    // bf16: the single-pass kernel keeps every intermediate on chip
-    return dtype == EDA_BF16 ? 0 : eda::chunked_ws_t<float>(B, T, H, d_k, d_v, chunk);
+    return dtype == EDA_BF16 ? eda::bf16_ws_bytes(B, T, H, d_k, d_v, chunk)
+                             : eda::chunked_ws_t<float>(B, T, H, d_k, d_v, chunk);
 }
 
 }  // extern "C"
 
 namespace {
 
-// Checks, then the launch.  bf16 runs the single-pass kernel (no workspace);
-// fp32 runs the two-kernel form (chunk factors to the workspace, then the
-// state pass).
+// Checks, then the launch.  Both dtypes run two kernels: the chunk factors
+// (all chunks in parallel) go to the workspace, then the state pass walks the
+// chunks of each head in order.
 eda_status_t chunked_call(const void *q, const void *k, const void *e, const void *v,
                           const float *alpha, const float *beta, const float *gamma,
                           const float *S0, void *o, float *S_final, int B, int T, int H, int d_k,
@@ -140,8 +141,8 @@ eda_status_t chunked_call(const void *q, const void *k, const void *e, const voi
 
     hipError_t err =
         dtype == EDA_BF16
-            ? eda::launch_fused(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v,
-                                chunk, (hipStream_t)stream)
+            ? eda::launch_bf16(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v,
+                               chunk, workspace, (hipStream_t)stream)
             : eda::launch_chunked<float>(3, q, k, e, v, alpha, beta, gamma, S0, o, S_final, B,
                                          T, H, d_k, d_v, chunk, workspace, (hipStream_t)stream);
     return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;

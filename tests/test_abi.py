@@ -48,8 +48,10 @@ def test_status_strings():
 def test_workspace_size():
     lib = eda.load_library()
     ws = lib.eda_fwd_chunked_workspace_size
-    assert ws(4, 2048, 16, 128, 128, 1, 32) == 0              # bf16: everything stays on chip
-    big = ws(4, 2048, 16, 128, 128, 0, 32)                    # fp32: staged chunk factors
+    bf = ws(4, 2048, 16, 128, 128, 1, 32)                     # bf16 chunk factors
+    assert bf == 4 * 16 * (2048 // 32) * 59136                # one padded block per chunk and head
+    assert ws(4, 2048 + 1, 16, 128, 128, 1, 32) == bf + 4 * 16 * 59136   # a ragged tail is a chunk
+    big = ws(4, 2048, 16, 128, 128, 0, 32)                    # fp32 chunk factors
     assert big > 0
     assert ws(4, 2048, 16, 128, 128, 0, 0) == big            # 0 selects the default chunk
     assert ws(4, 4096, 16, 128, 128, 0, 32) == 2 * big        # linear in the chunk count
