@@ -18,36 +18,41 @@
 // the pages -- checked against the token recurrence).  Decay ratios are split
 // per channel around r = G_C / 2:
 //   Kl = kap o e^{G - r},  Kr = kap o e^{r - G},  Ql = q o e^{G - r},
-// so A = Diag(b') strict_lower(Kl Kr^T), P = causal(Ql Kr^T), and with the
-// scaled state S' = Diag(e^r) S:
-//   Z = Diag(b') (N - Kl S'),  U = (I + A)^{-1} Z,  o = Ql S' + P U,
-//   S_next = Diag(e^r) (Diag(e^r) S + Kr^T U)            (e^{G_C} = e^{2r}).
-// Every factor stays within e^{+-|G_C|/2}; a chunk in which some channel
-// decays by more than e^-120 (only possible below the safe gate's floor
-// alpha = e^-5) computes A and P element-wise from e^{G_j - G_i} and stores
-// the unsplit factors kap o e^G, q o e^G and Khat instead.
+// so A = Diag(b') strict_lower(Kl Kr^T) and P = causal(Ql Kr^T).  With the
+// scaled state S' = Diag(e^r) S, M = (I + A)^{-1}, the WY factors
+//   W = M Diag(b') Kl   [L x d_k],     T' = (M Diag(b'))[:, delta sub-steps]   [L x C]
+// give, per chunk,
+//   U = T' V - W S',   o = Ql S' + P U,   S_next = Diag(e^r) (Diag(e^r) S + Kr^T U)
+// (e^{G_C} = e^{2r}).  Every factor stays within e^{+-|G_C|/2}; a chunk in
+// which some channel decays by more than e^-120 (only possible below the safe
+// gate's floor alpha = e^-5) computes A and P element-wise from e^{G_j - G_i}
+// and uses the unsplit factors kap o e^G, q o e^G and Khat instead.
 //
-// Kernel 1 (eda_bf16_factors): one workgroup per (head, chunk), all chunks in
-//   parallel.  Computes the state-independent factors -- Kl, Kr, Ql, the
-//   causal P, (I + A)^{-1} and the per-channel scales -- and writes them to the
-//   workspace.  The unit lower-triangular inverse: fp32 substitution on the
-//   16x16 diagonal blocks, then one column block of the off-diagonal part per
-//   wave, with the blocks held in registers.
-// Kernel 2 (eda_bf16_state): one workgroup per (head, slice of value columns),
-//   serial over chunks.  Keeps the fp32 state in registers and per chunk
-//   forms Z, U, the outputs and the next state on the matrix cores (three
-//   barriers per chunk), while the next chunk's factor block is fetched into
-//   the other half of a double buffer.
+// Kernel 1 (eda_bf16_factors): persistent workgroups walk the (head, chunk)
+//   items; each item's raw rows are fetched into registers while the previous
+//   item is processed.  Per item: the cumulative decay, the scaled operands,
+//   A and P on the matrix cores, (I + A)^{-1} (fp32 substitution on the 16x16
+//   diagonal blocks, then one column block of the rest per wave, held in
+//   registers), W on the matrix cores, and the export of -W, T', Kr^T, Ql, P
+//   and the per-channel scales to the workspace.
+// Kernel 2 (eda_bf16_state): one workgroup per (head, slice of value
+//   columns), serial over chunks, fp32 state in registers.  The factors are
+//   stored in the exact per-lane order of the matrix-core operands, so each
+//   wave fetches its own operands straight into registers two chunks ahead;
+//   only S'^T, U^T, the value slice and the outputs pass through LDS.  Two
+//   barriers per chunk.
 //
-// Workspace: one block of FacLayout<C, D>::bytes per chunk and head, rows
-// padded exactly like the LDS copies, so kernel 2 fetches a block as one
-// contiguous copy.
-#include <type_traits>
-
+// Workspace: one block of Fac<C, D>::bytes per chunk and head.  A "fragment"
+// of a matrix M (rows x k, row-major view) is the 16 x 32 block at
+// (16 rb, 32 ks): 64 lanes x 16 bytes, lane 16 g + r holding
+// M[16 rb + r][32 ks + 8 g .. 32 ks + 8 g + 7] -- the operand layout of the
+// 16x16x32 bf16 matrix instruction.
 #include "eda_common.h"
 
 namespace eda {
 namespace b16 {
+
+constexpr int NWAVES = 8, NTHREADS = 64 * NWAVES;
 
 // wide-chunk threshold on a chunk's log2-decay (e^-120 = 2^-173)
 constexpr float WIDE_G2 = 173.f;
@@ -61,6 +66,34 @@ __device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f
 
 // Make this wave's earlier LDS writes visible to its own later LDS reads.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Row fragment: lane 16 g + r gets p[r * ld + 8 g .. 8 g + 7] (any memory).
+__device__ __forceinline__ bf16x8 frag_row(const bf16 *p, int ld, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(p + (lane & 15) * ld + 8 * (lane >> 4));
+}
+// Column fragment from LDS: lane 16 g + n gets p[(8 g + j) * ld + n], j = 0..7.
+// The gfx950 transposing read: within a group of 16 lanes, lane i addresses
+// row i/4, columns 4(i%4)..4(i%4)+3 of a 4 x 16 block, and lane n receives
+// column n of the 4 rows.
+__device__ __forceinline__ bf16x8 frag_col(const bf16 *p, int ld, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const bf16 *mp = p + (8 * g + (i >> 2)) * ld + 4 * (i & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)mp);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(mp + 4 * ld));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 ld_frag(const char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ void st_frag(char *p, bf16x8 x) { *reinterpret_cast<bf16x8 *>(p) = x; }
 
 // Inclusive prefix sum over groups of N consecutive lanes (N a power of two);
 // `seg` is the lane's index in its group.  Groups of 16 use DPP row shifts.
@@ -93,31 +126,34 @@ __device__ __forceinline__ float group_last(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Workspace block of one chunk and head (byte offsets).
+// Workspace block of one chunk and head (byte offsets; fragments as above).
 // ---------------------------------------------------------------------------
 template <int C, int D>
-struct FacLayout {
-    static constexpr int L = 2 * C, LDA = D + 8, LDL = L + 8;
-    static constexpr int oKl = 0;                          // Kl    [L][LDA] bf16
-    static constexpr int oKr = oKl + L * LDA * 2;          // Kr    [L][LDA] bf16 (wide: Khat)
-    static constexpr int oQl = oKr + L * LDA * 2;          // Ql    [C][LDA] bf16
-    static constexpr int oMI = oQl + C * LDA * 2;          // (I+A)^-1 [L][LDL] bf16, lower blocks
-    static constexpr int oP = oMI + L * LDL * 2;           // P     [C][LDL] bf16, causal part
-    static constexpr int oErS = oP + C * LDL * 2;          // e^r (1 if wide)      [D] fp32
-    static constexpr int oLam = oErS + D * 4;              // e^r (e^{G_C} if wide) [D] fp32
-    static constexpr int oSK = oLam + D * 4;               // e^r (1 if wide)      [D] fp32
-    static constexpr int oBp = oSK + D * 4;                // b' per sub-step      [L] fp32
-    static constexpr int bytes = align256(oBp + L * 4);
-    static_assert(oKr % 16 == 0 && oQl % 16 == 0 && oMI % 16 == 0 && oP % 16 == 0 && oErS % 16 == 0,
-                  "16-byte sections");
+struct Fac {
+    static constexpr int L = 2 * C, NBL = L / 16, NBC = C / 16, NBD = D / 16;
+    static constexpr int KSD = D / 32, KSL = L / 32;
+    static constexpr int FR = 1024;                    // one fragment
+    static constexpr int oWn = 0;                      // -W    [NBL][KSD] fragments
+    static constexpr int oTv = oWn + NBL * KSD * FR;   // T'    [NBL] (k = C, zero-padded to 32)
+    static constexpr int oKr = oTv + NBL * FR;         // Kr^T  [NBD][KSL]   (wide: Khat^T)
+    static constexpr int oQl = oKr + NBD * KSL * FR;   // Ql    [NBC][KSD]
+    static constexpr int oP = oQl + NBC * KSD * FR;    // P     [NBC][KSL]
+    static constexpr int oEr = oP + NBC * KSL * FR;    // e^r (1 if wide)          [D] fp32
+    static constexpr int oLam = oEr + D * 4;           // e^r (e^{G_C} if wide)    [D] fp32
+    static constexpr int bytes = align256(oLam + D * 4);
+    static_assert(C == 16 || C == 32, "chunk");
+    static_assert(D % 32 == 0 && D <= 128, "head dim");
 };
 
 // ---------------------------------------------------------------------------
-// Kernel 1: chunk factors.  grid = B*H*NC, block = 64*NW.
+// Kernel 1: chunk factors.  Persistent: workgroup w takes items w, w + grid,
+// ...; item i is chunk NC - 1 - i / BH of head i % BH (last chunks first, so
+// the earliest chunks, which the state pass reads first, were written last).
 // ---------------------------------------------------------------------------
-template <int C, int D, int NW>
-struct K1Geom {
-    static constexpr int L = 2 * C, NB = L / 16, NT = 64 * NW;
+template <int C, int D>
+struct K1G {
+    using F = Fac<C, D>;
+    static constexpr int L = 2 * C, NB = L / 16, NT = NTHREADS, NW = NWAVES;
     static constexpr int LDA = D + 8, LDL = L + 8, ADS = 20, ASD = D + 8, MTW = 24;
     static constexpr int NQ = D / 4;
     static constexpr int TPC = imin(NT / NQ, C);       // threads per channel quad
@@ -127,198 +163,142 @@ struct K1Geom {
     static_assert(TPT == 1 || TPT == 2, "token run");
     static constexpr int NZW = NW - NB;                // matrix waves (A and P tiles)
     static_assert(NZW >= 1, "too few waves");
-    static constexpr int LPR = D / 8, RPP = NT / LPR, PQ = (C + RPP - 1) / RPP;   // 16-byte row loads
-    static constexpr int LPA = D / 4, RPA = NT / LPA, PA = (C + RPA - 1) / RPA;
+    // raw rows of one full chunk in 16-byte units: q, e, k (bf16), alpha (fp32)
+    static constexpr int RU = C * D / 8, AU = C * D / 4, NRAW = 3 * RU + AU;
+    static constexpr int PF = (NRAW + NT - 1) / NT;
+    // W^T tiles per wave
+    static constexpr int NWT = F::NBD * F::NBL, WPW = (NWT + NW - 1) / NW;
     // LDS (bytes).  Before the operands are formed, Kl holds the raw alpha
     // rows (fp32 [C][ASD]), Kr the raw e and k rows, Ql the raw q rows; in a
-    // wide chunk Kl then holds G (fp32 [C][D]) and Kr, Ql keep the raw keys.
+    // wide chunk Kl holds G (fp32 [C][D]) until the operands are formed.
+    // After the Kr^T export, the Kr region stages -W.
     static constexpr int szKl = align16(L * LDA * 2), szQl = align16(C * LDA * 2);
     static_assert(C * ASD * 4 <= szKl && C * D * 4 <= szKl, "Kl region reuse");
-    static constexpr int szAbf = align16(L * LDL * 2), szAd = NB * 16 * ADS * 4;
-    static constexpr int szMI = align16(L * LDL * 2), szMT = NB * 16 * MTW * 2;
+    static constexpr int szLL = align16(L * LDL * 2), szAd = NB * 16 * ADS * 4;
+    static constexpr int szMT = NB * 16 * MTW * 2, szPs = align16(C * LDL * 2);
     static constexpr int szMisc = (L + 2 * C + D) * 4;
     static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oAbf = oQl + szQl;
-    static constexpr int oAd = oAbf + szAbf, oMI = oAd + szAd, oMT = oMI + szMI, oMisc = oMT + szMT;
+    static constexpr int oAd = oAbf + szLL, oMI = oAd + szAd, oMT = oMI + szLL, oPs = oMT + szMT;
+    static constexpr int oMisc = oPs + szPs;
     static constexpr int LDS = oMisc + szMisc;
     static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
 };
 
-template <int C, int D, int NW>
-__global__ void __launch_bounds__(64 * NW)
+template <int C, int D>
+__global__ void __launch_bounds__(NTHREADS)
 eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ e,
                  const float *__restrict__ alpha, const float *__restrict__ beta,
                  const float *__restrict__ gamma, char *__restrict__ ws, int Tlen, int H, int dk,
-                 int NC, int vec) {
-    using G = K1Geom<C, D, NW>;
-    using F = FacLayout<C, D>;
+                 int NC, int BH, int vec) {
+    using G = K1G<C, D>;
+    using F = Fac<C, D>;
     using T = bf16;
-    constexpr int L = G::L, NB = G::NB, NT = G::NT, LDA = G::LDA, LDL = G::LDL, ADS = G::ADS;
-    constexpr int ASD = G::ASD, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT, NZW = G::NZW;
-    constexpr int LPR = G::LPR, RPP = G::RPP, PQ = G::PQ, LPA = G::LPA, RPA = G::RPA, PA = G::PA;
+    constexpr int L = G::L, NB = G::NB, NT = G::NT, NW = G::NW, LDA = G::LDA, LDL = G::LDL;
+    constexpr int ADS = G::ADS, ASD = G::ASD, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT, NZW = G::NZW;
+    constexpr int RU = G::RU, NRAW = G::NRAW, PF = G::PF, WPW = G::WPW, NWT = G::NWT;
+    constexpr int NBD = F::NBD, NBL = F::NBL, NBC = F::NBC, KSD = F::KSD, KSL = F::KSL;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    T *Kl = (T *)(smem + G::oKl);
-    float *As = (float *)(smem + G::oKl);   // raw alpha [C][ASD] (before the operands)
-    float *Gs = (float *)(smem + G::oKl);   // wide chunk: G (log2) [C][D]
-    T *Kr = (T *)(smem + G::oKr);
-    T *Ql = (T *)(smem + G::oQl);
-    T *Abf = (T *)(smem + G::oAbf);          // A, off-diagonal 16-blocks   [L][LDL]
-    float *Ad = (float *)(smem + G::oAd);    // A, diagonal 16-blocks      [NB][16][ADS]
-    T *MI = (T *)(smem + G::oMI);            // (I + A)^{-1}               [L][LDL]
+    T *Kl = (T *)(smem + G::oKl);            // Diag(b') Kl              [L][LDA]
+    float *As = (float *)(smem + G::oKl);    // raw alpha [C][ASD] (before the operands)
+    float *Gs = (float *)(smem + G::oKl);    // wide chunk: G (log2) [C][D]
+    T *Kr = (T *)(smem + G::oKr);            // Kr                       [L][LDA]
+    T *Wst = Kr;                             // -W, after the Kr^T export [L][LDA]
+    T *Ql = (T *)(smem + G::oQl);            // Ql                       [C][LDA]
+    T *Abf = (T *)(smem + G::oAbf);          // A, off-diagonal 16-blocks [L][LDL]
+    float *Ad = (float *)(smem + G::oAd);    // A, diagonal 16-blocks    [NB][16][ADS]
+    T *MI = (T *)(smem + G::oMI);            // (I + A)^{-1}             [L][LDL]
     T *MT = (T *)(smem + G::oMT);            // its diagonal blocks, transposed [NB][16][MTW]
-    float *bp = (float *)(smem + G::oMisc);  // b' per sub-step            [L]
-    float *sb = bp + L, *sg = sb + C;        // beta, gamma per token      [C]
-    float *glc = sg + C;                     // G_C per channel (log2)     [D]
+    T *Ps = (T *)(smem + G::oPs);            // P (causal)               [C][LDL]
+    float *bp = (float *)(smem + G::oMisc);  // b' per sub-step          [L]
+    float *sb = bp + L, *sg = sb + C;        // beta, gamma per token    [C]
+    float *glc = sg + C;                     // G_C per channel (log2)   [D]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = 4 * (lane >> 4), l16 = lane & 15;
-    const int bh = blockIdx.x / NC, cidx = blockIdx.x % NC;
-    const int b = bh / H, h = bh % H;
-    const int t0 = cidx * C, nval = min(C, Tlen - t0);
-    const long hrow = (long)b * Tlen * H + h;
     const int HK = H * dk;
-    const bf16 *qh = q + hrow * dk, *kh = k + hrow * dk, *eh = e + hrow * dk;
-    const float *ah = alpha + hrow * dk;
-    char *wsb = ws + ((long)bh * NC + cidx) * F::bytes;
-    T *gKl = (T *)(wsb + F::oKl), *gKr = (T *)(wsb + F::oKr), *gQl = (T *)(wsb + F::oQl);
-    T *gMI = (T *)(wsb + F::oMI), *gP = (T *)(wsb + F::oP);
-    float *gErS = (float *)(wsb + F::oErS), *gLam = (float *)(wsb + F::oLam);
-    float *gSK = (float *)(wsb + F::oSK), *gBp = (float *)(wsb + F::oBp);
+    const int items = BH * NC;
 
-    // ---- raw chunk rows -> LDS (whole-row 16-byte loads) -------------------------
-    if (vec && nval == C) {
-#pragma unroll
-        for (int p = 0; p < PQ; ++p) {
-            const int r = tid / LPR + RPP * p, blk = tid % LPR;
-            if (RPP * PQ == C || r < C) {
-                const int off = (t0 + r) * HK + 8 * blk;
-                *(uint4 *)(Ql + r * LDA + 8 * blk) = *(const uint4 *)(qh + off);
-                *(uint4 *)(Kr + (2 * r) * LDA + 8 * blk) = *(const uint4 *)(eh + off);
-                *(uint4 *)(Kr + (2 * r + 1) * LDA + 8 * blk) = *(const uint4 *)(kh + off);
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < PA; ++p) {
-            const int r = tid / LPA + RPA * p, blk = tid % LPA;
-            if (RPA * PA == C || r < C)
-                *(f32x4 *)(As + r * ASD + 4 * blk) = *(const f32x4 *)(ah + (t0 + r) * HK + 4 * blk);
-        }
-    } else {
-        for (int idx = tid; idx < C * D; idx += NT) {
-            const int r = idx / D, c = idx % D;
-            const bool ok = r < nval && c < dk;
-            const int off = (t0 + r) * HK + c;
-            Ql[r * LDA + c] = ok ? q[hrow * dk + off] : (T)0;
-            Kr[(2 * r) * LDA + c] = ok ? e[hrow * dk + off] : (T)0;
-            Kr[(2 * r + 1) * LDA + c] = ok ? k[hrow * dk + off] : (T)0;
-            As[r * ASD + c] = ok ? alpha[hrow * dk + off] : 1.f;
-        }
+    // The blocks of (I + A)^{-1} above the diagonal are never written: zero
+    // them (and the row padding) once.
+    for (int idx = tid; idx < L * LDL; idx += NT) {
+        const int r = idx / LDL, c = idx % LDL;
+        if (c >= L || (c >> 4) > (r >> 4)) MI[idx] = (T)0;
     }
-    if (tid < C) {
-        const bool ok = tid < nval;
-        const float bv = ok ? beta[hrow + (long)(t0 + tid) * H] : 0.f;
-        const float gv = ok ? gamma[hrow + (long)(t0 + tid) * H] : 0.f;
-        sb[tid] = bv;
-        sg[tid] = gv;
-        bp[2 * tid] = gv;
-        bp[2 * tid + 1] = bv;
-        *(f32x2 *)(gBp + 2 * tid) = f32x2{gv, bv};
-    }
-    __syncthreads();
 
-    // ---- cumulative log2-decay per channel; wide-chunk vote ----------------------
-    const bool act = tid < G::ACT;
-    const int seg = tid % TPC, c0 = 4 * (tid / TPC);
-    float g[TPT][4];
-    bool wide_here = false;
-    {
-        float base[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            // tokens seg + TPC i: one group scan per run, offset by the earlier runs' totals
-            const f32x4 pa = act ? *(const f32x4 *)(As + (seg + TPC * i) * ASD + c0) : f32x4{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                g[i][j] = base[j] + scan_group<TPC>(__builtin_amdgcn_logf(pa[j]), seg);
-                base[j] = group_last<TPC>(g[i][j]);
-            }
-        }
-        if (act && seg == TPC - 1) {
-            *(f32x4 *)(glc + c0) = f32x4{base[0], base[1], base[2], base[3]};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wide_here |= base[j] < -WIDE_G2;
-        }
-    }
-    const bool wide = __syncthreads_or(wide_here) != 0;
+    auto chunk_of = [&](int it) __attribute__((always_inline)) { return NC - 1 - it / BH; };
+    auto head_of = [&](int it) __attribute__((always_inline)) { return it % BH; };
+    auto is_fast = [&](int cidx) __attribute__((always_inline)) { return vec != 0 && cidx * C + C <= Tlen; };
 
-    // ---- scaled operands (LDS and workspace) and per-channel scales --------------
-    if (act) {
-        const f32x4 gl = *(const f32x4 *)(glc + c0);
-        float r[4];
+    // ---- raw rows of a full chunk -> registers (fetched one item ahead) ---------
+    uint4 pre[PF];
+    float pbeta = 0.f, pgamma = 0.f;
+    auto prefetch = [&](int it) __attribute__((always_inline)) {
+        const int bh = head_of(it), cidx = chunk_of(it);
+        const int b = bh / H, h = bh % H;
+        const long tok0 = ((long)b * Tlen + (long)cidx * C) * H + h;   // row of the chunk's first token
+        const bf16 *qh = q + tok0 * dk, *eh = e + tok0 * dk, *kh = k + tok0 * dk;
+        const float *ah = alpha + tok0 * dk;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = wide ? 0.f : 0.5f * gl[j];
+        for (int m = 0; m < PF; ++m) {
+            const int u = tid + NT * m;
+            const int part = u / RU, uu = u - part * RU;   // 0 q, 1 e, 2 k, 3.. alpha
+            const bf16 *rowp = part == 0 ? qh : (part == 1 ? eh : kh);
+            const char *src = part < 3 ? (const char *)(rowp + (uu / (D / 8)) * HK + 8 * (uu % (D / 8)))
+                                       : (const char *)(ah + ((u - 3 * RU) / (D / 4)) * HK + 4 * ((u - 3 * RU) % (D / 4)));
+            pre[m] = make_uint4(0u, 0u, 0u, 0u);
+            if (u < NRAW) pre[m] = *(const uint4 *)src;
+        }
+        if (tid < C) {
+            pbeta = beta[tok0 + (long)tid * H];
+            pgamma = gamma[tok0 + (long)tid * H];
+        }
+    };
+    // ---- registers (or, for a ragged or unaligned chunk, global) -> LDS ---------
+    auto stage = [&](int it, bool fast) __attribute__((always_inline)) {
+        const int bh = head_of(it), cidx = chunk_of(it);
+        const int b = bh / H, h = bh % H;
+        const int t0 = cidx * C, nval = min(C, Tlen - t0);
+        const long tok0 = ((long)b * Tlen + t0) * H + h;
+        float bv = 0.f, gv = 0.f;
+        if (fast) {
 #pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const int tau = seg + TPC * i;
-            const uint2 pq = *(const uint2 *)(Ql + tau * LDA + c0);
-            const uint2 pe = *(const uint2 *)(Kr + (2 * tau) * LDA + c0);
-            const uint2 pk = *(const uint2 *)(Kr + (2 * tau + 1) * LDA + c0);
-            const float ev[4] = {lo_bf16(pe.x), hi_bf16(pe.x), lo_bf16(pe.y), hi_bf16(pe.y)};
-            const float kv[4] = {lo_bf16(pk.x), hi_bf16(pk.x), lo_bf16(pk.y), hi_bf16(pk.y)};
-            const float qv[4] = {lo_bf16(pq.x), hi_bf16(pq.x), lo_bf16(pq.y), hi_bf16(pq.y)};
-            float f[4], fi[4];
-            if (!wide) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f[j] = exp2f_(g[i][j] - r[j]);
-                    fi[j] = exp2f_(r[j] - g[i][j]);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f[j] = exp2f_(g[i][j]);
-                    fi[j] = exp2f_(gl[j] - g[i][j]);   // Khat factor, <= 1
-                }
+            for (int m = 0; m < PF; ++m) {
+                const int u = tid + NT * m;
+                const int part = u / RU, uu = u - part * RU;
+                const int rr = uu / (D / 8), bb = uu % (D / 8);
+                char *dst = part == 0 ? (char *)(Ql + rr * LDA + 8 * bb)
+                          : part < 3  ? (char *)(Kr + (2 * rr + part - 1) * LDA + 8 * bb)
+                                      : (char *)(As + ((u - 3 * RU) / (D / 4)) * ASD + 4 * ((u - 3 * RU) % (D / 4)));
+                if (u < NRAW) *(uint4 *)dst = pre[m];
             }
-            const uint2 kl0 = make_uint2(pack_bf16(ev[0] * f[0], ev[1] * f[1]), pack_bf16(ev[2] * f[2], ev[3] * f[3]));
-            const uint2 kl1 = make_uint2(pack_bf16(kv[0] * f[0], kv[1] * f[1]), pack_bf16(kv[2] * f[2], kv[3] * f[3]));
-            const uint2 kr0 = make_uint2(pack_bf16(ev[0] * fi[0], ev[1] * fi[1]), pack_bf16(ev[2] * fi[2], ev[3] * fi[3]));
-            const uint2 kr1 = make_uint2(pack_bf16(kv[0] * fi[0], kv[1] * fi[1]), pack_bf16(kv[2] * fi[2], kv[3] * fi[3]));
-            const uint2 ql = make_uint2(pack_bf16(qv[0] * f[0], qv[1] * f[1]), pack_bf16(qv[2] * f[2], qv[3] * f[3]));
-            *(uint2 *)(gKl + (2 * tau) * LDA + c0) = kl0;
-            *(uint2 *)(gKl + (2 * tau + 1) * LDA + c0) = kl1;
-            *(uint2 *)(gKr + (2 * tau) * LDA + c0) = kr0;
-            *(uint2 *)(gKr + (2 * tau + 1) * LDA + c0) = kr1;
-            *(uint2 *)(gQl + tau * LDA + c0) = ql;
-            if (!wide) {
-                // Kl overwrites the raw alpha rows, which were last read before the vote
-                *(uint2 *)(Kl + (2 * tau) * LDA + c0) = kl0;
-                *(uint2 *)(Kl + (2 * tau + 1) * LDA + c0) = kl1;
-                *(uint2 *)(Kr + (2 * tau) * LDA + c0) = kr0;
-                *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = kr1;
-                *(uint2 *)(Ql + tau * LDA + c0) = ql;
-            } else {
-                *(f32x4 *)(Gs + tau * D + c0) = f32x4{g[i][0], g[i][1], g[i][2], g[i][3]};
+            bv = pbeta;
+            gv = pgamma;
+        } else {
+            for (int idx = tid; idx < C * D; idx += NT) {
+                const int r = idx / D, c = idx % D;
+                const bool ok = r < nval && c < dk;
+                const long off = (tok0 + (long)r * H) * dk + c;
+                Ql[r * LDA + c] = ok ? q[off] : (T)0;
+                Kr[(2 * r) * LDA + c] = ok ? e[off] : (T)0;
+                Kr[(2 * r + 1) * LDA + c] = ok ? k[off] : (T)0;
+                As[r * ASD + c] = ok ? alpha[off] : 1.f;
+            }
+            if (tid < nval) {
+                bv = beta[tok0 + (long)tid * H];
+                gv = gamma[tok0 + (long)tid * H];
             }
         }
-        if (seg == 0) {
-            f32x4 er, lam, skk;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float x = exp2f_(r[j]);
-                er[j] = wide ? 1.f : x;
-                lam[j] = wide ? exp2f_(gl[j]) : x;
-                skk[j] = wide ? 1.f : x;
-            }
-            *(f32x4 *)(gErS + c0) = er;
-            *(f32x4 *)(gLam + c0) = lam;
-            *(f32x4 *)(gSK + c0) = skk;
+        if (tid < C) {
+            sb[tid] = bv;
+            sg[tid] = gv;
+            bp[2 * tid] = gv;
+            bp[2 * tid + 1] = bv;
         }
-    }
-    __syncthreads();
+    };
 
-    // ---- A (strictly lower, b'-scaled) and P (causal); diagonal blocks inverted --
-    auto invert_diag = [&](int J) {
+    // ---- diagonal 16x16 blocks of (I + A)^{-1}: fp32 forward substitution ------
+    auto invert_diag = [&](int J) __attribute__((always_inline)) {
         if (lane < 16) {
             const int col = lane;
             float x[16];
@@ -343,157 +323,334 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                                pack_bf16(x[14], x[15]));
         }
     };
-    const int mw = wave - NB;   // matrix-wave index (< 0 on the inverse waves)
-    if (!wide) {
-        if (wave < NB) {
-            const int J = wave;
-            const f32x4 a = tile_nt<T, D>(Kl + 16 * J * LDA, LDA, Kr + 16 * J * LDA, LDA, zero4(), lane);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int jl = g4 + rr;
-                Ad[(J * 16 + jl) * ADS + l16] = (jl > l16) ? bp[16 * J + jl] * a[rr] : 0.f;
-            }
-            wave_lds_sync();
-            invert_diag(J);
+
+    int it = blockIdx.x;
+    if (it < items && is_fast(chunk_of(it))) prefetch(it);
+    for (; it < items; it += gridDim.x) {
+        const int bh = head_of(it), cidx = chunk_of(it);
+        stage(it, is_fast(cidx));
+        {
+            const int nx = it + gridDim.x;
+            if (nx < items && is_fast(chunk_of(nx))) prefetch(nx);
         }
-        constexpr int NOD = NB * (NB - 1) / 2;
-        constexpr int NPT = NB * (C / 16);
-        for (int t = mw; mw >= 0 && t < NOD + NPT; t += NZW) {
-            if (t < NOD) {
-                int J = 1, I = t;
-                while (I >= J) { I -= J; ++J; }
-                const f32x4 a = tile_nt<T, D>(Kl + 16 * J * LDA, LDA, Kr + 16 * I * LDA, LDA, zero4(), lane);
+        char *wsb = ws + ((long)bh * NC + cidx) * F::bytes;
+        __syncthreads();
+
+        // ---- cumulative log2-decay per channel; wide-chunk vote ------------------
+        const bool act = tid < G::ACT;
+        const int seg = tid % TPC, c0 = 4 * (tid / TPC);
+        float g[TPT][4];
+        bool wide_here = false;
+        {
+            float base[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int j = 16 * J + g4 + rr;
-                    Abf[j * LDL + 16 * I + l16] = from_f32<T>(bp[j] * a[rr]);
+            for (int i = 0; i < TPT; ++i) {
+                // tokens seg + TPC i: one group scan per run, offset by the earlier runs' totals
+                const f32x4 pa = act ? *(const f32x4 *)(As + (seg + TPC * i) * ASD + c0)
+                                     : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    g[i][j] = base[j] + scan_group<TPC>(__builtin_amdgcn_logf(pa[j]), seg);
+                    base[j] = group_last<TPC>(g[i][j]);
                 }
-            } else {
-                // P^T tile: rows = sub-steps i, cols = tokens; kept for i <= 2 tau + 1
-                const int I = (t - NOD) / (C / 16), Tb = (t - NOD) % (C / 16);
-                if (16 * I > 32 * Tb + 31) continue;   // beyond every token's causal range
-                const f32x4 a = tile_nt<T, D>(Kr + 16 * I * LDA, LDA, Ql + 16 * Tb * LDA, LDA, zero4(), lane);
-                const int tau = 16 * Tb + l16, i0 = 16 * I + g4;
-                float w4[4];
+            }
+            if (act && seg == TPC - 1) {
+                *(f32x4 *)(glc + c0) = f32x4{base[0], base[1], base[2], base[3]};
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) w4[rr] = (i0 + rr <= 2 * tau + 1) ? a[rr] : 0.f;
-                store4<T>(gP + tau * LDL + i0, w4[0], w4[1], w4[2], w4[3]);
+                for (int j = 0; j < 4; ++j) wide_here |= base[j] < -WIDE_G2;
             }
         }
-    } else {
-        // exact element-wise path: e^{G_j - G_i} is never split (Kr, Ql hold raw keys)
-        for (int idx = tid; idx < L * L; idx += NT) {
-            const int j = idx / L, ii = idx % L;
-            float s = 0.f;
-            if (ii < j) {
-                const int tj = j >> 1, ti = ii >> 1;
-#pragma unroll 2
-                for (int cc = 0; cc < D; ++cc)
-                    s += to_f32(Kr[j * LDA + cc]) * to_f32(Kr[ii * LDA + cc]) *
-                         exp2f_(Gs[tj * D + cc] - Gs[ti * D + cc]);
-                s *= bp[j];
+        const bool wide = __syncthreads_or(wide_here) != 0;
+
+        // ---- scaled operands (LDS) and per-channel scales (workspace) -------------
+        // Forms Diag(b') Kl, Kr and Ql from the raw rows the thread owns; in a
+        // wide chunk the exponents are unsplit (Kl = kap 2^G, Kr = kap 2^{G_C - G}).
+        f32x4 glq = zero4();
+        auto form_operands = [&]() __attribute__((always_inline)) {
+            float r[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[j] = wide ? 0.f : 0.5f * glq[j];
+#pragma unroll
+            for (int i = 0; i < TPT; ++i) {
+                const int tau = seg + TPC * i;
+                const uint2 pq = *(const uint2 *)(Ql + tau * LDA + c0);
+                const uint2 pe = *(const uint2 *)(Kr + (2 * tau) * LDA + c0);
+                const uint2 pk = *(const uint2 *)(Kr + (2 * tau + 1) * LDA + c0);
+                const float ev[4] = {lo_bf16(pe.x), hi_bf16(pe.x), lo_bf16(pe.y), hi_bf16(pe.y)};
+                const float kv[4] = {lo_bf16(pk.x), hi_bf16(pk.x), lo_bf16(pk.y), hi_bf16(pk.y)};
+                const float qv[4] = {lo_bf16(pq.x), hi_bf16(pq.x), lo_bf16(pq.y), hi_bf16(pq.y)};
+                const float gmt = sg[tau], btt = sb[tau];
+                float f[4], fi[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f[j] = exp2f_(g[i][j] - r[j]);
+                    fi[j] = wide ? exp2f_(glq[j] - g[i][j]) : exp2f_(r[j] - g[i][j]);
+                }
+                store4<T>(Kl + (2 * tau) * LDA + c0, gmt * ev[0] * f[0], gmt * ev[1] * f[1],
+                          gmt * ev[2] * f[2], gmt * ev[3] * f[3]);
+                store4<T>(Kl + (2 * tau + 1) * LDA + c0, btt * kv[0] * f[0], btt * kv[1] * f[1],
+                          btt * kv[2] * f[2], btt * kv[3] * f[3]);
+                store4<T>(Kr + (2 * tau) * LDA + c0, ev[0] * fi[0], ev[1] * fi[1], ev[2] * fi[2], ev[3] * fi[3]);
+                store4<T>(Kr + (2 * tau + 1) * LDA + c0, kv[0] * fi[0], kv[1] * fi[1], kv[2] * fi[2],
+                          kv[3] * fi[3]);
+                store4<T>(Ql + tau * LDA + c0, qv[0] * f[0], qv[1] * f[1], qv[2] * f[2], qv[3] * f[3]);
             }
-            if ((j >> 4) == (ii >> 4)) Ad[((j >> 4) * 16 + (j & 15)) * ADS + (ii & 15)] = s;
-            else if (ii < j) Abf[j * LDL + ii] = from_f32<T>(s);
-        }
-        for (int idx = tid; idx < C * L; idx += NT) {
-            const int tau = idx / L, ii = idx % L;
-            float s = 0.f;
-            if (ii <= 2 * tau + 1) {
-                const int ti = ii >> 1;
-#pragma unroll 2
-                for (int cc = 0; cc < D; ++cc)
-                    s += to_f32(Ql[tau * LDA + cc]) * to_f32(Kr[ii * LDA + cc]) *
-                         exp2f_(Gs[tau * D + cc] - Gs[ti * D + cc]);
+        };
+        if (act) {
+            glq = *(const f32x4 *)(glc + c0);
+            if (seg == 0) {
+                f32x4 er, lam;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float x = exp2f_(0.5f * glq[j]);
+                    er[j] = wide ? 1.f : x;
+                    lam[j] = wide ? exp2f_(glq[j]) : x;
+                }
+                *(f32x4 *)(wsb + F::oEr + 4 * c0) = er;
+                *(f32x4 *)(wsb + F::oLam + 4 * c0) = lam;
             }
-            gP[tau * LDL + ii] = from_f32<T>(s);
+            if (!wide) {
+                // Kl overwrites the raw alpha rows, which were last read before the vote
+                form_operands();
+            } else {
+#pragma unroll
+                for (int i = 0; i < TPT; ++i)
+                    *(f32x4 *)(Gs + (seg + TPC * i) * D + c0) = f32x4{g[i][0], g[i][1], g[i][2], g[i][3]};
+            }
         }
         __syncthreads();
-        if (wave < NB) invert_diag(wave);
-    }
-    __syncthreads();
 
-    // ---- off-diagonal blocks of (I + A)^{-1}, one column block per wave:
-    //      X_JI = -X_JJ sum_{I <= K < J} A_JK X_KI, for J = I+1, I+2, ...
-    // A 16x16 accumulator (lane: rows 4g..4g+3 of column l%16) is exactly the
-    // B operand of the 16x16x16 instruction, so the X_KI stay in registers.
-    if (wave < NB - 1) {
-        const int I = wave;
-        s16x4 xb[NB];   // X_KI as bf16 B operands (K >= I)
+        // ---- A (strictly lower) and P (causal); diagonal blocks inverted ----------
+        const int mw = wave - NB;   // matrix-wave index (< 0 on the inverse waves)
+        constexpr int NOD = NB * (NB - 1) / 2;
+        constexpr int NPT = NB * (C / 16);
+        if (!wide) {
+            if (wave < NB) {
+                const int J = wave;
+                const f32x4 a = tile_nt<T, D>(Kl + 16 * J * LDA, LDA, Kr + 16 * J * LDA, LDA, zero4(), lane);
 #pragma unroll
-        for (int K = 0; K < NB - 1; ++K)
-            if (K == I) xb[K] = *(const s16x4 *)(MT + (16 * K + l16) * MTW + g4);
-#pragma unroll
-        for (int J = 1; J < NB; ++J) {
-            if (J <= I) continue;
-            f32x4 t = zero4();
-#pragma unroll
-            for (int K = 0; K < J; ++K) {
-                if (K < I) continue;
-                const s16x4 a = *(const s16x4 *)(Abf + (16 * J + l16) * LDL + 16 * K + g4);
-                t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, xb[K], t, 0, 0, 0);
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int jl = g4 + rr;
+                    Ad[(J * 16 + jl) * ADS + l16] = (jl > l16) ? a[rr] : 0.f;
+                }
+                wave_lds_sync();
+                invert_diag(J);
             }
-            const s16x4 tb = __builtin_bit_cast(s16x4, make_uint2(pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])));
-            const s16x4 m = *(const s16x4 *)(MI + (16 * J + l16) * LDL + 16 * J + g4);
-            const f32x4 x = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(m, tb, zero4(), 0, 0, 0);
-            const uint32_t x01 = pack_bf16(-x[0], -x[1]), x23 = pack_bf16(-x[2], -x[3]);
-            xb[J] = __builtin_bit_cast(s16x4, make_uint2(x01, x23));
-            const int a0 = 16 * J + g4, ncol = 16 * I + l16;
-            MI[(a0 + 0) * LDL + ncol] = (T)(x01 & 0xffffu);
-            MI[(a0 + 1) * LDL + ncol] = (T)(x01 >> 16);
-            MI[(a0 + 2) * LDL + ncol] = (T)(x23 & 0xffffu);
-            MI[(a0 + 3) * LDL + ncol] = (T)(x23 >> 16);
+            for (int t = mw; mw >= 0 && t < NOD + NPT; t += NZW) {
+                if (t < NOD) {
+                    int J = 1, I = t;
+                    while (I >= J) { I -= J; ++J; }
+                    const f32x4 a = tile_nt<T, D>(Kl + 16 * J * LDA, LDA, Kr + 16 * I * LDA, LDA, zero4(), lane);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        Abf[(16 * J + g4 + rr) * LDL + 16 * I + l16] = from_f32<T>(a[rr]);
+                } else {
+                    // P^T tile: rows = sub-steps i, cols = tokens; kept for i <= 2 tau + 1
+                    const int I = (t - NOD) / (C / 16), Tb = (t - NOD) % (C / 16);
+                    const int tau = 16 * Tb + l16, i0 = 16 * I + g4;
+                    float w4[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (16 * I <= 32 * Tb + 31) {   // else beyond every token's causal range
+                        const f32x4 a = tile_nt<T, D>(Kr + 16 * I * LDA, LDA, Ql + 16 * Tb * LDA, LDA, zero4(), lane);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) w4[rr] = (i0 + rr <= 2 * tau + 1) ? a[rr] : 0.f;
+                    }
+                    store4<T>(Ps + tau * LDL + i0, w4[0], w4[1], w4[2], w4[3]);
+                }
+            }
+        } else {
+            // exact element-wise path: e^{G_j - G_i} is never split (Kr, Ql hold raw keys)
+            for (int idx = tid; idx < L * L; idx += NT) {
+                const int j = idx / L, ii = idx % L;
+                float s = 0.f;
+                if (ii < j) {
+                    const int tj = j >> 1, ti = ii >> 1;
+#pragma unroll 2
+                    for (int cc = 0; cc < D; ++cc)
+                        s += to_f32(Kr[j * LDA + cc]) * to_f32(Kr[ii * LDA + cc]) *
+                             exp2f_(Gs[tj * D + cc] - Gs[ti * D + cc]);
+                    s *= bp[j];
+                }
+                if ((j >> 4) == (ii >> 4)) Ad[((j >> 4) * 16 + (j & 15)) * ADS + (ii & 15)] = s;
+                else if (ii < j) Abf[j * LDL + ii] = from_f32<T>(s);
+            }
+            for (int idx = tid; idx < C * L; idx += NT) {
+                const int tau = idx / L, ii = idx % L;
+                float s = 0.f;
+                if (ii <= 2 * tau + 1) {
+                    const int ti = ii >> 1;
+#pragma unroll 2
+                    for (int cc = 0; cc < D; ++cc)
+                        s += to_f32(Ql[tau * LDA + cc]) * to_f32(Kr[ii * LDA + cc]) *
+                             exp2f_(Gs[tau * D + cc] - Gs[ti * D + cc]);
+                }
+                Ps[tau * LDL + ii] = from_f32<T>(s);
+            }
+            __syncthreads();
+            if (wave < NB) invert_diag(wave);
+            // every read of G and of the raw keys is done: form the operands in place
+            if (act) form_operands();
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- (I + A)^{-1} -> workspace (only its lower blocks are ever read) --------
-    for (int idx = tid; idx < L * LDL / 8; idx += NT)
-        ((uint4 *)gMI)[idx] = ((const uint4 *)MI)[idx];
+        // ---- off-diagonal blocks of (I + A)^{-1}, one column block per wave:
+        //      X_JI = -X_JJ sum_{I <= K < J} A_JK X_KI, for J = I+1, I+2, ...
+        // A 16x16 accumulator (lane: rows 4g..4g+3 of column l%16) is exactly the
+        // B operand of the 16x16x16 instruction, so the X_KI stay in registers.
+        if (wave < NB - 1) {
+            const int I = wave;
+            s16x4 xb[NB];   // X_KI as bf16 B operands (K >= I)
+#pragma unroll
+            for (int K = 0; K < NB - 1; ++K)
+                if (K == I) xb[K] = *(const s16x4 *)(MT + (16 * K + l16) * MTW + g4);
+#pragma unroll
+            for (int J = 1; J < NB; ++J) {
+                if (J <= I) continue;
+                f32x4 t = zero4();
+#pragma unroll
+                for (int K = 0; K < J; ++K) {
+                    if (K < I) continue;
+                    const s16x4 a = *(const s16x4 *)(Abf + (16 * J + l16) * LDL + 16 * K + g4);
+                    t = mma16(a, xb[K], t);
+                }
+                const s16x4 tb = __builtin_bit_cast(s16x4, make_uint2(pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])));
+                const s16x4 m = *(const s16x4 *)(MI + (16 * J + l16) * LDL + 16 * J + g4);
+                const f32x4 x = mma16(m, tb, zero4());
+                const uint32_t x01 = pack_bf16(-x[0], -x[1]), x23 = pack_bf16(-x[2], -x[3]);
+                xb[J] = __builtin_bit_cast(s16x4, make_uint2(x01, x23));
+                const int a0 = 16 * J + g4, ncol = 16 * I + l16;
+                MI[(a0 + 0) * LDL + ncol] = (T)(x01 & 0xffffu);
+                MI[(a0 + 1) * LDL + ncol] = (T)(x01 >> 16);
+                MI[(a0 + 2) * LDL + ncol] = (T)(x23 & 0xffffu);
+                MI[(a0 + 3) * LDL + ncol] = (T)(x23 >> 16);
+            }
+        }
+        __syncthreads();
+
+        // ---- W^T = Kl^T Diag(b') M^T tiles (kept in registers); Kr^T, Ql, P and T'
+        //      fragments -> workspace ------------------------------------------------
+        f32x4 wacc[WPW];
+#pragma unroll
+        for (int m = 0; m < WPW; ++m) {
+            const int t = wave + NW * m;
+            wacc[m] = zero4();
+            if (t < NWT) {
+                const int jb = t / NBD, nb = t % NBD;
+                // M's row block jb is zero beyond column 16 (jb + 1); round up to 32
+                const int K = 32 * ((jb + 2) / 2);
+                f32x4 acc = zero4();
+                for (int k0 = 0; k0 < K; k0 += 32)
+                    acc = mma32(frag_col(Kl + k0 * LDA + 16 * nb, LDA, lane),
+                                frag_row(MI + 16 * jb * LDL + k0, LDL, lane), acc);
+                wacc[m] = acc;
+            }
+        }
+        {
+            constexpr int NKR = NBD * KSL, NQL = NBC * KSD, NPF = NBC * KSL, NEX = NKR + NQL + NPF + NBL;
+            for (int f = wave; f < NEX; f += NW) {
+                if (f < NKR) {
+                    const int rb = f / KSL, ks = f % KSL;
+                    st_frag(wsb + F::oKr + (f * 64 + lane) * 16, frag_col(Kr + 32 * ks * LDA + 16 * rb, LDA, lane));
+                } else if (f < NKR + NQL) {
+                    const int ff = f - NKR, rb = ff / KSD, ks = ff % KSD;
+                    st_frag(wsb + F::oQl + (ff * 64 + lane) * 16, frag_row(Ql + 16 * rb * LDA + 32 * ks, LDA, lane));
+                } else if (f < NKR + NQL + NPF) {
+                    const int ff = f - NKR - NQL, rb = ff / KSL, ks = ff % KSL;
+                    st_frag(wsb + F::oP + (ff * 64 + lane) * 16, frag_row(Ps + 16 * rb * LDL + 32 * ks, LDL, lane));
+                } else {
+                    // T'[j][tau] = M[j][2 tau + 1] beta_tau (tau >= C: zero)
+                    const int rb = f - NKR - NQL - NPF, gg = lane >> 4;
+                    const T *mrow = MI + (16 * rb + l16) * LDL;
+                    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+                    if (8 * gg < C) {
+                        const uint4 u0 = *(const uint4 *)(mrow + 16 * gg);
+                        const uint4 u1 = *(const uint4 *)(mrow + 16 * gg + 8);
+                        const f32x4 b0 = *(const f32x4 *)(sb + 8 * gg), b1 = *(const f32x4 *)(sb + 8 * gg + 4);
+                        x = make_uint4(pack_bf16(hi_bf16(u0.x) * b0[0], hi_bf16(u0.y) * b0[1]),
+                                       pack_bf16(hi_bf16(u0.z) * b0[2], hi_bf16(u0.w) * b0[3]),
+                                       pack_bf16(hi_bf16(u1.x) * b1[0], hi_bf16(u1.y) * b1[1]),
+                                       pack_bf16(hi_bf16(u1.z) * b1[2], hi_bf16(u1.w) * b1[3]));
+                    }
+                    *(uint4 *)(wsb + F::oTv + (rb * 64 + lane) * 16) = x;
+                }
+            }
+        }
+        __syncthreads();   // the Kr region is free: stage -W there
+
+        // accumulator of W^T tile (nb, jb): lane holds W[16 jb + l16][16 nb + g4 + i]
+#pragma unroll
+        for (int m = 0; m < WPW; ++m) {
+            const int t = wave + NW * m;
+            if (t < NWT) {
+                const int jb = t / NBD, nb = t % NBD;
+                store4<T>(Wst + (16 * jb + l16) * LDA + 16 * nb + g4, -wacc[m][0], -wacc[m][1],
+                          -wacc[m][2], -wacc[m][3]);
+            }
+        }
+        __syncthreads();
+        for (int f = wave; f < NBL * KSD; f += NW) {
+            const int rb = f / KSD, ks = f % KSD;
+            st_frag(wsb + F::oWn + (f * 64 + lane) * 16, frag_row(Wst + 16 * rb * LDA + 32 * ks, LDA, lane));
+        }
+        __syncthreads();   // LDS free for the next item
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Kernel 2: state pass.  One workgroup per (head, BV-column slice); the
 // slices of one head get workgroup ids congruent mod 8 (same XCD, one L2 for
 // the shared factor blocks).
+//
+// Wave roles (per chunk): waves [0, L/16) each own a 16-row block of U
+// (U = T' V - W S'); waves [8 - C/16, 8) each own a 16-token block of the
+// outputs (o = Ql S' + P U, computed transposed so the stores are row runs);
+// the waves in between move the value slice in and the outputs out; waves
+// [0, D/16) each own a 16-row block of the state.  Every wave keeps the
+// operands of its roles for three chunks in registers (current, next, and
+// the one being fetched).
 // ---------------------------------------------------------------------------
-template <int C, int D, int BV, int NW>
-struct K2Geom {
-    using F = FacLayout<C, D>;
-    static constexpr int L = 2 * C, NB = L / 16, NT = 64 * NW;
-    static constexpr int LDA = D + 8, LDL = L + 8, LDO = BV + 8;
-    static constexpr int FB = F::bytes;                       // factor block
-    static constexpr int NFU = FB / 16;                       // its 16-byte units
-    static constexpr int VB = C * BV * 2, NVU = VB / 16;      // value slice of a chunk
-    static constexpr int NU = NFU + NVU, UPT = (NU + NT - 1) / NT;   // prefetch units per thread
-    static constexpr int NYT = NB * (BV / 16), YPW = (NYT + NW - 1) / NW;   // Z / U tiles
-    static constexpr int NOT = (BV / 16) * (C / 16), OPW = (NOT + NW - 1) / NW;  // output tiles
-    static constexpr int NST = (D / 16) * (BV / 16), SPW = (NST + NW - 1) / NW;  // state tiles
-    static constexpr int szSt = align16(BV * LDA * 2), szVs = align16(VB);
-    static constexpr int szZt = align16(BV * LDL * 2), szOs = align16(C * LDO * 2);
-    static constexpr int oBuf = 0, oSt = 2 * FB, oVs = oSt + szSt, oZt = oVs + 2 * szVs;
-    static constexpr int oUt = oZt + szZt, oOs = oUt + szZt;
-    static constexpr int LDS = oOs + szOs;
-    static_assert(LDS <= 160 * 1024, "LDS budget exceeded");
-    static_assert(VB % 16 == 0, "value slice in 16-byte units");
+template <int C, int D, int BV>
+struct K2G {
+    using F = Fac<C, D>;
+    static constexpr int NW = NWAVES, NT = NTHREADS, L = 2 * C;
+    static constexpr int NBL = F::NBL, NBC = F::NBC, NBD = F::NBD, NCB = BV / 16;
+    static constexpr int KSD = F::KSD, KSL = F::KSL;
+    static constexpr int NR = KSD + KSL;               // role operands per chunk
+    static constexpr int O0 = NW - NBC;                // first output wave
+    static constexpr int H0 = NBL, NH = O0 - NBL;      // value / output movers
+    static constexpr int VU = C * BV / 8;              // 16-byte units of a value (or output) slice
+    static_assert(NH >= 1 && VU <= 64 * NH, "mover waves");
+    static_assert(NBD <= NW, "one state row block per wave");
+    static constexpr int LDT = D + 8, LDU = L + 8, LDV = BV + 8, LDO = BV + 8;
+    static constexpr int oSt = 0;                                   // S'^T [BV][LDT] bf16
+    static constexpr int oUt = align16(oSt + BV * LDT * 2);         // U^T  [BV][LDU] bf16
+    static constexpr int VR = 32;                                   // value rows (>= C; rows >= C stay zero)
+    static constexpr int szVs = align16(VR * LDV * 2);
+    static constexpr int oVs = align16(oUt + BV * LDU * 2);         // V    [2][VR][LDV] bf16
+    static constexpr int oOs = oVs + 2 * szVs;                      // o    [C][LDO] bf16
+    static constexpr int LDS = align16(oOs + C * LDO * 2);
 };
 
-template <int C, int D, int BV, int NW>
-__global__ void __launch_bounds__(64 * NW)
+template <int NR, int KSL>
+struct FragSet {
+    bf16x8 R[NR];   // role operands: -W and T' (U waves), Ql and P (output waves), v (movers)
+    bf16x8 K[KSL];  // Kr^T row block (state waves)
+    f32x4 er, lm;   // scales of the state rows
+};
+
+template <int C, int D, int BV>
+__global__ void __launch_bounds__(NTHREADS)
 eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16 *__restrict__ o,
                const char *__restrict__ ws, int Tlen, int H, int BH, int dk, int dv, int NC, int R,
-               int vvec) {
-    using G = K2Geom<C, D, BV, NW>;
-    using F = FacLayout<C, D>;
+               int vvec, int ovec) {
+    using G = K2G<C, D, BV>;
+    using F = Fac<C, D>;
     using T = bf16;
-    constexpr int L = G::L, NT = G::NT, LDA = G::LDA, LDL = G::LDL, LDO = G::LDO, FB = G::FB;
-    constexpr int NFU = G::NFU, NU = G::NU, UPT = G::UPT;
-    constexpr int NYT = G::NYT, YPW = G::YPW, NOT = G::NOT, OPW = G::OPW, NST = G::NST, SPW = G::SPW;
+    constexpr int NCB = G::NCB, KSD = G::KSD, KSL = G::KSL, LDT = G::LDT, LDU = G::LDU;
+    constexpr int LDV = G::LDV, LDO = G::LDO, VU = G::VU, O0 = G::O0;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    T *St = (T *)(smem + G::oSt);   // S'^T (bf16 operand) [BV][LDA]
-    T *Zt = (T *)(smem + G::oZt);   // Z^T (bf16)          [BV][LDL]
-    T *Ut = (T *)(smem + G::oUt);   // U^T (bf16)          [BV][LDL]
-    T *Os = (T *)(smem + G::oOs);   // outputs awaiting their store [C][LDO]
+    T *St = (T *)(smem + G::oSt);
+    T *Ut = (T *)(smem + G::oUt);
+    T *Os = (T *)(smem + G::oOs);
 
     const int w = blockIdx.x, xcd = w & 7, slot = w >> 3;
     const int bh = (slot / R) * 8 + xcd, slice = slot % R;
@@ -501,212 +658,197 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
     const int b = bh / H, h = bh % H, n0 = slice * BV;
     const long sbase = (long)bh * dk * dv;
     const long hrow = (long)b * Tlen * H + h;
-    const int HV = H * dv;
-    const bf16 *vh = v + hrow * dv + n0;
-    const char *wsh = ws + (long)bh * NC * FB;
+    const long HV = (long)H * dv;
+    const T *vh = v + hrow * dv + n0;
+    T *oh = o + hrow * dv + n0;
+    const char *wsh = ws + (long)bh * NC * F::bytes;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = 4 * (lane >> 4), l16 = lane & 15;
+    const bool uw = wave < G::NBL, ow = wave >= O0, mv = !uw && !ow, sw = wave < G::NBD;
+    const int mu = (wave - G::H0) * 64 + lane;             // mover unit
+    const int mtau = mu / (BV / 8), mn = 8 * (mu % (BV / 8));
 
-    // ---- prefetch of one chunk: factor block + value slice, 16-byte units -----
-    uint4 pre[UPT];
-    auto load_chunk = [&](int cidx) {
-        const uint4 *src = (const uint4 *)(wsh + (long)cidx * FB);
-        const int t0 = cidx * C, nval = min(C, Tlen - t0);
+    using Set = FragSet<G::NR, KSL>;
+    auto load_set = [&](Set &s, int c) __attribute__((always_inline)) {
+        const char *blk = wsh + (long)c * F::bytes;
+        if (uw) {
 #pragma unroll
-        for (int m = 0; m < UPT; ++m) {
-            const int u = tid + NT * m;
-            if (u < NFU) {
-                pre[m] = src[u];
-            } else if (u < NU) {
-                const int vu = u - NFU, tau = vu / (BV / 8), n = 8 * (vu % (BV / 8));
-                if (vvec && tau < nval && n0 + n + 8 <= dv) {
-                    pre[m] = *(const uint4 *)(vh + (t0 + tau) * HV + n);
+            for (int ks = 0; ks < KSD; ++ks)
+                s.R[ks] = ld_frag(blk + F::oWn + ((wave * KSD + ks) * 64 + lane) * 16);
+            s.R[KSD] = ld_frag(blk + F::oTv + (wave * 64 + lane) * 16);
+        } else if (ow) {
+            const int ob = wave - O0;
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+                s.R[ks] = ld_frag(blk + F::oQl + ((ob * KSD + ks) * 64 + lane) * 16);
+#pragma unroll
+            for (int ks = 0; ks < KSL; ++ks)
+                s.R[KSD + ks] = ld_frag(blk + F::oP + ((ob * KSL + ks) * 64 + lane) * 16);
+        } else {
+            uint4 x = make_uint4(0u, 0u, 0u, 0u);
+            const int t = c * C + mtau;
+            if (mu < VU && t < Tlen) {
+                const T *src = vh + t * HV + mn;
+                if (vvec && n0 + mn + 8 <= dv) {
+                    x = *(const uint4 *)src;
                 } else {
-                    uint32_t x[8];
+                    uint32_t y[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        x[j] = (tau < nval && n0 + n + j < dv) ? vh[(t0 + tau) * HV + n + j] : 0u;
-                    pre[m] = make_uint4(x[0] | (x[1] << 16), x[2] | (x[3] << 16), x[4] | (x[5] << 16),
-                                        x[6] | (x[7] << 16));
+                    for (int j = 0; j < 8; ++j) y[j] = (n0 + mn + j < dv) ? src[j] : 0u;
+                    x = make_uint4(y[0] | (y[1] << 16), y[2] | (y[3] << 16), y[4] | (y[5] << 16), y[6] | (y[7] << 16));
                 }
             }
+            s.R[0] = __builtin_bit_cast(bf16x8, x);
         }
-    };
-    auto store_chunk = [&](int cidx) {
-        char *buf = smem + G::oBuf + (cidx & 1) * FB;
-        char *vs = smem + G::oVs + (cidx & 1) * G::szVs;
+        if (sw) {
 #pragma unroll
-        for (int m = 0; m < UPT; ++m) {
-            const int u = tid + NT * m;
-            if (u < NFU) ((uint4 *)buf)[u] = pre[m];
-            else if (u < NU) ((uint4 *)vs)[u - NFU] = pre[m];
+            for (int ks = 0; ks < KSL; ++ks)
+                s.K[ks] = ld_frag(blk + F::oKr + ((wave * KSL + ks) * 64 + lane) * 16);
+            s.er = *(const f32x4 *)(blk + F::oEr + 4 * (16 * wave + g4));
+            s.lm = *(const f32x4 *)(blk + F::oLam + 4 * (16 * wave + g4));
         }
     };
-    auto flush_outputs = [&](int cprev) {
-        const int tp0 = cprev * C, nv = min(C, Tlen - tp0);
-        for (int idx = tid; idx < C * (BV / 4); idx += NT) {
-            const int tau = idx / (BV / 4), n = 4 * (idx % (BV / 4));
-            if (tau >= nv) continue;
-            const uint2 val = *(const uint2 *)(Os + tau * LDO + n);
-            T *op = o + (hrow + (long)(tp0 + tau) * H) * dv + n0 + n;
-            if ((dv & 3) == 0 && n0 + n + 3 < dv) {
-                *(uint2 *)op = val;
+    auto put_v = [&](const Set &s, int c) __attribute__((always_inline)) {
+        if (mu < VU)
+            *(uint4 *)((T *)(smem + G::oVs + (c & 1) * G::szVs) + mtau * LDV + mn) = __builtin_bit_cast(uint4, s.R[0]);
+    };
+    auto flush = [&](int cp) __attribute__((always_inline)) {
+        const int t = cp * C + mtau;
+        if (mu < VU && t < Tlen) {
+            const uint4 val = *(const uint4 *)(Os + mtau * LDO + mn);
+            T *dst = oh + t * HV + mn;
+            if (ovec && n0 + mn + 8 <= dv) {
+                *(uint4 *)dst = val;
             } else {
-                const T vv[4] = {(T)(val.x & 0xffffu), (T)(val.x >> 16), (T)(val.y & 0xffffu), (T)(val.y >> 16)};
+                const uint32_t y[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    if (n0 + n + rr < dv) op[rr] = vv[rr];
-            }
-        }
-    };
-    // S'^T = (Diag(e^r) S)^T for chunk cidx, the bf16 operand of its products
-    f32x4 S[SPW];
-    auto write_St = [&](int cidx) {
-        const float *erS = (const float *)(smem + G::oBuf + (cidx & 1) * FB + F::oErS);
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int t = wave + NW * m;
-            if (t < NST) {
-                const int rb = t / (BV / 16), cb = t % (BV / 16);
-                const f32x4 sc = *(const f32x4 *)(erS + 16 * rb + g4);
-                store4<T>(St + (16 * cb + l16) * LDA + 16 * rb + g4, sc[0] * S[m][0], sc[1] * S[m][1],
-                          sc[2] * S[m][2], sc[3] * S[m][3]);
+                for (int j = 0; j < 8; ++j)
+                    if (n0 + mn + j < dv) dst[j] = (T)((y[j >> 1] >> (16 * (j & 1))) & 0xffffu);
             }
         }
     };
 
-    // ---- initial state (fp32, accumulator layout), first chunk -------------------
+    // ---- initial state: rows 16 wave + g4 + i, columns n0 + 16 cb + l16 --------
+    f32x4 S[NCB];
 #pragma unroll
-    for (int m = 0; m < SPW; ++m) {
-        S[m] = zero4();
-        const int t = wave + NW * m;
-        if (t < NST && S0) {
-            const int rb = t / (BV / 16), cb = t % (BV / 16);
+    for (int cb = 0; cb < NCB; ++cb) {
+        S[cb] = zero4();
+        if (sw && S0) {
             const int col = n0 + 16 * cb + l16;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int rw = 16 * rb + g4 + rr;
-                if (rw < dk && col < dv) S[m][rr] = S0[sbase + (long)rw * dv + col];
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * wave + g4 + i;
+                if (row < dk && col < dv) S[cb][i] = S0[sbase + (long)row * dv + col];
             }
         }
     }
-    load_chunk(0);
-    store_chunk(0);
-    if (NC > 1) load_chunk(1);
-    __syncthreads();
-    write_St(0);
-
-    for (int cidx = 0; cidx < NC; ++cidx) {
-        const char *buf = smem + G::oBuf + (cidx & 1) * FB;
-        const T *Kl = (const T *)(buf + F::oKl), *Kr = (const T *)(buf + F::oKr);
-        const T *Ql = (const T *)(buf + F::oQl), *MI = (const T *)(buf + F::oMI);
-        const T *Pm = (const T *)(buf + F::oP);
-        const float *lam1 = (const float *)(buf + F::oLam), *sK = (const float *)(buf + F::oSK);
-        const float *bp = (const float *)(buf + F::oBp);
-        const T *Vs = (const T *)(smem + G::oVs + (cidx & 1) * G::szVs);
-        __syncthreads();   // S' of this chunk and its factor block are in place
-
-        // ---- the next chunk's block goes to the other buffer (its previous
-        //      readers finished before the barrier above); the previous chunk's
-        //      outputs are stored before the loads are issued, so every later
-        //      wait is on operations issued a whole chunk earlier
-        if (cidx + 1 < NC) store_chunk(cidx + 1);
-        if (cidx > 0) flush_outputs(cidx - 1);
-        if (cidx + 2 < NC) load_chunk(cidx + 2);
-
-        // ---- Z = Diag(b') (N - Kl S') ; the state-independent half of o, Ql S' ---
-        f32x4 ZR[YPW];   // fp32 rounding residual of Z, added back in the U product
+    auto write_St = [&](const f32x4 &er) __attribute__((always_inline)) {
 #pragma unroll
-        for (int m = 0; m < YPW; ++m) {
-            const int t = wave + NW * m;
-            ZR[m] = zero4();
-            if (t < NYT) {
-                const int jb = t / (BV / 16), nb = t % (BV / 16);
-                const f32x4 y = tile_nt<T, D>(Kl + 16 * jb * LDA, LDA, St + 16 * nb * LDA, LDA, zero4(), lane);
-                float z[4];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int j = 16 * jb + g4 + rr;
-                    const float nv = (j & 1) ? to_f32(Vs[(j >> 1) * BV + 16 * nb + l16]) : 0.f;
-                    z[rr] = bp[j] * (nv - y[rr]);
-                }
-                const uint32_t z01 = pack_bf16(z[0], z[1]), z23 = pack_bf16(z[2], z[3]);
-                *(uint2 *)(Zt + (16 * nb + l16) * LDL + 16 * jb + g4) = make_uint2(z01, z23);
-                ZR[m] = f32x4{z[0] - lo_bf16(z01), z[1] - hi_bf16(z01), z[2] - lo_bf16(z23), z[3] - hi_bf16(z23)};
-            }
+        for (int cb = 0; cb < NCB; ++cb)
+            store4<T>(St + (16 * cb + l16) * LDT + 16 * wave + g4, er[0] * S[cb][0], er[1] * S[cb][1],
+                      er[2] * S[cb][2], er[3] * S[cb][3]);
+    };
+
+    if constexpr (C < G::VR) {
+        // the value rows beyond the chunk are read by the k = 32 product: zero them
+        for (int idx = tid; idx < 2 * (G::VR - C) * LDV; idx += G::NT) {
+            const int bsel = idx / ((G::VR - C) * LDV), rem = idx % ((G::VR - C) * LDV);
+            ((T *)(smem + G::oVs + bsel * G::szVs))[C * LDV + rem] = (T)0;
         }
-        f32x4 OA[OPW];
-#pragma unroll
-        for (int m = 0; m < OPW; ++m) {
-            const int t = (NW - 1 - wave) + NW * m;   // start on the waves with the fewest Z tiles
-            OA[m] = zero4();
-            if (t < NOT) {
-                const int nb = t / (C / 16), tb = t % (C / 16);
-                OA[m] = tile_nt<T, D>(St + 16 * nb * LDA, LDA, Ql + 16 * tb * LDA, LDA, zero4(), lane);
-            }
-        }
-        __syncthreads();
+    }
 
-        // ---- U = (I + A)^{-1} Z ----------------------------------------------------
-#pragma unroll
-        for (int m = 0; m < YPW; ++m) {
-            const int t = wave + NW * m;
-            if (t < NYT) {
-                const int jb = t / (BV / 16), nb = t % (BV / 16);
-                const f32x4 u = tile_nt_dyn<T>(MI + 16 * jb * LDL, LDL, Zt + 16 * nb * LDL, LDL,
-                                               16 * (jb + 1), ZR[m], lane);
-                store4<T>(Ut + (16 * nb + l16) * LDL + 16 * jb + g4, u[0], u[1], u[2], u[3]);
-            }
-        }
-        __syncthreads();
+    Set A, B, X;
+    load_set(A, 0);
+    if (NC > 1) load_set(B, 1);
+    if (mv) put_v(A, 0);
+    if (sw) write_St(A.er);
 
-        // ---- o = Ql S' + P U ; S <- e^r (e^r S + Kr^T U) ; S' of the next chunk ------
-#pragma unroll
-        for (int m = 0; m < OPW; ++m) {
-            const int t = (NW - 1 - wave) + NW * m;
-            if (t < NOT) {
-                const int nb = t / (C / 16), tb = t % (C / 16);
-                const f32x4 a = tile_nt_dyn<T>(Ut + 16 * nb * LDL, LDL, Pm + 16 * tb * LDL, LDL,
-                                               min(L, 32 * (tb + 1)), OA[m], lane);
-                store4<T>(Os + (16 * tb + l16) * LDO + 16 * nb + g4, a[0], a[1], a[2], a[3]);
-            }
+    auto body = [&](Set &cur, Set &nxt, Set &fut, int c) __attribute__((always_inline)) {
+        __syncthreads();   // S'^T, the value slice of chunk c and the last outputs are in LDS
+        if (c + 2 < NC) load_set(fut, c + 2);
+        if (mv) {
+            if (c > 0) flush(c - 1);
+            if (c + 1 < NC) put_v(nxt, c + 1);
         }
+        f32x4 acc[NCB];
+        if (uw) {
+            // U = T' V - W S'  (rows 16 wave.., all slice columns) -> U^T in LDS
+            const T *Vs = (const T *)(smem + G::oVs + (c & 1) * G::szVs);
+            // (one instruction shape for the whole accumulation chain: at C = 16
+            // the k = 32 product reads 16 zero rows of the value buffer)
 #pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int t = wave + NW * m;
-            if (t < NST) {
-                const int rb = t / (BV / 16), cb = t % (BV / 16);
-                const f32x4 lm = *(const f32x4 *)(lam1 + 16 * rb + g4);
-                const f32x4 sk = *(const f32x4 *)(sK + 16 * rb + g4);
+            for (int cb = 0; cb < NCB; ++cb)
+                acc[cb] = mma32(cur.R[KSD], frag_col(Vs + 16 * cb, LDV, lane), zero4());
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[cb] = mma32(cur.R[ks], frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), acc[cb]);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                store4<T>(Ut + (16 * cb + l16) * LDU + 16 * wave + g4, acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
+        } else if (ow) {
+            // o^T = S'^T Ql^T for the wave's 16 tokens (first half)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[cb] = mma32(frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), cur.R[ks], acc[cb]);
+        }
+        __syncthreads();   // U^T complete; S'^T no longer read
+        if (sw) {
+            // S <- e^r (lam S + Kr^T U); S'^T of the next chunk
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
                 f32x4 a;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) a[rr] = lm[rr] * S[m][rr];
-                a = tile_tn_bf16<L>(Kr + 16 * rb, LDA, Ut + 16 * cb * LDL, LDL, a, lane);
+                for (int i = 0; i < 4; ++i) a[i] = cur.lm[i] * S[cb][i];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) S[m][rr] = sk[rr] * a[rr];
+                for (int ks = 0; ks < KSL; ++ks)
+                    a = mma32(cur.K[ks], frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), a);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[cb][i] = cur.er[i] * a[i];
             }
+            if (c + 1 < NC) write_St(nxt.er);
         }
-        // St is read only by the Z and Ql S' products, before the previous barrier
-        if (cidx + 1 < NC) write_St(cidx + 1);
+        if (ow) {
+            // o^T += U^T P^T; rows of o -> LDS
+#pragma unroll
+            for (int ks = 0; ks < KSL; ++ks)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[cb] = mma32(frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), cur.R[KSD + ks], acc[cb]);
+            const int tr = 16 * (wave - O0) + l16;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                store4<T>(Os + tr * LDO + 16 * cb + g4, acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
+        }
+    };
+
+    int c = 0;
+    for (; c + 3 <= NC; c += 3) {
+        body(A, B, X, c);
+        body(B, X, A, c + 1);
+        body(X, A, B, c + 2);
     }
+    if (c < NC) body(A, B, X, c);
+    if (c + 1 < NC) body(B, X, A, c + 1);
 
     __syncthreads();
-    flush_outputs(NC - 1);
-    if (S_final) {
+    if (mv) flush(NC - 1);
+    if (S_final && sw) {
         // every read of S0 happened before the chunk loop, so S_final may be S0
 #pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int t = wave + NW * m;
-            if (t < NST) {
-                const int rb = t / (BV / 16), cb = t % (BV / 16);
-                const int col = n0 + 16 * cb + l16;
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int col = n0 + 16 * cb + l16;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int rw = 16 * rb + g4 + rr;
-                    if (rw < dk && col < dv) S_final[sbase + (long)rw * dv + col] = S[m][rr];
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * wave + g4 + i;
+                if (row < dk && col < dv) S_final[sbase + (long)row * dv + col] = S[cb][i];
             }
         }
     }
@@ -715,8 +857,6 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-constexpr int NWAVES = 8;
-
 static int pad_dim(int dk, int dv) {
     const int p = dk > dv ? dk : dv;
     return p <= 32 ? 32 : (p <= 64 ? 64 : 128);
@@ -733,35 +873,42 @@ static int slice_width(int BH, int D) {
 
 template <int C, int D>
 size_t ws_bytes(int B, int Tlen, int H) {
-    return (size_t)B * H * ((Tlen + C - 1) / C) * FacLayout<C, D>::bytes;
+    return (size_t)B * H * ((Tlen + C - 1) / C) * Fac<C, D>::bytes;
 }
 
 template <int C, int D, int BV>
 hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, const float *alpha,
                     const float *beta, const float *gamma, const float *S0, void *o, float *S_final,
                     int B, int Tlen, int H, int dk, int dv, void *ws, hipStream_t stream) {
-    using G1 = K1Geom<C, D, NWAVES>;
-    using G2 = K2Geom<C, D, BV, NWAVES>;
+    using G1 = K1G<C, D>;
+    using G2 = K2G<C, D, BV>;
     const int NC = (Tlen + C - 1) / C, BH = B * H;
     // 16-byte loads of whole rows need d_k == D and 16-byte aligned bases
     // (D is a multiple of 8, so every row start stays aligned)
     const int vec = (dk == D) && ((uintptr_t)q % 16 == 0) && ((uintptr_t)k % 16 == 0) &&
                     ((uintptr_t)e % 16 == 0) && ((uintptr_t)alpha % 16 == 0);
     const int vvec = (dv % 8 == 0) && ((uintptr_t)v % 16 == 0);
-    auto k1 = eda_bf16_factors<C, D, NWAVES>;
-    auto k2 = eda_bf16_state<C, D, BV, NWAVES>;
+    const int ovec = (dv % 8 == 0) && ((uintptr_t)o % 16 == 0);
+    auto k1 = eda_bf16_factors<C, D>;
+    auto k2 = eda_bf16_state<C, D, BV>;
     hipError_t err = hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, G1::LDS);
     if (err != hipSuccess) return err;
-    err = hipFuncSetAttribute((const void *)k2, hipFuncAttributeMaxDynamicSharedMemorySize, G2::LDS);
+    int dev = 0, ncu = 256;
+    err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k1, dim3((unsigned)(BH * NC)), dim3(G1::NT), G1::LDS, stream, (const bf16 *)q,
-                       (const bf16 *)k, (const bf16 *)e, alpha, beta, gamma, (char *)ws, Tlen, H, dk, NC, vec);
+    err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    const long items = (long)BH * NC;
+    const int grid1 = (int)(items < 2L * ncu ? items : 2L * ncu);   // two per compute unit (LDS)
+    hipLaunchKernelGGL(k1, dim3((unsigned)grid1), dim3(G1::NT), G1::LDS, stream, (const bf16 *)q,
+                       (const bf16 *)k, (const bf16 *)e, alpha, beta, gamma, (char *)ws, Tlen, H, dk, NC,
+                       BH, vec);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int R = (dv + BV - 1) / BV;
-    const int grid = 8 * ((BH + 7) / 8) * R;
-    hipLaunchKernelGGL(k2, dim3((unsigned)grid), dim3(G2::NT), G2::LDS, stream, (const bf16 *)v, S0,
-                       S_final, (bf16 *)o, (const char *)ws, Tlen, H, BH, dk, dv, NC, R, vvec);
+    const int grid2 = 8 * ((BH + 7) / 8) * R;
+    hipLaunchKernelGGL(k2, dim3((unsigned)grid2), dim3(G2::NT), G2::LDS, stream, (const bf16 *)v, S0,
+                       S_final, (bf16 *)o, (const char *)ws, Tlen, H, BH, dk, dv, NC, R, vvec, ovec);
     return hipGetLastError();
 }
 
