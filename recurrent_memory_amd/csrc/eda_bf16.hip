@@ -47,6 +47,8 @@
 // (16 rb, 32 ks): 64 lanes x 16 bytes, lane 16 g + r holding
 // M[16 rb + r][32 ks + 8 g .. 32 ks + 8 g + 7] -- the operand layout of the
 // 16x16x32 bf16 matrix instruction.
+#include <type_traits>
+
 #include "eda_common.h"
 
 namespace eda {
@@ -164,8 +166,8 @@ struct K1G {
     static constexpr int NZW = NW - NB;                // matrix waves (A and P tiles)
     static_assert(NZW >= 1, "too few waves");
     // raw rows of one full chunk in 16-byte units: q, e, k (bf16), alpha (fp32)
-    static constexpr int RU = C * D / 8, AU = C * D / 4, NRAW = 3 * RU + AU;
-    static constexpr int PF = (NRAW + NT - 1) / NT;
+    static constexpr int RU = C * D / 8, AU = C * D / 4;
+    static constexpr int PQ = (RU + NT - 1) / NT, PA = (AU + NT - 1) / NT;
     // W^T tiles per wave
     static constexpr int NWT = F::NBD * F::NBL, WPW = (NWT + NW - 1) / NW;
     // LDS (bytes).  Before the operands are formed, Kl holds the raw alpha
@@ -184,18 +186,21 @@ struct K1G {
     static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
 };
 
-template <int C, int D>
+// VEC: d_k == D and 16-byte aligned q, k, e, alpha (whole rows move as
+// 16-byte pieces and are fetched one item ahead); otherwise every item is
+// read element-wise with zero padding.
+template <int C, int D, bool VEC>
 __global__ void __launch_bounds__(NTHREADS)
 eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ e,
                  const float *__restrict__ alpha, const float *__restrict__ beta,
                  const float *__restrict__ gamma, char *__restrict__ ws, int Tlen, int H, int dk,
-                 int NC, int BH, int vec) {
+                 int NC, int BH) {
     using G = K1G<C, D>;
     using F = Fac<C, D>;
     using T = bf16;
     constexpr int L = G::L, NB = G::NB, NT = G::NT, NW = G::NW, LDA = G::LDA, LDL = G::LDL;
     constexpr int ADS = G::ADS, ASD = G::ASD, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT, NZW = G::NZW;
-    constexpr int RU = G::RU, NRAW = G::NRAW, PF = G::PF, WPW = G::WPW, NWT = G::NWT;
+    constexpr int RU = G::RU, AU = G::AU, PQ = G::PQ, PA = G::PA, WPW = G::WPW, NWT = G::NWT;
     constexpr int NBD = F::NBD, NBL = F::NBL, NBC = F::NBC, KSD = F::KSD, KSL = F::KSL;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Kl = (T *)(smem + G::oKl);            // Diag(b') Kl              [L][LDA]
@@ -228,31 +233,37 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 
     auto chunk_of = [&](int it) __attribute__((always_inline)) { return NC - 1 - it / BH; };
     auto head_of = [&](int it) __attribute__((always_inline)) { return it % BH; };
-    auto is_fast = [&](int cidx) __attribute__((always_inline)) { return vec != 0 && cidx * C + C <= Tlen; };
+    auto is_fast = [&](int cidx) __attribute__((always_inline)) { return VEC && cidx * C + C <= Tlen; };
 
-    // ---- raw rows of a full chunk -> registers (fetched one item ahead) ---------
-    uint4 pre[PF];
+    // ---- raw rows of a chunk -> registers, fetched one item ahead.  The same
+    //      fixed set of loads is issued for every item (rows clamped to the
+    //      sequence), so the only wait on them is where they are staged. --------
+    static_assert(PQ == 1 && PA <= 2, "raw rows: one 16-byte piece of q, e, k and two of alpha per thread");
+    uint4 pq, pe, pk, pa0, pa1;
     float pbeta = 0.f, pgamma = 0.f;
     auto prefetch = [&](int it) __attribute__((always_inline)) {
         const int bh = head_of(it), cidx = chunk_of(it);
         const int b = bh / H, h = bh % H;
-        const long tok0 = ((long)b * Tlen + (long)cidx * C) * H + h;   // row of the chunk's first token
-        const bf16 *qh = q + tok0 * dk, *eh = e + tok0 * dk, *kh = k + tok0 * dk;
-        const float *ah = alpha + tok0 * dk;
-#pragma unroll
-        for (int m = 0; m < PF; ++m) {
-            const int u = tid + NT * m;
-            const int part = u / RU, uu = u - part * RU;   // 0 q, 1 e, 2 k, 3.. alpha
-            const bf16 *rowp = part == 0 ? qh : (part == 1 ? eh : kh);
-            const char *src = part < 3 ? (const char *)(rowp + (uu / (D / 8)) * HK + 8 * (uu % (D / 8)))
-                                       : (const char *)(ah + ((u - 3 * RU) / (D / 4)) * HK + 4 * ((u - 3 * RU) % (D / 4)));
-            pre[m] = make_uint4(0u, 0u, 0u, 0u);
-            if (u < NRAW) pre[m] = *(const uint4 *)src;
+        const int t0 = cidx * C, last = Tlen - 1 - t0;                 // rows past `last` are clamped
+        const long tok0 = ((long)b * Tlen + t0) * H + h;              // row of the chunk's first token
+        {
+            const int u = min(tid, RU - 1);
+            const long off = (tok0 + (long)min(u / (D / 8), last) * H) * dk + 8 * (u % (D / 8));
+            pq = *(const uint4 *)(q + off);
+            pe = *(const uint4 *)(e + off);
+            pk = *(const uint4 *)(k + off);
         }
-        if (tid < C) {
-            pbeta = beta[tok0 + (long)tid * H];
-            pgamma = gamma[tok0 + (long)tid * H];
+        {
+            const int u = min(tid, AU - 1);
+            pa0 = *(const uint4 *)(alpha + (tok0 + (long)min(u / (D / 4), last) * H) * dk + 4 * (u % (D / 4)));
         }
+        if constexpr (PA == 2) {
+            const int u = min(tid + NT, AU - 1);
+            pa1 = *(const uint4 *)(alpha + (tok0 + (long)min(u / (D / 4), last) * H) * dk + 4 * (u % (D / 4)));
+        }
+        const long tb = tok0 + (long)min(tid % C, last) * H;
+        pbeta = beta[tb];
+        pgamma = gamma[tb];
     };
     // ---- registers (or, for a ragged or unaligned chunk, global) -> LDS ---------
     auto stage = [&](int it, bool fast) __attribute__((always_inline)) {
@@ -262,15 +273,16 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         const long tok0 = ((long)b * Tlen + t0) * H + h;
         float bv = 0.f, gv = 0.f;
         if (fast) {
-#pragma unroll
-            for (int m = 0; m < PF; ++m) {
-                const int u = tid + NT * m;
-                const int part = u / RU, uu = u - part * RU;
-                const int rr = uu / (D / 8), bb = uu % (D / 8);
-                char *dst = part == 0 ? (char *)(Ql + rr * LDA + 8 * bb)
-                          : part < 3  ? (char *)(Kr + (2 * rr + part - 1) * LDA + 8 * bb)
-                                      : (char *)(As + ((u - 3 * RU) / (D / 4)) * ASD + 4 * ((u - 3 * RU) % (D / 4)));
-                if (u < NRAW) *(uint4 *)dst = pre[m];
+            if (RU % NT == 0 || tid < RU) {
+                const int rr = tid / (D / 8), cc = 8 * (tid % (D / 8));
+                *(uint4 *)(Ql + rr * LDA + cc) = pq;
+                *(uint4 *)(Kr + (2 * rr) * LDA + cc) = pe;
+                *(uint4 *)(Kr + (2 * rr + 1) * LDA + cc) = pk;
+            }
+            if (AU % NT == 0 || tid < AU) *(uint4 *)(As + (tid / (D / 4)) * ASD + 4 * (tid % (D / 4))) = pa0;
+            if constexpr (PA == 2) {
+                const int u = tid + NT;
+                if (AU % NT == 0 || u < AU) *(uint4 *)(As + (u / (D / 4)) * ASD + 4 * (u % (D / 4))) = pa1;
             }
             bv = pbeta;
             gv = pgamma;
@@ -325,13 +337,13 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     };
 
     int it = blockIdx.x;
-    if (it < items && is_fast(chunk_of(it))) prefetch(it);
+    if constexpr (VEC) prefetch(it);
     for (; it < items; it += gridDim.x) {
         const int bh = head_of(it), cidx = chunk_of(it);
         stage(it, is_fast(cidx));
-        {
+        if constexpr (VEC) {
             const int nx = it + gridDim.x;
-            if (nx < items && is_fast(chunk_of(nx))) prefetch(nx);
+            prefetch(nx < items ? nx : items - 1);
         }
         char *wsb = ws + ((long)bh * NC + cidx) * F::bytes;
         __syncthreads();
@@ -637,11 +649,12 @@ struct FragSet {
     f32x4 er, lm;   // scales of the state rows
 };
 
-template <int C, int D, int BV>
+// VV: every value slice is whole (d_v a multiple of BV) and v is 16-byte
+// aligned, so values and outputs move as 16-byte row pieces.
+template <int C, int D, int BV, bool VV>
 __global__ void __launch_bounds__(NTHREADS)
 eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16 *__restrict__ o,
-               const char *__restrict__ ws, int Tlen, int H, int BH, int dk, int dv, int NC, int R,
-               int vvec, int ovec) {
+               const char *__restrict__ ws, int Tlen, int H, int BH, int dk, int dv, int NC, int R) {
     using G = K2G<C, D, BV>;
     using F = Fac<C, D>;
     using T = bf16;
@@ -666,90 +679,11 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = 4 * (lane >> 4), l16 = lane & 15;
-    const bool uw = wave < G::NBL, ow = wave >= O0, mv = !uw && !ow, sw = wave < G::NBD;
-    const int mu = (wave - G::H0) * 64 + lane;             // mover unit
-    const int mtau = mu / (BV / 8), mn = 8 * (mu % (BV / 8));
-
-    using Set = FragSet<G::NR, KSL>;
-    auto load_set = [&](Set &s, int c) __attribute__((always_inline)) {
-        const char *blk = wsh + (long)c * F::bytes;
-        if (uw) {
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
-                s.R[ks] = ld_frag(blk + F::oWn + ((wave * KSD + ks) * 64 + lane) * 16);
-            s.R[KSD] = ld_frag(blk + F::oTv + (wave * 64 + lane) * 16);
-        } else if (ow) {
-            const int ob = wave - O0;
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
-                s.R[ks] = ld_frag(blk + F::oQl + ((ob * KSD + ks) * 64 + lane) * 16);
-#pragma unroll
-            for (int ks = 0; ks < KSL; ++ks)
-                s.R[KSD + ks] = ld_frag(blk + F::oP + ((ob * KSL + ks) * 64 + lane) * 16);
-        } else {
-            uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            const int t = c * C + mtau;
-            if (mu < VU && t < Tlen) {
-                const T *src = vh + t * HV + mn;
-                if (vvec && n0 + mn + 8 <= dv) {
-                    x = *(const uint4 *)src;
-                } else {
-                    uint32_t y[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) y[j] = (n0 + mn + j < dv) ? src[j] : 0u;
-                    x = make_uint4(y[0] | (y[1] << 16), y[2] | (y[3] << 16), y[4] | (y[5] << 16), y[6] | (y[7] << 16));
-                }
-            }
-            s.R[0] = __builtin_bit_cast(bf16x8, x);
-        }
-        if (sw) {
-#pragma unroll
-            for (int ks = 0; ks < KSL; ++ks)
-                s.K[ks] = ld_frag(blk + F::oKr + ((wave * KSL + ks) * 64 + lane) * 16);
-            s.er = *(const f32x4 *)(blk + F::oEr + 4 * (16 * wave + g4));
-            s.lm = *(const f32x4 *)(blk + F::oLam + 4 * (16 * wave + g4));
-        }
-    };
-    auto put_v = [&](const Set &s, int c) __attribute__((always_inline)) {
-        if (mu < VU)
-            *(uint4 *)((T *)(smem + G::oVs + (c & 1) * G::szVs) + mtau * LDV + mn) = __builtin_bit_cast(uint4, s.R[0]);
-    };
-    auto flush = [&](int cp) __attribute__((always_inline)) {
-        const int t = cp * C + mtau;
-        if (mu < VU && t < Tlen) {
-            const uint4 val = *(const uint4 *)(Os + mtau * LDO + mn);
-            T *dst = oh + t * HV + mn;
-            if (ovec && n0 + mn + 8 <= dv) {
-                *(uint4 *)dst = val;
-            } else {
-                const uint32_t y[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (n0 + mn + j < dv) dst[j] = (T)((y[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-            }
-        }
-    };
-
-    // ---- initial state: rows 16 wave + g4 + i, columns n0 + 16 cb + l16 --------
-    f32x4 S[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        S[cb] = zero4();
-        if (sw && S0) {
-            const int col = n0 + 16 * cb + l16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * wave + g4 + i;
-                if (row < dk && col < dv) S[cb][i] = S0[sbase + (long)row * dv + col];
-            }
-        }
-    }
-    auto write_St = [&](const f32x4 &er) __attribute__((always_inline)) {
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-            store4<T>(St + (16 * cb + l16) * LDT + 16 * wave + g4, er[0] * S[cb][0], er[1] * S[cb][1],
-                      er[2] * S[cb][2], er[3] * S[cb][3]);
-    };
+    // mover unit: one 16-byte piece (8 columns of one token) of the value or output slice
+    const int mu = (wave - G::H0) * 64 + lane;
+    const bool mact = mu >= 0 && mu < VU;
+    const int muc = mact ? mu : 0;
+    const int mtau = muc / (BV / 8), mn = 8 * (muc % (BV / 8));
 
     if constexpr (C < G::VR) {
         // the value rows beyond the chunk are read by the k = 32 product: zero them
@@ -759,98 +693,211 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
         }
     }
 
-    Set A, B, X;
-    load_set(A, 0);
-    if (NC > 1) load_set(B, 1);
-    if (mv) put_v(A, 0);
-    if (sw) write_St(A.er);
-
-    auto body = [&](Set &cur, Set &nxt, Set &fut, int c) __attribute__((always_inline)) {
-        __syncthreads();   // S'^T, the value slice of chunk c and the last outputs are in LDS
-        if (c + 2 < NC) load_set(fut, c + 2);
-        if (mv) {
-            if (c > 0) flush(c - 1);
-            if (c + 1 < NC) put_v(nxt, c + 1);
-        }
-        f32x4 acc[NCB];
-        if (uw) {
-            // U = T' V - W S'  (rows 16 wave.., all slice columns) -> U^T in LDS
-            const T *Vs = (const T *)(smem + G::oVs + (c & 1) * G::szVs);
-            // (one instruction shape for the whole accumulation chain: at C = 16
-            // the k = 32 product reads 16 zero rows of the value buffer)
+    // ---- initial state: rows 16 wave + g4 + i, columns n0 + 16 cb + l16 --------
+    f32x4 S[NCB];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-                acc[cb] = mma32(cur.R[KSD], frag_col(Vs + 16 * cb, LDV, lane), zero4());
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    acc[cb] = mma32(cur.R[ks], frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), acc[cb]);
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-                store4<T>(Ut + (16 * cb + l16) * LDU + 16 * wave + g4, acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
-        } else if (ow) {
-            // o^T = S'^T Ql^T for the wave's 16 tokens (first half)
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    acc[cb] = mma32(frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), cur.R[ks], acc[cb]);
-        }
-        __syncthreads();   // U^T complete; S'^T no longer read
-        if (sw) {
-            // S <- e^r (lam S + Kr^T U); S'^T of the next chunk
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                f32x4 a;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = cur.lm[i] * S[cb][i];
-#pragma unroll
-                for (int ks = 0; ks < KSL; ++ks)
-                    a = mma32(cur.K[ks], frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), a);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[cb][i] = cur.er[i] * a[i];
-            }
-            if (c + 1 < NC) write_St(nxt.er);
-        }
-        if (ow) {
-            // o^T += U^T P^T; rows of o -> LDS
-#pragma unroll
-            for (int ks = 0; ks < KSL; ++ks)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    acc[cb] = mma32(frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), cur.R[KSD + ks], acc[cb]);
-            const int tr = 16 * (wave - O0) + l16;
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-                store4<T>(Os + tr * LDO + 16 * cb + g4, acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
-        }
-    };
-
-    int c = 0;
-    for (; c + 3 <= NC; c += 3) {
-        body(A, B, X, c);
-        body(B, X, A, c + 1);
-        body(X, A, B, c + 2);
-    }
-    if (c < NC) body(A, B, X, c);
-    if (c + 1 < NC) body(B, X, A, c + 1);
-
-    __syncthreads();
-    if (mv) flush(NC - 1);
-    if (S_final && sw) {
-        // every read of S0 happened before the chunk loop, so S_final may be S0
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
+        S[cb] = zero4();
+        if (wave < G::NBD && S0) {
             const int col = n0 + 16 * cb + l16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * wave + g4 + i;
-                if (row < dk && col < dv) S_final[sbase + (long)row * dv + col] = S[cb][i];
+                if (row < dk && col < dv) S[cb][i] = S0[sbase + (long)row * dv + col];
             }
         }
+    }
+
+    // One chunk loop per combination of roles, so that each wave runs straight-
+    // line code with a fixed number of memory operations per chunk: the
+    // operands of chunk c + 2 are fetched (addresses clamped, never skipped)
+    // while chunk c is computed, and the waits before each use only cover the
+    // fetches of two chunks earlier.
+    auto run = [&](auto ru, auto ro, auto rm, auto rs) __attribute__((always_inline)) {
+        constexpr bool RU = decltype(ru)::value, RO = decltype(ro)::value;
+        constexpr bool RM = decltype(rm)::value, RS = decltype(rs)::value;
+        using Set = FragSet<G::NR, KSL>;
+
+        auto load_set = [&](Set &s, int c) __attribute__((always_inline)) {
+            const char *blk = wsh + (long)c * F::bytes;
+            if constexpr (RU) {
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+                    s.R[ks] = ld_frag(blk + F::oWn + ((wave * KSD + ks) * 64 + lane) * 16);
+                s.R[KSD] = ld_frag(blk + F::oTv + (wave * 64 + lane) * 16);
+            }
+            if constexpr (RO) {
+                const int ob = wave - O0;
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+                    s.R[ks] = ld_frag(blk + F::oQl + ((ob * KSD + ks) * 64 + lane) * 16);
+#pragma unroll
+                for (int ks = 0; ks < KSL; ++ks)
+                    s.R[KSD + ks] = ld_frag(blk + F::oP + ((ob * KSL + ks) * 64 + lane) * 16);
+            }
+            if constexpr (RM) {
+                const int t = c * C + mtau, tc = t < Tlen ? t : Tlen - 1;
+                const bool ok = mact && t < Tlen;
+                uint4 x;
+                if constexpr (VV) {
+                    x = *(const uint4 *)(vh + tc * HV + mn);
+                } else {
+                    uint32_t y[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int col = mn + j, cc = n0 + col < dv ? col : dv - 1 - n0;
+                        y[j] = vh[tc * HV + cc];
+                        if (n0 + col >= dv) y[j] = 0u;
+                    }
+                    x = make_uint4(y[0] | (y[1] << 16), y[2] | (y[3] << 16), y[4] | (y[5] << 16), y[6] | (y[7] << 16));
+                }
+                if (!ok) x = make_uint4(0u, 0u, 0u, 0u);
+                s.R[0] = __builtin_bit_cast(bf16x8, x);
+            }
+            if constexpr (RS) {
+#pragma unroll
+                for (int ks = 0; ks < KSL; ++ks)
+                    s.K[ks] = ld_frag(blk + F::oKr + ((wave * KSL + ks) * 64 + lane) * 16);
+                s.er = *(const f32x4 *)(blk + F::oEr + 4 * (16 * wave + g4));
+                s.lm = *(const f32x4 *)(blk + F::oLam + 4 * (16 * wave + g4));
+            }
+        };
+        auto put_v = [&](const Set &s, int c) __attribute__((always_inline)) {
+            if (mact)
+                *(uint4 *)((T *)(smem + G::oVs + (c & 1) * G::szVs) + mtau * LDV + mn) = __builtin_bit_cast(uint4, s.R[0]);
+        };
+        auto flush = [&](int cp) __attribute__((always_inline)) {
+            const int t = cp * C + mtau;
+            if (mact && t < Tlen) {
+                const uint4 val = *(const uint4 *)(Os + mtau * LDO + mn);
+                T *dst = oh + t * HV + mn;
+                if constexpr (VV) {
+                    *(uint4 *)dst = val;
+                } else {
+                    const uint32_t y[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (n0 + mn + j < dv) dst[j] = (T)((y[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                }
+            }
+        };
+        auto write_St = [&](const f32x4 &er) __attribute__((always_inline)) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                store4<T>(St + (16 * cb + l16) * LDT + 16 * wave + g4, er[0] * S[cb][0], er[1] * S[cb][1],
+                          er[2] * S[cb][2], er[3] * S[cb][3]);
+        };
+
+        auto body = [&](Set &cur, Set &nxt, Set &fut, int c) __attribute__((always_inline)) {
+            __syncthreads();   // S'^T, the value slice of chunk c and the last outputs are in LDS
+            load_set(fut, c + 2 < NC ? c + 2 : NC - 1);
+            if constexpr (RM) {
+                if (c > 0) flush(c - 1);
+                if (c + 1 < NC) put_v(nxt, c + 1);
+            }
+            f32x4 acc[NCB];
+            if constexpr (RU) {
+                // U = T' V - W S'  (rows 16 wave.., all slice columns) -> U^T in LDS
+                // (one instruction shape for the whole accumulation chain: at C = 16
+                // the k = 32 product reads 16 zero rows of the value buffer)
+                const T *Vs = (const T *)(smem + G::oVs + (c & 1) * G::szVs);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[cb] = mma32(cur.R[KSD], frag_col(Vs + 16 * cb, LDV, lane), zero4());
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        acc[cb] = mma32(cur.R[ks], frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), acc[cb]);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    store4<T>(Ut + (16 * cb + l16) * LDU + 16 * wave + g4, acc[cb][0], acc[cb][1], acc[cb][2],
+                              acc[cb][3]);
+            }
+            if constexpr (RO) {
+                // o^T = S'^T Ql^T for the wave's 16 tokens (first half)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        acc[cb] = mma32(frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), cur.R[ks], acc[cb]);
+            }
+            __syncthreads();   // U^T complete; S'^T no longer read
+            if constexpr (RS) {
+                // S <- e^r (lam S + Kr^T U); S'^T of the next chunk
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    f32x4 a;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a[i] = cur.lm[i] * S[cb][i];
+#pragma unroll
+                    for (int ks = 0; ks < KSL; ++ks)
+                        a = mma32(cur.K[ks], frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), a);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[cb][i] = cur.er[i] * a[i];
+                }
+                if (c + 1 < NC) write_St(nxt.er);
+            }
+            if constexpr (RO) {
+                // o^T += U^T P^T; rows of o -> LDS
+#pragma unroll
+                for (int ks = 0; ks < KSL; ++ks)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        acc[cb] = mma32(frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), cur.R[KSD + ks], acc[cb]);
+                const int tr = 16 * (wave - O0) + l16;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    store4<T>(Os + tr * LDO + 16 * cb + g4, acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
+            }
+        };
+
+        Set A, B, X;
+        load_set(A, 0);
+        load_set(B, NC > 1 ? 1 : 0);
+        if constexpr (RM) put_v(A, 0);
+        if constexpr (RS) write_St(A.er);
+        int c = 0;
+        for (; c + 3 <= NC; c += 3) {
+            body(A, B, X, c);
+            body(B, X, A, c + 1);
+            body(X, A, B, c + 2);
+        }
+        if (c < NC) body(A, B, X, c);
+        if (c + 1 < NC) body(B, X, A, c + 1);
+
+        __syncthreads();
+        if constexpr (RM) flush(NC - 1);
+        if constexpr (RS) {
+            if (S_final) {
+                // every read of S0 happened before the chunk loop, so S_final may be S0
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const int col = n0 + 16 * cb + l16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * wave + g4 + i;
+                        if (row < dk && col < dv) S_final[sbase + (long)row * dv + col] = S[cb][i];
+                    }
+                }
+            }
+        }
+    };
+
+    using Y = std::true_type;
+    using N = std::false_type;
+    const bool sw = wave < G::NBD;
+    if (wave < G::NBL) {
+        if (sw) run(Y{}, N{}, N{}, Y{});
+        else if constexpr (G::NBD < G::NW) run(Y{}, N{}, N{}, N{});
+    } else if (wave >= O0) {
+        if (sw) run(N{}, Y{}, N{}, Y{});
+        else if constexpr (G::NBD < G::NW) run(N{}, Y{}, N{}, N{});
+    } else {
+        if (sw) run(N{}, N{}, Y{}, Y{});
+        else if constexpr (G::NBD < G::NW) run(N{}, N{}, Y{}, N{});
     }
 }
 
@@ -885,12 +932,11 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     const int NC = (Tlen + C - 1) / C, BH = B * H;
     // 16-byte loads of whole rows need d_k == D and 16-byte aligned bases
     // (D is a multiple of 8, so every row start stays aligned)
-    const int vec = (dk == D) && ((uintptr_t)q % 16 == 0) && ((uintptr_t)k % 16 == 0) &&
-                    ((uintptr_t)e % 16 == 0) && ((uintptr_t)alpha % 16 == 0);
-    const int vvec = (dv % 8 == 0) && ((uintptr_t)v % 16 == 0);
-    const int ovec = (dv % 8 == 0) && ((uintptr_t)o % 16 == 0);
-    auto k1 = eda_bf16_factors<C, D>;
-    auto k2 = eda_bf16_state<C, D, BV>;
+    const bool vec = (dk == D) && ((uintptr_t)q % 16 == 0) && ((uintptr_t)k % 16 == 0) &&
+                     ((uintptr_t)e % 16 == 0) && ((uintptr_t)alpha % 16 == 0);
+    const bool vv = (dv % BV == 0) && ((uintptr_t)v % 16 == 0) && ((uintptr_t)o % 16 == 0);
+    auto k1 = vec ? eda_bf16_factors<C, D, true> : eda_bf16_factors<C, D, false>;
+    auto k2 = vv ? eda_bf16_state<C, D, BV, true> : eda_bf16_state<C, D, BV, false>;
     hipError_t err = hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, G1::LDS);
     if (err != hipSuccess) return err;
     int dev = 0, ncu = 256;
@@ -902,13 +948,13 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     const int grid1 = (int)(items < 2L * ncu ? items : 2L * ncu);   // two per compute unit (LDS)
     hipLaunchKernelGGL(k1, dim3((unsigned)grid1), dim3(G1::NT), G1::LDS, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)e, alpha, beta, gamma, (char *)ws, Tlen, H, dk, NC,
-                       BH, vec);
+                       BH);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int R = (dv + BV - 1) / BV;
     const int grid2 = 8 * ((BH + 7) / 8) * R;
     hipLaunchKernelGGL(k2, dim3((unsigned)grid2), dim3(G2::NT), G2::LDS, stream, (const bf16 *)v, S0,
-                       S_final, (bf16 *)o, (const char *)ws, Tlen, H, BH, dk, dv, NC, R, vvec, ovec);
+                       S_final, (bf16 *)o, (const char *)ws, Tlen, H, BH, dk, dv, NC, R);
     return hipGetLastError();
 }
 
