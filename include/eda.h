@@ -64,7 +64,7 @@ const char *eda_status_string(eda_status_t s);
  * unsupported combination).  `chunk` is the number of tokens per chunk (0
  * selects the default, 32).  The workspace holds every chunk's
  * state-independent factors between the two kernels of the chunked forward:
- * for bf16 inputs with d_k = d_v = 128 and 32-token chunks that is 50176
+ * for bf16 inputs with d_k = d_v = 128 and 32-token chunks that is 47616
  * bytes per chunk and head (about 1.8 KB per token and head).
  */
 size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v,

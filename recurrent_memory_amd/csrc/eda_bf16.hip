@@ -135,14 +135,15 @@ struct Fac {
     static constexpr int L = 2 * C, NBL = L / 16, NBC = C / 16, NBD = D / 16;
     static constexpr int KSD = D / 32, KSL = L / 32;
     static constexpr int FR = 1024;                    // one fragment
-    static constexpr int oWn = 0;                      // -W    [NBL][KSD] fragments
-    static constexpr int oTv = oWn + NBL * KSD * FR;   // T'    [NBL] (k = C, zero-padded to 32)
-    static constexpr int oKr = oTv + NBL * FR;         // Kr^T  [NBD][KSL]   (wide: Khat^T)
-    static constexpr int oQl = oKr + NBD * KSL * FR;   // Ql    [NBC][KSD]
-    static constexpr int oP = oQl + NBC * KSD * FR;    // P     [NBC][KSL]
-    static constexpr int oEr = oP + NBC * KSL * FR;    // e^r (1 if wide)          [D] fp32
-    static constexpr int oLam = oEr + D * 4;           // e^r (e^{G_C} if wide)    [D] fp32
-    static constexpr int bytes = align256(oLam + D * 4);
+    // (every factor with a key-channel index carries the scale e^r of that
+    // channel, so the state pass works on the unscaled state)
+    static constexpr int oWn = 0;                      // -W Diag(e^r)             [NBL][KSD] fragments
+    static constexpr int oTv = oWn + NBL * KSD * FR;   // T'                       [NBL] (k = C, zero-padded)
+    static constexpr int oKr = oTv + NBL * FR;         // Diag(e^r) Kr^T           [NBD][KSL]
+    static constexpr int oQh = oKr + NBD * KSL * FR;   // (Ql - P W) Diag(e^r)     [NBC][KSD]
+    static constexpr int oPh = oQh + NBC * KSD * FR;   // P T'                     [NBC] (k = C, zero-padded)
+    static constexpr int oDec = oPh + NBC * FR;        // e^{G_C}                  [D] fp32
+    static constexpr int bytes = align256(oDec + D * 4);
     static_assert(C == 16 || C == 32, "chunk");
     static_assert(D % 32 == 0 && D <= 128, "head dim");
 };
@@ -178,7 +179,9 @@ struct K1G {
     static_assert(C * ASD * 4 <= szKl && C * D * 4 <= szKl, "Kl region reuse");
     static constexpr int szLL = align16(L * LDL * 2), szAd = NB * 16 * ADS * 4;
     static constexpr int szMT = NB * 16 * MTW * 2, szPs = align16(C * LDL * 2);
-    static constexpr int szMisc = (L + 2 * C + D) * 4;
+    static constexpr int szMisc = (L + 2 * C + 2 * D) * 4;
+    static constexpr int LDTV = C + 8;                 // T' and P T' staging rows (after the inverse)
+    static_assert(L * LDTV * 2 <= szLL && C * LDTV * 2 <= szAd, "staging reuse");
     static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oAbf = oQl + szQl;
     static constexpr int oAd = oAbf + szLL, oMI = oAd + szAd, oMT = oMI + szLL, oPs = oMT + szMT;
     static constexpr int oMisc = oPs + szPs;
@@ -217,6 +220,10 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     float *bp = (float *)(smem + G::oMisc);  // b' per sub-step          [L]
     float *sb = bp + L, *sg = sb + C;        // beta, gamma per token    [C]
     float *glc = sg + C;                     // G_C per channel (log2)   [D]
+    float *ers = glc + D;                    // e^r per channel (1 if wide) [D]
+    T *Tvs = (T *)(smem + G::oAbf);          // T', after the inverse    [L][LDTV]
+    T *Phs = (T *)(smem + G::oAd);           // P T', after the inverse  [C][LDTV]
+    constexpr int LDTV = G::LDTV;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -411,15 +418,14 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         if (act) {
             glq = *(const f32x4 *)(glc + c0);
             if (seg == 0) {
-                f32x4 er, lam;
+                f32x4 er, dec;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float x = exp2f_(0.5f * glq[j]);
-                    er[j] = wide ? 1.f : x;
-                    lam[j] = wide ? exp2f_(glq[j]) : x;
+                    er[j] = wide ? 1.f : exp2f_(0.5f * glq[j]);
+                    dec[j] = exp2f_(glq[j]);
                 }
-                *(f32x4 *)(wsb + F::oEr + 4 * c0) = er;
-                *(f32x4 *)(wsb + F::oLam + 4 * c0) = lam;
+                *(f32x4 *)(ers + c0) = er;
+                *(f32x4 *)(wsb + F::oDec + 4 * c0) = dec;
             }
             if (!wide) {
                 // Kl overwrites the raw alpha rows, which were last read before the vote
@@ -538,8 +544,17 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         __syncthreads();
 
-        // ---- W^T = Kl^T Diag(b') M^T tiles (kept in registers); Kr^T, Ql, P and T'
-        //      fragments -> workspace ------------------------------------------------
+        // ---- W^T = Kl^T Diag(b') M^T tiles (kept in registers); Diag(e^r) Kr^T and T'
+        //      fragments -> workspace, T' also -> LDS -------------------------------------
+        // scale the 8 values of a fragment lane by sc[0..7] (fp32) and repack
+        auto scaled = [&](bf16x8 x, const float *sc) __attribute__((always_inline)) {
+            const uint4 u = __builtin_bit_cast(uint4, x);
+            const f32x4 s0 = *(const f32x4 *)sc, s1 = *(const f32x4 *)(sc + 4);
+            return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(lo_bf16(u.x) * s0[0], hi_bf16(u.x) * s0[1]),
+                                                         pack_bf16(lo_bf16(u.y) * s0[2], hi_bf16(u.y) * s0[3]),
+                                                         pack_bf16(lo_bf16(u.z) * s1[0], hi_bf16(u.z) * s1[1]),
+                                                         pack_bf16(lo_bf16(u.w) * s1[2], hi_bf16(u.w) * s1[3])));
+        };
         f32x4 wacc[WPW];
 #pragma unroll
         for (int m = 0; m < WPW; ++m) {
@@ -557,20 +572,18 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             }
         }
         {
-            constexpr int NKR = NBD * KSL, NQL = NBC * KSD, NPF = NBC * KSL, NEX = NKR + NQL + NPF + NBL;
+            constexpr int NKR = NBD * KSL, NEX = NKR + NBL;
             for (int f = wave; f < NEX; f += NW) {
                 if (f < NKR) {
+                    // row n of Kr^T carries e^r_n: one scale per lane
                     const int rb = f / KSL, ks = f % KSL;
-                    st_frag(wsb + F::oKr + (f * 64 + lane) * 16, frag_col(Kr + 32 * ks * LDA + 16 * rb, LDA, lane));
-                } else if (f < NKR + NQL) {
-                    const int ff = f - NKR, rb = ff / KSD, ks = ff % KSD;
-                    st_frag(wsb + F::oQl + (ff * 64 + lane) * 16, frag_row(Ql + 16 * rb * LDA + 32 * ks, LDA, lane));
-                } else if (f < NKR + NQL + NPF) {
-                    const int ff = f - NKR - NQL, rb = ff / KSL, ks = ff % KSL;
-                    st_frag(wsb + F::oP + (ff * 64 + lane) * 16, frag_row(Ps + 16 * rb * LDL + 32 * ks, LDL, lane));
+                    const bf16x8 x = frag_col(Kr + 32 * ks * LDA + 16 * rb, LDA, lane);
+                    const float e = ers[16 * rb + l16];
+                    const float sc[8] = {e, e, e, e, e, e, e, e};
+                    st_frag(wsb + F::oKr + (f * 64 + lane) * 16, scaled(x, sc));
                 } else {
                     // T'[j][tau] = M[j][2 tau + 1] beta_tau (tau >= C: zero)
-                    const int rb = f - NKR - NQL - NPF, gg = lane >> 4;
+                    const int rb = f - NKR, gg = lane >> 4;
                     const T *mrow = MI + (16 * rb + l16) * LDL;
                     uint4 x = make_uint4(0u, 0u, 0u, 0u);
                     if (8 * gg < C) {
@@ -581,6 +594,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                                        pack_bf16(hi_bf16(u0.z) * b0[2], hi_bf16(u0.w) * b0[3]),
                                        pack_bf16(hi_bf16(u1.x) * b1[0], hi_bf16(u1.y) * b1[1]),
                                        pack_bf16(hi_bf16(u1.z) * b1[2], hi_bf16(u1.w) * b1[3]));
+                        *(uint4 *)(Tvs + (16 * rb + l16) * LDTV + 8 * gg) = x;
                     }
                     *(uint4 *)(wsb + F::oTv + (rb * 64 + lane) * 16) = x;
                 }
@@ -599,9 +613,54 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             }
         }
         __syncthreads();
-        for (int f = wave; f < NBL * KSD; f += NW) {
-            const int rb = f / KSD, ks = f % KSD;
-            st_frag(wsb + F::oWn + (f * 64 + lane) * 16, frag_row(Wst + 16 * rb * LDA + 32 * ks, LDA, lane));
+
+        // ---- -W Diag(e^r) -> workspace; Q^ = Ql - P W (in place over Ql) and
+        //      P^ = P T' (staged), both as transposed tiles so rows leave as runs --------
+        {
+            constexpr int NWF = NBL * KSD, NQT = NBD * NBC, NPT2 = NBC * NBC;
+            for (int f = wave; f < NWF + NQT + NPT2; f += NW) {
+                if (f < NWF) {
+                    const int rb = f / KSD, ks = f % KSD;
+                    st_frag(wsb + F::oWn + (f * 64 + lane) * 16,
+                            scaled(frag_row(Wst + 16 * rb * LDA + 32 * ks, LDA, lane), ers + 32 * ks + 8 * (lane >> 4)));
+                } else if (f < NWF + NQT) {
+                    // Q^T tile (channels 16 nb.., tokens 16 tb..); P is zero beyond sub-step 2t + 1
+                    const int t = f - NWF, nb = t % NBD, tb = t / NBD;
+                    const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * nb + g4);
+                    f32x4 acc = {lo_bf16(q0.x), hi_bf16(q0.x), lo_bf16(q0.y), hi_bf16(q0.y)};
+                    const int K = imin(L, 32 * (tb + 1));
+                    for (int k0 = 0; k0 < K; k0 += 32)
+                        acc = mma32(frag_col(Wst + k0 * LDA + 16 * nb, LDA, lane),
+                                    frag_row(Ps + 16 * tb * LDL + k0, LDL, lane), acc);
+                    store4<T>(Ql + (16 * tb + l16) * LDA + 16 * nb + g4, acc[0], acc[1], acc[2], acc[3]);
+                } else {
+                    // P^ ^T tile (tokens tau 16 nb.., tokens t 16 tb..)
+                    const int t = f - NWF - NQT, nb = t % NBC, tb = t / NBC;
+                    f32x4 acc = zero4();
+                    const int K = imin(L, 32 * (tb + 1));
+                    for (int k0 = 0; k0 < K; k0 += 32)
+                        acc = mma32(frag_col(Tvs + k0 * LDTV + 16 * nb, LDTV, lane),
+                                    frag_row(Ps + 16 * tb * LDL + k0, LDL, lane), acc);
+                    store4<T>(Phs + (16 * tb + l16) * LDTV + 16 * nb + g4, acc[0], acc[1], acc[2], acc[3]);
+                }
+            }
+        }
+        __syncthreads();
+        {
+            constexpr int NQF = NBC * KSD;
+            for (int f = wave; f < NQF + NBC; f += NW) {
+                if (f < NQF) {
+                    const int rb = f / KSD, ks = f % KSD;
+                    st_frag(wsb + F::oQh + (f * 64 + lane) * 16,
+                            scaled(frag_row(Ql + 16 * rb * LDA + 32 * ks, LDA, lane), ers + 32 * ks + 8 * (lane >> 4)));
+                } else {
+                    const int rb = f - NQF;
+                    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+                    if (8 * (lane >> 4) < C)
+                        x = __builtin_bit_cast(uint4, frag_row(Phs + 16 * rb * LDTV, LDTV, lane));
+                    *(uint4 *)(wsb + F::oPh + (rb * 64 + lane) * 16) = x;
+                }
+            }
         }
         __syncthreads();   // LDS free for the next item
     }
@@ -612,26 +671,32 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 // slices of one head get workgroup ids congruent mod 8 (same XCD, one L2 for
 // the shared factor blocks).
 //
-// Wave roles (per chunk): waves [0, L/16) each own a 16-row block of U
-// (U = T' V - W S'); waves [8 - C/16, 8) each own a 16-token block of the
-// outputs (o = Ql S' + P U, computed transposed so the stores are row runs);
-// the waves in between move the value slice in and the outputs out; waves
-// [0, D/16) each own a 16-row block of the state.  Every wave keeps the
-// operands of its roles for three chunks in registers (current, next, and
-// the one being fetched).
+// Every wave has one role, and each role fetches the operands it needs two
+// chunks ahead during the half of the chunk in which it has nothing else to
+// do, so the vector-memory traffic of the factors overlaps the products:
+//   U waves   (L/16):  U = T' V - W S for 16 rows of U, all slice columns;
+//                      fetch -W, T' while the state is updated
+//   state     (D/16):  S <- e^{G_C} S + Kr^T U for 16 state rows, then S^T
+//                      (bf16) for the next chunk; fetch Kr^T while U is formed
+//   output    (C/16):  o = Q^ S + P^ V for 16 tokens (transposed, so rows of o
+//                      leave as runs), Q^ = Ql - P W, P^ = P T'; fetch them
+//                      while the state is updated
+//   movers:            value slice and per-row decay in, outputs out.
+// (W, Kr^T and Q^ carry the per-channel e^r of the split, so S is unscaled.)
 // ---------------------------------------------------------------------------
 template <int C, int D, int BV>
 struct K2G {
     using F = Fac<C, D>;
-    static constexpr int NW = NWAVES, NT = NTHREADS, L = 2 * C;
+    static constexpr int L = 2 * C;
     static constexpr int NBL = F::NBL, NBC = F::NBC, NBD = F::NBD, NCB = BV / 16;
     static constexpr int KSD = F::KSD, KSL = F::KSL;
     static constexpr int NR = KSD + KSL;               // role operands per chunk
-    static constexpr int O0 = NW - NBC;                // first output wave
-    static constexpr int H0 = NBL, NH = O0 - NBL;      // value / output movers
     static constexpr int VU = C * BV / 8;              // 16-byte units of a value (or output) slice
-    static_assert(NH >= 1 && VU <= 64 * NH, "mover waves");
-    static_assert(NBD <= NW, "one state row block per wave");
+    static constexpr int SCU = D / 2;                  // 8-byte units of a chunk's decay e^{G_C}
+    static constexpr int NM = imax((VU + 63) / 64, (SCU + 63) / 64);
+    // wave order: U, state, output, movers
+    static constexpr int S0W = NBL, O0 = S0W + NBD, M0 = O0 + NBC, NW = M0 + NM, NT = 64 * NW;
+    static_assert(NT <= 1024, "workgroup size");
     static constexpr int LDT = D + 8, LDU = L + 8, LDV = BV + 8, LDO = BV + 8;
     static constexpr int oSt = 0;                                   // S'^T [BV][LDT] bf16
     static constexpr int oUt = align16(oSt + BV * LDT * 2);         // U^T  [BV][LDU] bf16
@@ -639,27 +704,27 @@ struct K2G {
     static constexpr int szVs = align16(VR * LDV * 2);
     static constexpr int oVs = align16(oUt + BV * LDU * 2);         // V    [2][VR][LDV] bf16
     static constexpr int oOs = oVs + 2 * szVs;                      // o    [C][LDO] bf16
-    static constexpr int LDS = align16(oOs + C * LDO * 2);
+    static constexpr int oSc = align16(oOs + C * LDO * 2);          // e^{G_C} [2][D] fp32
+    static constexpr int LDS = oSc + 2 * 4 * D;
 };
 
 template <int NR, int KSL>
 struct FragSet {
-    bf16x8 R[NR];   // role operands: -W and T' (U waves), Ql and P (output waves), v (movers)
-    bf16x8 K[KSL];  // Kr^T row block (state waves)
-    f32x4 er, lm;   // scales of the state rows
+    bf16x8 R[NR];   // role operands: -W and T' (U), Q^ and P^ (output), Kr^T (state), v (movers)
+    uint2 sc;       // movers: one 8-byte piece of the chunk's decay
 };
 
 // VV: every value slice is whole (d_v a multiple of BV) and v is 16-byte
 // aligned, so values and outputs move as 16-byte row pieces.
 template <int C, int D, int BV, bool VV>
-__global__ void __launch_bounds__(NTHREADS)
+__global__ void __launch_bounds__((K2G<C, D, BV>::NT))
 eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16 *__restrict__ o,
                const char *__restrict__ ws, int Tlen, int H, int BH, int dk, int dv, int NC, int R) {
     using G = K2G<C, D, BV>;
     using F = Fac<C, D>;
     using T = bf16;
     constexpr int NCB = G::NCB, KSD = G::KSD, KSL = G::KSL, LDT = G::LDT, LDU = G::LDU;
-    constexpr int LDV = G::LDV, LDO = G::LDO, VU = G::VU, O0 = G::O0;
+    constexpr int LDV = G::LDV, LDO = G::LDO, VU = G::VU, O0 = G::O0, S0W = G::S0W, M0 = G::M0;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *St = (T *)(smem + G::oSt);
     T *Ut = (T *)(smem + G::oUt);
@@ -679,11 +744,6 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = 4 * (lane >> 4), l16 = lane & 15;
-    // mover unit: one 16-byte piece (8 columns of one token) of the value or output slice
-    const int mu = (wave - G::H0) * 64 + lane;
-    const bool mact = mu >= 0 && mu < VU;
-    const int muc = mact ? mu : 0;
-    const int mtau = muc / (BV / 8), mn = 8 * (muc % (BV / 8));
 
     if constexpr (C < G::VR) {
         // the value rows beyond the chunk are read by the k = 32 product: zero them
@@ -693,47 +753,37 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
         }
     }
 
-    // ---- initial state: rows 16 wave + g4 + i, columns n0 + 16 cb + l16 --------
-    f32x4 S[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        S[cb] = zero4();
-        if (wave < G::NBD && S0) {
-            const int col = n0 + 16 * cb + l16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * wave + g4 + i;
-                if (row < dk && col < dv) S[cb][i] = S0[sbase + (long)row * dv + col];
-            }
-        }
-    }
-
-    // One chunk loop per combination of roles, so that each wave runs straight-
-    // line code with a fixed number of memory operations per chunk: the
-    // operands of chunk c + 2 are fetched (addresses clamped, never skipped)
-    // while chunk c is computed, and the waits before each use only cover the
-    // fetches of two chunks earlier.
-    auto run = [&](auto ru, auto ro, auto rm, auto rs) __attribute__((always_inline)) {
-        constexpr bool RU = decltype(ru)::value, RO = decltype(ro)::value;
-        constexpr bool RM = decltype(rm)::value, RS = decltype(rs)::value;
+    // One chunk loop per role: straight-line code with a fixed number of
+    // memory operations per chunk, so the waits before each use only cover
+    // operands fetched two chunks earlier (chunk indices clamped, never skipped).
+    auto run = [&](auto role) __attribute__((always_inline)) {
+        constexpr int RL = decltype(role)::value;   // 0 U, 1 state, 2 output, 3 mover
+        constexpr bool RU = RL == 0, RS = RL == 1, RO = RL == 2, RM = RL == 3;
         using Set = FragSet<G::NR, KSL>;
+        const int rb = RU ? wave : (RS ? wave - S0W : (RO ? wave - O0 : 0));   // row block of the role
+        const int mu = (wave - M0) * 64 + lane;                                 // mover unit
+        const bool mact = RM && mu < VU;
+        const int muc = mact ? mu : 0;
+        const int mtau = muc / (BV / 8), mn = 8 * (muc % (BV / 8));
 
-        auto load_set = [&](Set &s, int c) __attribute__((always_inline)) {
+        auto load = [&](Set &s, int c) __attribute__((always_inline)) {
             const char *blk = wsh + (long)c * F::bytes;
             if constexpr (RU) {
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
-                    s.R[ks] = ld_frag(blk + F::oWn + ((wave * KSD + ks) * 64 + lane) * 16);
-                s.R[KSD] = ld_frag(blk + F::oTv + (wave * 64 + lane) * 16);
+                    s.R[ks] = ld_frag(blk + F::oWn + ((rb * KSD + ks) * 64 + lane) * 16);
+                s.R[KSD] = ld_frag(blk + F::oTv + (rb * 64 + lane) * 16);
             }
-            if constexpr (RO) {
-                const int ob = wave - O0;
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks)
-                    s.R[ks] = ld_frag(blk + F::oQl + ((ob * KSD + ks) * 64 + lane) * 16);
+            if constexpr (RS) {
 #pragma unroll
                 for (int ks = 0; ks < KSL; ++ks)
-                    s.R[KSD + ks] = ld_frag(blk + F::oP + ((ob * KSL + ks) * 64 + lane) * 16);
+                    s.R[ks] = ld_frag(blk + F::oKr + ((rb * KSL + ks) * 64 + lane) * 16);
+            }
+            if constexpr (RO) {
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+                    s.R[ks] = ld_frag(blk + F::oQh + ((rb * KSD + ks) * 64 + lane) * 16);
+                s.R[KSD] = ld_frag(blk + F::oPh + (rb * 64 + lane) * 16);
             }
             if constexpr (RM) {
                 const int t = c * C + mtau, tc = t < Tlen ? t : Tlen - 1;
@@ -753,18 +803,14 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 }
                 if (!ok) x = make_uint4(0u, 0u, 0u, 0u);
                 s.R[0] = __builtin_bit_cast(bf16x8, x);
-            }
-            if constexpr (RS) {
-#pragma unroll
-                for (int ks = 0; ks < KSL; ++ks)
-                    s.K[ks] = ld_frag(blk + F::oKr + ((wave * KSL + ks) * 64 + lane) * 16);
-                s.er = *(const f32x4 *)(blk + F::oEr + 4 * (16 * wave + g4));
-                s.lm = *(const f32x4 *)(blk + F::oLam + 4 * (16 * wave + g4));
+                s.sc = *(const uint2 *)(blk + F::oDec + 8 * (mu < G::SCU ? mu : G::SCU - 1));
             }
         };
+        // movers: value slice and scales of chunk c -> LDS
         auto put_v = [&](const Set &s, int c) __attribute__((always_inline)) {
             if (mact)
                 *(uint4 *)((T *)(smem + G::oVs + (c & 1) * G::szVs) + mtau * LDV + mn) = __builtin_bit_cast(uint4, s.R[0]);
+            if (mu < G::SCU) *(uint2 *)(smem + G::oSc + (c & 1) * 4 * D + 8 * mu) = s.sc;
         };
         auto flush = [&](int cp) __attribute__((always_inline)) {
             const int t = cp * C + mtau;
@@ -781,26 +827,39 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 }
             }
         };
-        auto write_St = [&](const f32x4 &er) __attribute__((always_inline)) {
+        auto decay = [&](int c) __attribute__((always_inline)) {
+            return *(const f32x4 *)(smem + G::oSc + (c & 1) * 4 * D + 4 * (16 * rb + g4));
+        };
+
+        // state rows 16 rb + g4 + i, columns n0 + 16 cb + l16 (state role)
+        f32x4 S[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            S[cb] = zero4();
+            if (RS && S0) {
+                const int col = n0 + 16 * cb + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * rb + g4 + i;
+                    if (row < dk && col < dv) S[cb][i] = S0[sbase + (long)row * dv + col];
+                }
+            }
+        }
+        auto write_St = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
-                store4<T>(St + (16 * cb + l16) * LDT + 16 * wave + g4, er[0] * S[cb][0], er[1] * S[cb][1],
-                          er[2] * S[cb][2], er[3] * S[cb][3]);
+                store4<T>(St + (16 * cb + l16) * LDT + 16 * rb + g4, S[cb][0], S[cb][1], S[cb][2], S[cb][3]);
         };
 
         auto body = [&](Set &cur, Set &nxt, Set &fut, int c) __attribute__((always_inline)) {
-            __syncthreads();   // S'^T, the value slice of chunk c and the last outputs are in LDS
-            load_set(fut, c + 2 < NC ? c + 2 : NC - 1);
-            if constexpr (RM) {
-                if (c > 0) flush(c - 1);
-                if (c + 1 < NC) put_v(nxt, c + 1);
-            }
+            const int cf = c + 2 < NC ? c + 2 : NC - 1;   // chunk whose operands are fetched now
+            __syncthreads();   // S^T, the value slice of chunk c and its decay are in LDS
             f32x4 acc[NCB];
+            const T *Vs = (const T *)(smem + G::oVs + (c & 1) * G::szVs);
             if constexpr (RU) {
-                // U = T' V - W S'  (rows 16 wave.., all slice columns) -> U^T in LDS
+                // U = T' V - W S  (16 rows, all slice columns) -> U^T in LDS
                 // (one instruction shape for the whole accumulation chain: at C = 16
                 // the k = 32 product reads 16 zero rows of the value buffer)
-                const T *Vs = (const T *)(smem + G::oVs + (c & 1) * G::szVs);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
                     acc[cb] = mma32(cur.R[KSD], frag_col(Vs + 16 * cb, LDV, lane), zero4());
@@ -811,54 +870,55 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                         acc[cb] = mma32(cur.R[ks], frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), acc[cb]);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
-                    store4<T>(Ut + (16 * cb + l16) * LDU + 16 * wave + g4, acc[cb][0], acc[cb][1], acc[cb][2],
+                    store4<T>(Ut + (16 * cb + l16) * LDU + 16 * rb + g4, acc[cb][0], acc[cb][1], acc[cb][2],
                               acc[cb][3]);
             }
+            if constexpr (RS) load(fut, cf);
             if constexpr (RO) {
-                // o^T = S'^T Ql^T for the wave's 16 tokens (first half)
+                // o^T = S^T Q^^T + V^T P^^T for the wave's 16 tokens -> rows of o in LDS
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero4();
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[cb] = mma32(frag_col(Vs + 16 * cb, LDV, lane), cur.R[KSD], zero4());
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb)
                         acc[cb] = mma32(frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), cur.R[ks], acc[cb]);
-            }
-            __syncthreads();   // U^T complete; S'^T no longer read
-            if constexpr (RS) {
-                // S <- e^r (lam S + Kr^T U); S'^T of the next chunk
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    f32x4 a;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) a[i] = cur.lm[i] * S[cb][i];
-#pragma unroll
-                    for (int ks = 0; ks < KSL; ++ks)
-                        a = mma32(cur.K[ks], frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), a);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) S[cb][i] = cur.er[i] * a[i];
-                }
-                if (c + 1 < NC) write_St(nxt.er);
-            }
-            if constexpr (RO) {
-                // o^T += U^T P^T; rows of o -> LDS
-#pragma unroll
-                for (int ks = 0; ks < KSL; ++ks)
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
-                        acc[cb] = mma32(frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), cur.R[KSD + ks], acc[cb]);
-                const int tr = 16 * (wave - O0) + l16;
+                const int tr = 16 * rb + l16;
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
                     store4<T>(Os + tr * LDO + 16 * cb + g4, acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
             }
+            if constexpr (RM) {
+                if (c + 1 < NC) put_v(nxt, c + 1);
+                load(fut, cf);
+            }
+            __syncthreads();   // U^T and the outputs complete; S^T no longer read
+            if constexpr (RU || RO) load(fut, cf);
+            if constexpr (RS) {
+                // S <- e^{G_C} S + Kr^T U; S^T of the next chunk
+                const f32x4 dc = decay(c);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    f32x4 a;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a[i] = dc[i] * S[cb][i];
+#pragma unroll
+                    for (int ks = 0; ks < KSL; ++ks)
+                        a = mma32(cur.R[ks], frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), a);
+                    S[cb] = a;
+                }
+                if (c + 1 < NC) write_St();
+            }
+            // stores last: nothing after them waits on the vector-memory counter
+            if constexpr (RM) flush(c);
         };
 
         Set A, B, X;
-        load_set(A, 0);
-        load_set(B, NC > 1 ? 1 : 0);
+        load(A, 0);
+        load(B, NC > 1 ? 1 : 0);
         if constexpr (RM) put_v(A, 0);
-        if constexpr (RS) write_St(A.er);
+        if constexpr (RS) write_St();
         int c = 0;
         for (; c + 3 <= NC; c += 3) {
             body(A, B, X, c);
@@ -868,8 +928,6 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
         if (c < NC) body(A, B, X, c);
         if (c + 1 < NC) body(B, X, A, c + 1);
 
-        __syncthreads();
-        if constexpr (RM) flush(NC - 1);
         if constexpr (RS) {
             if (S_final) {
                 // every read of S0 happened before the chunk loop, so S_final may be S0
@@ -878,7 +936,7 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                     const int col = n0 + 16 * cb + l16;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int row = 16 * wave + g4 + i;
+                        const int row = 16 * rb + g4 + i;
                         if (row < dk && col < dv) S_final[sbase + (long)row * dv + col] = S[cb][i];
                     }
                 }
@@ -886,19 +944,10 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
         }
     };
 
-    using Y = std::true_type;
-    using N = std::false_type;
-    const bool sw = wave < G::NBD;
-    if (wave < G::NBL) {
-        if (sw) run(Y{}, N{}, N{}, Y{});
-        else if constexpr (G::NBD < G::NW) run(Y{}, N{}, N{}, N{});
-    } else if (wave >= O0) {
-        if (sw) run(N{}, Y{}, N{}, Y{});
-        else if constexpr (G::NBD < G::NW) run(N{}, Y{}, N{}, N{});
-    } else {
-        if (sw) run(N{}, N{}, Y{}, Y{});
-        else if constexpr (G::NBD < G::NW) run(N{}, N{}, Y{}, N{});
-    }
+    if (wave < S0W) run(std::integral_constant<int, 0>{});
+    else if (wave < O0) run(std::integral_constant<int, 1>{});
+    else if (wave < M0) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 3>{});
 }
 
 // ---------------------------------------------------------------------------
