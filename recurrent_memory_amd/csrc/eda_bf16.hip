@@ -54,7 +54,9 @@
 namespace eda {
 namespace b16 {
 
-constexpr int NWAVES = 8, NTHREADS = 64 * NWAVES;
+// factor kernel: 4 waves per workgroup, so that two workgroups (two chunks in
+// flight, each with its own barriers) share a compute unit
+constexpr int K1WAVES = 4, K1THREADS = 64 * K1WAVES;
 
 // wide-chunk threshold on a chunk's log2-decay (e^-120 = 2^-173)
 constexpr float WIDE_G2 = 173.f;
@@ -156,16 +158,15 @@ struct Fac {
 template <int C, int D>
 struct K1G {
     using F = Fac<C, D>;
-    static constexpr int L = 2 * C, NB = L / 16, NT = NTHREADS, NW = NWAVES;
+    static constexpr int L = 2 * C, NB = L / 16, NT = K1THREADS, NW = K1WAVES;
     static constexpr int LDA = D + 8, LDL = L + 8, ADS = 20, ASD = D + 8, MTW = 24;
     static constexpr int NQ = D / 4;
     static constexpr int TPC = imin(NT / NQ, C);       // threads per channel quad
     static constexpr int TPT = C / TPC;                // tokens per thread
     static constexpr int ACT = NQ * TPC;               // threads with an element-wise role
     static_assert((TPC & (TPC - 1)) == 0 && TPC <= 64 && C % TPC == 0 && ACT <= NT, "split");
-    static_assert(TPT == 1 || TPT == 2, "token run");
-    static constexpr int NZW = NW - NB;                // matrix waves (A and P tiles)
-    static_assert(NZW >= 1, "too few waves");
+    static_assert(TPT == 1 || TPT == 2 || TPT == 4, "token run");
+    static_assert(NB <= NW, "one diagonal block per wave");
     // raw rows of one full chunk in 16-byte units: q, e, k (bf16), alpha (fp32)
     static constexpr int RU = C * D / 8, AU = C * D / 4;
     static constexpr int PQ = (RU + NT - 1) / NT, PA = (AU + NT - 1) / NT;
@@ -193,7 +194,7 @@ struct K1G {
 // 16-byte pieces and are fetched one item ahead); otherwise every item is
 // read element-wise with zero padding.
 template <int C, int D, bool VEC>
-__global__ void __launch_bounds__(NTHREADS)
+__global__ void __launch_bounds__(K1THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ e,
                  const float *__restrict__ alpha, const float *__restrict__ beta,
                  const float *__restrict__ gamma, char *__restrict__ ws, int Tlen, int H, int dk,
@@ -202,7 +203,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     using F = Fac<C, D>;
     using T = bf16;
     constexpr int L = G::L, NB = G::NB, NT = G::NT, NW = G::NW, LDA = G::LDA, LDL = G::LDL;
-    constexpr int ADS = G::ADS, ASD = G::ASD, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT, NZW = G::NZW;
+    constexpr int ADS = G::ADS, ASD = G::ASD, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT;
     constexpr int RU = G::RU, AU = G::AU, PQ = G::PQ, PA = G::PA, WPW = G::WPW, NWT = G::NWT;
     constexpr int NBD = F::NBD, NBL = F::NBL, NBC = F::NBC, KSD = F::KSD, KSL = F::KSL;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -245,28 +246,36 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     // ---- raw rows of a chunk -> registers, fetched one item ahead.  The same
     //      fixed set of loads is issued for every item (rows clamped to the
     //      sequence), so the only wait on them is where they are staged. --------
-    static_assert(PQ == 1 && PA <= 2, "raw rows: one 16-byte piece of q, e, k and two of alpha per thread");
-    uint4 pq, pe, pk, pa0, pa1;
+    // (16-byte pieces kept in vector registers: up to 4 per tensor)
+    static_assert(PQ <= 4 && PA <= 4, "raw pieces per thread");
+    typedef unsigned __attribute__((ext_vector_type(4 * PQ))) vq_t;
+    typedef unsigned __attribute__((ext_vector_type(4 * PA))) va_t;
+    vq_t pq, pe, pk;
+    va_t pa;
+    auto put4 = [](auto &v, int m, uint4 x) __attribute__((always_inline)) {
+        v[4 * m] = x.x; v[4 * m + 1] = x.y; v[4 * m + 2] = x.z; v[4 * m + 3] = x.w;
+    };
+    auto get4 = [](const auto &v, int m) __attribute__((always_inline)) {
+        return make_uint4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
+    };
     float pbeta = 0.f, pgamma = 0.f;
     auto prefetch = [&](int it) __attribute__((always_inline)) {
         const int bh = head_of(it), cidx = chunk_of(it);
         const int b = bh / H, h = bh % H;
         const int t0 = cidx * C, last = Tlen - 1 - t0;                 // rows past `last` are clamped
         const long tok0 = ((long)b * Tlen + t0) * H + h;              // row of the chunk's first token
-        {
-            const int u = min(tid, RU - 1);
+#pragma unroll
+        for (int m = 0; m < PQ; ++m) {
+            const int u0 = tid + NT * m, u = u0 < RU ? u0 : RU - 1;
             const long off = (tok0 + (long)min(u / (D / 8), last) * H) * dk + 8 * (u % (D / 8));
-            pq = *(const uint4 *)(q + off);
-            pe = *(const uint4 *)(e + off);
-            pk = *(const uint4 *)(k + off);
+            put4(pq, m, *(const uint4 *)(q + off));
+            put4(pe, m, *(const uint4 *)(e + off));
+            put4(pk, m, *(const uint4 *)(k + off));
         }
-        {
-            const int u = min(tid, AU - 1);
-            pa0 = *(const uint4 *)(alpha + (tok0 + (long)min(u / (D / 4), last) * H) * dk + 4 * (u % (D / 4)));
-        }
-        if constexpr (PA == 2) {
-            const int u = min(tid + NT, AU - 1);
-            pa1 = *(const uint4 *)(alpha + (tok0 + (long)min(u / (D / 4), last) * H) * dk + 4 * (u % (D / 4)));
+#pragma unroll
+        for (int m = 0; m < PA; ++m) {
+            const int u0 = tid + NT * m, u = u0 < AU ? u0 : AU - 1;
+            put4(pa, m, *(const uint4 *)(alpha + (tok0 + (long)min(u / (D / 4), last) * H) * dk + 4 * (u % (D / 4))));
         }
         const long tb = tok0 + (long)min(tid % C, last) * H;
         pbeta = beta[tb];
@@ -280,16 +289,20 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         const long tok0 = ((long)b * Tlen + t0) * H + h;
         float bv = 0.f, gv = 0.f;
         if (fast) {
-            if (RU % NT == 0 || tid < RU) {
-                const int rr = tid / (D / 8), cc = 8 * (tid % (D / 8));
-                *(uint4 *)(Ql + rr * LDA + cc) = pq;
-                *(uint4 *)(Kr + (2 * rr) * LDA + cc) = pe;
-                *(uint4 *)(Kr + (2 * rr + 1) * LDA + cc) = pk;
+#pragma unroll
+            for (int m = 0; m < PQ; ++m) {
+                const int u = tid + NT * m;
+                if (RU % NT == 0 || u < RU) {
+                    const int rr = u / (D / 8), cc = 8 * (u % (D / 8));
+                    *(uint4 *)(Ql + rr * LDA + cc) = get4(pq, m);
+                    *(uint4 *)(Kr + (2 * rr) * LDA + cc) = get4(pe, m);
+                    *(uint4 *)(Kr + (2 * rr + 1) * LDA + cc) = get4(pk, m);
+                }
             }
-            if (AU % NT == 0 || tid < AU) *(uint4 *)(As + (tid / (D / 4)) * ASD + 4 * (tid % (D / 4))) = pa0;
-            if constexpr (PA == 2) {
-                const int u = tid + NT;
-                if (AU % NT == 0 || u < AU) *(uint4 *)(As + (u / (D / 4)) * ASD + 4 * (u % (D / 4))) = pa1;
+#pragma unroll
+            for (int m = 0; m < PA; ++m) {
+                const int u = tid + NT * m;
+                if (AU % NT == 0 || u < AU) *(uint4 *)(As + (u / (D / 4)) * ASD + 4 * (u % (D / 4))) = get4(pa, m);
             }
             bv = pbeta;
             gv = pgamma;
@@ -348,10 +361,6 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     for (; it < items; it += gridDim.x) {
         const int bh = head_of(it), cidx = chunk_of(it);
         stage(it, is_fast(cidx));
-        if constexpr (VEC) {
-            const int nx = it + gridDim.x;
-            prefetch(nx < items ? nx : items - 1);
-        }
         char *wsb = ws + ((long)bh * NC + cidx) * F::bytes;
         __syncthreads();
 
@@ -439,7 +448,6 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         __syncthreads();
 
         // ---- A (strictly lower) and P (causal); diagonal blocks inverted ----------
-        const int mw = wave - NB;   // matrix-wave index (< 0 on the inverse waves)
         constexpr int NOD = NB * (NB - 1) / 2;
         constexpr int NPT = NB * (C / 16);
         if (!wide) {
@@ -454,7 +462,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 wave_lds_sync();
                 invert_diag(J);
             }
-            for (int t = mw; mw >= 0 && t < NOD + NPT; t += NZW) {
+            // off-diagonal A and P tiles, spread over every wave
+            for (int t = (wave + NW - NB) % NW; t < NOD + NPT; t += NW) {
                 if (t < NOD) {
                     int J = 1, I = t;
                     while (I >= J) { I -= J; ++J; }
@@ -509,6 +518,13 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             if (act) form_operands();
         }
         __syncthreads();
+
+        // the next item's raw rows: fetched now, staged at the top of the next item
+        // (registers stay free during the scan and the operand formation)
+        if constexpr (VEC) {
+            const int nx = it + gridDim.x;
+            prefetch(nx < items ? nx : items - 1);
+        }
 
         // ---- off-diagonal blocks of (I + A)^{-1}, one column block per wave:
         //      X_JI = -X_JJ sum_{I <= K < J} A_JK X_KI, for J = I+1, I+2, ...
