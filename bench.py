@@ -2,32 +2,36 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
 
-A step is one chunked forward (`eda_fwd_chunked`; for bf16 inputs a single
-kernel that computes each chunk's factors on chip and carries the state
-through the chunks) over one batch of synthetic inputs already resident in
-HBM.
-The default workload is the training shape B=4, H=16, T=2048,
+A step is one chunked forward (`eda_fwd_chunked`: the chunk-factor kernel,
+then the state pass) over one batch of synthetic inputs already resident in
+HBM.  The default workload is the training shape B=4, H=16, T=2048,
 d_k=d_v=128, bf16 q/k/e/v, fp32 gates and state.  One JSON line is printed:
-tokens/s of the whole batch, the roofline of the chunked kernel (its
-average duration measured with HIP events on the launch stream), the fp64
-CPU oracle timed on the host on a bounded sample of the same workload, and a
-decode section (256 sequences x 32 heads, one token per step, state updated
-in place) with its own HBM roofline.
+tokens/s of the whole batch (wall clock around K steps), the roofline of the
+dominant kernel (its average duration from HIP events recorded on the launch
+stream around each kernel, over a second run of K steps through
+`eda_fwd_chunked_timed`), both kernels' figures, the fp64 CPU oracle timed on
+the host on a bounded sample of the same workload, and a decode section (256
+sequences x 32 heads, one token per step, state updated in place) with its own
+HBM roofline.
 
-Algorithmic work used for the rooflines (d_k = d_v = d, C tokens per chunk,
-L = 2C sub-steps; each token is an erase sub-step and a delta sub-step):
-  canonical chunk-form multiply-adds per chunk-head, state independent:
-      L^2 d (decayed Gram) + L^3/6 (triangular inverse) + L^2 d (W factor)
-      + C L d (query-key products)
-  and state dependent:
-      L d^2 (W S) + L C d (value part of U) + C d^2 (query-state product)
-      + C L d (intra-chunk output) + L d^2 (state update)
-  (counted once per chunk-head, however often the kernel recomputes them)
-  compulsory HBM bytes per token-head: q, k, e, v and o in the storage type,
-  alpha fp32 per key channel, beta and gamma fp32; decode adds the fp32
-  state read and written once (2 d_k d_v 4 bytes).
+Algorithmic work (d_k = d_v = d, C tokens per chunk, L = 2C sub-steps; each
+token is an erase sub-step and a delta sub-step), per chunk and head:
+  chunk factors: L^2 d (decayed Gram) + L^3/6 (triangular inverse)
+                 + L^2 d (W factor) + C L d (query-key products)  multiply-adds
+  state pass:    L d^2 (W S) + L C d (value part of U) + C d^2 (query-state
+                 product) + C L d (intra-chunk output) + L d^2 (state update)
+(counted once, however often a kernel recomputes them).  Algorithmic bytes per
+token and head: the factor kernel must read q, k, e (storage type), alpha
+(fp32 per key channel), beta and gamma (fp32); the state pass must read v and
+write o (storage type), plus the fp32 initial state read and final state
+written once per head.  The whole path moves the sum (1800 B per token-head
+for bf16, d = 128).  Decode moves the fp32 state in and out once per step
+(2 d_k d_v 4 bytes) plus the token's inputs and output.
 Peaks: MI355X dense bf16 matrix 2.5 PFLOP/s, fp32 matrix 157.3 TFLOP/s,
-HBM3E 8 TB/s.
+HBM3E 8 TB/s.  `traffic` is the measured HBM bytes per launch of the dominant
+kernel (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known
+size), read from the committed summary under profiles/ and reported only while
+the kernel source it was measured on is unchanged.
 """
 from __future__ import annotations
 
@@ -61,14 +65,35 @@ def state_macs_per_chunk_head(C: int, d: int) -> float:
 
 
 def token_bytes(dk: int, dv: int, es: int) -> dict:
-    """Compulsory bytes per token-head, split by the kernel that moves them."""
-    intra = 3 * dk * es + dk * 4 + 2 * 4          # q, k, e, alpha, beta, gamma
-    state = dv * es + 4 + dv * es                 # v, beta (re-read), o
-    return dict(intra=intra, state=state, chunked=3 * dk * es + dv * es + dk * 4 + 8 + dv * es)
+    """Algorithmic bytes per token-head, split by the kernel that must move them."""
+    factors = 3 * dk * es + dk * 4 + 2 * 4        # q, k, e, alpha, beta, gamma
+    state = dv * es + dv * es                     # v, o
+    return dict(factors=factors, state=state, chunked=factors + state)
 
 
 def decode_bytes_per_head(dk: int, dv: int, es: int) -> int:
     return 2 * dk * dv * 4 + (3 * dk + dv) * es + dk * 4 + 8 + dv * es
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    src = os.path.join(ROOT, "recurrent_memory_amd", "csrc", kv.get("source", ""))
+    if not os.path.exists(src) or hashlib.sha1(open(src, "rb").read()).hexdigest() != kv.get("source_sha1"):
+        return None
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # ---------------------------------------------------------------------------
@@ -139,8 +164,7 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     # timed region: wall clock around K steps, and HIP events on the launch
-    # stream (bf16 runs one kernel per step, so event time / K is the average
-    # duration of that kernel)
+    # stream around the whole loop
     s = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -157,29 +181,68 @@ def main() -> int:
     print(f"[bench] {ms_per_step:.4f} ms/step (events {ms_kernel:.4f} ms), {value:.4g} tokens/s",
           file=sys.stderr, flush=True)
 
+    # per-kernel durations: the same K steps again through the timed entry
+    # point (HIP events recorded by the library on the launch stream)
+    trip = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for t3 in trip:
+        for ev in t3:
+            ev.record(s)   # materialise the events before handing them over
+    torch.cuda.synchronize()
+    for t3 in trip:
+        eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
+                        chunk=chunk, out=o, S_final=S_final, workspace=ws,
+                        events=[ev.cuda_event for ev in t3])
+    torch.cuda.synchronize()
+    ms_k1 = sum(t3[0].elapsed_time(t3[1]) for t3 in trip) / args.steps
+    ms_k2 = sum(t3[1].elapsed_time(t3[2]) for t3 in trip) / args.steps
+
     d = dk  # d_k = d_v on every measured workload
     NC = (T + chunk - 1) // chunk
     n_ch = B * H * NC
     tb = token_bytes(dk, dv, es)
     peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    flop = 2 * (intra_macs_per_chunk_head(chunk, d) + state_macs_per_chunk_head(chunk, d)) * n_ch
-    byts = tb["chunked"] * B * T * H + (2 if x["S0"] is not None else 1) * B * H * dk * dv * 4
+    state_io = (2 if x["S0"] is not None else 1) * B * H * dk * dv * 4
+    work = {
+        "factors": dict(flop=2 * intra_macs_per_chunk_head(chunk, d) * n_ch,
+                        bytes=tb["factors"] * B * T * H, ms=ms_k1),
+        "state": dict(flop=2 * state_macs_per_chunk_head(chunk, d) * n_ch,
+                      bytes=tb["state"] * B * T * H + state_io, ms=ms_k2),
+    }
+    names = dict(factors="eda_bf16_factors", state="eda_bf16_state") if w.dtype == "bf16" else \
+        dict(factors="eda_chunk_intra", state="eda_chunk_state")
+
+    def roof(kind: str) -> dict:
+        wk = work[kind]
+        sec = wk["ms"] * 1e-3
+        # the binding roofline at the algorithmic level is the one with the larger floor
+        mfma = wk["flop"] / (peak_mm * 1e12) >= wk["bytes"] / (PEAK_HBM_GBS * 1e9)
+        if mfma:
+            ach = wk["flop"] / sec / 1e12
+            r = dict(kernel=names[kind], bound="mfma", achieved=round(ach, 3), peak=peak_mm,
+                     unit="TFLOP/s", frac=round(ach / peak_mm, 5))
+        else:
+            ach = wk["bytes"] / sec / 1e9
+            r = dict(kernel=names[kind], bound="hbm", achieved=round(ach, 2), peak=PEAK_HBM_GBS,
+                     unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 5))
+        r.update(ms=round(wk["ms"], 5), algorithmic_bytes=wk["bytes"], algorithmic_flop=wk["flop"])
+        return r
+
+    kernels = {k: roof(k) for k in work}
+    dom = max(work, key=lambda k: work[k]["ms"])
+    roof_line = dict(kernels[dom])
+    roof_line["traffic"] = measured_traffic(names[dom], w.name)
+    for k in ("ms", "algorithmic_bytes", "algorithmic_flop"):
+        roof_line.pop(k)
+
+    flop = work["factors"]["flop"] + work["state"]["flop"]
+    byts = tb["chunked"] * B * T * H + state_io
     tflops = flop / (ms_kernel * 1e-3) / 1e12
     gbs = byts / (ms_kernel * 1e-3) / 1e9
-    # the binding roofline at the algorithmic level is the one with the larger floor
-    mfma_bound = flop / (peak_mm * 1e12) >= byts / (PEAK_HBM_GBS * 1e9)
-    kname = "eda_chunk_fused"
-    if mfma_bound:
-        roof = dict(kernel=kname, bound="mfma", achieved=round(tflops, 3), peak=peak_mm,
-                    unit="TFLOP/s", frac=round(tflops / peak_mm, 5), traffic=None)
-    else:
-        roof = dict(kernel=kname, bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS,
-                    unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 5), traffic=None)
     path = dict(kernel_ms=round(ms_kernel, 5), canonical_flop=flop, compulsory_bytes=byts,
                 mfma_tflops=round(tflops, 3), mfma_frac=round(tflops / peak_mm, 5),
                 hbm_gbs=round(gbs, 2), hbm_frac=round(gbs / PEAK_HBM_GBS, 5),
                 canonical_flop_per_token_head=flop / (B * T * H),
-                compulsory_bytes_per_token_head=tb["chunked"])
+                compulsory_bytes_per_token_head=tb["chunked"], kernels=kernels)
     print(f"[bench] chunked path: {json.dumps(path)}", file=sys.stderr, flush=True)
 
     # decode: N sequences x H heads, one token per step, state in place
@@ -239,7 +302,7 @@ def main() -> int:
                              f"{w.dtype} inputs, fp32 gates and state, chunk={chunk}",
                     B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, tokens_per_step=tokens,
                     parallelism="single GPU"),
-        roofline=roof, cpu_baseline=cpu, chunked_path=path, decode=decode)
+        roofline=roof_line, cpu_baseline=cpu, chunked_path=path, decode=decode)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -108,6 +108,23 @@ eda_status_t eda_fwd_chunked(const void *q, const void *k, const void *e, const 
                              void *stream);
 
 /*
+ * eda_fwd_chunked, additionally recording three caller-created HIP events
+ * (hipEvent_t values passed as void *) on `stream`: events[0] before the
+ * chunk-factor kernel, events[1] between it and the state pass, events[2]
+ * after the state pass, so a caller can time the two kernels separately
+ * (benchmarks and profiling).  `events` may be NULL, which makes the call
+ * identical to eda_fwd_chunked; otherwise all three must be valid events of
+ * the stream's device.  Events are recorded only once every argument check
+ * has passed.
+ */
+eda_status_t eda_fwd_chunked_timed(const void *q, const void *k, const void *e, const void *v,
+                                   const float *alpha, const float *beta, const float *gamma,
+                                   const float *S0, void *o, float *S_final,
+                                   int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
+                                   int chunk, void *workspace, size_t workspace_bytes,
+                                   void *stream, void *const *events);
+
+/*
  * One token of the recurrence for N independent sequences (decode).
  *
  * For each (n, h): reads S_in once, applies decay, erase and corrected write

@@ -63,6 +63,9 @@ def load_library():
     lib.eda_fwd_chunked.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, vp, fp,
                                     i, i, i, i, i, i, i, vp, sz, vp]
     lib.eda_fwd_chunked.restype = i
+    lib.eda_fwd_chunked_timed.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, vp, fp,
+                                          i, i, i, i, i, i, i, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.eda_fwd_chunked_timed.restype = i
     lib.eda_fwd_recurrent_step.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp, vp,
                                            i, i, i, i, i, vp]
     lib.eda_fwd_recurrent_step.restype = i
@@ -109,8 +112,12 @@ def workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, dtype: torch.dtyp
 def fwd_chunked(q, k, e, v, alpha, beta, gamma, S0=None, *, chunk: int = 0,
                 want_state: bool = True, out: Optional[torch.Tensor] = None,
                 S_final: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunk-parallel forward over [B, T, H, d] inputs; returns (o, S_final)."""
+                workspace: Optional[torch.Tensor] = None,
+                events=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunk-parallel forward over [B, T, H, d] inputs; returns (o, S_final).
+    `events`: optional three raw HIP event handles recorded before the factor
+    kernel, between the two kernels and after the state pass
+    (eda_fwd_chunked_timed)."""
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -122,14 +129,17 @@ def fwd_chunked(q, k, e, v, alpha, beta, gamma, S0=None, *, chunk: int = 0,
     need = int(lib.eda_fwd_chunked_workspace_size(B, T, H, dk, dv, dt, chunk))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    code = lib.eda_fwd_chunked(
-        _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(e, "e", q.dtype), _ptr(v, "v", q.dtype),
-        _ptr(alpha, "alpha", torch.float32), _ptr(beta, "beta", torch.float32),
-        _ptr(gamma, "gamma", torch.float32), _ptr(S0, "S0", torch.float32),
-        _ptr(out, "o", q.dtype), _ptr(S_final, "S_final", torch.float32),
-        B, T, H, dk, dv, dt, chunk, _ptr(workspace, "workspace"),
-        0 if workspace is None else workspace.numel(), _stream(q.device))
-    _check("eda_fwd_chunked", code)
+    args = (_ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(e, "e", q.dtype), _ptr(v, "v", q.dtype),
+            _ptr(alpha, "alpha", torch.float32), _ptr(beta, "beta", torch.float32),
+            _ptr(gamma, "gamma", torch.float32), _ptr(S0, "S0", torch.float32),
+            _ptr(out, "o", q.dtype), _ptr(S_final, "S_final", torch.float32),
+            B, T, H, dk, dv, dt, chunk, _ptr(workspace, "workspace"),
+            0 if workspace is None else workspace.numel(), _stream(q.device))
+    if events is None:
+        _check("eda_fwd_chunked", lib.eda_fwd_chunked(*args))
+    else:
+        evs = (ctypes.c_void_p * 3)(*[ctypes.c_void_p(int(x)) for x in events])
+        _check("eda_fwd_chunked_timed", lib.eda_fwd_chunked_timed(*args, evs))
     return out, S_final
 
 

@@ -15,11 +15,12 @@ size_t chunked_ws_t(int, int, int, int, int, int);
 template <typename T>
 hipError_t launch_chunked(int, const void *, const void *, const void *, const void *,
                           const float *, const float *, const float *, const float *, void *,
-                          float *, int, int, int, int, int, int, void *, hipStream_t);
+                          float *, int, int, int, int, int, int, void *, hipStream_t,
+                          hipEvent_t const *);
 size_t bf16_ws_bytes(int, int, int, int, int, int);
 hipError_t launch_bf16(const void *, const void *, const void *, const void *, const float *,
                        const float *, const float *, const float *, void *, float *, int, int, int,
-                       int, int, int, void *, hipStream_t);
+                       int, int, int, void *, hipStream_t, hipEvent_t const *);
 }  // namespace eda
 
 namespace {
@@ -99,7 +100,7 @@ eda_status_t chunked_call(const void *q, const void *k, const void *e, const voi
                           const float *alpha, const float *beta, const float *gamma,
                           const float *S0, void *o, float *S_final, int B, int T, int H, int d_k,
                           int d_v, eda_dtype_t dtype, int chunk, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+                          size_t workspace_bytes, void *stream, void *const *events) {
     if (!q || !k || !e || !v || !alpha || !beta || !gamma || !o) return EDA_ERR_NULL;
     if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
     if (!dims_ok(B, T, H, d_k, d_v)) return EDA_ERR_SHAPE;
@@ -142,9 +143,10 @@ eda_status_t chunked_call(const void *q, const void *k, const void *e, const voi
     hipError_t err =
         dtype == EDA_BF16
             ? eda::launch_bf16(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v,
-                               chunk, workspace, (hipStream_t)stream)
+                               chunk, workspace, (hipStream_t)stream, (hipEvent_t const *)events)
             : eda::launch_chunked<float>(3, q, k, e, v, alpha, beta, gamma, S0, o, S_final, B,
-                                         T, H, d_k, d_v, chunk, workspace, (hipStream_t)stream);
+                                         T, H, d_k, d_v, chunk, workspace, (hipStream_t)stream,
+                                         (hipEvent_t const *)events);
     return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
 }
 
@@ -158,7 +160,17 @@ eda_status_t eda_fwd_chunked(const void *q, const void *k, const void *e, const 
                              int d_k, int d_v, eda_dtype_t dtype, int chunk, void *workspace,
                              size_t workspace_bytes, void *stream) {
     return chunked_call(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v, dtype,
-                        chunk, workspace, workspace_bytes, stream);
+                        chunk, workspace, workspace_bytes, stream, nullptr);
+}
+
+eda_status_t eda_fwd_chunked_timed(const void *q, const void *k, const void *e, const void *v,
+                                   const float *alpha, const float *beta, const float *gamma,
+                                   const float *S0, void *o, float *S_final, int B, int T, int H,
+                                   int d_k, int d_v, eda_dtype_t dtype, int chunk, void *workspace,
+                                   size_t workspace_bytes, void *stream, void *const *events) {
+    if (events && (!events[0] || !events[1] || !events[2])) return EDA_ERR_NULL;
+    return chunked_call(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v, dtype,
+                        chunk, workspace, workspace_bytes, stream, events);
 }
 
 eda_status_t eda_fwd_recurrent_step(const void *q, const void *k, const void *e, const void *v,

@@ -991,7 +991,8 @@ size_t ws_bytes(int B, int Tlen, int H) {
 template <int C, int D, int BV>
 hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, const float *alpha,
                     const float *beta, const float *gamma, const float *S0, void *o, float *S_final,
-                    int B, int Tlen, int H, int dk, int dv, void *ws, hipStream_t stream) {
+                    int B, int Tlen, int H, int dk, int dv, void *ws, hipStream_t stream,
+                    hipEvent_t const *ev) {
     using G1 = K1G<C, D>;
     using G2 = K2G<C, D, BV>;
     const int NC = (Tlen + C - 1) / C, BH = B * H;
@@ -1011,16 +1012,20 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     if (err != hipSuccess) return err;
     const long items = (long)BH * NC;
     const int grid1 = (int)(items < 2L * ncu ? items : 2L * ncu);   // two per compute unit (LDS)
+    if (ev && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
     hipLaunchKernelGGL(k1, dim3((unsigned)grid1), dim3(G1::NT), G1::LDS, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)e, alpha, beta, gamma, (char *)ws, Tlen, H, dk, NC,
                        BH);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     const int R = (dv + BV - 1) / BV;
     const int grid2 = 8 * ((BH + 7) / 8) * R;
     hipLaunchKernelGGL(k2, dim3((unsigned)grid2), dim3(G2::NT), G2::LDS, stream, (const bf16 *)v, S0,
                        S_final, (bf16 *)o, (const char *)ws, Tlen, H, BH, dk, dv, NC, R);
-    return hipGetLastError();
+    err = hipGetLastError();
+    if (err == hipSuccess && ev) err = hipEventRecord(ev[2], stream);
+    return err;
 }
 
 }  // namespace b16
@@ -1036,12 +1041,13 @@ size_t bf16_ws_bytes(int B, int Tlen, int H, int dk, int dv, int chunk) {
 
 hipError_t launch_bf16(const void *q, const void *k, const void *e, const void *v, const float *alpha,
                        const float *beta, const float *gamma, const float *S0, void *o, float *S_final,
-                       int B, int Tlen, int H, int dk, int dv, int chunk, void *ws, hipStream_t stream) {
+                       int B, int Tlen, int H, int dk, int dv, int chunk, void *ws, hipStream_t stream,
+                       hipEvent_t const *ev) {
     const int D = b16::pad_dim(dk, dv), BV = b16::slice_width(B * H, D);
 #define EDA_GO(CC, DD, BB)                                                                        \
     if (chunk == CC && D == DD && BV == BB)                                                       \
         return b16::launch_t<CC, DD, BB>(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, Tlen, \
-                                         H, dk, dv, ws, stream);
+                                         H, dk, dv, ws, stream, ev);
     EDA_GO(16, 32, 16) EDA_GO(16, 32, 32) EDA_GO(16, 64, 16) EDA_GO(16, 64, 32)
     EDA_GO(16, 128, 16) EDA_GO(16, 128, 32)
     EDA_GO(32, 32, 16) EDA_GO(32, 32, 32) EDA_GO(32, 64, 16) EDA_GO(32, 64, 32)

@@ -2,7 +2,7 @@
 // intra-chunk kernel writes each chunk's state-independent factors to a
 // workspace, then a state-pass kernel carries the state through the chunks.
 // This is the fp32-input path (fp32 matrix-core products throughout); bf16
-// inputs take the single-pass kernel in eda_fused.hip.
+// inputs take the two kernels of eda_bf16.hip.
 //
 // Sub-step form.  Each token t becomes two rank-1 sub-steps of the gated
 // delta recurrence S_j = (I - b'_j kap_j kap_j^T) D_j S_{j-1} + b'_j kap_j nu_j^T
@@ -515,26 +515,30 @@ template <typename T, int C, int D>
 hipError_t launch_chunked_t(int phase, const void *q, const void *k, const void *e, const void *v,
                             const float *alpha, const float *beta, const float *gamma,
                             const float *S0, void *o, float *S_final, int B, int Tlen, int H,
-                            int dk, int dv, void *ws, hipStream_t stream) {
+                            int dk, int dv, void *ws, hipStream_t stream, hipEvent_t const *ev) {
     constexpr int BV = 32;
     const int NC = (Tlen + C - 1) / C;
     const int BH = B * H;
+    hipError_t err;
+    if (ev && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
     if (phase & 1) {
         hipLaunchKernelGGL((eda_chunk_intra<T, C, D>), dim3((unsigned)(BH * NC)), dim3(256), 0,
                            stream, (const T *)q, (const T *)k, (const T *)e, alpha, beta, gamma,
                            (char *)ws, Tlen, H, dk, NC);
-        hipError_t err = hipGetLastError();
+        err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
+    if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     if (phase & 2) {
         const int NSv = (dv + BV - 1) / BV;
         const int grid = 8 * ((BH + 7) / 8) * NSv;
         hipLaunchKernelGGL((eda_chunk_state<T, C, D, BV>), dim3((unsigned)grid), dim3(256), 0,
                            stream, (const T *)v, beta, S0, S_final, (T *)o, (const char *)ws, Tlen,
                            H, BH, dk, dv, NC, NSv);
-        return hipGetLastError();
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
-    return hipSuccess;
+    return ev ? hipEventRecord(ev[2], stream) : hipSuccess;
 }
 
 static int pad_dim(int dk, int dv) {
@@ -557,12 +561,12 @@ template <typename T>
 hipError_t launch_chunked(int phase, const void *q, const void *k, const void *e, const void *v,
                           const float *alpha, const float *beta, const float *gamma,
                           const float *S0, void *o, float *S_final, int B, int Tlen, int H, int dk,
-                          int dv, int chunk, void *ws, hipStream_t stream) {
+                          int dv, int chunk, void *ws, hipStream_t stream, hipEvent_t const *ev) {
     const int D = pad_dim(dk, dv);
 #define EDA_GO(CC, DD)                                                                          \
     if (chunk == CC && D == DD)                                                                 \
         return launch_chunked_t<T, CC, DD>(phase, q, k, e, v, alpha, beta, gamma, S0, o,        \
-                                           S_final, B, Tlen, H, dk, dv, ws, stream);
+                                           S_final, B, Tlen, H, dk, dv, ws, stream, ev);
     EDA_GO(16, 32) EDA_GO(16, 64) EDA_GO(16, 128)
     EDA_GO(32, 32) EDA_GO(32, 64) EDA_GO(32, 128)
 #undef EDA_GO
@@ -573,6 +577,6 @@ template size_t chunked_ws_t<float>(int, int, int, int, int, int);
 template hipError_t launch_chunked<float>(int, const void *, const void *, const void *,
                                           const void *, const float *, const float *, const float *,
                                           const float *, void *, float *, int, int, int, int, int,
-                                          int, void *, hipStream_t);
+                                          int, void *, hipStream_t, hipEvent_t const *);
 
 }  // namespace eda

@@ -1,0 +1,149 @@
+"""HBM traffic of the chunked forward's kernels, from rocprofv3 counters.
+
+Two steps (the first is the program rocprofv3 profiles, once per counter):
+
+    cd /tmp && export TMPDIR=/tmp
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -o t -- \\
+        python3 REPO/recurrent_memory_amd/traffic.py run --workload train
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o t -- \\
+        python3 REPO/recurrent_memory_amd/traffic.py run --workload train
+    python3 REPO/recurrent_memory_amd/traffic.py summarize FETCH_DIR WRITE_DIR --workload train
+
+`run` builds the workload's inputs, then launches a calibration kernel that
+reads and writes a known number of bytes (an fp32 scale of 256 MiB, three
+times), then three chunked forwards.  `summarize` scales each kernel's
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same counter reported
+for the calibration kernel and writes profiles/traffic_<kernel>_<workload>.txt,
+tagged with the SHA-1 of the kernel source so that stale figures are not used.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CALIB_BYTES = 256 << 20
+NCALIB = 3
+KERNELS = {"eda_bf16_factors": "eda_bf16.hip", "eda_bf16_state": "eda_bf16.hip"}
+
+
+def run(workload: str) -> None:
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import recurrent_memory_amd as eda
+    from eda_inputs import WORKLOADS, make_workload
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[workload]
+    x = make_workload(w, device=dev)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(NCALIB):
+        torch.mul(src, 1.0, out=dst)   # reads and writes CALIB_BYTES each
+    torch.cuda.synchronize()
+    for _ in range(3):
+        eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
+                        out=o, S_final=S)
+    torch.cuda.synchronize()
+    print(f"[traffic] ran calibration and 3 forwards of {workload}", flush=True)
+
+
+def per_dispatch(directory: str, counter: str):
+    """[(dispatch id, kernel name, value in KiB)] in dispatch order."""
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    tot, names = defaultdict(float), {}
+    for row in csv.DictReader(open(files[0])):
+        if row["Counter_Name"] != counter:
+            continue
+        d = int(row["Dispatch_Id"])
+        tot[d] += float(row["Counter_Value"])
+        names[d] = row["Kernel_Name"]
+    return [(d, names[d], tot[d]) for d in sorted(tot)]
+
+
+def summarize(fetch_dir: str, write_dir: str, workload: str, algorithmic: dict) -> None:
+    out = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = per_dispatch(directory, counter)
+        first_eda = next(i for i, r in enumerate(rows) if "eda_" in r[1])
+        calib = rows[first_eda - NCALIB:first_eda]
+        calib_kib = sum(r[2] for r in calib) / len(calib)
+        scale = CALIB_BYTES / (calib_kib * 1024.0)
+        for kern in KERNELS:
+            vals = [r[2] for r in rows if kern in r[1]]
+            if vals:
+                out.setdefault(kern, {})[counter] = (sum(vals) / len(vals), calib_kib, scale)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for kern, src in KERNELS.items():
+        if kern not in out or len(out[kern]) != 2:
+            continue
+        fk, fc, fs = out[kern]["FETCH_SIZE"]
+        wk, wc, wsc = out[kern]["WRITE_SIZE"]
+        sha = hashlib.sha1(open(os.path.join(HERE, "csrc", src), "rb").read()).hexdigest()
+        total = fk * 1024 * fs + wk * 1024 * wsc
+        path = os.path.join(ROOT, "profiles", f"traffic_{kern}_{workload}.txt")
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic per launch of {kern} on the {workload} workload, from rocprofv3\n"
+                    "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over instances), each\n"
+                    f"# scaled by the same counter on a calibration kernel that reads and writes\n"
+                    f"# {CALIB_BYTES} bytes.  Commands (repo at REPO):\n"
+                    "#   cd /tmp && export TMPDIR=/tmp\n"
+                    "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d F -o t -- "
+                    f"python3 REPO/recurrent_memory_amd/traffic.py run --workload {workload}\n"
+                    "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d W -o t -- "
+                    f"python3 REPO/recurrent_memory_amd/traffic.py run --workload {workload}\n"
+                    f"#   python3 REPO/recurrent_memory_amd/traffic.py summarize F W --workload {workload}\n")
+            f.write(f"kernel = {kern}\nworkload = {workload}\nsource = {src}\nsource_sha1 = {sha}\n")
+            f.write(f"calibration_bytes = {CALIB_BYTES}\n")
+            f.write(f"fetch_kib_calibration = {fc:.1f}\nfetch_scale = {fs:.4f}\nfetch_kib = {fk:.1f}\n")
+            f.write(f"write_kib_calibration = {wc:.1f}\nwrite_scale = {wsc:.4f}\nwrite_kib = {wk:.1f}\n")
+            f.write(f"fetch_bytes = {fk * 1024 * fs:.0f}\nwrite_bytes = {wk * 1024 * wsc:.0f}\n")
+            f.write(f"bytes_per_launch = {total:.0f}\n")
+            if kern in algorithmic:
+                f.write(f"algorithmic_bytes = {algorithmic[kern]:.0f}\n"
+                        f"traffic_over_algorithmic = {total / algorithmic[kern]:.3f}\n")
+        print(f"[traffic] {path}: {total / 1e6:.1f} MB per launch")
+
+
+def algorithmic_bytes(workload: str) -> dict:
+    sys.path.insert(0, ROOT)
+    from eda_inputs import WORKLOADS
+    w = WORKLOADS[workload]
+    es = 2 if w.dtype == "bf16" else 4
+    n = w.B * w.T * w.H
+    state_io = (2 if w.s0_std > 0 else 1) * w.B * w.H * w.dk * w.dv * 4
+    return {"eda_bf16_factors": n * (3 * w.dk * es + w.dk * 4 + 8),
+            "eda_bf16_state": n * (2 * w.dv * es) + state_io}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", default="train")
+    sm = sub.add_parser("summarize")
+    sm.add_argument("fetch_dir")
+    sm.add_argument("write_dir")
+    sm.add_argument("--workload", default="train")
+    a = ap.parse_args()
+    if a.cmd == "run":
+        run(a.workload)
+    else:
+        summarize(a.fetch_dir, a.write_dir, a.workload, algorithmic_bytes(a.workload))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

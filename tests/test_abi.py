@@ -26,8 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("eda_fwd_chunked", "eda_fwd_recurrent_step", "eda_fwd_chunked_workspace_size",
-              "eda_status_string"):
+    for n in ("eda_fwd_chunked", "eda_fwd_chunked_timed", "eda_fwd_recurrent_step",
+              "eda_fwd_chunked_workspace_size", "eda_status_string"):
         assert n in names
 
 
@@ -112,6 +112,24 @@ def test_scalar_inputs_need_only_element_alignment():
 
 def test_bf16_misaligned_input_rejected():
     assert call_chunked(chunked_args(q=fake(1, 1), dt=1)) == 4
+
+
+def call_chunked_timed(a, events):
+    lib = eda.load_library()
+    return lib.eda_fwd_chunked_timed(a["q"], a["k"], a["e"], a["v"], a["alpha"], a["beta"], a["gamma"],
+                                     a["S0"], a["o"], a["S_final"], a["B"], a["T"], a["H"], a["dk"],
+                                     a["dv"], a["dt"], a["chunk"], a["ws"], a["wsb"], a["stream"], events)
+
+
+def test_timed_variant_checks_like_the_plain_call():
+    # a missing event is a NULL argument; every other check is the plain call's
+    evs = (ctypes.c_void_p * 3)(fake(20), None, fake(22))
+    assert call_chunked_timed(chunked_args(), evs) == 1
+    evs = (ctypes.c_void_p * 3)(fake(20), fake(21), fake(22))
+    assert call_chunked_timed(chunked_args(q=None), evs) == 1
+    assert call_chunked_timed(chunked_args(chunk=7), evs) == 5
+    assert call_chunked_timed(chunked_args(ws=None), evs) == 6
+    assert call_chunked_timed(chunked_args(o=fake(1, 256)), None) == 7
 
 
 def test_chunked_too_large_shape():
