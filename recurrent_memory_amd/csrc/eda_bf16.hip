@@ -103,11 +103,17 @@ __device__ __forceinline__ void st_frag(char *p, bf16x8 x) { *reinterpret_cast<b
 // `seg` is the lane's index in its group.  Groups of 16 use DPP row shifts.
 template <int N>
 __device__ __forceinline__ float scan_group(float x, int seg) {
-    if constexpr (N == 16) {
+    // DPP row shifts (rows of 16 lanes; lanes shifted in from outside the row read 0)
 #define EDA_ROW_SHR(n) \
-        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + (n), 0xf, 0xf, true))
-        EDA_ROW_SHR(1); EDA_ROW_SHR(2); EDA_ROW_SHR(4); EDA_ROW_SHR(8);
-#undef EDA_ROW_SHR
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + (n), 0xf, 0xf, true))
+    if constexpr (N == 16) {
+        x += EDA_ROW_SHR(1); x += EDA_ROW_SHR(2); x += EDA_ROW_SHR(4); x += EDA_ROW_SHR(8);
+    } else if constexpr (N == 8) {
+        // the upper 8 lanes of a row must not take values from the lower 8
+        float y;
+        y = EDA_ROW_SHR(1); x += seg >= 1 ? y : 0.f;
+        y = EDA_ROW_SHR(2); x += seg >= 2 ? y : 0.f;
+        y = EDA_ROW_SHR(4); x += seg >= 4 ? y : 0.f;
     } else {
 #pragma unroll
         for (int off = 1; off < N; off <<= 1) {
@@ -115,6 +121,7 @@ __device__ __forceinline__ float scan_group(float x, int seg) {
             if (seg >= off) x += y;
         }
     }
+#undef EDA_ROW_SHR
     return x;
 }
 
@@ -124,6 +131,9 @@ __device__ __forceinline__ float group_last(float x) {
     if constexpr (N == 16) {
         // ds_swizzle bit mode: lane' = (lane & 0x10) | 0xF within each 32 lanes
         return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F0));
+    } else if constexpr (N == 8) {
+        // lane' = (lane & 0x18) | 0x7
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0xF8));
     } else {
         return __shfl(x, N - 1, N);
     }
@@ -214,7 +224,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     T *Wst = Kr;                             // -W, after the Kr^T export [L][LDA]
     T *Ql = (T *)(smem + G::oQl);            // Ql                       [C][LDA]
     T *Abf = (T *)(smem + G::oAbf);          // A, off-diagonal 16-blocks [L][LDL]
-    float *Ad = (float *)(smem + G::oAd);    // A, diagonal 16-blocks    [NB][16][ADS]
+    float *AdT = (float *)(smem + G::oAd);   // A, diagonal 16-blocks, transposed: [J][p][i] = A_J[i][p]
     T *MI = (T *)(smem + G::oMI);            // (I + A)^{-1}             [L][LDL]
     T *MT = (T *)(smem + G::oMT);            // its diagonal blocks, transposed [NB][16][MTW]
     T *Ps = (T *)(smem + G::oPs);            // P (causal)               [C][LDL]
@@ -329,22 +339,23 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
     };
 
-    // ---- diagonal 16x16 blocks of (I + A)^{-1}: fp32 forward substitution ------
+    // ---- diagonal 16x16 blocks of (I + A)^{-1}: fp32 forward substitution, one
+    //      column per lane, column-oriented so each step's 15 updates are independent
     auto invert_diag = [&](int J) __attribute__((always_inline)) {
         if (lane < 16) {
             const int col = lane;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const f32x4 *arow = (const f32x4 *)(Ad + (J * 16 + i) * ADS);
+            for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
+#pragma unroll
+            for (int p = 0; p < 15; ++p) {
+                const f32x4 *acol = (const f32x4 *)(AdT + (J * 16 + p) * ADS);   // A[.][p]
                 f32x4 av[4];
 #pragma unroll
                 for (int v4 = 0; v4 < 4; ++v4)
-                    if (4 * v4 < i) av[v4] = arow[v4];
-                float sum = (i == col) ? 1.f : 0.f;
+                    if (4 * v4 + 3 > p) av[v4] = acol[v4];
 #pragma unroll
-                for (int p = 0; p < i; ++p) sum -= av[p >> 2][p & 3] * x[p];
-                x[i] = sum;
+                for (int i = p + 1; i < 16; ++i) x[i] -= av[i >> 2][i & 3] * x[p];
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) MI[(16 * J + i) * LDL + 16 * J + col] = from_f32<T>(x[i]);
@@ -454,11 +465,10 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             if (wave < NB) {
                 const int J = wave;
                 const f32x4 a = tile_nt<T, D>(Kl + 16 * J * LDA, LDA, Kr + 16 * J * LDA, LDA, zero4(), lane);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int jl = g4 + rr;
-                    Ad[(J * 16 + jl) * ADS + l16] = (jl > l16) ? a[rr] : 0.f;
-                }
+                // lane holds A[g4 + rr][l16]: one column run of the transposed block
+                *(f32x4 *)(AdT + (J * 16 + l16) * ADS + g4) =
+                    f32x4{g4 > l16 ? a[0] : 0.f, g4 + 1 > l16 ? a[1] : 0.f, g4 + 2 > l16 ? a[2] : 0.f,
+                          g4 + 3 > l16 ? a[3] : 0.f};
                 wave_lds_sync();
                 invert_diag(J);
             }
@@ -497,7 +507,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                              exp2f_(Gs[tj * D + cc] - Gs[ti * D + cc]);
                     s *= bp[j];
                 }
-                if ((j >> 4) == (ii >> 4)) Ad[((j >> 4) * 16 + (j & 15)) * ADS + (ii & 15)] = s;
+                if ((j >> 4) == (ii >> 4)) AdT[((j >> 4) * 16 + (ii & 15)) * ADS + (j & 15)] = s;
                 else if (ii < j) Abf[j * LDL + ii] = from_f32<T>(s);
             }
             for (int idx = tid; idx < C * L; idx += NT) {
