@@ -16,138 +16,156 @@
 // This is an exact algebraic restatement of Eqs. (11) and (13) (substitute
 // St = Sh - gamma e r_e^T into St^T k and S_new^T q).  The paper's Sec. 3.5
 // notes the decode cost is dominated by reading and writing the state; the
-// kernel is therefore laid out for HBM streaming: one workgroup per state,
-// 256 threads, each thread owns a 4-column strip of 16 rows (rows rg + 8m),
-// so every wavefront load/store instruction touches 1 KB of contiguous
-// memory, and all 16 loads of a thread are in flight together.
+// kernel is therefore laid out for HBM streaming.  A persistent grid of
+// 512-thread workgroups (four per compute unit) walks the states; per state
+// each thread owns a 4-column strip of 8 rows (rows rg + 16m), so every
+// wavefront load/store instruction touches 1 KB of contiguous memory and all
+// 8 loads of a thread are in flight together.  The state is touched exactly
+// once per step, so its loads and stores carry the non-temporal hint (no
+// reuse is expected from the caches; measured ~15% faster than plain
+// accesses at 8192 states of 64 KB).
 #include "eda_common.h"
 
 namespace eda {
 
+constexpr int DEC_NT = 512;           // threads per workgroup
+constexpr int DEC_RG = DEC_NT / 32;   // row groups (32 column quads per row)
+constexpr int DEC_R = 128 / DEC_RG;   // rows per thread
+constexpr int DEC_NW = DEC_NT / 64;   // wavefronts
+
 template <typename Tin, bool FULL>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(DEC_NT)
 eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ e,
                   const Tin *__restrict__ v, const float *__restrict__ alpha,
                   const float *__restrict__ beta, const float *__restrict__ gamma,
-                  const float *S_in, float *S_out, Tin *__restrict__ o, int dk, int dv) {
-    constexpr int R = 16;  // rows per thread
+                  const float *S_in, float *S_out, Tin *__restrict__ o, long NH, int dk, int dv) {
+    constexpr int R = DEC_R, RG = DEC_RG;
     __shared__ float sq[128], sk[128], se[128], sa[128];
-    __shared__ float red[4][3][128];
+    __shared__ float red[DEC_NW][3][128];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cq = tid & 31, rg = tid >> 5;  // column quad, row group
-    const long nh = blockIdx.x;
     if (FULL) { dk = 128; dv = 128; }
 
-    if (tid < 128) {
-        const bool ok = tid < dk;
-        sq[tid] = ok ? to_f32(q[nh * dk + tid]) : 0.f;
-        sk[tid] = ok ? to_f32(k[nh * dk + tid]) : 0.f;
-        se[tid] = ok ? to_f32(e[nh * dk + tid]) : 0.f;
-        sa[tid] = ok ? alpha[nh * dk + tid] : 0.f;
-    }
+    for (long nh = blockIdx.x; nh < NH; nh += gridDim.x) {
+        if (tid < 128) {
+            const bool ok = tid < dk;
+            sq[tid] = ok ? to_f32(q[nh * dk + tid]) : 0.f;
+            sk[tid] = ok ? to_f32(k[nh * dk + tid]) : 0.f;
+            se[tid] = ok ? to_f32(e[nh * dk + tid]) : 0.f;
+            sa[tid] = ok ? alpha[nh * dk + tid] : 0.f;
+        }
 
-    // Read the whole state strip first (independent of the vectors above).
-    float s[R][4];
-    const long sbase = nh * (long)dk * dv;
-    if (S_in) {
-        if (FULL) {
+        // Read the whole state strip first (independent of the vectors above).
+        float s[R][4];
+        const long sbase = nh * (long)dk * dv;
+        if (S_in) {
+            if (FULL) {
 #pragma unroll
-            for (int m = 0; m < R; ++m) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(S_in + sbase + (rg + 8 * m) * 128 + 4 * cq);
-                s[m][0] = x[0]; s[m][1] = x[1]; s[m][2] = x[2]; s[m][3] = x[3];
+                for (int m = 0; m < R; ++m) {
+                    const f32x4 x = __builtin_nontemporal_load(
+                        reinterpret_cast<const f32x4 *>(S_in + sbase + (rg + RG * m) * 128 + 4 * cq));
+                    s[m][0] = x[0]; s[m][1] = x[1]; s[m][2] = x[2]; s[m][3] = x[3];
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < R; ++m)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int i = rg + RG * m, j = 4 * cq + c;
+                        s[m][c] = (i < dk && j < dv) ? S_in[sbase + (long)i * dv + j] : 0.f;
+                    }
             }
         } else {
 #pragma unroll
             for (int m = 0; m < R; ++m)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int i = rg + 8 * m, j = 4 * cq + c;
-                    s[m][c] = (i < dk && j < dv) ? S_in[sbase + (long)i * dv + j] : 0.f;
-                }
+                for (int c = 0; c < 4; ++c) s[m][c] = 0.f;
         }
-    } else {
-#pragma unroll
-        for (int m = 0; m < R; ++m)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) s[m][c] = 0.f;
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // Address overlaps (k.e, q.e, q.k); every wave reduces them itself.
-    const float x0 = sk[lane] * se[lane] + sk[lane + 64] * se[lane + 64];
-    const float x1 = sq[lane] * se[lane] + sq[lane + 64] * se[lane + 64];
-    const float x2 = sq[lane] * sk[lane] + sq[lane + 64] * sk[lane + 64];
-    const float ke = wave_sum(x0), qe = wave_sum(x1), qk = wave_sum(x2);
+        // Address overlaps (k.e, q.e, q.k); every wave reduces them itself.
+        const float x0 = sk[lane] * se[lane] + sk[lane + 64] * se[lane + 64];
+        const float x1 = sq[lane] * se[lane] + sq[lane + 64] * se[lane + 64];
+        const float x2 = sq[lane] * sk[lane] + sq[lane + 64] * sk[lane + 64];
+        const float ke = wave_sum(x0), qe = wave_sum(x1), qk = wave_sum(x2);
 
-    // Decay folded into the reductions: Sh[i][j] = a_i S[i][j].
-    float pe[4] = {0, 0, 0, 0}, pk[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
+        // Decay folded into the reductions: Sh[i][j] = a_i S[i][j].
+        float pe[4] = {0, 0, 0, 0}, pk[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int m = 0; m < R; ++m) {
-        const int i = rg + 8 * m;
-        const float a = sa[i], ae = a * se[i], ak = a * sk[i], aq = a * sq[i];
+        for (int m = 0; m < R; ++m) {
+            const int i = rg + RG * m;
+            const float a = sa[i], ae = a * se[i], ak = a * sk[i], aq = a * sq[i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                pe[c] += ae * s[m][c];
+                pk[c] += ak * s[m][c];
+                pq[c] += aq * s[m][c];
+            }
+        }
+        // Sum over the row groups: two per wave (lane and lane^32), then the waves.
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            pe[c] += ae * s[m][c];
-            pk[c] += ak * s[m][c];
-            pq[c] += aq * s[m][c];
+            pe[c] += __shfl_xor(pe[c], 32, 64);
+            pk[c] += __shfl_xor(pk[c], 32, 64);
+            pq[c] += __shfl_xor(pq[c], 32, 64);
         }
-    }
-    // Sum over the 8 row groups: two per wave (lane and lane^32), then 4 waves.
+        if (lane < 32) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        pe[c] += __shfl_xor(pe[c], 32, 64);
-        pk[c] += __shfl_xor(pk[c], 32, 64);
-        pq[c] += __shfl_xor(pq[c], 32, 64);
-    }
-    if (lane < 32) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            red[wave][0][4 * cq + c] = pe[c];
-            red[wave][1][4 * cq + c] = pk[c];
-            red[wave][2][4 * cq + c] = pq[c];
+            for (int c = 0; c < 4; ++c) {
+                red[wave][0][4 * cq + c] = pe[c];
+                red[wave][1][4 * cq + c] = pk[c];
+                red[wave][2][4 * cq + c] = pq[c];
+            }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    const float b = beta[nh], g = gamma[nh];
-    float re[4], u[4], ov[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int j = 4 * cq + c;
-        re[c] = red[0][0][j] + red[1][0][j] + red[2][0][j] + red[3][0][j];
-        const float rhk = red[0][1][j] + red[1][1][j] + red[2][1][j] + red[3][1][j];
-        const float rhq = red[0][2][j] + red[1][2][j] + red[2][2][j] + red[3][2][j];
-        const float vj = (j < dv) ? to_f32(v[nh * dv + j]) : 0.f;
-        const float rk = rhk - g * ke * re[c];
-        u[c] = b * (vj - rk);
-        ov[c] = rhq - g * qe * re[c] + qk * u[c];
-    }
-    if (rg == 0) {
+        const float b = beta[nh], g = gamma[nh];
+        float re[4], u[4], ov[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int j = 4 * cq + c;
-            if (j < dv) o[nh * dv + j] = from_f32<Tin>(ov[c]);
+            float r0 = 0.f, r1 = 0.f, r2 = 0.f;
+#pragma unroll
+            for (int w = 0; w < DEC_NW; ++w) {
+                r0 += red[w][0][j];
+                r1 += red[w][1][j];
+                r2 += red[w][2][j];
+            }
+            re[c] = r0;
+            const float vj = (j < dv) ? to_f32(v[nh * dv + j]) : 0.f;
+            const float rk = r1 - g * ke * r0;
+            u[c] = b * (vj - rk);
+            ov[c] = r2 - g * qe * r0 + qk * u[c];
         }
-    }
-
-    // S_new = Sh - gamma e r_e^T + k u^T, written once.
-#pragma unroll
-    for (int m = 0; m < R; ++m) {
-        const int i = rg + 8 * m;
-        const float a = sa[i], ge = g * se[i], kk = sk[i];
-        float w[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) w[c] = a * s[m][c] - ge * re[c] + kk * u[c];
-        if (FULL) {
-            *reinterpret_cast<f32x4 *>(S_out + sbase + i * 128 + 4 * cq) = f32x4{w[0], w[1], w[2], w[3]};
-        } else {
+        if (rg == 0) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int j = 4 * cq + c;
-                if (i < dk && j < dv) S_out[sbase + (long)i * dv + j] = w[c];
+                if (j < dv) o[nh * dv + j] = from_f32<Tin>(ov[c]);
             }
         }
+
+        // S_new = Sh - gamma e r_e^T + k u^T, written once.
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+            const int i = rg + RG * m;
+            const float a = sa[i], ge = g * se[i], kk = sk[i];
+            float w[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w[c] = a * s[m][c] - ge * re[c] + kk * u[c];
+            if (FULL) {
+                __builtin_nontemporal_store(f32x4{w[0], w[1], w[2], w[3]},
+                                            reinterpret_cast<f32x4 *>(S_out + sbase + i * 128 + 4 * cq));
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int j = 4 * cq + c;
+                    if (i < dk && j < dv) S_out[sbase + (long)i * dv + j] = w[c];
+                }
+            }
+        }
+        __syncthreads();   // the shared vectors and partial sums are refilled next
     }
 }
 
@@ -156,15 +174,21 @@ hipError_t launch_decode(const void *q, const void *k, const void *e, const void
                          const float *alpha, const float *beta, const float *gamma,
                          const float *S_in, float *S_out, void *o, int N, int H, int dk, int dv,
                          hipStream_t stream) {
-    const dim3 grid((unsigned)((long)N * H)), block(256);
+    int dev = 0, ncu = 256;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    const long NH = (long)N * H;
+    const dim3 grid((unsigned)(NH < 4L * ncu ? NH : 4L * ncu)), block(DEC_NT);   // four per compute unit
     if (dk == 128 && dv == 128)
         hipLaunchKernelGGL((eda_decode_kernel<Tin, true>), grid, block, 0, stream,
                            (const Tin *)q, (const Tin *)k, (const Tin *)e, (const Tin *)v, alpha,
-                           beta, gamma, S_in, S_out, (Tin *)o, dk, dv);
+                           beta, gamma, S_in, S_out, (Tin *)o, NH, dk, dv);
     else
         hipLaunchKernelGGL((eda_decode_kernel<Tin, false>), grid, block, 0, stream,
                            (const Tin *)q, (const Tin *)k, (const Tin *)e, (const Tin *)v, alpha,
-                           beta, gamma, S_in, S_out, (Tin *)o, dk, dv);
+                           beta, gamma, S_in, S_out, (Tin *)o, NH, dk, dv);
     return hipGetLastError();
 }
 
