@@ -125,6 +125,12 @@ __device__ __forceinline__ float scan_group(float x, int seg) {
     return x;
 }
 
+// Value of lane S of each group of four lanes (DPP quad permutation).
+template <int S>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x55 * S, 0xf, 0xf, false));
+}
+
 // Value of the last lane of each group of N consecutive lanes.
 template <int N>
 __device__ __forceinline__ float group_last(float x) {
@@ -169,7 +175,7 @@ template <int C, int D>
 struct K1G {
     using F = Fac<C, D>;
     static constexpr int L = 2 * C, NB = L / 16, NT = K1THREADS, NW = K1WAVES;
-    static constexpr int LDA = D + 8, LDL = L + 8, ADS = 20, ASD = D + 8, MTW = 24;
+    static constexpr int LDA = D + 8, LDL = L + 8, ADS = 20, MTW = 24;
     static constexpr int NQ = D / 4;
     static constexpr int TPC = imin(NT / NQ, C);       // threads per channel quad
     static constexpr int TPT = C / TPC;                // tokens per thread
@@ -177,20 +183,16 @@ struct K1G {
     static_assert((TPC & (TPC - 1)) == 0 && TPC <= 64 && C % TPC == 0 && ACT <= NT, "split");
     static_assert(TPT == 1 || TPT == 2 || TPT == 4, "token run");
     static_assert(NB <= NW, "one diagonal block per wave");
-    // raw rows of one full chunk in 16-byte units: q, e, k (bf16), alpha (fp32)
-    static constexpr int RU = C * D / 8, AU = C * D / 4;
-    static constexpr int PQ = (RU + NT - 1) / NT, PA = (AU + NT - 1) / NT;
-    // W^T tiles per wave
-    static constexpr int NWT = F::NBD * F::NBL, WPW = (NWT + NW - 1) / NW;
-    // LDS (bytes).  Before the operands are formed, Kl holds the raw alpha
-    // rows (fp32 [C][ASD]), Kr the raw e and k rows, Ql the raw q rows; in a
-    // wide chunk Kl holds G (fp32 [C][D]) until the operands are formed.
-    // After the Kr^T export, the Kr region stages -W.
+    // W^T tiles
+    static constexpr int NWT = F::NBD * F::NBL;
+    // LDS (bytes).  In a wide chunk Kl holds G (fp32 [C][D]) and Kr, Ql the raw
+    // keys and queries until the operands are formed.  Once the W tiles are
+    // formed, the Kr region stages -W Diag(e^r).
     static constexpr int szKl = align16(L * LDA * 2), szQl = align16(C * LDA * 2);
-    static_assert(C * ASD * 4 <= szKl && C * D * 4 <= szKl, "Kl region reuse");
+    static_assert(C * D * 4 <= szKl, "Kl region reuse");
     static constexpr int szLL = align16(L * LDL * 2), szAd = NB * 16 * ADS * 4;
     static constexpr int szMT = NB * 16 * MTW * 2, szPs = align16(C * LDL * 2);
-    static constexpr int szMisc = (L + 2 * C + 2 * D) * 4;
+    static constexpr int szMisc = (L + 2 * C + D) * 4;
     static constexpr int LDTV = C + 8;                 // T' and P T' staging rows (after the inverse)
     static_assert(L * LDTV * 2 <= szLL && C * LDTV * 2 <= szAd, "staging reuse");
     static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oAbf = oQl + szQl;
@@ -213,12 +215,11 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     using F = Fac<C, D>;
     using T = bf16;
     constexpr int L = G::L, NB = G::NB, NT = G::NT, NW = G::NW, LDA = G::LDA, LDL = G::LDL;
-    constexpr int ADS = G::ADS, ASD = G::ASD, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT;
-    constexpr int RU = G::RU, AU = G::AU, PQ = G::PQ, PA = G::PA, WPW = G::WPW, NWT = G::NWT;
+    constexpr int ADS = G::ADS, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT;
+    constexpr int NWT = G::NWT;
     constexpr int NBD = F::NBD, NBL = F::NBL, NBC = F::NBC, KSD = F::KSD, KSL = F::KSL;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Kl = (T *)(smem + G::oKl);            // Diag(b') Kl              [L][LDA]
-    float *As = (float *)(smem + G::oKl);    // raw alpha [C][ASD] (before the operands)
     float *Gs = (float *)(smem + G::oKl);    // wide chunk: G (log2) [C][D]
     T *Kr = (T *)(smem + G::oKr);            // Kr                       [L][LDA]
     T *Wst = Kr;                             // -W, after the Kr^T export [L][LDA]
@@ -230,8 +231,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     T *Ps = (T *)(smem + G::oPs);            // P (causal)               [C][LDL]
     float *bp = (float *)(smem + G::oMisc);  // b' per sub-step          [L]
     float *sb = bp + L, *sg = sb + C;        // beta, gamma per token    [C]
-    float *glc = sg + C;                     // G_C per channel (log2)   [D]
-    float *ers = glc + D;                    // e^r per channel (1 if wide) [D]
+    float *ers = sg + C;                     // e^r per channel (1 if wide) [D]
     T *Tvs = (T *)(smem + G::oAbf);          // T', after the inverse    [L][LDTV]
     T *Phs = (T *)(smem + G::oAd);           // P T', after the inverse  [C][LDTV]
     constexpr int LDTV = G::LDTV;
@@ -253,177 +253,164 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     auto head_of = [&](int it) __attribute__((always_inline)) { return it % BH; };
     auto is_fast = [&](int cidx) __attribute__((always_inline)) { return VEC && cidx * C + C <= Tlen; };
 
-    // ---- raw rows of a chunk -> registers, fetched one item ahead.  The same
-    //      fixed set of loads is issued for every item (rows clamped to the
-    //      sequence), so the only wait on them is where they are staged. --------
-    // (16-byte pieces kept in vector registers: up to 4 per tensor)
-    static_assert(PQ <= 4 && PA <= 4, "raw pieces per thread");
-    typedef unsigned __attribute__((ext_vector_type(4 * PQ))) vq_t;
-    typedef unsigned __attribute__((ext_vector_type(4 * PA))) va_t;
-    vq_t pq, pe, pk;
-    va_t pa;
-    auto put4 = [](auto &v, int m, uint4 x) __attribute__((always_inline)) {
-        v[4 * m] = x.x; v[4 * m + 1] = x.y; v[4 * m + 2] = x.z; v[4 * m + 3] = x.w;
-    };
-    auto get4 = [](const auto &v, int m) __attribute__((always_inline)) {
-        return make_uint4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
-    };
+    // Thread (seg, quad) owns tokens TPT seg .. TPT seg + TPT - 1 of the chunk and
+    // key channels c0 .. c0 + 3 for the decay scan and the operand formation; its
+    // raw q, e, k (bf16) and alpha (fp32) values stay in registers.
+    const bool act = tid < G::ACT;
+    const int seg = tid % TPC, c0 = act ? 4 * (tid / TPC) : 0;
+    uint2 xq[TPT], xe[TPT], xk[TPT];
+    f32x4 xa[TPT];
     float pbeta = 0.f, pgamma = 0.f;
+
+    // ---- full aligned chunk: fetched one item ahead.  Rows are clamped to the
+    //      sequence so the same loads are issued for every item and the only
+    //      wait on them is where they are first used. -----------------------------
     auto prefetch = [&](int it) __attribute__((always_inline)) {
         const int bh = head_of(it), cidx = chunk_of(it);
         const int b = bh / H, h = bh % H;
-        const int t0 = cidx * C, last = Tlen - 1 - t0;                 // rows past `last` are clamped
-        const long tok0 = ((long)b * Tlen + t0) * H + h;              // row of the chunk's first token
+        const int t0 = cidx * C, last = Tlen - 1 - t0;
+        const long tok0 = ((long)b * Tlen + t0) * H + h;
 #pragma unroll
-        for (int m = 0; m < PQ; ++m) {
-            const int u0 = tid + NT * m, u = u0 < RU ? u0 : RU - 1;
-            const long off = (tok0 + (long)min(u / (D / 8), last) * H) * dk + 8 * (u % (D / 8));
-            put4(pq, m, *(const uint4 *)(q + off));
-            put4(pe, m, *(const uint4 *)(e + off));
-            put4(pk, m, *(const uint4 *)(k + off));
-        }
-#pragma unroll
-        for (int m = 0; m < PA; ++m) {
-            const int u0 = tid + NT * m, u = u0 < AU ? u0 : AU - 1;
-            put4(pa, m, *(const uint4 *)(alpha + (tok0 + (long)min(u / (D / 4), last) * H) * dk + 4 * (u % (D / 4))));
+        for (int i = 0; i < TPT; ++i) {
+            const long off = (tok0 + (long)min(TPT * seg + i, last) * H) * dk + c0;
+            xq[i] = *(const uint2 *)(q + off);
+            xe[i] = *(const uint2 *)(e + off);
+            xk[i] = *(const uint2 *)(k + off);
+            xa[i] = *(const f32x4 *)(alpha + off);
         }
         const long tb = tok0 + (long)min(tid % C, last) * H;
         pbeta = beta[tb];
         pgamma = gamma[tb];
     };
-    // ---- registers (or, for a ragged or unaligned chunk, global) -> LDS ---------
-    auto stage = [&](int it, bool fast) __attribute__((always_inline)) {
+    // ---- ragged or unaligned chunk: element-wise, zero keys and queries and
+    //      alpha = 1 outside the sequence and beyond d_k -----------------------------
+    auto fetch_slow = [&](int it) __attribute__((always_inline)) {
         const int bh = head_of(it), cidx = chunk_of(it);
         const int b = bh / H, h = bh % H;
         const int t0 = cidx * C, nval = min(C, Tlen - t0);
         const long tok0 = ((long)b * Tlen + t0) * H + h;
-        float bv = 0.f, gv = 0.f;
-        if (fast) {
 #pragma unroll
-            for (int m = 0; m < PQ; ++m) {
-                const int u = tid + NT * m;
-                if (RU % NT == 0 || u < RU) {
-                    const int rr = u / (D / 8), cc = 8 * (u % (D / 8));
-                    *(uint4 *)(Ql + rr * LDA + cc) = get4(pq, m);
-                    *(uint4 *)(Kr + (2 * rr) * LDA + cc) = get4(pe, m);
-                    *(uint4 *)(Kr + (2 * rr + 1) * LDA + cc) = get4(pk, m);
-                }
-            }
+        for (int i = 0; i < TPT; ++i) {
+            const int tau = TPT * seg + i;
+            float qv[4], ev[4], kv[4], av[4];
 #pragma unroll
-            for (int m = 0; m < PA; ++m) {
-                const int u = tid + NT * m;
-                if (AU % NT == 0 || u < AU) *(uint4 *)(As + (u / (D / 4)) * ASD + 4 * (u % (D / 4))) = get4(pa, m);
+            for (int j = 0; j < 4; ++j) {
+                const bool ok = act && tau < nval && c0 + j < dk;
+                const long off = (tok0 + (long)tau * H) * dk + c0 + j;
+                qv[j] = ok ? to_f32(q[off]) : 0.f;
+                ev[j] = ok ? to_f32(e[off]) : 0.f;
+                kv[j] = ok ? to_f32(k[off]) : 0.f;
+                av[j] = ok ? alpha[off] : 1.f;
             }
-            bv = pbeta;
-            gv = pgamma;
-        } else {
-            for (int idx = tid; idx < C * D; idx += NT) {
-                const int r = idx / D, c = idx % D;
-                const bool ok = r < nval && c < dk;
-                const long off = (tok0 + (long)r * H) * dk + c;
-                Ql[r * LDA + c] = ok ? q[off] : (T)0;
-                Kr[(2 * r) * LDA + c] = ok ? e[off] : (T)0;
-                Kr[(2 * r + 1) * LDA + c] = ok ? k[off] : (T)0;
-                As[r * ASD + c] = ok ? alpha[off] : 1.f;
-            }
-            if (tid < nval) {
-                bv = beta[tok0 + (long)tid * H];
-                gv = gamma[tok0 + (long)tid * H];
-            }
+            // (exact: the values are bf16 already)
+            xq[i] = make_uint2(pack_bf16(qv[0], qv[1]), pack_bf16(qv[2], qv[3]));
+            xe[i] = make_uint2(pack_bf16(ev[0], ev[1]), pack_bf16(ev[2], ev[3]));
+            xk[i] = make_uint2(pack_bf16(kv[0], kv[1]), pack_bf16(kv[2], kv[3]));
+            xa[i] = f32x4{av[0], av[1], av[2], av[3]};
         }
-        if (tid < C) {
-            sb[tid] = bv;
-            sg[tid] = gv;
-            bp[2 * tid] = gv;
-            bp[2 * tid + 1] = bv;
-        }
+        const bool okt = tid < nval;
+        pbeta = okt ? beta[tok0 + (long)tid * H] : 0.f;
+        pgamma = okt ? gamma[tok0 + (long)tid * H] : 0.f;
     };
 
-    // ---- diagonal 16x16 blocks of (I + A)^{-1}: fp32 forward substitution, one
-    //      column per lane, column-oriented so each step's 15 updates are independent
+    // ---- diagonal 16x16 blocks of (I + A)^{-1}: fp32 forward substitution over
+    //      the whole wave.  Lane 4 col + s holds rows 4 s .. 4 s + 3 of solution
+    //      column col; at step p every row below p takes -A[i][p] x[p], with x[p]
+    //      broadcast inside the lane quad (rows on or above p see A = 0).
     auto invert_diag = [&](int J) __attribute__((always_inline)) {
-        if (lane < 16) {
-            const int col = lane;
-            float x[16];
+        const int col = lane >> 2, s4 = 4 * (lane & 3);
+        f32x4 x;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
+        for (int i = 0; i < 4; ++i) x[i] = (s4 + i == col) ? 1.f : 0.f;
 #pragma unroll
-            for (int p = 0; p < 15; ++p) {
-                const f32x4 *acol = (const f32x4 *)(AdT + (J * 16 + p) * ADS);   // A[.][p]
-                f32x4 av[4];
+        for (int p = 0; p < 15; ++p) {
+            const f32x4 a = *(const f32x4 *)(AdT + (J * 16 + p) * ADS + s4);   // A[s4 + i][p]
+            const float xs = x[p & 3];
+            const float xp = (p >> 2) == 0 ? quad_bcast<0>(xs) : (p >> 2) == 1 ? quad_bcast<1>(xs)
+                           : (p >> 2) == 2 ? quad_bcast<2>(xs) : quad_bcast<3>(xs);
 #pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4)
-                    if (4 * v4 + 3 > p) av[v4] = acol[v4];
-#pragma unroll
-                for (int i = p + 1; i < 16; ++i) x[i] -= av[i >> 2][i & 3] * x[p];
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) MI[(16 * J + i) * LDL + 16 * J + col] = from_f32<T>(x[i]);
-            uint4 *mt = (uint4 *)(MT + (16 * J + col) * MTW);
-            mt[0] = make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
-                               pack_bf16(x[6], x[7]));
-            mt[1] = make_uint4(pack_bf16(x[8], x[9]), pack_bf16(x[10], x[11]), pack_bf16(x[12], x[13]),
-                               pack_bf16(x[14], x[15]));
+            for (int i = 0; i < 4; ++i) x[i] -= a[i] * xp;
         }
+        const uint32_t x01 = pack_bf16(x[0], x[1]), x23 = pack_bf16(x[2], x[3]);
+        T *mi = MI + (16 * J + s4) * LDL + 16 * J + col;
+        mi[0] = (T)(x01 & 0xffffu);
+        mi[LDL] = (T)(x01 >> 16);
+        mi[2 * LDL] = (T)(x23 & 0xffffu);
+        mi[3 * LDL] = (T)(x23 >> 16);
+        *(uint2 *)(MT + (16 * J + col) * MTW + s4) = make_uint2(x01, x23);
     };
 
     int it = blockIdx.x;
     if constexpr (VEC) prefetch(it);
     for (; it < items; it += gridDim.x) {
         const int bh = head_of(it), cidx = chunk_of(it);
-        stage(it, is_fast(cidx));
+        if (!is_fast(cidx)) fetch_slow(it);
+        if (tid < C) {
+            sb[tid] = pbeta;
+            sg[tid] = pgamma;
+            bp[2 * tid] = pgamma;
+            bp[2 * tid + 1] = pbeta;
+        }
         char *wsb = ws + ((long)bh * NC + cidx) * F::bytes;
-        __syncthreads();
 
-        // ---- cumulative log2-decay per channel; wide-chunk vote ------------------
-        const bool act = tid < G::ACT;
-        const int seg = tid % TPC, c0 = 4 * (tid / TPC);
+        // ---- cumulative log2-decay per channel: a sequential sum over the
+        //      thread's own tokens, then one scan of the run totals over the
+        //      TPC threads of the channel quad; wide-chunk vote -----------------------
         float g[TPT][4];
+        f32x4 glq;
         bool wide_here = false;
         {
-            float base[4] = {0.f, 0.f, 0.f, 0.f};
+            float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) {
-                // tokens seg + TPC i: one group scan per run, offset by the earlier runs' totals
-                const f32x4 pa = act ? *(const f32x4 *)(As + (seg + TPC * i) * ASD + c0)
-                                     : f32x4{1.f, 1.f, 1.f, 1.f};
+            for (int i = 0; i < TPT; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    g[i][j] = base[j] + scan_group<TPC>(__builtin_amdgcn_logf(pa[j]), seg);
-                    base[j] = group_last<TPC>(g[i][j]);
+                    run[j] += __builtin_amdgcn_logf(xa[i][j]);
+                    g[i][j] = run[j];
                 }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float incl = scan_group<TPC>(run[j], seg);
+                const float excl = incl - run[j];
+#pragma unroll
+                for (int i = 0; i < TPT; ++i) g[i][j] += excl;
+                glq[j] = group_last<TPC>(incl);   // G_C of the channel
             }
             if (act && seg == TPC - 1) {
-                *(f32x4 *)(glc + c0) = f32x4{base[0], base[1], base[2], base[3]};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wide_here |= base[j] < -WIDE_G2;
+                for (int j = 0; j < 4; ++j) wide_here |= glq[j] < -WIDE_G2;
             }
         }
         const bool wide = __syncthreads_or(wide_here) != 0;
 
-        // ---- scaled operands (LDS) and per-channel scales (workspace) -------------
-        // Forms Diag(b') Kl, Kr and Ql from the raw rows the thread owns; in a
-        // wide chunk the exponents are unsplit (Kl = kap 2^G, Kr = kap 2^{G_C - G}).
-        f32x4 glq = zero4();
+        // ---- scaled operands (LDS), Diag(e^r) Kr^T (workspace) and the
+        //      per-channel scales -------------------------------------------------------
+        // Forms Diag(b') Kl, Kr and Ql from the thread's raw values; in a wide
+        // chunk the exponents are unsplit (Kl = kap 2^G, Kr = kap 2^{G_C - G}).
+        // Diag(e^r) Kr^T = Khat^T in both cases: each thread's run of 2 TPT
+        // sub-steps of one channel is one piece of a fragment lane.
+        f32x4 er;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) er[j] = wide ? 1.f : exp2f_(0.5f * glq[j]);
         auto form_operands = [&]() __attribute__((always_inline)) {
             float r[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) r[j] = wide ? 0.f : 0.5f * glq[j];
+            uint32_t kh[4][TPT];   // Khat^T run per channel: (e, k) of each token, packed
 #pragma unroll
             for (int i = 0; i < TPT; ++i) {
-                const int tau = seg + TPC * i;
-                const uint2 pq = *(const uint2 *)(Ql + tau * LDA + c0);
-                const uint2 pe = *(const uint2 *)(Kr + (2 * tau) * LDA + c0);
-                const uint2 pk = *(const uint2 *)(Kr + (2 * tau + 1) * LDA + c0);
-                const float ev[4] = {lo_bf16(pe.x), hi_bf16(pe.x), lo_bf16(pe.y), hi_bf16(pe.y)};
-                const float kv[4] = {lo_bf16(pk.x), hi_bf16(pk.x), lo_bf16(pk.y), hi_bf16(pk.y)};
-                const float qv[4] = {lo_bf16(pq.x), hi_bf16(pq.x), lo_bf16(pq.y), hi_bf16(pq.y)};
+                const int tau = TPT * seg + i;
+                const float ev[4] = {lo_bf16(xe[i].x), hi_bf16(xe[i].x), lo_bf16(xe[i].y), hi_bf16(xe[i].y)};
+                const float kv[4] = {lo_bf16(xk[i].x), hi_bf16(xk[i].x), lo_bf16(xk[i].y), hi_bf16(xk[i].y)};
+                const float qv[4] = {lo_bf16(xq[i].x), hi_bf16(xq[i].x), lo_bf16(xq[i].y), hi_bf16(xq[i].y)};
                 const float gmt = sg[tau], btt = sb[tau];
                 float f[4], fi[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     f[j] = exp2f_(g[i][j] - r[j]);
                     fi[j] = wide ? exp2f_(glq[j] - g[i][j]) : exp2f_(r[j] - g[i][j]);
+                    const float fh = fi[j] * er[j];
+                    kh[j][i] = pack_bf16(ev[j] * fh, kv[j] * fh);
                 }
                 store4<T>(Kl + (2 * tau) * LDA + c0, gmt * ev[0] * f[0], gmt * ev[1] * f[1],
                           gmt * ev[2] * f[2], gmt * ev[3] * f[3]);
@@ -434,26 +421,38 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                           kv[3] * fi[3]);
                 store4<T>(Ql + tau * LDA + c0, qv[0] * f[0], qv[1] * f[1], qv[2] * f[2], qv[3] * f[3]);
             }
+            // fragment (16 x 32 block (n / 16, j0 / 32)), lane 16 ((j0 % 32) / 8) + n % 16, element j0 % 8
+            const int j0 = 2 * TPT * seg;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = c0 + j;
+                char *dst = wsb + F::oKr + (((n >> 4) * KSL + (j0 >> 5)) * 64 + 16 * ((j0 & 31) >> 3) + (n & 15)) * 16 +
+                            2 * (j0 & 7);
+                if constexpr (TPT == 4) *(uint4 *)dst = make_uint4(kh[j][0], kh[j][1], kh[j][2], kh[j][3]);
+                else if constexpr (TPT == 2) *(uint2 *)dst = make_uint2(kh[j][0], kh[j][1]);
+                else *(uint32_t *)dst = kh[j][0];
+            }
         };
         if (act) {
-            glq = *(const f32x4 *)(glc + c0);
             if (seg == 0) {
-                f32x4 er, dec;
+                f32x4 dec;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    er[j] = wide ? 1.f : exp2f_(0.5f * glq[j]);
-                    dec[j] = exp2f_(glq[j]);
-                }
+                for (int j = 0; j < 4; ++j) dec[j] = exp2f_(glq[j]);
                 *(f32x4 *)(ers + c0) = er;
                 *(f32x4 *)(wsb + F::oDec + 4 * c0) = dec;
             }
             if (!wide) {
-                // Kl overwrites the raw alpha rows, which were last read before the vote
                 form_operands();
             } else {
+                // raw keys and queries, and G, for the element-wise path
 #pragma unroll
-                for (int i = 0; i < TPT; ++i)
-                    *(f32x4 *)(Gs + (seg + TPC * i) * D + c0) = f32x4{g[i][0], g[i][1], g[i][2], g[i][3]};
+                for (int i = 0; i < TPT; ++i) {
+                    const int tau = TPT * seg + i;
+                    *(uint2 *)(Kr + (2 * tau) * LDA + c0) = xe[i];
+                    *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = xk[i];
+                    *(uint2 *)(Ql + tau * LDA + c0) = xq[i];
+                    *(f32x4 *)(Gs + tau * D + c0) = f32x4{g[i][0], g[i][1], g[i][2], g[i][3]};
+                }
             }
         }
         __syncthreads();
@@ -570,90 +569,57 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         __syncthreads();
 
-        // ---- W^T = Kl^T Diag(b') M^T tiles (kept in registers); Diag(e^r) Kr^T and T'
-        //      fragments -> workspace, T' also -> LDS -------------------------------------
-        // scale the 8 values of a fragment lane by sc[0..7] (fp32) and repack
-        auto scaled = [&](bf16x8 x, const float *sc) __attribute__((always_inline)) {
-            const uint4 u = __builtin_bit_cast(uint4, x);
-            const f32x4 s0 = *(const f32x4 *)sc, s1 = *(const f32x4 *)(sc + 4);
-            return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(lo_bf16(u.x) * s0[0], hi_bf16(u.x) * s0[1]),
-                                                         pack_bf16(lo_bf16(u.y) * s0[2], hi_bf16(u.y) * s0[3]),
-                                                         pack_bf16(lo_bf16(u.z) * s1[0], hi_bf16(u.z) * s1[1]),
-                                                         pack_bf16(lo_bf16(u.w) * s1[2], hi_bf16(u.w) * s1[3])));
-        };
-        f32x4 wacc[WPW];
-#pragma unroll
-        for (int m = 0; m < WPW; ++m) {
-            const int t = wave + NW * m;
-            wacc[m] = zero4();
-            if (t < NWT) {
-                const int jb = t / NBD, nb = t % NBD;
-                // M's row block jb is zero beyond column 16 (jb + 1); round up to 32
-                const int K = 32 * ((jb + 2) / 2);
-                f32x4 acc = zero4();
-                for (int k0 = 0; k0 < K; k0 += 32)
-                    acc = mma32(frag_col(Kl + k0 * LDA + 16 * nb, LDA, lane),
-                                frag_row(MI + 16 * jb * LDL + k0, LDL, lane), acc);
-                wacc[m] = acc;
-            }
+        // ---- W^T = Kl^T Diag(b') M^T tiles, staged as -W Diag(e^r) in the Kr
+        //      region (Kr was last read by the A and P tiles); T' fragments ->
+        //      workspace and LDS ---------------------------------------------------------
+        for (int t = wave; t < NWT; t += NW) {
+            const int jb = t / NBD, nb = t % NBD;
+            // M's row block jb is zero beyond column 16 (jb + 1); round up to 32
+            const int K = 32 * ((jb + 2) / 2);
+            f32x4 acc = zero4();
+            for (int k0 = 0; k0 < K; k0 += 32)
+                acc = mma32(frag_col(Kl + k0 * LDA + 16 * nb, LDA, lane),
+                            frag_row(MI + 16 * jb * LDL + k0, LDL, lane), acc);
+            // lane holds W[16 jb + l16][16 nb + g4 + i]
+            const f32x4 es = *(const f32x4 *)(ers + 16 * nb + g4);
+            store4<T>(Wst + (16 * jb + l16) * LDA + 16 * nb + g4, -acc[0] * es[0], -acc[1] * es[1],
+                      -acc[2] * es[2], -acc[3] * es[3]);
         }
-        {
-            constexpr int NKR = NBD * KSL, NEX = NKR + NBL;
-            for (int f = wave; f < NEX; f += NW) {
-                if (f < NKR) {
-                    // row n of Kr^T carries e^r_n: one scale per lane
-                    const int rb = f / KSL, ks = f % KSL;
-                    const bf16x8 x = frag_col(Kr + 32 * ks * LDA + 16 * rb, LDA, lane);
-                    const float e = ers[16 * rb + l16];
-                    const float sc[8] = {e, e, e, e, e, e, e, e};
-                    st_frag(wsb + F::oKr + (f * 64 + lane) * 16, scaled(x, sc));
-                } else {
-                    // T'[j][tau] = M[j][2 tau + 1] beta_tau (tau >= C: zero)
-                    const int rb = f - NKR, gg = lane >> 4;
-                    const T *mrow = MI + (16 * rb + l16) * LDL;
-                    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-                    if (8 * gg < C) {
-                        const uint4 u0 = *(const uint4 *)(mrow + 16 * gg);
-                        const uint4 u1 = *(const uint4 *)(mrow + 16 * gg + 8);
-                        const f32x4 b0 = *(const f32x4 *)(sb + 8 * gg), b1 = *(const f32x4 *)(sb + 8 * gg + 4);
-                        x = make_uint4(pack_bf16(hi_bf16(u0.x) * b0[0], hi_bf16(u0.y) * b0[1]),
-                                       pack_bf16(hi_bf16(u0.z) * b0[2], hi_bf16(u0.w) * b0[3]),
-                                       pack_bf16(hi_bf16(u1.x) * b1[0], hi_bf16(u1.y) * b1[1]),
-                                       pack_bf16(hi_bf16(u1.z) * b1[2], hi_bf16(u1.w) * b1[3]));
-                        *(uint4 *)(Tvs + (16 * rb + l16) * LDTV + 8 * gg) = x;
-                    }
-                    *(uint4 *)(wsb + F::oTv + (rb * 64 + lane) * 16) = x;
-                }
+        for (int rb = wave; rb < NBL; rb += NW) {
+            // T'[j][tau] = M[j][2 tau + 1] beta_tau (tau >= C: zero)
+            const int gg = lane >> 4;
+            const T *mrow = MI + (16 * rb + l16) * LDL;
+            uint4 x = make_uint4(0u, 0u, 0u, 0u);
+            if (8 * gg < C) {
+                const uint4 u0 = *(const uint4 *)(mrow + 16 * gg);
+                const uint4 u1 = *(const uint4 *)(mrow + 16 * gg + 8);
+                const f32x4 b0 = *(const f32x4 *)(sb + 8 * gg), b1 = *(const f32x4 *)(sb + 8 * gg + 4);
+                x = make_uint4(pack_bf16(hi_bf16(u0.x) * b0[0], hi_bf16(u0.y) * b0[1]),
+                               pack_bf16(hi_bf16(u0.z) * b0[2], hi_bf16(u0.w) * b0[3]),
+                               pack_bf16(hi_bf16(u1.x) * b1[0], hi_bf16(u1.y) * b1[1]),
+                               pack_bf16(hi_bf16(u1.z) * b1[2], hi_bf16(u1.w) * b1[3]));
+                *(uint4 *)(Tvs + (16 * rb + l16) * LDTV + 8 * gg) = x;
             }
-        }
-        __syncthreads();   // the Kr region is free: stage -W there
-
-        // accumulator of W^T tile (nb, jb): lane holds W[16 jb + l16][16 nb + g4 + i]
-#pragma unroll
-        for (int m = 0; m < WPW; ++m) {
-            const int t = wave + NW * m;
-            if (t < NWT) {
-                const int jb = t / NBD, nb = t % NBD;
-                store4<T>(Wst + (16 * jb + l16) * LDA + 16 * nb + g4, -wacc[m][0], -wacc[m][1],
-                          -wacc[m][2], -wacc[m][3]);
-            }
+            *(uint4 *)(wsb + F::oTv + (rb * 64 + lane) * 16) = x;
         }
         __syncthreads();
 
-        // ---- -W Diag(e^r) -> workspace; Q^ = Ql - P W (in place over Ql) and
-        //      P^ = P T' (staged), both as transposed tiles so rows leave as runs --------
+        // ---- -W Diag(e^r) -> workspace; Q^ = (Ql - P W) Diag(e^r) (in place over
+        //      Ql) and P^ = P T' (staged), both as transposed tiles so rows leave
+        //      as runs -------------------------------------------------------------------
         {
             constexpr int NWF = NBL * KSD, NQT = NBD * NBC, NPT2 = NBC * NBC;
             for (int f = wave; f < NWF + NQT + NPT2; f += NW) {
                 if (f < NWF) {
                     const int rb = f / KSD, ks = f % KSD;
-                    st_frag(wsb + F::oWn + (f * 64 + lane) * 16,
-                            scaled(frag_row(Wst + 16 * rb * LDA + 32 * ks, LDA, lane), ers + 32 * ks + 8 * (lane >> 4)));
+                    st_frag(wsb + F::oWn + (f * 64 + lane) * 16, frag_row(Wst + 16 * rb * LDA + 32 * ks, LDA, lane));
                 } else if (f < NWF + NQT) {
                     // Q^T tile (channels 16 nb.., tokens 16 tb..); P is zero beyond sub-step 2t + 1
                     const int t = f - NWF, nb = t % NBD, tb = t / NBD;
                     const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * nb + g4);
-                    f32x4 acc = {lo_bf16(q0.x), hi_bf16(q0.x), lo_bf16(q0.y), hi_bf16(q0.y)};
+                    const f32x4 es = *(const f32x4 *)(ers + 16 * nb + g4);
+                    f32x4 acc = {lo_bf16(q0.x) * es[0], hi_bf16(q0.x) * es[1], lo_bf16(q0.y) * es[2],
+                                 hi_bf16(q0.y) * es[3]};
                     const int K = imin(L, 32 * (tb + 1));
                     for (int k0 = 0; k0 < K; k0 += 32)
                         acc = mma32(frag_col(Wst + k0 * LDA + 16 * nb, LDA, lane),
@@ -677,8 +643,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             for (int f = wave; f < NQF + NBC; f += NW) {
                 if (f < NQF) {
                     const int rb = f / KSD, ks = f % KSD;
-                    st_frag(wsb + F::oQh + (f * 64 + lane) * 16,
-                            scaled(frag_row(Ql + 16 * rb * LDA + 32 * ks, LDA, lane), ers + 32 * ks + 8 * (lane >> 4)));
+                    st_frag(wsb + F::oQh + (f * 64 + lane) * 16, frag_row(Ql + 16 * rb * LDA + 32 * ks, LDA, lane));
                 } else {
                     const int rb = f - NQF;
                     uint4 x = make_uint4(0u, 0u, 0u, 0u);
