@@ -12,7 +12,11 @@ stream around each kernel, over a second run of K steps through
 `eda_fwd_chunked_timed`), both kernels' figures, the fp64 CPU oracle timed on
 the host on a bounded sample of the same workload, and a decode section (256
 sequences x 32 heads, one token per step, state updated in place) with its own
-HBM roofline.
+HBM roofline, and a layer section: the layer-form forward
+(`eda_fwd_chunked_layer`: safe gate, q/k/e normalisation and 8 key heads shared
+by 16 value heads fused into the factor kernel) beside the same computation
+unfused (the prologue as PyTorch element-wise ops, then `eda_fwd_chunked` on
+the expanded value-head inputs), and the layer-form decode step.
 
 Algorithmic work (d_k = d_v = d, C tokens per chunk, L = 2C sub-steps; each
 token is an erase sub-step and a delta sub-step), per chunk and head:
@@ -112,6 +116,76 @@ def time_events(torch, fn, reps: int) -> float:
     return start.elapsed_time(end) / reps
 
 
+def bench_layer(torch, eda, dev, chunk: int, steps: int) -> dict:
+    """Layer form (fused prologue) against the unfused pipeline on the same
+    inputs, and the layer-form decode step."""
+    import torch.nn.functional as Fn
+    from eda_inputs import WORKLOADS, make_workload
+
+    w = WORKLOADS["train_layer"]
+    x = make_workload(w, device=dev)
+    B, T, Hk, Hv, dk, dv = w.B, w.T, w.hk, w.H, w.dk, w.dv
+    o = torch.empty((B, T, Hv, dv), dtype=x["q"].dtype, device=dev)
+    Sf = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(eda.layer_workspace_size(B, T, Hk, Hv, dk, dv, x["q"].dtype, chunk),
+                     dtype=torch.uint8, device=dev)
+    names = ("q", "k", "e", "v", "a", "A_log", "dt_bias", "beta", "gamma")
+
+    def fused():
+        eda.fwd_chunked_layer(*(x[n] for n in names), x["S0"], chunk=chunk, out=o, S_final=Sf,
+                              workspace=ws)
+
+    ws2 = torch.empty(eda.workspace_size(B, T, Hv, dk, dv, x["q"].dtype, chunk), dtype=torch.uint8,
+                      device=dev)
+
+    def unfused():
+        # the same prologue as separate element-wise passes over HBM
+        grp = Hv // Hk
+        qn, kn, en = (Fn.normalize(x[n].float(), dim=-1, eps=1e-6).to(x[n].dtype)
+                      .repeat_interleave(grp, dim=2) for n in ("q", "k", "e"))
+        delta = Fn.softplus(x["a"].float() + x["dt_bias"])
+        alpha = torch.exp(-5.0 + 5.0 * torch.exp(-(torch.exp(x["A_log"]) / 5.0) * delta))
+        alpha = alpha.repeat_interleave(grp, dim=2)
+        eda.fwd_chunked(qn, kn, en, x["v"], alpha, x["beta"], x["gamma"], x["S0"], chunk=chunk,
+                        out=o, S_final=Sf, workspace=ws2)
+
+    for f in (fused, unfused):
+        f()
+    torch.cuda.synchronize()
+    ms_f = time_events(torch, fused, steps)
+    ms_u = time_events(torch, unfused, steps)
+    tok = B * T
+    res = dict(workload=f"{w.name}: layer-form chunked forward B={B} T={T} H_k={Hk} H_v={Hv} "
+                        f"d_k=d_v={dk} {w.dtype}, chunk={chunk}",
+               value=round(tok / (ms_f * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms_f, 5),
+               unfused_ms_per_step=round(ms_u, 5), fused_speedup=round(ms_u / ms_f, 3))
+    print(f"[bench] layer fused {ms_f:.4f} ms, unfused {ms_u:.4f} ms", file=sys.stderr, flush=True)
+    del x, o, Sf, ws, ws2
+
+    wd = WORKLOADS["decode_layer"]
+    xd = make_workload(wd, device=dev)
+    Sd = xd["S0"].clone()
+    od = torch.empty((wd.B, wd.H, wd.dv), dtype=xd["q"].dtype, device=dev)
+    per = [tuple(xd[n][t] if n not in ("A_log", "dt_bias") else xd[n] for n in names)
+           for t in range(wd.steps)]
+
+    def dec():
+        for t in range(wd.steps):
+            eda.recurrent_step_layer(*per[t], Sd, S_out=Sd, o=od)
+
+    dec()
+    torch.cuda.synchronize()
+    ms_tok = time_events(torch, dec, 3) / wd.steps
+    dbytes = (2 * wd.dk * wd.dv * 4 + wd.dv * 4) * wd.B * wd.H   # state in and out dominate
+    res["decode"] = dict(workload=f"{wd.name}: N={wd.B} H_k={wd.hk} H_v={wd.H} d_k=d_v={wd.dk} "
+                                  f"{wd.dtype}, {wd.steps} steps in place",
+                         value=round(wd.B / (ms_tok * 1e-3), 1), unit="tokens/s",
+                         ms_per_token_step=round(ms_tok, 5),
+                         state_gbs=round(dbytes / (ms_tok * 1e-3) / 1e9, 2))
+    print(f"[bench] layer decode {ms_tok * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +196,7 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -275,6 +350,8 @@ def main() -> int:
         print(f"[bench] decode {ms_tok * 1e3:.2f} us/step, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
         del xd, per
 
+    layer = None if args.no_layer else bench_layer(torch, eda, dev, chunk, args.steps)
+
     # fp64 CPU oracle on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -302,7 +379,7 @@ def main() -> int:
                              f"{w.dtype} inputs, fp32 gates and state, chunk={chunk}",
                     B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, tokens_per_step=tokens,
                     parallelism="single GPU"),
-        roofline=roof_line, cpu_baseline=cpu, chunked_path=path, decode=decode)
+        roofline=roof_line, cpu_baseline=cpu, chunked_path=path, decode=decode, layer=layer)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -41,6 +41,7 @@ class Workload:
     chunk: int = 64
     seed: int = 0
     steps: int = 0  # decode workloads: number of one-token steps (T == 1)
+    hk: int = 0  # layer-form workloads: key heads (H counts value heads); 0 = plain form
 
     @property
     def token_heads(self) -> int:
@@ -62,6 +63,12 @@ WORKLOADS = {
                          alpha_mu=3.0, gamma_mu=-1.0, seed=3),
     "decode": Workload("decode", B=256, T=1, H=32, dk=128, dv=128, dtype="bf16",
                        s0_std=0.02, seed=4, steps=128),
+    # layer form (raw q, k, e, safe-gate input a): the Dense model's 8 key /
+    # 16 value heads at the training length, the MoE model's 16 / 32 for decode
+    "train_layer": Workload("train_layer", B=4, T=2048, H=16, dk=128, dv=128, dtype="bf16",
+                            seed=6, hk=8),
+    "decode_layer": Workload("decode_layer", B=256, T=1, H=32, dk=128, dv=128, dtype="bf16",
+                             s0_std=0.02, seed=7, steps=8, hk=16),
 }
 
 
@@ -106,11 +113,51 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16", *
                 gamma=gamma.contiguous(), S0=S0)
 
 
+def make_layer_inputs(B: int, T: int, H_k: int, H_v: int, dk: int, dv: int, dtype: str = "bf16", *,
+                      seed: int = 0, gamma_mu: float = 0.0, s0_std: float = 0.0,
+                      device: str | torch.device = "cpu") -> dict:
+    """Inputs of the layer form: raw (unnormalised) q, k, e ~ N(0, 1) per
+    element and the decay gate's input a ~ N(0, 1), all [B, T, H_k, d_k] in
+    `dtype`; A_log = log(U(1, 16)) and dt_bias ~ U(-7, -2.3) per key head and
+    channel (so softplus(dt_bias) lies in about [1e-3, 0.1]); v ~ N(0, 1)
+    [B, T, H_v, d_v]; beta = sigmoid(N(0, 1)), gamma = sigmoid(N(gamma_mu, 1))
+    per value head; S0 ~ N(0, s0_std) [B, H_v, d_k, d_v] or None.  The pages
+    fix the gate's form, not its parameter values; these give retentions
+    spread over roughly (0.05, 1)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    td = torch_dtype(dtype)
+    q = torch.randn((B, T, H_k, dk), generator=g, device=device).to(td)
+    k = torch.randn((B, T, H_k, dk), generator=g, device=device).to(td)
+    e = torch.randn((B, T, H_k, dk), generator=g, device=device).to(td)
+    a = torch.randn((B, T, H_k, dk), generator=g, device=device).to(td)
+    v = torch.randn((B, T, H_v, dv), generator=g, device=device).to(td)
+    A_log = torch.log(1.0 + 15.0 * torch.rand((H_k, dk), generator=g, device=device))
+    dt_bias = -7.0 + 4.7 * torch.rand((H_k, dk), generator=g, device=device)
+    beta = torch.sigmoid(torch.randn((B, T, H_v), generator=g, device=device))
+    gamma = torch.sigmoid(gamma_mu + torch.randn((B, T, H_v), generator=g, device=device))
+    S0: Optional[torch.Tensor] = None
+    if s0_std > 0:
+        S0 = s0_std * torch.randn((B, H_v, dk, dv), generator=g, device=device)
+    return dict(q=q, k=k, e=e, v=v, a=a, A_log=A_log.contiguous(), dt_bias=dt_bias.contiguous(),
+                beta=beta.contiguous(), gamma=gamma.contiguous(), S0=S0)
+
+
 def make_workload(w: Workload, device: str | torch.device = "cpu", seed: Optional[int] = None) -> dict:
     """Inputs for a named workload.  Decode workloads return per-step inputs
     stacked on a leading step axis: q, k, e, v, alpha are [steps, N, H, d],
     beta, gamma are [steps, N, H], and S0 is [N, H, d_k, d_v]."""
     s = w.seed if seed is None else seed
+    if w.hk:
+        if w.steps:
+            x = make_layer_inputs(w.steps, w.B, w.hk, w.H, w.dk, w.dv, w.dtype, seed=s,
+                                  gamma_mu=w.gamma_mu, device=device)
+            gen = torch.Generator(device=device)
+            gen.manual_seed(s + 1_000_003)
+            x["S0"] = w.s0_std * torch.randn((w.B, w.H, w.dk, w.dv), generator=gen, device=device)
+            return x
+        return make_layer_inputs(w.B, w.T, w.hk, w.H, w.dk, w.dv, w.dtype, seed=s,
+                                 gamma_mu=w.gamma_mu, s0_std=w.s0_std, device=device)
     if w.steps:
         x = make_inputs(w.steps, w.B, w.H, w.dk, w.dv, w.dtype, seed=s,
                         alpha_mu=w.alpha_mu, gamma_mu=w.gamma_mu, s0_std=0.0,

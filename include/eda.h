@@ -147,6 +147,51 @@ eda_status_t eda_fwd_recurrent_step(const void *q, const void *k, const void *e,
                                     int N, int H, int d_k, int d_v, eda_dtype_t dtype,
                                     void *stream);
 
+/*
+ * Layer form: the same recurrence with the layer's prologue fused in (EDA
+ * paper Fig. 1 and Eqs. (14)-(15); slides frames on the layer structure and
+ * on the safe decay parameterization), for H_v value heads that share H_k
+ * key heads (H_v a multiple of H_k; value head h reads key head
+ * h / (H_v / H_k), as in the paper's models with 8/16 and 16/32 heads):
+ *
+ *   q, k, e <- x / max(||x||_2, 1e-6)       per token and key head (raw inputs)
+ *   alpha    = exp(g),  g = l + (-l) exp(-(A / |l|) softplus(a + b)),
+ *              A = exp(A_log), b = dt_bias, l = -5, per key channel,
+ *
+ * so e^-5 < alpha <= 1.  beta, gamma, v, o and the states are per value head.
+ *
+ *   q, k, e, a : [B, T, H_k, d_k]  dtype (a: the decay gate's input)
+ *   A_log, dt_bias : [H_k, d_k]    fp32
+ *   v : [B, T, H_v, d_v] dtype;  beta, gamma : [B, T, H_v] fp32
+ *   S0, S_final : [B, H_v, d_k, d_v] fp32;  o : [B, T, H_v, d_v] dtype
+ *
+ * Everything else (chunk, workspace, aliasing, errors) is as for
+ * eda_fwd_chunked, with the workspace sized by
+ * eda_fwd_chunked_layer_workspace_size.  H_v not a multiple of H_k (or a
+ * head count < 1) returns EDA_ERR_SHAPE.
+ */
+size_t eda_fwd_chunked_layer_workspace_size(int B, int T, int H_k, int H_v, int d_k, int d_v,
+                                            eda_dtype_t dtype, int chunk);
+
+eda_status_t eda_fwd_chunked_layer(const void *q, const void *k, const void *e, const void *v,
+                                   const void *a, const float *A_log, const float *dt_bias,
+                                   const float *beta, const float *gamma, const float *S0, void *o,
+                                   float *S_final, int B, int T, int H_k, int H_v, int d_k, int d_v,
+                                   eda_dtype_t dtype, int chunk, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/*
+ * One decode token in layer form: as eda_fwd_recurrent_step with the prologue
+ * above.  q, k, e, a : [N, H_k, d_k] dtype;  A_log, dt_bias : [H_k, d_k] fp32;
+ * v : [N, H_v, d_v];  beta, gamma : [N, H_v];  S_in, S_out : [N, H_v, d_k, d_v];
+ * o : [N, H_v, d_v].  Same checks and aliasing rules as eda_fwd_recurrent_step.
+ */
+eda_status_t eda_fwd_recurrent_step_layer(const void *q, const void *k, const void *e, const void *v,
+                                          const void *a, const float *A_log, const float *dt_bias,
+                                          const float *beta, const float *gamma, const float *S_in,
+                                          float *S_out, void *o, int N, int H_k, int H_v, int d_k,
+                                          int d_v, eda_dtype_t dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -121,3 +121,72 @@ def eda_ref_decode(q, k, e, v, alpha, beta, gamma, S0, *, nthreads: Optional[int
     o, S = eda_ref_fwd(sw(q), sw(k), sw(e), sw(v), sw(alpha), sw(beta), sw(gamma),
                        _f64(S0), nthreads=nthreads)
     return np.ascontiguousarray(np.swapaxes(o, 0, 1)), S
+
+
+# ---------------------------------------------------------------------------
+# Layer prologue: safe decay gate, L2 normalisation of q, k, e, grouped value
+# heads.  Plain fp64 numpy, written out from the definitions; the recurrence
+# itself is eda_ref_fwd above.
+# ---------------------------------------------------------------------------
+SAFE_GATE_FLOOR = -5.0   # the lower bound l of the log-retention (EDA paper, Eqs. (14)-(15))
+L2NORM_EPS = 1e-6        # x / max(||x||, eps): the pages do not state an epsilon
+
+
+def softplus(x):
+    """log(1 + e^x) in fp64 (the stable split max(x, 0) + log1p(e^-|x|))."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def eda_ref_safe_gate(a, A_log, dt_bias, ell: float = SAFE_GATE_FLOOR):
+    """Retention alpha from the safe decay gate (EDA paper Eqs. (14)-(15); slides
+    frame "EDA also changes the safe decay parameterization"):
+
+        A = exp(A_log),  Delta_t = softplus(a_t + b_Delta),
+        g_t = l + (-l) exp(-(A / |l|) Delta_t),  alpha_t = exp(g_t),
+
+    element-wise per key channel.  a: [..., H, d_k]; A_log, dt_bias: [H, d_k]
+    (broadcast over the leading axes).  Returns alpha (fp64), in (e^l, 1].
+    """
+    a, A_log, dt_bias = _f64(a), _f64(A_log), _f64(dt_bias)
+    A = np.exp(A_log)
+    delta = softplus(a + dt_bias)
+    g = ell + (-ell) * np.exp(-(A / abs(ell)) * delta)
+    return np.exp(g)
+
+
+def eda_ref_l2norm(x, eps: float = L2NORM_EPS):
+    """x / max(||x||_2, eps) over the last axis (the layer's normalisation of
+    q, k and e; EDA paper Fig. 1)."""
+    x = _f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)
+
+
+def expand_key_heads(x, H_v: int):
+    """Key-head tensor [B, T, H_k, ...] -> value-head tensor [B, T, H_v, ...]:
+    value head h reads key head h // (H_v / H_k) (grouped value heads, EDA paper
+    Appendix, model table)."""
+    x = _f64(x)
+    H_k = x.shape[2]
+    if H_v % H_k:
+        raise ValueError(f"oracle: H_v={H_v} is not a multiple of H_k={H_k}")
+    return np.repeat(x, H_v // H_k, axis=2)
+
+
+def eda_ref_fwd_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S0=None, *,
+                      nthreads: Optional[int] = None, want_state: bool = True):
+    """The kernel-level EDA forward with its layer prologue:
+
+    q, k, e, a: [B, T, H_k, d_k] raw (unnormalised) queries, keys, erase
+    addresses and decay inputs; v: [B, T, H_v, d_v]; A_log, dt_bias: [H_k, d_k];
+    beta, gamma: [B, T, H_v]; S0: [B, H_v, d_k, d_v] or None.  q, k, e are
+    L2-normalised per token and head, alpha comes from the safe gate, key heads
+    are shared by H_v / H_k value heads, then the token recurrence runs per
+    value head.  Returns (o [B, T, H_v, d_v], S_final).
+    """
+    v = _f64(v)
+    H_v = v.shape[2]
+    qn, kn, en = (expand_key_heads(eda_ref_l2norm(x), H_v) for x in (q, k, e))
+    alpha = expand_key_heads(eda_ref_safe_gate(a, A_log, dt_bias), H_v)
+    return eda_ref_fwd(qn, kn, en, v, alpha, beta, gamma, S0, nthreads=nthreads, want_state=want_state)

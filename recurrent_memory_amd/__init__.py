@@ -8,11 +8,16 @@ GPU, the call raises.
 
     o, S = fwd_chunked(q, k, e, v, alpha, beta, gamma, S0=None)
     o, S = recurrent_step(q, k, e, v, alpha, beta, gamma, S_in, inplace=True)
+    o, S = fwd_chunked_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S0=None)
+    o, S = recurrent_step_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S_in)
 
 Layouts follow the C ABI: q, k, e, alpha [B, T, H, d_k]; v, o [B, T, H, d_v];
 beta, gamma [B, T, H]; states [B, H, d_k, d_v] fp32 (decode drops the T
 axis).  q, k, e, v share one dtype (bfloat16 or float32); alpha, beta,
-gamma and the states are float32.
+gamma and the states are float32.  The layer forms take raw q, k, e and the
+decay gate's input a per key head ([..., H_k, d_k]), A_log and dt_bias
+[H_k, d_k] float32, and v, beta, gamma, o, states per value head (H_v, a
+multiple of H_k).
 """
 from __future__ import annotations
 
@@ -22,7 +27,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd_chunked", "recurrent_step", "workspace_size", "library_path", "load_library",
+__all__ = ["fwd_chunked", "recurrent_step", "fwd_chunked_layer", "recurrent_step_layer",
+           "workspace_size", "layer_workspace_size", "library_path", "load_library",
            "EdaError", "STATUS", "DEFAULT_CHUNK"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +75,14 @@ def load_library():
     lib.eda_fwd_recurrent_step.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp, vp,
                                            i, i, i, i, i, vp]
     lib.eda_fwd_recurrent_step.restype = i
+    lib.eda_fwd_chunked_layer_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    lib.eda_fwd_chunked_layer_workspace_size.restype = sz
+    lib.eda_fwd_chunked_layer.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp,
+                                          i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.eda_fwd_chunked_layer.restype = i
+    lib.eda_fwd_recurrent_step_layer.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp,
+                                                 i, i, i, i, i, i, vp]
+    lib.eda_fwd_recurrent_step_layer.restype = i
     _lib = lib
     return lib
 
@@ -166,4 +180,67 @@ def recurrent_step(q, k, e, v, alpha, beta, gamma, S_in=None, *, S_out: Optional
         _ptr(S_out, "S_out", torch.float32), _ptr(o, "o", q.dtype), N, H, dk, dv, dt,
         _stream(q.device))
     _check("eda_fwd_recurrent_step", code)
+    return o, S_out
+
+
+def layer_workspace_size(B: int, T: int, H_k: int, H_v: int, d_k: int, d_v: int,
+                         dtype: torch.dtype, chunk: int = 0) -> int:
+    code = EDA_BF16 if dtype == torch.bfloat16 else EDA_F32
+    return int(load_library().eda_fwd_chunked_layer_workspace_size(B, T, H_k, H_v, d_k, d_v, code, chunk))
+
+
+def fwd_chunked_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S0=None, *, chunk: int = 0,
+                      want_state: bool = True, out: Optional[torch.Tensor] = None,
+                      S_final: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None):
+    """Layer-form chunked forward (eda_fwd_chunked_layer): raw q, k, e, a
+    [B, T, H_k, d_k], v [B, T, H_v, d_v]; returns (o, S_final)."""
+    lib = load_library()
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    need = int(lib.eda_fwd_chunked_layer_workspace_size(B, T, Hk, Hv, dk, dv, dt, chunk))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    code = lib.eda_fwd_chunked_layer(
+        _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(e, "e", q.dtype), _ptr(v, "v", q.dtype),
+        _ptr(a, "a", q.dtype), _ptr(A_log, "A_log", torch.float32),
+        _ptr(dt_bias, "dt_bias", torch.float32), _ptr(beta, "beta", torch.float32),
+        _ptr(gamma, "gamma", torch.float32), _ptr(S0, "S0", torch.float32),
+        _ptr(out, "o", q.dtype), _ptr(S_final, "S_final", torch.float32),
+        B, T, Hk, Hv, dk, dv, dt, chunk, _ptr(workspace, "workspace"),
+        0 if workspace is None else workspace.numel(), _stream(q.device))
+    _check("eda_fwd_chunked_layer", code)
+    return out, S_final
+
+
+def recurrent_step_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S_in=None, *,
+                         S_out: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                         inplace: bool = False):
+    """Layer-form decode token (eda_fwd_recurrent_step_layer): raw q, k, e, a
+    [N, H_k, d_k], v [N, H_v, d_v]; returns (o, S_out)."""
+    lib = load_library()
+    N, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    dt = _dtype_code(q)
+    if inplace:
+        if S_in is None:
+            raise ValueError("inplace=True needs S_in")
+        S_out = S_in
+    if S_out is None:
+        S_out = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    if o is None:
+        o = torch.empty((N, Hv, dv), dtype=q.dtype, device=q.device)
+    code = lib.eda_fwd_recurrent_step_layer(
+        _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(e, "e", q.dtype), _ptr(v, "v", q.dtype),
+        _ptr(a, "a", q.dtype), _ptr(A_log, "A_log", torch.float32),
+        _ptr(dt_bias, "dt_bias", torch.float32), _ptr(beta, "beta", torch.float32),
+        _ptr(gamma, "gamma", torch.float32), _ptr(S_in, "S_in", torch.float32),
+        _ptr(S_out, "S_out", torch.float32), _ptr(o, "o", q.dtype), N, Hk, Hv, dk, dv, dt,
+        _stream(q.device))
+    _check("eda_fwd_recurrent_step_layer", code)
     return o, S_out

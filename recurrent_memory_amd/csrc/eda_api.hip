@@ -7,9 +7,13 @@
 
 namespace eda {
 template <typename Tin>
-hipError_t launch_decode(const void *, const void *, const void *, const void *, const float *,
-                         const float *, const float *, const float *, float *, void *, int, int,
-                         int, int, hipStream_t);
+hipError_t launch_decode(const void *, const void *, const void *, const void *, const void *,
+                         const float *, const float *, const float *, const float *, const float *,
+                         float *, void *, int, int, int, int, int, hipStream_t);
+template <typename Tin>
+hipError_t launch_layer_prep(const void *, const void *, const void *, const void *, const float *,
+                             const float *, float *, float *, float *, float *, int, int, int, int,
+                             int, hipStream_t);
 template <typename T>
 size_t chunked_ws_t(int, int, int, int, int, int);
 template <typename T>
@@ -18,9 +22,10 @@ hipError_t launch_chunked(int, const void *, const void *, const void *, const v
                           float *, int, int, int, int, int, int, void *, hipStream_t,
                           hipEvent_t const *);
 size_t bf16_ws_bytes(int, int, int, int, int, int);
-hipError_t launch_bf16(const void *, const void *, const void *, const void *, const float *,
-                       const float *, const float *, const float *, void *, float *, int, int, int,
-                       int, int, int, void *, hipStream_t, hipEvent_t const *);
+hipError_t launch_bf16(const void *, const void *, const void *, const void *, const void *,
+                       const float *, const float *, const float *, const float *, const float *,
+                       void *, float *, int, int, int, int, int, int, int, void *, hipStream_t,
+                       hipEvent_t const *);
 }  // namespace eda
 
 namespace {
@@ -142,8 +147,9 @@ eda_status_t chunked_call(const void *q, const void *k, const void *e, const voi
 
     hipError_t err =
         dtype == EDA_BF16
-            ? eda::launch_bf16(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v,
-                               chunk, workspace, (hipStream_t)stream, (hipEvent_t const *)events)
+            ? eda::launch_bf16(q, k, e, v, alpha, nullptr, nullptr, beta, gamma, S0, o, S_final, B,
+                               T, H, H, d_k, d_v, chunk, workspace, (hipStream_t)stream,
+                               (hipEvent_t const *)events)
             : eda::launch_chunked<float>(3, q, k, e, v, alpha, beta, gamma, S0, o, S_final, B,
                                          T, H, d_k, d_v, chunk, workspace, (hipStream_t)stream,
                                          (hipEvent_t const *)events);
@@ -207,10 +213,145 @@ eda_status_t eda_fwd_recurrent_step(const void *q, const void *k, const void *e,
 
     hipError_t err =
         dtype == EDA_BF16
-            ? eda::launch_decode<eda::bf16>(q, k, e, v, alpha, beta, gamma, S_in, S_out, o, N, H,
-                                            d_k, d_v, (hipStream_t)stream)
-            : eda::launch_decode<float>(q, k, e, v, alpha, beta, gamma, S_in, S_out, o, N, H, d_k,
-                                        d_v, (hipStream_t)stream);
+            ? eda::launch_decode<eda::bf16>(q, k, e, v, alpha, nullptr, nullptr, beta, gamma, S_in,
+                                            S_out, o, N, H, H, d_k, d_v, (hipStream_t)stream)
+            : eda::launch_decode<float>(q, k, e, v, alpha, nullptr, nullptr, beta, gamma, S_in,
+                                        S_out, o, N, H, H, d_k, d_v, (hipStream_t)stream);
+    return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Layer-form entry points: safe gate, q/k/e normalisation and grouped value
+// heads in front of the same recurrence.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+bool heads_ok(int H_k, int H_v) { return H_k >= 1 && H_v >= 1 && H_v % H_k == 0; }
+
+// fp32: the prologue pass writes q, k, e and alpha per value head after the
+// chunked path's own workspace
+size_t layer_prep_bytes(int B, int T, int H_v, int d_k) { return align256((size_t)B * T * H_v * d_k * 4); }
+
+}  // namespace
+
+extern "C" {
+
+size_t eda_fwd_chunked_layer_workspace_size(int B, int T, int H_k, int H_v, int d_k, int d_v,
+                                            eda_dtype_t dtype, int chunk) {
+    if (!heads_ok(H_k, H_v)) return 0;
+    const size_t base = eda_fwd_chunked_workspace_size(B, T, H_v, d_k, d_v, dtype, chunk);
+    if (base == 0 || dtype == EDA_BF16) return base;
+    return align256(base) + 4 * layer_prep_bytes(B, T, H_v, d_k);
+}
+
+eda_status_t eda_fwd_chunked_layer(const void *q, const void *k, const void *e, const void *v,
+                                   const void *a, const float *A_log, const float *dt_bias,
+                                   const float *beta, const float *gamma, const float *S0, void *o,
+                                   float *S_final, int B, int T, int H_k, int H_v, int d_k, int d_v,
+                                   eda_dtype_t dtype, int chunk, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    if (!q || !k || !e || !v || !a || !A_log || !dt_bias || !beta || !gamma || !o) return EDA_ERR_NULL;
+    if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
+    if (!heads_ok(H_k, H_v) || !dims_ok(B, T, H_v, d_k, d_v)) return EDA_ERR_SHAPE;
+    chunk = resolve_chunk(chunk);
+    if (!head_dims_supported(d_k, d_v) || !chunk_supported(chunk)) return EDA_ERR_UNSUPPORTED;
+    const size_t es = elem_size(dtype);
+    const void *elem_ptrs[] = {q, k, e, v, a};
+    for (const void *p : elem_ptrs)
+        if (!aligned(p, es)) return EDA_ERR_ALIGN;
+    const void *f32_ptrs[] = {A_log, dt_bias, beta, gamma};
+    for (const void *p : f32_ptrs)
+        if (!aligned(p, 4)) return EDA_ERR_ALIGN;
+    const void *vec_ptrs[] = {S0, o, S_final};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned(p, 16)) return EDA_ERR_ALIGN;
+    const size_t need = eda_fwd_chunked_layer_workspace_size(B, T, H_k, H_v, d_k, d_v, dtype, chunk);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return EDA_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return EDA_ERR_ALIGN;
+    }
+
+    const size_t btk = (size_t)B * T * H_k, btv = (size_t)B * T * H_v;
+    const Range in[] = {range_of(q, btk * d_k * es), range_of(k, btk * d_k * es),
+                        range_of(e, btk * d_k * es), range_of(a, btk * d_k * es),
+                        range_of(v, btv * d_v * es), range_of(A_log, (size_t)H_k * d_k * 4),
+                        range_of(dt_bias, (size_t)H_k * d_k * 4), range_of(beta, btv * 4),
+                        range_of(gamma, btv * 4)};
+    const Range rS0 = range_of(S0, (size_t)B * H_v * d_k * d_v * 4);
+    const Range rSf = range_of(S_final, (size_t)B * H_v * d_k * d_v * 4);
+    const Range rO = range_of(o, btv * d_v * es);
+    const Range rW = range_of(need > 0 ? workspace : nullptr, need);
+    for (const Range &r : in)
+        if (overlap(rO, r) || overlap(rSf, r) || overlap(rW, r)) return EDA_ERR_ALIAS;
+    if (overlap(rO, rS0) || overlap(rO, rSf) || overlap(rO, rW)) return EDA_ERR_ALIAS;
+    if (overlap(rW, rS0) || overlap(rW, rSf)) return EDA_ERR_ALIAS;
+    if (overlap(rSf, rS0) && S_final != S0) return EDA_ERR_ALIAS;
+
+    hipError_t err;
+    if (dtype == EDA_BF16) {
+        err = eda::launch_bf16(q, k, e, v, a, A_log, dt_bias, beta, gamma, S0, o, S_final, B, T, H_v,
+                               H_k, d_k, d_v, chunk, workspace, (hipStream_t)stream, nullptr);
+    } else {
+        char *w = (char *)workspace;
+        const size_t base = align256(eda_fwd_chunked_workspace_size(B, T, H_v, d_k, d_v, dtype, chunk));
+        const size_t pb = layer_prep_bytes(B, T, H_v, d_k);
+        float *qn = (float *)(w + base), *kn = (float *)(w + base + pb);
+        float *en = (float *)(w + base + 2 * pb), *al = (float *)(w + base + 3 * pb);
+        err = eda::launch_layer_prep<float>(q, k, e, a, A_log, dt_bias, qn, kn, en, al, B, T, H_v, H_k,
+                                            d_k, (hipStream_t)stream);
+        if (err == hipSuccess)
+            err = eda::launch_chunked<float>(3, qn, kn, en, v, al, beta, gamma, S0, o, S_final, B, T,
+                                             H_v, d_k, d_v, chunk, workspace, (hipStream_t)stream,
+                                             nullptr);
+    }
+    return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
+}
+
+eda_status_t eda_fwd_recurrent_step_layer(const void *q, const void *k, const void *e, const void *v,
+                                          const void *a, const float *A_log, const float *dt_bias,
+                                          const float *beta, const float *gamma, const float *S_in,
+                                          float *S_out, void *o, int N, int H_k, int H_v, int d_k,
+                                          int d_v, eda_dtype_t dtype, void *stream) {
+    if (!q || !k || !e || !v || !a || !A_log || !dt_bias || !beta || !gamma || !S_out || !o)
+        return EDA_ERR_NULL;
+    if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
+    if (!heads_ok(H_k, H_v) || !dims_ok(N, 1, H_v, d_k, d_v)) return EDA_ERR_SHAPE;
+    if (!head_dims_supported(d_k, d_v)) return EDA_ERR_UNSUPPORTED;
+    const size_t es = elem_size(dtype);
+    const void *elem_ptrs[] = {q, k, e, v, a, o};
+    for (const void *p : elem_ptrs)
+        if (!aligned(p, es)) return EDA_ERR_ALIGN;
+    const void *f32_ptrs[] = {A_log, dt_bias, beta, gamma};
+    for (const void *p : f32_ptrs)
+        if (!aligned(p, 4)) return EDA_ERR_ALIGN;
+    const void *vec_ptrs[] = {S_in, S_out};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned(p, 16)) return EDA_ERR_ALIGN;
+
+    const size_t nk = (size_t)N * H_k, nv = (size_t)N * H_v;
+    const Range in[] = {range_of(q, nk * d_k * es), range_of(k, nk * d_k * es),
+                        range_of(e, nk * d_k * es), range_of(a, nk * d_k * es),
+                        range_of(v, nv * d_v * es), range_of(A_log, (size_t)H_k * d_k * 4),
+                        range_of(dt_bias, (size_t)H_k * d_k * 4), range_of(beta, nv * 4),
+                        range_of(gamma, nv * 4)};
+    const Range rSi = range_of(S_in, nv * d_k * d_v * 4);
+    const Range rSo = range_of(S_out, nv * d_k * d_v * 4);
+    const Range rO = range_of(o, nv * d_v * es);
+    for (const Range &r : in)
+        if (overlap(rO, r) || overlap(rSo, r)) return EDA_ERR_ALIAS;
+    if (overlap(rO, rSi) || overlap(rO, rSo)) return EDA_ERR_ALIAS;
+    if (overlap(rSo, rSi) && S_out != S_in) return EDA_ERR_ALIAS;
+
+    hipError_t err =
+        dtype == EDA_BF16
+            ? eda::launch_decode<eda::bf16>(q, k, e, v, a, A_log, dt_bias, beta, gamma, S_in, S_out, o,
+                                            N, H_v, H_k, d_k, d_v, (hipStream_t)stream)
+            : eda::launch_decode<float>(q, k, e, v, a, A_log, dt_bias, beta, gamma, S_in, S_out, o, N,
+                                        H_v, H_k, d_k, d_v, (hipStream_t)stream);
     return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
 }
 

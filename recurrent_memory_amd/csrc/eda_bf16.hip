@@ -125,6 +125,19 @@ __device__ __forceinline__ float scan_group(float x, int seg) {
     return x;
 }
 
+constexpr float L2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+constexpr float GATE_FLOOR = -5.f;   // lower bound l of the safe gate's log-retention
+constexpr float NORM_EPS = 1e-6f;    // x / max(||x||, eps)
+
+// log2 of the safe gate's retention (EDA paper Eqs. (14)-(15)):
+//   Delta = softplus(a + b),  g = l + (-l) exp(-(A / |l|) Delta),  log2 alpha = g log2 e,
+// with Ap = (A / |l|) log2 e precomputed per channel; softplus(x) = max(x, 0) + ln(1 + e^-|x|).
+__device__ __forceinline__ float safe_gate_log2(float a, float Ap, float b) {
+    const float x = a + b;
+    const float sp = fmaxf(x, 0.f) + LN2 * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * L2E));
+    return -GATE_FLOOR * L2E * (__builtin_amdgcn_exp2f(-Ap * sp) - 1.f);
+}
+
 // Value of lane S of each group of four lanes (DPP quad permutation).
 template <int S>
 __device__ __forceinline__ float quad_bcast(float x) {
@@ -192,7 +205,7 @@ struct K1G {
     static_assert(C * D * 4 <= szKl, "Kl region reuse");
     static constexpr int szLL = align16(L * LDL * 2), szAd = NB * 16 * ADS * 4;
     static constexpr int szMT = NB * 16 * MTW * 2, szPs = align16(C * LDL * 2);
-    static constexpr int szMisc = (L + 2 * C + D) * 4;
+    static constexpr int szMisc = (L + 2 * C + D) * 4 + NW * C * 16;   // + per-wave norm partials
     static constexpr int LDTV = C + 8;                 // T' and P T' staging rows (after the inverse)
     static_assert(L * LDTV * 2 <= szLL && C * LDTV * 2 <= szAd, "staging reuse");
     static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oAbf = oQl + szQl;
@@ -205,12 +218,19 @@ struct K1G {
 // VEC: d_k == D and 16-byte aligned q, k, e, alpha (whole rows move as
 // 16-byte pieces and are fetched one item ahead); otherwise every item is
 // read element-wise with zero padding.
-template <int C, int D, bool VEC>
+//
+// LAYER: the layer prologue is fused -- `decay` holds the safe gate's input
+// a (bf16, key heads) instead of alpha (fp32), A_log and dt_bias ([Hk][dk]
+// fp32) give alpha per key channel, q, k, e are L2-normalised per token here,
+// and the Hk key heads are shared by groups of H / Hk value heads (q, k, e, a
+// per key head; beta, gamma, v per value head).  Otherwise Hk == H.
+template <int C, int D, bool VEC, bool LAYER>
 __global__ void __launch_bounds__(K1THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ e,
-                 const float *__restrict__ alpha, const float *__restrict__ beta,
-                 const float *__restrict__ gamma, char *__restrict__ ws, int Tlen, int H, int dk,
-                 int NC, int BH) {
+                 const void *__restrict__ decay, const float *__restrict__ A_log,
+                 const float *__restrict__ dt_bias, const float *__restrict__ beta,
+                 const float *__restrict__ gamma, char *__restrict__ ws, int Tlen, int H, int Hk,
+                 int dk, int NC, int BH) {
     using G = K1G<C, D>;
     using F = Fac<C, D>;
     using T = bf16;
@@ -232,6 +252,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     float *bp = (float *)(smem + G::oMisc);  // b' per sub-step          [L]
     float *sb = bp + L, *sg = sb + C;        // beta, gamma per token    [C]
     float *ers = sg + C;                     // e^r per channel (1 if wide) [D]
+    float *nrm = ers + D;                    // LAYER: per-wave |q|^2, |k|^2, |e|^2 partials [NW][C][4]
     T *Tvs = (T *)(smem + G::oAbf);          // T', after the inverse    [L][LDTV]
     T *Phs = (T *)(smem + G::oAd);           // P T', after the inverse  [C][LDTV]
     constexpr int LDTV = G::LDTV;
@@ -239,7 +260,9 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = 4 * (lane >> 4), l16 = lane & 15;
-    const int HK = H * dk;
+    const int grp = H / Hk;                  // value heads per key head
+    const float *alpha = (const float *)decay;
+    const bf16 *agate = (const bf16 *)decay;
     const int items = BH * NC;
 
     // The blocks of (I + A)^{-1} above the diagonal are never written: zero
@@ -259,7 +282,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     const bool act = tid < G::ACT;
     const int seg = tid % TPC, c0 = act ? 4 * (tid / TPC) : 0;
     uint2 xq[TPT], xe[TPT], xk[TPT];
-    f32x4 xa[TPT];
+    f32x4 xa[TPT];           // alpha (or, LAYER, the gate input a in .x, .y as bf16 pairs)
+    f32x4 xA, xB;            // LAYER: A_log, dt_bias of the thread's channels
     float pbeta = 0.f, pgamma = 0.f;
 
     // ---- full aligned chunk: fetched one item ahead.  Rows are clamped to the
@@ -268,15 +292,25 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     auto prefetch = [&](int it) __attribute__((always_inline)) {
         const int bh = head_of(it), cidx = chunk_of(it);
         const int b = bh / H, h = bh % H;
-        const int t0 = cidx * C, last = Tlen - 1 - t0;
-        const long tok0 = ((long)b * Tlen + t0) * H + h;
+        const int t0 = cidx * C, last = Tlen - 1 - t0, hk = h / grp;
+        const long tok0 = ((long)b * Tlen + t0) * H + h;       // value-head rows
+        const long tokk0 = ((long)b * Tlen + t0) * Hk + hk;    // key-head rows
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
-            const long off = (tok0 + (long)min(TPT * seg + i, last) * H) * dk + c0;
+            const long off = (tokk0 + (long)min(TPT * seg + i, last) * Hk) * dk + c0;
             xq[i] = *(const uint2 *)(q + off);
             xe[i] = *(const uint2 *)(e + off);
             xk[i] = *(const uint2 *)(k + off);
-            xa[i] = *(const f32x4 *)(alpha + off);
+            if constexpr (LAYER) {
+                const uint2 u = *(const uint2 *)(agate + off);
+                xa[i] = f32x4{__uint_as_float(u.x), __uint_as_float(u.y), 0.f, 0.f};
+            } else {
+                xa[i] = *(const f32x4 *)(alpha + off);
+            }
+        }
+        if constexpr (LAYER) {
+            xA = *(const f32x4 *)(A_log + (long)hk * dk + c0);
+            xB = *(const f32x4 *)(dt_bias + (long)hk * dk + c0);
         }
         const long tb = tok0 + (long)min(tid % C, last) * H;
         pbeta = beta[tb];
@@ -287,8 +321,9 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     auto fetch_slow = [&](int it) __attribute__((always_inline)) {
         const int bh = head_of(it), cidx = chunk_of(it);
         const int b = bh / H, h = bh % H;
-        const int t0 = cidx * C, nval = min(C, Tlen - t0);
+        const int t0 = cidx * C, nval = min(C, Tlen - t0), hk = h / grp;
         const long tok0 = ((long)b * Tlen + t0) * H + h;
+        const long tokk0 = ((long)b * Tlen + t0) * Hk + hk;
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             const int tau = TPT * seg + i;
@@ -296,17 +331,33 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool ok = act && tau < nval && c0 + j < dk;
-                const long off = (tok0 + (long)tau * H) * dk + c0 + j;
+                const long off = (tokk0 + (long)tau * Hk) * dk + c0 + j;
                 qv[j] = ok ? to_f32(q[off]) : 0.f;
                 ev[j] = ok ? to_f32(e[off]) : 0.f;
                 kv[j] = ok ? to_f32(k[off]) : 0.f;
-                av[j] = ok ? alpha[off] : 1.f;
+                // (LAYER: a = -inf gives softplus = 0, i.e. alpha = 1, for padding)
+                if constexpr (LAYER) av[j] = ok ? to_f32(agate[off]) : -INFINITY;
+                else av[j] = ok ? alpha[off] : 1.f;
             }
             // (exact: the values are bf16 already)
             xq[i] = make_uint2(pack_bf16(qv[0], qv[1]), pack_bf16(qv[2], qv[3]));
             xe[i] = make_uint2(pack_bf16(ev[0], ev[1]), pack_bf16(ev[2], ev[3]));
             xk[i] = make_uint2(pack_bf16(kv[0], kv[1]), pack_bf16(kv[2], kv[3]));
-            xa[i] = f32x4{av[0], av[1], av[2], av[3]};
+            if constexpr (LAYER)
+                xa[i] = f32x4{__uint_as_float(pack_bf16(av[0], av[1])), __uint_as_float(pack_bf16(av[2], av[3])), 0.f, 0.f};
+            else
+                xa[i] = f32x4{av[0], av[1], av[2], av[3]};
+        }
+        if constexpr (LAYER) {
+            float pa[4], pb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool ok = act && c0 + j < dk;
+                pa[j] = ok ? A_log[(long)hk * dk + c0 + j] : 0.f;
+                pb[j] = ok ? dt_bias[(long)hk * dk + c0 + j] : 0.f;
+            }
+            xA = f32x4{pa[0], pa[1], pa[2], pa[3]};
+            xB = f32x4{pb[0], pb[1], pb[2], pb[3]};
         }
         const bool okt = tid < nval;
         pbeta = okt ? beta[tok0 + (long)tid * H] : 0.f;
@@ -361,11 +412,21 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         bool wide_here = false;
         {
             float run[4] = {0.f, 0.f, 0.f, 0.f};
+            f32x4 Ap;
+            if constexpr (LAYER) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Ap[j] = exp2f_(xA[j] * L2E) * (L2E / -GATE_FLOOR);
+            }
 #pragma unroll
             for (int i = 0; i < TPT; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    run[j] += __builtin_amdgcn_logf(xa[i][j]);
+                    if constexpr (LAYER) {
+                        const uint32_t u = __float_as_uint(xa[i][j >> 1]);
+                        run[j] += safe_gate_log2((j & 1) ? hi_bf16(u) : lo_bf16(u), Ap[j], xB[j]);
+                    } else {
+                        run[j] += __builtin_amdgcn_logf(xa[i][j]);
+                    }
                     g[i][j] = run[j];
                 }
 #pragma unroll
@@ -381,7 +442,44 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 for (int j = 0; j < 4; ++j) wide_here |= glq[j] < -WIDE_G2;
             }
         }
+        // LAYER: squared norms of q, k, e per token, summed over the channel
+        // quads of a wave here and over the waves after the barrier
+        if constexpr (LAYER) {
+            constexpr int NWA = (G::ACT + 63) / 64;   // waves with channels
+            if (wave < NWA) {
+#pragma unroll
+                for (int i = 0; i < TPT; ++i) {
+                    f32x4 ps = zero4();
+                    const uint2 *src[3] = {&xq[i], &xk[i], &xe[i]};
+#pragma unroll
+                    for (int v = 0; v < 3; ++v) {
+                        const uint2 u = *src[v];
+                        const float x0 = lo_bf16(u.x), x1 = hi_bf16(u.x), x2 = lo_bf16(u.y), x3 = hi_bf16(u.y);
+                        float sq = x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+#pragma unroll
+                        for (int m = TPC; m < 64; m <<= 1) sq += __shfl_xor(sq, m, 64);
+                        ps[v] = sq;
+                    }
+                    if (lane < TPC) *(f32x4 *)(nrm + (wave * C + TPT * seg + i) * 4) = ps;
+                }
+            }
+        }
         const bool wide = __syncthreads_or(wide_here) != 0;
+        // LAYER: 1 / max(|x|, eps) of the thread's tokens, for q, k, e
+        float inq[TPT], ink[TPT], ine[TPT];
+        if constexpr (LAYER) {
+            constexpr int NWA = (G::ACT + 63) / 64;
+#pragma unroll
+            for (int i = 0; i < TPT; ++i) {
+                f32x4 tot = zero4();
+#pragma unroll
+                for (int w = 0; w < NWA; ++w) tot += *(const f32x4 *)(nrm + (w * C + TPT * seg + i) * 4);
+                auto inv = [](float ss) { return ss > NORM_EPS * NORM_EPS ? __builtin_amdgcn_rsqf(ss) : 1.f / NORM_EPS; };
+                inq[i] = inv(tot[0]);
+                ink[i] = inv(tot[1]);
+                ine[i] = inv(tot[2]);
+            }
+        }
 
         // ---- scaled operands (LDS), Diag(e^r) Kr^T (workspace) and the
         //      per-channel scales -------------------------------------------------------
@@ -400,9 +498,17 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 #pragma unroll
             for (int i = 0; i < TPT; ++i) {
                 const int tau = TPT * seg + i;
-                const float ev[4] = {lo_bf16(xe[i].x), hi_bf16(xe[i].x), lo_bf16(xe[i].y), hi_bf16(xe[i].y)};
-                const float kv[4] = {lo_bf16(xk[i].x), hi_bf16(xk[i].x), lo_bf16(xk[i].y), hi_bf16(xk[i].y)};
-                const float qv[4] = {lo_bf16(xq[i].x), hi_bf16(xq[i].x), lo_bf16(xq[i].y), hi_bf16(xq[i].y)};
+                float ev[4] = {lo_bf16(xe[i].x), hi_bf16(xe[i].x), lo_bf16(xe[i].y), hi_bf16(xe[i].y)};
+                float kv[4] = {lo_bf16(xk[i].x), hi_bf16(xk[i].x), lo_bf16(xk[i].y), hi_bf16(xk[i].y)};
+                float qv[4] = {lo_bf16(xq[i].x), hi_bf16(xq[i].x), lo_bf16(xq[i].y), hi_bf16(xq[i].y)};
+                if constexpr (LAYER) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        ev[j] *= ine[i];
+                        kv[j] *= ink[i];
+                        qv[j] *= inq[i];
+                    }
+                }
                 const float gmt = sg[tau], btt = sb[tau];
                 float f[4], fi[4];
 #pragma unroll
@@ -448,9 +554,14 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 #pragma unroll
                 for (int i = 0; i < TPT; ++i) {
                     const int tau = TPT * seg + i;
-                    *(uint2 *)(Kr + (2 * tau) * LDA + c0) = xe[i];
-                    *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = xk[i];
-                    *(uint2 *)(Ql + tau * LDA + c0) = xq[i];
+                    auto nz = [&](uint2 u, float s) __attribute__((always_inline)) {
+                        if constexpr (!LAYER) return u;
+                        return make_uint2(pack_bf16(lo_bf16(u.x) * s, hi_bf16(u.x) * s),
+                                          pack_bf16(lo_bf16(u.y) * s, hi_bf16(u.y) * s));
+                    };
+                    *(uint2 *)(Kr + (2 * tau) * LDA + c0) = nz(xe[i], LAYER ? ine[i] : 1.f);
+                    *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = nz(xk[i], LAYER ? ink[i] : 1.f);
+                    *(uint2 *)(Ql + tau * LDA + c0) = nz(xq[i], LAYER ? inq[i] : 1.f);
                     *(f32x4 *)(Gs + tau * D + c0) = f32x4{g[i][0], g[i][1], g[i][2], g[i][3]};
                 }
             }
@@ -964,19 +1075,22 @@ size_t ws_bytes(int B, int Tlen, int H) {
 }
 
 template <int C, int D, int BV>
-hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, const float *alpha,
-                    const float *beta, const float *gamma, const float *S0, void *o, float *S_final,
-                    int B, int Tlen, int H, int dk, int dv, void *ws, hipStream_t stream,
-                    hipEvent_t const *ev) {
+hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, const void *decay,
+                    const float *A_log, const float *dt_bias, const float *beta, const float *gamma,
+                    const float *S0, void *o, float *S_final, int B, int Tlen, int H, int Hk, int dk,
+                    int dv, void *ws, hipStream_t stream, hipEvent_t const *ev) {
     using G1 = K1G<C, D>;
     using G2 = K2G<C, D, BV>;
     const int NC = (Tlen + C - 1) / C, BH = B * H;
     // 16-byte loads of whole rows need d_k == D and 16-byte aligned bases
     // (D is a multiple of 8, so every row start stays aligned)
+    const bool layer = A_log != nullptr;
     const bool vec = (dk == D) && ((uintptr_t)q % 16 == 0) && ((uintptr_t)k % 16 == 0) &&
-                     ((uintptr_t)e % 16 == 0) && ((uintptr_t)alpha % 16 == 0);
+                     ((uintptr_t)e % 16 == 0) && ((uintptr_t)decay % 16 == 0) &&
+                     (!layer || ((uintptr_t)A_log % 16 == 0 && (uintptr_t)dt_bias % 16 == 0));
     const bool vv = (dv % BV == 0) && ((uintptr_t)v % 16 == 0) && ((uintptr_t)o % 16 == 0);
-    auto k1 = vec ? eda_bf16_factors<C, D, true> : eda_bf16_factors<C, D, false>;
+    auto k1 = layer ? (vec ? eda_bf16_factors<C, D, true, true> : eda_bf16_factors<C, D, false, true>)
+                    : (vec ? eda_bf16_factors<C, D, true, false> : eda_bf16_factors<C, D, false, false>);
     auto k2 = vv ? eda_bf16_state<C, D, BV, true> : eda_bf16_state<C, D, BV, false>;
     hipError_t err = hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, G1::LDS);
     if (err != hipSuccess) return err;
@@ -989,8 +1103,8 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     const int grid1 = (int)(items < 2L * ncu ? items : 2L * ncu);   // two per compute unit (LDS)
     if (ev && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
     hipLaunchKernelGGL(k1, dim3((unsigned)grid1), dim3(G1::NT), G1::LDS, stream, (const bf16 *)q,
-                       (const bf16 *)k, (const bf16 *)e, alpha, beta, gamma, (char *)ws, Tlen, H, dk, NC,
-                       BH);
+                       (const bf16 *)k, (const bf16 *)e, decay, A_log, dt_bias, beta, gamma, (char *)ws,
+                       Tlen, H, Hk, dk, NC, BH);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
@@ -1014,15 +1128,17 @@ size_t bf16_ws_bytes(int B, int Tlen, int H, int dk, int dv, int chunk) {
     return 0;
 }
 
-hipError_t launch_bf16(const void *q, const void *k, const void *e, const void *v, const float *alpha,
-                       const float *beta, const float *gamma, const float *S0, void *o, float *S_final,
-                       int B, int Tlen, int H, int dk, int dv, int chunk, void *ws, hipStream_t stream,
-                       hipEvent_t const *ev) {
+// decay: alpha (fp32), or with A_log != NULL the safe gate's input a (bf16)
+// of Hk key heads (the fused layer prologue); otherwise Hk == H.
+hipError_t launch_bf16(const void *q, const void *k, const void *e, const void *v, const void *decay,
+                       const float *A_log, const float *dt_bias, const float *beta, const float *gamma,
+                       const float *S0, void *o, float *S_final, int B, int Tlen, int H, int Hk, int dk,
+                       int dv, int chunk, void *ws, hipStream_t stream, hipEvent_t const *ev) {
     const int D = b16::pad_dim(dk, dv), BV = b16::slice_width(B * H, D);
-#define EDA_GO(CC, DD, BB)                                                                        \
-    if (chunk == CC && D == DD && BV == BB)                                                       \
-        return b16::launch_t<CC, DD, BB>(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, Tlen, \
-                                         H, dk, dv, ws, stream, ev);
+#define EDA_GO(CC, DD, BB)                                                                          \
+    if (chunk == CC && D == DD && BV == BB)                                                         \
+        return b16::launch_t<CC, DD, BB>(q, k, e, v, decay, A_log, dt_bias, beta, gamma, S0, o,     \
+                                         S_final, B, Tlen, H, Hk, dk, dv, ws, stream, ev);
     EDA_GO(16, 32, 16) EDA_GO(16, 32, 32) EDA_GO(16, 64, 16) EDA_GO(16, 64, 32)
     EDA_GO(16, 128, 16) EDA_GO(16, 128, 32)
     EDA_GO(32, 32, 16) EDA_GO(32, 32, 32) EDA_GO(32, 64, 16) EDA_GO(32, 64, 32)

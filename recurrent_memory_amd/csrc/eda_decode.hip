@@ -24,21 +24,44 @@
 // once per step, so its loads and stores carry the non-temporal hint (no
 // reuse is expected from the caches; measured ~15% faster than plain
 // accesses at 8192 states of 64 KB).
+//
+// LAYER variant (the layer prologue fused in): q, k, e and the safe gate's
+// input a come per key head (Hk heads shared by groups of H / Hk value
+// heads), alpha = exp(l + (-l) exp(-(A / |l|) softplus(a + b))) with l = -5
+// (EDA paper Eqs. (14)-(15)), and q, k, e are L2-normalised here; the
+// normalisation scales are applied to the reductions and the update terms.
 #include "eda_common.h"
 
 namespace eda {
+
+constexpr float DEC_L2E = 1.4426950408889634f, DEC_LN2 = 0.6931471805599453f;
+constexpr float DEC_FLOOR = -5.f, DEC_EPS = 1e-6f;
+
+// natural-log-free safe gate: alpha from a, A_log, dt_bias (fp32)
+__device__ __forceinline__ float dec_safe_gate(float a, float A_log, float b) {
+    const float x = a + b;
+    const float sp = fmaxf(x, 0.f) + DEC_LN2 * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * DEC_L2E));
+    const float A = __builtin_amdgcn_exp2f(A_log * DEC_L2E);
+    const float gl = DEC_FLOOR - DEC_FLOOR * __builtin_amdgcn_exp2f(-(A / -DEC_FLOOR) * sp * DEC_L2E);
+    return __builtin_amdgcn_exp2f(gl * DEC_L2E);
+}
+__device__ __forceinline__ float dec_inv_norm(float ss) {
+    return ss > DEC_EPS * DEC_EPS ? __builtin_amdgcn_rsqf(ss) : 1.f / DEC_EPS;
+}
 
 constexpr int DEC_NT = 512;           // threads per workgroup
 constexpr int DEC_RG = DEC_NT / 32;   // row groups (32 column quads per row)
 constexpr int DEC_R = 128 / DEC_RG;   // rows per thread
 constexpr int DEC_NW = DEC_NT / 64;   // wavefronts
 
-template <typename Tin, bool FULL>
+template <typename Tin, bool FULL, bool LAYER>
 __global__ void __launch_bounds__(DEC_NT)
 eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ e,
-                  const Tin *__restrict__ v, const float *__restrict__ alpha,
+                  const Tin *__restrict__ v, const void *__restrict__ decay,
+                  const float *__restrict__ A_log, const float *__restrict__ dt_bias,
                   const float *__restrict__ beta, const float *__restrict__ gamma,
-                  const float *S_in, float *S_out, Tin *__restrict__ o, long NH, int dk, int dv) {
+                  const float *S_in, float *S_out, Tin *__restrict__ o, long NH, int H, int Hk,
+                  int dk, int dv) {
     constexpr int R = DEC_R, RG = DEC_RG;
     __shared__ float sq[128], sk[128], se[128], sa[128];
     __shared__ float red[DEC_NW][3][128];
@@ -47,13 +70,21 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
     const int cq = tid & 31, rg = tid >> 5;  // column quad, row group
     if (FULL) { dk = 128; dv = 128; }
 
+    const int grp = H / Hk;
     for (long nh = blockIdx.x; nh < NH; nh += gridDim.x) {
+        // key row of this (sequence, value head)
+        const long hk = (nh % H) / grp, nk = (nh / H) * Hk + hk;
         if (tid < 128) {
             const bool ok = tid < dk;
-            sq[tid] = ok ? to_f32(q[nh * dk + tid]) : 0.f;
-            sk[tid] = ok ? to_f32(k[nh * dk + tid]) : 0.f;
-            se[tid] = ok ? to_f32(e[nh * dk + tid]) : 0.f;
-            sa[tid] = ok ? alpha[nh * dk + tid] : 0.f;
+            sq[tid] = ok ? to_f32(q[nk * dk + tid]) : 0.f;
+            sk[tid] = ok ? to_f32(k[nk * dk + tid]) : 0.f;
+            se[tid] = ok ? to_f32(e[nk * dk + tid]) : 0.f;
+            if constexpr (LAYER)
+                sa[tid] = ok ? dec_safe_gate(to_f32(((const Tin *)decay)[nk * dk + tid]), A_log[hk * dk + tid],
+                                             dt_bias[hk * dk + tid])
+                             : 0.f;
+            else
+                sa[tid] = ok ? ((const float *)decay)[nk * dk + tid] : 0.f;
         }
 
         // Read the whole state strip first (independent of the vectors above).
@@ -88,7 +119,17 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
         const float x0 = sk[lane] * se[lane] + sk[lane + 64] * se[lane + 64];
         const float x1 = sq[lane] * se[lane] + sq[lane + 64] * se[lane + 64];
         const float x2 = sq[lane] * sk[lane] + sq[lane + 64] * sk[lane + 64];
-        const float ke = wave_sum(x0), qe = wave_sum(x1), qk = wave_sum(x2);
+        float ke = wave_sum(x0), qe = wave_sum(x1), qk = wave_sum(x2);
+        // LAYER: inverse norms of q, k, e (uniform), applied to every term below
+        float inq = 1.f, ink = 1.f, ine = 1.f;
+        if constexpr (LAYER) {
+            inq = dec_inv_norm(wave_sum(sq[lane] * sq[lane] + sq[lane + 64] * sq[lane + 64]));
+            ink = dec_inv_norm(wave_sum(sk[lane] * sk[lane] + sk[lane + 64] * sk[lane + 64]));
+            ine = dec_inv_norm(wave_sum(se[lane] * se[lane] + se[lane + 64] * se[lane + 64]));
+            ke *= ink * ine;
+            qe *= inq * ine;
+            qk *= inq * ink;
+        }
 
         // Decay folded into the reductions: Sh[i][j] = a_i S[i][j].
         float pe[4] = {0, 0, 0, 0}, pk[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
@@ -132,6 +173,9 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
                 r1 += red[w][1][j];
                 r2 += red[w][2][j];
             }
+            r0 *= ine;
+            r1 *= ink;
+            r2 *= inq;
             re[c] = r0;
             const float vj = (j < dv) ? to_f32(v[nh * dv + j]) : 0.f;
             const float rk = r1 - g * ke * r0;
@@ -150,7 +194,7 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
 #pragma unroll
         for (int m = 0; m < R; ++m) {
             const int i = rg + RG * m;
-            const float a = sa[i], ge = g * se[i], kk = sk[i];
+            const float a = sa[i], ge = g * se[i] * ine, kk = sk[i] * ink;
             float w[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) w[c] = a * s[m][c] - ge * re[c] + kk * u[c];
@@ -169,11 +213,13 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
     }
 }
 
+// decay: alpha (fp32, [N, H, d_k]), or with A_log != NULL the safe gate's
+// input a (Tin, [N, Hk, d_k]) of the fused layer prologue; Hk == H otherwise.
 template <typename Tin>
 hipError_t launch_decode(const void *q, const void *k, const void *e, const void *v,
-                         const float *alpha, const float *beta, const float *gamma,
-                         const float *S_in, float *S_out, void *o, int N, int H, int dk, int dv,
-                         hipStream_t stream) {
+                         const void *decay, const float *A_log, const float *dt_bias,
+                         const float *beta, const float *gamma, const float *S_in, float *S_out,
+                         void *o, int N, int H, int Hk, int dk, int dv, hipStream_t stream) {
     int dev = 0, ncu = 256;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
@@ -181,22 +227,22 @@ hipError_t launch_decode(const void *q, const void *k, const void *e, const void
     if (err != hipSuccess) return err;
     const long NH = (long)N * H;
     const dim3 grid((unsigned)(NH < 4L * ncu ? NH : 4L * ncu)), block(DEC_NT);   // four per compute unit
-    if (dk == 128 && dv == 128)
-        hipLaunchKernelGGL((eda_decode_kernel<Tin, true>), grid, block, 0, stream,
-                           (const Tin *)q, (const Tin *)k, (const Tin *)e, (const Tin *)v, alpha,
-                           beta, gamma, S_in, S_out, (Tin *)o, NH, dk, dv);
-    else
-        hipLaunchKernelGGL((eda_decode_kernel<Tin, false>), grid, block, 0, stream,
-                           (const Tin *)q, (const Tin *)k, (const Tin *)e, (const Tin *)v, alpha,
-                           beta, gamma, S_in, S_out, (Tin *)o, NH, dk, dv);
+    const bool full = dk == 128 && dv == 128, layer = A_log != nullptr;
+    auto kern = full ? (layer ? eda_decode_kernel<Tin, true, true> : eda_decode_kernel<Tin, true, false>)
+                     : (layer ? eda_decode_kernel<Tin, false, true> : eda_decode_kernel<Tin, false, false>);
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, (const Tin *)q, (const Tin *)k, (const Tin *)e,
+                       (const Tin *)v, decay, A_log, dt_bias, beta, gamma, S_in, S_out, (Tin *)o, NH, H,
+                       Hk, dk, dv);
     return hipGetLastError();
 }
 
 template hipError_t launch_decode<float>(const void *, const void *, const void *, const void *,
-                                         const float *, const float *, const float *, const float *,
-                                         float *, void *, int, int, int, int, hipStream_t);
+                                         const void *, const float *, const float *, const float *,
+                                         const float *, const float *, float *, void *, int, int, int,
+                                         int, int, hipStream_t);
 template hipError_t launch_decode<bf16>(const void *, const void *, const void *, const void *,
-                                        const float *, const float *, const float *, const float *,
-                                        float *, void *, int, int, int, int, hipStream_t);
+                                        const void *, const float *, const float *, const float *,
+                                        const float *, const float *, float *, void *, int, int, int,
+                                        int, int, hipStream_t);
 
 }  // namespace eda

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("eda_fwd_chunked", "eda_fwd_chunked_timed", "eda_fwd_recurrent_step",
-              "eda_fwd_chunked_workspace_size", "eda_status_string"):
+              "eda_fwd_chunked_workspace_size", "eda_status_string", "eda_fwd_chunked_layer",
+              "eda_fwd_chunked_layer_workspace_size", "eda_fwd_recurrent_step_layer"):
         assert n in names
 
 
@@ -163,3 +164,69 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros((1, 4, 1, 8))
     with pytest.raises(ValueError, match="GPU tensor"):
         eda.fwd_chunked(x, x, x, x, x, x[..., 0], x[..., 0])
+
+
+# ---- layer form ------------------------------------------------------------
+def test_layer_workspace_size():
+    lib = eda.load_library()
+    ws, lws = lib.eda_fwd_chunked_workspace_size, lib.eda_fwd_chunked_layer_workspace_size
+    # bf16: the prologue is fused, the workspace is the value heads' factor blocks
+    assert lws(4, 2048, 8, 16, 128, 128, 1, 32) == ws(4, 2048, 16, 128, 128, 1, 32)
+    # fp32: the prologue pass adds q, k, e, alpha per value head after the factors
+    base = ws(1, 64, 4, 16, 16, 0, 16)
+    assert lws(1, 64, 2, 4, 16, 16, 0, 16) >= base + 4 * 64 * 4 * 16 * 4
+    assert lws(1, 64, 3, 4, 16, 16, 0, 16) == 0              # H_v not a multiple of H_k
+    assert lws(1, 64, 0, 4, 16, 16, 0, 16) == 0
+
+
+def layer_args(**kw):
+    a = dict(q=fake(1), k=fake(2), e=fake(3), v=fake(4), a=fake(5), A_log=fake(12), dt_bias=fake(13),
+             beta=fake(6), gamma=fake(7), S0=fake(8), o=fake(9), S_final=fake(10), B=2, T=64, Hk=2,
+             Hv=4, dk=64, dv=64, dt=0, chunk=32, ws=fake(11), wsb=1 << 30, stream=None)
+    a.update(kw)
+    return a
+
+
+def call_layer(a):
+    lib = eda.load_library()
+    return lib.eda_fwd_chunked_layer(a["q"], a["k"], a["e"], a["v"], a["a"], a["A_log"], a["dt_bias"],
+                                     a["beta"], a["gamma"], a["S0"], a["o"], a["S_final"], a["B"], a["T"],
+                                     a["Hk"], a["Hv"], a["dk"], a["dv"], a["dt"], a["chunk"], a["ws"],
+                                     a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("field,val,code", [
+    ("a", None, 1), ("A_log", None, 1), ("dt_bias", None, 1), ("q", None, 1),
+    ("dt", 4, 3),
+    ("Hv", 5, 2), ("Hk", 0, 2), ("Hv", 1, 2),          # H_v must be a positive multiple of H_k
+    ("dk", 200, 5), ("chunk", 48, 5),
+    ("A_log", fake(12, 2), 4), ("a", fake(5, 2), 4),
+    ("ws", None, 6), ("wsb", 4096, 6),
+    ("o", fake(5, 512), 7),           # o inside a
+    ("S_final", fake(12), 7),         # state over A_log
+])
+def test_layer_rejects(field, val, code):
+    assert call_layer(layer_args(**{field: val})) == code
+
+
+def call_step_layer(**kw):
+    a = dict(q=fake(1), k=fake(2), e=fake(3), v=fake(4), a=fake(5), A_log=fake(12), dt_bias=fake(13),
+             beta=fake(6), gamma=fake(7), S_in=fake(8), S_out=fake(9), o=fake(10), N=4, Hk=2, Hv=4,
+             dk=128, dv=128, dt=1, stream=None)
+    a.update(kw)
+    lib = eda.load_library()
+    return lib.eda_fwd_recurrent_step_layer(a["q"], a["k"], a["e"], a["v"], a["a"], a["A_log"],
+                                            a["dt_bias"], a["beta"], a["gamma"], a["S_in"], a["S_out"],
+                                            a["o"], a["N"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["dt"],
+                                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=None), 1), (dict(dt_bias=None), 1), (dict(S_out=None), 1),
+    (dict(dt=9), 3), (dict(Hv=3), 2), (dict(N=0), 2), (dict(dk=0), 2), (dict(dv=129), 5),
+    (dict(dt_bias=fake(13, 2)), 4), (dict(S_out=fake(9, 8)), 4),
+    (dict(o=fake(5, 64)), 7), (dict(S_out=fake(8, 4096)), 7),
+])
+def test_step_layer_rejects(kw, code):
+    assert call_step_layer(**kw) == code
+
