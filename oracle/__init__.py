@@ -190,3 +190,45 @@ def eda_ref_fwd_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S0=None, *,
     qn, kn, en = (expand_key_heads(eda_ref_l2norm(x), H_v) for x in (q, k, e))
     alpha = expand_key_heads(eda_ref_safe_gate(a, A_log, dt_bias), H_v)
     return eda_ref_fwd(qn, kn, en, v, alpha, beta, gamma, S0, nthreads=nthreads, want_state=want_state)
+
+
+# ---------------------------------------------------------------------------
+# Second workload: the rank-1 DPLR update of GDN-2 and QED (QED slides, frames
+# "GDN-2 separates decay, erase, and write" and "QED adds a query term to the
+# erase vector").  Plain fp64 numpy, token by token, vectorised over heads.
+# ---------------------------------------------------------------------------
+def gdn2_erase_vector(k, b):
+    """a_t = b_t o k_t (GDN-2's erase vector: a channel-gated key)."""
+    return _f64(b) * _f64(k)
+
+
+def qed_erase_vector(q, k, b, lam):
+    """QED's erase vector: u = b o q, d = u - k (k . u) (the gated query with
+    its component along the unit key removed, gate first, then projection),
+    a = b o k + lam d.  q, k, b: [..., d_k]; lam: scalar or broadcastable."""
+    q, k, b = _f64(q), _f64(k), _f64(b)
+    u = b * q
+    d = u - k * np.sum(k * u, axis=-1, keepdims=True)
+    lam = np.asarray(lam, dtype=np.float64)
+    return b * k + (lam[..., None] if lam.ndim else lam) * d
+
+
+def eda_ref_dplr_fwd(q, k, a, v, alpha, S0=None, want_state: bool = True):
+    """Token-by-token fp64 forward of the rank-1 DPLR recurrence
+
+        Sbar_t = Diag(alpha_t) S_{t-1},   S_t = Sbar_t + k_t (v_t - Sbar_t^T a_t)^T,   o_t = S_t^T q_t,
+
+    i.e. S_t = (I - k_t a_t^T) Diag(alpha_t) S_{t-1} + k_t v_t^T.  v stands for
+    the gated value w o v of GDN-2/QED.  q, k, a, alpha: [B, T, H, d_k];
+    v: [B, T, H, d_v]; S0: [B, H, d_k, d_v] or None.  Returns (o, S_final)."""
+    q, k, a, v, alpha = map(_f64, (q, k, a, v, alpha))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if S0 is None else _f64(S0).copy()
+    o = np.zeros((B, T, H, dv))
+    for t in range(T):
+        Sb = alpha[:, t, :, :, None] * S                             # decay rows (key channels)
+        r = v[:, t] - np.einsum("bhkv,bhk->bhv", Sb, a[:, t])         # residual to write
+        S = Sb + k[:, t, :, :, None] * r[:, :, None, :]               # write along k
+        o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])              # read the new state
+    return o, (S if want_state else None)
