@@ -16,7 +16,9 @@ HBM roofline, and a layer section: the layer-form forward
 (`eda_fwd_chunked_layer`: safe gate, q/k/e normalisation and 8 key heads shared
 by 16 value heads fused into the factor kernel) beside the same computation
 unfused (the prologue as PyTorch element-wise ops, then `eda_fwd_chunked` on
-the expanded value-head inputs), and the layer-form decode step.
+the expanded value-head inputs), and the layer-form decode step; and a dplr
+section: the rank-1 DPLR update of GDN-2/QED (`eda_fwd_chunked_dplr`) on the
+same training shape with QED erase vectors.
 
 Algorithmic work (d_k = d_v = d, C tokens per chunk, L = 2C sub-steps; each
 token is an erase sub-step and a delta sub-step), per chunk and head:
@@ -186,6 +188,34 @@ def bench_layer(torch, eda, dev, chunk: int, steps: int) -> dict:
     return res
 
 
+def bench_dplr(torch, eda, dev, chunk: int, steps: int) -> dict:
+    """The second workload: rank-1 DPLR update with QED erase vectors."""
+    from eda_inputs import WORKLOADS, make_dplr_inputs
+
+    w = WORKLOADS["train_qed"]
+    x = make_dplr_inputs(w.B, w.T, w.H, w.dk, w.dv, w.dtype, seed=w.seed, device=dev)
+    q, k, b = x["q"].float(), x["k"].float(), x["b"]
+    u = b * q
+    a = (b * k + x["lam"].view(1, 1, -1, 1) * (u - k * (k * u).sum(-1, keepdim=True))).to(x["q"].dtype)
+    v = (x["w"] * x["v"].float()).to(x["q"].dtype)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
+    Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(eda.workspace_size(w.B, w.T, w.H, w.dk, w.dv, x["q"].dtype, chunk), dtype=torch.uint8,
+                     device=dev)
+
+    def run():
+        eda.fwd_chunked_dplr(x["q"], x["k"], a, v, x["alpha"], None, chunk=chunk, out=o, S_final=Sf,
+                             workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    ms = time_events(torch, run, steps)
+    print(f"[bench] dplr {ms:.4f} ms", file=sys.stderr, flush=True)
+    return dict(workload=f"{w.name}: rank-1 DPLR (QED erase vectors) chunked forward B={w.B} T={w.T} "
+                         f"H={w.H} d_k=d_v={w.dk} {w.dtype}, chunk={chunk}",
+                value=round(w.B * w.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +227,7 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--no-dplr", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -351,6 +382,7 @@ def main() -> int:
         del xd, per
 
     layer = None if args.no_layer else bench_layer(torch, eda, dev, chunk, args.steps)
+    dplr = None if args.no_dplr else bench_dplr(torch, eda, dev, chunk, args.steps)
 
     # fp64 CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -379,7 +411,8 @@ def main() -> int:
                              f"{w.dtype} inputs, fp32 gates and state, chunk={chunk}",
                     B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, tokens_per_step=tokens,
                     parallelism="single GPU"),
-        roofline=roof_line, cpu_baseline=cpu, chunked_path=path, decode=decode, layer=layer)
+        roofline=roof_line, cpu_baseline=cpu, chunked_path=path, decode=decode, layer=layer,
+        dplr=dplr)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -69,6 +69,8 @@ WORKLOADS = {
                             seed=6, hk=8),
     "decode_layer": Workload("decode_layer", B=256, T=1, H=32, dk=128, dv=128, dtype="bf16",
                              s0_std=0.02, seed=7, steps=8, hk=16),
+    # the second workload (rank-1 DPLR, QED erase vectors) at the training shape
+    "train_qed": Workload("train_qed", B=4, T=2048, H=16, dk=128, dv=128, dtype="bf16", seed=8),
 }
 
 
@@ -141,6 +143,31 @@ def make_layer_inputs(B: int, T: int, H_k: int, H_v: int, dk: int, dv: int, dtyp
         S0 = s0_std * torch.randn((B, H_v, dk, dv), generator=g, device=device)
     return dict(q=q, k=k, e=e, v=v, a=a, A_log=A_log.contiguous(), dt_bias=dt_bias.contiguous(),
                 beta=beta.contiguous(), gamma=gamma.contiguous(), S0=S0)
+
+
+def make_dplr_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16", *,
+                     seed: int = 0, alpha_mu: float = 2.0, s0_std: float = 0.0,
+                     device: str | torch.device = "cpu") -> dict:
+    """Raw draws for the rank-1 DPLR workloads (GDN-2 / QED): unit q, k
+    (N(0, 1), L2-normalised in fp32, stored in `dtype`); channel gates
+    b = sigmoid(N(0, 1)) [B, T, H, d_k] and w = sigmoid(N(0, 1)) [B, T, H, d_v]
+    (fp32); v ~ N(0, 1) (`dtype`); a per-head query weight lam ~ U(0, 0.5) [H];
+    alpha = sigmoid(N(alpha_mu, 0.5)) per key channel; S0 ~ N(0, s0_std) or
+    None.  The erase vector and the gated value are formed by the caller."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    td = torch_dtype(dtype)
+    q = _unit(g, (B, T, H, dk), device).to(td)
+    k = _unit(g, (B, T, H, dk), device).to(td)
+    b = torch.sigmoid(torch.randn((B, T, H, dk), generator=g, device=device))
+    w = torch.sigmoid(torch.randn((B, T, H, dv), generator=g, device=device))
+    v = torch.randn((B, T, H, dv), generator=g, device=device).to(td)
+    lam = 0.5 * torch.rand((H,), generator=g, device=device)
+    alpha = torch.sigmoid(alpha_mu + 0.5 * torch.randn((B, T, H, dk), generator=g, device=device))
+    S0: Optional[torch.Tensor] = None
+    if s0_std > 0:
+        S0 = s0_std * torch.randn((B, H, dk, dv), generator=g, device=device)
+    return dict(q=q, k=k, b=b, w=w, v=v, lam=lam, alpha=alpha.contiguous(), S0=S0)
 
 
 def make_workload(w: Workload, device: str | torch.device = "cpu", seed: Optional[int] = None) -> dict:

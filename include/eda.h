@@ -192,6 +192,44 @@ eda_status_t eda_fwd_recurrent_step_layer(const void *q, const void *k, const vo
                                           float *S_out, void *o, int N, int H_k, int H_v, int d_k,
                                           int d_v, eda_dtype_t dtype, void *stream);
 
+/*
+ * Second workload: the rank-1 DPLR update of GDN-2 and QED (QED slides,
+ * frames "GDN-2 separates decay, erase, and write" and "QED adds a query
+ * term to the erase vector"), per head and token
+ *
+ *     Sbar_t = Diag(alpha_t) S_{t-1},   S_t = Sbar_t + k_t (v_t - Sbar_t^T a_t)^T,   o_t = S_t^T q_t,
+ *
+ * i.e. S_t = (I - k_t a_t^T) Diag(alpha_t) S_{t-1} + k_t v_t^T: decay, then a
+ * rank-1 edit that reads along the erase vector a_t and writes along k_t.
+ * The caller forms a_t (GDN-2: b_t o k_t; QED: b_t o k_t + lambda d_t with
+ * d_t the gated query projected off k_t) and passes the gated value w_t o v_t
+ * as v.  It runs on the same two chunked kernels as eda_fwd_chunked, with a
+ * non-symmetric decayed Gram.
+ *
+ *   q, k, a : [B, T, H, d_k] dtype   v : [B, T, H, d_v] dtype
+ *   alpha   : [B, T, H, d_k] fp32
+ *   S0, S_final, o, chunk, workspace : as for eda_fwd_chunked (same
+ *             workspace size, eda_fwd_chunked_workspace_size)
+ *
+ * Results are defined for finite inputs and alpha in (0, 1]; a and k are not
+ * required to be unit or related.  Checks, aliasing rules and errors as for
+ * eda_fwd_chunked.
+ */
+eda_status_t eda_fwd_chunked_dplr(const void *q, const void *k, const void *a, const void *v,
+                                  const float *alpha, const float *S0, void *o, float *S_final,
+                                  int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
+                                  int chunk, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode token of the DPLR update above for N independent sequences:
+ * q, k, a : [N, H, d_k] dtype;  v : [N, H, d_v];  alpha : [N, H, d_k] fp32;
+ * S_in, S_out, o as for eda_fwd_recurrent_step (same checks and aliasing rules).
+ */
+eda_status_t eda_fwd_recurrent_step_dplr(const void *q, const void *k, const void *a, const void *v,
+                                         const float *alpha, const float *S_in, float *S_out,
+                                         void *o, int N, int H, int d_k, int d_v, eda_dtype_t dtype,
+                                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,8 @@ GPU, the call raises.
     o, S = recurrent_step(q, k, e, v, alpha, beta, gamma, S_in, inplace=True)
     o, S = fwd_chunked_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S0=None)
     o, S = recurrent_step_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S_in)
+    o, S = fwd_chunked_dplr(q, k, a, v, alpha, S0=None)       # GDN-2 / QED update
+    o, S = recurrent_step_dplr(q, k, a, v, alpha, S_in)
 
 Layouts follow the C ABI: q, k, e, alpha [B, T, H, d_k]; v, o [B, T, H, d_v];
 beta, gamma [B, T, H]; states [B, H, d_k, d_v] fp32 (decode drops the T
@@ -28,6 +30,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["fwd_chunked", "recurrent_step", "fwd_chunked_layer", "recurrent_step_layer",
+           "fwd_chunked_dplr", "recurrent_step_dplr",
            "workspace_size", "layer_workspace_size", "library_path", "load_library",
            "EdaError", "STATUS", "DEFAULT_CHUNK"]
 
@@ -83,6 +86,10 @@ def load_library():
     lib.eda_fwd_recurrent_step_layer.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp,
                                                  i, i, i, i, i, i, vp]
     lib.eda_fwd_recurrent_step_layer.restype = i
+    lib.eda_fwd_chunked_dplr.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.eda_fwd_chunked_dplr.restype = i
+    lib.eda_fwd_recurrent_step_dplr.argtypes = [vp, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, vp]
+    lib.eda_fwd_recurrent_step_dplr.restype = i
     _lib = lib
     return lib
 
@@ -244,3 +251,52 @@ def recurrent_step_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S_in=None, 
         _stream(q.device))
     _check("eda_fwd_recurrent_step_layer", code)
     return o, S_out
+
+
+def fwd_chunked_dplr(q, k, a, v, alpha, S0=None, *, chunk: int = 0, want_state: bool = True,
+                     out: Optional[torch.Tensor] = None, S_final: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Rank-1 DPLR (GDN-2 / QED) chunked forward (eda_fwd_chunked_dplr):
+    q, k, a, alpha [B, T, H, d_k], v [B, T, H, d_v]; returns (o, S_final)."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = int(lib.eda_fwd_chunked_workspace_size(B, T, H, dk, dv, dt, chunk))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    code = lib.eda_fwd_chunked_dplr(
+        _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(a, "a", q.dtype), _ptr(v, "v", q.dtype),
+        _ptr(alpha, "alpha", torch.float32), _ptr(S0, "S0", torch.float32), _ptr(out, "o", q.dtype),
+        _ptr(S_final, "S_final", torch.float32), B, T, H, dk, dv, dt, chunk,
+        _ptr(workspace, "workspace"), 0 if workspace is None else workspace.numel(), _stream(q.device))
+    _check("eda_fwd_chunked_dplr", code)
+    return out, S_final
+
+
+def recurrent_step_dplr(q, k, a, v, alpha, S_in=None, *, S_out: Optional[torch.Tensor] = None,
+                        o: Optional[torch.Tensor] = None, inplace: bool = False):
+    """One DPLR decode token (eda_fwd_recurrent_step_dplr) for [N, H, d] inputs."""
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if inplace:
+        if S_in is None:
+            raise ValueError("inplace=True needs S_in")
+        S_out = S_in
+    if S_out is None:
+        S_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    code = lib.eda_fwd_recurrent_step_dplr(
+        _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(a, "a", q.dtype), _ptr(v, "v", q.dtype),
+        _ptr(alpha, "alpha", torch.float32), _ptr(S_in, "S_in", torch.float32),
+        _ptr(S_out, "S_out", torch.float32), _ptr(o, "o", q.dtype), N, H, dk, dv, dt, _stream(q.device))
+    _check("eda_fwd_recurrent_step_dplr", code)
+    return o, S_out
+

@@ -98,6 +98,10 @@ size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v, eda
 
 namespace {
 
+eda_status_t step_call(const void *q, const void *k, const void *e, const void *v, const float *alpha,
+                       const float *beta, const float *gamma, const float *S_in, float *S_out, void *o,
+                       int N, int H, int d_k, int d_v, eda_dtype_t dtype, void *stream);
+
 // Checks, then the launch.  Both dtypes run two kernels: the chunk factors
 // (all chunks in parallel) go to the workspace, then the state pass walks the
 // chunks of each head in order.
@@ -105,8 +109,10 @@ eda_status_t chunked_call(const void *q, const void *k, const void *e, const voi
                           const float *alpha, const float *beta, const float *gamma,
                           const float *S0, void *o, float *S_final, int B, int T, int H, int d_k,
                           int d_v, eda_dtype_t dtype, int chunk, void *workspace,
-                          size_t workspace_bytes, void *stream, void *const *events) {
-    if (!q || !k || !e || !v || !alpha || !beta || !gamma || !o) return EDA_ERR_NULL;
+                          size_t workspace_bytes, void *stream, void *const *events,
+                          bool dplr = false) {
+    // (dplr: the rank-1 DPLR update; `e` is its erase vector, beta and gamma are NULL)
+    if (!q || !k || !e || !v || !alpha || !o || (!dplr && (!beta || !gamma))) return EDA_ERR_NULL;
     if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
     if (!dims_ok(B, T, H, d_k, d_v)) return EDA_ERR_SHAPE;
     chunk = resolve_chunk(chunk);
@@ -133,7 +139,7 @@ eda_status_t chunked_call(const void *q, const void *k, const void *e, const voi
     const Range in[] = {range_of(q, btH * d_k * es), range_of(k, btH * d_k * es),
                         range_of(e, btH * d_k * es), range_of(v, btH * d_v * es),
                         range_of(alpha, btH * d_k * 4), range_of(beta, btH * 4),
-                        range_of(gamma, btH * 4)};
+                        range_of(gamma, btH * 4)};   // (NULL pointers give empty ranges)
     const Range rS0 = range_of(S0, (size_t)B * H * d_k * d_v * 4);
     const Range rSf = range_of(S_final, (size_t)B * H * d_k * d_v * 4);
     const Range rO = range_of(o, btH * d_v * es);
@@ -183,7 +189,36 @@ eda_status_t eda_fwd_recurrent_step(const void *q, const void *k, const void *e,
                                     const float *alpha, const float *beta, const float *gamma,
                                     const float *S_in, float *S_out, void *o, int N, int H,
                                     int d_k, int d_v, eda_dtype_t dtype, void *stream) {
-    if (!q || !k || !e || !v || !alpha || !beta || !gamma || !S_out || !o) return EDA_ERR_NULL;
+    if (!beta || !gamma) return EDA_ERR_NULL;
+    return step_call(q, k, e, v, alpha, beta, gamma, S_in, S_out, o, N, H, d_k, d_v, dtype, stream);
+}
+
+eda_status_t eda_fwd_recurrent_step_dplr(const void *q, const void *k, const void *a, const void *v,
+                                         const float *alpha, const float *S_in, float *S_out, void *o,
+                                         int N, int H, int d_k, int d_v, eda_dtype_t dtype,
+                                         void *stream) {
+    if (!a) return EDA_ERR_NULL;
+    return step_call(q, k, a, v, alpha, nullptr, nullptr, S_in, S_out, o, N, H, d_k, d_v, dtype, stream);
+}
+
+eda_status_t eda_fwd_chunked_dplr(const void *q, const void *k, const void *a, const void *v,
+                                  const float *alpha, const float *S0, void *o, float *S_final, int B,
+                                  int T, int H, int d_k, int d_v, eda_dtype_t dtype, int chunk,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    if (!a) return EDA_ERR_NULL;
+    return chunked_call(q, k, a, v, alpha, nullptr, nullptr, S0, o, S_final, B, T, H, d_k, d_v, dtype,
+                        chunk, workspace, workspace_bytes, stream, nullptr, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks, then the decode launch; beta == gamma == NULL is the DPLR update.
+eda_status_t step_call(const void *q, const void *k, const void *e, const void *v, const float *alpha,
+                       const float *beta, const float *gamma, const float *S_in, float *S_out, void *o,
+                       int N, int H, int d_k, int d_v, eda_dtype_t dtype, void *stream) {
+    if (!q || !k || !e || !v || !alpha || !S_out || !o) return EDA_ERR_NULL;
     if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
     if (!dims_ok(N, 1, H, d_k, d_v)) return EDA_ERR_SHAPE;
     if (!head_dims_supported(d_k, d_v)) return EDA_ERR_UNSUPPORTED;
@@ -193,7 +228,7 @@ eda_status_t eda_fwd_recurrent_step(const void *q, const void *k, const void *e,
         if (!aligned(p, es0)) return EDA_ERR_ALIGN;
     const void *f32_ptrs[] = {alpha, beta, gamma};
     for (const void *p : f32_ptrs)
-        if (!aligned(p, 4)) return EDA_ERR_ALIGN;
+        if (p && !aligned(p, 4)) return EDA_ERR_ALIGN;
     const void *vec_ptrs[] = {S_in, S_out};
     for (const void *p : vec_ptrs)
         if (p && !aligned(p, 16)) return EDA_ERR_ALIGN;
@@ -224,6 +259,10 @@ eda_status_t eda_fwd_recurrent_step(const void *q, const void *k, const void *e,
 // Layer-form entry points: safe gate, q/k/e normalisation and grouped value
 // heads in front of the same recurrence.
 // ---------------------------------------------------------------------------
+
+}  // namespace
+
+extern "C" {
 }  // extern "C"
 
 namespace {

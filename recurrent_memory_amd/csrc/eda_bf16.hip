@@ -224,7 +224,16 @@ struct K1G {
 // fp32) give alpha per key channel, q, k, e are L2-normalised per token here,
 // and the Hk key heads are shared by groups of H / Hk value heads (q, k, e, a
 // per key head; beta, gamma, v per value head).  Otherwise Hk == H.
-template <int C, int D, bool VEC, bool LAYER>
+//
+// DPLR: the rank-1 DPLR update S_t = (I - k_t a_t^T) Diag(alpha_t) S_{t-1} + k_t v_t^T
+// (GDN-2 and QED; QED slides, frames on GDN-2's decay/erase/write split and
+// on QED's erase vector) in the same sub-step form: the erase sub-step only
+// decays (kap = 0, b' = 0) and the delta sub-step reads along a (the `e`
+// input) and writes along k with b' = 1, so Kl's delta rows come from a and
+// Kr's from k (a non-symmetric Gram); beta and gamma are not read.
+constexpr int MODE_PLAIN = 0, MODE_LAYER = 1, MODE_DPLR = 2;
+
+template <int C, int D, bool VEC, int MODE>
 __global__ void __launch_bounds__(K1THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ e,
                  const void *__restrict__ decay, const float *__restrict__ A_log,
@@ -234,6 +243,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     using G = K1G<C, D>;
     using F = Fac<C, D>;
     using T = bf16;
+    constexpr bool LAYER = MODE == MODE_LAYER, DPLR = MODE == MODE_DPLR;
     constexpr int L = G::L, NB = G::NB, NT = G::NT, NW = G::NW, LDA = G::LDA, LDL = G::LDL;
     constexpr int ADS = G::ADS, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT;
     constexpr int NWT = G::NWT;
@@ -313,8 +323,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             xB = *(const f32x4 *)(dt_bias + (long)hk * dk + c0);
         }
         const long tb = tok0 + (long)min(tid % C, last) * H;
-        pbeta = beta[tb];
-        pgamma = gamma[tb];
+        pbeta = DPLR ? 1.f : beta[tb];
+        pgamma = DPLR ? 0.f : gamma[tb];
     };
     // ---- ragged or unaligned chunk: element-wise, zero keys and queries and
     //      alpha = 1 outside the sequence and beyond d_k -----------------------------
@@ -360,8 +370,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             xB = f32x4{pb[0], pb[1], pb[2], pb[3]};
         }
         const bool okt = tid < nval;
-        pbeta = okt ? beta[tok0 + (long)tid * H] : 0.f;
-        pgamma = okt ? gamma[tok0 + (long)tid * H] : 0.f;
+        pbeta = okt ? (DPLR ? 1.f : beta[tok0 + (long)tid * H]) : 0.f;
+        pgamma = okt && !DPLR ? gamma[tok0 + (long)tid * H] : 0.f;
     };
 
     // ---- diagonal 16x16 blocks of (I + A)^{-1}: fp32 forward substitution over
@@ -516,13 +526,22 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     f[j] = exp2f_(g[i][j] - r[j]);
                     fi[j] = wide ? exp2f_(glq[j] - g[i][j]) : exp2f_(r[j] - g[i][j]);
                     const float fh = fi[j] * er[j];
-                    kh[j][i] = pack_bf16(ev[j] * fh, kv[j] * fh);
+                    kh[j][i] = pack_bf16(DPLR ? 0.f : ev[j] * fh, kv[j] * fh);
                 }
                 store4<T>(Kl + (2 * tau) * LDA + c0, gmt * ev[0] * f[0], gmt * ev[1] * f[1],
                           gmt * ev[2] * f[2], gmt * ev[3] * f[3]);
-                store4<T>(Kl + (2 * tau + 1) * LDA + c0, btt * kv[0] * f[0], btt * kv[1] * f[1],
-                          btt * kv[2] * f[2], btt * kv[3] * f[3]);
-                store4<T>(Kr + (2 * tau) * LDA + c0, ev[0] * fi[0], ev[1] * fi[1], ev[2] * fi[2], ev[3] * fi[3]);
+                // (DPLR: the delta sub-step reads along a, held in ev; its erase sub-step has no key)
+                if constexpr (DPLR)
+                    store4<T>(Kl + (2 * tau + 1) * LDA + c0, btt * ev[0] * f[0], btt * ev[1] * f[1],
+                              btt * ev[2] * f[2], btt * ev[3] * f[3]);
+                else
+                    store4<T>(Kl + (2 * tau + 1) * LDA + c0, btt * kv[0] * f[0], btt * kv[1] * f[1],
+                              btt * kv[2] * f[2], btt * kv[3] * f[3]);
+                if constexpr (DPLR)
+                    store4<T>(Kr + (2 * tau) * LDA + c0, 0.f, 0.f, 0.f, 0.f);
+                else
+                    store4<T>(Kr + (2 * tau) * LDA + c0, ev[0] * fi[0], ev[1] * fi[1], ev[2] * fi[2],
+                              ev[3] * fi[3]);
                 store4<T>(Kr + (2 * tau + 1) * LDA + c0, kv[0] * fi[0], kv[1] * fi[1], kv[2] * fi[2],
                           kv[3] * fi[3]);
                 store4<T>(Ql + tau * LDA + c0, qv[0] * f[0], qv[1] * f[1], qv[2] * f[2], qv[3] * f[3]);
@@ -609,11 +628,12 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             for (int idx = tid; idx < L * L; idx += NT) {
                 const int j = idx / L, ii = idx % L;
                 float s = 0.f;
-                if (ii < j) {
-                    const int tj = j >> 1, ti = ii >> 1;
+                // (DPLR: only delta rows and columns; row j reads along a, held in row j - 1)
+                if (ii < j && (!DPLR || ((j & 1) && (ii & 1)))) {
+                    const int tj = j >> 1, ti = ii >> 1, jr = DPLR ? j - 1 : j;
 #pragma unroll 2
                     for (int cc = 0; cc < D; ++cc)
-                        s += to_f32(Kr[j * LDA + cc]) * to_f32(Kr[ii * LDA + cc]) *
+                        s += to_f32(Kr[jr * LDA + cc]) * to_f32(Kr[ii * LDA + cc]) *
                              exp2f_(Gs[tj * D + cc] - Gs[ti * D + cc]);
                     s *= bp[j];
                 }
@@ -623,7 +643,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             for (int idx = tid; idx < C * L; idx += NT) {
                 const int tau = idx / L, ii = idx % L;
                 float s = 0.f;
-                if (ii <= 2 * tau + 1) {
+                if (ii <= 2 * tau + 1 && (!DPLR || (ii & 1))) {
                     const int ti = ii >> 1;
 #pragma unroll 2
                     for (int cc = 0; cc < D; ++cc)
@@ -1084,13 +1104,14 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     const int NC = (Tlen + C - 1) / C, BH = B * H;
     // 16-byte loads of whole rows need d_k == D and 16-byte aligned bases
     // (D is a multiple of 8, so every row start stays aligned)
-    const bool layer = A_log != nullptr;
+    const bool layer = A_log != nullptr, dplr = beta == nullptr;
     const bool vec = (dk == D) && ((uintptr_t)q % 16 == 0) && ((uintptr_t)k % 16 == 0) &&
                      ((uintptr_t)e % 16 == 0) && ((uintptr_t)decay % 16 == 0) &&
                      (!layer || ((uintptr_t)A_log % 16 == 0 && (uintptr_t)dt_bias % 16 == 0));
     const bool vv = (dv % BV == 0) && ((uintptr_t)v % 16 == 0) && ((uintptr_t)o % 16 == 0);
-    auto k1 = layer ? (vec ? eda_bf16_factors<C, D, true, true> : eda_bf16_factors<C, D, false, true>)
-                    : (vec ? eda_bf16_factors<C, D, true, false> : eda_bf16_factors<C, D, false, false>);
+    auto k1 = layer  ? (vec ? eda_bf16_factors<C, D, true, MODE_LAYER> : eda_bf16_factors<C, D, false, MODE_LAYER>)
+              : dplr ? (vec ? eda_bf16_factors<C, D, true, MODE_DPLR> : eda_bf16_factors<C, D, false, MODE_DPLR>)
+                     : (vec ? eda_bf16_factors<C, D, true, MODE_PLAIN> : eda_bf16_factors<C, D, false, MODE_PLAIN>);
     auto k2 = vv ? eda_bf16_state<C, D, BV, true> : eda_bf16_state<C, D, BV, false>;
     hipError_t err = hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, G1::LDS);
     if (err != hipSuccess) return err;
@@ -1129,7 +1150,8 @@ size_t bf16_ws_bytes(int B, int Tlen, int H, int dk, int dv, int chunk) {
 }
 
 // decay: alpha (fp32), or with A_log != NULL the safe gate's input a (bf16)
-// of Hk key heads (the fused layer prologue); otherwise Hk == H.
+// of Hk key heads (the fused layer prologue); otherwise Hk == H.  beta ==
+// NULL selects the rank-1 DPLR update, with its erase vector a in `e`.
 hipError_t launch_bf16(const void *q, const void *k, const void *e, const void *v, const void *decay,
                        const float *A_log, const float *dt_bias, const float *beta, const float *gamma,
                        const float *S0, void *o, float *S_final, int B, int Tlen, int H, int Hk, int dk,

@@ -92,7 +92,11 @@ size_t chunk_workspace_bytes(int B, int T_, int H) {
 // ---------------------------------------------------------------------------
 // Kernel 1: intra-chunk factors.  grid = B*H*NC, block = 256.
 // ---------------------------------------------------------------------------
-template <typename T, int C, int D>
+// DPLR: the rank-1 DPLR update S_t = (I - k_t a_t^T) Diag(alpha_t) S_{t-1} + k_t v_t^T
+// (GDN-2 and QED) in the same sub-step form: erase sub-steps only decay
+// (kap = 0, b' = 0), delta sub-steps read along a (passed as `e`) and write
+// along k with b' = 1; beta and gamma are not read.
+template <typename T, int C, int D, bool DPLR>
 __global__ void __launch_bounds__(256)
 eda_chunk_intra(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ e,
                 const float *__restrict__ alpha, const float *__restrict__ beta,
@@ -134,8 +138,8 @@ eda_chunk_intra(const T *__restrict__ q, const T *__restrict__ k, const T *__res
     // ---- phase A: gates and cumulative log-decay ------------------------------
     if (tid < C) {
         const bool ok = tid < nvalid;
-        sb[tid] = ok ? beta[row(tid)] : 0.f;
-        sgm[tid] = ok ? gamma[row(tid)] : 0.f;
+        sb[tid] = ok ? (DPLR ? 1.f : beta[row(tid)]) : 0.f;
+        sgm[tid] = ok && !DPLR ? gamma[row(tid)] : 0.f;
     }
     const int c = tid % D, seg = tid / D;
     const bool cok = c < dk;
@@ -182,8 +186,8 @@ eda_chunk_intra(const T *__restrict__ q, const T *__restrict__ k, const T *__res
         if (!wide) {
             const float f = __expf(Gt - r), fi = __expf(r - Gt);
             Kl[(2 * tau) * LDA + c] = from_f32<T>(ev * f);
-            Kl[(2 * tau + 1) * LDA + c] = from_f32<T>(kv * f);
-            Kr[(2 * tau) * LDA + c] = from_f32<T>(ev * fi);
+            Kl[(2 * tau + 1) * LDA + c] = from_f32<T>((DPLR ? ev : kv) * f);   // DPLR: reads along a
+            Kr[(2 * tau) * LDA + c] = from_f32<T>(DPLR ? 0.f : ev * fi);        // DPLR: no erase key
             Kr[(2 * tau + 1) * LDA + c] = from_f32<T>(kv * fi);
             Ql[tau * LDA + c] = from_f32<T>(qv * f);
             fw = f;
@@ -196,10 +200,10 @@ eda_chunk_intra(const T *__restrict__ q, const T *__restrict__ k, const T *__res
         }
         // b'-scaled, transposed copy for W (gates are zero past the tail).
         KlT[c * LDL + 2 * tau] = from_f32<T>(sgm[tau] * ev * fw);
-        KlT[c * LDL + 2 * tau + 1] = from_f32<T>(sb[tau] * kv * fw);
+        KlT[c * LDL + 2 * tau + 1] = from_f32<T>(sb[tau] * (DPLR ? ev : kv) * fw);
         gQ[tau * D + c] = from_f32<T>(qv * __expf(Gt));
         const float fk = __expf(glast - Gt);
-        gK[(long)c * L + 2 * tau] = from_f32<T>(ev * fk);
+        gK[(long)c * L + 2 * tau] = from_f32<T>(DPLR ? 0.f : ev * fk);
         gK[(long)c * L + 2 * tau + 1] = from_f32<T>(kv * fk);
     }
     __syncthreads();
@@ -246,10 +250,11 @@ eda_chunk_intra(const T *__restrict__ q, const T *__restrict__ k, const T *__res
             float s = 0.f;
             if (idx < L * L) {
                 const int j = idx / L, ii = idx % L;
-                if (ii < j) {
-                    const int tj = j >> 1, ti = ii >> 1;
+                // (DPLR: delta rows and columns only; row j reads along a, raw in row j - 1)
+                if (ii < j && (!DPLR || ((j & 1) && (ii & 1)))) {
+                    const int tj = j >> 1, ti = ii >> 1, jr = DPLR ? j - 1 : j;
                     for (int cc = 0; cc < D; ++cc)
-                        s += to_f32(Kl[j * LDA + cc]) * to_f32(Kl[ii * LDA + cc]) *
+                        s += to_f32(Kl[jr * LDA + cc]) * to_f32(Kl[ii * LDA + cc]) *
                              __expf(Gs[tj * D + cc] - Gs[ti * D + cc]);
                     s *= bp[j];
                 }
@@ -259,7 +264,7 @@ eda_chunk_intra(const T *__restrict__ q, const T *__restrict__ k, const T *__res
         for (int idx = tid; idx < C * L; idx += 256) {
             const int tau = idx / L, ii = idx % L;
             float s = 0.f;
-            if (ii <= 2 * tau + 1) {
+            if (ii <= 2 * tau + 1 && (!DPLR || (ii & 1))) {
                 const int ti = ii >> 1;
                 for (int cc = 0; cc < D; ++cc)
                     s += to_f32(Qraw[tau * LDA + cc]) * to_f32(Kl[ii * LDA + cc]) *
@@ -447,8 +452,8 @@ eda_chunk_state(const T *__restrict__ v, const float *__restrict__ beta,
                 for (int rr = 0; rr < 4; ++rr) {
                     const int j = 16 * jb + g4 + rr, tau = j >> 1;
                     acc[rr] = 0.f;
-                    if ((j & 1) && tau < nvalid)
-                        acc[rr] = beta[((long)b * Tlen + t0 + tau) * H + h] *
+                    if ((j & 1) && tau < nvalid)   // (no beta: the DPLR update writes v itself)
+                        acc[rr] = (beta ? beta[((long)b * Tlen + t0 + tau) * H + h] : 1.f) *
                                   to_f32(vt[(16 * nb + l16) * LDS_V + tau]);
                 }
                 acc = tile_nt<T, D>(gW + (long)16 * jb * D, D, st + 16 * nb * LDS_S, LDS_S, acc, lane);
@@ -522,9 +527,10 @@ hipError_t launch_chunked_t(int phase, const void *q, const void *k, const void 
     hipError_t err;
     if (ev && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
     if (phase & 1) {
-        hipLaunchKernelGGL((eda_chunk_intra<T, C, D>), dim3((unsigned)(BH * NC)), dim3(256), 0,
-                           stream, (const T *)q, (const T *)k, (const T *)e, alpha, beta, gamma,
-                           (char *)ws, Tlen, H, dk, NC);
+        // beta == NULL selects the rank-1 DPLR update (erase vector a in `e`)
+        auto k1 = beta ? eda_chunk_intra<T, C, D, false> : eda_chunk_intra<T, C, D, true>;
+        hipLaunchKernelGGL(k1, dim3((unsigned)(BH * NC)), dim3(256), 0, stream, (const T *)q,
+                           (const T *)k, (const T *)e, alpha, beta, gamma, (char *)ws, Tlen, H, dk, NC);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

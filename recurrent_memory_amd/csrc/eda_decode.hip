@@ -30,6 +30,12 @@
 // heads), alpha = exp(l + (-l) exp(-(A / |l|) softplus(a + b))) with l = -5
 // (EDA paper Eqs. (14)-(15)), and q, k, e are L2-normalised here; the
 // normalisation scales are applied to the reductions and the update terms.
+//
+// DPLR variant: the rank-1 DPLR update of GDN-2 and QED (QED slides, frame
+// "GDN-2 separates decay, erase, and write"), Sh = Diag(alpha) S,
+// S_new = Sh + k (v - Sh^T a)^T, o = S_new^T q = Sh^T q + (q.k)(v - Sh^T a),
+// with the erase vector a passed as `e` and no beta or gamma: the same pass
+// with gamma = 0, beta = 1 and Sh^T a in place of the corrected read.
 #include "eda_common.h"
 
 namespace eda {
@@ -54,7 +60,9 @@ constexpr int DEC_RG = DEC_NT / 32;   // row groups (32 column quads per row)
 constexpr int DEC_R = 128 / DEC_RG;   // rows per thread
 constexpr int DEC_NW = DEC_NT / 64;   // wavefronts
 
-template <typename Tin, bool FULL, bool LAYER>
+constexpr int DEC_PLAIN = 0, DEC_LAYER = 1, DEC_DPLR = 2;
+
+template <typename Tin, bool FULL, int MODE>
 __global__ void __launch_bounds__(DEC_NT)
 eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ e,
                   const Tin *__restrict__ v, const void *__restrict__ decay,
@@ -63,6 +71,7 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
                   const float *S_in, float *S_out, Tin *__restrict__ o, long NH, int H, int Hk,
                   int dk, int dv) {
     constexpr int R = DEC_R, RG = DEC_RG;
+    constexpr bool LAYER = MODE == DEC_LAYER, DPLR = MODE == DEC_DPLR;
     __shared__ float sq[128], sk[128], se[128], sa[128];
     __shared__ float red[DEC_NW][3][128];
 
@@ -161,7 +170,7 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
         }
         __syncthreads();
 
-        const float b = beta[nh], g = gamma[nh];
+        const float b = DPLR ? 1.f : beta[nh], g = DPLR ? 0.f : gamma[nh];
         float re[4], u[4], ov[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -178,7 +187,7 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
             r2 *= inq;
             re[c] = r0;
             const float vj = (j < dv) ? to_f32(v[nh * dv + j]) : 0.f;
-            const float rk = r1 - g * ke * r0;
+            const float rk = DPLR ? r0 : r1 - g * ke * r0;   // DPLR: the read along a
             u[c] = b * (vj - rk);
             ov[c] = r2 - g * qe * r0 + qk * u[c];
         }
@@ -215,6 +224,7 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
 
 // decay: alpha (fp32, [N, H, d_k]), or with A_log != NULL the safe gate's
 // input a (Tin, [N, Hk, d_k]) of the fused layer prologue; Hk == H otherwise.
+// beta == NULL (and A_log == NULL) selects the DPLR update, erase vector in `e`.
 template <typename Tin>
 hipError_t launch_decode(const void *q, const void *k, const void *e, const void *v,
                          const void *decay, const float *A_log, const float *dt_bias,
@@ -227,9 +237,14 @@ hipError_t launch_decode(const void *q, const void *k, const void *e, const void
     if (err != hipSuccess) return err;
     const long NH = (long)N * H;
     const dim3 grid((unsigned)(NH < 4L * ncu ? NH : 4L * ncu)), block(DEC_NT);   // four per compute unit
-    const bool full = dk == 128 && dv == 128, layer = A_log != nullptr;
-    auto kern = full ? (layer ? eda_decode_kernel<Tin, true, true> : eda_decode_kernel<Tin, true, false>)
-                     : (layer ? eda_decode_kernel<Tin, false, true> : eda_decode_kernel<Tin, false, false>);
+    const bool full = dk == 128 && dv == 128;
+    const int mode = A_log ? DEC_LAYER : (beta ? DEC_PLAIN : DEC_DPLR);
+    auto kern = full ? (mode == DEC_LAYER  ? eda_decode_kernel<Tin, true, DEC_LAYER>
+                        : mode == DEC_DPLR ? eda_decode_kernel<Tin, true, DEC_DPLR>
+                                           : eda_decode_kernel<Tin, true, DEC_PLAIN>)
+                     : (mode == DEC_LAYER  ? eda_decode_kernel<Tin, false, DEC_LAYER>
+                        : mode == DEC_DPLR ? eda_decode_kernel<Tin, false, DEC_DPLR>
+                                           : eda_decode_kernel<Tin, false, DEC_PLAIN>);
     hipLaunchKernelGGL(kern, grid, block, 0, stream, (const Tin *)q, (const Tin *)k, (const Tin *)e,
                        (const Tin *)v, decay, A_log, dt_bias, beta, gamma, S_in, S_out, (Tin *)o, NH, H,
                        Hk, dk, dv);

@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("eda_fwd_chunked", "eda_fwd_chunked_timed", "eda_fwd_recurrent_step",
               "eda_fwd_chunked_workspace_size", "eda_status_string", "eda_fwd_chunked_layer",
-              "eda_fwd_chunked_layer_workspace_size", "eda_fwd_recurrent_step_layer"):
+              "eda_fwd_chunked_layer_workspace_size", "eda_fwd_recurrent_step_layer",
+              "eda_fwd_chunked_dplr", "eda_fwd_recurrent_step_dplr"):
         assert n in names
 
 
@@ -229,4 +230,42 @@ def call_step_layer(**kw):
 ])
 def test_step_layer_rejects(kw, code):
     assert call_step_layer(**kw) == code
+
+
+# ---- rank-1 DPLR update -----------------------------------------------------
+def call_dplr(**kw):
+    a = chunked_args(**kw)
+    a.setdefault("a", fake(3))
+    lib = eda.load_library()
+    return lib.eda_fwd_chunked_dplr(a["q"], a["k"], a.get("a_vec", fake(3)), a["v"], a["alpha"], a["S0"], a["o"],
+                                    a["S_final"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], a["chunk"],
+                                    a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a_vec=None), 1), (dict(q=None), 1), (dict(alpha=None), 1),
+    (dict(dt=3), 3), (dict(T=0), 2), (dict(dk=256), 5), (dict(chunk=8), 5),
+    (dict(a_vec=fake(3, 2)), 4), (dict(ws=None), 6), (dict(o=fake(3, 256)), 7),
+])
+def test_dplr_rejects(kw, code):
+    assert call_dplr(**kw) == code
+
+
+def test_dplr_reaches_the_workspace_check_without_gates():
+    # beta and gamma are not arguments of the DPLR update: a valid call fails only on the workspace
+    assert call_dplr(wsb=16) == 6
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=None), 1), (dict(S_out=None), 1), (dict(dt=7), 3), (dict(H=0), 2), (dict(dk=129), 5),
+    (dict(a=fake(3, 1)), 4), (dict(o=fake(1, 64)), 7),
+])
+def test_step_dplr_rejects(kw, code):
+    a = dict(q=fake(1), k=fake(2), a=fake(3), v=fake(4), alpha=fake(5), S_in=fake(8), S_out=fake(9),
+             o=fake(10), N=4, H=2, dk=128, dv=128, dt=1, stream=None)
+    a.update(kw)
+    lib = eda.load_library()
+    assert lib.eda_fwd_recurrent_step_dplr(a["q"], a["k"], a["a"], a["v"], a["alpha"], a["S_in"], a["S_out"],
+                                           a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dt"],
+                                           a["stream"]) == code
 
