@@ -232,3 +232,48 @@ def eda_ref_dplr_fwd(q, k, a, v, alpha, S0=None, want_state: bool = True):
         S = Sb + k[:, t, :, :, None] * r[:, :, None, :]               # write along k
         o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])              # read the new state
     return o, (S if want_state else None)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass: fp64 gradients of the token recurrence.  The forward is the
+# three ordered stages of eda_ref_fwd written out once more in fp64 torch
+# (EDA paper Sec. 3.3, Eqs. (9)-(13)), and the adjoint is taken by reverse-mode
+# automatic differentiation of exactly that computation -- a library
+# primitive standing in for the hand-derived reverse recurrence.  Pinned by
+# finite differences of the C oracle and by closed forms.
+# ---------------------------------------------------------------------------
+def eda_ref_bwd(q, k, e, v, alpha, beta, gamma, S0, dO, dS_final=None):
+    """Gradients of L = <o, dO> + <S_final, dS_final> (o = eda_ref_fwd's
+    outputs) with respect to q, k, e, v, alpha, beta, gamma and S0 (S0 = None
+    means zeros, and its gradient is still returned).  Shapes as for
+    eda_ref_fwd; dO: [B, T, H, d_v]; dS_final: [B, H, d_k, d_v] or None.
+    Returns a dict of fp64 numpy arrays keyed dq, dk, de, dv, dalpha, dbeta,
+    dgamma, dS0."""
+    import torch
+
+    names = ("q", "k", "e", "v", "alpha", "beta", "gamma")
+    x = {n: torch.tensor(_f64(a), dtype=torch.float64, requires_grad=True)
+         for n, a in zip(names, (q, k, e, v, alpha, beta, gamma))}
+    B, T, H, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    S0t = torch.zeros((B, H, dk, dv), dtype=torch.float64) if S0 is None else \
+        torch.tensor(_f64(S0), dtype=torch.float64)
+    S0t.requires_grad_(True)
+    S = S0t
+    outs = []
+    for t in range(T):
+        qt, kt, et, vt = (x[n][:, t] for n in ("q", "k", "e", "v"))
+        Sh = x["alpha"][:, t, :, :, None] * S                                   # decay
+        re = torch.einsum("bhkv,bhk->bhv", Sh, et)
+        St = Sh - x["gamma"][:, t, :, None, None] * et[..., None] * re[..., None, :]   # erase
+        rk = torch.einsum("bhkv,bhk->bhv", St, kt)
+        S = St + x["beta"][:, t, :, None, None] * kt[..., None] * (vt - rk)[..., None, :]   # write
+        outs.append(torch.einsum("bhkv,bhk->bhv", S, qt))                       # read
+    o = torch.stack(outs, dim=1)
+    loss = (o * torch.tensor(_f64(dO))).sum()
+    if dS_final is not None:
+        loss = loss + (S * torch.tensor(_f64(dS_final))).sum()
+    loss.backward()
+    g = {"d" + n: x[n].grad.numpy() for n in names}
+    g["dS0"] = S0t.grad.numpy()
+    return g
