@@ -18,7 +18,8 @@ by 16 value heads fused into the factor kernel) beside the same computation
 unfused (the prologue as PyTorch element-wise ops, then `eda_fwd_chunked` on
 the expanded value-head inputs), and the layer-form decode step; and a dplr
 section: the rank-1 DPLR update of GDN-2/QED (`eda_fwd_chunked_dplr`) on the
-same training shape with QED erase vectors.
+same training shape with QED erase vectors; and a backward section: `eda_bwd`
+(gradients of every input) on the training shape.
 
 Algorithmic work (d_k = d_v = d, C tokens per chunk, L = 2C sub-steps; each
 token is an erase sub-step and a delta sub-step), per chunk and head:
@@ -216,6 +217,36 @@ def bench_dplr(torch, eda, dev, chunk: int, steps: int) -> dict:
                 value=round(w.B * w.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5))
 
 
+def bench_bwd(torch, eda, dev, w) -> dict:
+    """Backward pass on the benchmark workload's shape: gradients of every
+    input for a random dO (and no final-state gradient)."""
+    from eda_inputs import make_workload
+
+    x = make_workload(w, device=dev)
+    g = torch.Generator(device=dev).manual_seed(7)
+    dO = torch.randn((w.B, w.T, w.H, w.dv), generator=g, device=dev).to(x["q"].dtype)
+    ws = torch.empty(eda.load_library().eda_bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8,
+                     device=dev)
+
+    def run():
+        eda.backward(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"], dO,
+                     workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    ms = time_events(torch, run, 3)
+    es = 2 if w.dtype == "bf16" else 4
+    # algorithmic bytes per token-head: q, k, e, v, dO in, alpha, beta, gamma in,
+    # dq, dk, de, dalpha, dv, dbeta, dgamma out (fp32)
+    per = (3 * w.dk + 2 * w.dv) * es + w.dk * 4 + 8 + (4 * w.dk + w.dv) * 4 + 8
+    gbs = per * w.B * w.T * w.H / (ms * 1e-3) / 1e9
+    print(f"[bench] backward {ms:.3f} ms", file=sys.stderr, flush=True)
+    return dict(workload=f"{w.name}: backward (all input gradients) B={w.B} T={w.T} H={w.H} d_k={w.dk} "
+                         f"d_v={w.dv} {w.dtype}", value=round(w.B * w.T / (ms * 1e-3), 1), unit="tokens/s",
+                ms_per_step=round(ms, 4), hbm_gbs_algorithmic=round(gbs, 1),
+                hbm_frac_algorithmic=round(gbs / PEAK_HBM_GBS, 5))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +259,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-dplr", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -383,6 +415,7 @@ def main() -> int:
 
     layer = None if args.no_layer else bench_layer(torch, eda, dev, chunk, args.steps)
     dplr = None if args.no_dplr else bench_dplr(torch, eda, dev, chunk, args.steps)
+    bwd = None if args.no_bwd else bench_bwd(torch, eda, dev, w)
 
     # fp64 CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -412,7 +445,7 @@ def main() -> int:
                     B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, tokens_per_step=tokens,
                     parallelism="single GPU"),
         roofline=roof_line, cpu_baseline=cpu, chunked_path=path, decode=decode, layer=layer,
-        dplr=dplr)
+        dplr=dplr, backward=bwd)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -230,6 +230,41 @@ eda_status_t eda_fwd_recurrent_step_dplr(const void *q, const void *k, const voi
                                          void *o, int N, int H, int d_k, int d_v, eda_dtype_t dtype,
                                          void *stream);
 
+/*
+ * Backward pass of the recurrence above (training; the EDA paper trains its
+ * models in BF16 with AdamW, Sec. 4).  Given the forward's inputs, the
+ * gradient dO of the outputs and the gradient dS_final of the final state,
+ * computes the gradients of L = <o, dO> + <S_T, dS_final> with respect to
+ * q, k, e, v, alpha, beta, gamma and S0.  Each stage's adjoint:
+ *
+ *   dq = S_t dO_t,  w = G^T k,  dv = beta w,  dbeta = w.(v - r_k),
+ *   dk = beta (G (v - r_k) - St w),  de = -gamma (dSt r_e + Sh z),  dgamma = -z.r_e,
+ *   dalpha = rowsum(dSh o S_{t-1}),  dS_{t-1} = Diag(alpha) dSh,
+ *
+ * with G = dL/dS_t, Sh, St, r_e, r_k the decayed and erased states and reads
+ * of the forward, dSt = G - beta k w^T, z = dSt^T e, dSh = dSt - gamma e z^T.
+ * The states are recomputed from fp32 checkpoints (every 8 tokens) kept in
+ * the workspace; all arithmetic is fp32.
+ *
+ *   q, k, e : [B, T, H, d_k] dtype;  v, dO : [B, T, H, d_v] dtype
+ *   alpha : [B, T, H, d_k] fp32;  beta, gamma : [B, T, H] fp32
+ *   S0, dS_final : [B, H, d_k, d_v] fp32 or NULL (zeros)
+ *   dq, dk, de, dalpha : [B, T, H, d_k] fp32;  dv : [B, T, H, d_v] fp32
+ *   dbeta, dgamma : [B, T, H] fp32;  dS0 : [B, H, d_k, d_v] fp32 or NULL
+ *   workspace : eda_bwd_workspace_size(...) bytes, 256-byte aligned (about
+ *               2.6 GB for B = 4, T = 2048, H = 16, d = 128)
+ *
+ * Supported: 1 <= d_k, d_v <= 128.  No output may overlap an input, the
+ * workspace or another output.  Errors as for eda_fwd_chunked.
+ */
+size_t eda_bwd_workspace_size(int B, int T, int H, int d_k, int d_v);
+
+eda_status_t eda_bwd(const void *q, const void *k, const void *e, const void *v, const float *alpha,
+                     const float *beta, const float *gamma, const float *S0, const void *dO,
+                     const float *dS_final, float *dq, float *dk, float *de, float *dv, float *dalpha,
+                     float *dbeta, float *dgamma, float *dS0, int B, int T, int H, int d_k, int d_v,
+                     eda_dtype_t dtype, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

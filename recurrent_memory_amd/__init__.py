@@ -12,6 +12,7 @@ GPU, the call raises.
     o, S = recurrent_step_layer(q, k, e, v, a, A_log, dt_bias, beta, gamma, S_in)
     o, S = fwd_chunked_dplr(q, k, a, v, alpha, S0=None)       # GDN-2 / QED update
     o, S = recurrent_step_dplr(q, k, a, v, alpha, S_in)
+    grads = backward(q, k, e, v, alpha, beta, gamma, S0, dO, dS_final)
 
 Layouts follow the C ABI: q, k, e, alpha [B, T, H, d_k]; v, o [B, T, H, d_v];
 beta, gamma [B, T, H]; states [B, H, d_k, d_v] fp32 (decode drops the T
@@ -30,7 +31,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["fwd_chunked", "recurrent_step", "fwd_chunked_layer", "recurrent_step_layer",
-           "fwd_chunked_dplr", "recurrent_step_dplr",
+           "fwd_chunked_dplr", "recurrent_step_dplr", "backward",
            "workspace_size", "layer_workspace_size", "library_path", "load_library",
            "EdaError", "STATUS", "DEFAULT_CHUNK"]
 
@@ -90,6 +91,11 @@ def load_library():
     lib.eda_fwd_chunked_dplr.restype = i
     lib.eda_fwd_recurrent_step_dplr.argtypes = [vp, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, vp]
     lib.eda_fwd_recurrent_step_dplr.restype = i
+    lib.eda_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    lib.eda_bwd_workspace_size.restype = sz
+    lib.eda_bwd.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                            i, i, i, i, i, i, vp, sz, vp]
+    lib.eda_bwd.restype = i
     _lib = lib
     return lib
 
@@ -299,4 +305,33 @@ def recurrent_step_dplr(q, k, a, v, alpha, S_in=None, *, S_out: Optional[torch.T
         _ptr(S_out, "S_out", torch.float32), _ptr(o, "o", q.dtype), N, H, dk, dv, dt, _stream(q.device))
     _check("eda_fwd_recurrent_step_dplr", code)
     return o, S_out
+
+
+def backward(q, k, e, v, alpha, beta, gamma, S0, dO, dS_final=None, *, want_dS0: bool = True,
+             workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of <o, dO> + <S_final, dS_final> (eda_bwd); returns a dict of
+    float32 tensors dq, dk, de, dv, dalpha, dbeta, dgamma and dS0 (None when
+    want_dS0 is False)."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dvd = v.shape[-1]
+    dt = _dtype_code(q)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = dict(dq=torch.empty((B, T, H, dk), **f32), dk=torch.empty((B, T, H, dk), **f32),
+             de=torch.empty((B, T, H, dk), **f32), dv=torch.empty((B, T, H, dvd), **f32),
+             dalpha=torch.empty((B, T, H, dk), **f32), dbeta=torch.empty((B, T, H), **f32),
+             dgamma=torch.empty((B, T, H), **f32),
+             dS0=torch.empty((B, H, dk, dvd), **f32) if want_dS0 else None)
+    need = int(lib.eda_bwd_workspace_size(B, T, H, dk, dvd))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    code = lib.eda_bwd(
+        _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(e, "e", q.dtype), _ptr(v, "v", q.dtype),
+        _ptr(alpha, "alpha", torch.float32), _ptr(beta, "beta", torch.float32),
+        _ptr(gamma, "gamma", torch.float32), _ptr(S0, "S0", torch.float32), _ptr(dO, "dO", q.dtype),
+        _ptr(dS_final, "dS_final", torch.float32),
+        *(_ptr(g[n], n, torch.float32) for n in ("dq", "dk", "de", "dv", "dalpha", "dbeta", "dgamma", "dS0")),
+        B, T, H, dk, dvd, dt, _ptr(workspace, "workspace"), workspace.numel(), _stream(q.device))
+    _check("eda_bwd", code)
+    return g
 

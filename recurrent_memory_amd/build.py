@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libeda.so")
-SOURCES = ["eda_api.hip", "eda_decode.hip", "eda_chunk.hip", "eda_bf16.hip", "eda_layer.hip"]
+SOURCES = ["eda_api.hip", "eda_decode.hip", "eda_chunk.hip", "eda_bf16.hip", "eda_layer.hip", "eda_bwd.hip"]
 ARCH = os.environ.get("EDA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -22,6 +22,12 @@ hipError_t launch_chunked(int, const void *, const void *, const void *, const v
                           float *, int, int, int, int, int, int, void *, hipStream_t,
                           hipEvent_t const *);
 size_t bf16_ws_bytes(int, int, int, int, int, int);
+size_t bwd_ws_bytes(int, int, int, int, int);
+template <typename Tin>
+hipError_t launch_bwd(const void *, const void *, const void *, const void *, const float *, const float *,
+                      const float *, const float *, const void *, const float *, float *, float *, float *,
+                      float *, float *, float *, float *, float *, int, int, int, int, int, void *,
+                      hipStream_t);
 hipError_t launch_bf16(const void *, const void *, const void *, const void *, const void *,
                        const float *, const float *, const float *, const float *, const float *,
                        void *, float *, int, int, int, int, int, int, int, void *, hipStream_t,
@@ -391,6 +397,66 @@ eda_status_t eda_fwd_recurrent_step_layer(const void *q, const void *k, const vo
                                             N, H_v, H_k, d_k, d_v, (hipStream_t)stream)
             : eda::launch_decode<float>(q, k, e, v, a, A_log, dt_bias, beta, gamma, S_in, S_out, o, N,
                                         H_v, H_k, d_k, d_v, (hipStream_t)stream);
+    return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward pass.
+// ---------------------------------------------------------------------------
+extern "C" {
+
+size_t eda_bwd_workspace_size(int B, int T, int H, int d_k, int d_v) {
+    if (!dims_ok(B, T, H, d_k, d_v) || !head_dims_supported(d_k, d_v)) return 0;
+    return eda::bwd_ws_bytes(B, T, H, d_k, d_v);
+}
+
+eda_status_t eda_bwd(const void *q, const void *k, const void *e, const void *v, const float *alpha,
+                     const float *beta, const float *gamma, const float *S0, const void *dO,
+                     const float *dS_final, float *dq, float *dk, float *de, float *dv, float *dalpha,
+                     float *dbeta, float *dgamma, float *dS0, int B, int T, int H, int d_k, int d_v,
+                     eda_dtype_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k || !e || !v || !alpha || !beta || !gamma || !dO || !dq || !dk || !de || !dv || !dalpha ||
+        !dbeta || !dgamma)
+        return EDA_ERR_NULL;
+    if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
+    if (!dims_ok(B, T, H, d_k, d_v)) return EDA_ERR_SHAPE;
+    if (!head_dims_supported(d_k, d_v)) return EDA_ERR_UNSUPPORTED;
+    const size_t es = elem_size(dtype);
+    const void *elem_ptrs[] = {q, k, e, v, dO};
+    for (const void *p : elem_ptrs)
+        if (!aligned(p, es)) return EDA_ERR_ALIGN;
+    const void *f32_ptrs[] = {alpha, beta, gamma, S0, dS_final, dq, dk, de, dv, dalpha, dbeta, dgamma, dS0};
+    for (const void *p : f32_ptrs)
+        if (p && !aligned(p, 4)) return EDA_ERR_ALIGN;
+    const size_t need = eda_bwd_workspace_size(B, T, H, d_k, d_v);
+    if (!workspace || workspace_bytes < need) return EDA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return EDA_ERR_ALIGN;
+
+    const size_t btH = (size_t)B * T * H, st = (size_t)B * H * d_k * d_v * 4;
+    const Range in[] = {range_of(q, btH * d_k * es), range_of(k, btH * d_k * es), range_of(e, btH * d_k * es),
+                        range_of(v, btH * d_v * es), range_of(alpha, btH * d_k * 4), range_of(beta, btH * 4),
+                        range_of(gamma, btH * 4), range_of(S0, st), range_of(dO, btH * d_v * es),
+                        range_of(dS_final, st)};
+    const Range out[] = {range_of(dq, btH * d_k * 4), range_of(dk, btH * d_k * 4), range_of(de, btH * d_k * 4),
+                         range_of(dv, btH * d_v * 4), range_of(dalpha, btH * d_k * 4), range_of(dbeta, btH * 4),
+                         range_of(dgamma, btH * 4), range_of(dS0, st), range_of(workspace, need)};
+    // no output may overlap an input, the workspace or another output
+    for (size_t a = 0; a < sizeof(out) / sizeof(out[0]); ++a) {
+        for (const Range &r : in)
+            if (overlap(out[a], r)) return EDA_ERR_ALIAS;
+        for (size_t c = a + 1; c < sizeof(out) / sizeof(out[0]); ++c)
+            if (overlap(out[a], out[c])) return EDA_ERR_ALIAS;
+    }
+
+    hipError_t err =
+        dtype == EDA_BF16
+            ? eda::launch_bwd<eda::bf16>(q, k, e, v, alpha, beta, gamma, S0, dO, dS_final, dq, dk, de, dv,
+                                         dalpha, dbeta, dgamma, dS0, B, T, H, d_k, d_v, workspace,
+                                         (hipStream_t)stream)
+            : eda::launch_bwd<float>(q, k, e, v, alpha, beta, gamma, S0, dO, dS_final, dq, dk, de, dv, dalpha,
+                                     dbeta, dgamma, dS0, B, T, H, d_k, d_v, workspace, (hipStream_t)stream);
     return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
 }
 

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     for n in ("eda_fwd_chunked", "eda_fwd_chunked_timed", "eda_fwd_recurrent_step",
               "eda_fwd_chunked_workspace_size", "eda_status_string", "eda_fwd_chunked_layer",
               "eda_fwd_chunked_layer_workspace_size", "eda_fwd_recurrent_step_layer",
-              "eda_fwd_chunked_dplr", "eda_fwd_recurrent_step_dplr"):
+              "eda_fwd_chunked_dplr", "eda_fwd_recurrent_step_dplr", "eda_bwd",
+              "eda_bwd_workspace_size"):
         assert n in names
 
 
@@ -268,4 +269,41 @@ def test_step_dplr_rejects(kw, code):
     assert lib.eda_fwd_recurrent_step_dplr(a["q"], a["k"], a["a"], a["v"], a["alpha"], a["S_in"], a["S_out"],
                                            a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dt"],
                                            a["stream"]) == code
+
+
+# ---- backward ----------------------------------------------------------------
+def call_bwd(**kw):
+    a = dict(q=fake(1), k=fake(2), e=fake(3), v=fake(4), alpha=fake(5), beta=fake(6), gamma=fake(7),
+             S0=fake(8), dO=fake(9), dSf=fake(10), dq=fake(20), dk=fake(21), de=fake(22), dv=fake(23),
+             da=fake(24), db=fake(25), dg=fake(26), dS0=fake(27), B=2, T=64, H=2, dk_=64, dv_=64, dt=1,
+             ws=fake(11), wsb=1 << 34, stream=None)
+    a.update(kw)
+    lib = eda.load_library()
+    return lib.eda_bwd(a["q"], a["k"], a["e"], a["v"], a["alpha"], a["beta"], a["gamma"], a["S0"], a["dO"],
+                       a["dSf"], a["dq"], a["dk"], a["de"], a["dv"], a["da"], a["db"], a["dg"], a["dS0"], a["B"],
+                       a["T"], a["H"], a["dk_"], a["dv_"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_bwd_workspace_size():
+    ws = eda.load_library().eda_bwd_workspace_size
+    assert ws(4, 2048, 16, 128, 128) > ws(4, 1024, 16, 128, 128) > 0
+    assert ws(1, 1, 1, 129, 4) == 0 and ws(0, 8, 1, 4, 4) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dO=None), 1), (dict(dq=None), 1), (dict(dg=None), 1), (dict(gamma=None), 1),
+    (dict(dt=5), 3), (dict(T=0), 2), (dict(dk_=130), 5),
+    (dict(dO=fake(9, 1)), 4), (dict(da=fake(24, 2)), 4), (dict(ws=fake(11, 64)), 4),
+    (dict(ws=None), 6), (dict(wsb=1024), 6),
+    (dict(dq=fake(1, 256)), 7),       # gradient over an input
+    (dict(dk=fake(20, 4096)), 7),     # two gradients overlap
+    (dict(dv=fake(11, 512)), 7),      # gradient inside the workspace
+])
+def test_bwd_rejects(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_optional_state_arguments():
+    # S0, dS_final and dS0 may be NULL; such a call fails only on the workspace
+    assert call_bwd(S0=None, dSf=None, dS0=None, wsb=16) == 6
 
