@@ -28,8 +28,8 @@ namespace eda {
 
 constexpr int BW_NT = 128;   // threads: one key row each (d_k <= 128)
 constexpr int BW_NC = 16;    // value columns per workgroup
-constexpr int BW_CB = 8;     // tokens between state checkpoints
-constexpr int BW_SP = BW_NC + 4;        // padded LDS row of a state slice
+constexpr int BW_CB = 4;     // tokens between state checkpoints (LDS: four workgroups per CU)
+constexpr int BW_SP = BW_NC;            // LDS row of a state slice
 constexpr int BW_RW = 2 * BW_NC + 4;    // recorded column sums per token: r_e, r_k, k.e
 
 struct BwdArgs {
@@ -42,13 +42,29 @@ struct BwdArgs {
     int B, T, H, dk, dvd, NS, NCK;
 };
 
+// Sum over the 64 lanes of a wave, returned to every lane: prefix sums
+// inside each row of 16 lanes with DPP row shifts, the rows combined with
+// the row broadcasts, then lane 63 (which now holds the total) read back.
+#define EDA_BW_DPP(v, ctrl, rmask) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, rmask, 0xf, false))
+__device__ __forceinline__ float wave_total(float x) {
+    x += EDA_BW_DPP(x, 0x111, 0xf);   // row_shr:1
+    x += EDA_BW_DPP(x, 0x112, 0xf);   // row_shr:2
+    x += EDA_BW_DPP(x, 0x114, 0xf);   // row_shr:4
+    x += EDA_BW_DPP(x, 0x118, 0xf);   // row_shr:8 (lane 15 of each row: the row's sum)
+    x += EDA_BW_DPP(x, 0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+    x += EDA_BW_DPP(x, 0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+#undef EDA_BW_DPP
+
 // Sum of x over the 128 threads of the workgroup (both waves), returned to
 // every thread.  `xw` is a two-buffer exchange area [2][2][N]; `par` flips
 // between calls so that a fast wave never overwrites values still being read.
 template <int N>
 __device__ __forceinline__ void wg_colsum(float (&x)[N], float *xw, int &par, int lane, int wave) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) x[n] = wave_sum(x[n]);
+    for (int n = 0; n < N; ++n) x[n] = wave_total(x[n]);
     float *mine = xw + (par * 2 + wave) * N, *other = xw + (par * 2 + (wave ^ 1)) * N;
     if (lane == 0) {
 #pragma unroll
@@ -82,14 +98,33 @@ __global__ void __launch_bounds__(BW_NT) eda_bwd_kernel(BwdArgs a) {
     for (int j = 0; j < NC; ++j)
         S[j] = (a.S0 && rok && n0 + j < a.dvd) ? a.S0[((long)bh * a.dk + i) * a.dvd + n0 + j] : 0.f;
 
-    // one token forward from S (the state before token t); the column sums
-    // are returned in r (r_e, r_k, k.e)
-    auto fwd_step = [&](float (&St)[NC], int t, float (&r)[2 * NC + 1]) {
+    // the inputs of one token for this thread's row and the slice's columns,
+    // loaded one token ahead of their use
+    struct Tok {
+        float q, k, e, a, bt, gm, v[NC], dO[NC];
+    };
+    auto load_tok = [&](int t, bool with_out) {
+        Tok x;
         const long row = tokrow(t);
-        const float ki = rok ? ld(a.k, row * a.dk + i) : 0.f;
-        const float ei = rok ? ld(a.e, row * a.dk + i) : 0.f;
-        const float ai = rok ? a.alpha[row * a.dk + i] : 1.f;
-        const float bt = a.beta[row], gm = a.gamma[row];
+        x.q = rok && with_out ? ld(a.q, row * a.dk + i) : 0.f;
+        x.k = rok ? ld(a.k, row * a.dk + i) : 0.f;
+        x.e = rok ? ld(a.e, row * a.dk + i) : 0.f;
+        x.a = rok ? a.alpha[row * a.dk + i] : 1.f;
+        x.bt = a.beta[row];
+        x.gm = a.gamma[row];
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const bool cj = n0 + j < a.dvd;
+            x.v[j] = cj ? ld(a.v, row * a.dvd + n0 + j) : 0.f;
+            x.dO[j] = cj && with_out ? ld(a.dO, row * a.dvd + n0 + j) : 0.f;
+        }
+        return x;
+    };
+
+    // one token forward from S (the state before the token); the column sums
+    // are returned in r (r_e, r_k, k.e)
+    auto fwd_step = [&](float (&St)[NC], const Tok &x, float (&r)[2 * NC + 1]) {
+        const float ki = x.k, ei = x.e, ai = x.a, bt = x.bt, gm = x.gm;
         float Sh[NC];
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
@@ -102,21 +137,25 @@ __global__ void __launch_bounds__(BW_NT) eda_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
             r[NC + j] -= gm * r[2 * NC] * r[j];                        // r_k = Sh^T k - gamma (k.e) r_e
-            const float vj = n0 + j < a.dvd ? ld(a.v, row * a.dvd + n0 + j) : 0.f;
-            St[j] = Sh[j] - gm * ei * r[j] + bt * ki * (vj - r[NC + j]);
+            St[j] = Sh[j] - gm * ei * r[j] + bt * ki * (x.v[j] - r[NC + j]);
         }
     };
 
     // ---- sweep 1: checkpoints of the state before tokens 0, CB, 2 CB, ...
     float *ck = a.ckpt + ((long)s * BH + bh) * a.NCK * (BW_NT * NC);
-    for (int t = 0; t < a.T; ++t) {
-        if (t % CB == 0) {
-            float4 *dst = (float4 *)(ck + ((long)(t / CB) * BW_NT + i) * NC);
+    {
+        Tok cur = load_tok(0, false);
+        for (int t = 0; t < a.T; ++t) {
+            const Tok nxt = load_tok(t + 1 < a.T ? t + 1 : t, false);
+            if (t % CB == 0) {
+                float4 *dst = (float4 *)(ck + ((long)(t / CB) * BW_NT + i) * NC);
 #pragma unroll
-            for (int j = 0; j < NC; j += 4) dst[j / 4] = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+                for (int j = 0; j < NC; j += 4) dst[j / 4] = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+            }
+            float r[2 * NC + 1];
+            fwd_step(S, cur, r);
+            cur = nxt;
         }
-        float r[2 * NC + 1];
-        fwd_step(S, t, r);
     }
 
     // ---- sweep 2: backwards over the segments
@@ -134,25 +173,28 @@ __global__ void __launch_bounds__(BW_NT) eda_bwd_kernel(BwdArgs a) {
                 S[j] = x.x; S[j + 1] = x.y; S[j + 2] = x.z; S[j + 3] = x.w;
             }
         }
-        for (int tau = 0; tau < nt; ++tau) {
+        {
+            Tok cur = load_tok(t0, false);
+            for (int tau = 0; tau < nt; ++tau) {
+                const Tok nxt = load_tok(tau + 1 < nt ? t0 + tau + 1 : t0 + tau, false);
 #pragma unroll
-            for (int j = 0; j < NC; ++j) Sbuf[tau][i][j] = S[j];
-            float r[2 * NC + 1];
-            fwd_step(S, t0 + tau, r);
-            if (i == 0) {
+                for (int j = 0; j < NC; ++j) Sbuf[tau][i][j] = S[j];
+                float r[2 * NC + 1];
+                fwd_step(S, cur, r);
+                if (i == 0) {
 #pragma unroll
-                for (int n = 0; n < 2 * NC + 1; ++n) rec[tau][n] = r[n];
+                    for (int n = 0; n < 2 * NC + 1; ++n) rec[tau][n] = r[n];
+                }
+                cur = nxt;
             }
         }
         __syncthreads();
+        Tok cur = load_tok(t0 + nt - 1, true);
         for (int tau = nt - 1; tau >= 0; --tau) {
             const int t = t0 + tau;
             const long row = tokrow(t);
-            const float qi = rok ? ld(a.q, row * a.dk + i) : 0.f;
-            const float ki = rok ? ld(a.k, row * a.dk + i) : 0.f;
-            const float ei = rok ? ld(a.e, row * a.dk + i) : 0.f;
-            const float ai = rok ? a.alpha[row * a.dk + i] : 1.f;
-            const float bt = a.beta[row], gm = a.gamma[row];
+            const Tok nxt = load_tok(tau > 0 ? t - 1 : t, true);
+            const float qi = cur.q, ki = cur.k, ei = cur.e, ai = cur.a, bt = cur.bt, gm = cur.gm;
             const float ke = rec[tau][2 * NC];
             float Sp[NC], Sh[NC], St[NC], up[NC], dO[NC], re[NC];
             float dq = 0.f;
@@ -160,9 +202,8 @@ __global__ void __launch_bounds__(BW_NT) eda_bwd_kernel(BwdArgs a) {
             for (int j = 0; j < NC; ++j) {
                 Sp[j] = Sbuf[tau][i][j];
                 re[j] = rec[tau][j];
-                const bool cj = n0 + j < a.dvd;
-                const float vj = cj ? ld(a.v, row * a.dvd + n0 + j) : 0.f;
-                dO[j] = cj ? ld(a.dO, row * a.dvd + n0 + j) : 0.f;
+                const float vj = cur.v[j];
+                dO[j] = cur.dO[j];
                 Sh[j] = ai * Sp[j];
                 St[j] = Sh[j] - gm * ei * re[j];
                 up[j] = vj - rec[tau][NC + j];
@@ -204,6 +245,7 @@ __global__ void __launch_bounds__(BW_NT) eda_bwd_kernel(BwdArgs a) {
             a.pk[pr * BW_NT + i] = bt * dkp;
             a.pe[pr * BW_NT + i] = -gm * dep;
             a.pa[pr * BW_NT + i] = dap;
+            cur = nxt;
         }
         __syncthreads();   // Sbuf and rec are refilled by the next segment
     }
