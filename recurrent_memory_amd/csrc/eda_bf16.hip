@@ -29,12 +29,13 @@
 // and uses the unsplit factors kap o e^G, q o e^G and Khat instead.
 //
 // Kernel 1 (eda_bf16_factors): persistent workgroups walk the (head, chunk)
-//   items; each item's raw rows are fetched into registers while the previous
-//   item is processed.  Per item: the cumulative decay, the scaled operands,
-//   A and P on the matrix cores, (I + A)^{-1} (fp32 substitution on the 16x16
-//   diagonal blocks, then one column block of the rest per wave, held in
-//   registers), W on the matrix cores, and the export of -W, T', Kr^T, Ql, P
-//   and the per-channel scales to the workspace.
+//   items; each item's raw values are fetched into registers while the
+//   previous item is processed.  Per item: the cumulative decay, the scaled
+//   operands (and Diag(e^r) Kr^T straight to the workspace), A and P on the
+//   matrix cores, (I + A)^{-1} (fp32 substitution on the 16x16 diagonal
+//   blocks, then one column block of the rest per wave, held in registers),
+//   W, Q^ and P^ on the matrix cores, and the export of -W Diag(e^r), T', Q^,
+//   P^ and the per-channel decay to the workspace.
 // Kernel 2 (eda_bf16_state): one workgroup per (head, slice of value
 //   columns), serial over chunks, fp32 state in registers.  The factors are
 //   stored in the exact per-lane order of the matrix-core operands, so each
@@ -215,9 +216,10 @@ struct K1G {
     static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
 };
 
-// VEC: d_k == D and 16-byte aligned q, k, e, alpha (whole rows move as
-// 16-byte pieces and are fetched one item ahead); otherwise every item is
-// read element-wise with zero padding.
+// VEC: d_k == D and 16-byte aligned q, k, e and decay input (each thread's
+// 4-channel pieces move as single vector loads and are fetched one item
+// ahead); otherwise, and for a ragged last chunk, the item is read
+// element-wise with zero padding.
 //
 // LAYER: the layer prologue is fused -- `decay` holds the safe gate's input
 // a (bf16, key heads) instead of alpha (fp32), A_log and dt_bias ([Hk][dk]
@@ -252,7 +254,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     T *Kl = (T *)(smem + G::oKl);            // Diag(b') Kl              [L][LDA]
     float *Gs = (float *)(smem + G::oKl);    // wide chunk: G (log2) [C][D]
     T *Kr = (T *)(smem + G::oKr);            // Kr                       [L][LDA]
-    T *Wst = Kr;                             // -W, after the Kr^T export [L][LDA]
+    T *Wst = Kr;                             // -W Diag(e^r), once A and P are done [L][LDA]
     T *Ql = (T *)(smem + G::oQl);            // Ql                       [C][LDA]
     T *Abf = (T *)(smem + G::oAbf);          // A, off-diagonal 16-blocks [L][LDL]
     float *AdT = (float *)(smem + G::oAd);   // A, diagonal 16-blocks, transposed: [J][p][i] = A_J[i][p]
@@ -659,8 +661,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         __syncthreads();
 
-        // the next item's raw rows: fetched now, staged at the top of the next item
-        // (registers stay free during the scan and the operand formation)
+        // the next item's raw values: fetched now, first used by the next item's
+        // scan (the current item's raw registers are dead once the operands exist)
         if constexpr (VEC) {
             const int nx = it + gridDim.x;
             prefetch(nx < items ? nx : items - 1);
@@ -700,24 +702,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         __syncthreads();
 
-        // ---- W^T = Kl^T Diag(b') M^T tiles, staged as -W Diag(e^r) in the Kr
-        //      region (Kr was last read by the A and P tiles); T' fragments ->
-        //      workspace and LDS ---------------------------------------------------------
-        for (int t = wave; t < NWT; t += NW) {
-            const int jb = t / NBD, nb = t % NBD;
-            // M's row block jb is zero beyond column 16 (jb + 1); round up to 32
-            const int K = 32 * ((jb + 2) / 2);
-            f32x4 acc = zero4();
-            for (int k0 = 0; k0 < K; k0 += 32)
-                acc = mma32(frag_col(Kl + k0 * LDA + 16 * nb, LDA, lane),
-                            frag_row(MI + 16 * jb * LDL + k0, LDL, lane), acc);
-            // lane holds W[16 jb + l16][16 nb + g4 + i]
-            const f32x4 es = *(const f32x4 *)(ers + 16 * nb + g4);
-            store4<T>(Wst + (16 * jb + l16) * LDA + 16 * nb + g4, -acc[0] * es[0], -acc[1] * es[1],
-                      -acc[2] * es[2], -acc[3] * es[3]);
-        }
-        for (int rb = wave; rb < NBL; rb += NW) {
-            // T'[j][tau] = M[j][2 tau + 1] beta_tau (tau >= C: zero)
+        // T'[j][tau] = M[j][2 tau + 1] beta_tau (tau >= C: zero): row block rb -> workspace and LDS
+        auto export_tv = [&](int rb) __attribute__((always_inline)) {
             const int gg = lane >> 4;
             const T *mrow = MI + (16 * rb + l16) * LDL;
             uint4 x = make_uint4(0u, 0u, 0u, 0u);
@@ -732,59 +718,113 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 *(uint4 *)(Tvs + (16 * rb + l16) * LDTV + 8 * gg) = x;
             }
             *(uint4 *)(wsb + F::oTv + (rb * 64 + lane) * 16) = x;
-        }
-        __syncthreads();
+        };
+        // W^T tile (channel block nb, sub-step block jb) = Kl^T Diag(b') M^T, staged
+        // as -W Diag(e^r) in the Kr region (Kr was last read by the A and P tiles)
+        auto w_tile = [&](int jb, int nb) __attribute__((always_inline)) {
+            // M's row block jb is zero beyond column 16 (jb + 1); round up to 32
+            const int K = 32 * ((jb + 2) / 2);
+            f32x4 acc = zero4();
+            for (int k0 = 0; k0 < K; k0 += 32)
+                acc = mma32(frag_col(Kl + k0 * LDA + 16 * nb, LDA, lane),
+                            frag_row(MI + 16 * jb * LDL + k0, LDL, lane), acc);
+            // lane holds W[16 jb + l16][16 nb + g4 + i]
+            const f32x4 es = *(const f32x4 *)(ers + 16 * nb + g4);
+            store4<T>(Wst + (16 * jb + l16) * LDA + 16 * nb + g4, -acc[0] * es[0], -acc[1] * es[1],
+                      -acc[2] * es[2], -acc[3] * es[3]);
+        };
+        // Q^T tile (channels 16 nb.., tokens 16 tb..) = ((Ql - P W) Diag(e^r))^T, in
+        // place over Ql; P is zero beyond sub-step 2t + 1
+        auto qh_tile = [&](int nb, int tb) __attribute__((always_inline)) {
+            const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * nb + g4);
+            const f32x4 es = *(const f32x4 *)(ers + 16 * nb + g4);
+            f32x4 acc = {lo_bf16(q0.x) * es[0], hi_bf16(q0.x) * es[1], lo_bf16(q0.y) * es[2],
+                         hi_bf16(q0.y) * es[3]};
+            const int K = imin(L, 32 * (tb + 1));
+            for (int k0 = 0; k0 < K; k0 += 32)
+                acc = mma32(frag_col(Wst + k0 * LDA + 16 * nb, LDA, lane),
+                            frag_row(Ps + 16 * tb * LDL + k0, LDL, lane), acc);
+            store4<T>(Ql + (16 * tb + l16) * LDA + 16 * nb + g4, acc[0], acc[1], acc[2], acc[3]);
+        };
+        // P^ ^T tile (tokens tau 16 nb.., tokens t 16 tb..) = (P T')^T, staged
+        auto ph_tile = [&](int nb, int tb) __attribute__((always_inline)) {
+            f32x4 acc = zero4();
+            const int K = imin(L, 32 * (tb + 1));
+            for (int k0 = 0; k0 < K; k0 += 32)
+                acc = mma32(frag_col(Tvs + k0 * LDTV + 16 * nb, LDTV, lane),
+                            frag_row(Ps + 16 * tb * LDL + k0, LDL, lane), acc);
+            store4<T>(Phs + (16 * tb + l16) * LDTV + 16 * nb + g4, acc[0], acc[1], acc[2], acc[3]);
+        };
+        auto export_ph = [&](int rb) __attribute__((always_inline)) {
+            uint4 x = make_uint4(0u, 0u, 0u, 0u);
+            if (8 * (lane >> 4) < C) x = __builtin_bit_cast(uint4, frag_row(Phs + 16 * rb * LDTV, LDTV, lane));
+            *(uint4 *)(wsb + F::oPh + (rb * 64 + lane) * 16) = x;
+        };
 
-        // ---- -W Diag(e^r) -> workspace; Q^ = (Ql - P W) Diag(e^r) (in place over
-        //      Ql) and P^ = P T' (staged), both as transposed tiles so rows leave
-        //      as runs -------------------------------------------------------------------
-        {
+        if constexpr (NBD == 2 * NW) {
+            // ---- wave-local exports: wave w owns channels 32 w .. 32 w + 31 (one
+            //      fragment column): its W tiles, -W fragments, Q^ tiles and Q^
+            //      fragments need no other wave's results, so no barrier; wave 0
+            //      also forms T' and P^ = P T' ----------------------------------------------
+            const int ks = wave;
+            for (int jb = 0; jb < NBL; ++jb) {
+                w_tile(jb, 2 * wave);
+                w_tile(jb, 2 * wave + 1);
+            }
+            if (wave == 0)
+                for (int rb = 0; rb < NBL; ++rb) export_tv(rb);
+            wave_lds_sync();
+            for (int rb = 0; rb < NBL; ++rb)
+                st_frag(wsb + F::oWn + ((rb * KSD + ks) * 64 + lane) * 16,
+                        frag_row(Wst + 16 * rb * LDA + 32 * ks, LDA, lane));
+            for (int tb = 0; tb < NBC; ++tb) {
+                qh_tile(2 * wave, tb);
+                qh_tile(2 * wave + 1, tb);
+            }
+            if (wave == 0)
+                for (int t = 0; t < NBC * NBC; ++t) ph_tile(t % NBC, t / NBC);
+            wave_lds_sync();
+            for (int tb = 0; tb < NBC; ++tb)
+                st_frag(wsb + F::oQh + ((tb * KSD + ks) * 64 + lane) * 16,
+                        frag_row(Ql + 16 * tb * LDA + 32 * ks, LDA, lane));
+            if (wave == 0)
+                for (int rb = 0; rb < NBC; ++rb) export_ph(rb);
+        } else {
+            // ---- W tiles and T' over all waves; barrier; -W fragments, Q^ and P^
+            //      tiles; barrier; Q^ and P^ fragments ------------------------------------
+            for (int t = wave; t < NWT; t += NW) w_tile(t / NBD, t % NBD);
+            for (int rb = wave; rb < NBL; rb += NW) export_tv(rb);
+            __syncthreads();
             constexpr int NWF = NBL * KSD, NQT = NBD * NBC, NPT2 = NBC * NBC;
             for (int f = wave; f < NWF + NQT + NPT2; f += NW) {
                 if (f < NWF) {
                     const int rb = f / KSD, ks = f % KSD;
                     st_frag(wsb + F::oWn + (f * 64 + lane) * 16, frag_row(Wst + 16 * rb * LDA + 32 * ks, LDA, lane));
                 } else if (f < NWF + NQT) {
-                    // Q^T tile (channels 16 nb.., tokens 16 tb..); P is zero beyond sub-step 2t + 1
-                    const int t = f - NWF, nb = t % NBD, tb = t / NBD;
-                    const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * nb + g4);
-                    const f32x4 es = *(const f32x4 *)(ers + 16 * nb + g4);
-                    f32x4 acc = {lo_bf16(q0.x) * es[0], hi_bf16(q0.x) * es[1], lo_bf16(q0.y) * es[2],
-                                 hi_bf16(q0.y) * es[3]};
-                    const int K = imin(L, 32 * (tb + 1));
-                    for (int k0 = 0; k0 < K; k0 += 32)
-                        acc = mma32(frag_col(Wst + k0 * LDA + 16 * nb, LDA, lane),
-                                    frag_row(Ps + 16 * tb * LDL + k0, LDL, lane), acc);
-                    store4<T>(Ql + (16 * tb + l16) * LDA + 16 * nb + g4, acc[0], acc[1], acc[2], acc[3]);
+                    const int t = f - NWF;
+                    qh_tile(t % NBD, t / NBD);
                 } else {
-                    // P^ ^T tile (tokens tau 16 nb.., tokens t 16 tb..)
-                    const int t = f - NWF - NQT, nb = t % NBC, tb = t / NBC;
-                    f32x4 acc = zero4();
-                    const int K = imin(L, 32 * (tb + 1));
-                    for (int k0 = 0; k0 < K; k0 += 32)
-                        acc = mma32(frag_col(Tvs + k0 * LDTV + 16 * nb, LDTV, lane),
-                                    frag_row(Ps + 16 * tb * LDL + k0, LDL, lane), acc);
-                    store4<T>(Phs + (16 * tb + l16) * LDTV + 16 * nb + g4, acc[0], acc[1], acc[2], acc[3]);
+                    const int t = f - NWF - NQT;
+                    ph_tile(t % NBC, t / NBC);
                 }
             }
-        }
-        __syncthreads();
-        {
+            __syncthreads();
             constexpr int NQF = NBC * KSD;
             for (int f = wave; f < NQF + NBC; f += NW) {
                 if (f < NQF) {
                     const int rb = f / KSD, ks = f % KSD;
                     st_frag(wsb + F::oQh + (f * 64 + lane) * 16, frag_row(Ql + 16 * rb * LDA + 32 * ks, LDA, lane));
                 } else {
-                    const int rb = f - NQF;
-                    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-                    if (8 * (lane >> 4) < C)
-                        x = __builtin_bit_cast(uint4, frag_row(Phs + 16 * rb * LDTV, LDTV, lane));
-                    *(uint4 *)(wsb + F::oPh + (rb * 64 + lane) * 16) = x;
+                    export_ph(f - NQF);
                 }
             }
         }
-        __syncthreads();   // LDS free for the next item
+        // No barrier here: the exports above read only Wst, Ql, Tvs, Phs, Ps, MI,
+        // ers and sb, and the next item first writes any of those after its
+        // wide-chunk vote, which every wave reaches only after finishing its own
+        // exports; before the vote it writes only b', beta and gamma (by wave 0,
+        // after its own reads of sb) and the norm partials, which nothing above
+        // reads.
     }
 }
 
