@@ -19,7 +19,9 @@ unfused (the prologue as PyTorch element-wise ops, then `eda_fwd_chunked` on
 the expanded value-head inputs), and the layer-form decode step; and a dplr
 section: the rank-1 DPLR update of GDN-2/QED (`eda_fwd_chunked_dplr`) on the
 same training shape with QED erase vectors; and a backward section: `eda_bwd`
-(gradients of every input) on the training shape.
+(gradients of every input) on the training shape; and a long_context section:
+the chunked forward at T = 32768 with 32 heads (the long-context
+configuration) and with 16 heads (the metric's H = 16), tokens/s each.
 
 Algorithmic work (d_k = d_v = d, C tokens per chunk, L = 2C sub-steps; each
 token is an erase sub-step and a delta sub-step), per chunk and head:
@@ -217,6 +219,36 @@ def bench_dplr(torch, eda, dev, chunk: int, steps: int) -> dict:
                 value=round(w.B * w.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5))
 
 
+def bench_long(torch, eda, dev, chunk: int) -> dict:
+    """The chunked forward at the 32K-token workloads (sequential chunk chain
+    of 1024 chunks per head)."""
+    from eda_inputs import WORKLOADS, make_workload
+
+    out = {}
+    for name in ("long", "long_h16"):
+        w = WORKLOADS[name]
+        x = make_workload(w, device=dev)
+        o = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
+        Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+        ws = torch.empty(eda.workspace_size(w.B, w.T, w.H, w.dk, w.dv, x["q"].dtype, chunk), dtype=torch.uint8,
+                         device=dev)
+
+        def run():
+            eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
+                            chunk=chunk, out=o, S_final=Sf, workspace=ws)
+
+        run()
+        torch.cuda.synchronize()
+        ms = time_events(torch, run, 5)
+        out[name] = dict(workload=f"{name}: B={w.B} T={w.T} H={w.H} d_k=d_v={w.dk} {w.dtype}, S0 ~ N(0, {w.s0_std})",
+                         value=round(w.B * w.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 4),
+                         token_heads_per_s=round(w.B * w.T * w.H / (ms * 1e-3), 1))
+        print(f"[bench] {name} {ms:.3f} ms", file=sys.stderr, flush=True)
+        del x, o, Sf, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_bwd(torch, eda, dev, w) -> dict:
     """Backward pass on the benchmark workload's shape: gradients of every
     input for a random dO (and no final-state gradient)."""
@@ -260,6 +292,7 @@ def main() -> int:
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-dplr", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -416,6 +449,7 @@ def main() -> int:
     layer = None if args.no_layer else bench_layer(torch, eda, dev, chunk, args.steps)
     dplr = None if args.no_dplr else bench_dplr(torch, eda, dev, chunk, args.steps)
     bwd = None if args.no_bwd else bench_bwd(torch, eda, dev, w)
+    longc = None if (args.no_long or args.workload != "train") else bench_long(torch, eda, dev, chunk)
 
     # fp64 CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -445,7 +479,7 @@ def main() -> int:
                     B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, tokens_per_step=tokens,
                     parallelism="single GPU"),
         roofline=roof_line, cpu_baseline=cpu, chunked_path=path, decode=decode, layer=layer,
-        dplr=dplr, backward=bwd)
+        dplr=dplr, backward=bwd, long_context=longc)
     print(json.dumps(line), flush=True)
     return 0
 
