@@ -243,8 +243,9 @@ eda_status_t eda_fwd_recurrent_step_dplr(const void *q, const void *k, const voi
  *
  * with G = dL/dS_t, Sh, St, r_e, r_k the decayed and erased states and reads
  * of the forward, dSt = G - beta k w^T, z = dSt^T e, dSh = dSt - gamma e z^T.
- * The states are recomputed from fp32 checkpoints (every 4 tokens) kept in
- * the workspace; all arithmetic is fp32.
+ * The states are recomputed from fp32 checkpoints (every 8 tokens) and the
+ * per-token column sums of a first forward sweep, kept in the workspace; all
+ * arithmetic is fp32.
  *
  *   q, k, e : [B, T, H, d_k] dtype;  v, dO : [B, T, H, d_v] dtype
  *   alpha : [B, T, H, d_k] fp32;  beta, gamma : [B, T, H] fp32
@@ -252,7 +253,7 @@ eda_status_t eda_fwd_recurrent_step_dplr(const void *q, const void *k, const voi
  *   dq, dk, de, dalpha : [B, T, H, d_k] fp32;  dv : [B, T, H, d_v] fp32
  *   dbeta, dgamma : [B, T, H] fp32;  dS0 : [B, H, d_k, d_v] fp32 or NULL
  *   workspace : eda_bwd_workspace_size(...) bytes, 256-byte aligned (about
- *               4.3 GB for B = 4, T = 2048, H = 16, d = 128)
+ *               3.4 GB for B = 4, T = 2048, H = 16, d = 128)
  *
  * Supported: 1 <= d_k, d_v <= 128.  No output may overlap an input, the
  * workspace or another output.  Errors as for eda_fwd_chunked.

@@ -15,28 +15,35 @@
 //
 // Layout: one workgroup per (sequence, head, 16-column slice of the values),
 // 128 threads, thread i owns key row i of the state slice and of G in
-// registers.  Column sums (over key rows) are butterflies within a wave plus
-// one exchange between the two waves; row sums (over the slice's columns)
-// stay in the thread, so dq, dk, de, dalpha leave as per-slice partials
-// that a second kernel adds up (deterministically).  The states are not
-// stored per token: a first sweep writes fp32 checkpoints every CB tokens to
+// registers.  Column sums (over key rows) go through LDS: adjacent rows are
+// paired within the wave, the 64 x 32 pair sums are transposed through LDS,
+// four threads add up each column, and the totals come back to everyone.
+// Row sums (over the slice's columns) stay in the thread, so dq, dk, de,
+// dalpha leave as per-slice partials that a second kernel adds up
+// (deterministically).  The states are not stored per token: a first sweep
+// writes fp32 checkpoints every CB tokens and each token's column sums to
 // the workspace, and the reverse sweep recomputes each CB-token segment's
-// states (and their column sums) into LDS before walking it backwards.
+// states from them (no reductions) into LDS before walking it backwards.
+// Every input of a segment is fetched a whole segment ahead of its use.
+#include <type_traits>
+
 #include "eda_common.h"
 
 namespace eda {
 
 constexpr int BW_NT = 128;   // threads: one key row each (d_k <= 128)
 constexpr int BW_NC = 16;    // value columns per workgroup
-constexpr int BW_CB = 4;     // tokens between state checkpoints (LDS: four workgroups per CU)
+constexpr int BW_CB = 8;     // tokens per segment: between state checkpoints, and per input fetch
 constexpr int BW_SP = BW_NC;            // LDS row of a state slice
-constexpr int BW_RW = 2 * BW_NC + 4;    // recorded column sums per token: r_e, r_k, k.e
+constexpr int BW_NR = 2 * BW_NC + 1;    // recorded column sums per token: r_e, r_k, k.e
+constexpr int BW_RW = 2 * BW_NC + 4;    // their LDS row
 
 struct BwdArgs {
     const void *q, *k, *e, *v, *dO;
     const float *alpha, *beta, *gamma, *S0, *dSf;
     float *dv, *dS0;
     float *ckpt;                          // [NS][BH][NCK][128][16]
+    float *recg;                          // [NS][BH][T][NR] column sums of each token
     float *pq, *pk, *pe, *pa;             // [NS][B*T*H][128] partial row sums
     float *pb, *pg;                       // [NS][B*T*H]
     int B, T, H, dk, dvd, NS, NCK;
@@ -58,30 +65,71 @@ __device__ __forceinline__ float wave_total(float x) {
 }
 #undef EDA_BW_DPP
 
-// Sum of x over the 128 threads of the workgroup (both waves), returned to
-// every thread.  `xw` is a two-buffer exchange area [2][2][N]; `par` flips
-// between calls so that a fast wave never overwrites values still being read.
-template <int N>
-__device__ __forceinline__ void wg_colsum(float (&x)[N], float *xw, int &par, int lane, int wave) {
+// Column sums of 32 values over the 128 threads of the workgroup, returned to
+// every thread (and, with EXTRA, of one more value).  Lanes 2m and 2m + 1 add
+// their values with a DPP quad swap, the even lane writes the first 16 pair
+// sums and the odd lane the last 16 to row i/2 of Xs [64][33]; after a
+// barrier thread t adds column t % 32 over 16 of those rows, the two such
+// partials of a wave meet with a lane swap, and the two waves' sums go
+// through Ps [2][36] to everyone.  Xs and Ps are read only between this
+// call's two barriers (and after the second), so consecutive calls need no
+// further synchronisation.
+constexpr int BW_XS = 33, BW_PS = 36;
+template <bool EXTRA>
+__device__ __forceinline__ void wg_colsum32(float (&x)[32], float &extra, float *Xs, float *Ps, int i, int lane,
+                                            int wave) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) x[n] = wave_total(x[n]);
-    float *mine = xw + (par * 2 + wave) * N, *other = xw + (par * 2 + (wave ^ 1)) * N;
-    if (lane == 0) {
+    for (int n = 0; n < 32; ++n)
+        x[n] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x[n]), 0xb1, 0xf, 0xf,
+                                                                      false));   // quad_perm [1,0,3,2]
+    {
+        // (a bit-mask select: a conditional choice between the two halves
+        // would be compiled into an indexed access to a stack copy of x)
+        const int odd = i & 1, msk = -odd;
+        float *row = Xs + (i >> 1) * BW_XS + 16 * odd;
 #pragma unroll
-        for (int n = 0; n < N; ++n) mine[n] = x[n];
+        for (int n = 0; n < 16; ++n) {
+            const int lo = __builtin_bit_cast(int, x[n]), hi = __builtin_bit_cast(int, x[16 + n]);
+            row[n] = __builtin_bit_cast(float, (lo & ~msk) | (hi & msk));
+        }
+    }
+    if (EXTRA) extra = wave_total(extra);
+    __syncthreads();
+    {
+        const int j = i & 31, p = i >> 5;
+        const float *col = Xs + 16 * p * BW_XS + j;
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            s0 += col[r * BW_XS];
+            s1 += col[(r + 1) * BW_XS];
+        }
+        float s = s0 + s1;
+        s += __shfl_xor(s, 32, 64);
+        if (lane < 32) Ps[wave * BW_PS + j] = s;
+        if (EXTRA && lane == 0) Ps[wave * BW_PS + 32] = extra;
     }
     __syncthreads();
 #pragma unroll
-    for (int n = 0; n < N; ++n) x[n] += other[n];
-    par ^= 1;
+    for (int n = 0; n < 32; n += 4) {
+        const float4 u = *(const float4 *)(Ps + n), w = *(const float4 *)(Ps + BW_PS + n);
+        x[n] = u.x + w.x; x[n + 1] = u.y + w.y; x[n + 2] = u.z + w.z; x[n + 3] = u.w + w.w;
+    }
+    if (EXTRA) extra = Ps[32] + Ps[BW_PS + 32];
 }
 
 template <typename Tin>
 __global__ void __launch_bounds__(BW_NT) eda_bwd_kernel(BwdArgs a) {
-    constexpr int NC = BW_NC, CB = BW_CB;
+    constexpr int NC = BW_NC, CB = BW_CB, NR = BW_NR, RW = BW_RW;
+    constexpr int NCOL = CB * 2 * NC, CPT = NCOL / BW_NT;          // slice entries per thread
+    constexpr int NREC = CB * NR, RPT = (NREC + BW_NT - 1) / BW_NT;  // recorded sums per thread
+    static_assert(NCOL % BW_NT == 0 && 2 * CB <= BW_NT && 2 * NC == 32, "segment staging split");
     __shared__ __attribute__((aligned(16))) float Sbuf[CB][BW_NT][BW_SP];   // states before each token
-    __shared__ float rec[CB][BW_RW];                                         // their column sums
-    __shared__ float xw[2 * 2 * (2 * NC + 1)];
+    __shared__ __attribute__((aligned(16))) float rec[2][CB][RW];           // their column sums, two segments
+    __shared__ __attribute__((aligned(16))) float colb[2][CB][2][NC];       // v and dO slices, two segments
+    __shared__ float unib[2][CB][2];                                        // beta and gamma, two segments
+    __shared__ __attribute__((aligned(16))) float Xs[64 * BW_XS];
+    __shared__ __attribute__((aligned(16))) float Ps[2 * BW_PS];
 
     const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
     const int s = blockIdx.x % a.NS, bh = blockIdx.x / a.NS;
@@ -89,72 +137,153 @@ __global__ void __launch_bounds__(BW_NT) eda_bwd_kernel(BwdArgs a) {
     const int BH = a.B * a.H;
     const long BTH = (long)a.B * a.T * a.H;
     const bool rok = i < a.dk;
-    int par = 0;
+    const int ri = rok ? i : a.dk - 1;   // a valid row to read for padded rows
     auto tokrow = [&](int t) { return ((long)b * a.T + t) * a.H + h; };
-    auto ld = [](const void *p, long idx) { return to_f32(((const Tin *)p)[idx]); };
+    auto tclamp = [&](int t) { return t < a.T ? t : a.T - 1; };
 
     float S[NC];
 #pragma unroll
     for (int j = 0; j < NC; ++j)
         S[j] = (a.S0 && rok && n0 + j < a.dvd) ? a.S0[((long)bh * a.dk + i) * a.dvd + n0 + j] : 0.f;
 
-    // the inputs of one token for this thread's row and the slice's columns,
-    // loaded one token ahead of their use
-    struct Tok {
-        float q, k, e, a, bt, gm, v[NC], dO[NC];
+    float *ck = a.ckpt + ((long)s * BH + bh) * a.NCK * (BW_NT * NC);
+    float *rg = a.recg + ((long)s * BH + bh) * a.T * NR;
+
+    // The inputs of one segment of CB tokens, fetched a whole segment ahead
+    // of their use, raw and from clamped (always valid) addresses so that no
+    // load waits before the next segment: this thread's key row of every
+    // token; CPT entries of the segment's value / output-gradient slice and
+    // one beta or gamma (threads below 2 CB), which go to LDS for everyone;
+    // in the reverse sweep also the checkpoint row and RPT recorded sums.
+    // Padding (rows past d_k, columns past d_v) is zeroed when committed;
+    // tokens past the end are never used.
+    struct Seg {
+        Tin q[CB], k[CB], e[CB];
+        float al[CB];
+        Tin cv[CPT];
+        float u;
+        float ckp[NC];
+        float rc[RPT];
     };
-    auto load_tok = [&](int t, bool with_out) {
-        Tok x;
-        const long row = tokrow(t);
-        x.q = rok && with_out ? ld(a.q, row * a.dk + i) : 0.f;
-        x.k = rok ? ld(a.k, row * a.dk + i) : 0.f;
-        x.e = rok ? ld(a.e, row * a.dk + i) : 0.f;
-        x.a = rok ? a.alpha[row * a.dk + i] : 1.f;
-        x.bt = a.beta[row];
-        x.gm = a.gamma[row];
+    auto load_seg = [&](int c, auto rev_c) __attribute__((always_inline)) {
+        constexpr bool REV = decltype(rev_c)::value;
+        Seg x;
+        const int t0 = c * CB;
 #pragma unroll
-        for (int j = 0; j < NC; ++j) {
-            const bool cj = n0 + j < a.dvd;
-            x.v[j] = cj ? ld(a.v, row * a.dvd + n0 + j) : 0.f;
-            x.dO[j] = cj && with_out ? ld(a.dO, row * a.dvd + n0 + j) : 0.f;
+        for (int tau = 0; tau < CB; ++tau) {
+            const long ro = tokrow(tclamp(t0 + tau)) * a.dk + ri;
+            if (REV) x.q[tau] = ((const Tin *)a.q)[ro];
+            x.k[tau] = ((const Tin *)a.k)[ro];
+            x.e[tau] = ((const Tin *)a.e)[ro];
+            x.al[tau] = a.alpha[ro];
+        }
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) {
+            const int f = i + BW_NT * m, tau = f / (2 * NC), which = (f / NC) & 1, j = f % NC;
+            const int col = n0 + j < a.dvd ? n0 + j : a.dvd - 1;
+            const Tin *src = (REV && which) ? (const Tin *)a.dO : (const Tin *)a.v;
+            x.cv[m] = src[tokrow(tclamp(t0 + tau)) * a.dvd + col];
+        }
+        x.u = ((i & 1) ? a.gamma : a.beta)[tokrow(tclamp(t0 + ((i >> 1) % CB)))];
+        if (REV) {
+            const float4 *src = (const float4 *)(ck + ((long)c * BW_NT + i) * NC);
+#pragma unroll
+            for (int j = 0; j < NC; j += 4) {
+                const float4 y = src[j / 4];
+                x.ckp[j] = y.x; x.ckp[j + 1] = y.y; x.ckp[j + 2] = y.z; x.ckp[j + 3] = y.w;
+            }
+            const long last = (long)a.T * NR - 1;
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const long f = (long)t0 * NR + i + BW_NT * m;
+                x.rc[m] = rg[f < last ? f : last];
+            }
         }
         return x;
     };
-
-    // one token forward from S (the state before the token); the column sums
-    // are returned in r (r_e, r_k, k.e)
-    auto fwd_step = [&](float (&St)[NC], const Tok &x, float (&r)[2 * NC + 1]) {
-        const float ki = x.k, ei = x.e, ai = x.a, bt = x.bt, gm = x.gm;
-        float Sh[NC];
+    // the shared part of a fetched segment -> LDS buffers `buf`; the row part
+    // -> the caller's token queues
+    float qr[CB], kr[CB], er[CB], ar[CB];
+    auto commit = [&](const Seg &x, int buf, auto rev_c) __attribute__((always_inline)) {
+        constexpr bool REV = decltype(rev_c)::value;
 #pragma unroll
-        for (int j = 0; j < NC; ++j) {
-            Sh[j] = ai * St[j];
-            r[j] = ei * Sh[j];
-            r[NC + j] = ki * Sh[j];
+        for (int m = 0; m < CPT; ++m) {
+            const int f = i + BW_NT * m, which = (f / NC) & 1, j = f % NC;
+            const bool ok = n0 + j < a.dvd && (REV || which == 0);
+            (&colb[buf][0][0][0])[f] = ok ? to_f32(x.cv[m]) : 0.f;
         }
-        r[2 * NC] = ki * ei;
-        wg_colsum<2 * NC + 1>(r, xw, par, lane, wave);
+        if (i < 2 * CB) (&unib[buf][0][0])[i] = x.u;
+        if (REV) {
 #pragma unroll
-        for (int j = 0; j < NC; ++j) {
-            r[NC + j] -= gm * r[2 * NC] * r[j];                        // r_k = Sh^T k - gamma (k.e) r_e
-            St[j] = Sh[j] - gm * ei * r[j] + bt * ki * (x.v[j] - r[NC + j]);
+            for (int m = 0; m < RPT; ++m) {
+                const int f = i + BW_NT * m;
+                if (f < NREC) rec[buf][f / NR][f % NR] = x.rc[m];
+            }
+        }
+#pragma unroll
+        for (int tau = 0; tau < CB; ++tau) {
+            qr[tau] = REV && rok ? to_f32(x.q[tau]) : 0.f;
+            kr[tau] = rok ? to_f32(x.k[tau]) : 0.f;
+            er[tau] = rok ? to_f32(x.e[tau]) : 0.f;
+            ar[tau] = rok ? x.al[tau] : 1.f;
         }
     };
-
-    // ---- sweep 1: checkpoints of the state before tokens 0, CB, 2 CB, ...
-    float *ck = a.ckpt + ((long)s * BH + bh) * a.NCK * (BW_NT * NC);
-    {
-        Tok cur = load_tok(0, false);
-        for (int t = 0; t < a.T; ++t) {
-            const Tok nxt = load_tok(t + 1 < a.T ? t + 1 : t, false);
-            if (t % CB == 0) {
-                float4 *dst = (float4 *)(ck + ((long)(t / CB) * BW_NT + i) * NC);
+    // The token loops stay rolled (the kernel's code must fit the instruction
+    // cache), so the per-token row inputs are queues rotated by one token per
+    // step: the forward walk reads slot 0 and rotates left, which leaves token
+    // nt - 1 in slot CB - 1 for the backward walk, which rotates right.
+    auto rotl = [](float (&x)[CB]) {
+        const float f = x[0];
 #pragma unroll
-                for (int j = 0; j < NC; j += 4) dst[j / 4] = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+        for (int j = 0; j + 1 < CB; ++j) x[j] = x[j + 1];
+        x[CB - 1] = f;
+    };
+    auto rotr = [](float (&x)[CB]) {
+        const float l = x[CB - 1];
+#pragma unroll
+        for (int j = CB - 1; j > 0; --j) x[j] = x[j - 1];
+        x[0] = l;
+    };
+    using Fwd = std::integral_constant<bool, false>;
+    using Rev = std::integral_constant<bool, true>;
+
+    // ---- sweep 1: checkpoints of the state before tokens 0, CB, 2 CB, ...,
+    // and every token's column sums r_e, r_k (after the erase), k.e
+    {
+        Seg nxt = load_seg(0, Fwd{});
+        for (int c = 0; c < a.NCK; ++c) {
+            const int t0 = c * CB, nt = min(CB, a.T - t0), buf = c & 1;
+            commit(nxt, buf, Fwd{});
+            __syncthreads();   // this segment's slice is in LDS; the previous one is no longer read
+            if (c + 1 < a.NCK) nxt = load_seg(c + 1, Fwd{});
+            float4 *dst = (float4 *)(ck + ((long)c * BW_NT + i) * NC);
+#pragma unroll
+            for (int j = 0; j < NC; j += 4) dst[j / 4] = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+#pragma unroll 1
+            for (int tau = 0; tau < nt; ++tau) {
+                const float ki = kr[0], ei = er[0], ai = ar[0];
+                const float bt = unib[buf][tau][0], gm = unib[buf][tau][1];
+                const float *vs = colb[buf][tau][0];
+                float Sh[NC], r[2 * NC];
+#pragma unroll
+                for (int j = 0; j < NC; ++j) {
+                    Sh[j] = ai * S[j];
+                    r[j] = ei * Sh[j];
+                    r[NC + j] = ki * Sh[j];
+                }
+                float ke = ki * ei;
+                wg_colsum32<true>(r, ke, Xs, Ps, i, lane, wave);
+                float mine = ke;   // thread n records sum n
+#pragma unroll
+                for (int j = 0; j < NC; ++j) {
+                    r[NC + j] -= gm * ke * r[j];                          // r_k = Sh^T k - gamma (k.e) r_e
+                    S[j] = Sh[j] - gm * ei * r[j] + bt * ki * (vs[j] - r[NC + j]);
+                    mine = i == j ? r[j] : mine;
+                    mine = i == NC + j ? r[NC + j] : mine;
+                }
+                if (i < NR) rg[(long)(t0 + tau) * NR + i] = mine;
+                rotl(kr); rotl(er); rotl(ar);
             }
-            float r[2 * NC + 1];
-            fwd_step(S, cur, r);
-            cur = nxt;
         }
     }
 
@@ -163,63 +292,60 @@ __global__ void __launch_bounds__(BW_NT) eda_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NC; ++j)
         G[j] = (a.dSf && rok && n0 + j < a.dvd) ? a.dSf[((long)bh * a.dk + i) * a.dvd + n0 + j] : 0.f;
+    // (sweep 1's stores of the checkpoints and sums are complete: the
+    // workgroup barriers since then wait for every wave's memory operations)
+    __syncthreads();
+    Seg nxt = load_seg(a.NCK - 1, Rev{});
     for (int c = a.NCK - 1; c >= 0; --c) {
-        const int t0 = c * CB, nt = min(CB, a.T - t0);
-        {
-            const float4 *src = (const float4 *)(ck + ((long)c * BW_NT + i) * NC);
+        const int t0 = c * CB, nt = min(CB, a.T - t0), buf = c & 1;
+        commit(nxt, buf, Rev{});
 #pragma unroll
-            for (int j = 0; j < NC; j += 4) {
-                const float4 x = src[j / 4];
-                S[j] = x.x; S[j + 1] = x.y; S[j + 2] = x.z; S[j + 3] = x.w;
-            }
+        for (int j = 0; j < NC; ++j) S[j] = nxt.ckp[j];
+        __syncthreads();   // slice and sums in LDS; the previous segment's buffers no longer read
+        if (c > 0) nxt = load_seg(c - 1, Rev{});
+        // recompute the segment's states into this thread's rows of Sbuf
+#pragma unroll 1
+        for (int tau = 0; tau < nt; ++tau) {
+#pragma unroll
+            for (int j = 0; j < NC; j += 4)
+                *(float4 *)&Sbuf[tau][i][j] = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+            const float ki = kr[0], ei = er[0], ai = ar[0];
+            const float bt = unib[buf][tau][0], gm = unib[buf][tau][1];
+            const float *vs = colb[buf][tau][0], *rr = rec[buf][tau];
+#pragma unroll
+            for (int j = 0; j < NC; ++j) S[j] = ai * S[j] - gm * ei * rr[j] + bt * ki * (vs[j] - rr[NC + j]);
+            rotl(qr); rotl(kr); rotl(er); rotl(ar);
         }
-        {
-            Tok cur = load_tok(t0, false);
-            for (int tau = 0; tau < nt; ++tau) {
-                const Tok nxt = load_tok(tau + 1 < nt ? t0 + tau + 1 : t0 + tau, false);
-#pragma unroll
-                for (int j = 0; j < NC; ++j) Sbuf[tau][i][j] = S[j];
-                float r[2 * NC + 1];
-                fwd_step(S, cur, r);
-                if (i == 0) {
-#pragma unroll
-                    for (int n = 0; n < 2 * NC + 1; ++n) rec[tau][n] = r[n];
-                }
-                cur = nxt;
-            }
-        }
-        __syncthreads();
-        Tok cur = load_tok(t0 + nt - 1, true);
+#pragma unroll 1
         for (int tau = nt - 1; tau >= 0; --tau) {
             const int t = t0 + tau;
             const long row = tokrow(t);
-            const Tok nxt = load_tok(tau > 0 ? t - 1 : t, true);
-            const float qi = cur.q, ki = cur.k, ei = cur.e, ai = cur.a, bt = cur.bt, gm = cur.gm;
-            const float ke = rec[tau][2 * NC];
-            float Sp[NC], Sh[NC], St[NC], up[NC], dO[NC], re[NC];
+            const float qi = qr[CB - 1], ki = kr[CB - 1], ei = er[CB - 1], ai = ar[CB - 1];
+            rotr(qr); rotr(kr); rotr(er); rotr(ar);
+            const float bt = unib[buf][tau][0], gm = unib[buf][tau][1];
+            const float *vs = colb[buf][tau][0], *dOs = colb[buf][tau][1], *rr = rec[buf][tau];
+            const float ke = rr[2 * NC];
+            float Sp[NC], Sh[NC], St[NC], up[NC], re[NC];
             float dq = 0.f;
 #pragma unroll
             for (int j = 0; j < NC; ++j) {
                 Sp[j] = Sbuf[tau][i][j];
-                re[j] = rec[tau][j];
-                const float vj = cur.v[j];
-                dO[j] = cur.dO[j];
+                re[j] = rr[j];
                 Sh[j] = ai * Sp[j];
                 St[j] = Sh[j] - gm * ei * re[j];
-                up[j] = vj - rec[tau][NC + j];
+                up[j] = vs[j] - rr[NC + j];
                 const float Sn = St[j] + bt * ki * up[j];
-                G[j] += qi * dO[j];                                      // dL/dS' includes q dO^T
-                dq += Sn * dO[j];
+                G[j] += qi * dOs[j];                                     // dL/dS' includes q dO^T
+                dq += Sn * dOs[j];
             }
-            float wz[2 * NC + 1];
+            float wz[2 * NC], unused = 0.f;
 #pragma unroll
             for (int j = 0; j < NC; ++j) {
                 wz[j] = G[j] * ki;                                       // -> w = G^T k
                 wz[NC + j] = G[j] * ei;                                  // -> G^T e
             }
-            wz[2 * NC] = 0.f;
-            wg_colsum<2 * NC + 1>(wz, xw, par, lane, wave);
-            float dkp = 0.f, dep = 0.f, dap = 0.f, dbp = 0.f, dgp = 0.f;
+            wg_colsum32<false>(wz, unused, Xs, Ps, i, lane, wave);
+            float dkp = 0.f, dep = 0.f, dap = 0.f, dbp = 0.f, dgp = 0.f, dvj = 0.f;
 #pragma unroll
             for (int j = 0; j < NC; ++j) {
                 const float w = wz[j];
@@ -232,22 +358,17 @@ __global__ void __launch_bounds__(BW_NT) eda_bwd_kernel(BwdArgs a) {
                 dbp += w * up[j];
                 dgp += z * re[j];
                 G[j] = ai * dSh;
+                dvj = i == j ? w : dvj;
             }
             const long pr = (long)s * BTH + row;
-            if (i == 0) {
-#pragma unroll
-                for (int j = 0; j < NC; ++j)
-                    if (n0 + j < a.dvd) a.dv[row * a.dvd + n0 + j] = bt * wz[j];
-                a.pb[pr] = dbp;
-                a.pg[pr] = -dgp;
-            }
+            if (i < NC && n0 + i < a.dvd) a.dv[row * a.dvd + n0 + i] = bt * dvj;
+            if (i == NC) a.pb[pr] = dbp;
+            if (i == NC + 1) a.pg[pr] = -dgp;
             a.pq[pr * BW_NT + i] = dq;
             a.pk[pr * BW_NT + i] = bt * dkp;
             a.pe[pr * BW_NT + i] = -gm * dep;
             a.pa[pr * BW_NT + i] = dap;
-            cur = nxt;
         }
-        __syncthreads();   // Sbuf and rec are refilled by the next segment
     }
     if (a.dS0 && rok) {
 #pragma unroll
@@ -288,8 +409,8 @@ size_t bwd_ws_bytes(int B, int T, int H, int dk, int dv) {
     (void)dk;
     const long NS = (dv + BW_NC - 1) / BW_NC, NCK = (T + BW_CB - 1) / BW_CB, BTH = (long)B * T * H;
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-    return al((size_t)NS * B * H * NCK * BW_NT * BW_NC * 4) + 4 * al((size_t)NS * BTH * BW_NT * 4) +
-           2 * al((size_t)NS * BTH * 4);
+    return al((size_t)NS * B * H * NCK * BW_NT * BW_NC * 4) + al((size_t)NS * BTH * BW_NR * 4) +
+           4 * al((size_t)NS * BTH * BW_NT * 4) + 2 * al((size_t)NS * BTH * 4);
 }
 
 template <typename Tin>
@@ -308,6 +429,8 @@ hipError_t launch_bwd(const void *q, const void *k, const void *e, const void *v
     a.dv = dv; a.dS0 = dS0;
     a.ckpt = (float *)w;
     w += al((size_t)NS * B * H * NCK * BW_NT * BW_NC * 4);
+    a.recg = (float *)w;
+    w += al((size_t)NS * BTH * BW_NR * 4);
     float **parts[4] = {&a.pq, &a.pk, &a.pe, &a.pa};
     for (float **p : parts) {
         *p = (float *)w;

@@ -17,7 +17,8 @@
 // St = Sh - gamma e r_e^T into St^T k and S_new^T q).  The paper's Sec. 3.5
 // notes the decode cost is dominated by reading and writing the state; the
 // kernel is therefore laid out for HBM streaming.  A persistent grid of
-// 512-thread workgroups (four per compute unit) walks the states; per state
+// 512-thread workgroups (four per compute unit launched, one or two resident
+// at a time by register use) walks the states; per state
 // each thread owns a 4-column strip of 8 rows (rows rg + 16m), so every
 // wavefront load/store instruction touches 1 KB of contiguous memory and all
 // 8 loads of a thread are in flight together.  The state is touched exactly
@@ -62,8 +63,11 @@ constexpr int DEC_NW = DEC_NT / 64;   // wavefronts
 
 constexpr int DEC_PLAIN = 0, DEC_LAYER = 1, DEC_DPLR = 2;
 
+// The 128-square plain and DPLR variants fit in 128 VGPRs, which lets two
+// workgroups share a CU so that one streams while the other reduces (about 2%
+// faster than one per CU); the others would spill at that limit.
 template <typename Tin, bool FULL, int MODE>
-__global__ void __launch_bounds__(DEC_NT)
+__global__ void __launch_bounds__(DEC_NT) __attribute__((amdgpu_waves_per_eu(FULL && MODE != 1 ? 4 : 1)))
 eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ e,
                   const Tin *__restrict__ v, const void *__restrict__ decay,
                   const float *__restrict__ A_log, const float *__restrict__ dt_bias,

@@ -54,6 +54,7 @@ def check_grads(got, ref, dtype, label):
     ("f32", 1, 20, 2, 16, 16, True, True),
     ("f32", 2, 13, 1, 31, 20, True, False),      # ragged segment, two value slices, padded rows
     ("f32", 1, 9, 1, 2, 1, False, True),
+    ("f32", 1, 3, 2, 16, 16, True, True),        # shorter than one input segment
     ("bf16", 2, 70, 2, 128, 128, True, True),
     ("bf16", 1, 40, 3, 64, 48, False, False),
 ])
