@@ -39,8 +39,9 @@
 // Kernel 2 (eda_bf16_state): one workgroup per (head, slice of value
 //   columns), serial over chunks, fp32 state in registers.  The factors are
 //   stored in the exact per-lane order of the matrix-core operands, so each
-//   wave fetches its own operands straight into registers two chunks ahead;
-//   only S'^T, U^T, the value slice and the outputs pass through LDS.  Two
+//   wave fetches its own operands straight into registers three chunks
+//   ahead; only S'^T, U^T, the value slice and the outputs pass through LDS,
+//   and each role reads all its LDS operands before its first product.  Two
 //   barriers per chunk.
 //
 // Workspace: one block of Fac<C, D>::bytes per chunk and head.  A "fragment"
@@ -917,7 +918,8 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
 
     // One chunk loop per role: straight-line code with a fixed number of
     // memory operations per chunk, so the waits before each use only cover
-    // operands fetched two chunks earlier (chunk indices clamped, never skipped).
+    // operands fetched three chunks earlier (chunk indices clamped, never
+    // skipped).
     auto run = [&](auto role) __attribute__((always_inline)) {
         constexpr int RL = decltype(role)::value;   // 0 U, 1 state, 2 output, 3 mover
         constexpr bool RU = RL == 0, RS = RL == 1, RO = RL == 2, RM = RL == 3;
@@ -1013,39 +1015,53 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 store4<T>(St + (16 * cb + l16) * LDT + 16 * rb + g4, S[cb][0], S[cb][1], S[cb][2], S[cb][3]);
         };
 
-        auto body = [&](Set &cur, Set &nxt, Set &fut, int c) __attribute__((always_inline)) {
-            const int cf = c + 2 < NC ? c + 2 : NC - 1;   // chunk whose operands are fetched now
+        auto body = [&](Set &cur, Set &nxt, Set &far, int c) __attribute__((always_inline)) {
+            const int cf = c + 3 < NC ? c + 3 : NC - 1;   // chunk whose operands are fetched now
             __syncthreads();   // S^T, the value slice of chunk c and its decay are in LDS
             f32x4 acc[NCB];
             const T *Vs = (const T *)(smem + G::oVs + (c & 1) * G::szVs);
             if constexpr (RU) {
                 // U = T' V - W S  (16 rows, all slice columns) -> U^T in LDS
                 // (one instruction shape for the whole accumulation chain: at C = 16
-                // the k = 32 product reads 16 zero rows of the value buffer)
+                // the k = 32 product reads 16 zero rows of the value buffer).  All
+                // LDS operands are read before the first product, so the chain pays
+                // one LDS latency instead of one per step.
+                bf16x8 vf[NCB], sf[KSD][NCB];
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    acc[cb] = mma32(cur.R[KSD], frag_col(Vs + 16 * cb, LDV, lane), zero4());
+                for (int cb = 0; cb < NCB; ++cb) vf[cb] = frag_col(Vs + 16 * cb, LDV, lane);
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
-                        acc[cb] = mma32(cur.R[ks], frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), acc[cb]);
+                    for (int cb = 0; cb < NCB; ++cb) sf[ks][cb] = frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(cur.R[KSD], vf[cb], zero4());
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(cur.R[ks], sf[ks][cb], acc[cb]);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
                     store4<T>(Ut + (16 * cb + l16) * LDU + 16 * rb + g4, acc[cb][0], acc[cb][1], acc[cb][2],
                               acc[cb][3]);
             }
-            if constexpr (RS) load(fut, cf);
+            if constexpr (RS) load(far, cf);
             if constexpr (RO) {
                 // o^T = S^T Q^^T + V^T P^^T for the wave's 16 tokens -> rows of o in LDS
+                bf16x8 vf[NCB], sf[KSD][NCB];
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    acc[cb] = mma32(frag_col(Vs + 16 * cb, LDV, lane), cur.R[KSD], zero4());
+                for (int cb = 0; cb < NCB; ++cb) vf[cb] = frag_col(Vs + 16 * cb, LDV, lane);
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
-                        acc[cb] = mma32(frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane), cur.R[ks], acc[cb]);
+                    for (int cb = 0; cb < NCB; ++cb) sf[ks][cb] = frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(vf[cb], cur.R[KSD], zero4());
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(sf[ks][cb], cur.R[ks], acc[cb]);
                 const int tr = 16 * rb + l16;
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
@@ -1053,21 +1069,26 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
             }
             if constexpr (RM) {
                 if (c + 1 < NC) put_v(nxt, c + 1);
-                load(fut, cf);
+                load(far, cf);
             }
             __syncthreads();   // U^T and the outputs complete; S^T no longer read
-            if constexpr (RU || RO) load(fut, cf);
+            if constexpr (RU || RO) load(far, cf);
             if constexpr (RS) {
                 // S <- e^{G_C} S + Kr^T U; S^T of the next chunk
                 const f32x4 dc = decay(c);
+                bf16x8 uf[KSL][NCB];
+#pragma unroll
+                for (int ks = 0; ks < KSL; ++ks)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) uf[ks][cb] = frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
                     f32x4 a;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) a[i] = dc[i] * S[cb][i];
 #pragma unroll
-                    for (int ks = 0; ks < KSL; ++ks)
-                        a = mma32(cur.R[ks], frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane), a);
+                    for (int ks = 0; ks < KSL; ++ks) a = mma32(cur.R[ks], uf[ks][cb], a);
                     S[cb] = a;
                 }
                 if (c + 1 < NC) write_St();
@@ -1076,19 +1097,24 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
             if constexpr (RM) flush(c);
         };
 
-        Set A, B, X;
+        // four operand sets in rotation: the chunk in use, the next two, and
+        // the one being fetched
+        Set A, B, X, Y;
         load(A, 0);
         load(B, NC > 1 ? 1 : 0);
+        load(X, NC > 2 ? 2 : NC - 1);
         if constexpr (RM) put_v(A, 0);
         if constexpr (RS) write_St();
         int c = 0;
-        for (; c + 3 <= NC; c += 3) {
-            body(A, B, X, c);
+        for (; c + 4 <= NC; c += 4) {
+            body(A, B, Y, c);
             body(B, X, A, c + 1);
-            body(X, A, B, c + 2);
+            body(X, Y, B, c + 2);
+            body(Y, A, X, c + 3);
         }
-        if (c < NC) body(A, B, X, c);
+        if (c < NC) body(A, B, Y, c);
         if (c + 1 < NC) body(B, X, A, c + 1);
+        if (c + 2 < NC) body(X, Y, B, c + 2);
 
         if constexpr (RS) {
             if (S_final) {
