@@ -444,7 +444,7 @@ def main() -> int:
                       ms_per_token_step=round(ms_tok, 5),
                       roofline=dict(kernel="eda_decode_kernel", bound="hbm", achieved=round(gbs, 2),
                                     peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 5),
-                                    traffic=None))
+                                    traffic=measured_traffic("eda_decode_kernel", "decode")))
         print(f"[bench] decode {ms_tok * 1e3:.2f} us/step, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
         del xd, per
 

@@ -11,7 +11,8 @@ Two steps (the first is the program rocprofv3 profiles, once per counter):
 
 `run` builds the workload's inputs, then launches a calibration kernel that
 reads and writes a known number of bytes (an fp32 scale of 256 MiB, three
-times), then three chunked forwards.  `summarize` scales each kernel's
+times), then three chunked forwards (for the decode workload: three decode
+steps, state in place).  `summarize` scales each kernel's
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same counter reported
 for the calibration kernel and writes profiles/traffic_<kernel>_<workload>.txt,
 tagged with the SHA-1 of the kernel source so that stale figures are not used.
@@ -30,7 +31,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CALIB_BYTES = 256 << 20
 NCALIB = 3
-KERNELS = {"eda_bf16_factors": "eda_bf16.hip", "eda_bf16_state": "eda_bf16.hip"}
+KERNELS = {"eda_bf16_factors": "eda_bf16.hip", "eda_bf16_state": "eda_bf16.hip",
+           "eda_decode_kernel": "eda_decode.hip"}
 
 
 def run(workload: str) -> None:
@@ -43,19 +45,29 @@ def run(workload: str) -> None:
     dev = torch.device("cuda:0")
     w = WORKLOADS[workload]
     x = make_workload(w, device=dev)
-    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
-    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    decode = w.T == 1
+    if decode:
+        S = x["S0"].clone()
+        o = torch.empty((w.B, w.H, w.dv), dtype=x["q"].dtype, device=dev)
+    else:
+        o = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
+        S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(NCALIB):
         torch.mul(src, 1.0, out=dst)   # reads and writes CALIB_BYTES each
     torch.cuda.synchronize()
-    for _ in range(3):
-        eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
-                        out=o, S_final=S)
+    for t in range(3):
+        if decode:
+            eda.recurrent_step(*(x[n][t] for n in ("q", "k", "e", "v", "alpha", "beta", "gamma")), S,
+                               S_out=S, o=o)
+        else:
+            eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
+                            out=o, S_final=S)
     torch.cuda.synchronize()
-    print(f"[traffic] ran calibration and 3 forwards of {workload}", flush=True)
+    print(f"[traffic] ran calibration and 3 {'decode steps' if decode else 'forwards'} of {workload}",
+          flush=True)
 
 
 def per_dispatch(directory: str, counter: str):
@@ -125,7 +137,10 @@ def algorithmic_bytes(workload: str) -> dict:
     n = w.B * w.T * w.H
     state_io = (2 if w.s0_std > 0 else 1) * w.B * w.H * w.dk * w.dv * 4
     return {"eda_bf16_factors": n * (3 * w.dk * es + w.dk * 4 + 8),
-            "eda_bf16_state": n * (2 * w.dv * es) + state_io}
+            "eda_bf16_state": n * (2 * w.dv * es) + state_io,
+            # decode: the state read and written, one token's q, k, e, v, alpha,
+            # beta, gamma in and o out per (sequence, head)
+            "eda_decode_kernel": w.B * w.H * (2 * w.dk * w.dv * 4 + (3 * w.dk + 2 * w.dv) * es + w.dk * 4 + 8)}
 
 
 def main() -> int:
