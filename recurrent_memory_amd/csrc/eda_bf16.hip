@@ -875,14 +875,25 @@ template <int NR, int KSL>
 struct FragSet {
     bf16x8 R[NR];   // role operands: -W and T' (U), Q^ and P^ (output), Kr^T (state), v (movers)
     uint2 sc;       // movers: one 8-byte piece of the chunk's decay
+    uint32_t pf[2]; // movers: one word of each of this slice's lines of a later chunk's block
 };
+
+// L2 warm-up of the state pass (when the workspace exceeds the MALL): while
+// fetching chunk c's operands, the mover wave of slice j also reads one word
+// of every R-th 128-byte line (j, j + R, ...) of chunk c + WARM_AHEAD's block,
+// so the R slices of a head (same XCD, one L2) together bring that block into
+// L2 before its fragments are fetched, at 1/R of a block of extra traffic per
+// compute unit.  The words are consumed, unused, when the chunk's set is.
+constexpr int WARM_AHEAD = 4;
+constexpr size_t WARM_MIN_BYTES = (size_t)256 << 20;   // MI355X MALL capacity
 
 // VV: every value slice is whole (d_v a multiple of BV) and v is 16-byte
 // aligned, so values and outputs move as 16-byte row pieces.
 template <int C, int D, int BV, bool VV>
 __global__ void __launch_bounds__((K2G<C, D, BV>::NT))
 eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16 *__restrict__ o,
-               const char *__restrict__ ws, int Tlen, int H, int BH, int dk, int dv, int NC, int R) {
+               const char *__restrict__ ws, int Tlen, int H, int BH, int dk, int dv, int NC, int R,
+               int warm) {
     using G = K2G<C, D, BV>;
     using F = Fac<C, D>;
     using T = bf16;
@@ -968,6 +979,16 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 if (!ok) x = make_uint4(0u, 0u, 0u, 0u);
                 s.R[0] = __builtin_bit_cast(bf16x8, x);
                 s.sc = *(const uint2 *)(blk + F::oDec + 8 * (mu < G::SCU ? mu : G::SCU - 1));
+                s.pf[0] = s.pf[1] = 0u;
+                if (warm) {
+                    const int cw = c + WARM_AHEAD < NC ? c + WARM_AHEAD : NC - 1;
+                    const char *wb = wsh + (long)cw * F::bytes;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int off = (slice + R * (64 * i + lane)) * 128;   // beyond the block: its last word
+                        s.pf[i] = *(const uint32_t *)(wb + (off < F::bytes - 4 ? off : F::bytes - 4));
+                    }
+                }
             }
         };
         // movers: value slice and scales of chunk c -> LDS
@@ -1069,6 +1090,7 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
             }
             if constexpr (RM) {
                 if (c + 1 < NC) put_v(nxt, c + 1);
+                asm volatile("" ::"v"(cur.pf[0]), "v"(cur.pf[1]));   // the warm-up words, consumed
                 load(far, cf);
             }
             __syncthreads();   // U^T and the outputs complete; S^T no longer read
@@ -1197,8 +1219,9 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     const int R = (dv + BV - 1) / BV;
     const int grid2 = 8 * ((BH + 7) / 8) * R;
+    const int warm = ws_bytes<C, D>(B, Tlen, H) > WARM_MIN_BYTES;
     hipLaunchKernelGGL(k2, dim3((unsigned)grid2), dim3(G2::NT), G2::LDS, stream, (const bf16 *)v, S0,
-                       S_final, (bf16 *)o, (const char *)ws, Tlen, H, BH, dk, dv, NC, R);
+                       S_final, (bf16 *)o, (const char *)ws, Tlen, H, BH, dk, dv, NC, R, warm);
     err = hipGetLastError();
     if (err == hipSuccess && ev) err = hipEventRecord(ev[2], stream);
     return err;

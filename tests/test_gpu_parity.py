@@ -216,6 +216,26 @@ def sampled_check(name, n_heads, seed=0):
     return check(go, gs, ro, rs, "bf16", f"{name} heads={heads}")
 
 
+@pytest.mark.slow
+def test_large_workspace_ragged_slices():
+    """A workspace beyond 256 MB (the state pass then warms L2 ahead of its
+    factor fetches) with a ragged tail, d_v = 100 (seven 16-column slices per
+    head, the last one partial) and an initial state; sampled heads against
+    the oracle."""
+    B, T, H, dk, dv = 1, 32768 + 17, 7, 128, 100
+    need = eda.workspace_size(B, T, H, dk, dv, torch.bfloat16)
+    assert need > 256 << 20
+    say(f"large workspace B={B} T={T} H={H} dk={dk} dv={dv} ({need >> 20} MB)")
+    x = make_inputs(B, T, H, dk, dv, "bf16", seed=51, s0_std=0.02)
+    o, S = run_chunked(dev(x))
+    heads = [(0, 0), (0, H - 1)]
+    refs = oracle_heads(x, heads)
+    go = np.concatenate([to64(o[b, :, h]) for b, h in heads])
+    gs = np.concatenate([to64(S[b, h]) for b, h in heads])
+    check(go, gs, np.concatenate([r[0] for r in refs]), np.concatenate([r[1] for r in refs]), "bf16",
+          f"large workspace heads={heads}")
+
+
 def test_train_workload_sampled():
     sampled_check("train", 8)
 
