@@ -21,7 +21,8 @@ section: the rank-1 DPLR update of GDN-2/QED (`eda_fwd_chunked_dplr`) on the
 same training shape with QED erase vectors; and a backward section: `eda_bwd`
 (gradients of every input) on the training shape; and a long_context section:
 the chunked forward at T = 32768 with 32 heads (the long-context
-configuration) and with 16 heads (the metric's H = 16), tokens/s each.
+configuration), with 16 heads (the metric's H = 16), and at T = 131072 with 16
+heads (the very-long configuration), tokens/s each.
 
 Algorithmic work (d_k = d_v = d, C tokens per chunk, L = 2C sub-steps; each
 token is an erase sub-step and a delta sub-step), per chunk and head:
@@ -220,12 +221,13 @@ def bench_dplr(torch, eda, dev, chunk: int, steps: int) -> dict:
 
 
 def bench_long(torch, eda, dev, chunk: int) -> dict:
-    """The chunked forward at the 32K-token workloads (sequential chunk chain
-    of 1024 chunks per head)."""
+    """The chunked forward at the long-context workloads: T = 32768 with 32
+    and 16 heads, and T = 131072 with 16 heads (sequential chains of 1024 and
+    4096 chunks per head)."""
     from eda_inputs import WORKLOADS, make_workload
 
     out = {}
-    for name in ("long", "long_h16"):
+    for name in ("long", "long_h16", "verylong"):
         w = WORKLOADS[name]
         x = make_workload(w, device=dev)
         o = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
@@ -240,7 +242,8 @@ def bench_long(torch, eda, dev, chunk: int) -> dict:
         run()
         torch.cuda.synchronize()
         ms = time_events(torch, run, 5)
-        out[name] = dict(workload=f"{name}: B={w.B} T={w.T} H={w.H} d_k=d_v={w.dk} {w.dtype}, S0 ~ N(0, {w.s0_std})",
+        s0 = f"S0 ~ N(0, {w.s0_std})" if w.s0_std > 0 else "S0 = 0"
+        out[name] = dict(workload=f"{name}: B={w.B} T={w.T} H={w.H} d_k=d_v={w.dk} {w.dtype}, {s0}",
                          value=round(w.B * w.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 4),
                          token_heads_per_s=round(w.B * w.T * w.H / (ms * 1e-3), 1))
         print(f"[bench] {name} {ms:.3f} ms", file=sys.stderr, flush=True)
