@@ -236,6 +236,30 @@ def test_large_workspace_ragged_slices():
           f"large workspace heads={heads}")
 
 
+@pytest.mark.slow
+def test_maximum_size_heads_match_single_head_runs():
+    """The largest input the ABI accepts in one call: B*T*H*d just below 2^31
+    elements per token tensor (T = 131072, 127 heads) and a 24.8 GB
+    workspace, so every 32-bit product of token, head and channel indices
+    would overflow.  Heads are independent and each output column is computed
+    by the same instructions whatever the value-slice width, so the first and
+    last heads must equal, bit for bit, runs on those heads alone (which the
+    oracle checks at this length in the very-long workload test)."""
+    B, T, H, d = 1, 131072, 127, 128
+    assert B * T * H * d < 2 ** 31 <= B * T * (H + 1) * d
+    say(f"maximum size B={B} T={T} H={H} d={d}")
+    x = make_inputs(B, T, H, d, d, "bf16", seed=61, s0_std=0.02, device=DEV)
+    o, S = run_chunked(x)
+    for h in (0, H - 1):
+        say(f"maximum size: head {h} alone")
+        xh = {n: (None if t is None else t[:, :, h:h + 1].contiguous() if t.dim() >= 3 and n != "S0"
+                  else t[:, h:h + 1].contiguous()) for n, t in x.items()}
+        oh, Sh = run_chunked(xh)
+        assert torch.equal(oh[:, :, 0], o[:, :, h]) and torch.equal(Sh[:, 0], S[:, h]), f"head {h}"
+    del x, o, S
+    torch.cuda.empty_cache()
+
+
 def test_train_workload_sampled():
     sampled_check("train", 8)
 
