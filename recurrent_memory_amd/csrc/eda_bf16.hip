@@ -375,6 +375,13 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         const bool okt = tid < nval;
         pbeta = okt ? (DPLR ? 1.f : beta[tok0 + (long)tid * H]) : 0.f;
         pgamma = okt && !DPLR ? gamma[tok0 + (long)tid * H] : 0.f;
+        // Drain these loads here (vmcnt(0)): they fill the registers the fast
+        // path prefetches, and the waits where both paths meet would otherwise
+        // be counted for this path's short tail of loads, which on the fast path
+        // also waits for the previous item's workspace stores.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // ---- diagonal 16x16 blocks of (I + A)^{-1}: fp32 forward substitution over
@@ -405,7 +412,21 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     };
 
     int it = blockIdx.x;
-    if constexpr (VEC) prefetch(it);
+    if constexpr (VEC) {
+        prefetch(it);
+        // The first item's inputs are consumed (unused) right here, so the
+        // compiler waits for them once, before the item loop.  The waits at the
+        // top of the loop are then counted for the loop path alone, where the
+        // previous item's workspace stores follow the prefetch, and leave those
+        // stores in flight instead of waiting for them as well.
+#pragma unroll
+        for (int i = 0; i < TPT; ++i)
+            asm volatile("" ::"v"(xq[i].x), "v"(xq[i].y), "v"(xe[i].x), "v"(xe[i].y), "v"(xk[i].x),
+                         "v"(xk[i].y), "v"(xa[i][0]), "v"(xa[i][1]), "v"(xa[i][2]), "v"(xa[i][3]));
+        asm volatile("" ::"v"(pbeta), "v"(pgamma));
+        if constexpr (LAYER) asm volatile("" ::"v"(xA[0]), "v"(xA[1]), "v"(xA[2]), "v"(xA[3]), "v"(xB[0]),
+                                          "v"(xB[1]), "v"(xB[2]), "v"(xB[3]));
+    }
     for (; it < items; it += gridDim.x) {
         const int bh = head_of(it), cidx = chunk_of(it);
         if (!is_fast(cidx)) fetch_slow(it);
