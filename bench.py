@@ -41,7 +41,10 @@ Peaks: MI355X dense bf16 matrix 2.5 PFLOP/s, fp32 matrix 157.3 TFLOP/s,
 HBM3E 8 TB/s.  `traffic` is the measured HBM bytes per launch of the dominant
 kernel (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known
 size), read from the committed summary under profiles/ and reported only while
-the kernel source it was measured on is unchanged.
+the kernel source it was measured on is unchanged; each chunked kernel's
+`rocprof_mfma` is, on the same terms, its measured matrix-core busy fraction
+and issued bf16 flop per launch (SQ_VALU_MFMA_BUSY_CYCLES,
+SQ_INSTS_VALU_MFMA_MOPS_BF16 over GRBM_GUI_ACTIVE).
 """
 from __future__ import annotations
 
@@ -102,6 +105,30 @@ def measured_traffic(kernel: str, workload: str):
         return None
     try:
         return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def measured_mfma(kernel: str, workload: str):
+    """Matrix-core busy fraction and issued bf16 flop per launch of `kernel`
+    from the committed rocprofv3 counter summary (SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE), or None when there is none
+    or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"mfma_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    src = os.path.join(ROOT, "recurrent_memory_amd", "csrc", kv.get("source", ""))
+    if not os.path.exists(src) or hashlib.sha1(open(src, "rb").read()).hexdigest() != kv.get("source_sha1"):
+        return None
+    try:
+        return dict(busy_fraction=float(kv["mfma_busy_fraction"]), issued_bf16_flop=float(kv["issued_bf16_flop"]),
+                    issued_over_canonical=float(kv["issued_over_canonical"]))
     except (KeyError, ValueError):
         return None
 
@@ -400,14 +427,15 @@ def main() -> int:
             ach = wk["bytes"] / sec / 1e9
             r = dict(kernel=names[kind], bound="hbm", achieved=round(ach, 2), peak=PEAK_HBM_GBS,
                      unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 5))
-        r.update(ms=round(wk["ms"], 5), algorithmic_bytes=wk["bytes"], algorithmic_flop=wk["flop"])
+        r.update(ms=round(wk["ms"], 5), algorithmic_bytes=wk["bytes"], algorithmic_flop=wk["flop"],
+                 rocprof_mfma=measured_mfma(names[kind], w.name))
         return r
 
     kernels = {k: roof(k) for k in work}
     dom = max(work, key=lambda k: work[k]["ms"])
     roof_line = dict(kernels[dom])
     roof_line["traffic"] = measured_traffic(names[dom], w.name)
-    for k in ("ms", "algorithmic_bytes", "algorithmic_flop"):
+    for k in ("ms", "algorithmic_bytes", "algorithmic_flop", "rocprof_mfma"):
         roof_line.pop(k)
 
     flop = work["factors"]["flop"] + work["state"]["flop"]

@@ -1,4 +1,4 @@
-"""HBM traffic of the chunked forward's kernels, from rocprofv3 counters.
+"""HBM traffic and matrix-core use of the EDA kernels, from rocprofv3 counters.
 
 Two steps (the first is the program rocprofv3 profiles, once per counter):
 
@@ -8,6 +8,13 @@ Two steps (the first is the program rocprofv3 profiles, once per counter):
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o t -- \\
         python3 REPO/recurrent_memory_amd/traffic.py run --workload train
     python3 REPO/recurrent_memory_amd/traffic.py summarize FETCH_DIR WRITE_DIR --workload train
+
+Matrix-core use (one pass, four counters):
+
+    rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES \\
+        GRBM_GUI_ACTIVE --output-format csv -d MFMA_DIR -o t -- \\
+        python3 REPO/recurrent_memory_amd/traffic.py run --workload train
+    python3 REPO/recurrent_memory_amd/traffic.py summarize-mfma MFMA_DIR --workload train
 
 `run` builds the workload's inputs, then launches a calibration kernel that
 reads and writes a known number of bytes (an fp32 scale of 256 MiB, three
@@ -129,6 +136,76 @@ def summarize(fetch_dir: str, write_dir: str, workload: str, algorithmic: dict) 
         print(f"[traffic] {path}: {total / 1e6:.1f} MB per launch")
 
 
+N_XCC, N_SIMD = 8, 1024   # MI355X: 8 XCDs, 256 compute units x 4 SIMDs
+
+
+def summarize_mfma(directory: str, workload: str, canonical: dict) -> None:
+    """Per launch of each chunked kernel: the bf16 matrix operations issued
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts add and multiply operations / 512),
+    the matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES summed over the
+    SIMDs, over the kernel's GRBM_GUI_ACTIVE cycles -- summed over the XCDs in
+    the CSV -- times the SIMD count), and the issued rate against the dense
+    bf16 peak over the same cycles."""
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    vals = defaultdict(lambda: defaultdict(list))
+    per = defaultdict(dict)
+    names = {}
+    for row in csv.DictReader(open(files[0])):
+        d = int(row["Dispatch_Id"])
+        per[d][row["Counter_Name"]] = per[d].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+        names[d] = row["Kernel_Name"]
+    for d, c in per.items():
+        for kern in ("eda_bf16_factors", "eda_bf16_state"):
+            if kern in names[d]:
+                for k, v in c.items():
+                    vals[kern][k].append(v)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for kern, c in vals.items():
+        avg = {k: sum(v) / len(v) for k, v in c.items()}
+        cycles = avg["GRBM_GUI_ACTIVE"] / N_XCC
+        issued = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMD)
+        # dense bf16 peak: 1024 flop per SIMD per cycle (2.5 PFLOP/s at 2.4 GHz over 1024 SIMDs;
+        # a 16x16x32 bf16 instruction is 16384 flop in 16 busy cycles)
+        rate = issued / (cycles * N_SIMD * 1024.0)
+        sha = hashlib.sha1(open(os.path.join(HERE, "csrc", KERNELS[kern]), "rb").read()).hexdigest()
+        path = os.path.join(ROOT, "profiles", f"mfma_{kern}_{workload}.txt")
+        with open(path, "w") as f:
+            f.write(f"# Matrix-core use per launch of {kern} on the {workload} workload, from rocprofv3\n"
+                    "# counters (averages over the launches).  Commands (repo at REPO):\n"
+                    "#   cd /tmp && export TMPDIR=/tmp\n"
+                    "#   rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES "
+                    f"GRBM_GUI_ACTIVE --output-format csv -d M -o t -- python3 REPO/recurrent_memory_amd/traffic.py "
+                    f"run --workload {workload}\n"
+                    f"#   python3 REPO/recurrent_memory_amd/traffic.py summarize-mfma M --workload {workload}\n")
+            f.write(f"kernel = {kern}\nworkload = {workload}\nsource = {KERNELS[kern]}\nsource_sha1 = {sha}\n")
+            f.write(f"launches = {len(c['GRBM_GUI_ACTIVE'])}\n")
+            for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
+                      "GRBM_GUI_ACTIVE"):
+                f.write(f"{k} = {avg[k]:.0f}\n")
+            f.write(f"gpu_active_cycles_per_xcd = {cycles:.0f}\n")
+            f.write(f"issued_bf16_flop = {issued:.0f}\n")
+            if kern in canonical:
+                f.write(f"canonical_flop = {canonical[kern]:.0f}\n"
+                        f"issued_over_canonical = {issued / canonical[kern]:.3f}\n")
+            f.write(f"mfma_busy_fraction = {busy:.4f}\n")
+            f.write(f"issued_rate_over_bf16_peak = {rate:.4f}\n")
+        print(f"[mfma] {path}: busy {100 * busy:.1f} %, issued {issued / 1e9:.2f} GFLOP")
+
+
+def canonical_flop(workload: str, chunk: int = 32) -> dict:
+    """The chunk formulation's multiply-adds x 2 per launch (counted once)."""
+    sys.path.insert(0, ROOT)
+    from eda_inputs import WORKLOADS
+    w = WORKLOADS[workload]
+    C, L, d = chunk, 2 * chunk, w.dk
+    n = w.B * w.H * ((w.T + C - 1) // C)
+    return {"eda_bf16_factors": 2.0 * n * (L * L * d + L ** 3 / 6.0 + L * L * d + C * L * d),
+            "eda_bf16_state": 2.0 * n * (L * d * d + L * C * d + C * d * d + C * L * d + L * d * d)}
+
+
 def algorithmic_bytes(workload: str) -> dict:
     sys.path.insert(0, ROOT)
     from eda_inputs import WORKLOADS
@@ -152,9 +229,14 @@ def main() -> int:
     sm.add_argument("fetch_dir")
     sm.add_argument("write_dir")
     sm.add_argument("--workload", default="train")
+    mf = sub.add_parser("summarize-mfma")
+    mf.add_argument("mfma_dir")
+    mf.add_argument("--workload", default="train")
     a = ap.parse_args()
     if a.cmd == "run":
         run(a.workload)
+    elif a.cmd == "summarize-mfma":
+        summarize_mfma(a.mfma_dir, a.workload, canonical_flop(a.workload))
     else:
         summarize(a.fetch_dir, a.write_dir, a.workload, algorithmic_bytes(a.workload))
     return 0
