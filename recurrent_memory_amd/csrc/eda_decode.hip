@@ -37,6 +37,8 @@
 // S_new = Sh + k (v - Sh^T a)^T, o = S_new^T q = Sh^T q + (q.k)(v - Sh^T a),
 // with the erase vector a passed as `e` and no beta or gamma: the same pass
 // with gamma = 0, beta = 1 and Sh^T a in place of the corrected read.
+#include <type_traits>
+
 #include "eda_common.h"
 
 namespace eda {
@@ -56,52 +58,79 @@ __device__ __forceinline__ float dec_inv_norm(float ss) {
     return ss > DEC_EPS * DEC_EPS ? __builtin_amdgcn_rsqf(ss) : 1.f / DEC_EPS;
 }
 
-constexpr int DEC_NT = 512;           // threads per workgroup
-constexpr int DEC_RG = DEC_NT / 32;   // row groups (32 column quads per row)
-constexpr int DEC_R = 128 / DEC_RG;   // rows per thread
-constexpr int DEC_NW = DEC_NT / 64;   // wavefronts
-
 constexpr int DEC_PLAIN = 0, DEC_LAYER = 1, DEC_DPLR = 2;
 
-// The 128-square plain and DPLR variants fit in 128 VGPRs, which lets two
-// workgroups share a CU so that one streams while the other reduces (about 2%
-// faster than one per CU); the others would spill at that limit.
+// Workgroup shape.  The 128-square plain and DPLR variants run 1024 threads
+// (4 rows per thread, one workgroup per CU): the state strip of the state in
+// hand and of the next one both fit in 128 VGPRs.  The layer and ragged
+// variants keep 512 threads (8 rows per thread), which they need to stay
+// within the registers of one 512-thread workgroup.
+template <bool FULL, int MODE>
+struct DecShape {
+    static constexpr int NT = FULL && MODE != DEC_LAYER ? 1024 : 512;   // threads per workgroup
+    static constexpr int RG = NT / 32;                                   // row groups (32 column quads per row)
+    static constexpr int R = 128 / RG;                                   // rows per thread
+    static constexpr int NW = NT / 64;                                   // wavefronts
+};
+
+// Software pipelining: every input of state n + 1 (its token vectors, gates,
+// value and state strip) is fetched at the start of state n, before its
+// reductions and its stores.  Vector
+// loads and stores share one in-order counter, so a wait for a load issued
+// after those stores would also wait for them; issued before, the loads are
+// waited for at the top of the next state while the stores stay in flight.
+// States never overlap in memory, so fetching state n + 1 before writing state
+// n is exact also when S_out == S_in.
 template <typename Tin, bool FULL, int MODE>
-__global__ void __launch_bounds__(DEC_NT) __attribute__((amdgpu_waves_per_eu(FULL && MODE != 1 ? 4 : 1)))
+__global__ void __launch_bounds__((DecShape<FULL, MODE>::NT))
+    __attribute__((amdgpu_waves_per_eu(DecShape<FULL, MODE>::NT == 1024 ? 4 : 1)))
 eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ e,
                   const Tin *__restrict__ v, const void *__restrict__ decay,
                   const float *__restrict__ A_log, const float *__restrict__ dt_bias,
                   const float *__restrict__ beta, const float *__restrict__ gamma,
                   const float *S_in, float *S_out, Tin *__restrict__ o, long NH, int H, int Hk,
                   int dk, int dv) {
-    constexpr int R = DEC_R, RG = DEC_RG;
+    using SH = DecShape<FULL, MODE>;
+    constexpr int R = SH::R, RG = SH::RG, NW = SH::NW;
     constexpr bool LAYER = MODE == DEC_LAYER, DPLR = MODE == DEC_DPLR;
     __shared__ float sq[128], sk[128], se[128], sa[128];
-    __shared__ float red[DEC_NW][3][128];
+    __shared__ float red[NW][3][128];
+    __shared__ float fin[3][128];   // the three reductions, summed over the waves
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cq = tid & 31, rg = tid >> 5;  // column quad, row group
     if (FULL) { dk = 128; dv = 128; }
-
     const int grp = H / Hk;
-    for (long nh = blockIdx.x; nh < NH; nh += gridDim.x) {
-        // key row of this (sequence, value head)
+
+    // inputs of one state, in registers from the fetch to their use; the token
+    // values stay raw (loaded from clamped, always valid addresses) and are
+    // converted and masked where they are used, so nothing waits for them
+    // before the previous state's stores are issued
+    using DT = typename std::conditional<LAYER, Tin, float>::type;   // decay input
+    Tin rq = Tin(0), rk = Tin(0), rce = Tin(0), rv[4] = {Tin(0), Tin(0), Tin(0), Tin(0)};
+    DT ra = DT(0);
+    float rA = 0.f, rB = 0.f, xb = 0.f, xg = 0.f;
+    float s[R][4], sn[R][4];   // the strip of the state in hand and of the next one
+    auto fetch = [&](long nh, float (&st)[R][4]) __attribute__((always_inline)) {
         const long hk = (nh % H) / grp, nk = (nh / H) * Hk + hk;
         if (tid < 128) {
-            const bool ok = tid < dk;
-            sq[tid] = ok ? to_f32(q[nk * dk + tid]) : 0.f;
-            sk[tid] = ok ? to_f32(k[nk * dk + tid]) : 0.f;
-            se[tid] = ok ? to_f32(e[nk * dk + tid]) : 0.f;
-            if constexpr (LAYER)
-                sa[tid] = ok ? dec_safe_gate(to_f32(((const Tin *)decay)[nk * dk + tid]), A_log[hk * dk + tid],
-                                             dt_bias[hk * dk + tid])
-                             : 0.f;
-            else
-                sa[tid] = ok ? ((const float *)decay)[nk * dk + tid] : 0.f;
+            const long ch = nk * dk + (tid < dk ? tid : 0);
+            rq = q[ch];
+            rk = k[ch];
+            rce = e[ch];
+            ra = ((const DT *)decay)[ch];
+            if constexpr (LAYER) {
+                rA = A_log[hk * dk + (tid < dk ? tid : 0)];
+                rB = dt_bias[hk * dk + (tid < dk ? tid : 0)];
+            }
         }
-
-        // Read the whole state strip first (independent of the vectors above).
-        float s[R][4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = 4 * cq + c;
+            rv[c] = v[nh * dv + (j < dv ? j : 0)];
+        }
+        xb = DPLR ? 1.f : beta[nh];
+        xg = DPLR ? 0.f : gamma[nh];
         const long sbase = nh * (long)dk * dv;
         if (S_in) {
             if (FULL) {
@@ -109,7 +138,7 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
                 for (int m = 0; m < R; ++m) {
                     const f32x4 x = __builtin_nontemporal_load(
                         reinterpret_cast<const f32x4 *>(S_in + sbase + (rg + RG * m) * 128 + 4 * cq));
-                    s[m][0] = x[0]; s[m][1] = x[1]; s[m][2] = x[2]; s[m][3] = x[3];
+                    st[m][0] = x[0]; st[m][1] = x[1]; st[m][2] = x[2]; st[m][3] = x[3];
                 }
             } else {
 #pragma unroll
@@ -117,15 +146,47 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const int i = rg + RG * m, j = 4 * cq + c;
-                        s[m][c] = (i < dk && j < dv) ? S_in[sbase + (long)i * dv + j] : 0.f;
+                        st[m][c] = (i < dk && j < dv) ? S_in[sbase + (long)i * dv + j] : 0.f;
                     }
             }
         } else {
 #pragma unroll
             for (int m = 0; m < R; ++m)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) s[m][c] = 0.f;
+                for (int c = 0; c < 4; ++c) st[m][c] = 0.f;
         }
+    };
+
+    long nh = blockIdx.x;
+    if (nh < NH) {
+        fetch(nh, s);
+        // The first state's inputs are consumed (unused) here, so the compiler
+        // waits for them once, before the loop; the waits at the top of the loop
+        // are then counted for the loop path alone, where the previous state's
+        // stores follow the fetch and stay in flight.
+        asm volatile("" ::"v"((uint32_t)rq), "v"((uint32_t)rk), "v"((uint32_t)rce), "v"(ra), "v"(rA), "v"(rB),
+                     "v"(xb), "v"(xg));
+        asm volatile("" ::"v"((uint32_t)rv[0]), "v"((uint32_t)rv[1]), "v"((uint32_t)rv[2]), "v"((uint32_t)rv[3]));
+#pragma unroll
+        for (int m = 0; m < R; ++m) asm volatile("" ::"v"(s[m][0]), "v"(s[m][1]), "v"(s[m][2]), "v"(s[m][3]));
+    }
+    for (; nh < NH; nh += gridDim.x) {
+        if (tid < 128) {
+            const bool ok = tid < dk;
+            sq[tid] = ok ? to_f32(rq) : 0.f;
+            sk[tid] = ok ? to_f32(rk) : 0.f;
+            se[tid] = ok ? to_f32(rce) : 0.f;
+            if constexpr (LAYER) sa[tid] = ok ? dec_safe_gate(to_f32(ra), rA, rB) : 0.f;
+            else sa[tid] = ok ? ra : 0.f;
+        }
+        const float b = xb, g = xg;
+        float vv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vv[c] = (4 * cq + c < dv) ? to_f32(rv[c]) : 0.f;
+        // the next state's inputs, fetched now: they arrive while this state is
+        // reduced and updated, and they precede this state's stores
+        const long cur = nh, nxt = nh + gridDim.x;
+        if (nxt < NH) fetch(nxt, sn);
         __syncthreads();
 
         // Address overlaps (k.e, q.e, q.k); every wave reduces them itself.
@@ -173,56 +234,68 @@ eda_decode_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k, const Ti
             }
         }
         __syncthreads();
+        // each of 384 threads adds one (reduction, column) over the waves, in wave order
+        if (tid < 384) {
+            const int ty = tid >> 7, j = tid & 127;
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) acc += red[w][ty][j];
+            fin[ty][j] = acc;
+        }
+        __syncthreads();
 
-        const float b = DPLR ? 1.f : beta[nh], g = DPLR ? 0.f : gamma[nh];
         float re[4], u[4], ov[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int j = 4 * cq + c;
-            float r0 = 0.f, r1 = 0.f, r2 = 0.f;
-#pragma unroll
-            for (int w = 0; w < DEC_NW; ++w) {
-                r0 += red[w][0][j];
-                r1 += red[w][1][j];
-                r2 += red[w][2][j];
-            }
+            float r0 = fin[0][j], r1 = fin[1][j], r2 = fin[2][j];
             r0 *= ine;
             r1 *= ink;
             r2 *= inq;
             re[c] = r0;
-            const float vj = (j < dv) ? to_f32(v[nh * dv + j]) : 0.f;
             const float rk = DPLR ? r0 : r1 - g * ke * r0;   // DPLR: the read along a
-            u[c] = b * (vj - rk);
+            u[c] = b * (vv[c] - rk);
             ov[c] = r2 - g * qe * r0 + qk * u[c];
         }
-        if (rg == 0) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int j = 4 * cq + c;
-                if (j < dv) o[nh * dv + j] = from_f32<Tin>(ov[c]);
-            }
-        }
 
-        // S_new = Sh - gamma e r_e^T + k u^T, written once.
+        // S_new = Sh - gamma e r_e^T + k u^T
+        float w[R][4];
 #pragma unroll
         for (int m = 0; m < R; ++m) {
             const int i = rg + RG * m;
             const float a = sa[i], ge = g * se[i] * ine, kk = sk[i] * ink;
-            float w[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) w[c] = a * s[m][c] - ge * re[c] + kk * u[c];
+            for (int c = 0; c < 4; ++c) w[m][c] = a * s[m][c] - ge * re[c] + kk * u[c];
+        }
+        // the shared vectors and partial sums are refilled by the next state
+        __syncthreads();
+
+        const long sbase = cur * (long)dk * dv;
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+            const int i = rg + RG * m;
             if (FULL) {
-                __builtin_nontemporal_store(f32x4{w[0], w[1], w[2], w[3]},
+                __builtin_nontemporal_store(f32x4{w[m][0], w[m][1], w[m][2], w[m][3]},
                                             reinterpret_cast<f32x4 *>(S_out + sbase + i * 128 + 4 * cq));
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int j = 4 * cq + c;
-                    if (i < dk && j < dv) S_out[sbase + (long)i * dv + j] = w[c];
+                    if (i < dk && j < dv) S_out[sbase + (long)i * dv + j] = w[m][c];
                 }
             }
         }
-        __syncthreads();   // the shared vectors and partial sums are refilled next
+        if (rg == 0) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int j = 4 * cq + c;
+                if (j < dv) o[cur * dv + j] = from_f32<Tin>(ov[c]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < R; ++m)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s[m][c] = sn[m][c];
     }
 }
 
@@ -240,9 +313,13 @@ hipError_t launch_decode(const void *q, const void *k, const void *e, const void
     err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     const long NH = (long)N * H;
-    const dim3 grid((unsigned)(NH < 4L * ncu ? NH : 4L * ncu)), block(DEC_NT);   // four per compute unit
     const bool full = dk == 128 && dv == 128;
     const int mode = A_log ? DEC_LAYER : (beta ? DEC_PLAIN : DEC_DPLR);
+    // a persistent grid: one 1024-thread workgroup per compute unit, or four
+    // 512-thread workgroups launched per compute unit (one or two resident)
+    const bool wide = full && mode != DEC_LAYER;
+    const long per = wide ? (long)ncu : 4L * ncu;
+    const dim3 grid((unsigned)(NH < per ? NH : per)), block(wide ? 1024 : 512);
     auto kern = full ? (mode == DEC_LAYER  ? eda_decode_kernel<Tin, true, DEC_LAYER>
                         : mode == DEC_DPLR ? eda_decode_kernel<Tin, true, DEC_DPLR>
                                            : eda_decode_kernel<Tin, true, DEC_PLAIN>)
