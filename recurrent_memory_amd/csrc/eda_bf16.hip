@@ -207,7 +207,7 @@ struct K1G {
     static_assert(C * D * 4 <= szKl, "Kl region reuse");
     static constexpr int szLL = align16(L * LDL * 2), szAd = NB * 16 * ADS * 4;
     static constexpr int szMT = NB * 16 * MTW * 2, szPs = align16(C * LDL * 2);
-    static constexpr int szMisc = (L + 2 * C + D) * 4 + NW * C * 16;   // + per-wave norm partials
+    static constexpr int szMisc = (L + 2 * C + D) * 4 + NW * C * 16 + NW * 4;   // + norm partials, votes
     static constexpr int LDTV = C + 8;                 // T' and P T' staging rows (after the inverse)
     static_assert(L * LDTV * 2 <= szLL && C * LDTV * 2 <= szAd, "staging reuse");
     static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oAbf = oQl + szQl;
@@ -266,6 +266,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     float *sb = bp + L, *sg = sb + C;        // beta, gamma per token    [C]
     float *ers = sg + C;                     // e^r per channel (1 if wide) [D]
     float *nrm = ers + D;                    // LAYER: per-wave |q|^2, |k|^2, |e|^2 partials [NW][C][4]
+    uint32_t *vote = (uint32_t *)(nrm + NW * C * 4);   // LAYER: per-wave wide-chunk votes [NW]
     T *Tvs = (T *)(smem + G::oAbf);          // T', after the inverse    [L][LDTV]
     T *Phs = (T *)(smem + G::oAd);           // P T', after the inverse  [C][LDTV]
     constexpr int LDTV = G::LDTV;
@@ -498,22 +499,34 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 }
             }
         }
-        const bool wide = __syncthreads_or(wide_here) != 0;
-        // LAYER: 1 / max(|x|, eps) of the thread's tokens, for q, k, e
-        float inq[TPT], ink[TPT], ine[TPT];
+        // Wide-chunk vote.  Layer mode: one slot per wave and one barrier (a wave
+        // rewrites its slot only at the next item's vote, after barriers of this
+        // item that every wave passes once its reads below are done), which
+        // spares the mode's registers.  The plain and DPLR modes keep the
+        // block-wide OR, measured faster there.
+        bool wide = false;
         if constexpr (LAYER) {
-            constexpr int NWA = (G::ACT + 63) / 64;
+            const bool wv = __ballot(wide_here) != 0ull;
+            if (lane == 0) vote[wave] = wv ? 1u : 0u;
+            __syncthreads();
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) {
-                f32x4 tot = zero4();
+            for (int w = 0; w < NW; ++w) wide |= vote[w] != 0u;
+        } else {
+            wide = __syncthreads_or(wide_here) != 0;
+        }
+        // LAYER: 1 / max(|x|, eps) of the thread's token i, for q, k, e (formed
+        // where each token is used, so the scales are not held across the loop)
+        auto inv_norms = [&](int i) __attribute__((always_inline)) {
+            f32x4 tot = zero4();
+            if constexpr (LAYER) {
+                constexpr int NWA = (G::ACT + 63) / 64;
 #pragma unroll
                 for (int w = 0; w < NWA; ++w) tot += *(const f32x4 *)(nrm + (w * C + TPT * seg + i) * 4);
                 auto inv = [](float ss) { return ss > NORM_EPS * NORM_EPS ? __builtin_amdgcn_rsqf(ss) : 1.f / NORM_EPS; };
-                inq[i] = inv(tot[0]);
-                ink[i] = inv(tot[1]);
-                ine[i] = inv(tot[2]);
+                tot = f32x4{inv(tot[0]), inv(tot[1]), inv(tot[2]), 0.f};
             }
-        }
+            return tot;   // (1/|q|, 1/|k|, 1/|e|)
+        };
 
         // ---- scaled operands (LDS), Diag(e^r) Kr^T (workspace) and the
         //      per-channel scales -------------------------------------------------------
@@ -536,11 +549,12 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 float kv[4] = {lo_bf16(xk[i].x), hi_bf16(xk[i].x), lo_bf16(xk[i].y), hi_bf16(xk[i].y)};
                 float qv[4] = {lo_bf16(xq[i].x), hi_bf16(xq[i].x), lo_bf16(xq[i].y), hi_bf16(xq[i].y)};
                 if constexpr (LAYER) {
+                    const f32x4 nv = inv_norms(i);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        ev[j] *= ine[i];
-                        kv[j] *= ink[i];
-                        qv[j] *= inq[i];
+                        ev[j] *= nv[2];
+                        kv[j] *= nv[1];
+                        qv[j] *= nv[0];
                     }
                 }
                 const float gmt = sg[tau], btt = sb[tau];
@@ -602,9 +616,10 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                         return make_uint2(pack_bf16(lo_bf16(u.x) * s, hi_bf16(u.x) * s),
                                           pack_bf16(lo_bf16(u.y) * s, hi_bf16(u.y) * s));
                     };
-                    *(uint2 *)(Kr + (2 * tau) * LDA + c0) = nz(xe[i], LAYER ? ine[i] : 1.f);
-                    *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = nz(xk[i], LAYER ? ink[i] : 1.f);
-                    *(uint2 *)(Ql + tau * LDA + c0) = nz(xq[i], LAYER ? inq[i] : 1.f);
+                    const f32x4 nv = inv_norms(i);
+                    *(uint2 *)(Kr + (2 * tau) * LDA + c0) = nz(xe[i], nv[2]);
+                    *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = nz(xk[i], nv[1]);
+                    *(uint2 *)(Ql + tau * LDA + c0) = nz(xq[i], nv[0]);
                     *(f32x4 *)(Gs + tau * D + c0) = f32x4{g[i][0], g[i][1], g[i][2], g[i][3]};
                 }
             }
