@@ -216,6 +216,22 @@ def sampled_check(name, n_heads, seed=0):
     return check(go, gs, ro, rs, "bf16", f"{name} heads={heads}")
 
 
+def test_timed_entry_point_matches_plain_call():
+    """eda_fwd_chunked_timed (the benchmark's per-kernel timing) computes the
+    same outputs, bit for bit, as eda_fwd_chunked, and its events bracket the
+    two kernels in order."""
+    say("timed entry point")
+    x = dev(make_inputs(2, 300, 3, 128, 128, "bf16", seed=71, s0_std=0.02))
+    o0, S0 = run_chunked(x)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for ev in evs:
+        ev.record()
+    torch.cuda.synchronize()
+    o1, S1 = run_chunked(x, events=[ev.cuda_event for ev in evs])
+    assert torch.equal(o0, o1) and torch.equal(S0, S1)
+    assert evs[0].elapsed_time(evs[1]) > 0 and evs[1].elapsed_time(evs[2]) > 0
+
+
 @pytest.mark.slow
 def test_large_workspace_ragged_slices():
     """A workspace beyond 256 MB (the state pass then warms L2 ahead of its
