@@ -1072,6 +1072,10 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 store4<T>(St + (16 * cb + l16) * LDT + 16 * rb + g4, S[cb][0], S[cb][1], S[cb][2], S[cb][3]);
         };
 
+        // T'V (U role) and P^V (output role) of the next chunk, formed during the
+        // half of this chunk in which those roles wait, so that their chains on
+        // the next chunk start from it
+        f32x4 pre[NCB];
         auto body = [&](Set &cur, Set &nxt, Set &far, int c) __attribute__((always_inline)) {
             const int cf = c + 3 < NC ? c + 3 : NC - 1;   // chunk whose operands are fetched now
             __syncthreads();   // S^T, the value slice of chunk c and its decay are in LDS
@@ -1083,16 +1087,18 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 // the k = 32 product reads 16 zero rows of the value buffer).  All
                 // LDS operands are read before the first product, so the chain pays
                 // one LDS latency instead of one per step.
-                bf16x8 vf[NCB], sf[KSD][NCB];
+                bf16x8 sf[KSD][NCB];
+                if (c == 0) {
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) vf[cb] = frag_col(Vs + 16 * cb, LDV, lane);
+                    for (int cb = 0; cb < NCB; ++cb) pre[cb] = mma32(cur.R[KSD], frag_col(Vs + 16 * cb, LDV, lane), zero4());
+                }
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) sf[ks][cb] = frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(cur.R[KSD], vf[cb], zero4());
+                for (int cb = 0; cb < NCB; ++cb) acc[cb] = pre[cb];
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
@@ -1105,16 +1111,18 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
             if constexpr (RS) load(far, cf);
             if constexpr (RO) {
                 // o^T = S^T Q^^T + V^T P^^T for the wave's 16 tokens -> rows of o in LDS
-                bf16x8 vf[NCB], sf[KSD][NCB];
+                bf16x8 sf[KSD][NCB];
+                if (c == 0) {
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) vf[cb] = frag_col(Vs + 16 * cb, LDV, lane);
+                    for (int cb = 0; cb < NCB; ++cb) pre[cb] = mma32(frag_col(Vs + 16 * cb, LDV, lane), cur.R[KSD], zero4());
+                }
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) sf[ks][cb] = frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(vf[cb], cur.R[KSD], zero4());
+                for (int cb = 0; cb < NCB; ++cb) acc[cb] = pre[cb];
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
@@ -1130,7 +1138,19 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 load(far, cf);
             }
             __syncthreads();   // U^T and the outputs complete; S^T no longer read
-            if constexpr (RU || RO) load(far, cf);
+            if constexpr (RU || RO) {
+                load(far, cf);
+                // the next chunk's value slice is in LDS (written by the movers before
+                // the barrier above, into the other buffer)
+                if (c + 1 < NC) {
+                    const T *Vn = (const T *)(smem + G::oVs + ((c + 1) & 1) * G::szVs);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const bf16x8 vn = frag_col(Vn + 16 * cb, LDV, lane);
+                        pre[cb] = RU ? mma32(nxt.R[KSD], vn, zero4()) : mma32(vn, nxt.R[KSD], zero4());
+                    }
+                }
+            }
             if constexpr (RS) {
                 // S <- e^{G_C} S + Kr^T U; S^T of the next chunk
                 const f32x4 dc = decay(c);
