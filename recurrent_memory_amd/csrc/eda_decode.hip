@@ -16,15 +16,14 @@
 // This is an exact algebraic restatement of Eqs. (11) and (13) (substitute
 // St = Sh - gamma e r_e^T into St^T k and S_new^T q).  The paper's Sec. 3.5
 // notes the decode cost is dominated by reading and writing the state; the
-// kernel is therefore laid out for HBM streaming.  A persistent grid of
-// 512-thread workgroups (four per compute unit launched, one or two resident
-// at a time by register use) walks the states; per state
-// each thread owns a 4-column strip of 8 rows (rows rg + 16m), so every
-// wavefront load/store instruction touches 1 KB of contiguous memory and all
-// 8 loads of a thread are in flight together.  The state is touched exactly
-// once per step, so its loads and stores carry the non-temporal hint (no
-// reuse is expected from the caches; measured ~15% faster than plain
-// accesses at 8192 states of 64 KB).
+// kernel is therefore laid out for HBM streaming.  A persistent grid walks
+// the states; per state each thread owns a 4-column strip of R rows (rows
+// rg + RG m), so every wavefront load/store instruction touches 1 KB of
+// contiguous memory, and the loop is software-pipelined (below) so that the
+// next state's loads are in flight while this one is reduced and written.
+// The state is touched exactly once per step, so its loads and stores carry
+// the non-temporal hint (no reuse is expected from the caches; measured ~15%
+// faster than plain accesses at 8192 states of 64 KB).
 //
 // LAYER variant (the layer prologue fused in): q, k, e and the safe gate's
 // input a come per key head (Hk heads shared by groups of H / Hk value
@@ -61,10 +60,10 @@ __device__ __forceinline__ float dec_inv_norm(float ss) {
 constexpr int DEC_PLAIN = 0, DEC_LAYER = 1, DEC_DPLR = 2;
 
 // Workgroup shape.  The 128-square plain and DPLR variants run 1024 threads
-// (4 rows per thread, one workgroup per CU): the state strip of the state in
-// hand and of the next one both fit in 128 VGPRs.  The layer and ragged
-// variants keep 512 threads (8 rows per thread), which they need to stay
-// within the registers of one 512-thread workgroup.
+// (4 rows per thread, one workgroup per CU): the strips of the state in hand
+// and of the next one both fit in the 128 VGPRs a 1024-thread workgroup
+// allows.  The layer and ragged variants need more registers than that and
+// keep 512 threads (8 rows per thread).
 template <bool FULL, int MODE>
 struct DecShape {
     static constexpr int NT = FULL && MODE != DEC_LAYER ? 1024 : 512;   // threads per workgroup
