@@ -290,6 +290,28 @@ def test_verylong_workload_sampled():
     sampled_check("verylong", 2)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_uneven_grid(dtype):
+    """300 states of 128 x 128 on a grid of at most one workgroup per compute
+    unit: workgroups take one or two states, so the software-pipelined loop
+    runs both its prologue-only and its steady path; five steps in place,
+    element-wise against the oracle's five-token recurrence."""
+    N, H, d, steps = 100, 3, 128, 5
+    say(f"decode uneven grid {dtype} N={N} H={H} d={d} steps={steps}")
+    x = make_inputs(N, steps, H, d, d, dtype, seed=81, s0_std=0.02)
+    ro, rS = full_oracle(x)
+    xd = dev(x)
+    S = xd["S0"].clone()
+    outs = []
+    for t in range(steps):
+        o, S = eda.recurrent_step(*(xd[n][:, t].contiguous() for n in
+                                    ("q", "k", "e", "v", "alpha", "beta", "gamma")), S, inplace=True)
+        outs.append(o.clone())
+    torch.cuda.synchronize()
+    got = torch.stack(outs, 1)
+    check(to64(got), to64(S), ro, rS, dtype, f"decode uneven grid")
+
+
 def test_decode_workload_sampled():
     """256 sequences x 32 heads, 128 one-token steps updating the state in
     place; the oracle runs the sampled (n, h) heads over the same 128 steps."""
