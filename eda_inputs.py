@@ -115,6 +115,60 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16", *
                 gamma=gamma.contiguous(), S0=S0)
 
 
+# Address-overlap recipes: the erase address e and the write address k
+# interact through the cross term gamma beta (k^T e) k e^T of the one-step
+# operator (EDA paper Sec. 3.3, Eq. (16); slides frame "Order matters when the
+# two addresses overlap"), which independent random directions leave at
+# |cos(e, k)| ~ 0.07.  Each recipe below rebuilds e (or the gates) of a
+# make_inputs() draw so that term is large:
+#   e_eq_k     e = k (the paper's degenerate case: old content along k shrinks
+#              by (1 - beta)(1 - gamma))
+#   e_neg_k    e = -k
+#   e_prev_k   e_t = k_{t-1} (e_0 kept): erase what the previous token wrote
+#   cos09      e = 0.9 k + sqrt(1 - 0.81) n, n a unit vector orthogonal to k
+#   gates_one  beta = gamma = 1 (the worked example's limit)
+#   beta_zero  beta = 0 (no write)
+#   gamma_zero gamma = 0 (no erase: the KDA update)
+OVERLAP_KINDS = ("e_eq_k", "e_neg_k", "e_prev_k", "cos09", "gates_one", "beta_zero", "gamma_zero")
+
+
+def make_overlap_inputs(kind: str, B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16", *,
+                        seed: int = 0, s0_std: float = 0.5, device: str | torch.device = "cpu") -> dict:
+    """make_inputs() draw with one address-overlap recipe applied (see
+    OVERLAP_KINDS).  Rebuilt vectors are formed in fp32 from the stored
+    (rounded) k and re-normalised before the cast, so they are unit vectors
+    up to the storage rounding like every other address."""
+    if kind not in OVERLAP_KINDS:
+        raise ValueError(f"unknown overlap recipe {kind!r}")
+    x = make_inputs(B, T, H, dk, dv, dtype, seed=seed, s0_std=s0_std, device=device)
+    td = torch_dtype(dtype)
+    k = x["k"].float()
+    if kind == "e_eq_k":
+        x["e"] = x["k"].clone()
+    elif kind == "e_neg_k":
+        x["e"] = (-k).to(td)
+    elif kind == "e_prev_k":
+        e = x["e"].clone()
+        e[:, 1:] = x["k"][:, :-1]
+        x["e"] = e
+    elif kind == "cos09":
+        g = torch.Generator(device=device)
+        g.manual_seed(seed + 7_000_001)
+        n = torch.randn(k.shape, generator=g, device=device)
+        n = n - (n * k).sum(-1, keepdim=True) * k / (k * k).sum(-1, keepdim=True)
+        n = n / n.norm(dim=-1, keepdim=True)
+        e = 0.9 * k + math.sqrt(1.0 - 0.81) * n
+        x["e"] = (e / e.norm(dim=-1, keepdim=True)).to(td)
+    elif kind == "gates_one":
+        x["beta"] = torch.ones_like(x["beta"])
+        x["gamma"] = torch.ones_like(x["gamma"])
+    elif kind == "beta_zero":
+        x["beta"] = torch.zeros_like(x["beta"])
+    elif kind == "gamma_zero":
+        x["gamma"] = torch.zeros_like(x["gamma"])
+    return x
+
+
 def make_layer_inputs(B: int, T: int, H_k: int, H_v: int, dk: int, dv: int, dtype: str = "bf16", *,
                       seed: int = 0, gamma_mu: float = 0.0, s0_std: float = 0.0,
                       device: str | torch.device = "cpu") -> dict:

@@ -62,10 +62,14 @@ const char *eda_status_string(eda_status_t s);
 /*
  * Bytes of device workspace eda_fwd_chunked needs for these sizes (0 for an
  * unsupported combination).  `chunk` is the number of tokens per chunk (0
- * selects the default, 32).  The workspace holds every chunk's
- * state-independent factors between the two kernels of the chunked forward:
- * for bf16 inputs with d_k = d_v = 128 and 32-token chunks that is 47616
- * bytes per chunk and head (about 1.8 KB per token and head).
+ * selects the default, 64).  The workspace holds every chunk's
+ * state-independent factors between the two kernels of the chunked forward.
+ * For bf16 inputs those are the chunk's affine state map (S -> Lambda S +
+ * Phi S + Psi V, O = Qhat S + Phat V): with d_k = d_v = 128 that is 74240
+ * bytes per 64-token chunk and head (1.16 KB per token and head), 51712 per
+ * 32-token chunk and 46592 per 16-token chunk.  fp32 inputs compute chunk 64
+ * as 32-token chunks (a 64-token chunk's fp32 operands exceed one compute
+ * unit's LDS) and need the same workspace as chunk 32.
  */
 size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v,
                                       eda_dtype_t dtype, int chunk);
@@ -96,7 +100,7 @@ size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v,
  *             eda_fwd_chunked_workspace_size(...) bytes, 256-byte aligned;
  *             its contents on entry are ignored and on return undefined
  *
- * Supported: 1 <= d_k, d_v <= 128; chunk in {0, 16, 32}; B, T, H >= 1 with
+ * Supported: 1 <= d_k, d_v <= 128; chunk in {0, 16, 32, 64}; B, T, H >= 1 with
  * B*T*H*max(d_k, d_v) < 2^31.  o may not overlap any input; S_final may
  * overlap S0 only as the identical pointer.
  */

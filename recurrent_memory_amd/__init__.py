@@ -38,7 +38,7 @@ __all__ = ["fwd_chunked", "recurrent_step", "fwd_chunked_layer", "recurrent_step
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libeda.so")
 _lib = None
-DEFAULT_CHUNK = 32
+DEFAULT_CHUNK = 64
 
 STATUS = {0: "EDA_OK", 1: "EDA_ERR_NULL", 2: "EDA_ERR_SHAPE", 3: "EDA_ERR_DTYPE",
           4: "EDA_ERR_ALIGN", 5: "EDA_ERR_UNSUPPORTED", 6: "EDA_ERR_WORKSPACE",

@@ -36,7 +36,7 @@ hipError_t launch_bf16(const void *, const void *, const void *, const void *, c
 
 namespace {
 
-constexpr int kDefaultChunk = 32;
+constexpr int kDefaultChunk = 64;
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -69,7 +69,13 @@ bool head_dims_supported(int dk, int dv) { return dk >= 1 && dk <= 128 && dv >= 
 
 int resolve_chunk(int chunk) { return chunk == 0 ? kDefaultChunk : chunk; }
 
-bool chunk_supported(int chunk) { return chunk == 16 || chunk == 32; }
+bool chunk_supported(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
+
+// fp32 inputs: a 64-token chunk's fp32 operands (two 128 x 128 key-side
+// tiles and their inverse) exceed one compute unit's LDS, so the fp32 path
+// computes chunk 64 as 32-token chunks; the chunk size does not change the
+// exact result.
+int f32_chunk(int chunk) { return chunk == 64 ? 32 : chunk; }
 
 }  // namespace
 
@@ -97,7 +103,7 @@ size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v, eda
         !chunk_supported(chunk))
         return 0;
     return dtype == EDA_BF16 ? eda::bf16_ws_bytes(B, T, H, d_k, d_v, chunk)
-                             : eda::chunked_ws_t<float>(B, T, H, d_k, d_v, chunk);
+                             : eda::chunked_ws_t<float>(B, T, H, d_k, d_v, f32_chunk(chunk));
 }
 
 }  // extern "C"
@@ -163,7 +169,7 @@ eda_status_t chunked_call(const void *q, const void *k, const void *e, const voi
                                T, H, H, d_k, d_v, chunk, workspace, (hipStream_t)stream,
                                (hipEvent_t const *)events)
             : eda::launch_chunked<float>(3, q, k, e, v, alpha, beta, gamma, S0, o, S_final, B,
-                                         T, H, d_k, d_v, chunk, workspace, (hipStream_t)stream,
+                                         T, H, d_k, d_v, f32_chunk(chunk), workspace, (hipStream_t)stream,
                                          (hipEvent_t const *)events);
     return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;
 }
@@ -350,7 +356,7 @@ eda_status_t eda_fwd_chunked_layer(const void *q, const void *k, const void *e, 
                                             d_k, (hipStream_t)stream);
         if (err == hipSuccess)
             err = eda::launch_chunked<float>(3, qn, kn, en, v, al, beta, gamma, S0, o, S_final, B, T,
-                                             H_v, d_k, d_v, chunk, workspace, (hipStream_t)stream,
+                                             H_v, d_k, d_v, f32_chunk(chunk), workspace, (hipStream_t)stream,
                                              nullptr);
     }
     return err == hipSuccess ? EDA_OK : EDA_ERR_HIP;

@@ -4,50 +4,62 @@
 // "Two virtual steps recover a standard delta recurrence"): token t is an
 // erase sub-step (key e_t, gate gamma_t, decay alpha_t, no value) followed by
 // a delta sub-step (key k_t, gate beta_t, value v_t, no decay).  Writing sub-
-// step j as S_j = D_j S_{j-1} + kap_j u_j^T, u_j = b'_j (nu_j - (D_j S_{j-1})^T kap_j),
-// and unrolling over a chunk of C tokens (L = 2C sub-steps) from the state S
-// at the chunk start (G = cumulative log-decay inside the chunk, per key
-// channel; t(j) = token of sub-step j):
+// step j as S_j = D_j S_{j-1} + kap_j u_j^T, u_j = b'_j (nu_j - (D_j S_{j-1})^T lam_j)
+// (lam = kap for EDA) and unrolling over a chunk of C tokens (L = 2C sub-
+// steps) from the state S at the chunk start (G = cumulative log-decay inside
+// the chunk, per key channel; t(j) = token of sub-step j) gives, with
+// A_ji = b'_j sum_c lam_jc kap_ic e^{G_t(j)c - G_t(i)c} (i < j), M = (I + A)^{-1},
+// P_ti = sum_c q_tc kap_ic e^{G_tc - G_t(i)c} (i <= 2t+1), Khat_i = kap_i o e^{G_C - G_t(i)}:
 //
-//   (I + A) U = Diag(b') (N - (kap o e^G) S),  A_ji = b'_j sum_c kap_jc kap_ic e^{G_t(j)c - G_t(i)c}  (i < j)
-//   o_t       = (q_t o e^{G_t})^T S + sum_{i <= 2t+1} P_ti u_i,   P_ti = sum_c q_tc kap_ic e^{G_tc - G_t(i)c}
-//   S_next    = Diag(e^{G_C}) S + Khat^T U,                        Khat_ic = kap_ic e^{G_Cc - G_t(i)c}
+//   U = T' V - W S,   W = M Diag(b') (lam o e^G),   T'[:, t] = M[:, 2t+1] beta_t
+//   o = (q o e^G) S + P U,      S_next = Diag(e^{G_C}) S + Khat^T U
 //
-// (N holds v_t on delta rows and 0 on erase rows; our own derivation of the
-// chunk form the paper outlines -- its WY/UT equations are not legible on
-// the pages -- checked against the token recurrence).  Decay ratios are split
-// per channel around r = G_C / 2:
-//   Kl = kap o e^{G - r},  Kr = kap o e^{r - G},  Ql = q o e^{G - r},
-// so A = Diag(b') strict_lower(Kl Kr^T) and P = causal(Ql Kr^T).  With the
-// scaled state S' = Diag(e^r) S, M = (I + A)^{-1}, the WY factors
-//   W = M Diag(b') Kl   [L x d_k],     T' = (M Diag(b'))[:, delta sub-steps]   [L x C]
-// give, per chunk,
-//   U = T' V - W S',   o = Ql S' + P U,   S_next = Diag(e^r) (Diag(e^r) S + Kr^T U)
-// (e^{G_C} = e^{2r}).  Every factor stays within e^{+-|G_C|/2}; a chunk in
-// which some channel decays by more than e^-120 (only possible below the safe
-// gate's floor alpha = e^-5) computes A and P element-wise from e^{G_j - G_i}
-// and uses the unsplit factors kap o e^G, q o e^G and Khat instead.
+// (our own derivation of the chunk form the paper outlines -- its WY/UT
+// equations are not legible on the pages -- checked in fp64 against the
+// token recurrence by the CPU tests).  Substituting U, the chunk is an affine
+// map of the state with chunk-constant factors:
+//
+//   S_next = Diag(e^{G_C}) S + Phi S + Psi V,   O = Qhat S + Phat V
+//   Phi = -Khat^T W  [d_k x d_k],  Psi = Khat^T T'  [d_k x C],
+//   Qhat = (q o e^G) - P W  [C x d_k],  Phat = P T'  [C x C]
+//
+// so the serial pass over chunks needs one product per chunk on its chain.
+// With Y = M^T Khat and Z = P M these are Phi = -Y^T Diag(b')(lam o e^G),
+// Psi = Y[delta rows]^T Diag(beta), Qhat = q o e^G - Z Diag(b')(lam o e^G),
+// Phat = Z[:, delta cols] Diag(beta): W and T' are never formed.
+//
+// Range safety: decay ratios are split per channel around r = G_C / 2,
+//   Kl = Diag(b') lam o e^{G - r},  Kr = kap o e^{r - G},  Ql = q o e^{G - r},
+// so A = strict_lower(Kl Kr^T) and P = causal(Ql Kr^T) only see factors
+// within e^{+-|G_C|/2}; the exports carry the scale e^r of each key channel
+// (lam o e^G = Kl e^r / b', Khat = Kr e^r, q o e^G = Ql e^r).  A chunk in
+// which some channel decays by more than e^-120 (only possible below the
+// safe gate's floor alpha = e^-5) forms A and P element-wise from
+// e^{G_j - G_i} and uses unsplit operands (r = 0).
+//
+// Rounding: every matrix-core operand is bf16; products accumulate in fp32.
+// Each exported factor is rounded once, from fp32 accumulators: beta and e^r
+// are applied to the fp32 products, never to a rounded operand, so the
+// rounded M enters W-like and T'-like terms identically (a write followed by
+// an erase of the same address then cancels as in exact arithmetic).  P is
+// kept as a bf16 pair P_hi + P_lo in Z = P M.
 //
 // Kernel 1 (eda_bf16_factors): persistent workgroups walk the (head, chunk)
-//   items; each item's raw values are fetched into registers while the
-//   previous item is processed.  Per item: the cumulative decay, the scaled
-//   operands (and Diag(e^r) Kr^T straight to the workspace), A and P on the
-//   matrix cores, (I + A)^{-1} (fp32 substitution on the 16x16 diagonal
-//   blocks, then one column block of the rest per wave, held in registers),
-//   W, Q^ and P^ on the matrix cores, and the export of -W Diag(e^r), T', Q^,
-//   P^ and the per-channel decay to the workspace.
+//   items; each item's raw inputs are fetched into registers while the
+//   previous item is processed.  Per item: cumulative decay, operands, A and
+//   P on the matrix cores, (I + A)^{-1} (fp32 substitution on the 16 x 16
+//   diagonal blocks, then one column block of the rest per wave), Y and Z,
+//   then Phi and Qhat; Psi, Phat, Phi, Qhat and e^{G_C} go to the workspace.
 // Kernel 2 (eda_bf16_state): one workgroup per (head, slice of value
-//   columns), serial over chunks, fp32 state in registers.  The factors are
-//   stored in the exact per-lane order of the matrix-core operands, so each
-//   wave fetches its own operands straight into registers three chunks
-//   ahead; only S'^T, U^T, the value slice and the outputs pass through LDS,
-//   and each role reads all its LDS operands before its first product.  Two
-//   barriers per chunk.
+//   columns), serial over chunks, fp32 state in registers, one barrier per
+//   chunk.  The factors are stored in the per-lane order of the matrix-core
+//   operands, so each wave fetches its own operands straight into registers
+//   two chunks ahead.
 //
 // Workspace: one block of Fac<C, D>::bytes per chunk and head.  A "fragment"
-// of a matrix M (rows x k, row-major view) is the 16 x 32 block at
+// of a matrix X (rows x k, row-major view) is the 16 x 32 block at
 // (16 rb, 32 ks): 64 lanes x 16 bytes, lane 16 g + r holding
-// M[16 rb + r][32 ks + 8 g .. 32 ks + 8 g + 7] -- the operand layout of the
+// X[16 rb + r][32 ks + 8 g .. 32 ks + 8 g + 7] -- the operand layout of the
 // 16x16x32 bf16 matrix instruction.
 #include <type_traits>
 
@@ -55,10 +67,6 @@
 
 namespace eda {
 namespace b16 {
-
-// factor kernel: 4 waves per workgroup, so that two workgroups (two chunks in
-// flight, each with its own barriers) share a compute unit
-constexpr int K1WAVES = 4, K1THREADS = 64 * K1WAVES;
 
 // wide-chunk threshold on a chunk's log2-decay (e^-120 = 2^-173)
 constexpr float WIDE_G2 = 173.f;
@@ -97,7 +105,6 @@ __device__ __forceinline__ bf16x8 frag_col(const bf16 *p, int ld, int lane) {
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(mp + 4 * ld));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-
 __device__ __forceinline__ bf16x8 ld_frag(const char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 __device__ __forceinline__ void st_frag(char *p, bf16x8 x) { *reinterpret_cast<bf16x8 *>(p) = x; }
 
@@ -162,22 +169,20 @@ __device__ __forceinline__ float group_last(float x) {
 
 // ---------------------------------------------------------------------------
 // Workspace block of one chunk and head (byte offsets; fragments as above).
+// Every factor is in natural units (the split scale e^r folded back in).
 // ---------------------------------------------------------------------------
 template <int C, int D>
 struct Fac {
     static constexpr int L = 2 * C, NBL = L / 16, NBC = C / 16, NBD = D / 16;
-    static constexpr int KSD = D / 32, KSL = L / 32;
-    static constexpr int FR = 1024;                    // one fragment
-    // (every factor with a key-channel index carries the scale e^r of that
-    // channel, so the state pass works on the unscaled state)
-    static constexpr int oWn = 0;                      // -W Diag(e^r)             [NBL][KSD] fragments
-    static constexpr int oTv = oWn + NBL * KSD * FR;   // T'                       [NBL] (k = C, zero-padded)
-    static constexpr int oKr = oTv + NBL * FR;         // Diag(e^r) Kr^T           [NBD][KSL]
-    static constexpr int oQh = oKr + NBD * KSL * FR;   // (Ql - P W) Diag(e^r)     [NBC][KSD]
-    static constexpr int oPh = oQh + NBC * KSD * FR;   // P T'                     [NBC] (k = C, zero-padded)
-    static constexpr int oDec = oPh + NBC * FR;        // e^{G_C}                  [D] fp32
+    static constexpr int KSD = D / 32, KSC = (C + 31) / 32;   // k-steps over channels, over tokens
+    static constexpr int FR = 1024;                            // one fragment
+    static constexpr int oPhi = 0;                             // Phi  [NBD][KSD]  (rows, k: key channels)
+    static constexpr int oPsi = oPhi + NBD * KSD * FR;         // Psi  [NBD][KSC]  (rows: channels, k: tokens; zero-padded)
+    static constexpr int oQh = oPsi + NBD * KSC * FR;          // Qhat [NBC][KSD]  (rows: tokens, k: channels)
+    static constexpr int oPh = oQh + NBC * KSD * FR;           // Phat [NBC][KSC]  (rows, k: tokens; zero-padded)
+    static constexpr int oDec = oPh + NBC * KSC * FR;          // e^{G_C} [D] fp32
     static constexpr int bytes = align256(oDec + D * 4);
-    static_assert(C == 16 || C == 32, "chunk");
+    static_assert(C == 16 || C == 32 || C == 64, "chunk");
     static_assert(D % 32 == 0 && D <= 128, "head dim");
 };
 
@@ -189,7 +194,10 @@ struct Fac {
 template <int C, int D>
 struct K1G {
     using F = Fac<C, D>;
-    static constexpr int L = 2 * C, NB = L / 16, NT = K1THREADS, NW = K1WAVES;
+    static constexpr int L = 2 * C, NB = L / 16, NBC = C / 16, NBD = D / 16;
+    // 64-token chunks: one 8-wave workgroup per compute unit (LDS); smaller
+    // chunks: 4-wave workgroups, two per compute unit
+    static constexpr int NW = C == 64 ? 8 : 4, NT = 64 * NW;
     static constexpr int LDA = D + 8, LDL = L + 8, ADS = 20, MTW = 24;
     static constexpr int NQ = D / 4;
     static constexpr int TPC = imin(NT / NQ, C);       // threads per channel quad
@@ -198,23 +206,33 @@ struct K1G {
     static_assert((TPC & (TPC - 1)) == 0 && TPC <= 64 && C % TPC == 0 && ACT <= NT, "split");
     static_assert(TPT == 1 || TPT == 2 || TPT == 4, "token run");
     static_assert(NB <= NW, "one diagonal block per wave");
-    // W^T tiles
-    static constexpr int NWT = F::NBD * F::NBL;
-    // LDS (bytes).  In a wide chunk Kl holds G (fp32 [C][D]) and Kr, Ql the raw
-    // keys and queries until the operands are formed.  Once the W tiles are
-    // formed, the Kr region stages -W Diag(e^r).
+    static_assert(C <= 64, "beta/gamma staging by the first wave");
+    // P (and later Z = P M) is stored packed: the rows of token block tb hold
+    // sub-steps 0 .. 32 tb + 31 (P is zero beyond 2t + 1), row stride 32 tb + 40.
+    static __host__ __device__ constexpr int pld(int tb) { return 32 * tb + 40; }
+    static __host__ __device__ constexpr int poff(int tb) { return 16 * tb * (16 * tb + 24); }
+    static constexpr int PSZ = poff(NBC);
+    // LDS (bytes).  Kl holds G (fp32 [C][D]) in a wide chunk until the operands
+    // are formed; Kr becomes Y = M^T Khat; the off-diagonal blocks of A sit in
+    // the (otherwise unused) upper blocks of M, block (J, I) at (I, J), during
+    // the inversion; the diagonal-inverse scratch becomes Z; M holds the layer
+    // form's norm partials before the operands exist.
     static constexpr int szKl = align16(L * LDA * 2), szQl = align16(C * LDA * 2);
-    static_assert(C * D * 4 <= szKl, "Kl region reuse");
-    static constexpr int szLL = align16(L * LDL * 2), szAd = NB * 16 * ADS * 4;
-    static constexpr int szMT = NB * 16 * MTW * 2, szPs = align16(C * LDL * 2);
-    static constexpr int szMisc = (L + 2 * C + D) * 4 + NW * C * 16 + NW * 4;   // + norm partials, votes
-    static constexpr int LDTV = C + 8;                 // T' and P T' staging rows (after the inverse)
-    static_assert(L * LDTV * 2 <= szLL && C * LDTV * 2 <= szAd, "staging reuse");
-    static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oAbf = oQl + szQl;
-    static constexpr int oAd = oAbf + szLL, oMI = oAd + szAd, oMT = oMI + szLL, oPs = oMT + szMT;
-    static constexpr int oMisc = oPs + szPs;
-    static constexpr int LDS = oMisc + szMisc;
-    static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
+    static constexpr int szMI = align16(L * LDL * 2);
+    static constexpr int szAd = NB * 16 * ADS * 4, szMT = NB * 16 * MTW * 2;
+    static constexpr int szP = align16(PSZ * 2);
+    static_assert(szAd + szMT >= szP, "Z in the inversion scratch");
+    static_assert(C * D * 4 <= szKl, "G in the Kl region");
+    static_assert(NW * C * 16 <= szMI, "norm partials in the M region");
+    static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oMI = oQl + szQl;
+    static constexpr int oAd = oMI + szMI, oMT = oAd + szAd, oPh = oMT + szMT, oPl = oPh + szP;
+    static constexpr int oMisc = oPl + szP;
+    static constexpr int LDS = oMisc + (L + 2 * C + D) * 4 + NW * 4 + C * 16;
+    static_assert(LDS <= (NW == 8 ? 160 : 80) * 1024, "LDS budget");
+    // phase 4/5 work lists
+    static constexpr int NZT = NBC * (NBC + 1);         // Z tiles (tb, J <= 2 tb + 1)
+    static constexpr int BM = 2, BN = imin(4, NBD);     // Phi register block (tiles)
+    static constexpr int NPB = (NBD / BM) * (NBD / BN); // Phi blocks
 };
 
 // VEC: d_k == D and 16-byte aligned q, k, e and decay input (each thread's
@@ -237,7 +255,7 @@ struct K1G {
 constexpr int MODE_PLAIN = 0, MODE_LAYER = 1, MODE_DPLR = 2;
 
 template <int C, int D, bool VEC, int MODE>
-__global__ void __launch_bounds__(K1THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__((K1G<C, D>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
 eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ e,
                  const void *__restrict__ decay, const float *__restrict__ A_log,
                  const float *__restrict__ dt_bias, const float *__restrict__ beta,
@@ -249,42 +267,32 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     constexpr bool LAYER = MODE == MODE_LAYER, DPLR = MODE == MODE_DPLR;
     constexpr int L = G::L, NB = G::NB, NT = G::NT, NW = G::NW, LDA = G::LDA, LDL = G::LDL;
     constexpr int ADS = G::ADS, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT;
-    constexpr int NWT = G::NWT;
-    constexpr int NBD = F::NBD, NBL = F::NBL, NBC = F::NBC, KSD = F::KSD, KSL = F::KSL;
+    constexpr int NBD = F::NBD, NBC = F::NBC, KSD = F::KSD, KSC = F::KSC;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Kl = (T *)(smem + G::oKl);            // Diag(b') Kl              [L][LDA]
     float *Gs = (float *)(smem + G::oKl);    // wide chunk: G (log2) [C][D]
-    T *Kr = (T *)(smem + G::oKr);            // Kr                       [L][LDA]
-    T *Wst = Kr;                             // -W Diag(e^r), once A and P are done [L][LDA]
+    T *Kr = (T *)(smem + G::oKr);            // Kr, then Y = M^T Khat    [L][LDA]
     T *Ql = (T *)(smem + G::oQl);            // Ql                       [C][LDA]
-    T *Abf = (T *)(smem + G::oAbf);          // A, off-diagonal 16-blocks [L][LDL]
+    T *MI = (T *)(smem + G::oMI);            // (I + A)^{-1}; A's off-diagonal blocks mirrored above [L][LDL]
     float *AdT = (float *)(smem + G::oAd);   // A, diagonal 16-blocks, transposed: [J][p][i] = A_J[i][p]
-    T *MI = (T *)(smem + G::oMI);            // (I + A)^{-1}             [L][LDL]
-    T *MT = (T *)(smem + G::oMT);            // its diagonal blocks, transposed [NB][16][MTW]
-    T *Ps = (T *)(smem + G::oPs);            // P (causal)               [C][LDL]
+    T *MT = (T *)(smem + G::oMT);            // diagonal blocks of M, transposed [NB][16][MTW]
+    T *Zs = (T *)(smem + G::oAd);            // Z = P M (packed like P), once the inverse is done
+    T *Ph = (T *)(smem + G::oPh);            // P, high bf16 part (packed)
+    T *Pl = (T *)(smem + G::oPl);            // P, low bf16 part (packed)
     float *bp = (float *)(smem + G::oMisc);  // b' per sub-step          [L]
     float *sb = bp + L, *sg = sb + C;        // beta, gamma per token    [C]
     float *ers = sg + C;                     // e^r per channel (1 if wide) [D]
-    float *nrm = ers + D;                    // LAYER: per-wave |q|^2, |k|^2, |e|^2 partials [NW][C][4]
-    uint32_t *vote = (uint32_t *)(nrm + NW * C * 4);   // LAYER: per-wave wide-chunk votes [NW]
-    T *Tvs = (T *)(smem + G::oAbf);          // T', after the inverse    [L][LDTV]
-    T *Phs = (T *)(smem + G::oAd);           // P T', after the inverse  [C][LDTV]
-    constexpr int LDTV = G::LDTV;
+    uint32_t *vote = (uint32_t *)(ers + D);  // LAYER: per-wave wide-chunk votes [NW]
+    float *invn = (float *)(vote + NW);      // LAYER, wide chunk: 1/|q|, 1/|k|, 1/|e| per token [C][4]
+    float *nrm = (float *)(smem + G::oMI);   // LAYER: per-wave |q|^2, |k|^2, |e|^2 partials [NW][C][4]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g4 = 4 * (lane >> 4), l16 = lane & 15;
+    const int g4 = 4 * (lane >> 4), l16 = lane & 15, gq = lane >> 4;
     const int grp = H / Hk;                  // value heads per key head
     const float *alpha = (const float *)decay;
     const bf16 *agate = (const bf16 *)decay;
     const int items = BH * NC;
-
-    // The blocks of (I + A)^{-1} above the diagonal are never written: zero
-    // them (and the row padding) once.
-    for (int idx = tid; idx < L * LDL; idx += NT) {
-        const int r = idx / LDL, c = idx % LDL;
-        if (c >= L || (c >> 4) > (r >> 4)) MI[idx] = (T)0;
-    }
 
     auto chunk_of = [&](int it) __attribute__((always_inline)) { return NC - 1 - it / BH; };
     auto head_of = [&](int it) __attribute__((always_inline)) { return it % BH; };
@@ -412,6 +420,16 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         *(uint2 *)(MT + (16 * J + col) * MTW + s4) = make_uint2(x01, x23);
     };
 
+    // P tile value -> P_hi, P_lo at row tau (packed), sub-steps i0 .. i0 + 3
+    auto store_p = [&](int tau, int i0, float a0, float a1, float a2, float a3) __attribute__((always_inline)) {
+        const int tb = tau >> 4;
+        const int off = G::poff(tb) + (tau & 15) * G::pld(tb) + i0;
+        const uint32_t h01 = pack_bf16(a0, a1), h23 = pack_bf16(a2, a3);
+        *(uint2 *)(Ph + off) = make_uint2(h01, h23);
+        *(uint2 *)(Pl + off) = make_uint2(pack_bf16(a0 - lo_bf16(h01), a1 - hi_bf16(h01)),
+                                          pack_bf16(a2 - lo_bf16(h23), a3 - hi_bf16(h23)));
+    };
+
     int it = blockIdx.x;
     if constexpr (VEC) {
         prefetch(it);
@@ -431,6 +449,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     for (; it < items; it += gridDim.x) {
         const int bh = head_of(it), cidx = chunk_of(it);
         if (!is_fast(cidx)) fetch_slow(it);
+        // (nothing read after this item's last barrier uses bp, sb or sg)
         if (tid < C) {
             sb[tid] = pbeta;
             sg[tid] = pgamma;
@@ -503,7 +522,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         // rewrites its slot only at the next item's vote, after barriers of this
         // item that every wave passes once its reads below are done), which
         // spares the mode's registers.  The plain and DPLR modes keep the
-        // block-wide OR, measured faster there.
+        // block-wide OR.
         bool wide = false;
         if constexpr (LAYER) {
             const bool wv = __ballot(wide_here) != 0ull;
@@ -515,10 +534,13 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             wide = __syncthreads_or(wide_here) != 0;
         }
         // LAYER: 1 / max(|x|, eps) of the thread's token i, for q, k, e (formed
-        // where each token is used, so the scales are not held across the loop)
-        auto inv_norms = [&](int i) __attribute__((always_inline)) {
+        // where each token is used, so the scales are not held across the loop).
+        // A wide chunk forms its operands a second time, after its element-wise A
+        // and P have overwritten the partials' region; it keeps the scales in invn.
+        auto inv_norms = [&](int i, bool saved = false) __attribute__((always_inline)) {
             f32x4 tot = zero4();
             if constexpr (LAYER) {
+                if (saved) return *(const f32x4 *)(invn + 4 * (TPT * seg + i));
                 constexpr int NWA = (G::ACT + 63) / 64;
 #pragma unroll
                 for (int w = 0; w < NWA; ++w) tot += *(const f32x4 *)(nrm + (w * C + TPT * seg + i) * 4);
@@ -528,20 +550,16 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             return tot;   // (1/|q|, 1/|k|, 1/|e|)
         };
 
-        // ---- scaled operands (LDS), Diag(e^r) Kr^T (workspace) and the
-        //      per-channel scales -------------------------------------------------------
+        // ---- scaled operands (LDS) and the per-channel scales ----------------------
         // Forms Diag(b') Kl, Kr and Ql from the thread's raw values; in a wide
-        // chunk the exponents are unsplit (Kl = kap 2^G, Kr = kap 2^{G_C - G}).
-        // Diag(e^r) Kr^T = Khat^T in both cases: each thread's run of 2 TPT
-        // sub-steps of one channel is one piece of a fragment lane.
+        // chunk the exponents are unsplit (Kl = lam 2^G, Kr = kap 2^{G_C - G}).
         f32x4 er;
 #pragma unroll
         for (int j = 0; j < 4; ++j) er[j] = wide ? 1.f : exp2f_(0.5f * glq[j]);
-        auto form_operands = [&]() __attribute__((always_inline)) {
+        auto form_operands = [&](bool saved_norms) __attribute__((always_inline)) {
             float r[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) r[j] = wide ? 0.f : 0.5f * glq[j];
-            uint32_t kh[4][TPT];   // Khat^T run per channel: (e, k) of each token, packed
 #pragma unroll
             for (int i = 0; i < TPT; ++i) {
                 const int tau = TPT * seg + i;
@@ -549,7 +567,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 float kv[4] = {lo_bf16(xk[i].x), hi_bf16(xk[i].x), lo_bf16(xk[i].y), hi_bf16(xk[i].y)};
                 float qv[4] = {lo_bf16(xq[i].x), hi_bf16(xq[i].x), lo_bf16(xq[i].y), hi_bf16(xq[i].y)};
                 if constexpr (LAYER) {
-                    const f32x4 nv = inv_norms(i);
+                    const f32x4 nv = inv_norms(i, saved_norms);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         ev[j] *= nv[2];
@@ -563,8 +581,6 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 for (int j = 0; j < 4; ++j) {
                     f[j] = exp2f_(g[i][j] - r[j]);
                     fi[j] = wide ? exp2f_(glq[j] - g[i][j]) : exp2f_(r[j] - g[i][j]);
-                    const float fh = fi[j] * er[j];
-                    kh[j][i] = pack_bf16(DPLR ? 0.f : ev[j] * fh, kv[j] * fh);
                 }
                 store4<T>(Kl + (2 * tau) * LDA + c0, gmt * ev[0] * f[0], gmt * ev[1] * f[1],
                           gmt * ev[2] * f[2], gmt * ev[3] * f[3]);
@@ -584,17 +600,6 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                           kv[3] * fi[3]);
                 store4<T>(Ql + tau * LDA + c0, qv[0] * f[0], qv[1] * f[1], qv[2] * f[2], qv[3] * f[3]);
             }
-            // fragment (16 x 32 block (n / 16, j0 / 32)), lane 16 ((j0 % 32) / 8) + n % 16, element j0 % 8
-            const int j0 = 2 * TPT * seg;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = c0 + j;
-                char *dst = wsb + F::oKr + (((n >> 4) * KSL + (j0 >> 5)) * 64 + 16 * ((j0 & 31) >> 3) + (n & 15)) * 16 +
-                            2 * (j0 & 7);
-                if constexpr (TPT == 4) *(uint4 *)dst = make_uint4(kh[j][0], kh[j][1], kh[j][2], kh[j][3]);
-                else if constexpr (TPT == 2) *(uint2 *)dst = make_uint2(kh[j][0], kh[j][1]);
-                else *(uint32_t *)dst = kh[j][0];
-            }
         };
         if (act) {
             if (seg == 0) {
@@ -605,7 +610,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 *(f32x4 *)(wsb + F::oDec + 4 * c0) = dec;
             }
             if (!wide) {
-                form_operands();
+                form_operands(false);
             } else {
                 // raw keys and queries, and G, for the element-wise path
 #pragma unroll
@@ -617,6 +622,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                                           pack_bf16(lo_bf16(u.y) * s, hi_bf16(u.y) * s));
                     };
                     const f32x4 nv = inv_norms(i);
+                    if (LAYER && c0 == 0) *(f32x4 *)(invn + 4 * tau) = nv;
                     *(uint2 *)(Kr + (2 * tau) * LDA + c0) = nz(xe[i], nv[2]);
                     *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = nz(xk[i], nv[1]);
                     *(uint2 *)(Ql + tau * LDA + c0) = nz(xq[i], nv[0]);
@@ -626,9 +632,10 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         __syncthreads();
 
-        // ---- A (strictly lower) and P (causal); diagonal blocks inverted ----------
+        // ---- A (strictly lower) and P (causal, as a bf16 pair); diagonal blocks
+        //      of A inverted ------------------------------------------------------------
         constexpr int NOD = NB * (NB - 1) / 2;
-        constexpr int NPT = NB * (C / 16);
+        constexpr int NPT = NB * NBC;
         if (!wide) {
             if (wave < NB) {
                 const int J = wave;
@@ -646,20 +653,21 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     int J = 1, I = t;
                     while (I >= J) { I -= J; ++J; }
                     const f32x4 a = tile_nt<T, D>(Kl + 16 * J * LDA, LDA, Kr + 16 * I * LDA, LDA, zero4(), lane);
+                    // A[16 J + g4 + rr][16 I + l16] -> mirrored block (I, J) of M's storage
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        Abf[(16 * J + g4 + rr) * LDL + 16 * I + l16] = from_f32<T>(a[rr]);
+                        MI[(16 * I + g4 + rr) * LDL + 16 * J + l16] = from_f32<T>(a[rr]);
                 } else {
                     // P^T tile: rows = sub-steps i, cols = tokens; kept for i <= 2 tau + 1
-                    const int I = (t - NOD) / (C / 16), Tb = (t - NOD) % (C / 16);
+                    const int I = (t - NOD) / NBC, Tb = (t - NOD) % NBC;
                     const int tau = 16 * Tb + l16, i0 = 16 * I + g4;
-                    float w4[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (16 * I <= 32 * Tb + 31) {   // else beyond every token's causal range
+                    if (16 * I < 32 * Tb + 32) {   // else beyond the stored row
                         const f32x4 a = tile_nt<T, D>(Kr + 16 * I * LDA, LDA, Ql + 16 * Tb * LDA, LDA, zero4(), lane);
+                        float w4[4];
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr) w4[rr] = (i0 + rr <= 2 * tau + 1) ? a[rr] : 0.f;
+                        store_p(tau, i0, w4[0], w4[1], w4[2], w4[3]);
                     }
-                    store4<T>(Ps + tau * LDL + i0, w4[0], w4[1], w4[2], w4[3]);
                 }
             }
         } else {
@@ -677,24 +685,31 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     s *= bp[j];
                 }
                 if ((j >> 4) == (ii >> 4)) AdT[((j >> 4) * 16 + (ii & 15)) * ADS + (j & 15)] = s;
-                else if (ii < j) Abf[j * LDL + ii] = from_f32<T>(s);
+                else if (ii < j) MI[(16 * (ii >> 4) + (j & 15)) * LDL + 16 * (j >> 4) + (ii & 15)] = from_f32<T>(s);
             }
             for (int idx = tid; idx < C * L; idx += NT) {
                 const int tau = idx / L, ii = idx % L;
-                float s = 0.f;
-                if (ii <= 2 * tau + 1 && (!DPLR || (ii & 1))) {
-                    const int ti = ii >> 1;
+                if (ii >= 32 * (tau >> 4) + 32 || (ii & 3)) continue;   // four sub-steps per thread, stored rows only
+                float s4[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = ii + u;
+                    float s = 0.f;
+                    if (i <= 2 * tau + 1 && (!DPLR || (i & 1))) {
+                        const int ti = i >> 1;
 #pragma unroll 2
-                    for (int cc = 0; cc < D; ++cc)
-                        s += to_f32(Ql[tau * LDA + cc]) * to_f32(Kr[ii * LDA + cc]) *
-                             exp2f_(Gs[tau * D + cc] - Gs[ti * D + cc]);
+                        for (int cc = 0; cc < D; ++cc)
+                            s += to_f32(Ql[tau * LDA + cc]) * to_f32(Kr[i * LDA + cc]) *
+                                 exp2f_(Gs[tau * D + cc] - Gs[ti * D + cc]);
+                    }
+                    s4[u] = s;
                 }
-                Ps[tau * LDL + ii] = from_f32<T>(s);
+                store_p(tau, ii, s4[0], s4[1], s4[2], s4[3]);
             }
             __syncthreads();
             if (wave < NB) invert_diag(wave);
             // every read of G and of the raw keys is done: form the operands in place
-            if (act) form_operands();
+            if (act) form_operands(true);
         }
         __syncthreads();
 
@@ -722,7 +737,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 #pragma unroll
                 for (int K = 0; K < J; ++K) {
                     if (K < I) continue;
-                    const s16x4 a = *(const s16x4 *)(Abf + (16 * J + l16) * LDL + 16 * K + g4);
+                    // A[16 J + l16][16 K + g4 ..] from its mirrored block (K, J)
+                    const s16x4 a = *(const s16x4 *)(MI + (16 * K + l16) * LDL + 16 * J + g4);
                     t = mma16(a, xb[K], t);
                 }
                 const s16x4 tb = __builtin_bit_cast(s16x4, make_uint2(pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])));
@@ -739,187 +755,186 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         __syncthreads();
 
-        // T'[j][tau] = M[j][2 tau + 1] beta_tau (tau >= C: zero): row block rb -> workspace and LDS
-        auto export_tv = [&](int rb) __attribute__((always_inline)) {
-            const int gg = lane >> 4;
-            const T *mrow = MI + (16 * rb + l16) * LDL;
-            uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            if (8 * gg < C) {
-                const uint4 u0 = *(const uint4 *)(mrow + 16 * gg);
-                const uint4 u1 = *(const uint4 *)(mrow + 16 * gg + 8);
-                const f32x4 b0 = *(const f32x4 *)(sb + 8 * gg), b1 = *(const f32x4 *)(sb + 8 * gg + 4);
-                x = make_uint4(pack_bf16(hi_bf16(u0.x) * b0[0], hi_bf16(u0.y) * b0[1]),
-                               pack_bf16(hi_bf16(u0.z) * b0[2], hi_bf16(u0.w) * b0[3]),
-                               pack_bf16(hi_bf16(u1.x) * b1[0], hi_bf16(u1.y) * b1[1]),
-                               pack_bf16(hi_bf16(u1.z) * b1[2], hi_bf16(u1.w) * b1[3]));
-                *(uint4 *)(Tvs + (16 * rb + l16) * LDTV + 8 * gg) = x;
+        // ---- Y = M^T Kr (in place over Kr, by column block) and Z = P M; from their
+        //      fp32 accumulators the exports Psi = e^r Y[delta rows]^T Diag(beta) and
+        //      Phat = Z[:, delta cols] Diag(beta).  A product over sub-steps from 16 J
+        //      on starts at the 32-row step holding row 16 J; when J is odd its first
+        //      16 rows (M's block above the diagonal, which holds A during the
+        //      inversion) are masked out of M's operand.  Every product here is the
+        //      16x16x32 instruction: a 16x16x16 result fed straight into a 16x16x32
+        //      accumulator was found to need wait states the compiler did not insert
+        //      (its last accumulator register was read stale).
+        const bool lo_half = lane < 32;   // lanes holding k = 0..15 of a 16x16x32 operand
+        auto m_frag = [&](int s, int J) __attribute__((always_inline)) {
+            bf16x8 m = frag_col(MI + 32 * s * LDL + 16 * J, LDL, lane);
+            if ((J & 1) && s == (J >> 1) && lo_half) m = bf16x8{};
+            return m;
+        };
+        for (int nb = wave; nb < NBD; nb += NW) {
+            // Kr column block nb, all sub-steps, as B operands (read before Y overwrites it)
+            bf16x8 kb[L / 32];
+#pragma unroll
+            for (int s = 0; s < L / 32; ++s) kb[s] = frag_col(Kr + 32 * s * LDA + 16 * nb, LDA, lane);
+            const float ern = ers[16 * nb + l16];
+            f32x4 y[NB];
+#pragma unroll
+            for (int J = 0; J < NB; ++J) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = J >> 1; s < L / 32; ++s) acc = mma32(m_frag(s, J), kb[s], acc);
+                // lane: Y[16 J + g4 + i][16 nb + l16], kept as Yhat = Y Diag(e^r) = M^T Khat
+                // (bounded by |M|: Y^T Kl below would otherwise reach e^{|G_C|}, past
+                // the fp32 range, for channels decaying by more than about e^-88)
+                y[J] = acc * ern;
+                // Psi[n][t] for delta rows j = 16 J + g4 + 1, + 3: t = 8 J + gq * 2 (+1)
+                const int t0 = 8 * J + 2 * gq;
+                const float2 bt = *(const float2 *)(sb + t0);
+                const uint32_t pv = pack_bf16(y[J][1] * bt.x, y[J][3] * bt.y);
+                *(uint32_t *)(wsb + F::oPsi + ((nb * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
+                              2 * (t0 & 7)) = pv;
             }
-            *(uint4 *)(wsb + F::oTv + (rb * 64 + lane) * 16) = x;
-        };
-        // W^T tile (channel block nb, sub-step block jb) = Kl^T Diag(b') M^T, staged
-        // as -W Diag(e^r) in the Kr region (Kr was last read by the A and P tiles)
-        auto w_tile = [&](int jb, int nb) __attribute__((always_inline)) {
-            // M's row block jb is zero beyond column 16 (jb + 1); round up to 32
-            const int K = 32 * ((jb + 2) / 2);
+            if constexpr (C == 16) {
+                // tokens 16 .. 31 of the k = 32 fragment are zero
+                if (lane >= 32) *(uint4 *)(wsb + F::oPsi + (nb * KSC * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int J = 0; J < NB; ++J)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Kr[(16 * J + g4 + i) * LDA + 16 * nb + l16] = from_f32<T>(y[J][i]);
+        }
+        for (int z = (wave + NBD) % NW; z < G::NZT; z += NW) {
+            // Z^T tile (sub-steps 16 J.., tokens 16 tb..): z enumerates tb = 0.., J = 0..2 tb + 1
+            int tb = 0, J = z;
+            while (J >= 2 * tb + 2) { J -= 2 * tb + 2; ++tb; }
+            const int pr = G::poff(tb) + l16 * G::pld(tb);   // this lane's P row (token 16 tb + l16)
             f32x4 acc = zero4();
-            for (int k0 = 0; k0 < K; k0 += 32)
-                acc = mma32(frag_col(Kl + k0 * LDA + 16 * nb, LDA, lane),
-                            frag_row(MI + 16 * jb * LDL + k0, LDL, lane), acc);
-            // lane holds W[16 jb + l16][16 nb + g4 + i]
-            const f32x4 es = *(const f32x4 *)(ers + 16 * nb + g4);
-            store4<T>(Wst + (16 * jb + l16) * LDA + 16 * nb + g4, -acc[0] * es[0], -acc[1] * es[1],
-                      -acc[2] * es[2], -acc[3] * es[3]);
-        };
-        // Q^T tile (channels 16 nb.., tokens 16 tb..) = ((Ql - P W) Diag(e^r))^T, in
-        // place over Ql; P is zero beyond sub-step 2t + 1
-        auto qh_tile = [&](int nb, int tb) __attribute__((always_inline)) {
-            const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * nb + g4);
-            const f32x4 es = *(const f32x4 *)(ers + 16 * nb + g4);
-            f32x4 acc = {lo_bf16(q0.x) * es[0], hi_bf16(q0.x) * es[1], lo_bf16(q0.y) * es[2],
-                         hi_bf16(q0.y) * es[3]};
-            const int K = imin(L, 32 * (tb + 1));
-            for (int k0 = 0; k0 < K; k0 += 32)
-                acc = mma32(frag_col(Wst + k0 * LDA + 16 * nb, LDA, lane),
-                            frag_row(Ps + 16 * tb * LDL + k0, LDL, lane), acc);
-            store4<T>(Ql + (16 * tb + l16) * LDA + 16 * nb + g4, acc[0], acc[1], acc[2], acc[3]);
-        };
-        // P^ ^T tile (tokens tau 16 nb.., tokens t 16 tb..) = (P T')^T, staged
-        auto ph_tile = [&](int nb, int tb) __attribute__((always_inline)) {
-            f32x4 acc = zero4();
-            const int K = imin(L, 32 * (tb + 1));
-            for (int k0 = 0; k0 < K; k0 += 32)
-                acc = mma32(frag_col(Tvs + k0 * LDTV + 16 * nb, LDTV, lane),
-                            frag_row(Ps + 16 * tb * LDL + k0, LDL, lane), acc);
-            store4<T>(Phs + (16 * tb + l16) * LDTV + 16 * nb + g4, acc[0], acc[1], acc[2], acc[3]);
-        };
-        auto export_ph = [&](int rb) __attribute__((always_inline)) {
-            uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            if (8 * (lane >> 4) < C) x = __builtin_bit_cast(uint4, frag_row(Phs + 16 * rb * LDTV, LDTV, lane));
-            *(uint4 *)(wsb + F::oPh + (rb * 64 + lane) * 16) = x;
-        };
+            for (int s = J >> 1; s < tb + 1; ++s) {
+                const bf16x8 m = m_frag(s, J);
+                acc = mma32(m, *(const bf16x8 *)(Ph + pr + 32 * s + 8 * gq), acc);
+                acc = mma32(m, *(const bf16x8 *)(Pl + pr + 32 * s + 8 * gq), acc);
+            }
+            // lane: Z[t = 16 tb + l16][j = 16 J + g4 + i]
+            *(uint2 *)(Zs + pr + 16 * J + g4) = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
+            const int t0 = 8 * J + 2 * gq;
+            const float2 bt = *(const float2 *)(sb + t0);
+            *(uint32_t *)(wsb + F::oPh + ((tb * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
+                          2 * (t0 & 7)) = pack_bf16(acc[1] * bt.x, acc[3] * bt.y);
+        }
+        // Phat is causal: the Z tiles of token block tb write tokens t' < 16 (tb + 1);
+        // the rest of its fragments (which the state pass reads whole) is zeroed
+        // here, by lanes whose 8 tokens all lie beyond that range.
+        for (int f = wave; f < NBC * KSC; f += NW) {
+            const int tb = f / KSC, ks = f % KSC;
+            if (32 * ks + 8 * gq >= 16 * (tb + 1))
+                *(uint4 *)(wsb + F::oPh + (f * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
+        }
+        __syncthreads();
 
-        if constexpr (NBD == 2 * NW) {
-            // ---- wave-local exports: wave w owns channels 32 w .. 32 w + 31 (one
-            //      fragment column): its W tiles, -W fragments, Q^ tiles and Q^
-            //      fragments need no other wave's results, so no barrier; wave 0
-            //      also forms T' and P^ = P T' ----------------------------------------------
-            const int ks = wave;
-            for (int jb = 0; jb < NBL; ++jb) {
-                w_tile(jb, 2 * wave);
-                w_tile(jb, 2 * wave + 1);
+        // ---- Phi = -(Yhat^T Kl) e^r as transposed tiles, BM x BN tiles per block ---
+        for (int pb = wave; pb < G::NPB; pb += NW) {
+            constexpr int BM = G::BM, BN = G::BN;
+            const int mb0 = BM * (pb % (NBD / BM)), nb0 = BN * (pb / (NBD / BM));
+            f32x4 acc[BM][BN];
+#pragma unroll
+            for (int a = 0; a < BM; ++a)
+#pragma unroll
+                for (int b = 0; b < BN; ++b) acc[a][b] = zero4();
+#pragma unroll
+            for (int s = 0; s < L / 32; ++s) {
+                bf16x8 xa8[BM], yb8[BN];
+#pragma unroll
+                for (int a = 0; a < BM; ++a) xa8[a] = frag_col(Kl + 32 * s * LDA + 16 * (mb0 + a), LDA, lane);
+#pragma unroll
+                for (int b = 0; b < BN; ++b) yb8[b] = frag_col(Kr + 32 * s * LDA + 16 * (nb0 + b), LDA, lane);
+#pragma unroll
+                for (int a = 0; a < BM; ++a)
+#pragma unroll
+                    for (int b = 0; b < BN; ++b) acc[a][b] = mma32(xa8[a], yb8[b], acc[a][b]);
             }
-            if (wave == 0)
-                for (int rb = 0; rb < NBL; ++rb) export_tv(rb);
-            wave_lds_sync();
-            for (int rb = 0; rb < NBL; ++rb)
-                st_frag(wsb + F::oWn + ((rb * KSD + ks) * 64 + lane) * 16,
-                        frag_row(Wst + 16 * rb * LDA + 32 * ks, LDA, lane));
-            for (int tb = 0; tb < NBC; ++tb) {
-                qh_tile(2 * wave, tb);
-                qh_tile(2 * wave + 1, tb);
-            }
-            if (wave == 0)
-                for (int t = 0; t < NBC * NBC; ++t) ph_tile(t % NBC, t / NBC);
-            wave_lds_sync();
-            for (int tb = 0; tb < NBC; ++tb)
-                st_frag(wsb + F::oQh + ((tb * KSD + ks) * 64 + lane) * 16,
-                        frag_row(Ql + 16 * tb * LDA + 32 * ks, LDA, lane));
-            if (wave == 0)
-                for (int rb = 0; rb < NBC; ++rb) export_ph(rb);
-        } else {
-            // ---- W tiles and T' over all waves; barrier; -W fragments, Q^ and P^
-            //      tiles; barrier; Q^ and P^ fragments ------------------------------------
-            for (int t = wave; t < NWT; t += NW) w_tile(t / NBD, t % NBD);
-            for (int rb = wave; rb < NBL; rb += NW) export_tv(rb);
-            __syncthreads();
-            constexpr int NWF = NBL * KSD, NQT = NBD * NBC, NPT2 = NBC * NBC;
-            for (int f = wave; f < NWF + NQT + NPT2; f += NW) {
-                if (f < NWF) {
-                    const int rb = f / KSD, ks = f % KSD;
-                    st_frag(wsb + F::oWn + (f * 64 + lane) * 16, frag_row(Wst + 16 * rb * LDA + 32 * ks, LDA, lane));
-                } else if (f < NWF + NQT) {
-                    const int t = f - NWF;
-                    qh_tile(t % NBD, t / NBD);
-                } else {
-                    const int t = f - NWF - NQT;
-                    ph_tile(t % NBC, t / NBC);
-                }
-            }
-            __syncthreads();
-            constexpr int NQF = NBC * KSD;
-            for (int f = wave; f < NQF + NBC; f += NW) {
-                if (f < NQF) {
-                    const int rb = f / KSD, ks = f % KSD;
-                    st_frag(wsb + F::oQh + (f * 64 + lane) * 16, frag_row(Ql + 16 * rb * LDA + 32 * ks, LDA, lane));
-                } else {
-                    export_ph(f - NQF);
+            // lane: Phi[n = 16 nb + l16][m = 16 mb + g4 + i]
+#pragma unroll
+            for (int a = 0; a < BM; ++a) {
+                const int mb = mb0 + a;
+                const f32x4 erm = *(const f32x4 *)(ers + 16 * mb + g4);
+#pragma unroll
+                for (int b = 0; b < BN; ++b) {
+                    const int nb = nb0 + b;
+                    const f32x4 v = acc[a][b];
+                    *(uint2 *)(wsb + F::oPhi + ((nb * KSD + mb / 2) * 64 + 16 * (2 * (mb & 1) + (gq >> 1)) + l16) * 16 +
+                               8 * (gq & 1)) =
+                        make_uint2(pack_bf16(-v[0] * erm[0], -v[1] * erm[1]), pack_bf16(-v[2] * erm[2], -v[3] * erm[3]));
                 }
             }
         }
-        // No barrier here: the exports above read only Wst, Ql, Tvs, Phs, Ps, MI,
-        // ers and sb, and the next item first writes any of those after its
-        // wide-chunk vote, which every wave reaches only after finishing its own
-        // exports; before the vote it writes only b', beta and gamma (by wave 0,
-        // after its own reads of sb) and the norm partials, which nothing above
-        // reads.
+        // ---- Qhat = (Ql - Z Kl) e^r as transposed tiles -------------------------------
+        for (int mb = wave; mb < NBD; mb += NW) {
+            const f32x4 erm = *(const f32x4 *)(ers + 16 * mb + g4);
+#pragma unroll
+            for (int tb = 0; tb < NBC; ++tb) {
+                const int pr = G::poff(tb) + l16 * G::pld(tb);
+                const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * mb + g4);
+                f32x4 acc = {-lo_bf16(q0.x), -hi_bf16(q0.x), -lo_bf16(q0.y), -hi_bf16(q0.y)};
+#pragma unroll
+                for (int s = 0; s < tb + 1; ++s)
+                    acc = mma32(frag_col(Kl + 32 * s * LDA + 16 * mb, LDA, lane),
+                                *(const bf16x8 *)(Zs + pr + 32 * s + 8 * gq), acc);
+                // lane: -Qhat[t = 16 tb + l16][m = 16 mb + g4 + i] / e^r
+                *(uint2 *)(wsb + F::oQh + ((tb * KSD + mb / 2) * 64 + 16 * (2 * (mb & 1) + (gq >> 1)) + l16) * 16 +
+                           8 * (gq & 1)) =
+                    make_uint2(pack_bf16(-acc[0] * erm[0], -acc[1] * erm[1]), pack_bf16(-acc[2] * erm[2], -acc[3] * erm[3]));
+            }
+        }
+        // No barrier here: the next item writes LDS before its first barrier only
+        // in b', beta, gamma (read above only by the Y and Z exports, before the
+        // last barrier) and in the layer form's norm partials (in M's region, not
+        // read since that barrier).
     }
 }
 
 // ---------------------------------------------------------------------------
 // Kernel 2: state pass.  One workgroup per (head, BV-column slice); the
 // slices of one head get workgroup ids congruent mod 8 (same XCD, one L2 for
-// the shared factor blocks).
-//
-// Every wave has one role, and each role fetches the operands it needs two
-// chunks ahead during the half of the chunk in which it has nothing else to
-// do, so the vector-memory traffic of the factors overlaps the products:
-//   U waves   (L/16):  U = T' V - W S for 16 rows of U, all slice columns;
-//                      fetch -W, T' while the state is updated
-//   state     (D/16):  S <- e^{G_C} S + Kr^T U for 16 state rows, then S^T
-//                      (bf16) for the next chunk; fetch Kr^T while U is formed
-//   output    (C/16):  o = Q^ S + P^ V for 16 tokens (transposed, so rows of o
-//                      leave as runs), Q^ = Ql - P W, P^ = P T'; fetch them
-//                      while the state is updated
-//   movers:            value slice and per-row decay in, outputs out.
-// (W, Kr^T and Q^ carry the per-channel e^r of the split, so S is unscaled.)
+// the shared factor blocks).  Per chunk c, one barrier, then
+//   state waves (D/16): 16 rows of S <- e^{G_C} S + Phi S + Psi V, then S^T (bf16)
+//                       for the next chunk;
+//   output waves (C/16): 16 tokens of o = Qhat S + Phat V (transposed, so rows of
+//                       o leave as 16-byte runs), and the value rows and outputs
+//                       between HBM and LDS.
+// Each wave fetches its own factor fragments two chunks ahead (chunk indices
+// clamped, never skipped, so every wait covers only those fetches).
 // ---------------------------------------------------------------------------
 template <int C, int D, int BV>
 struct K2G {
     using F = Fac<C, D>;
-    static constexpr int L = 2 * C;
-    static constexpr int NBL = F::NBL, NBC = F::NBC, NBD = F::NBD, NCB = BV / 16;
-    static constexpr int KSD = F::KSD, KSL = F::KSL;
-    static constexpr int NR = KSD + KSL;               // role operands per chunk
-    static constexpr int VU = C * BV / 8;              // 16-byte units of a value (or output) slice
-    static constexpr int SCU = D / 2;                  // 8-byte units of a chunk's decay e^{G_C}
-    static constexpr int NM = imax((VU + 63) / 64, (SCU + 63) / 64);
-    // wave order: U, state, output, movers
-    static constexpr int S0W = NBL, O0 = S0W + NBD, M0 = O0 + NBC, NW = M0 + NM, NT = 64 * NW;
+    static constexpr int NBC = F::NBC, NBD = F::NBD, NCB = BV / 16;
+    static constexpr int KSD = F::KSD, KSC = F::KSC;
+    static constexpr int NSW = NBD, NW = NBD + NBC, NT = 64 * NW;
     static_assert(NT <= 1024, "workgroup size");
-    static constexpr int LDT = D + 8, LDU = L + 8, LDV = BV + 8, LDO = BV + 8;
-    static constexpr int oSt = 0;                                   // S'^T [BV][LDT] bf16
-    static constexpr int oUt = align16(oSt + BV * LDT * 2);         // U^T  [BV][LDU] bf16
-    static constexpr int VR = 32;                                   // value rows (>= C; rows >= C stay zero)
-    static constexpr int szVs = align16(VR * LDV * 2);
-    static constexpr int oVs = align16(oUt + BV * LDU * 2);         // V    [2][VR][LDV] bf16
-    static constexpr int oOs = oVs + 2 * szVs;                      // o    [C][LDO] bf16
-    static constexpr int oSc = align16(oOs + C * LDO * 2);          // e^{G_C} [2][D] fp32
-    static constexpr int LDS = oSc + 2 * 4 * D;
+    static constexpr int LDT = D + 8, LDV = BV + 8, LDO = BV + 8;
+    static constexpr int VR = imax(C, 32);                          // value rows (rows >= C stay zero)
+    static constexpr int VPL = BV / 8;                              // 16-byte pieces per value row
+    static_assert(16 * VPL <= 64, "one value piece per lane per token block");
+    static constexpr int szSt = align16(BV * LDT * 2), szVs = align16(VR * LDV * 2);
+    static constexpr int oSt = 0;                                   // S^T [2][BV][LDT] bf16
+    static constexpr int oVs = oSt + 2 * szSt;                      // V   [2][VR][LDV] bf16
+    static constexpr int oOs = oVs + 2 * szVs;                      // o   [C][LDO] bf16 (per output wave: its rows)
+    static constexpr int LDS = oOs + align16(C * LDO * 2);
 };
 
-template <int NR, int KSL>
+template <int NF>
 struct FragSet {
-    bf16x8 R[NR];   // role operands: -W and T' (U), Q^ and P^ (output), Kr^T (state), v (movers)
-    uint2 sc;       // movers: one 8-byte piece of the chunk's decay
-    uint32_t pf[2]; // movers: one word of each of this slice's lines of a later chunk's block
+    bf16x8 R[NF];   // the role's factor fragments of one chunk
+    f32x4 dec;      // state role: e^{G_C} of its rows
+    uint4 v;        // output role: one 16-byte piece of the value slice
+    uint32_t pf[2]; // output role: L2 warm-up words
 };
 
 // L2 warm-up of the state pass (when the workspace exceeds the MALL): while
-// fetching chunk c's operands, the mover wave of slice j also reads one word
-// of every R-th 128-byte line (j, j + R, ...) of chunk c + WARM_AHEAD's block,
-// so the R slices of a head (same XCD, one L2) together bring that block into
-// L2 before its fragments are fetched, at 1/R of a block of extra traffic per
-// compute unit.  The words are consumed, unused, when the chunk's set is.
+// fetching chunk c's operands, output wave w of slice j also reads one word
+// of every (R NBC)-th 128-byte line of chunk c + WARM_AHEAD's block, so the R
+// slices of a head (same XCD, one L2) together bring that block into L2
+// before its fragments are fetched.  The words are consumed, unused, when the
+// chunk's set is.
 constexpr int WARM_AHEAD = 4;
 constexpr size_t WARM_MIN_BYTES = (size_t)256 << 20;   // MI355X MALL capacity
 
@@ -933,11 +948,9 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
     using G = K2G<C, D, BV>;
     using F = Fac<C, D>;
     using T = bf16;
-    constexpr int NCB = G::NCB, KSD = G::KSD, KSL = G::KSL, LDT = G::LDT, LDU = G::LDU;
-    constexpr int LDV = G::LDV, LDO = G::LDO, VU = G::VU, O0 = G::O0, S0W = G::S0W, M0 = G::M0;
+    constexpr int NCB = G::NCB, KSD = G::KSD, KSC = G::KSC, LDT = G::LDT, LDV = G::LDV, LDO = G::LDO;
+    constexpr int NSW = G::NSW, VPL = G::VPL;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    T *St = (T *)(smem + G::oSt);
-    T *Ut = (T *)(smem + G::oUt);
     T *Os = (T *)(smem + G::oOs);
 
     const int w = blockIdx.x, xcd = w & 7, slot = w >> 3;
@@ -955,101 +968,69 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = 4 * (lane >> 4), l16 = lane & 15;
 
+    // the value rows beyond the chunk (read by the k = 32 products at C = 16) are zero
     if constexpr (C < G::VR) {
-        // the value rows beyond the chunk are read by the k = 32 product: zero them
         for (int idx = tid; idx < 2 * (G::VR - C) * LDV; idx += G::NT) {
             const int bsel = idx / ((G::VR - C) * LDV), rem = idx % ((G::VR - C) * LDV);
             ((T *)(smem + G::oVs + bsel * G::szVs))[C * LDV + rem] = (T)0;
         }
     }
+    auto St = [&](int c) __attribute__((always_inline)) { return (T *)(smem + G::oSt + (c & 1) * G::szSt); };
+    auto Vs = [&](int c) __attribute__((always_inline)) { return (T *)(smem + G::oVs + (c & 1) * G::szVs); };
 
-    // One chunk loop per role: straight-line code with a fixed number of
-    // memory operations per chunk, so the waits before each use only cover
-    // operands fetched three chunks earlier (chunk indices clamped, never
-    // skipped).
     auto run = [&](auto role) __attribute__((always_inline)) {
-        constexpr int RL = decltype(role)::value;   // 0 U, 1 state, 2 output, 3 mover
-        constexpr bool RU = RL == 0, RS = RL == 1, RO = RL == 2, RM = RL == 3;
-        using Set = FragSet<G::NR, KSL>;
-        const int rb = RU ? wave : (RS ? wave - S0W : (RO ? wave - O0 : 0));   // row block of the role
-        const int mu = (wave - M0) * 64 + lane;                                 // mover unit
-        const bool mact = RM && mu < VU;
-        const int muc = mact ? mu : 0;
-        const int mtau = muc / (BV / 8), mn = 8 * (muc % (BV / 8));
+        constexpr bool RS = decltype(role)::value == 0;   // state role, else output role
+        constexpr int NF = KSD + KSC;
+        using Set = FragSet<NF>;
+        const int rb = RS ? wave : wave - NSW;            // row block: state rows or tokens
+        // output role: this lane's piece of the value slice (token 16 rb + vr, columns 8 vc ..)
+        const int vr = lane / VPL, vc = lane % VPL;
+        const bool vact = !RS && lane < 16 * VPL;
 
         auto load = [&](Set &s, int c) __attribute__((always_inline)) {
             const char *blk = wsh + (long)c * F::bytes;
-            if constexpr (RU) {
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks)
-                    s.R[ks] = ld_frag(blk + F::oWn + ((rb * KSD + ks) * 64 + lane) * 16);
-                s.R[KSD] = ld_frag(blk + F::oTv + (rb * 64 + lane) * 16);
-            }
             if constexpr (RS) {
 #pragma unroll
-                for (int ks = 0; ks < KSL; ++ks)
-                    s.R[ks] = ld_frag(blk + F::oKr + ((rb * KSL + ks) * 64 + lane) * 16);
-            }
-            if constexpr (RO) {
+                for (int ks = 0; ks < KSD; ++ks) s.R[ks] = ld_frag(blk + F::oPhi + ((rb * KSD + ks) * 64 + lane) * 16);
 #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks)
-                    s.R[ks] = ld_frag(blk + F::oQh + ((rb * KSD + ks) * 64 + lane) * 16);
-                s.R[KSD] = ld_frag(blk + F::oPh + (rb * 64 + lane) * 16);
-            }
-            if constexpr (RM) {
-                const int t = c * C + mtau, tc = t < Tlen ? t : Tlen - 1;
-                const bool ok = mact && t < Tlen;
+                for (int ks = 0; ks < KSC; ++ks) s.R[KSD + ks] = ld_frag(blk + F::oPsi + ((rb * KSC + ks) * 64 + lane) * 16);
+                s.dec = *(const f32x4 *)(blk + F::oDec + 4 * (16 * rb + g4));
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) s.R[ks] = ld_frag(blk + F::oQh + ((rb * KSD + ks) * 64 + lane) * 16);
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) s.R[KSD + ks] = ld_frag(blk + F::oPh + ((rb * KSC + ks) * 64 + lane) * 16);
+                const int t = c * C + 16 * rb + vr, tc = t < Tlen ? t : Tlen - 1;
+                const bool ok = vact && t < Tlen;
                 uint4 x;
                 if constexpr (VV) {
-                    x = *(const uint4 *)(vh + tc * HV + mn);
+                    x = *(const uint4 *)(vh + tc * HV + 8 * vc);
                 } else {
                     uint32_t y[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const int col = mn + j, cc = n0 + col < dv ? col : dv - 1 - n0;
+                        const int col = 8 * vc + j, cc = n0 + col < dv ? col : dv - 1 - n0;
                         y[j] = vh[tc * HV + cc];
                         if (n0 + col >= dv) y[j] = 0u;
                     }
                     x = make_uint4(y[0] | (y[1] << 16), y[2] | (y[3] << 16), y[4] | (y[5] << 16), y[6] | (y[7] << 16));
                 }
-                if (!ok) x = make_uint4(0u, 0u, 0u, 0u);
-                s.R[0] = __builtin_bit_cast(bf16x8, x);
-                s.sc = *(const uint2 *)(blk + F::oDec + 8 * (mu < G::SCU ? mu : G::SCU - 1));
+                s.v = ok ? x : make_uint4(0u, 0u, 0u, 0u);
                 s.pf[0] = s.pf[1] = 0u;
                 if (warm) {
                     const int cw = c + WARM_AHEAD < NC ? c + WARM_AHEAD : NC - 1;
                     const char *wb = wsh + (long)cw * F::bytes;
+                    const int stride = R * G::NBC;
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
-                        const int off = (slice + R * (64 * i + lane)) * 128;   // beyond the block: its last word
+                        const int off = (slice * G::NBC + rb + stride * (64 * i + lane)) * 128;
                         s.pf[i] = *(const uint32_t *)(wb + (off < F::bytes - 4 ? off : F::bytes - 4));
                     }
                 }
             }
         };
-        // movers: value slice and scales of chunk c -> LDS
         auto put_v = [&](const Set &s, int c) __attribute__((always_inline)) {
-            if (mact)
-                *(uint4 *)((T *)(smem + G::oVs + (c & 1) * G::szVs) + mtau * LDV + mn) = __builtin_bit_cast(uint4, s.R[0]);
-            if (mu < G::SCU) *(uint2 *)(smem + G::oSc + (c & 1) * 4 * D + 8 * mu) = s.sc;
-        };
-        auto flush = [&](int cp) __attribute__((always_inline)) {
-            const int t = cp * C + mtau;
-            if (mact && t < Tlen) {
-                const uint4 val = *(const uint4 *)(Os + mtau * LDO + mn);
-                T *dst = oh + t * HV + mn;
-                if constexpr (VV) {
-                    *(uint4 *)dst = val;
-                } else {
-                    const uint32_t y[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (n0 + mn + j < dv) dst[j] = (T)((y[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-                }
-            }
-        };
-        auto decay = [&](int c) __attribute__((always_inline)) {
-            return *(const f32x4 *)(smem + G::oSc + (c & 1) * 4 * D + 4 * (16 * rb + g4));
+            if (vact) *(uint4 *)(Vs(c) + (16 * rb + vr) * LDV + 8 * vc) = s.v;
         };
 
         // state rows 16 rb + g4 + i, columns n0 + 16 cb + l16 (state role)
@@ -1066,133 +1047,104 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 }
             }
         }
-        auto write_St = [&]() __attribute__((always_inline)) {
+        auto write_St = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
-                store4<T>(St + (16 * cb + l16) * LDT + 16 * rb + g4, S[cb][0], S[cb][1], S[cb][2], S[cb][3]);
+                store4<T>(St(c) + (16 * cb + l16) * LDT + 16 * rb + g4, S[cb][0], S[cb][1], S[cb][2], S[cb][3]);
         };
 
-        // T'V (U role) and P^V (output role) of the next chunk, formed during the
-        // half of this chunk in which those roles wait, so that their chains on
-        // the next chunk start from it
-        f32x4 pre[NCB];
+        // Phase c (one barrier): S_c^T is in St(c) and V_c in Vs(c).  The state
+        // waves write S_{c+1}^T to St(c + 1), the output waves write V_{c+1} to
+        // Vs(c + 1): both buffers were last read in phase c - 1.
         auto body = [&](Set &cur, Set &nxt, Set &far, int c) __attribute__((always_inline)) {
-            const int cf = c + 3 < NC ? c + 3 : NC - 1;   // chunk whose operands are fetched now
-            __syncthreads();   // S^T, the value slice of chunk c and its decay are in LDS
+            const int cf = c + 2 < NC ? c + 2 : NC - 1;   // chunk whose operands are fetched now
+            __syncthreads();
+            const T *Sc = St(c), *Vc = Vs(c);
+            // value products first: they do not wait for the state
             f32x4 acc[NCB];
-            const T *Vs = (const T *)(smem + G::oVs + (c & 1) * G::szVs);
-            if constexpr (RU) {
-                // U = T' V - W S  (16 rows, all slice columns) -> U^T in LDS
-                // (one instruction shape for the whole accumulation chain: at C = 16
-                // the k = 32 product reads 16 zero rows of the value buffer).  All
-                // LDS operands are read before the first product, so the chain pays
-                // one LDS latency instead of one per step.
-                bf16x8 sf[KSD][NCB];
-                if (c == 0) {
+            bf16x8 vf[KSC][NCB];
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) pre[cb] = mma32(cur.R[KSD], frag_col(Vs + 16 * cb, LDV, lane), zero4());
+            for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) vf[ks][cb] = frag_col(Vc + 32 * ks * LDV + 16 * cb, LDV, lane);
+            bf16x8 sf[KSD][NCB];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) sf[ks][cb] = frag_row(Sc + 16 * cb * LDT + 32 * ks, LDT, lane);
+            if constexpr (RS) {
+                // S <- e^{G_C} S + Psi V + Phi S  (rows 16 rb.., all slice columns)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    f32x4 a;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a[i] = cur.dec[i] * S[cb][i];
+#pragma unroll
+                    for (int ks = 0; ks < KSC; ++ks) a = mma32(cur.R[KSD + ks], vf[ks][cb], a);
+                    acc[cb] = a;
                 }
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) sf[ks][cb] = frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) acc[cb] = pre[cb];
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(cur.R[ks], sf[ks][cb], acc[cb]);
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    store4<T>(Ut + (16 * cb + l16) * LDU + 16 * rb + g4, acc[cb][0], acc[cb][1], acc[cb][2],
-                              acc[cb][3]);
-            }
-            if constexpr (RS) load(far, cf);
-            if constexpr (RO) {
-                // o^T = S^T Q^^T + V^T P^^T for the wave's 16 tokens -> rows of o in LDS
-                bf16x8 sf[KSD][NCB];
-                if (c == 0) {
+                for (int cb = 0; cb < NCB; ++cb) S[cb] = acc[cb];
+                if (c + 1 < NC) write_St(c + 1);
+                load(far, cf);
+            } else {
+                // o^T = V^T Phat^T + S^T Qhat^T for the wave's 16 tokens
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) pre[cb] = mma32(frag_col(Vs + 16 * cb, LDV, lane), cur.R[KSD], zero4());
+                for (int cb = 0; cb < NCB; ++cb) {
+                    f32x4 a = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < KSC; ++ks) a = mma32(vf[ks][cb], cur.R[KSD + ks], a);
+                    acc[cb] = a;
                 }
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) sf[ks][cb] = frag_row(St + 16 * cb * LDT + 32 * ks, LDT, lane);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) acc[cb] = pre[cb];
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(sf[ks][cb], cur.R[ks], acc[cb]);
+                if (c + 1 < NC) put_v(nxt, c + 1);
+                asm volatile("" ::"v"(cur.pf[0]), "v"(cur.pf[1]));   // the warm-up words, consumed
+                // the wave's own 16 token rows: staged in LDS, then written as
+                // 16-byte row pieces (the rows are this wave's alone: no barrier)
                 const int tr = 16 * rb + l16;
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
                     store4<T>(Os + tr * LDO + 16 * cb + g4, acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
-            }
-            if constexpr (RM) {
-                if (c + 1 < NC) put_v(nxt, c + 1);
-                asm volatile("" ::"v"(cur.pf[0]), "v"(cur.pf[1]));   // the warm-up words, consumed
+                wave_lds_sync();
                 load(far, cf);
-            }
-            __syncthreads();   // U^T and the outputs complete; S^T no longer read
-            if constexpr (RU || RO) {
-                load(far, cf);
-                // the next chunk's value slice is in LDS (written by the movers before
-                // the barrier above, into the other buffer)
-                if (c + 1 < NC) {
-                    const T *Vn = (const T *)(smem + G::oVs + ((c + 1) & 1) * G::szVs);
+                const int t = c * C + 16 * rb + vr;
+                if (vact && t < Tlen) {
+                    const uint4 val = *(const uint4 *)(Os + (16 * rb + vr) * LDO + 8 * vc);
+                    T *dst = oh + t * HV + 8 * vc;
+                    if constexpr (VV) {
+                        *(uint4 *)dst = val;
+                    } else {
+                        const uint32_t y[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) {
-                        const bf16x8 vn = frag_col(Vn + 16 * cb, LDV, lane);
-                        pre[cb] = RU ? mma32(nxt.R[KSD], vn, zero4()) : mma32(vn, nxt.R[KSD], zero4());
+                        for (int j = 0; j < 8; ++j)
+                            if (n0 + 8 * vc + j < dv) dst[j] = (T)((y[j >> 1] >> (16 * (j & 1))) & 0xffffu);
                     }
                 }
             }
-            if constexpr (RS) {
-                // S <- e^{G_C} S + Kr^T U; S^T of the next chunk
-                const f32x4 dc = decay(c);
-                bf16x8 uf[KSL][NCB];
-#pragma unroll
-                for (int ks = 0; ks < KSL; ++ks)
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) uf[ks][cb] = frag_row(Ut + 16 * cb * LDU + 32 * ks, LDU, lane);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    f32x4 a;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) a[i] = dc[i] * S[cb][i];
-#pragma unroll
-                    for (int ks = 0; ks < KSL; ++ks) a = mma32(cur.R[ks], uf[ks][cb], a);
-                    S[cb] = a;
-                }
-                if (c + 1 < NC) write_St();
-            }
-            // stores last: nothing after them waits on the vector-memory counter
-            if constexpr (RM) flush(c);
         };
 
-        // four operand sets in rotation: the chunk in use, the next two, and
-        // the one being fetched
-        Set A, B, X, Y;
+        // three operand sets in rotation: the chunk in use, the next, and the one
+        // being fetched
+        Set A, B, X;
         load(A, 0);
         load(B, NC > 1 ? 1 : 0);
-        load(X, NC > 2 ? 2 : NC - 1);
-        if constexpr (RM) put_v(A, 0);
-        if constexpr (RS) write_St();
+        if constexpr (RS) write_St(0);
+        else put_v(A, 0);
         int c = 0;
-        for (; c + 4 <= NC; c += 4) {
-            body(A, B, Y, c);
+        for (; c + 3 <= NC; c += 3) {
+            body(A, B, X, c);
             body(B, X, A, c + 1);
-            body(X, Y, B, c + 2);
-            body(Y, A, X, c + 3);
+            body(X, A, B, c + 2);
         }
-        if (c < NC) body(A, B, Y, c);
+        if (c < NC) body(A, B, X, c);
         if (c + 1 < NC) body(B, X, A, c + 1);
-        if (c + 2 < NC) body(X, Y, B, c + 2);
 
         if constexpr (RS) {
             if (S_final) {
@@ -1210,10 +1162,8 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
         }
     };
 
-    if (wave < S0W) run(std::integral_constant<int, 0>{});
-    else if (wave < O0) run(std::integral_constant<int, 1>{});
-    else if (wave < M0) run(std::integral_constant<int, 2>{});
-    else run(std::integral_constant<int, 3>{});
+    if (wave < NSW) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1265,7 +1215,8 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     const long items = (long)BH * NC;
-    const int grid1 = (int)(items < 2L * ncu ? items : 2L * ncu);   // two per compute unit (LDS)
+    const long per_cu = G1::NW == 8 ? 1 : 2;   // workgroups per compute unit (LDS)
+    const int grid1 = (int)(items < per_cu * ncu ? items : per_cu * ncu);
     if (ev && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
     hipLaunchKernelGGL(k1, dim3((unsigned)grid1), dim3(G1::NT), G1::LDS, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)e, decay, A_log, dt_bias, beta, gamma, (char *)ws,
@@ -1290,6 +1241,7 @@ size_t bf16_ws_bytes(int B, int Tlen, int H, int dk, int dv, int chunk) {
 #define EDA_WS(CC, DD) if (chunk == CC && D == DD) return b16::ws_bytes<CC, DD>(B, Tlen, H);
     EDA_WS(16, 32) EDA_WS(16, 64) EDA_WS(16, 128)
     EDA_WS(32, 32) EDA_WS(32, 64) EDA_WS(32, 128)
+    EDA_WS(64, 32) EDA_WS(64, 64) EDA_WS(64, 128)
 #undef EDA_WS
     return 0;
 }
@@ -1310,6 +1262,8 @@ hipError_t launch_bf16(const void *q, const void *k, const void *e, const void *
     EDA_GO(16, 128, 16) EDA_GO(16, 128, 32)
     EDA_GO(32, 32, 16) EDA_GO(32, 32, 32) EDA_GO(32, 64, 16) EDA_GO(32, 64, 32)
     EDA_GO(32, 128, 16) EDA_GO(32, 128, 32)
+    EDA_GO(64, 32, 16) EDA_GO(64, 32, 32) EDA_GO(64, 64, 16) EDA_GO(64, 64, 32)
+    EDA_GO(64, 128, 16) EDA_GO(64, 128, 32)
 #undef EDA_GO
     return hipErrorInvalidValue;
 }

@@ -51,11 +51,22 @@ def test_status_strings():
 def test_workspace_size():
     lib = eda.load_library()
     ws = lib.eda_fwd_chunked_workspace_size
-    bf = ws(4, 2048, 16, 128, 128, 1, 32)                     # bf16 chunk factors
-    assert bf == 4 * 16 * (2048 // 32) * 47616                # one padded block per chunk and head
-    assert ws(4, 2048 + 1, 16, 128, 128, 1, 32) == bf + 4 * 16 * 47616   # a ragged tail is a chunk
+    # bf16: one block per chunk and head holding Phi (d_k x d_k), Psi (d_k x C),
+    # Qhat (C x d_k), Phat (C x C) as 1 KB operand fragments and e^{G_C} (fp32)
+    frag = lambda C, D: (D // 16) * (D // 32) + (D // 16) * -(-C // 32) + (C // 16) * (D // 32) + (C // 16) * -(-C // 32)
+    blk = lambda C, D: -(-(frag(C, D) * 1024 + 4 * D) // 256) * 256
+    assert (blk(64, 128), blk(32, 128), blk(16, 128)) == (74240, 51712, 46592)
+    bf = ws(4, 2048, 16, 128, 128, 1, 32)
+    assert bf == 4 * 16 * (2048 // 32) * blk(32, 128)
+    assert ws(4, 2048 + 1, 16, 128, 128, 1, 32) == bf + 4 * 16 * blk(32, 128)   # a ragged tail is a chunk
+    bf64 = ws(4, 2048, 16, 128, 128, 1, 64)
+    assert bf64 == 4 * 16 * (2048 // 64) * blk(64, 128)
+    assert ws(4, 2048, 16, 128, 128, 1, 0) == bf64            # 0 selects the default chunk, 64
+    assert ws(1, 100, 3, 64, 40, 1, 16) == 3 * 7 * blk(16, 64)   # head dims padded to 32, 64 or 128
     big = ws(4, 2048, 16, 128, 128, 0, 32)                    # fp32 chunk factors
     assert big > 0
+    # fp32 computes chunk 64 as 32-token chunks (same workspace)
+    assert ws(4, 2048, 16, 128, 128, 0, 64) == big
     assert ws(4, 2048, 16, 128, 128, 0, 0) == big            # 0 selects the default chunk
     assert ws(4, 4096, 16, 128, 128, 0, 32) == 2 * big        # linear in the chunk count
     assert ws(1, 1, 1, 2, 1, 0, 16) > 0
@@ -95,7 +106,7 @@ def call_chunked(a):
     ("q", None, 1), ("v", None, 1), ("alpha", None, 1), ("o", None, 1),
     ("dt", 5, 3),
     ("B", 0, 2), ("T", -1, 2), ("dk", 0, 2),
-    ("dk", 129, 5), ("dv", 200, 5), ("chunk", 64, 5), ("chunk", 7, 5),
+    ("dk", 129, 5), ("dv", 200, 5), ("chunk", 128, 5), ("chunk", 7, 5),
     ("q", fake(1, 2), 4), ("alpha", fake(5, 2), 4), ("S0", fake(8, 4), 4), ("o", fake(9, 8), 4),
     ("ws", fake(11, 128), 4),
     ("ws", None, 6), ("wsb", 1024, 6),

@@ -50,6 +50,10 @@ def ref_dplr(y):
     ("bf16", 1, 333, 2, 128, 128, 16, True),
     ("bf16", 1, 150, 3, 64, 64, 32, False),
     ("bf16", 1, 100, 2, 100, 80, 32, True),     # element-wise loads (d_k < 128)
+    ("f32", 1, 130, 2, 32, 16, 64, True),
+    ("bf16", 2, 200, 2, 128, 128, 64, True),
+    ("bf16", 1, 190, 3, 64, 64, 64, False),
+    ("bf16", 1, 140, 2, 100, 80, 64, True),
 ])
 def test_dplr_chunked(dtype, B, T, H, dk, dv, chunk, qed):
     say(f"dplr chunked {dtype} B={B} T={T} H={H} dk={dk} dv={dv} chunk={chunk} qed={qed}")

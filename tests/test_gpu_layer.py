@@ -44,6 +44,10 @@ CASES = [
     ("bf16", 1, 333, 1, 2, 128, 128, 16),
     ("bf16", 1, 200, 2, 2, 64, 64, 32),
     ("bf16", 1, 130, 1, 3, 100, 80, 32),     # d_k < 128: the element-wise load path
+    ("f32", 1, 150, 1, 2, 64, 48, 64),
+    ("bf16", 2, 200, 2, 4, 128, 128, 64),
+    ("bf16", 1, 129, 1, 2, 64, 64, 64),
+    ("bf16", 1, 140, 1, 3, 100, 80, 64),
 ]
 
 
@@ -70,16 +74,17 @@ def test_layer_unaligned_inputs():
     check(to64(o), to64(S), ro, rS, "bf16", "layer unaligned q")
 
 
-def test_layer_gate_floor_wide_chunks():
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_layer_gate_floor_wide_chunks(chunk):
     # every retention at the safe gate's floor e^-5: 32 tokens decay by e^-160,
     # past the split-exponent range, so every chunk takes the element-wise path
-    say("layer chunked bf16 at the gate floor")
+    say(f"layer chunked bf16 at the gate floor chunk={chunk}")
     x = make_layer_inputs(1, 160, 1, 2, 128, 128, "bf16", seed=5)
     x["a"] = torch.full_like(x["a"], 40.0)
     x["A_log"] = torch.full_like(x["A_log"], float(np.log(16.0)))
     al = oracle.eda_ref_safe_gate(x["a"], x["A_log"], x["dt_bias"])
     assert np.allclose(al, np.exp(-5.0), rtol=1e-6)
-    o, S = run_layer(dev(x))
+    o, S = run_layer(dev(x), chunk=chunk)
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
     ro, rS = ref_layer(x)
     check(to64(o), to64(S), ro, rS, "bf16", "layer gate floor")

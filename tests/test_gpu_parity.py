@@ -13,7 +13,7 @@ import torch
 
 import recurrent_memory_amd as eda
 import oracle
-from eda_inputs import WORKLOADS, hand_example, make_inputs, make_workload
+from eda_inputs import OVERLAP_KINDS, WORKLOADS, hand_example, make_inputs, make_overlap_inputs, make_workload
 from _helpers import check, oracle_heads, to64
 
 pytestmark = pytest.mark.gpu
@@ -44,7 +44,7 @@ def full_oracle(x):
 # the hand-worked example, exact
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_hand_example_chunked(dtype, chunk):
     say(f"hand example chunked {dtype} chunk={chunk}")
     x = hand_example()
@@ -76,7 +76,7 @@ def test_hand_example_decode(dtype):
 # ---------------------------------------------------------------------------
 # small and ragged cases, every element
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_tiny_workload_fp32(chunk):
     w = WORKLOADS["tiny"]
     say(f"tiny fp32 chunk={chunk}")
@@ -104,7 +104,9 @@ def test_tiny_workload_fp32_decode():
 
 
 RAGGED = [(1, 1, 1, 16), (1, 1, 1, 32), (2, 15, 3, 16), (1, 33, 2, 32), (2, 100, 2, 16),
-          (1, 64, 1, 32), (1, 65, 1, 32), (3, 47, 1, 16)]
+          (1, 64, 1, 32), (1, 65, 1, 32), (3, 47, 1, 16),
+          (1, 1, 1, 64), (1, 63, 1, 64), (2, 64, 2, 64), (1, 65, 2, 64), (1, 127, 1, 64),
+          (2, 129, 1, 64), (1, 200, 3, 64)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -137,14 +139,15 @@ def test_head_dims_fp32(dk, dv):
 
 
 def test_chunk_sizes_agree_bf16():
-    say("chunk 16 vs 32 bf16")
+    """Chunks of 16, 32 and 64 tokens each match the oracle on the same
+    inputs (the chunk size is an implementation parameter)."""
+    say("chunk 16 vs 32 vs 64 bf16")
     x = dev(make_inputs(2, 300, 4, 128, 128, "bf16", seed=5, s0_std=0.02))
-    o16, S16 = run_chunked(x, chunk=16)
-    o32, S32 = run_chunked(x, chunk=32)
     xo = {n: (None if t is None else t.cpu()) for n, t in x.items()}
     ro, rS = full_oracle(xo)
-    check(to64(o16), to64(S16), ro, rS, "bf16", "chunk16")
-    check(to64(o32), to64(S32), ro, rS, "bf16", "chunk32")
+    for chunk in (16, 32, 64):
+        o, S = run_chunked(x, chunk=chunk)
+        check(to64(o), to64(S), ro, rS, "bf16", f"chunk{chunk}")
 
 
 def test_resume_and_inplace_state():
@@ -183,27 +186,81 @@ def test_prefill_then_decode_handoff():
     check(to64(torch.cat(outs, 1)), to64(S), ro, rS, "bf16", "handoff")
 
 
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 @pytest.mark.parametrize("kind", ["floor", "one"])
-def test_stress_decay_extremes(kind):
+def test_stress_decay_extremes(kind, chunk):
     """alpha at the safe gate's floor e^-5 on every channel (the chunk's decay
     leaves fp32 range, exercising the exact wide-decay path) and alpha = 1."""
-    say(f"stress alpha={kind}")
+    say(f"stress alpha={kind} chunk={chunk}")
     x = make_inputs(1, 4096, 2, 128, 128, "bf16", seed=5)
     x["alpha"] = torch.full_like(x["alpha"], math.exp(-5.0) if kind == "floor" else 1.0)
     ro, rS = full_oracle(x)
-    o, S = run_chunked(dev(x))
+    o, S = run_chunked(dev(x), chunk=chunk)
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
-    check(to64(o), to64(S), ro, rS, "bf16", f"stress {kind}")
+    check(to64(o), to64(S), ro, rS, "bf16", f"stress {kind} chunk={chunk}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_strong_decay_inside_split_range(chunk):
+    """Half of the key channels decay by e^-100 over each chunk: still inside
+    the split-exponent range (the element-wise path starts past e^-120), where
+    the split operands reach e^{50} and a product of two of them would leave
+    the fp32 range; the other half barely decays."""
+    say(f"strong decay inside the split range chunk={chunk}")
+    x = make_inputs(2, 3 * chunk + 9, 2, 128, 128, "bf16", seed=41, s0_std=0.5)
+    x["alpha"][..., ::2] = math.exp(-100.0 / chunk)
+    x["alpha"][..., 1::2] = 0.999
+    ro, rS = full_oracle(x)
+    o, S = run_chunked(dev(x), chunk=chunk)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    check(to64(o), to64(S), ro, rS, "bf16", f"strong decay chunk={chunk}")
+
+
+# ---------------------------------------------------------------------------
+# address overlap: the erase and write addresses interact through Eq. (16)'s
+# cross term gamma beta (k^T e) k e^T, which independent random directions
+# leave small (|cos| ~ 0.07); gates at their limits
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("kind", OVERLAP_KINDS)
+def test_address_overlap_chunked(kind, chunk, dtype):
+    """d = 128, an initial state, three chunks and a ragged tail."""
+    T = 3 * chunk + 5
+    say(f"overlap {kind} {dtype} chunk={chunk} T={T}")
+    x = make_overlap_inputs(kind, 2, T, 2, 128, 128, dtype, seed=31, s0_std=0.5)
+    ro, rS = full_oracle(x)
+    o, S = run_chunked(dev(x), chunk=chunk)
+    check(to64(o), to64(S), ro, rS, dtype, f"overlap {kind} chunk={chunk}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", OVERLAP_KINDS)
+def test_address_overlap_decode(kind, dtype):
+    """The decode step on the same recipes, 40 steps in place."""
+    steps = 40
+    say(f"overlap decode {kind} {dtype} steps={steps}")
+    x = make_overlap_inputs(kind, 64, steps, 4, 128, 128, dtype, seed=33, s0_std=0.5)
+    ro, rS = full_oracle(x)
+    xd = dev(x)
+    S = xd["S0"].clone()
+    outs = []
+    for t in range(steps):
+        o, S = eda.recurrent_step(*(xd[n][:, t].contiguous() for n in
+                                    ("q", "k", "e", "v", "alpha", "beta", "gamma")), S, inplace=True)
+        outs.append(o.clone())
+    torch.cuda.synchronize()
+    check(to64(torch.stack(outs, 1)), to64(S), ro, rS, dtype, f"overlap decode {kind}")
 
 
 # ---------------------------------------------------------------------------
 # full-size workloads, sampled heads
 # ---------------------------------------------------------------------------
-def sampled_check(name, n_heads, seed=0):
+def sampled_check(name, n_heads, seed=0, chunk=0):
     w = WORKLOADS[name]
-    say(f"{name} full size B={w.B} T={w.T} H={w.H}, {n_heads} sampled heads")
+    say(f"{name} full size B={w.B} T={w.T} H={w.H} chunk={chunk}, {n_heads} sampled heads")
     x = make_workload(w, device=DEV)
-    o, S = run_chunked(x, chunk=0)
+    o, S = run_chunked(x, chunk=chunk)
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
     rng = np.random.default_rng(seed)
     heads = sorted({(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(n_heads)})
@@ -213,7 +270,7 @@ def sampled_check(name, n_heads, seed=0):
     gs = np.concatenate([to64(S[b, h]) for b, h in heads])
     ro = np.concatenate([r[0] for r in refs])
     rs = np.concatenate([r[1] for r in refs])
-    return check(go, gs, ro, rs, "bf16", f"{name} heads={heads}")
+    return check(go, gs, ro, rs, "bf16", f"{name} chunk={chunk} heads={heads}")
 
 
 def test_timed_entry_point_matches_plain_call():
@@ -238,7 +295,7 @@ def test_large_workspace_ragged_slices():
     factor fetches) with a ragged tail, d_v = 100 (seven 16-column slices per
     head, the last one partial) and an initial state; sampled heads against
     the oracle."""
-    B, T, H, dk, dv = 1, 32768 + 17, 7, 128, 100
+    B, T, H, dk, dv = 1, 32768 + 17, 8, 128, 100
     need = eda.workspace_size(B, T, H, dk, dv, torch.bfloat16)
     assert need > 256 << 20
     say(f"large workspace B={B} T={T} H={H} dk={dk} dv={dv} ({need >> 20} MB)")
@@ -276,8 +333,9 @@ def test_maximum_size_heads_match_single_head_runs():
     torch.cuda.empty_cache()
 
 
-def test_train_workload_sampled():
-    sampled_check("train", 8)
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_train_workload_sampled(chunk):
+    sampled_check("train", 8, chunk=chunk)
 
 
 @pytest.mark.slow
