@@ -25,18 +25,21 @@ configuration), with 16 heads (the metric's H = 16), and at T = 131072 with 16
 heads (the very-long configuration), tokens/s each.
 
 Algorithmic work (d_k = d_v = d, C tokens per chunk, L = 2C sub-steps; each
-token is an erase sub-step and a delta sub-step), per chunk and head:
-  chunk factors: L^2 d (decayed Gram) + L^3/6 (triangular inverse)
-                 + L^2 d (W factor) + C L d (query-key products)  multiply-adds
-  state pass:    L d^2 (W S) + L C d (value part of U) + C d^2 (query-state
-                 product) + C L d (intra-chunk output) + L d^2 (state update)
-(counted once, however often a kernel recomputes them).  Algorithmic bytes per
-token and head: the factor kernel must read q, k, e (storage type), alpha
-(fp32 per key channel), beta and gamma (fp32); the state pass must read v and
-write o (storage type), plus the fp32 initial state read and final state
-written once per head.  The whole path moves the sum (1800 B per token-head
-for bf16, d = 128).  Decode moves the fp32 state in and out once per step
-(2 d_k d_v 4 bytes) plus the token's inputs and output.
+token is an erase sub-step and a delta sub-step), per chunk and head, in the
+canonical chunk formulation:
+  factor side: L^2 d (decayed Gram) + L^3/6 (triangular inverse)
+               + L^2 d (W factor) + C L d (query-key products)  multiply-adds
+  state side:  L d^2 (W S) + L C d (value part of U) + C d^2 (query-state
+               product) + C L d (intra-chunk output) + L d^2 (state update)
+(counted once, however the kernels regroup them: the factor kernel here also
+forms the chunk's state map Phi = -Khat^T W and Psi = Khat^T T', so the state
+pass issues d^2 d_v + d C d_v + C d d_v + C^2 d_v per chunk instead).
+Algorithmic bytes per token and head: the factor kernel must read q, k, e
+(storage type), alpha (fp32 per key channel), beta and gamma (fp32); the state
+pass must read v and write o (storage type), plus the fp32 initial state read
+and final state written once per head.  The whole path moves the sum (1800 B
+per token-head for bf16, d = 128).  Decode moves the fp32 state in and out
+once per step (2 d_k d_v 4 bytes) plus the token's inputs and output.
 Peaks: MI355X dense bf16 matrix 2.5 PFLOP/s, fp32 matrix 157.3 TFLOP/s,
 HBM3E 8 TB/s.  `traffic` is the measured HBM bytes per launch of the dominant
 kernel (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known
@@ -149,6 +152,102 @@ def time_events(torch, fn, reps: int) -> float:
     return start.elapsed_time(end) / reps
 
 
+def measure_chunked(torch, eda, x, w, chunk: int, steps: int, warmup: int = 3) -> dict:
+    """One chunked forward per step on resident inputs: wall-clock tokens/s
+    over `steps` steps, then the same steps through eda_fwd_chunked_timed for
+    each kernel's average duration (HIP events on the launch stream), and the
+    path- and kernel-level fractions of the bf16 matrix and HBM peaks."""
+    dev = x["q"].device
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    es = 2 if w.dtype == "bf16" else 4
+    o = torch.empty((B, T, H, dv), dtype=x["q"].dtype, device=dev)
+    S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    need = eda.workspace_size(B, T, H, dk, dv, x["q"].dtype, chunk)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+
+    def step(events=None):
+        eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
+                        chunk=chunk, out=o, S_final=S_final, workspace=ws, events=events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(s)
+    for _ in range(steps):
+        step()
+    ev1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_kernel = ev0.elapsed_time(ev1) / steps
+    # per-kernel durations: the same steps through the timed entry point
+    trip = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for t3 in trip:
+        for ev in t3:
+            ev.record(s)   # materialise the events before handing them over
+    torch.cuda.synchronize()
+    for t3 in trip:
+        step(events=[ev.cuda_event for ev in t3])
+    torch.cuda.synchronize()
+    ms_k1 = sum(t3[0].elapsed_time(t3[1]) for t3 in trip) / steps
+    ms_k2 = sum(t3[1].elapsed_time(t3[2]) for t3 in trip) / steps
+
+    d = dk
+    n_ch = B * H * ((T + chunk - 1) // chunk)
+    tb = token_bytes(dk, dv, es)
+    peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    state_io = (2 if x["S0"] is not None else 1) * B * H * dk * dv * 4
+    work = {
+        "factors": dict(flop=2 * intra_macs_per_chunk_head(chunk, d) * n_ch,
+                        bytes=tb["factors"] * B * T * H, ms=ms_k1),
+        "state": dict(flop=2 * state_macs_per_chunk_head(chunk, d) * n_ch,
+                      bytes=tb["state"] * B * T * H + state_io, ms=ms_k2),
+    }
+    names = dict(factors="eda_bf16_factors", state="eda_bf16_state") if w.dtype == "bf16" else \
+        dict(factors="eda_chunk_intra", state="eda_chunk_state")
+
+    def roof(kind: str) -> dict:
+        wk = work[kind]
+        sec = wk["ms"] * 1e-3
+        # the binding roofline at the algorithmic level is the one with the larger floor
+        mfma = wk["flop"] / (peak_mm * 1e12) >= wk["bytes"] / (PEAK_HBM_GBS * 1e9)
+        tf, gb = wk["flop"] / sec / 1e12, wk["bytes"] / sec / 1e9
+        if mfma:
+            r = dict(kernel=names[kind], bound="mfma", achieved=round(tf, 3), peak=peak_mm,
+                     unit="TFLOP/s", frac=round(tf / peak_mm, 5))
+        else:
+            r = dict(kernel=names[kind], bound="hbm", achieved=round(gb, 2), peak=PEAK_HBM_GBS,
+                     unit="GB/s", frac=round(gb / PEAK_HBM_GBS, 5))
+        r.update(ms=round(wk["ms"], 5), algorithmic_bytes=wk["bytes"], algorithmic_flop=wk["flop"],
+                 mfma_frac=round(tf / peak_mm, 5), hbm_frac=round(gb / PEAK_HBM_GBS, 5),
+                 rocprof_mfma=measured_mfma(names[kind], w.name) if chunk == eda.DEFAULT_CHUNK else None)
+        return r
+
+    kernels = {k: roof(k) for k in work}
+    flop = work["factors"]["flop"] + work["state"]["flop"]
+    byts = tb["chunked"] * B * T * H + state_io
+    sec = ms_kernel * 1e-3
+    tflops, gbs = flop / sec / 1e12, byts / sec / 1e9
+    # path-level binding roofline: the larger of the two floors over the path's time
+    mfma_bound = flop / (peak_mm * 1e12) >= byts / (PEAK_HBM_GBS * 1e9)
+    path_roof = (dict(bound="mfma", achieved=round(tflops, 3), peak=peak_mm, unit="TFLOP/s",
+                      frac=round(tflops / peak_mm, 5)) if mfma_bound else
+                 dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=round(gbs / PEAK_HBM_GBS, 5)))
+    dom = max(work, key=lambda k: work[k]["ms"])
+    return dict(chunk=chunk, value=round(B * T * steps / wall, 1), unit="tokens/s",
+                ms_per_step=round(wall * 1e3 / steps, 5), kernel_ms=round(ms_kernel, 5),
+                token_heads_per_s=round(B * T * H * steps / wall, 1),
+                canonical_flop=flop, compulsory_bytes=byts,
+                mfma_tflops=round(tflops, 3), mfma_frac=round(tflops / peak_mm, 5),
+                hbm_gbs=round(gbs, 2), hbm_frac=round(gbs / PEAK_HBM_GBS, 5),
+                canonical_flop_per_token_head=flop / (B * T * H),
+                compulsory_bytes_per_token_head=tb["chunked"], path_roofline=path_roof,
+                dominant=dom, kernels=kernels)
+
+
 def bench_layer(torch, eda, dev, chunk: int, steps: int) -> dict:
     """Layer form (fused prologue) against the unfused pipeline on the same
     inputs, and the layer-form decode step."""
@@ -249,32 +348,22 @@ def bench_dplr(torch, eda, dev, chunk: int, steps: int) -> dict:
 
 def bench_long(torch, eda, dev, chunk: int) -> dict:
     """The chunked forward at the long-context workloads: T = 32768 with 32
-    and 16 heads, and T = 131072 with 16 heads (sequential chains of 1024 and
-    4096 chunks per head)."""
+    and 16 heads, and T = 131072 with 16 heads; tokens/s, both fractions of
+    the path and the per-kernel split for each."""
     from eda_inputs import WORKLOADS, make_workload
 
     out = {}
     for name in ("long", "long_h16", "verylong"):
         w = WORKLOADS[name]
         x = make_workload(w, device=dev)
-        o = torch.empty((w.B, w.T, w.H, w.dv), dtype=x["q"].dtype, device=dev)
-        Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
-        ws = torch.empty(eda.workspace_size(w.B, w.T, w.H, w.dk, w.dv, x["q"].dtype, chunk), dtype=torch.uint8,
-                         device=dev)
-
-        def run():
-            eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
-                            chunk=chunk, out=o, S_final=Sf, workspace=ws)
-
-        run()
-        torch.cuda.synchronize()
-        ms = time_events(torch, run, 5)
+        r = measure_chunked(torch, eda, x, w, chunk, steps=5, warmup=1)
         s0 = f"S0 ~ N(0, {w.s0_std})" if w.s0_std > 0 else "S0 = 0"
-        out[name] = dict(workload=f"{name}: B={w.B} T={w.T} H={w.H} d_k=d_v={w.dk} {w.dtype}, {s0}",
-                         value=round(w.B * w.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 4),
-                         token_heads_per_s=round(w.B * w.T * w.H / (ms * 1e-3), 1))
-        print(f"[bench] {name} {ms:.3f} ms", file=sys.stderr, flush=True)
-        del x, o, Sf, ws
+        r["workload"] = f"{name}: B={w.B} T={w.T} H={w.H} d_k=d_v={w.dk} {w.dtype}, {s0}, chunk={chunk}"
+        out[name] = r
+        print(f"[bench] {name} {r['kernel_ms']:.3f} ms (factors {r['kernels']['factors']['ms']:.3f}, "
+              f"state {r['kernels']['state']['ms']:.3f}); mfma {100 * r['mfma_frac']:.1f} %, "
+              f"hbm {100 * r['hbm_frac']:.1f} %", file=sys.stderr, flush=True)
+        del x
         torch.cuda.empty_cache()
     return out
 
@@ -325,6 +414,7 @@ def main() -> int:
     ap.add_argument("--no-dplr", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-chunk-sweep", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -351,103 +441,32 @@ def main() -> int:
     chunk = args.chunk or eda.DEFAULT_CHUNK
     x = make_workload(w, device=dev)
     B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
-    es = 2 if w.dtype == "bf16" else 4
-    o = torch.empty((B, T, H, dv), dtype=x["q"].dtype, device=dev)
-    S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    need = eda.workspace_size(B, T, H, dk, dv, x["q"].dtype, chunk)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
-
-    def step():
-        eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
-                        chunk=chunk, out=o, S_final=S_final, workspace=ws)
-
     print(f"[bench] workload {w.name}: B={B} T={T} H={H} d_k={dk} d_v={dv} {w.dtype} chunk={chunk}",
           file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # timed region: wall clock around K steps, and HIP events on the launch
-    # stream around the whole loop
-    s = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(s)
-    for _ in range(args.steps):
-        step()
-    ev1.record(s)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_kernel = ev0.elapsed_time(ev1) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
-    tokens = B * T
-    value = tokens * args.steps / wall
-    print(f"[bench] {ms_per_step:.4f} ms/step (events {ms_kernel:.4f} ms), {value:.4g} tokens/s",
+    path = measure_chunked(torch, eda, x, w, chunk, args.steps, args.warmup)
+    value, ms_per_step, tokens = path["value"], path["ms_per_step"], B * T
+    print(f"[bench] {ms_per_step:.4f} ms/step (events {path['kernel_ms']:.4f} ms), {value:.4g} tokens/s",
           file=sys.stderr, flush=True)
-
-    # per-kernel durations: the same K steps again through the timed entry
-    # point (HIP events recorded by the library on the launch stream)
-    trip = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for t3 in trip:
-        for ev in t3:
-            ev.record(s)   # materialise the events before handing them over
-    torch.cuda.synchronize()
-    for t3 in trip:
-        eda.fwd_chunked(x["q"], x["k"], x["e"], x["v"], x["alpha"], x["beta"], x["gamma"], x["S0"],
-                        chunk=chunk, out=o, S_final=S_final, workspace=ws,
-                        events=[ev.cuda_event for ev in t3])
-    torch.cuda.synchronize()
-    ms_k1 = sum(t3[0].elapsed_time(t3[1]) for t3 in trip) / args.steps
-    ms_k2 = sum(t3[1].elapsed_time(t3[2]) for t3 in trip) / args.steps
-
-    d = dk  # d_k = d_v on every measured workload
-    NC = (T + chunk - 1) // chunk
-    n_ch = B * H * NC
-    tb = token_bytes(dk, dv, es)
-    peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    state_io = (2 if x["S0"] is not None else 1) * B * H * dk * dv * 4
-    work = {
-        "factors": dict(flop=2 * intra_macs_per_chunk_head(chunk, d) * n_ch,
-                        bytes=tb["factors"] * B * T * H, ms=ms_k1),
-        "state": dict(flop=2 * state_macs_per_chunk_head(chunk, d) * n_ch,
-                      bytes=tb["state"] * B * T * H + state_io, ms=ms_k2),
-    }
-    names = dict(factors="eda_bf16_factors", state="eda_bf16_state") if w.dtype == "bf16" else \
-        dict(factors="eda_chunk_intra", state="eda_chunk_state")
-
-    def roof(kind: str) -> dict:
-        wk = work[kind]
-        sec = wk["ms"] * 1e-3
-        # the binding roofline at the algorithmic level is the one with the larger floor
-        mfma = wk["flop"] / (peak_mm * 1e12) >= wk["bytes"] / (PEAK_HBM_GBS * 1e9)
-        if mfma:
-            ach = wk["flop"] / sec / 1e12
-            r = dict(kernel=names[kind], bound="mfma", achieved=round(ach, 3), peak=peak_mm,
-                     unit="TFLOP/s", frac=round(ach / peak_mm, 5))
-        else:
-            ach = wk["bytes"] / sec / 1e9
-            r = dict(kernel=names[kind], bound="hbm", achieved=round(ach, 2), peak=PEAK_HBM_GBS,
-                     unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 5))
-        r.update(ms=round(wk["ms"], 5), algorithmic_bytes=wk["bytes"], algorithmic_flop=wk["flop"],
-                 rocprof_mfma=measured_mfma(names[kind], w.name))
-        return r
-
-    kernels = {k: roof(k) for k in work}
-    dom = max(work, key=lambda k: work[k]["ms"])
-    roof_line = dict(kernels[dom])
-    roof_line["traffic"] = measured_traffic(names[dom], w.name)
-    for k in ("ms", "algorithmic_bytes", "algorithmic_flop", "rocprof_mfma"):
+    kernels = path["kernels"]
+    roof_line = dict(kernels[path["dominant"]])
+    roof_line["traffic"] = measured_traffic(roof_line["kernel"], w.name) if chunk == eda.DEFAULT_CHUNK else None
+    for k in ("ms", "algorithmic_bytes", "algorithmic_flop", "rocprof_mfma", "mfma_frac", "hbm_frac"):
         roof_line.pop(k)
-
-    flop = work["factors"]["flop"] + work["state"]["flop"]
-    byts = tb["chunked"] * B * T * H + state_io
-    tflops = flop / (ms_kernel * 1e-3) / 1e12
-    gbs = byts / (ms_kernel * 1e-3) / 1e9
-    path = dict(kernel_ms=round(ms_kernel, 5), canonical_flop=flop, compulsory_bytes=byts,
-                mfma_tflops=round(tflops, 3), mfma_frac=round(tflops / peak_mm, 5),
-                hbm_gbs=round(gbs, 2), hbm_frac=round(gbs / PEAK_HBM_GBS, 5),
-                canonical_flop_per_token_head=flop / (B * T * H),
-                compulsory_bytes_per_token_head=tb["chunked"], kernels=kernels)
     print(f"[bench] chunked path: {json.dumps(path)}", file=sys.stderr, flush=True)
+    # the same step at the other chunk sizes, for comparison
+    other_chunks = {}
+    if not args.no_chunk_sweep:
+        for c in (32, 16):
+            if c == chunk:
+                continue
+            r = measure_chunked(torch, eda, x, w, c, max(5, args.steps // 2), 2)
+            for kk in r["kernels"].values():
+                kk.pop("rocprof_mfma")
+            other_chunks[f"chunk_{c}"] = r
+            print(f"[bench] chunk {c}: {r['kernel_ms']:.4f} ms ({r['value']:.4g} tokens/s)", file=sys.stderr,
+                  flush=True)
+    del x
+    torch.cuda.empty_cache()
 
     # decode: N sequences x H heads, one token per step, state in place
     decode = None
@@ -489,7 +508,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         import oracle
         from eda_inputs import make_inputs
-        threads = min(oracle.default_threads(), 16)
+        threads = oracle.default_threads()   # every core this process may run on
         Tc = min(T, 2048)
         Bc = 1 if w.B * Tc * w.H > 4 * 2048 * 16 else w.B
         xc = make_inputs(Bc, Tc, w.H, dk, dv, w.dtype, seed=w.seed, alpha_mu=w.alpha_mu,
@@ -502,7 +521,16 @@ def main() -> int:
                                xc["S0"], nthreads=threads)
             dt += time.perf_counter() - t1
             reps += 1
+        model = None
+        try:
+            for ln in open("/proc/cpuinfo"):
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         cpu = dict(value=round(reps * Bc * Tc / dt, 2), unit="tokens/s", cores=threads, kind="oracle",
+                   host_cpu_count=os.cpu_count(), cpu_model=model,
                    sample=f"B={Bc} T={Tc} H={w.H} d_k=d_v={dk} (all heads), fp64 token recurrence, "
                           f"{reps} passes in {dt:.2f} s")
         print(f"[bench] cpu oracle {cpu}", file=sys.stderr, flush=True)
@@ -515,7 +543,8 @@ def main() -> int:
                              f"{w.dtype} inputs, fp32 gates and state, chunk={chunk}",
                     B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, tokens_per_step=tokens,
                     parallelism="single GPU"),
-        roofline=roof_line, cpu_baseline=cpu, chunked_path=path, decode=decode, layer=layer,
+        roofline=roof_line, roofline_path=path["path_roofline"], cpu_baseline=cpu, chunked_path=path,
+        other_chunk_sizes=other_chunks or None, decode=decode, layer=layer,
         dplr=dplr, backward=bwd, long_context=longc)
     print(json.dumps(line), flush=True)
     return 0

@@ -105,34 +105,29 @@ __device__ __forceinline__ bf16x8 frag_col(const bf16 *p, int ld, int lane) {
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(mp + 4 * ld));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+// The same for a k = 16 operand of the 16x16x16 instruction: lane 16 g + n
+// gets p[(4 g + j) * ld + n], j = 0..3.
+__device__ __forceinline__ s16x4 frag_col4(const bf16 *p, int ld, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + (4 * g + (i >> 2)) * ld + 4 * (i & 3)));
+}
+
+// Lane coordinates for 16x16 MFMA tiles (lane = 16 gq + l16, g4 = 4 gq), from
+// an opaque copy of the lane id.  Each phase of a persistent kernel's item
+// loop takes its own copy, so the lane-dependent LDS and workspace addresses
+// are formed inside the phase instead of being hoisted out of the loop and
+// held in registers across every phase.
+struct LaneIds {
+    int lane, g4, l16, gq;
+};
+__device__ __forceinline__ LaneIds lane_ids(int tid) {
+    int x = tid & 63;
+    asm volatile("" : "+v"(x));
+    return {x, 4 * (x >> 4), x & 15, x >> 4};
+}
+
 __device__ __forceinline__ bf16x8 ld_frag(const char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 __device__ __forceinline__ void st_frag(char *p, bf16x8 x) { *reinterpret_cast<bf16x8 *>(p) = x; }
-
-// Inclusive prefix sum over groups of N consecutive lanes (N a power of two);
-// `seg` is the lane's index in its group.  Groups of 16 use DPP row shifts.
-template <int N>
-__device__ __forceinline__ float scan_group(float x, int seg) {
-    // DPP row shifts (rows of 16 lanes; lanes shifted in from outside the row read 0)
-#define EDA_ROW_SHR(n) \
-    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + (n), 0xf, 0xf, true))
-    if constexpr (N == 16) {
-        x += EDA_ROW_SHR(1); x += EDA_ROW_SHR(2); x += EDA_ROW_SHR(4); x += EDA_ROW_SHR(8);
-    } else if constexpr (N == 8) {
-        // the upper 8 lanes of a row must not take values from the lower 8
-        float y;
-        y = EDA_ROW_SHR(1); x += seg >= 1 ? y : 0.f;
-        y = EDA_ROW_SHR(2); x += seg >= 2 ? y : 0.f;
-        y = EDA_ROW_SHR(4); x += seg >= 4 ? y : 0.f;
-    } else {
-#pragma unroll
-        for (int off = 1; off < N; off <<= 1) {
-            const float y = __shfl_up(x, off, N);
-            if (seg >= off) x += y;
-        }
-    }
-#undef EDA_ROW_SHR
-    return x;
-}
 
 constexpr float L2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
 constexpr float GATE_FLOOR = -5.f;   // lower bound l of the safe gate's log-retention
@@ -151,20 +146,6 @@ __device__ __forceinline__ float safe_gate_log2(float a, float Ap, float b) {
 template <int S>
 __device__ __forceinline__ float quad_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x55 * S, 0xf, 0xf, false));
-}
-
-// Value of the last lane of each group of N consecutive lanes.
-template <int N>
-__device__ __forceinline__ float group_last(float x) {
-    if constexpr (N == 16) {
-        // ds_swizzle bit mode: lane' = (lane & 0x10) | 0xF within each 32 lanes
-        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F0));
-    } else if constexpr (N == 8) {
-        // lane' = (lane & 0x18) | 0x7
-        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0xF8));
-    } else {
-        return __shfl(x, N - 1, N);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -199,12 +180,14 @@ struct K1G {
     // chunks: 4-wave workgroups, two per compute unit
     static constexpr int NW = C == 64 ? 8 : 4, NT = 64 * NW;
     static constexpr int LDA = D + 8, LDL = L + 8, ADS = 20, MTW = 24;
-    static constexpr int NQ = D / 4;
-    static constexpr int TPC = imin(NT / NQ, C);       // threads per channel quad
-    static constexpr int TPT = C / TPC;                // tokens per thread
-    static constexpr int ACT = NQ * TPC;               // threads with an element-wise role
-    static_assert((TPC & (TPC - 1)) == 0 && TPC <= 64 && C % TPC == 0 && ACT <= NT, "split");
-    static_assert(TPT == 1 || TPT == 2 || TPT == 4, "token run");
+    // Decay scan and operand formation: lane (r, o) of wave w owns channels
+    // 8 o .. 8 o + 7 of tokens w TPW + i TI + r (i < NI, r < RA).
+    static constexpr int NO = D / 8;                   // 16-byte channel pieces per token row
+    static constexpr int TI = 64 / NO;                 // token rows per wave instruction
+    static constexpr int TPW = C / NW;                 // tokens per wave
+    static constexpr int NI = imax(1, TPW / TI);       // token rows per lane
+    static constexpr int RA = imin(TI, TPW);           // row groups of a wave holding tokens
+    static_assert(TPW % TI == 0 || TPW < TI, "token split");
     static_assert(NB <= NW, "one diagonal block per wave");
     static_assert(C <= 64, "beta/gamma staging by the first wave");
     // P (and later Z = P M) is stored packed: the rows of token block tb hold
@@ -213,21 +196,20 @@ struct K1G {
     static __host__ __device__ constexpr int poff(int tb) { return 16 * tb * (16 * tb + 24); }
     static constexpr int PSZ = poff(NBC);
     // LDS (bytes).  Kl holds G (fp32 [C][D]) in a wide chunk until the operands
-    // are formed; Kr becomes Y = M^T Khat; the off-diagonal blocks of A sit in
-    // the (otherwise unused) upper blocks of M, block (J, I) at (I, J), during
-    // the inversion; the diagonal-inverse scratch becomes Z; M holds the layer
-    // form's norm partials before the operands exist.
+    // are formed; Kr becomes Yhat = M^T Khat and P's high part becomes Z = P M;
+    // the off-diagonal blocks of A are stored in the upper blocks of the L x L
+    // region, block (J, I) at (I, J), which before the operands exist holds the
+    // per-wave decay totals of the scan; MT holds the inverted diagonal blocks.
     static constexpr int szKl = align16(L * LDA * 2), szQl = align16(C * LDA * 2);
     static constexpr int szMI = align16(L * LDL * 2);
     static constexpr int szAd = NB * 16 * ADS * 4, szMT = NB * 16 * MTW * 2;
     static constexpr int szP = align16(PSZ * 2);
-    static_assert(szAd + szMT >= szP, "Z in the inversion scratch");
     static_assert(C * D * 4 <= szKl, "G in the Kl region");
-    static_assert(NW * C * 16 <= szMI, "norm partials in the M region");
+    static_assert(NW * D * 4 <= szMI, "per-wave decay totals in the L x L region");
     static constexpr int oKl = 0, oKr = oKl + szKl, oQl = oKr + szKl, oMI = oQl + szQl;
     static constexpr int oAd = oMI + szMI, oMT = oAd + szAd, oPh = oMT + szMT, oPl = oPh + szP;
     static constexpr int oMisc = oPl + szP;
-    static constexpr int LDS = oMisc + (L + 2 * C + D) * 4 + NW * 4 + C * 16;
+    static constexpr int LDS = oMisc + (L + 2 * C + D) * 4;
     static_assert(LDS <= (NW == 8 ? 160 : 80) * 1024, "LDS budget");
     // phase 4/5 work lists
     static constexpr int NZT = NBC * (NBC + 1);         // Z tiles (tb, J <= 2 tb + 1)
@@ -266,29 +248,26 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     using T = bf16;
     constexpr bool LAYER = MODE == MODE_LAYER, DPLR = MODE == MODE_DPLR;
     constexpr int L = G::L, NB = G::NB, NT = G::NT, NW = G::NW, LDA = G::LDA, LDL = G::LDL;
-    constexpr int ADS = G::ADS, MTW = G::MTW, TPC = G::TPC, TPT = G::TPT;
+    constexpr int ADS = G::ADS, MTW = G::MTW, NO = G::NO, TI = G::TI, NI = G::NI, RA = G::RA;
     constexpr int NBD = F::NBD, NBC = F::NBC, KSD = F::KSD, KSC = F::KSC;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Kl = (T *)(smem + G::oKl);            // Diag(b') Kl              [L][LDA]
     float *Gs = (float *)(smem + G::oKl);    // wide chunk: G (log2) [C][D]
     T *Kr = (T *)(smem + G::oKr);            // Kr, then Y = M^T Khat    [L][LDA]
     T *Ql = (T *)(smem + G::oQl);            // Ql                       [C][LDA]
-    T *MI = (T *)(smem + G::oMI);            // (I + A)^{-1}; A's off-diagonal blocks mirrored above [L][LDL]
+    T *MI = (T *)(smem + G::oMI);            // A's off-diagonal blocks, block (J, I) stored at (I, J) [L][LDL]
     float *AdT = (float *)(smem + G::oAd);   // A, diagonal 16-blocks, transposed: [J][p][i] = A_J[i][p]
-    T *MT = (T *)(smem + G::oMT);            // diagonal blocks of M, transposed [NB][16][MTW]
-    T *Zs = (T *)(smem + G::oAd);            // Z = P M (packed like P), once the inverse is done
+    T *MT = (T *)(smem + G::oMT);            // diagonal blocks of M = (I + A)^{-1}, transposed [NB][16][MTW]
+    T *Zs = (T *)(smem + G::oPh);            // Z = P M (packed like P), over P's high part
     T *Ph = (T *)(smem + G::oPh);            // P, high bf16 part (packed)
     T *Pl = (T *)(smem + G::oPl);            // P, low bf16 part (packed)
     float *bp = (float *)(smem + G::oMisc);  // b' per sub-step          [L]
     float *sb = bp + L, *sg = sb + C;        // beta, gamma per token    [C]
     float *ers = sg + C;                     // e^r per channel (1 if wide) [D]
-    uint32_t *vote = (uint32_t *)(ers + D);  // LAYER: per-wave wide-chunk votes [NW]
-    float *invn = (float *)(vote + NW);      // LAYER, wide chunk: 1/|q|, 1/|k|, 1/|e| per token [C][4]
-    float *nrm = (float *)(smem + G::oMI);   // LAYER: per-wave |q|^2, |k|^2, |e|^2 partials [NW][C][4]
+    float *wtot = (float *)(smem + G::oMI);  // per-wave decay totals of the scan [NW][D]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g4 = 4 * (lane >> 4), l16 = lane & 15, gq = lane >> 4;
     const int grp = H / Hk;                  // value heads per key head
     const float *alpha = (const float *)decay;
     const bf16 *agate = (const bf16 *)decay;
@@ -298,14 +277,18 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     auto head_of = [&](int it) __attribute__((always_inline)) { return it % BH; };
     auto is_fast = [&](int cidx) __attribute__((always_inline)) { return VEC && cidx * C + C <= Tlen; };
 
-    // Thread (seg, quad) owns tokens TPT seg .. TPT seg + TPT - 1 of the chunk and
-    // key channels c0 .. c0 + 3 for the decay scan and the operand formation; its
-    // raw q, e, k (bf16) and alpha (fp32) values stay in registers.
-    const bool act = tid < G::ACT;
-    const int seg = tid % TPC, c0 = act ? 4 * (tid / TPC) : 0;
-    uint2 xq[TPT], xe[TPT], xk[TPT];
-    f32x4 xa[TPT];           // alpha (or, LAYER, the gate input a in .x, .y as bf16 pairs)
-    f32x4 xA, xB;            // LAYER: A_log, dt_bias of the thread's channels
+    // Lane (r, o) of wave w owns key channels c0 .. c0 + 7 (c0 = 8 o) of tokens
+    // w TPW + i TI + r, i < NI: each wave instruction moves TI whole token rows,
+    // and the operand stores are 16-byte row pieces (consecutive lanes, no LDS
+    // bank conflicts).  Its raw q, e, k (bf16) and alpha (fp32) stay in registers.
+    const int o = lane % NO, r = lane / NO;
+    const bool act = r < RA;                 // lanes holding tokens
+    const int c0 = 8 * o;
+    auto tok = [&](int i) __attribute__((always_inline)) { return wave * G::TPW + i * TI + r; };
+    uint4 xq[NI], xe[NI], xk[NI];
+    f32x4 xa[NI][2];         // alpha of the 8 channels
+    uint4 xg[NI];            // LAYER: the gate input a (8 bf16)
+    f32x4 xA[2], xB[2];      // LAYER: A_log, dt_bias of the 8 channels
     float pbeta = 0.f, pgamma = 0.f;
 
     // ---- full aligned chunk: fetched one item ahead.  Rows are clamped to the
@@ -318,21 +301,24 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         const long tok0 = ((long)b * Tlen + t0) * H + h;       // value-head rows
         const long tokk0 = ((long)b * Tlen + t0) * Hk + hk;    // key-head rows
 #pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const long off = (tokk0 + (long)min(TPT * seg + i, last) * Hk) * dk + c0;
-            xq[i] = *(const uint2 *)(q + off);
-            xe[i] = *(const uint2 *)(e + off);
-            xk[i] = *(const uint2 *)(k + off);
+        for (int i = 0; i < NI; ++i) {
+            const long off = (tokk0 + (long)min(tok(i), last) * Hk) * dk + c0;
+            xq[i] = *(const uint4 *)(q + off);
+            xe[i] = *(const uint4 *)(e + off);
+            xk[i] = *(const uint4 *)(k + off);
             if constexpr (LAYER) {
-                const uint2 u = *(const uint2 *)(agate + off);
-                xa[i] = f32x4{__uint_as_float(u.x), __uint_as_float(u.y), 0.f, 0.f};
+                xg[i] = *(const uint4 *)(agate + off);
             } else {
-                xa[i] = *(const f32x4 *)(alpha + off);
+                xa[i][0] = *(const f32x4 *)(alpha + off);
+                xa[i][1] = *(const f32x4 *)(alpha + off + 4);
             }
         }
         if constexpr (LAYER) {
-            xA = *(const f32x4 *)(A_log + (long)hk * dk + c0);
-            xB = *(const f32x4 *)(dt_bias + (long)hk * dk + c0);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                xA[hh] = *(const f32x4 *)(A_log + (long)hk * dk + c0 + 4 * hh);
+                xB[hh] = *(const f32x4 *)(dt_bias + (long)hk * dk + c0 + 4 * hh);
+            }
         }
         const long tb = tok0 + (long)min(tid % C, last) * H;
         pbeta = DPLR ? 1.f : beta[tb];
@@ -346,12 +332,16 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         const int t0 = cidx * C, nval = min(C, Tlen - t0), hk = h / grp;
         const long tok0 = ((long)b * Tlen + t0) * H + h;
         const long tokk0 = ((long)b * Tlen + t0) * Hk + hk;
+        auto pack8 = [](const float *x) __attribute__((always_inline)) {
+            return make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+                              pack_bf16(x[6], x[7]));
+        };
 #pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const int tau = TPT * seg + i;
-            float qv[4], ev[4], kv[4], av[4];
+        for (int i = 0; i < NI; ++i) {
+            const int tau = tok(i);
+            float qv[8], ev[8], kv[8], av[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 8; ++j) {
                 const bool ok = act && tau < nval && c0 + j < dk;
                 const long off = (tokk0 + (long)tau * Hk) * dk + c0 + j;
                 qv[j] = ok ? to_f32(q[off]) : 0.f;
@@ -362,24 +352,28 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 else av[j] = ok ? alpha[off] : 1.f;
             }
             // (exact: the values are bf16 already)
-            xq[i] = make_uint2(pack_bf16(qv[0], qv[1]), pack_bf16(qv[2], qv[3]));
-            xe[i] = make_uint2(pack_bf16(ev[0], ev[1]), pack_bf16(ev[2], ev[3]));
-            xk[i] = make_uint2(pack_bf16(kv[0], kv[1]), pack_bf16(kv[2], kv[3]));
-            if constexpr (LAYER)
-                xa[i] = f32x4{__uint_as_float(pack_bf16(av[0], av[1])), __uint_as_float(pack_bf16(av[2], av[3])), 0.f, 0.f};
-            else
-                xa[i] = f32x4{av[0], av[1], av[2], av[3]};
+            xq[i] = pack8(qv);
+            xe[i] = pack8(ev);
+            xk[i] = pack8(kv);
+            if constexpr (LAYER) {
+                xg[i] = pack8(av);
+            } else {
+                xa[i][0] = f32x4{av[0], av[1], av[2], av[3]};
+                xa[i][1] = f32x4{av[4], av[5], av[6], av[7]};
+            }
         }
         if constexpr (LAYER) {
-            float pa[4], pb[4];
+            float pa[8], pb[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 8; ++j) {
                 const bool ok = act && c0 + j < dk;
                 pa[j] = ok ? A_log[(long)hk * dk + c0 + j] : 0.f;
                 pb[j] = ok ? dt_bias[(long)hk * dk + c0 + j] : 0.f;
             }
-            xA = f32x4{pa[0], pa[1], pa[2], pa[3]};
-            xB = f32x4{pb[0], pb[1], pb[2], pb[3]};
+            xA[0] = f32x4{pa[0], pa[1], pa[2], pa[3]};
+            xA[1] = f32x4{pa[4], pa[5], pa[6], pa[7]};
+            xB[0] = f32x4{pb[0], pb[1], pb[2], pb[3]};
+            xB[1] = f32x4{pb[4], pb[5], pb[6], pb[7]};
         }
         const bool okt = tid < nval;
         pbeta = okt ? (DPLR ? 1.f : beta[tok0 + (long)tid * H]) : 0.f;
@@ -398,7 +392,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     //      column col; at step p every row below p takes -A[i][p] x[p], with x[p]
     //      broadcast inside the lane quad (rows on or above p see A = 0).
     auto invert_diag = [&](int J) __attribute__((always_inline)) {
-        const int col = lane >> 2, s4 = 4 * (lane & 3);
+        const int ln = lane_ids(tid).lane;
+        const int col = ln >> 2, s4 = 4 * (ln & 3);
         f32x4 x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = (s4 + i == col) ? 1.f : 0.f;
@@ -412,11 +407,6 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             for (int i = 0; i < 4; ++i) x[i] -= a[i] * xp;
         }
         const uint32_t x01 = pack_bf16(x[0], x[1]), x23 = pack_bf16(x[2], x[3]);
-        T *mi = MI + (16 * J + s4) * LDL + 16 * J + col;
-        mi[0] = (T)(x01 & 0xffffu);
-        mi[LDL] = (T)(x01 >> 16);
-        mi[2 * LDL] = (T)(x23 & 0xffffu);
-        mi[3 * LDL] = (T)(x23 >> 16);
         *(uint2 *)(MT + (16 * J + col) * MTW + s4) = make_uint2(x01, x23);
     };
 
@@ -439,12 +429,20 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         // previous item's workspace stores follow the prefetch, and leave those
         // stores in flight instead of waiting for them as well.
 #pragma unroll
-        for (int i = 0; i < TPT; ++i)
-            asm volatile("" ::"v"(xq[i].x), "v"(xq[i].y), "v"(xe[i].x), "v"(xe[i].y), "v"(xk[i].x),
-                         "v"(xk[i].y), "v"(xa[i][0]), "v"(xa[i][1]), "v"(xa[i][2]), "v"(xa[i][3]));
+        for (int i = 0; i < NI; ++i) {
+            asm volatile("" ::"v"(xq[i].x), "v"(xq[i].y), "v"(xq[i].z), "v"(xq[i].w), "v"(xe[i].x), "v"(xe[i].y),
+                         "v"(xe[i].z), "v"(xe[i].w), "v"(xk[i].x), "v"(xk[i].y), "v"(xk[i].z), "v"(xk[i].w));
+            if constexpr (LAYER)
+                asm volatile("" ::"v"(xg[i].x), "v"(xg[i].y), "v"(xg[i].z), "v"(xg[i].w));
+            else
+                asm volatile("" ::"v"(xa[i][0][0]), "v"(xa[i][0][1]), "v"(xa[i][0][2]), "v"(xa[i][0][3]),
+                             "v"(xa[i][1][0]), "v"(xa[i][1][1]), "v"(xa[i][1][2]), "v"(xa[i][1][3]));
+        }
         asm volatile("" ::"v"(pbeta), "v"(pgamma));
-        if constexpr (LAYER) asm volatile("" ::"v"(xA[0]), "v"(xA[1]), "v"(xA[2]), "v"(xA[3]), "v"(xB[0]),
-                                          "v"(xB[1]), "v"(xB[2]), "v"(xB[3]));
+        if constexpr (LAYER)
+            asm volatile("" ::"v"(xA[0][0]), "v"(xA[0][1]), "v"(xA[0][2]), "v"(xA[0][3]), "v"(xA[1][0]),
+                         "v"(xA[1][1]), "v"(xA[1][2]), "v"(xA[1][3]), "v"(xB[0][0]), "v"(xB[0][1]), "v"(xB[0][2]),
+                         "v"(xB[0][3]), "v"(xB[1][0]), "v"(xB[1][1]), "v"(xB[1][2]), "v"(xB[1][3]));
     }
     for (; it < items; it += gridDim.x) {
         const int bh = head_of(it), cidx = chunk_of(it);
@@ -458,175 +456,177 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         char *wsb = ws + ((long)bh * NC + cidx) * F::bytes;
 
-        // ---- cumulative log2-decay per channel: a sequential sum over the
-        //      thread's own tokens, then one scan of the run totals over the
-        //      TPC threads of the channel quad; wide-chunk vote -----------------------
-        float g[TPT][4];
-        f32x4 glq;
+        // ---- cumulative log2-decay per channel: an inclusive scan over the RA row
+        //      groups of the wave (lanes NO apart) for each of the lane's token rows,
+        //      carried across its rows; then the waves' totals through LDS --------------
+        float g[NI][8];
+        float glq[8];
+        {
+            f32x4 Ap[2];
+            if constexpr (LAYER) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) Ap[hh][j] = exp2f_(xA[hh][j] * L2E) * (L2E / -GATE_FLOOR);
+            }
+            float carry[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) carry[j] = 0.f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float x;
+                    if constexpr (LAYER) {
+                        const uint32_t u = j < 2 ? xg[i].x : j < 4 ? xg[i].y : j < 6 ? xg[i].z : xg[i].w;
+                        x = safe_gate_log2((j & 1) ? hi_bf16(u) : lo_bf16(u), Ap[j >> 2][j & 3], xB[j >> 2][j & 3]);
+                    } else {
+                        x = __builtin_amdgcn_logf(xa[i][j >> 2][j & 3]);
+                    }
+#pragma unroll
+                    for (int sh = 1; sh < RA; sh <<= 1) {
+                        const float y = __shfl_up(x, sh * NO, 64);
+                        if (r >= sh) x += y;
+                    }
+                    g[i][j] = carry[j] + x;
+                    carry[j] += __shfl(x, (RA - 1) * NO + o, 64);
+                }
+            if (r == 0) {
+                *(f32x4 *)(wtot + wave * D + c0) = f32x4{carry[0], carry[1], carry[2], carry[3]};
+                *(f32x4 *)(wtot + wave * D + c0 + 4) = f32x4{carry[4], carry[5], carry[6], carry[7]};
+            }
+        }
+        __syncthreads();
         bool wide_here = false;
         {
-            float run[4] = {0.f, 0.f, 0.f, 0.f};
-            f32x4 Ap;
-            if constexpr (LAYER) {
+            float pre[8], tot[8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) Ap[j] = exp2f_(xA[j] * L2E) * (L2E / -GATE_FLOOR);
-            }
+            for (int j = 0; j < 8; ++j) pre[j] = tot[j] = 0.f;
 #pragma unroll
-            for (int i = 0; i < TPT; ++i)
+            for (int w = 0; w < NW; ++w) {
+                const f32x4 a = *(const f32x4 *)(wtot + w * D + c0), b = *(const f32x4 *)(wtot + w * D + c0 + 4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    if constexpr (LAYER) {
-                        const uint32_t u = __float_as_uint(xa[i][j >> 1]);
-                        run[j] += safe_gate_log2((j & 1) ? hi_bf16(u) : lo_bf16(u), Ap[j], xB[j]);
-                    } else {
-                        run[j] += __builtin_amdgcn_logf(xa[i][j]);
+                    tot[j] += a[j];
+                    tot[4 + j] += b[j];
+                    if (w < wave) {
+                        pre[j] += a[j];
+                        pre[4 + j] += b[j];
                     }
-                    g[i][j] = run[j];
-                }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float incl = scan_group<TPC>(run[j], seg);
-                const float excl = incl - run[j];
-#pragma unroll
-                for (int i = 0; i < TPT; ++i) g[i][j] += excl;
-                glq[j] = group_last<TPC>(incl);   // G_C of the channel
-            }
-            if (act && seg == TPC - 1) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) wide_here |= glq[j] < -WIDE_G2;
-            }
-        }
-        // LAYER: squared norms of q, k, e per token, summed over the channel
-        // quads of a wave here and over the waves after the barrier
-        if constexpr (LAYER) {
-            constexpr int NWA = (G::ACT + 63) / 64;   // waves with channels
-            if (wave < NWA) {
-#pragma unroll
-                for (int i = 0; i < TPT; ++i) {
-                    f32x4 ps = zero4();
-                    const uint2 *src[3] = {&xq[i], &xk[i], &xe[i]};
-#pragma unroll
-                    for (int v = 0; v < 3; ++v) {
-                        const uint2 u = *src[v];
-                        const float x0 = lo_bf16(u.x), x1 = hi_bf16(u.x), x2 = lo_bf16(u.y), x3 = hi_bf16(u.y);
-                        float sq = x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
-#pragma unroll
-                        for (int m = TPC; m < 64; m <<= 1) sq += __shfl_xor(sq, m, 64);
-                        ps[v] = sq;
-                    }
-                    if (lane < TPC) *(f32x4 *)(nrm + (wave * C + TPT * seg + i) * 4) = ps;
                 }
             }
-        }
-        // Wide-chunk vote.  Layer mode: one slot per wave and one barrier (a wave
-        // rewrites its slot only at the next item's vote, after barriers of this
-        // item that every wave passes once its reads below are done), which
-        // spares the mode's registers.  The plain and DPLR modes keep the
-        // block-wide OR.
-        bool wide = false;
-        if constexpr (LAYER) {
-            const bool wv = __ballot(wide_here) != 0ull;
-            if (lane == 0) vote[wave] = wv ? 1u : 0u;
-            __syncthreads();
 #pragma unroll
-            for (int w = 0; w < NW; ++w) wide |= vote[w] != 0u;
-        } else {
-            wide = __syncthreads_or(wide_here) != 0;
+            for (int j = 0; j < 8; ++j) {
+                glq[j] = tot[j];   // G_C of the channel
+#pragma unroll
+                for (int i = 0; i < NI; ++i) g[i][j] += pre[j];
+                wide_here |= act && tot[j] < -WIDE_G2;
+            }
         }
-        // LAYER: 1 / max(|x|, eps) of the thread's token i, for q, k, e (formed
-        // where each token is used, so the scales are not held across the loop).
-        // A wide chunk forms its operands a second time, after its element-wise A
-        // and P have overwritten the partials' region; it keeps the scales in invn.
-        auto inv_norms = [&](int i, bool saved = false) __attribute__((always_inline)) {
-            f32x4 tot = zero4();
+        // wide-chunk vote (every read of the totals precedes this barrier)
+        const bool wide = __syncthreads_or(wide_here) != 0;
+
+        // LAYER: (1/|q|, 1/|k|, 1/|e|) of token row i, reduced over the NO lanes of
+        // the row (x / max(|x|, eps))
+        auto inv_norms = [&](int i) __attribute__((always_inline)) {
+            f32x4 res = zero4();
             if constexpr (LAYER) {
-                if (saved) return *(const f32x4 *)(invn + 4 * (TPT * seg + i));
-                constexpr int NWA = (G::ACT + 63) / 64;
+                const uint4 *src[3] = {&xq[i], &xk[i], &xe[i]};
 #pragma unroll
-                for (int w = 0; w < NWA; ++w) tot += *(const f32x4 *)(nrm + (w * C + TPT * seg + i) * 4);
-                auto inv = [](float ss) { return ss > NORM_EPS * NORM_EPS ? __builtin_amdgcn_rsqf(ss) : 1.f / NORM_EPS; };
-                tot = f32x4{inv(tot[0]), inv(tot[1]), inv(tot[2]), 0.f};
+                for (int v = 0; v < 3; ++v) {
+                    const uint4 u = *src[v];
+                    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+                    float sq = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const float a = lo_bf16(w4[m]), b = hi_bf16(w4[m]);
+                        sq += a * a + b * b;
+                    }
+#pragma unroll
+                    for (int m = 1; m < NO; m <<= 1) sq += __shfl_xor(sq, m, 64);
+                    res[v] = sq > NORM_EPS * NORM_EPS ? __builtin_amdgcn_rsqf(sq) : 1.f / NORM_EPS;
+                }
             }
-            return tot;   // (1/|q|, 1/|k|, 1/|e|)
+            return res;
+        };
+        auto unpack8 = [](uint4 u, float *x, float sc) __attribute__((always_inline)) {
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                x[2 * m] = lo_bf16(w4[m]) * sc;
+                x[2 * m + 1] = hi_bf16(w4[m]) * sc;
+            }
+        };
+        auto store8 = [](T *p, const float *x, float sc, const float *f) __attribute__((always_inline)) {
+            *(uint4 *)p = make_uint4(pack_bf16(sc * x[0] * f[0], sc * x[1] * f[1]), pack_bf16(sc * x[2] * f[2], sc * x[3] * f[3]),
+                                     pack_bf16(sc * x[4] * f[4], sc * x[5] * f[5]), pack_bf16(sc * x[6] * f[6], sc * x[7] * f[7]));
         };
 
         // ---- scaled operands (LDS) and the per-channel scales ----------------------
-        // Forms Diag(b') Kl, Kr and Ql from the thread's raw values; in a wide
-        // chunk the exponents are unsplit (Kl = lam 2^G, Kr = kap 2^{G_C - G}).
-        f32x4 er;
+        // Forms Diag(b') Kl, Kr and Ql from the lane's raw values; in a wide chunk the
+        // exponents are unsplit (Kl = lam 2^G, Kr = kap 2^{G_C - G}).
+        float er[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) er[j] = wide ? 1.f : exp2f_(0.5f * glq[j]);
-        auto form_operands = [&](bool saved_norms) __attribute__((always_inline)) {
-            float r[4];
+        for (int j = 0; j < 8; ++j) er[j] = wide ? 1.f : exp2f_(0.5f * glq[j]);
+        auto form_operands = [&]() __attribute__((always_inline)) {
+            float rr[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) r[j] = wide ? 0.f : 0.5f * glq[j];
+            for (int j = 0; j < 8; ++j) rr[j] = wide ? 0.f : 0.5f * glq[j];
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) {
-                const int tau = TPT * seg + i;
-                float ev[4] = {lo_bf16(xe[i].x), hi_bf16(xe[i].x), lo_bf16(xe[i].y), hi_bf16(xe[i].y)};
-                float kv[4] = {lo_bf16(xk[i].x), hi_bf16(xk[i].x), lo_bf16(xk[i].y), hi_bf16(xk[i].y)};
-                float qv[4] = {lo_bf16(xq[i].x), hi_bf16(xq[i].x), lo_bf16(xq[i].y), hi_bf16(xq[i].y)};
-                if constexpr (LAYER) {
-                    const f32x4 nv = inv_norms(i, saved_norms);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        ev[j] *= nv[2];
-                        kv[j] *= nv[1];
-                        qv[j] *= nv[0];
-                    }
-                }
+            for (int i = 0; i < NI; ++i) {
+                const int tau = tok(i);
+                const f32x4 nv = LAYER ? inv_norms(i) : f32x4{1.f, 1.f, 1.f, 0.f};
+                float ev[8], kv[8], qv[8];
+                unpack8(xe[i], ev, nv[2]);
+                unpack8(xk[i], kv, nv[1]);
+                unpack8(xq[i], qv, nv[0]);
                 const float gmt = sg[tau], btt = sb[tau];
-                float f[4], fi[4];
+                float f[8], fi[8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f[j] = exp2f_(g[i][j] - r[j]);
-                    fi[j] = wide ? exp2f_(glq[j] - g[i][j]) : exp2f_(r[j] - g[i][j]);
+                for (int j = 0; j < 8; ++j) {
+                    f[j] = exp2f_(g[i][j] - rr[j]);
+                    fi[j] = wide ? exp2f_(glq[j] - g[i][j]) : exp2f_(rr[j] - g[i][j]);
                 }
-                store4<T>(Kl + (2 * tau) * LDA + c0, gmt * ev[0] * f[0], gmt * ev[1] * f[1],
-                          gmt * ev[2] * f[2], gmt * ev[3] * f[3]);
+                store8(Kl + (2 * tau) * LDA + c0, ev, gmt, f);
                 // (DPLR: the delta sub-step reads along a, held in ev; its erase sub-step has no key)
+                store8(Kl + (2 * tau + 1) * LDA + c0, DPLR ? ev : kv, btt, f);
                 if constexpr (DPLR)
-                    store4<T>(Kl + (2 * tau + 1) * LDA + c0, btt * ev[0] * f[0], btt * ev[1] * f[1],
-                              btt * ev[2] * f[2], btt * ev[3] * f[3]);
+                    *(uint4 *)(Kr + (2 * tau) * LDA + c0) = make_uint4(0u, 0u, 0u, 0u);
                 else
-                    store4<T>(Kl + (2 * tau + 1) * LDA + c0, btt * kv[0] * f[0], btt * kv[1] * f[1],
-                              btt * kv[2] * f[2], btt * kv[3] * f[3]);
-                if constexpr (DPLR)
-                    store4<T>(Kr + (2 * tau) * LDA + c0, 0.f, 0.f, 0.f, 0.f);
-                else
-                    store4<T>(Kr + (2 * tau) * LDA + c0, ev[0] * fi[0], ev[1] * fi[1], ev[2] * fi[2],
-                              ev[3] * fi[3]);
-                store4<T>(Kr + (2 * tau + 1) * LDA + c0, kv[0] * fi[0], kv[1] * fi[1], kv[2] * fi[2],
-                          kv[3] * fi[3]);
-                store4<T>(Ql + tau * LDA + c0, qv[0] * f[0], qv[1] * f[1], qv[2] * f[2], qv[3] * f[3]);
+                    store8(Kr + (2 * tau) * LDA + c0, ev, 1.f, fi);
+                store8(Kr + (2 * tau + 1) * LDA + c0, kv, 1.f, fi);
+                store8(Ql + tau * LDA + c0, qv, 1.f, f);
             }
         };
         if (act) {
-            if (seg == 0) {
-                f32x4 dec;
+            if (wave == 0 && r == 0) {
+                float dec[8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dec[j] = exp2f_(glq[j]);
-                *(f32x4 *)(ers + c0) = er;
-                *(f32x4 *)(wsb + F::oDec + 4 * c0) = dec;
+                for (int j = 0; j < 8; ++j) dec[j] = exp2f_(glq[j]);
+                *(f32x4 *)(ers + c0) = f32x4{er[0], er[1], er[2], er[3]};
+                *(f32x4 *)(ers + c0 + 4) = f32x4{er[4], er[5], er[6], er[7]};
+                *(f32x4 *)(wsb + F::oDec + 4 * c0) = f32x4{dec[0], dec[1], dec[2], dec[3]};
+                *(f32x4 *)(wsb + F::oDec + 4 * c0 + 16) = f32x4{dec[4], dec[5], dec[6], dec[7]};
             }
             if (!wide) {
-                form_operands(false);
+                form_operands();
             } else {
-                // raw keys and queries, and G, for the element-wise path
+                // raw keys and queries (normalised in the layer form), and G, for the
+                // element-wise path
 #pragma unroll
-                for (int i = 0; i < TPT; ++i) {
-                    const int tau = TPT * seg + i;
-                    auto nz = [&](uint2 u, float s) __attribute__((always_inline)) {
-                        if constexpr (!LAYER) return u;
-                        return make_uint2(pack_bf16(lo_bf16(u.x) * s, hi_bf16(u.x) * s),
-                                          pack_bf16(lo_bf16(u.y) * s, hi_bf16(u.y) * s));
-                    };
-                    const f32x4 nv = inv_norms(i);
-                    if (LAYER && c0 == 0) *(f32x4 *)(invn + 4 * tau) = nv;
-                    *(uint2 *)(Kr + (2 * tau) * LDA + c0) = nz(xe[i], nv[2]);
-                    *(uint2 *)(Kr + (2 * tau + 1) * LDA + c0) = nz(xk[i], nv[1]);
-                    *(uint2 *)(Ql + tau * LDA + c0) = nz(xq[i], nv[0]);
+                for (int i = 0; i < NI; ++i) {
+                    const int tau = tok(i);
+                    const f32x4 nv = LAYER ? inv_norms(i) : f32x4{1.f, 1.f, 1.f, 0.f};
+                    float ev[8], kv[8], qv[8];
+                    const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+                    unpack8(xe[i], ev, nv[2]);
+                    unpack8(xk[i], kv, nv[1]);
+                    unpack8(xq[i], qv, nv[0]);
+                    store8(Kr + (2 * tau) * LDA + c0, ev, 1.f, one);
+                    store8(Kr + (2 * tau + 1) * LDA + c0, kv, 1.f, one);
+                    store8(Ql + tau * LDA + c0, qv, 1.f, one);
                     *(f32x4 *)(Gs + tau * D + c0) = f32x4{g[i][0], g[i][1], g[i][2], g[i][3]};
+                    *(f32x4 *)(Gs + tau * D + c0 + 4) = f32x4{g[i][4], g[i][5], g[i][6], g[i][7]};
                 }
             }
         }
@@ -639,6 +639,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         if (!wide) {
             if (wave < NB) {
                 const int J = wave;
+                const auto [lane, g4, l16, gq] = lane_ids(tid);
                 const f32x4 a = tile_nt<T, D>(Kl + 16 * J * LDA, LDA, Kr + 16 * J * LDA, LDA, zero4(), lane);
                 // lane holds A[g4 + rr][l16]: one column run of the transposed block
                 *(f32x4 *)(AdT + (J * 16 + l16) * ADS + g4) =
@@ -649,6 +650,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             }
             // off-diagonal A and P tiles, spread over every wave
             for (int t = (wave + NW - NB) % NW; t < NOD + NPT; t += NW) {
+                const auto [lane, g4, l16, gq] = lane_ids(tid);
                 if (t < NOD) {
                     int J = 1, I = t;
                     while (I >= J) { I -= J; ++J; }
@@ -709,7 +711,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             __syncthreads();
             if (wave < NB) invert_diag(wave);
             // every read of G and of the raw keys is done: form the operands in place
-            if (act) form_operands(true);
+            if (act) form_operands();
         }
         __syncthreads();
 
@@ -720,110 +722,95 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             prefetch(nx < items ? nx : items - 1);
         }
 
-        // ---- off-diagonal blocks of (I + A)^{-1}, one column block per wave:
-        //      X_JI = -X_JJ sum_{I <= K < J} A_JK X_KI, for J = I+1, I+2, ...
-        // A 16x16 accumulator (lane: rows 4g..4g+3 of column l%16) is exactly the
-        // B operand of the 16x16x16 instruction, so the X_KI stay in registers.
-        if (wave < NB - 1) {
-            const int I = wave;
-            s16x4 xb[NB];   // X_KI as bf16 B operands (K >= I)
-#pragma unroll
-            for (int K = 0; K < NB - 1; ++K)
-                if (K == I) xb[K] = *(const s16x4 *)(MT + (16 * K + l16) * MTW + g4);
-#pragma unroll
-            for (int J = 1; J < NB; ++J) {
-                if (J <= I) continue;
-                f32x4 t = zero4();
-#pragma unroll
-                for (int K = 0; K < J; ++K) {
-                    if (K < I) continue;
-                    // A[16 J + l16][16 K + g4 ..] from its mirrored block (K, J)
-                    const s16x4 a = *(const s16x4 *)(MI + (16 * K + l16) * LDL + 16 * J + g4);
-                    t = mma16(a, xb[K], t);
-                }
-                const s16x4 tb = __builtin_bit_cast(s16x4, make_uint2(pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])));
-                const s16x4 m = *(const s16x4 *)(MI + (16 * J + l16) * LDL + 16 * J + g4);
-                const f32x4 x = mma16(m, tb, zero4());
-                const uint32_t x01 = pack_bf16(-x[0], -x[1]), x23 = pack_bf16(-x[2], -x[3]);
-                xb[J] = __builtin_bit_cast(s16x4, make_uint2(x01, x23));
-                const int a0 = 16 * J + g4, ncol = 16 * I + l16;
-                MI[(a0 + 0) * LDL + ncol] = (T)(x01 & 0xffffu);
-                MI[(a0 + 1) * LDL + ncol] = (T)(x01 >> 16);
-                MI[(a0 + 2) * LDL + ncol] = (T)(x23 & 0xffffu);
-                MI[(a0 + 3) * LDL + ncol] = (T)(x23 >> 16);
-            }
-        }
-        __syncthreads();
-
-        // ---- Y = M^T Kr (in place over Kr, by column block) and Z = P M; from their
-        //      fp32 accumulators the exports Psi = e^r Y[delta rows]^T Diag(beta) and
-        //      Phat = Z[:, delta cols] Diag(beta).  A product over sub-steps from 16 J
-        //      on starts at the 32-row step holding row 16 J; when J is odd its first
-        //      16 rows (M's block above the diagonal, which holds A during the
-        //      inversion) are masked out of M's operand.  Every product here is the
-        //      16x16x32 instruction: a 16x16x16 result fed straight into a 16x16x32
-        //      accumulator was found to need wait states the compiler did not insert
-        //      (its last accumulator register was read stale).
-        const bool lo_half = lane < 32;   // lanes holding k = 0..15 of a 16x16x32 operand
-        auto m_frag = [&](int s, int J) __attribute__((always_inline)) {
-            bf16x8 m = frag_col(MI + 32 * s * LDL + 16 * J, LDL, lane);
-            if ((J & 1) && s == (J >> 1) && lo_half) m = bf16x8{};
-            return m;
-        };
-        for (int nb = wave; nb < NBD; nb += NW) {
-            // Kr column block nb, all sub-steps, as B operands (read before Y overwrites it)
-            bf16x8 kb[L / 32];
-#pragma unroll
-            for (int s = 0; s < L / 32; ++s) kb[s] = frag_col(Kr + 32 * s * LDA + 16 * nb, LDA, lane);
-            const float ern = ers[16 * nb + l16];
-            f32x4 y[NB];
+        // ---- Y = M^T Khat and Z^T = M^T P^T, M = (I + A)^{-1}, by block backward
+        //      substitution: (I + A)^T X = R for the right-hand sides R = [Khat | P^T],
+        //      one 16-column block of R per wave, with no barrier:
+        //          X_K = M_KK^T (R_K - sum_{J > K} A_JK^T X_J),   K = NB-1 .. 0.
+        //      The solved blocks feed the later steps as bf16; the bracket enters the
+        //      diagonal-inverse product as a bf16 pair.  Y overwrites Kr and Z overwrites
+        //      P's high part, in place (each column block belongs to one wave, and each
+        //      row block of it is read before it is written).  From the fp32 results:
+        //      Psi = Yhat[delta rows]^T Diag(beta), Phat = Z[:, delta cols] Diag(beta).
+        //      Every product here is the 16x16x16 instruction.  (Yhat = Y Diag(e^r) =
+        //      M^T Khat is kept, bounded by |M|: Y^T Kl would otherwise reach e^{|G_C|},
+        //      past the fp32 range, for channels decaying by more than about e^-88.)
+        for (int cb = wave; cb < NBD + NBC; cb += NW) {
+            const auto [lane, g4, l16, gq] = lane_ids(tid);
+            const bool isY = cb < NBD;
+            const int nb = cb, tb = cb - NBD;
+            const int Jtop = isY ? NB - 1 : imin(NB - 1, 2 * tb + 1);   // Z: P is zero below 32 tb + 32
+            const float scale = isY ? ers[16 * nb + l16] : 1.f;        // Khat = Kr e^r, column n
+            const int pr = isY ? 0 : G::poff(tb) + l16 * G::pld(tb);    // P row of token 16 tb + l16
+            // right-looking: every row block's bracket starts as R_J; once X_K is solved
+            // it updates all the brackets above it at once (independent products), so
+            // the chain from one solved block to the next is one update, the pair split
+            // and the two diagonal-inverse products
+            f32x4 acc[NB];
 #pragma unroll
             for (int J = 0; J < NB; ++J) {
-                f32x4 acc = zero4();
+                if (J > Jtop) continue;
+                if (isY) {
+                    const s16x4 r = frag_col4(Kr + 16 * J * LDA + 16 * nb, LDA, lane);   // rows 16 J + g4 + i
+                    const uint2 u = __builtin_bit_cast(uint2, r);
+                    acc[J] = f32x4{lo_bf16(u.x), hi_bf16(u.x), lo_bf16(u.y), hi_bf16(u.y)} * scale;
+                } else {
+                    const uint2 h = *(const uint2 *)(Ph + pr + 16 * J + g4);
+                    const uint2 l = *(const uint2 *)(Pl + pr + 16 * J + g4);
+                    acc[J] = f32x4{lo_bf16(h.x) + lo_bf16(l.x), hi_bf16(h.x) + hi_bf16(l.x),
+                                   lo_bf16(h.y) + lo_bf16(l.y), hi_bf16(h.y) + hi_bf16(l.y)};
+                }
+            }
 #pragma unroll
-                for (int s = J >> 1; s < L / 32; ++s) acc = mma32(m_frag(s, J), kb[s], acc);
-                // lane: Y[16 J + g4 + i][16 nb + l16], kept as Yhat = Y Diag(e^r) = M^T Khat
-                // (bounded by |M|: Y^T Kl below would otherwise reach e^{|G_C|}, past
-                // the fp32 range, for channels decaying by more than about e^-88)
-                y[J] = acc * ern;
-                // Psi[n][t] for delta rows j = 16 J + g4 + 1, + 3: t = 8 J + gq * 2 (+1)
-                const int t0 = 8 * J + 2 * gq;
+            for (int K = NB - 1; K >= 0; --K) {
+                if (K > Jtop) continue;
+                // X_K = M_KK^T acc[K], acc[K] as a bf16 pair
+                const s16x4 mt = *(const s16x4 *)(MT + (16 * K + l16) * MTW + g4);
+                const f32x4 a = acc[K];
+                const uint32_t h01 = pack_bf16(a[0], a[1]), h23 = pack_bf16(a[2], a[3]);
+                const uint32_t l01 = pack_bf16(a[0] - lo_bf16(h01), a[1] - hi_bf16(h01));
+                const uint32_t l23 = pack_bf16(a[2] - lo_bf16(h23), a[3] - hi_bf16(h23));
+                f32x4 x = mma16(mt, __builtin_bit_cast(s16x4, make_uint2(h01, h23)), zero4());
+                x = mma16(mt, __builtin_bit_cast(s16x4, make_uint2(l01, l23)), x);
+                const uint32_t x01 = pack_bf16(x[0], x[1]), x23 = pack_bf16(x[2], x[3]);
+                const s16x4 xn = __builtin_bit_cast(s16x4, make_uint2(x01 ^ 0x80008000u, x23 ^ 0x80008000u));
+                // acc[J] -= A_KJ^T X_K for every J < K (A_KJ stored at block (J, K)); the
+                // bracket solved next (J = K - 1) is updated first, and every operand
+                // is read before the first product
+                s16x4 ak[NB];
+#pragma unroll
+                for (int J = K - 1; J >= 0; --J) ak[J] = frag_col4(MI + 16 * J * LDL + 16 * K, LDL, lane);
+#pragma unroll
+                for (int J = K - 1; J >= 0; --J) acc[J] = mma16(ak[J], xn, acc[J]);
+                // lane: X[16 K + g4 + i][column l16 of the block]; delta rows j = 16 K + g4 + 1, + 3
+                const int t0 = 8 * K + 2 * gq;
                 const float2 bt = *(const float2 *)(sb + t0);
-                const uint32_t pv = pack_bf16(y[J][1] * bt.x, y[J][3] * bt.y);
-                *(uint32_t *)(wsb + F::oPsi + ((nb * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
-                              2 * (t0 & 7)) = pv;
+                const uint32_t ev = pack_bf16(x[1] * bt.x, x[3] * bt.y);
+                if (isY) {
+                    // Psi[n][t], n = 16 nb + l16
+                    *(uint32_t *)(wsb + F::oPsi + ((nb * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
+                                  2 * (t0 & 7)) = ev;
+                    T *yk = Kr + (16 * K + g4) * LDA + 16 * nb + l16;
+                    yk[0] = (T)(x01 & 0xffffu);
+                    yk[LDA] = (T)(x01 >> 16);
+                    yk[2 * LDA] = (T)(x23 & 0xffffu);
+                    yk[3 * LDA] = (T)(x23 >> 16);
+                } else {
+                    // Phat[t][t'], t = 16 tb + l16; Z[t][16 K + g4 ..]
+                    *(uint32_t *)(wsb + F::oPh + ((tb * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
+                                  2 * (t0 & 7)) = ev;
+                    *(uint2 *)(Zs + pr + 16 * K + g4) = make_uint2(x01, x23);
+                }
             }
             if constexpr (C == 16) {
                 // tokens 16 .. 31 of the k = 32 fragment are zero
-                if (lane >= 32) *(uint4 *)(wsb + F::oPsi + (nb * KSC * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
+                if (isY && lane >= 32) *(uint4 *)(wsb + F::oPsi + (nb * KSC * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
             }
-#pragma unroll
-            for (int J = 0; J < NB; ++J)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Kr[(16 * J + g4 + i) * LDA + 16 * nb + l16] = from_f32<T>(y[J][i]);
-        }
-        for (int z = (wave + NBD) % NW; z < G::NZT; z += NW) {
-            // Z^T tile (sub-steps 16 J.., tokens 16 tb..): z enumerates tb = 0.., J = 0..2 tb + 1
-            int tb = 0, J = z;
-            while (J >= 2 * tb + 2) { J -= 2 * tb + 2; ++tb; }
-            const int pr = G::poff(tb) + l16 * G::pld(tb);   // this lane's P row (token 16 tb + l16)
-            f32x4 acc = zero4();
-            for (int s = J >> 1; s < tb + 1; ++s) {
-                const bf16x8 m = m_frag(s, J);
-                acc = mma32(m, *(const bf16x8 *)(Ph + pr + 32 * s + 8 * gq), acc);
-                acc = mma32(m, *(const bf16x8 *)(Pl + pr + 32 * s + 8 * gq), acc);
-            }
-            // lane: Z[t = 16 tb + l16][j = 16 J + g4 + i]
-            *(uint2 *)(Zs + pr + 16 * J + g4) = make_uint2(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]));
-            const int t0 = 8 * J + 2 * gq;
-            const float2 bt = *(const float2 *)(sb + t0);
-            *(uint32_t *)(wsb + F::oPh + ((tb * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
-                          2 * (t0 & 7)) = pack_bf16(acc[1] * bt.x, acc[3] * bt.y);
         }
         // Phat is causal: the Z tiles of token block tb write tokens t' < 16 (tb + 1);
         // the rest of its fragments (which the state pass reads whole) is zeroed
         // here, by lanes whose 8 tokens all lie beyond that range.
         for (int f = wave; f < NBC * KSC; f += NW) {
+            const auto [lane, g4, l16, gq] = lane_ids(tid);
             const int tb = f / KSC, ks = f % KSC;
             if (32 * ks + 8 * gq >= 16 * (tb + 1))
                 *(uint4 *)(wsb + F::oPh + (f * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
@@ -831,7 +818,10 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         __syncthreads();
 
         // ---- Phi = -(Yhat^T Kl) e^r as transposed tiles, BM x BN tiles per block ---
+        //      (this and the Qhat loop are kept rolled: unrolled, their fragments
+        //      are hoisted beside the next item's inputs and the kernel spills)
         for (int pb = wave; pb < G::NPB; pb += NW) {
+            const auto [lane, g4, l16, gq] = lane_ids(tid);
             constexpr int BM = G::BM, BN = G::BN;
             const int mb0 = BM * (pb % (NBD / BM)), nb0 = BN * (pb / (NBD / BM));
             f32x4 acc[BM][BN];
@@ -839,9 +829,10 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             for (int a = 0; a < BM; ++a)
 #pragma unroll
                 for (int b = 0; b < BN; ++b) acc[a][b] = zero4();
-#pragma unroll
+#pragma unroll 1
             for (int s = 0; s < L / 32; ++s) {
                 bf16x8 xa8[BM], yb8[BN];
+
 #pragma unroll
                 for (int a = 0; a < BM; ++a) xa8[a] = frag_col(Kl + 32 * s * LDA + 16 * (mb0 + a), LDA, lane);
 #pragma unroll
@@ -868,10 +859,12 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         // ---- Qhat = (Ql - Z Kl) e^r as transposed tiles -------------------------------
         for (int mb = wave; mb < NBD; mb += NW) {
+            const auto [lane, g4, l16, gq] = lane_ids(tid);
             const f32x4 erm = *(const f32x4 *)(ers + 16 * mb + g4);
-#pragma unroll
+#pragma unroll 1
             for (int tb = 0; tb < NBC; ++tb) {
                 const int pr = G::poff(tb) + l16 * G::pld(tb);
+
                 const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * mb + g4);
                 f32x4 acc = {-lo_bf16(q0.x), -hi_bf16(q0.x), -lo_bf16(q0.y), -hi_bf16(q0.y)};
 #pragma unroll
@@ -886,7 +879,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         // No barrier here: the next item writes LDS before its first barrier only
         // in b', beta, gamma (read above only by the Y and Z exports, before the
-        // last barrier) and in the layer form's norm partials (in M's region, not
+        // last barrier) and in the scan's per-wave decay totals (in M's region, not
         // read since that barrier).
     }
 }
