@@ -51,7 +51,9 @@ typedef enum {
     EDA_ERR_UNSUPPORTED = 5, /* head dims or chunk size outside the supported set */
     EDA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required        */
     EDA_ERR_ALIAS = 7,       /* an output overlaps an input it may not overlap     */
-    EDA_ERR_HIP = 8          /* a HIP launch failed                               */
+    EDA_ERR_HIP = 8,         /* a HIP launch failed                               */
+    EDA_ERR_SCRATCH = 9      /* eda_fwd_chunked_noalloc: the problem needs more
+                                workspace than EDA_NOALLOC_SCRATCH_BYTES          */
 } eda_status_t;
 
 typedef enum { EDA_F32 = 0, EDA_BF16 = 1 } eda_dtype_t;
@@ -127,6 +129,36 @@ eda_status_t eda_fwd_chunked_timed(const void *q, const void *k, const void *e, 
                                    int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
                                    int chunk, void *workspace, size_t workspace_bytes,
                                    void *stream, void *const *events);
+
+/*
+ * eda_fwd_chunked for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks and results as eda_fwd_chunked, without the
+ * workspace arguments: the workspace is a scratch array of
+ * EDA_NOALLOC_SCRATCH_BYTES (160 MiB) that the library holds on every device
+ * it runs on, from the first use until the process ends.  The call makes no
+ * hipMalloc, hipFree or other allocating call; the caller still passes every
+ * input and output.
+ *
+ *   - The array of the calling thread's current device is used; `stream`
+ *     must belong to that device.  Its address is looked up on the first
+ *     call on each device.
+ *   - A problem whose eda_fwd_chunked_workspace_size exceeds
+ *     EDA_NOALLOC_SCRATCH_BYTES (bf16 at d_k = d_v = 128 and chunk 64 fits
+ *     B*H*ceil(T/64) <= 2259 chunk-heads, e.g. B=4, H=16, T=2048) is rejected with
+ *     EDA_ERR_SCRATCH before anything is enqueued; use eda_fwd_chunked.
+ *   - Every call on a device shares that device's array, which keeps the
+ *     last call's contents (no call reads what an earlier call left there).
+ *     Calls that can overlap in time on one device -- on different streams,
+ *     or from different host threads without ordering -- race on the array
+ *     and give undefined results: serialise them.
+ */
+#define EDA_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+eda_status_t eda_fwd_chunked_noalloc(const void *q, const void *k, const void *e, const void *v,
+                                     const float *alpha, const float *beta, const float *gamma,
+                                     const float *S0, void *o, float *S_final,
+                                     int B, int T, int H, int d_k, int d_v, eda_dtype_t dtype,
+                                     int chunk, void *stream);
 
 /*
  * One token of the recurrence for N independent sequences (decode).

@@ -42,7 +42,7 @@ DEFAULT_CHUNK = 64
 
 STATUS = {0: "EDA_OK", 1: "EDA_ERR_NULL", 2: "EDA_ERR_SHAPE", 3: "EDA_ERR_DTYPE",
           4: "EDA_ERR_ALIGN", 5: "EDA_ERR_UNSUPPORTED", 6: "EDA_ERR_WORKSPACE",
-          7: "EDA_ERR_ALIAS", 8: "EDA_ERR_HIP"}
+          7: "EDA_ERR_ALIAS", 8: "EDA_ERR_HIP", 9: "EDA_ERR_SCRATCH"}
 EDA_F32, EDA_BF16 = 0, 1
 
 
@@ -73,6 +73,9 @@ def load_library():
     lib.eda_fwd_chunked.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, vp, fp,
                                     i, i, i, i, i, i, i, vp, sz, vp]
     lib.eda_fwd_chunked.restype = i
+    lib.eda_fwd_chunked_noalloc.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, vp, fp,
+                                            i, i, i, i, i, i, i, vp]
+    lib.eda_fwd_chunked_noalloc.restype = i
     lib.eda_fwd_chunked_timed.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, vp, fp,
                                           i, i, i, i, i, i, i, vp, sz, vp, ctypes.POINTER(vp)]
     lib.eda_fwd_chunked_timed.restype = i
@@ -167,6 +170,25 @@ def fwd_chunked(q, k, e, v, alpha, beta, gamma, S0=None, *, chunk: int = 0,
     else:
         evs = (ctypes.c_void_p * 3)(*[ctypes.c_void_p(int(x)) for x in events])
         _check("eda_fwd_chunked_timed", lib.eda_fwd_chunked_timed(*args, evs))
+    return out, S_final
+
+
+def fwd_chunked_noalloc(q, k, e, v, alpha, beta, gamma, S0=None, *, out: torch.Tensor,
+                        S_final: Optional[torch.Tensor] = None,
+                        chunk: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fwd_chunked through eda_fwd_chunked_noalloc: the caller passes the
+    outputs (`out`, and `S_final` or None) and the library takes its workspace
+    from its per-device scratch array, so nothing is allocated."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    args = (_ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype), _ptr(e, "e", q.dtype), _ptr(v, "v", q.dtype),
+            _ptr(alpha, "alpha", torch.float32), _ptr(beta, "beta", torch.float32),
+            _ptr(gamma, "gamma", torch.float32), _ptr(S0, "S0", torch.float32),
+            _ptr(out, "o", q.dtype), _ptr(S_final, "S_final", torch.float32),
+            B, T, H, dk, dv, dt, chunk, _stream(q.device))
+    _check("eda_fwd_chunked_noalloc", lib.eda_fwd_chunked_noalloc(*args))
     return out, S_final
 
 

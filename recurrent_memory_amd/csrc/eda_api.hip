@@ -2,8 +2,17 @@
 // kernel launches.  Every check runs before anything is enqueued.
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/eda.h"
 #include "eda_common.h"
+
+// Workspace of eda_fwd_chunked_noalloc: one array per device, loaded with the
+// library's code object and held until the process ends.  In host code its
+// name is a stand-in, not a device address: the address is looked up once per
+// device with hipGetSymbolAddress and only that address is used.
+static __device__ __align__(256) char scratch[EDA_NOALLOC_SCRATCH_BYTES];
 
 namespace eda {
 template <typename Tin>
@@ -71,6 +80,32 @@ int resolve_chunk(int chunk) { return chunk == 0 ? kDefaultChunk : chunk; }
 
 bool chunk_supported(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call per device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (err != hipSuccess) return err;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 // fp32 inputs: a 64-token chunk's fp32 operands (two 128 x 128 key-side
 // tiles and their inverse) exceed one compute unit's LDS, so the fp32 path
 // computes chunk 64 as 32-token chunks; the chunk size does not change the
@@ -92,6 +127,7 @@ const char *eda_status_string(eda_status_t s) {
         case EDA_ERR_WORKSPACE: return "workspace missing or too small";
         case EDA_ERR_ALIAS: return "output overlaps an input";
         case EDA_ERR_HIP: return "HIP launch failed";
+        case EDA_ERR_SCRATCH: return "workspace needed exceeds the no-allocation scratch array (EDA_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
@@ -122,8 +158,9 @@ eda_status_t chunked_call(const void *q, const void *k, const void *e, const voi
                           const float *S0, void *o, float *S_final, int B, int T, int H, int d_k,
                           int d_v, eda_dtype_t dtype, int chunk, void *workspace,
                           size_t workspace_bytes, void *stream, void *const *events,
-                          bool dplr = false) {
-    // (dplr: the rank-1 DPLR update; `e` is its erase vector, beta and gamma are NULL)
+                          bool dplr = false, bool use_scratch = false) {
+    // (dplr: the rank-1 DPLR update; `e` is its erase vector, beta and gamma are NULL;
+    //  use_scratch: the workspace is the device's scratch array, not an argument)
     if (!q || !k || !e || !v || !alpha || !o || (!dplr && (!beta || !gamma))) return EDA_ERR_NULL;
     if (!dtype_ok(dtype)) return EDA_ERR_DTYPE;
     if (!dims_ok(B, T, H, d_k, d_v)) return EDA_ERR_SHAPE;
@@ -142,6 +179,12 @@ eda_status_t chunked_call(const void *q, const void *k, const void *e, const voi
     for (const void *p : vec_ptrs)
         if (p && !aligned(p, 16)) return EDA_ERR_ALIGN;
     const size_t need = eda_fwd_chunked_workspace_size(B, T, H, d_k, d_v, dtype, chunk);
+    if (use_scratch && need > 0) {
+        // every argument check above runs first; this is the first HIP call
+        if (need > EDA_NOALLOC_SCRATCH_BYTES) return EDA_ERR_SCRATCH;
+        if (scratch_address(&workspace) != hipSuccess) return EDA_ERR_HIP;
+        workspace_bytes = EDA_NOALLOC_SCRATCH_BYTES;
+    }
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return EDA_ERR_WORKSPACE;
         if (((uintptr_t)workspace & 255u) != 0) return EDA_ERR_ALIGN;
@@ -185,6 +228,14 @@ eda_status_t eda_fwd_chunked(const void *q, const void *k, const void *e, const 
                              size_t workspace_bytes, void *stream) {
     return chunked_call(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v, dtype,
                         chunk, workspace, workspace_bytes, stream, nullptr);
+}
+
+eda_status_t eda_fwd_chunked_noalloc(const void *q, const void *k, const void *e, const void *v,
+                                     const float *alpha, const float *beta, const float *gamma,
+                                     const float *S0, void *o, float *S_final, int B, int T, int H,
+                                     int d_k, int d_v, eda_dtype_t dtype, int chunk, void *stream) {
+    return chunked_call(q, k, e, v, alpha, beta, gamma, S0, o, S_final, B, T, H, d_k, d_v, dtype,
+                        chunk, nullptr, 0, stream, nullptr, false, true);
 }
 
 eda_status_t eda_fwd_chunked_timed(const void *q, const void *k, const void *e, const void *v,

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = eda.load_library()
-    for code in range(9):
+    for code in range(10):
         s = lib.eda_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.eda_status_string(99).decode() == "unknown status"
@@ -144,6 +144,28 @@ def test_timed_variant_checks_like_the_plain_call():
     assert call_chunked_timed(chunked_args(chunk=7), evs) == 5
     assert call_chunked_timed(chunked_args(ws=None), evs) == 6
     assert call_chunked_timed(chunked_args(o=fake(1, 256)), None) == 7
+
+
+def call_chunked_noalloc(a):
+    lib = eda.load_library()
+    return lib.eda_fwd_chunked_noalloc(a["q"], a["k"], a["e"], a["v"], a["alpha"], a["beta"], a["gamma"],
+                                       a["S0"], a["o"], a["S_final"], a["B"], a["T"], a["H"], a["dk"],
+                                       a["dv"], a["dt"], a["chunk"], a["stream"])
+
+
+def test_noalloc_variant_checks_before_any_hip_call():
+    # argument checks are the plain call's; a problem beyond the scratch array
+    # is rejected (EDA_ERR_SCRATCH) before the array is looked up
+    assert call_chunked_noalloc(chunked_args(q=None)) == 1
+    assert call_chunked_noalloc(chunked_args(dt=5)) == 3
+    assert call_chunked_noalloc(chunked_args(chunk=7)) == 5
+    assert call_chunked_noalloc(chunked_args(o=fake(9, 8))) == 4
+    ws = eda.load_library().eda_fwd_chunked_workspace_size
+    limit = 160 << 20
+    # bf16, d = 128, chunk 64: 74240 bytes per chunk-head, 2259 fit
+    assert ws(1, 64 * 2259, 1, 128, 128, 1, 64) <= limit < ws(1, 64 * 2260, 1, 128, 128, 1, 64)
+    assert call_chunked_noalloc(chunked_args(B=1, T=64 * 2260, H=1, dk=128, dv=128, dt=1, chunk=64)) == 9
+    assert call_chunked_noalloc(chunked_args(B=8, T=4096, H=16, dk=128, dv=128, dt=0, chunk=0)) == 9
 
 
 def test_chunked_too_large_shape():
