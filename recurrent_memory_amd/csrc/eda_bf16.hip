@@ -294,7 +294,11 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     // ---- full aligned chunk: fetched one item ahead.  Rows are clamped to the
     //      sequence so the same loads are issued for every item and the only
     //      wait on them is where they are first used. -----------------------------
-    auto prefetch = [&](int it) __attribute__((always_inline)) {
+    auto prefetch_at = [&](int it, auto part) __attribute__((always_inline)) {
+        // part 1: the decay input (alpha, or the layer form's gate input and
+        // parameters), consumed by the scan; part 2: q, e, k and the gates,
+        // consumed by the formation; 3: both
+        constexpr int PART = decltype(part)::value;
         const int bh = head_of(it), cidx = chunk_of(it);
         const int b = bh / H, h = bh % H;
         const int t0 = cidx * C, last = Tlen - 1 - t0, hk = h / grp;
@@ -303,26 +307,38 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const long off = (tokk0 + (long)min(tok(i), last) * Hk) * dk + c0;
-            xq[i] = *(const uint4 *)(q + off);
-            xe[i] = *(const uint4 *)(e + off);
-            xk[i] = *(const uint4 *)(k + off);
-            if constexpr (LAYER) {
-                xg[i] = *(const uint4 *)(agate + off);
-            } else {
-                xa[i][0] = *(const f32x4 *)(alpha + off);
-                xa[i][1] = *(const f32x4 *)(alpha + off + 4);
+            if constexpr (PART & 2) {
+                xq[i] = *(const uint4 *)(q + off);
+                xe[i] = *(const uint4 *)(e + off);
+                xk[i] = *(const uint4 *)(k + off);
+            }
+            if constexpr (PART & 1) {
+                if constexpr (LAYER) {
+                    xg[i] = *(const uint4 *)(agate + off);
+                } else {
+                    xa[i][0] = *(const f32x4 *)(alpha + off);
+                    xa[i][1] = *(const f32x4 *)(alpha + off + 4);
+                }
             }
         }
-        if constexpr (LAYER) {
+        if constexpr (LAYER && (PART & 1)) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 xA[hh] = *(const f32x4 *)(A_log + (long)hk * dk + c0 + 4 * hh);
                 xB[hh] = *(const f32x4 *)(dt_bias + (long)hk * dk + c0 + 4 * hh);
             }
         }
-        const long tb = tok0 + (long)min(tid % C, last) * H;
-        pbeta = DPLR ? 1.f : beta[tb];
-        pgamma = DPLR ? 0.f : gamma[tb];
+        if constexpr (PART & 2) {
+            const long tb = tok0 + (long)min(tid % C, last) * H;
+            pbeta = DPLR ? 1.f : beta[tb];
+            pgamma = DPLR ? 0.f : gamma[tb];
+        }
+    };
+    auto prefetch = [&](int it) __attribute__((always_inline)) { prefetch_at(it, std::integral_constant<int, 3>{}); };
+    // the next item of this workgroup (clamped: the last item refetches itself)
+    auto next_item = [&](int it) __attribute__((always_inline)) {
+        const int nx = it + gridDim.x;
+        return nx < items ? nx : items - 1;
     };
     // ---- ragged or unaligned chunk: element-wise, zero keys and queries and
     //      alpha = 1 outside the sequence and beyond d_k -----------------------------
@@ -491,6 +507,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     g[i][j] = carry[j] + x;
                     carry[j] += __shfl(x, (RA - 1) * NO + o, 64);
                 }
+            // the decay input is consumed: the next item's is fetched now
+            if constexpr (VEC) prefetch_at(next_item(it), std::integral_constant<int, 1>{});
             if (r == 0) {
                 *(f32x4 *)(wtot + wave * D + c0) = f32x4{carry[0], carry[1], carry[2], carry[3]};
                 *(f32x4 *)(wtot + wave * D + c0 + 4) = f32x4{carry[4], carry[5], carry[6], carry[7]};
@@ -523,8 +541,10 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 wide_here |= act && tot[j] < -WIDE_G2;
             }
         }
-        // wide-chunk vote (every read of the totals precedes this barrier)
-        const bool wide = __syncthreads_or(wide_here) != 0;
+        // wide chunk: every wave sums the same totals in the same order, and its lanes
+        // cover every channel, so a ballot gives each wave the same decision with no
+        // barrier (the totals' region is next written after the formation barrier)
+        const bool wide = __ballot(wide_here) != 0ull;
 
         // LAYER: (1/|q|, 1/|k|, 1/|e|) of token row i, reduced over the NO lanes of
         // the row (x / max(|x|, eps))
@@ -635,7 +655,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         // ---- A (strictly lower) and P (causal, as a bf16 pair); diagonal blocks
         //      of A inverted ------------------------------------------------------------
         constexpr int NOD = NB * (NB - 1) / 2;
-        constexpr int NPT = NB * NBC;
+        constexpr int NPV = NBC * (NBC + 1);   // P tiles (I, Tb) with rows i < 32 Tb + 32
+        static_assert(NB == 2 * NBC, "two sub-step blocks per token block");
         if (!wide) {
             if (wave < NB) {
                 const int J = wave;
@@ -649,7 +670,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 invert_diag(J);
             }
             // off-diagonal A and P tiles, spread over every wave
-            for (int t = (wave + NW - NB) % NW; t < NOD + NPT; t += NW) {
+            for (int t = (wave + NW - NB) % NW; t < NOD + NPV; t += NW) {
                 const auto [lane, g4, l16, gq] = lane_ids(tid);
                 if (t < NOD) {
                     int J = 1, I = t;
@@ -661,15 +682,15 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                         MI[(16 * I + g4 + rr) * LDL + 16 * J + l16] = from_f32<T>(a[rr]);
                 } else {
                     // P^T tile: rows = sub-steps i, cols = tokens; kept for i <= 2 tau + 1
-                    const int I = (t - NOD) / NBC, Tb = (t - NOD) % NBC;
+                    // (token block Tb holds the 2 Tb + 2 row blocks I of its stored rows)
+                    int Tb = 0, I = t - NOD;
+                    while (I >= 2 * Tb + 2) { I -= 2 * Tb + 2; ++Tb; }
                     const int tau = 16 * Tb + l16, i0 = 16 * I + g4;
-                    if (16 * I < 32 * Tb + 32) {   // else beyond the stored row
-                        const f32x4 a = tile_nt<T, D>(Kr + 16 * I * LDA, LDA, Ql + 16 * Tb * LDA, LDA, zero4(), lane);
-                        float w4[4];
+                    const f32x4 a = tile_nt<T, D>(Kr + 16 * I * LDA, LDA, Ql + 16 * Tb * LDA, LDA, zero4(), lane);
+                    float w4[4];
 #pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) w4[rr] = (i0 + rr <= 2 * tau + 1) ? a[rr] : 0.f;
-                        store_p(tau, i0, w4[0], w4[1], w4[2], w4[3]);
-                    }
+                    for (int rr = 0; rr < 4; ++rr) w4[rr] = (i0 + rr <= 2 * tau + 1) ? a[rr] : 0.f;
+                    store_p(tau, i0, w4[0], w4[1], w4[2], w4[3]);
                 }
             }
         } else {
@@ -713,14 +734,12 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             // every read of G and of the raw keys is done: form the operands in place
             if (act) form_operands();
         }
+        // the raw keys and queries are consumed: the next item's are fetched now,
+        // before the barrier, so waves with fewer tiles issue them while the others
+        // finish (the decay input was fetched after the scan; spread out this way,
+        // the fetches stall less on the memory system)
+        if constexpr (VEC) prefetch_at(next_item(it), std::integral_constant<int, 2>{});
         __syncthreads();
-
-        // the next item's raw values: fetched now, first used by the next item's
-        // scan (the current item's raw registers are dead once the operands exist)
-        if constexpr (VEC) {
-            const int nx = it + gridDim.x;
-            prefetch(nx < items ? nx : items - 1);
-        }
 
         // ---- Y = M^T Khat and Z^T = M^T P^T, M = (I + A)^{-1}, by block backward
         //      substitution: (I + A)^T X = R for the right-hand sides R = [Khat | P^T],
@@ -734,76 +753,129 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         //      Every product here is the 16x16x16 instruction.  (Yhat = Y Diag(e^r) =
         //      M^T Khat is kept, bounded by |M|: Y^T Kl would otherwise reach e^{|G_C|},
         //      past the fp32 range, for channels decaying by more than about e^-88.)
-        for (int cb = wave; cb < NBD + NBC; cb += NW) {
+        // Column blocks ("chains": Y blocks nb < NBD, then Z blocks tb) go round-robin
+        // to the waves; a wave runs its chains two at a time, interleaved step by step,
+        // so one chain's latency hides behind the other's work, and both share the
+        // diagonal-inverse and off-diagonal block reads of each step.  The chain kinds
+        // are template arguments, so the unrolled steps hold no branch: a Z chain runs
+        // every step (its bracket is zero above its last row block, so X_K = 0 there
+        // exactly, and its Phat entries there are the causal zeros), and sends its
+        // dead Z stores to the diagonal blocks' fp32 region, unused by now.
+        auto run_chains = [&](auto kinds, int c0, int c1) __attribute__((always_inline)) {
+            // kinds: bit 0 set = first chain is a Z block, bit 1 = second is, bit 2 = a pair
+            constexpr int KIND = decltype(kinds)::value;
+            constexpr int NCH = (KIND & 4) ? 2 : 1;
+            constexpr bool KY[2] = {(KIND & 1) == 0, (KIND & 2) == 0};
             const auto [lane, g4, l16, gq] = lane_ids(tid);
-            const bool isY = cb < NBD;
-            const int nb = cb, tb = cb - NBD;
-            const int Jtop = isY ? NB - 1 : imin(NB - 1, 2 * tb + 1);   // Z: P is zero below 32 tb + 32
-            const float scale = isY ? ers[16 * nb + l16] : 1.f;        // Khat = Kr e^r, column n
-            const int pr = isY ? 0 : G::poff(tb) + l16 * G::pld(tb);    // P row of token 16 tb + l16
-            // right-looking: every row block's bracket starts as R_J; once X_K is solved
-            // it updates all the brackets above it at once (independent products), so
-            // the chain from one solved block to the next is one update, the pair split
-            // and the two diagonal-inverse products
-            f32x4 acc[NB];
+            const int cbs[2] = {c0, c1};
+            int nb[NCH], tb[NCH], Jtop[NCH], pr[NCH];
+            f32x4 acc[NCH][NB];
 #pragma unroll
-            for (int J = 0; J < NB; ++J) {
-                if (J > Jtop) continue;
-                if (isY) {
-                    const s16x4 r = frag_col4(Kr + 16 * J * LDA + 16 * nb, LDA, lane);   // rows 16 J + g4 + i
-                    const uint2 u = __builtin_bit_cast(uint2, r);
-                    acc[J] = f32x4{lo_bf16(u.x), hi_bf16(u.x), lo_bf16(u.y), hi_bf16(u.y)} * scale;
+            for (int c = 0; c < NCH; ++c) {
+                const int cb = cbs[c];
+                nb[c] = cb;
+                tb[c] = cb - NBD;
+                Jtop[c] = KY[c] ? NB - 1 : imin(NB - 1, 2 * tb[c] + 1);   // Z: P is zero below 32 tb + 32
+                pr[c] = KY[c] ? 0 : G::poff(tb[c]) + l16 * G::pld(tb[c]); // P row of token 16 tb + l16
+                // right-looking: every row block's bracket starts as R_J; once X_K is solved
+                // it updates all the brackets above it at once (independent products), so
+                // the chain from one solved block to the next is one update, the pair split
+                // and the two diagonal-inverse products
+                if (KY[c]) {
+                    const float scale = ers[16 * nb[c] + l16];   // Khat = Kr e^r, column n
+#pragma unroll
+                    for (int J = 0; J < NB; ++J) {
+                        const s16x4 r = frag_col4(Kr + 16 * J * LDA + 16 * nb[c], LDA, lane);   // rows 16 J + g4 + i
+                        const uint2 u = __builtin_bit_cast(uint2, r);
+                        acc[c][J] = f32x4{lo_bf16(u.x), hi_bf16(u.x), lo_bf16(u.y), hi_bf16(u.y)} * scale;
+                    }
                 } else {
-                    const uint2 h = *(const uint2 *)(Ph + pr + 16 * J + g4);
-                    const uint2 l = *(const uint2 *)(Pl + pr + 16 * J + g4);
-                    acc[J] = f32x4{lo_bf16(h.x) + lo_bf16(l.x), hi_bf16(h.x) + hi_bf16(l.x),
-                                   lo_bf16(h.y) + lo_bf16(l.y), hi_bf16(h.y) + hi_bf16(l.y)};
+#pragma unroll
+                    for (int J = 0; J < NB; ++J) {
+                        // (rows beyond the stored part read as zero)
+                        const bool in = J <= Jtop[c];
+                        const int off = in ? pr[c] + 16 * J + g4 : pr[c];
+                        const uint2 h = *(const uint2 *)(Ph + off);
+                        const uint2 l = *(const uint2 *)(Pl + off);
+                        const f32x4 v = f32x4{lo_bf16(h.x) + lo_bf16(l.x), hi_bf16(h.x) + hi_bf16(l.x),
+                                              lo_bf16(h.y) + lo_bf16(l.y), hi_bf16(h.y) + hi_bf16(l.y)};
+                        acc[c][J] = in ? v : zero4();
+                    }
                 }
             }
 #pragma unroll
             for (int K = NB - 1; K >= 0; --K) {
-                if (K > Jtop) continue;
                 // X_K = M_KK^T acc[K], acc[K] as a bf16 pair
                 const s16x4 mt = *(const s16x4 *)(MT + (16 * K + l16) * MTW + g4);
-                const f32x4 a = acc[K];
-                const uint32_t h01 = pack_bf16(a[0], a[1]), h23 = pack_bf16(a[2], a[3]);
-                const uint32_t l01 = pack_bf16(a[0] - lo_bf16(h01), a[1] - hi_bf16(h01));
-                const uint32_t l23 = pack_bf16(a[2] - lo_bf16(h23), a[3] - hi_bf16(h23));
-                f32x4 x = mma16(mt, __builtin_bit_cast(s16x4, make_uint2(h01, h23)), zero4());
-                x = mma16(mt, __builtin_bit_cast(s16x4, make_uint2(l01, l23)), x);
-                const uint32_t x01 = pack_bf16(x[0], x[1]), x23 = pack_bf16(x[2], x[3]);
-                const s16x4 xn = __builtin_bit_cast(s16x4, make_uint2(x01 ^ 0x80008000u, x23 ^ 0x80008000u));
-                // acc[J] -= A_KJ^T X_K for every J < K (A_KJ stored at block (J, K)); the
-                // bracket solved next (J = K - 1) is updated first, and every operand
-                // is read before the first product
                 s16x4 ak[NB];
 #pragma unroll
                 for (int J = K - 1; J >= 0; --J) ak[J] = frag_col4(MI + 16 * J * LDL + 16 * K, LDL, lane);
+                uint32_t x01[NCH], x23[NCH];
+                f32x4 x[NCH];
 #pragma unroll
-                for (int J = K - 1; J >= 0; --J) acc[J] = mma16(ak[J], xn, acc[J]);
+                for (int c = 0; c < NCH; ++c) {
+                    const f32x4 a = acc[c][K];
+                    const uint32_t h01 = pack_bf16(a[0], a[1]), h23 = pack_bf16(a[2], a[3]);
+                    const uint32_t l01 = pack_bf16(a[0] - lo_bf16(h01), a[1] - hi_bf16(h01));
+                    const uint32_t l23 = pack_bf16(a[2] - lo_bf16(h23), a[3] - hi_bf16(h23));
+                    x[c] = mma16(mt, __builtin_bit_cast(s16x4, make_uint2(h01, h23)), zero4());
+                    x[c] = mma16(mt, __builtin_bit_cast(s16x4, make_uint2(l01, l23)), x[c]);
+                }
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    x01[c] = pack_bf16(x[c][0], x[c][1]);
+                    x23[c] = pack_bf16(x[c][2], x[c][3]);
+                }
+                // acc[J] -= A_KJ^T X_K for every J < K (A_KJ stored at block (J, K)); the
+                // bracket solved next (J = K - 1) is updated first
+#pragma unroll
+                for (int J = K - 1; J >= 0; --J)
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+                        acc[c][J] = mma16(ak[J], __builtin_bit_cast(s16x4, make_uint2(x01[c] ^ 0x80008000u,
+                                                                                      x23[c] ^ 0x80008000u)),
+                                          acc[c][J]);
                 // lane: X[16 K + g4 + i][column l16 of the block]; delta rows j = 16 K + g4 + 1, + 3
                 const int t0 = 8 * K + 2 * gq;
                 const float2 bt = *(const float2 *)(sb + t0);
-                const uint32_t ev = pack_bf16(x[1] * bt.x, x[3] * bt.y);
-                if (isY) {
-                    // Psi[n][t], n = 16 nb + l16
-                    *(uint32_t *)(wsb + F::oPsi + ((nb * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
-                                  2 * (t0 & 7)) = ev;
-                    T *yk = Kr + (16 * K + g4) * LDA + 16 * nb + l16;
-                    yk[0] = (T)(x01 & 0xffffu);
-                    yk[LDA] = (T)(x01 >> 16);
-                    yk[2 * LDA] = (T)(x23 & 0xffffu);
-                    yk[3 * LDA] = (T)(x23 >> 16);
-                } else {
-                    // Phat[t][t'], t = 16 tb + l16; Z[t][16 K + g4 ..]
-                    *(uint32_t *)(wsb + F::oPh + ((tb * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
-                                  2 * (t0 & 7)) = ev;
-                    *(uint2 *)(Zs + pr + 16 * K + g4) = make_uint2(x01, x23);
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const uint32_t ev = pack_bf16(x[c][1] * bt.x, x[c][3] * bt.y);
+                    if (KY[c]) {
+                        // Psi[n][t], n = 16 nb + l16
+                        *(uint32_t *)(wsb + F::oPsi + ((nb[c] * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
+                                      2 * (t0 & 7)) = ev;
+                        T *yk = Kr + (16 * K + g4) * LDA + 16 * nb[c] + l16;
+                        yk[0] = (T)(x01[c] & 0xffffu);
+                        yk[LDA] = (T)(x01[c] >> 16);
+                        yk[2 * LDA] = (T)(x23[c] & 0xffffu);
+                        yk[3 * LDA] = (T)(x23[c] >> 16);
+                    } else {
+                        // Phat[t][t'], t = 16 tb + l16; Z[t][16 K + g4 ..]
+                        *(uint32_t *)(wsb + F::oPh + ((tb[c] * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
+                                      2 * (t0 & 7)) = ev;
+                        T *zd = K <= Jtop[c] ? Zs + pr[c] + 16 * K + g4 : (T *)AdT + 4 * lane;
+                        *(uint2 *)zd = make_uint2(x01[c], x23[c]);
+                    }
                 }
             }
             if constexpr (C == 16) {
                 // tokens 16 .. 31 of the k = 32 fragment are zero
-                if (isY && lane >= 32) *(uint4 *)(wsb + F::oPsi + (nb * KSC * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    if (KY[c] && lane >= 32)
+                        *(uint4 *)(wsb + F::oPsi + (nb[c] * KSC * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
+            }
+        };
+        for (int cb = wave; cb < NBD + NBC; cb += 2 * NW) {
+            const int cb1 = cb + NW;
+            if (cb1 < NBD + NBC) {
+                if (cb1 < NBD) run_chains(std::integral_constant<int, 4>{}, cb, cb1);
+                else if (cb < NBD) run_chains(std::integral_constant<int, 6>{}, cb, cb1);
+                else run_chains(std::integral_constant<int, 7>{}, cb, cb1);
+            } else {
+                if (cb < NBD) run_chains(std::integral_constant<int, 0>{}, cb, 0);
+                else run_chains(std::integral_constant<int, 1>{}, cb, 0);
             }
         }
         // Phat is causal: the Z tiles of token block tb write tokens t' < 16 (tb + 1);
