@@ -144,8 +144,8 @@ eda_status_t eda_fwd_chunked_timed(const void *q, const void *k, const void *e, 
  *     must belong to that device.  Its address is looked up on the first
  *     call on each device.
  *   - A problem whose eda_fwd_chunked_workspace_size exceeds
- *     EDA_NOALLOC_SCRATCH_BYTES (bf16 at d_k = d_v = 128 and chunk 64 fits
- *     B*H*ceil(T/64) <= 2259 chunk-heads, e.g. B=4, H=16, T=2048) is rejected with
+ *     EDA_NOALLOC_SCRATCH_BYTES (bf16 at d_k = d_v = 128 and chunk 64 with 64
+ *     heads fits T <= 2240, e.g. B=4, H=16, T=2048) is rejected with
  *     EDA_ERR_SCRATCH before anything is enqueued; use eda_fwd_chunked.
  *   - Every call on a device shares that device's array, which keeps the
  *     last call's contents (no call reads what an earlier call left there).

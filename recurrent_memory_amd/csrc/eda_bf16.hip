@@ -957,17 +957,31 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: state pass.  One workgroup per (head, BV-column slice); the
-// slices of one head get workgroup ids congruent mod 8 (same XCD, one L2 for
-// the shared factor blocks).  Per chunk c, one barrier, then
+// Kernel 2: state pass.  The chunks of a head are walked in order; one
+// workgroup owns a BV-column slice of one head's state over one range of
+// chunks.  Per chunk c, one barrier, then
 //   state waves (D/16): 16 rows of S <- e^{G_C} S + Phi S + Psi V, then S^T (bf16)
 //                       for the next chunk;
 //   output waves (C/16): 16 tokens of o = Qhat S + Phat V (transposed, so rows of
 //                       o leave as 16-byte runs), and the value rows and outputs
 //                       between HBM and LDS.
 // Each wave fetches its own factor fragments two chunks ahead (chunk indices
-// clamped, never skipped, so every wait covers only those fetches).
+// clamped, never skipped, so every wait covers only those fetches).  The
+// slices of one (head, range) get workgroup ids congruent mod 8 (same XCD, one
+// L2 for the shared factor blocks).
+//
+// Segments.  A workgroup's time per chunk is bound by fetching the chunk's
+// factor blocks, whatever the slice width, so with few heads the chunks of a
+// head are cut into P ranges ("segments") walked at the same time, with wide
+// slices.  The chunk maps compose: over segment s, S_out = M_s S_in + N_s, with
+// M_s the product of the chunk maps e^{G_C} + Phi and N_s the end state from a
+// zero start.  KIND_SUMMARY walks segment s < P - 1 on the augmented state
+// [M | N], started from [I | 0] (no outputs; the M columns take no value
+// term); eda_bf16_combine takes the prefix S_in(s + 1) = M_s S_in(s) + N_s in
+// fp32; KIND_PASS walks every segment from its start state, with outputs.
 // ---------------------------------------------------------------------------
+constexpr int KIND_PASS = 0, KIND_SUMMARY = 1;
+
 template <int C, int D, int BV>
 struct K2G {
     using F = Fac<C, D>;
@@ -978,7 +992,7 @@ struct K2G {
     static constexpr int LDT = D + 8, LDV = BV + 8, LDO = BV + 8;
     static constexpr int VR = imax(C, 32);                          // value rows (rows >= C stay zero)
     static constexpr int VPL = BV / 8;                              // 16-byte pieces per value row
-    static_assert(16 * VPL <= 64, "one value piece per lane per token block");
+    static constexpr int NPO = (16 * VPL + 63) / 64;                // pieces per output-wave lane
     static constexpr int szSt = align16(BV * LDT * 2), szVs = align16(VR * LDV * 2);
     static constexpr int oSt = 0;                                   // S^T [2][BV][LDT] bf16
     static constexpr int oVs = oSt + 2 * szSt;                      // V   [2][VR][LDV] bf16
@@ -986,11 +1000,11 @@ struct K2G {
     static constexpr int LDS = oOs + align16(C * LDO * 2);
 };
 
-template <int NF>
+template <int NF, int NPO>
 struct FragSet {
     bf16x8 R[NF];   // the role's factor fragments of one chunk
     f32x4 dec;      // state role: e^{G_C} of its rows
-    uint4 v;        // output role: one 16-byte piece of the value slice
+    uint4 v[NPO];   // output role: 16-byte pieces of the value slice
     uint32_t pf[2]; // output role: L2 warm-up words
 };
 
@@ -1005,27 +1019,40 @@ constexpr size_t WARM_MIN_BYTES = (size_t)256 << 20;   // MI355X MALL capacity
 
 // VV: every value slice is whole (d_v a multiple of BV) and v is 16-byte
 // aligned, so values and outputs move as 16-byte row pieces.
-template <int C, int D, int BV, bool VV>
+//
+// Work units: KIND_PASS, NSEG = P units per head (one per segment), R = the
+// value slices; KIND_SUMMARY, NSEG = P - 1, R = RX + the value slices, slices
+// below RX holding the M columns (key channels).  NCS chunks per segment.
+// segbuf: KIND_PASS, the start states of segments 1 .. P-1, [BH][P-1][d_k][d_v]
+// (NULL when P = 1); KIND_SUMMARY, the maps written, [BH][P-1][d_k][d_k + d_v]
+// (M in the first d_k columns, N in the rest).
+template <int C, int D, int BV, bool VV, int KIND>
 __global__ void __launch_bounds__((K2G<C, D, BV>::NT))
 eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16 *__restrict__ o,
-               const char *__restrict__ ws, int Tlen, int H, int BH, int dk, int dv, int NC, int R,
-               int warm) {
+               const char *__restrict__ ws, float *segbuf, int Tlen, int H, int BH, int dk, int dv,
+               int NC, int R, int RX, int NSEG, int NCS, int warm) {
     using G = K2G<C, D, BV>;
     using F = Fac<C, D>;
     using T = bf16;
+    constexpr bool SUM = KIND == KIND_SUMMARY;
     constexpr int NCB = G::NCB, KSD = G::KSD, KSC = G::KSC, LDT = G::LDT, LDV = G::LDV, LDO = G::LDO;
-    constexpr int NSW = G::NSW, VPL = G::VPL;
+    constexpr int NSW = G::NSW, VPL = G::VPL, NPO = G::NPO;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Os = (T *)(smem + G::oOs);
 
     const int w = blockIdx.x, xcd = w & 7, slot = w >> 3;
-    const int bh = (slot / R) * 8 + xcd, slice = slot % R;
-    if (bh >= BH) return;
-    const int b = bh / H, h = bh % H, n0 = slice * BV;
-    const long sbase = (long)bh * dk * dv;
+    const int unit = (slot / R) * 8 + xcd, slice = slot % R;
+    if (unit >= BH * NSEG) return;
+    const int bh = unit / NSEG, seg = unit % NSEG;
+    const int c_lo = seg * NCS, c_hi = min(NC, c_lo + NCS);
+    // KIND_SUMMARY: slices below RX hold M's columns (identity start, no value term)
+    const bool mcols = SUM && slice < RX;
+    const int n0 = SUM && !mcols ? (slice - RX) * BV : slice * BV;   // first column within its part
+    const int ncols = mcols ? dk : dv;                                // columns of that part
+    const int b = bh / H, h = bh % H;
     const long hrow = (long)b * Tlen * H + h;
     const long HV = (long)H * dv;
-    const T *vh = v + hrow * dv + n0;
+    const T *vh = v + hrow * dv + (mcols ? 0 : n0);
     T *oh = o + hrow * dv + n0;
     const char *wsh = ws + (long)bh * NC * F::bytes;
 
@@ -1046,11 +1073,11 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
     auto run = [&](auto role) __attribute__((always_inline)) {
         constexpr bool RS = decltype(role)::value == 0;   // state role, else output role
         constexpr int NF = KSD + KSC;
-        using Set = FragSet<NF>;
+        using Set = FragSet<NF, NPO>;
         const int rb = RS ? wave : wave - NSW;            // row block: state rows or tokens
-        // output role: this lane's piece of the value slice (token 16 rb + vr, columns 8 vc ..)
-        const int vr = lane / VPL, vc = lane % VPL;
-        const bool vact = !RS && lane < 16 * VPL;
+        // output role: the lane's pieces p = lane + 64 j of the value slice (token
+        // 16 rb + p / VPL, columns 8 (p % VPL) ..)
+        auto vpiece = [&](int j) __attribute__((always_inline)) { return lane + 64 * j; };
 
         auto load = [&](Set &s, int c) __attribute__((always_inline)) {
             const char *blk = wsh + (long)c * F::bytes;
@@ -1061,26 +1088,33 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 for (int ks = 0; ks < KSC; ++ks) s.R[KSD + ks] = ld_frag(blk + F::oPsi + ((rb * KSC + ks) * 64 + lane) * 16);
                 s.dec = *(const f32x4 *)(blk + F::oDec + 4 * (16 * rb + g4));
             } else {
+                if constexpr (!SUM) {
 #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) s.R[ks] = ld_frag(blk + F::oQh + ((rb * KSD + ks) * 64 + lane) * 16);
+                    for (int ks = 0; ks < KSD; ++ks) s.R[ks] = ld_frag(blk + F::oQh + ((rb * KSD + ks) * 64 + lane) * 16);
 #pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) s.R[KSD + ks] = ld_frag(blk + F::oPh + ((rb * KSC + ks) * 64 + lane) * 16);
-                const int t = c * C + 16 * rb + vr, tc = t < Tlen ? t : Tlen - 1;
-                const bool ok = vact && t < Tlen;
-                uint4 x;
-                if constexpr (VV) {
-                    x = *(const uint4 *)(vh + tc * HV + 8 * vc);
-                } else {
-                    uint32_t y[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int col = 8 * vc + j, cc = n0 + col < dv ? col : dv - 1 - n0;
-                        y[j] = vh[tc * HV + cc];
-                        if (n0 + col >= dv) y[j] = 0u;
-                    }
-                    x = make_uint4(y[0] | (y[1] << 16), y[2] | (y[3] << 16), y[4] | (y[5] << 16), y[6] | (y[7] << 16));
+                    for (int ks = 0; ks < KSC; ++ks) s.R[KSD + ks] = ld_frag(blk + F::oPh + ((rb * KSC + ks) * 64 + lane) * 16);
                 }
-                s.v = ok ? x : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int j = 0; j < NPO; ++j) {
+                    const int p = vpiece(j), vr = p / VPL, vc = p % VPL;
+                    const int t = c * C + 16 * rb + vr, tc = t < Tlen ? t : Tlen - 1;
+                    const bool ok = p < 16 * VPL && t < Tlen && !mcols;
+                    const int vcc = p < 16 * VPL ? vc : 0;
+                    uint4 x;
+                    if constexpr (VV) {
+                        x = *(const uint4 *)(vh + tc * HV + 8 * vcc);
+                    } else {
+                        uint32_t y[8];
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) {
+                            const int col = 8 * vcc + jj, cc = n0 + col < dv ? col : dv - 1 - n0;
+                            y[jj] = mcols ? 0u : (uint32_t)vh[tc * HV + (cc < 0 ? 0 : cc)];
+                            if (n0 + col >= dv) y[jj] = 0u;
+                        }
+                        x = make_uint4(y[0] | (y[1] << 16), y[2] | (y[3] << 16), y[4] | (y[5] << 16), y[6] | (y[7] << 16));
+                    }
+                    s.v[j] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
+                }
                 s.pf[0] = s.pf[1] = 0u;
                 if (warm) {
                     const int cw = c + WARM_AHEAD < NC ? c + WARM_AHEAD : NC - 1;
@@ -1095,20 +1129,31 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
             }
         };
         auto put_v = [&](const Set &s, int c) __attribute__((always_inline)) {
-            if (vact) *(uint4 *)(Vs(c) + (16 * rb + vr) * LDV + 8 * vc) = s.v;
+#pragma unroll
+            for (int j = 0; j < NPO; ++j) {
+                const int p = vpiece(j);
+                if (!RS && p < 16 * VPL) *(uint4 *)(Vs(c) + (16 * rb + p / VPL) * LDV + 8 * (p % VPL)) = s.v[j];
+            }
         };
 
-        // state rows 16 rb + g4 + i, columns n0 + 16 cb + l16 (state role)
+        // state rows 16 rb + g4 + i, columns n0 + 16 cb + l16 of its part (state role)
         f32x4 S[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             S[cb] = zero4();
-            if (RS && S0) {
+            if (RS) {
                 const int col = n0 + 16 * cb + l16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * rb + g4 + i;
-                    if (row < dk && col < dv) S[cb][i] = S0[sbase + (long)row * dv + col];
+                    if (row >= dk || col >= ncols) continue;
+                    if constexpr (SUM) {
+                        S[cb][i] = mcols && row == col ? 1.f : 0.f;
+                    } else if (seg == 0) {
+                        if (S0) S[cb][i] = S0[((long)bh * dk + row) * dv + col];
+                    } else {
+                        S[cb][i] = segbuf[(((long)bh * (NSEG - 1) + seg - 1) * dk + row) * dv + col];
+                    }
                 }
             }
         }
@@ -1120,77 +1165,95 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
 
         // Phase c (one barrier): S_c^T is in St(c) and V_c in Vs(c).  The state
         // waves write S_{c+1}^T to St(c + 1), the output waves write V_{c+1} to
-        // Vs(c + 1): both buffers were last read in phase c - 1.
+        // Vs(c + 1): both buffers were last read in phase c - 1.  Each 16-column
+        // block's operands are read just before its products.
         auto body = [&](Set &cur, Set &nxt, Set &far, int c) __attribute__((always_inline)) {
-            const int cf = c + 2 < NC ? c + 2 : NC - 1;   // chunk whose operands are fetched now
+            const int cf = c + 2 < c_hi ? c + 2 : c_hi - 1;   // chunk whose operands are fetched now
             __syncthreads();
             const T *Sc = St(c), *Vc = Vs(c);
-            // value products first: they do not wait for the state
-            f32x4 acc[NCB];
-            bf16x8 vf[KSC][NCB];
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) vf[ks][cb] = frag_col(Vc + 32 * ks * LDV + 16 * cb, LDV, lane);
-            bf16x8 sf[KSD][NCB];
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) sf[ks][cb] = frag_row(Sc + 16 * cb * LDT + 32 * ks, LDT, lane);
+            // k-step outer, column block inner: the NCB accumulation chains interleave,
+            // and each k-step's operand fragments are read just before its products
             if constexpr (RS) {
                 // S <- e^{G_C} S + Psi V + Phi S  (rows 16 rb.., all slice columns)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    f32x4 a;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) a[i] = cur.dec[i] * S[cb][i];
-#pragma unroll
-                    for (int ks = 0; ks < KSC; ++ks) a = mma32(cur.R[KSD + ks], vf[ks][cb], a);
-                    acc[cb] = a;
-                }
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(cur.R[ks], sf[ks][cb], acc[cb]);
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) S[cb] = acc[cb];
-                if (c + 1 < NC) write_St(c + 1);
-                load(far, cf);
-            } else {
-                // o^T = V^T Phat^T + S^T Qhat^T for the wave's 16 tokens
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    f32x4 a = zero4();
-#pragma unroll
-                    for (int ks = 0; ks < KSC; ++ks) a = mma32(vf[ks][cb], cur.R[KSD + ks], a);
-                    acc[cb] = a;
-                }
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(sf[ks][cb], cur.R[ks], acc[cb]);
-                if (c + 1 < NC) put_v(nxt, c + 1);
-                asm volatile("" ::"v"(cur.pf[0]), "v"(cur.pf[1]));   // the warm-up words, consumed
-                // the wave's own 16 token rows: staged in LDS, then written as
-                // 16-byte row pieces (the rows are this wave's alone: no barrier)
-                const int tr = 16 * rb + l16;
+                f32x4 acc[NCB];
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
-                    store4<T>(Os + tr * LDO + 16 * cb + g4, acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
-                wave_lds_sync();
-                load(far, cf);
-                const int t = c * C + 16 * rb + vr;
-                if (vact && t < Tlen) {
-                    const uint4 val = *(const uint4 *)(Os + (16 * rb + vr) * LDO + 8 * vc);
-                    T *dst = oh + t * HV + 8 * vc;
-                    if constexpr (VV) {
-                        *(uint4 *)dst = val;
-                    } else {
-                        const uint32_t y[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            if (n0 + 8 * vc + j < dv) dst[j] = (T)((y[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                    for (int i = 0; i < 4; ++i) acc[cb][i] = cur.dec[i] * S[cb][i];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) {
+                    bf16x8 vf[NCB];
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) vf[cb] = frag_col(Vc + 32 * ks * LDV + 16 * cb, LDV, lane);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(cur.R[KSD + ks], vf[cb], acc[cb]);
+                }
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) {
+                    bf16x8 sf[NCB];
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) sf[cb] = frag_row(Sc + 16 * cb * LDT + 32 * ks, LDT, lane);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(cur.R[ks], sf[cb], acc[cb]);
+                }
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) S[cb] = acc[cb];
+                if (c + 1 < c_hi) write_St(c + 1);
+                load(far, cf);
+            } else {
+                if constexpr (!SUM) {
+                    // o^T = V^T Phat^T + S^T Qhat^T for the wave's 16 tokens
+                    f32x4 acc[NCB];
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < KSC; ++ks) {
+                        bf16x8 vf[NCB];
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) vf[cb] = frag_col(Vc + 32 * ks * LDV + 16 * cb, LDV, lane);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(vf[cb], cur.R[KSD + ks], acc[cb]);
                     }
+#pragma unroll
+                    for (int ks = 0; ks < KSD; ++ks) {
+                        bf16x8 sf[NCB];
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) sf[cb] = frag_row(Sc + 16 * cb * LDT + 32 * ks, LDT, lane);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma32(sf[cb], cur.R[ks], acc[cb]);
+                    }
+                    if (c + 1 < c_hi) put_v(nxt, c + 1);
+                    asm volatile("" ::"v"(cur.pf[0]), "v"(cur.pf[1]));   // the warm-up words, consumed
+                    // the wave's own 16 token rows: staged in LDS, then written as
+                    // 16-byte row pieces (the rows are this wave's alone: no barrier)
+                    const int tr = 16 * rb + l16;
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        store4<T>(Os + tr * LDO + 16 * cb + g4, acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
+                    wave_lds_sync();
+                    load(far, cf);
+#pragma unroll
+                    for (int j = 0; j < NPO; ++j) {
+                        const int p = vpiece(j), vr = p / VPL, vc = p % VPL;
+                        const int t = c * C + 16 * rb + vr;
+                        if (p < 16 * VPL && t < Tlen) {
+                            const uint4 val = *(const uint4 *)(Os + (16 * rb + vr) * LDO + 8 * vc);
+                            T *dst = oh + t * HV + 8 * vc;
+                            if constexpr (VV) {
+                                *(uint4 *)dst = val;
+                            } else {
+                                const uint32_t y[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+                                for (int jj = 0; jj < 8; ++jj)
+                                    if (n0 + 8 * vc + jj < dv) dst[jj] = (T)((y[jj >> 1] >> (16 * (jj & 1))) & 0xffffu);
+                            }
+                        }
+                    }
+                } else {
+                    // (summary: the values only)
+                    if (c + 1 < c_hi) put_v(nxt, c + 1);
+                    asm volatile("" ::"v"(cur.pf[0]), "v"(cur.pf[1]));
+                    load(far, cf);
                 }
             }
         };
@@ -1198,29 +1261,33 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
         // three operand sets in rotation: the chunk in use, the next, and the one
         // being fetched
         Set A, B, X;
-        load(A, 0);
-        load(B, NC > 1 ? 1 : 0);
-        if constexpr (RS) write_St(0);
-        else put_v(A, 0);
-        int c = 0;
-        for (; c + 3 <= NC; c += 3) {
+        load(A, c_lo);
+        load(B, c_lo + 1 < c_hi ? c_lo + 1 : c_lo);
+        if constexpr (RS) write_St(c_lo);
+        else put_v(A, c_lo);
+        int c = c_lo;
+        for (; c + 3 <= c_hi; c += 3) {
             body(A, B, X, c);
             body(B, X, A, c + 1);
             body(X, A, B, c + 2);
         }
-        if (c < NC) body(A, B, X, c);
-        if (c + 1 < NC) body(B, X, A, c + 1);
+        if (c < c_hi) body(A, B, X, c);
+        if (c + 1 < c_hi) body(B, X, A, c + 1);
 
         if constexpr (RS) {
-            if (S_final) {
-                // every read of S0 happened before the chunk loop, so S_final may be S0
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    const int col = n0 + 16 * cb + l16;
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int col = n0 + 16 * cb + l16;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 16 * rb + g4 + i;
-                        if (row < dk && col < dv) S_final[sbase + (long)row * dv + col] = S[cb][i];
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * rb + g4 + i;
+                    if (row >= dk || col >= ncols) continue;
+                    if constexpr (SUM) {
+                        // M_s in columns 0 .. d_k - 1, N_s after them
+                        segbuf[(((long)bh * NSEG + seg) * dk + row) * (dk + dv) + (mcols ? col : dk + col)] = S[cb][i];
+                    } else if (seg == NSEG - 1 && S_final) {
+                        // every read of S0 happened before the chunk loop, so S_final may be S0
+                        S_final[((long)bh * dk + row) * dv + col] = S[cb][i];
                     }
                 }
             }
@@ -1231,6 +1298,63 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
     else run(std::integral_constant<int, 1>{});
 }
 
+// Prefix over segments, fp32: S_in(s + 1) = M_s S_in(s) + N_s for s = 0 .. P-2,
+// with S_in(0) = S0 (zero when S0 is NULL).  One workgroup per (head, 16-column
+// slice of the value dimension); thread (row, half) holds 8 columns of one
+// state row.  Per step, S_in(s) and M_s (in two halves of its columns, loaded
+// row-contiguous) are staged in LDS.  maps: [BH][P-1][d_k][d_k + d_v]; starts
+// (written): [BH][P-1][d_k][d_v] for segments 1 .. P-1.
+constexpr int COMB_T = 256, COMB_KH = 64;
+__global__ void __launch_bounds__(COMB_T)
+eda_bf16_combine(const float *S0, const float *__restrict__ maps, float *__restrict__ starts, int BH, int dk,
+                 int dv, int P) {
+    __shared__ float Xs[128][16];
+    __shared__ float Ms[128][COMB_KH + 1];   // (+1: rows of one wave fall in distinct banks)
+    const int nsl = (dv + 15) / 16;
+    const int bh = blockIdx.x / nsl, c0 = 16 * (blockIdx.x % nsl);
+    const int tid = threadIdx.x, row = tid >> 1, cq = 8 * (tid & 1);
+    const bool live = row < dk;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int col = c0 + cq + j;
+        x[j] = (live && col < dv && S0) ? S0[((long)bh * dk + row) * dv + col] : 0.f;
+    }
+    for (int s = 0; s + 1 < P; ++s) {
+        const float *m = maps + ((long)bh * (P - 1) + s) * dk * (dk + dv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Xs[row][cq + j] = x[j];
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = c0 + cq + j;
+            y[j] = (live && col < dv) ? m[(long)row * (dk + dv) + dk + col] : 0.f;   // N_s
+        }
+        for (int k0 = 0; k0 < dk; k0 += COMB_KH) {
+            __syncthreads();
+            // M_s[:, k0 .. k0 + 63]: consecutive threads read consecutive columns
+            for (int idx = tid; idx < 128 * COMB_KH; idx += COMB_T) {
+                const int r = idx / COMB_KH, k = idx % COMB_KH;
+                Ms[r][k] = (r < dk && k0 + k < dk) ? m[(long)r * (dk + dv) + k0 + k] : 0.f;
+            }
+            __syncthreads();
+            const int kn = min(COMB_KH, dk - k0);
+            for (int k = 0; k < kn; ++k) {
+                const float mk = Ms[row][k];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) y[j] = fmaf(mk, Xs[k0 + k][cq + j], y[j]);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x[j] = y[j];
+            const int col = c0 + cq + j;
+            if (live && col < dv) starts[(((long)bh * (P - 1) + s) * dk + row) * dv + col] = y[j];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -1239,18 +1363,48 @@ static int pad_dim(int dk, int dv) {
     return p <= 32 ? 32 : (p <= 64 ? 64 : 128);
 }
 
-// Value-column slice width of the state pass: the narrowest slice (>= 16
-// columns) that still leaves at most one workgroup per compute unit (256 on
-// MI355X).
-static int slice_width(int BH, int D) {
-    int bv = 16;
-    while (bv < 32 && bv < D && (long)BH * (D / bv) > 256) bv *= 2;
-    return bv;
+// Plan of the state pass, a function of the sizes alone (the workspace size
+// repeats it): the value-column slice width BV and the segment count P.
+// Many heads: no segments, and the narrowest slice (>= 16 columns) that
+// still leaves at most one workgroup per compute unit (256 on MI355X).
+// Fewer heads than fill the chip even with 16-column slices, and a long
+// sequence: 64-column slices and P segments, the largest power of two that
+// keeps at least 128 chunks per segment and at most 256 workgroups in the
+// pass (segment maps double the factor reads of the state side, so shorter
+// segments cost more than they gain; measured on MI355X at d = 128).  NCS
+// chunks per segment; P is recounted from NCS so that no segment is empty.
+struct SegPlan {
+    int BV, P, NCS;
+};
+static SegPlan seg_plan(int BH, int NC, int D, int dv) {
+    SegPlan sp{16, 1, NC};
+    while (sp.BV < 32 && sp.BV < D && (long)BH * (D / sp.BV) > 256) sp.BV *= 2;
+    if (D >= 64 && (long)BH * (D / 16) < 256 && NC >= 256) {
+        sp.BV = 64;
+        const long units = (long)BH * ((dv + 63) / 64);
+        while (sp.P < 64 && NC >= 128 * 2 * sp.P && units * 2 * sp.P <= 256) sp.P *= 2;
+    }
+    sp.NCS = (NC + sp.P - 1) / sp.P;
+    sp.P = (NC + sp.NCS - 1) / sp.NCS;
+    return sp;
 }
 
 template <int C, int D>
-size_t ws_bytes(int B, int Tlen, int H) {
+size_t fac_bytes(int B, int Tlen, int H) {
     return (size_t)B * H * ((Tlen + C - 1) / C) * Fac<C, D>::bytes;
+}
+
+// segment maps [BH][P-1][d_k][d_k + d_v] and start states [BH][P-1][d_k][d_v]
+// (fp32), after the chunk factors
+static size_t seg_bytes(int BH, int dk, int dv, int P) {
+    return P > 1 ? (size_t)BH * (P - 1) * dk * ((size_t)dk + 2 * (size_t)dv) * 4 : 0;
+}
+
+template <int C, int D>
+size_t ws_bytes(int B, int Tlen, int H, int dk, int dv) {
+    const int NC = (Tlen + C - 1) / C;
+    const SegPlan sp = seg_plan(B * H, NC, D, dv);
+    return fac_bytes<C, D>(B, Tlen, H) + seg_bytes(B * H, dk, dv, sp.P);
 }
 
 template <int C, int D, int BV>
@@ -1271,7 +1425,7 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     auto k1 = layer  ? (vec ? eda_bf16_factors<C, D, true, MODE_LAYER> : eda_bf16_factors<C, D, false, MODE_LAYER>)
               : dplr ? (vec ? eda_bf16_factors<C, D, true, MODE_DPLR> : eda_bf16_factors<C, D, false, MODE_DPLR>)
                      : (vec ? eda_bf16_factors<C, D, true, MODE_PLAIN> : eda_bf16_factors<C, D, false, MODE_PLAIN>);
-    auto k2 = vv ? eda_bf16_state<C, D, BV, true> : eda_bf16_state<C, D, BV, false>;
+    auto k2 = vv ? eda_bf16_state<C, D, BV, true, KIND_PASS> : eda_bf16_state<C, D, BV, false, KIND_PASS>;
     hipError_t err = hipFuncSetAttribute((const void *)k1, hipFuncAttributeMaxDynamicSharedMemorySize, G1::LDS);
     if (err != hipSuccess) return err;
     int dev = 0, ncu = 256;
@@ -1289,11 +1443,29 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
+    const SegPlan sp = seg_plan(BH, NC, D, dv);
     const int R = (dv + BV - 1) / BV;
-    const int grid2 = 8 * ((BH + 7) / 8) * R;
-    const int warm = ws_bytes<C, D>(B, Tlen, H) > WARM_MIN_BYTES;
+    const int warm = fac_bytes<C, D>(B, Tlen, H) > WARM_MIN_BYTES;
+    float *maps = nullptr, *starts = nullptr;
+    if (sp.P > 1) {
+        // segment maps, their prefix, then the segments' passes
+        maps = (float *)((char *)ws + fac_bytes<C, D>(B, Tlen, H));
+        starts = maps + (size_t)BH * (sp.P - 1) * dk * (dk + dv);
+        const int RX = (dk + BV - 1) / BV;
+        const int gridS = 8 * ((BH * (sp.P - 1) + 7) / 8) * (RX + R);
+        auto ks = vv ? eda_bf16_state<C, D, BV, true, KIND_SUMMARY> : eda_bf16_state<C, D, BV, false, KIND_SUMMARY>;
+        hipLaunchKernelGGL(ks, dim3((unsigned)gridS), dim3(G2::NT), G2::LDS, stream, (const bf16 *)v, S0,
+                           S_final, (bf16 *)o, (const char *)ws, maps, Tlen, H, BH, dk, dv, NC, RX + R, RX,
+                           sp.P - 1, sp.NCS, warm);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(eda_bf16_combine, dim3((unsigned)(BH * ((dv + 15) / 16))), dim3(COMB_T), 0, stream,
+                           S0, (const float *)maps, starts, BH, dk, dv, sp.P);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    const int grid2 = 8 * ((BH * sp.P + 7) / 8) * R;
     hipLaunchKernelGGL(k2, dim3((unsigned)grid2), dim3(G2::NT), G2::LDS, stream, (const bf16 *)v, S0,
-                       S_final, (bf16 *)o, (const char *)ws, Tlen, H, BH, dk, dv, NC, R, warm);
+                       S_final, (bf16 *)o, (const char *)ws, starts, Tlen, H, BH, dk, dv, NC, R, 0, sp.P,
+                       sp.NCS, warm);
     err = hipGetLastError();
     if (err == hipSuccess && ev) err = hipEventRecord(ev[2], stream);
     return err;
@@ -1303,7 +1475,7 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
 
 size_t bf16_ws_bytes(int B, int Tlen, int H, int dk, int dv, int chunk) {
     const int D = b16::pad_dim(dk, dv);
-#define EDA_WS(CC, DD) if (chunk == CC && D == DD) return b16::ws_bytes<CC, DD>(B, Tlen, H);
+#define EDA_WS(CC, DD) if (chunk == CC && D == DD) return b16::ws_bytes<CC, DD>(B, Tlen, H, dk, dv);
     EDA_WS(16, 32) EDA_WS(16, 64) EDA_WS(16, 128)
     EDA_WS(32, 32) EDA_WS(32, 64) EDA_WS(32, 128)
     EDA_WS(64, 32) EDA_WS(64, 64) EDA_WS(64, 128)
@@ -1318,17 +1490,18 @@ hipError_t launch_bf16(const void *q, const void *k, const void *e, const void *
                        const float *A_log, const float *dt_bias, const float *beta, const float *gamma,
                        const float *S0, void *o, float *S_final, int B, int Tlen, int H, int Hk, int dk,
                        int dv, int chunk, void *ws, hipStream_t stream, hipEvent_t const *ev) {
-    const int D = b16::pad_dim(dk, dv), BV = b16::slice_width(B * H, D);
+    const int D = b16::pad_dim(dk, dv);
+    const int BV = b16::seg_plan(B * H, (Tlen + chunk - 1) / chunk, D, dv).BV;
 #define EDA_GO(CC, DD, BB)                                                                          \
     if (chunk == CC && D == DD && BV == BB)                                                         \
         return b16::launch_t<CC, DD, BB>(q, k, e, v, decay, A_log, dt_bias, beta, gamma, S0, o,     \
                                          S_final, B, Tlen, H, Hk, dk, dv, ws, stream, ev);
-    EDA_GO(16, 32, 16) EDA_GO(16, 32, 32) EDA_GO(16, 64, 16) EDA_GO(16, 64, 32)
-    EDA_GO(16, 128, 16) EDA_GO(16, 128, 32)
-    EDA_GO(32, 32, 16) EDA_GO(32, 32, 32) EDA_GO(32, 64, 16) EDA_GO(32, 64, 32)
-    EDA_GO(32, 128, 16) EDA_GO(32, 128, 32)
-    EDA_GO(64, 32, 16) EDA_GO(64, 32, 32) EDA_GO(64, 64, 16) EDA_GO(64, 64, 32)
-    EDA_GO(64, 128, 16) EDA_GO(64, 128, 32)
+    EDA_GO(16, 32, 16) EDA_GO(16, 32, 32) EDA_GO(16, 64, 16) EDA_GO(16, 64, 32) EDA_GO(16, 64, 64)
+    EDA_GO(16, 128, 16) EDA_GO(16, 128, 32) EDA_GO(16, 128, 64)
+    EDA_GO(32, 32, 16) EDA_GO(32, 32, 32) EDA_GO(32, 64, 16) EDA_GO(32, 64, 32) EDA_GO(32, 64, 64)
+    EDA_GO(32, 128, 16) EDA_GO(32, 128, 32) EDA_GO(32, 128, 64)
+    EDA_GO(64, 32, 16) EDA_GO(64, 32, 32) EDA_GO(64, 64, 16) EDA_GO(64, 64, 32) EDA_GO(64, 64, 64)
+    EDA_GO(64, 128, 16) EDA_GO(64, 128, 32) EDA_GO(64, 128, 64)
 #undef EDA_GO
     return hipErrorInvalidValue;
 }

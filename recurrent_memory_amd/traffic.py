@@ -195,11 +195,15 @@ def summarize_mfma(directory: str, workload: str, canonical: dict) -> None:
         print(f"[mfma] {path}: busy {100 * busy:.1f} %, issued {issued / 1e9:.2f} GFLOP")
 
 
-def canonical_flop(workload: str, chunk: int = 32) -> dict:
-    """The chunk formulation's multiply-adds x 2 per launch (counted once)."""
+def canonical_flop(workload: str, chunk: int = 0) -> dict:
+    """The chunk formulation's multiply-adds x 2 per launch (counted once), at
+    `chunk` tokens per chunk (0: the library default, which `run` uses)."""
     sys.path.insert(0, ROOT)
     from eda_inputs import WORKLOADS
     w = WORKLOADS[workload]
+    if chunk == 0:
+        import recurrent_memory_amd as eda
+        chunk = eda.DEFAULT_CHUNK
     C, L, d = chunk, 2 * chunk, w.dk
     n = w.B * w.H * ((w.T + C - 1) // C)
     return {"eda_bf16_factors": 2.0 * n * (L * L * d + L ** 3 / 6.0 + L * L * d + C * L * d),

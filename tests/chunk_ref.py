@@ -41,6 +41,14 @@ e^{G_j - G_i} instead, never splitting the exponent.
 Padding: a ragged last chunk is padded with zero keys and queries, alpha = 1
 and zero gates, which are identity sub-steps; `chunk_forward` pads exactly as
 the kernels do.
+
+Segments (`segmented_forward`): the chunk maps S -> (Diag(Gam_C) + Phi') S +
+Psi V compose, so over a run of chunks ("segment" s) S_out = M_s S_in + N_s,
+with M_s the product of the chunk maps' linear parts and N_s the end state
+from a zero start.  Walking segments 0 .. P-2 on the augmented state [M | N]
+from [I | 0] (the M columns take no value term), taking the prefix
+S_in(s + 1) = M_s S_in(s) + N_s, and then walking every segment from its
+start state gives the sequential result exactly (up to rounding).
 """
 from __future__ import annotations
 
@@ -164,3 +172,54 @@ def chunk_forward(sub, S0, C, *, form="phi", wide_log=None):
         outs.append(O[:n])
         facs.append(f)
     return np.concatenate(outs, axis=0), S, facs
+
+
+def _chunk_list(sub, C, wide_log=None):
+    """Per-chunk factors and values (padded as the kernels pad)."""
+    T = sub["q"].shape[0]
+    out = []
+    for t0 in range(0, T, C):
+        n = min(C, T - t0)
+        sl = slice(2 * t0, 2 * (t0 + n))
+        lam = _pad_chunk(sub["lam"][sl], 2 * C, 0.0)
+        kap = _pad_chunk(sub["kap"][sl], 2 * C, 0.0)
+        bp = _pad_chunk(sub["bp"][sl], 2 * C, 0.0)
+        nu = _pad_chunk(sub["nu"][sl], 2 * C, 0.0)
+        logdec = _pad_chunk(sub["logdec"][t0:t0 + n], C, 0.0)
+        q = _pad_chunk(sub["q"][t0:t0 + n], C, 0.0)
+        out.append((chunk_factors(lam, kap, bp, logdec, q, wide_log=wide_log), nu[1::2], n))
+    return out
+
+
+def segmented_forward(sub, S0, C, P, *, wide_log=None):
+    """The chunked forward with the chunks of the head cut into P segments of
+    ceil(NC / P) chunks (the last may be shorter): segment maps on the
+    augmented state, their prefix, then each segment's pass with outputs.
+    Returns (o [T, dv], S_final, [(M_s, N_s)])."""
+    dk = sub["q"].shape[1]
+    dv = sub["nu"].shape[1]
+    chunks = _chunk_list(sub, C, wide_log)
+    NC = len(chunks)
+    ncs = -(-NC // P)
+    segs = [chunks[i:i + ncs] for i in range(0, NC, ncs)]
+    # maps of every segment but the last: [M | N] from [I | 0]
+    maps = []
+    for seg in segs[:-1]:
+        X = np.concatenate([np.eye(dk), np.zeros((dk, dv))], axis=1)
+        for f, V, _ in seg:
+            Vaug = np.concatenate([np.zeros((V.shape[0], dk)), V], axis=1)
+            X = f["dec"][:, None] * X + f["Phi"] @ X + f["Psi"] @ Vaug
+        maps.append((X[:, :dk], X[:, dk:]))
+    # prefix of start states
+    starts = [np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=float)]
+    for M, N in maps:
+        starts.append(M @ starts[-1] + N)
+    outs = []
+    S = None
+    for seg, S in zip(segs, starts):
+        S = S.copy()
+        for f, V, n in seg:
+            O = f["Qh"] @ S + f["Ph"] @ V
+            S = f["dec"][:, None] * S + f["Phi"] @ S + f["Psi"] @ V
+            outs.append(O[:n])
+    return np.concatenate(outs, axis=0), S, maps

@@ -162,9 +162,9 @@ def test_noalloc_variant_checks_before_any_hip_call():
     assert call_chunked_noalloc(chunked_args(o=fake(9, 8))) == 4
     ws = eda.load_library().eda_fwd_chunked_workspace_size
     limit = 160 << 20
-    # bf16, d = 128, chunk 64: 74240 bytes per chunk-head, 2259 fit
-    assert ws(1, 64 * 2259, 1, 128, 128, 1, 64) <= limit < ws(1, 64 * 2260, 1, 128, 128, 1, 64)
-    assert call_chunked_noalloc(chunked_args(B=1, T=64 * 2260, H=1, dk=128, dv=128, dt=1, chunk=64)) == 9
+    # bf16, d = 128, chunk 64, 64 heads: 74240 bytes per chunk-head, 35 chunks fit
+    assert ws(4, 64 * 35, 16, 128, 128, 1, 64) <= limit < ws(4, 64 * 36, 16, 128, 128, 1, 64)
+    assert call_chunked_noalloc(chunked_args(B=4, T=64 * 36, H=16, dk=128, dv=128, dt=1, chunk=64)) == 9
     assert call_chunked_noalloc(chunked_args(B=8, T=4096, H=16, dk=128, dv=128, dt=0, chunk=0)) == 9
 
 

@@ -212,3 +212,36 @@ def test_planted_mistakes_are_caught():
     bad = dict(sub, lam=lam, kap=lam)
     o, S, _ = chunk_ref.chunk_forward(bad, hd["S0"], 16)
     assert np.max(np.abs(o - ro)) > 1e-3
+
+
+@pytest.mark.parametrize("C", CHUNKS)
+@pytest.mark.parametrize("P", [2, 3, 5])
+@pytest.mark.parametrize("T", [300, 333])
+def test_segmented_state_pass(C, P, T):
+    """Segments: the maps [M_s | N_s] of every segment but the last, walked on
+    the augmented state from [I | 0], their prefix, and each
+    segment walked from its start state reproduce the token recurrence
+    (ragged last chunk and segment, random S0, d_k != d_v)."""
+    x = eda_inputs.make_inputs(1, T, 1, 16, 12, "f32", seed=700 + T + P, s0_std=0.5)
+    hd = _head(x)
+    sub = chunk_ref.substeps_eda(hd["q"], hd["k"], hd["e"], hd["v"], hd["alpha"], hd["beta"], hd["gamma"])
+    o, S, maps = chunk_ref.segmented_forward(sub, hd["S0"], C, P, wide_log=WIDE_LOG)
+    ro, rS = _oracle_head(x)
+    _assert_close(o, ro, 1e-12, f"o C={C} P={P} T={T}")
+    _assert_close(S, rS, 1e-12, f"S C={C} P={P} T={T}")
+    assert 1 <= len(maps) <= P - 1
+
+
+def test_segment_map_is_the_chunk_map_product():
+    """M_s of one segment is the ordered product of its chunks' linear maps
+    (a later chunk on the left), checked on a two-chunk segment; a planted
+    reversal of the order fails."""
+    x = eda_inputs.make_inputs(1, 64, 1, 16, 12, "f32", seed=77)
+    hd = _head(x)
+    sub = chunk_ref.substeps_eda(hd["q"], hd["k"], hd["e"], hd["v"], hd["alpha"], hd["beta"], hd["gamma"])
+    _, _, maps = chunk_ref.segmented_forward(sub, None, 16, 2, wide_log=WIDE_LOG)
+    _, _, facs = chunk_ref.chunk_forward(sub, None, 16, wide_log=WIDE_LOG)
+    A = [np.diag(f["dec"]) + f["Phi"] for f in facs]
+    M0 = maps[0][0]
+    assert np.allclose(M0, A[1] @ A[0], atol=1e-12, rtol=0)
+    assert not np.allclose(M0, A[0] @ A[1], atol=1e-6, rtol=0)

@@ -109,6 +109,53 @@ RAGGED = [(1, 1, 1, 16), (1, 1, 1, 32), (2, 15, 3, 16), (1, 33, 2, 32), (2, 100,
           (2, 129, 1, 64), (1, 200, 3, 64)]
 
 
+def segment_count(B, T, H, dk, dv, chunk):
+    """Segments per head of the bf16 state pass, read back from the workspace
+    size: the chunk factors (one block per chunk and head, as documented in
+    eda.h) plus, with P > 1 segments, B H (P - 1) d_k (d_k + 2 d_v) fp32."""
+    D = 32 if max(dk, dv) <= 32 else 64 if max(dk, dv) <= 64 else 128
+    nc = -(-T // chunk)
+    frag = (D // 16) * (D // 32) + (D // 16) * -(-chunk // 32) + (chunk // 16) * (D // 32) + (chunk // 16) * -(-chunk // 32)
+    blk = -(-(frag * 1024 + 4 * D) // 256) * 256
+    extra = eda.workspace_size(B, T, H, dk, dv, torch.bfloat16, chunk) - B * H * nc * blk
+    assert extra % (B * H * dk * (dk + 2 * dv) * 4) == 0
+    return 1 + extra // (B * H * dk * (dk + 2 * dv) * 4)
+
+
+# Few heads and long sequences: the state pass cuts each head's chunks into
+# segments walked at the same time (B, T, H, d_k, d_v, chunk, segments)
+SEGMENTED = [(1, 64 * 260 + 17, 2, 128, 128, 64, 2),     # ragged last chunk and segment
+             (1, 16 * 520, 2, 128, 128, 16, 4),
+             (2, 32 * 300 + 5, 1, 64, 40, 32, 2),        # d_k != d_v, partial value slice
+             (1, 16 * 1100, 1, 128, 100, 16, 8)]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,chunk,P", SEGMENTED)
+def test_segmented_state_pass(B, T, H, dk, dv, chunk, P):
+    """Segment maps [M | N], their prefix and the segments' passes against the
+    token recurrence over whole heads, with an initial state."""
+    assert segment_count(B, T, H, dk, dv, chunk) == P
+    say(f"segmented B={B} T={T} H={H} dk={dk} dv={dv} chunk={chunk} P={P}")
+    x = make_inputs(B, T, H, dk, dv, "bf16", seed=300 + T, s0_std=0.05)
+    ro, rS = full_oracle(x)
+    o, S = run_chunked(dev(x), chunk=chunk)
+    check(to64(o), to64(S), ro, rS, "bf16", f"segmented P={P} T={T}")
+
+
+def test_segmented_strong_decay_and_no_decay():
+    """Segments where the chunk maps contract to nearly zero (alpha ~ e^-5 per
+    token) and where they do not contract at all (alpha = 1), with S0."""
+    B, T, H, d, chunk = 1, 64 * 300, 1, 128, 64
+    assert segment_count(B, T, H, d, d, chunk) == 2
+    for kind in ("floor", "one"):
+        say(f"segmented decay {kind}")
+        x = make_inputs(B, T, H, d, d, "bf16", seed=41, s0_std=0.05)
+        x["alpha"] = torch.full_like(x["alpha"], math.exp(-5.0) if kind == "floor" else 1.0)
+        ro, rS = full_oracle(x)
+        o, S = run_chunked(dev(x), chunk=chunk)
+        check(to64(o), to64(S), ro, rS, "bf16", f"segmented {kind}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,T,H,chunk", RAGGED)
 def test_ragged(dtype, B, T, H, chunk):
@@ -314,21 +361,24 @@ def test_maximum_size_heads_match_single_head_runs():
     """The largest input the ABI accepts in one call: B*T*H*d just below 2^31
     elements per token tensor (T = 131072, 127 heads) and a 24.8 GB
     workspace, so every 32-bit product of token, head and channel indices
-    would overflow.  Heads are independent and each output column is computed
-    by the same instructions whatever the value-slice width, so the first and
-    last heads must equal, bit for bit, runs on those heads alone (which the
-    oracle checks at this length in the very-long workload test)."""
+    would overflow.  Heads are independent, so the first and last heads must
+    equal, bit for bit, a run of that head repeated over 64 heads, for which
+    the state pass takes the same plan (32-column slices, no segments) and so
+    the same instructions per output column (the oracle checks this length in
+    the very-long workload test)."""
     B, T, H, d = 1, 131072, 127, 128
     assert B * T * H * d < 2 ** 31 <= B * T * (H + 1) * d
     say(f"maximum size B={B} T={T} H={H} d={d}")
     x = make_inputs(B, T, H, d, d, "bf16", seed=61, s0_std=0.02, device=DEV)
     o, S = run_chunked(x)
     for h in (0, H - 1):
-        say(f"maximum size: head {h} alone")
-        xh = {n: (None if t is None else t[:, :, h:h + 1].contiguous() if t.dim() >= 3 and n != "S0"
-                  else t[:, h:h + 1].contiguous()) for n, t in x.items()}
+        say(f"maximum size: head {h} repeated")
+        rep = [h] * 64
+        xh = {n: (None if t is None else t[:, :, rep].contiguous() if t.dim() >= 3 and n != "S0"
+                  else t[:, rep].contiguous()) for n, t in x.items()}
         oh, Sh = run_chunked(xh)
         assert torch.equal(oh[:, :, 0], o[:, :, h]) and torch.equal(Sh[:, 0], S[:, h]), f"head {h}"
+        del xh, oh, Sh
     del x, o, S
     torch.cuda.empty_cache()
 

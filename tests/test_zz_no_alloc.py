@@ -48,8 +48,8 @@ def test_noalloc_matches_workspace_call(dtype, chunk):
 
 
 def test_noalloc_rejects_oversize_problem():
-    # bf16, chunk 64, d = 128: 2260 chunk-heads need more than the 160 MiB array
-    B, T, H = 1, 64 * 2260, 1
+    # bf16, chunk 64, d = 128, 64 heads: 36 chunks per head need more than the 160 MiB array
+    B, T, H = 4, 64 * 36, 16
     assert eda.workspace_size(B, T, H, 128, 128, torch.bfloat16, 64) > 160 << 20
     say("noalloc oversize rejection")
     x = make_inputs(B, T, H, 128, 128, "bf16", seed=7, device=DEV)
