@@ -69,9 +69,13 @@ const char *eda_status_string(eda_status_t s);
  * For bf16 inputs those are the chunk's affine state map (S -> Lambda S +
  * Phi S + Psi V, O = Qhat S + Phat V): with d_k = d_v = 128 that is 74240
  * bytes per 64-token chunk and head (1.16 KB per token and head), 51712 per
- * 32-token chunk and 46592 per 16-token chunk.  fp32 inputs compute chunk 64
- * as 32-token chunks (a 64-token chunk's fp32 operands exceed one compute
- * unit's LDS) and need the same workspace as chunk 32.
+ * 32-token chunk and 46592 per 16-token chunk.  With few heads and a long
+ * sequence (B*H*d/16 < 256 with d = 64 or 128, and at least 256 chunks), the
+ * bf16 state pass walks P segments of each head at the same time, and the
+ * workspace also holds B*H*(P-1)*d_k*(d_k + 2 d_v) fp32 values: the segment
+ * maps and start states.  fp32 inputs compute chunk 64 as 32-token chunks (a
+ * 64-token chunk's fp32 operands exceed one compute unit's LDS) and need the
+ * same workspace as chunk 32.
  */
 size_t eda_fwd_chunked_workspace_size(int B, int T, int H, int d_k, int d_v,
                                       eda_dtype_t dtype, int chunk);
