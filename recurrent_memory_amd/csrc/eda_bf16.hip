@@ -669,28 +669,54 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 wave_lds_sync();
                 invert_diag(J);
             }
-            // off-diagonal A and P tiles, spread over every wave
-            for (int t = (wave + NW - NB) % NW; t < NOD + NPV; t += NW) {
+            // off-diagonal A and P tiles, listed by the Kr row block I they share:
+            // A tiles (J, I) for J > I, then P^T tiles (I, Tb) for the token blocks
+            // Tb >= I / 2 whose stored rows reach block I.  Each wave takes a
+            // contiguous run of the list and keeps Kr_I's fragments while I stays,
+            // so a tile reads one operand from LDS instead of two.
+            {
                 const auto [lane, g4, l16, gq] = lane_ids(tid);
-                if (t < NOD) {
-                    int J = 1, I = t;
-                    while (I >= J) { I -= J; ++J; }
-                    const f32x4 a = tile_nt<T, D>(Kl + 16 * J * LDA, LDA, Kr + 16 * I * LDA, LDA, zero4(), lane);
-                    // A[16 J + g4 + rr][16 I + l16] -> mirrored block (I, J) of M's storage
+                constexpr int NKS = D / 32;
+                constexpr int PER = (NOD + NPV + NW - 1) / NW;
+                auto count = [](int I) { return NB - 1 - I + NBC - I / 2; };
+                const int tbeg = wave * PER, tend = imin(NOD + NPV, tbeg + PER);
+                int I = 0, r = tbeg;
+                while (I < NB && r >= count(I)) { r -= count(I); ++I; }
+                bf16x8 kr[NKS];
+                int Ihave = -1;
+                for (int t = tbeg; t < tend; ++t) {
+                    if (I != Ihave) {
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        MI[(16 * I + g4 + rr) * LDL + 16 * J + l16] = from_f32<T>(a[rr]);
-                } else {
-                    // P^T tile: rows = sub-steps i, cols = tokens; kept for i <= 2 tau + 1
-                    // (token block Tb holds the 2 Tb + 2 row blocks I of its stored rows)
-                    int Tb = 0, I = t - NOD;
-                    while (I >= 2 * Tb + 2) { I -= 2 * Tb + 2; ++Tb; }
-                    const int tau = 16 * Tb + l16, i0 = 16 * I + g4;
-                    const f32x4 a = tile_nt<T, D>(Kr + 16 * I * LDA, LDA, Ql + 16 * Tb * LDA, LDA, zero4(), lane);
-                    float w4[4];
+                        for (int ks = 0; ks < NKS; ++ks) kr[ks] = *(const bf16x8 *)(Kr + (16 * I + l16) * LDA + 32 * ks + 8 * gq);
+                        Ihave = I;
+                    }
+                    const int na = NB - 1 - I;
+                    f32x4 a = zero4();
+                    if (r < na) {
+                        const int J = I + 1 + r;
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) w4[rr] = (i0 + rr <= 2 * tau + 1) ? a[rr] : 0.f;
-                    store_p(tau, i0, w4[0], w4[1], w4[2], w4[3]);
+                        for (int ks = 0; ks < NKS; ++ks)
+                            a = mma32(*(const bf16x8 *)(Kl + (16 * J + l16) * LDA + 32 * ks + 8 * gq), kr[ks], a);
+                        // A[16 J + g4 + rr][16 I + l16] -> mirrored block (I, J) of M's storage
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            MI[(16 * I + g4 + rr) * LDL + 16 * J + l16] = from_f32<T>(a[rr]);
+                    } else {
+                        // P^T tile: rows = sub-steps i, cols = tokens; kept for i <= 2 tau + 1
+                        const int Tb = I / 2 + (r - na);
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks)
+                            a = mma32(kr[ks], *(const bf16x8 *)(Ql + (16 * Tb + l16) * LDA + 32 * ks + 8 * gq), a);
+                        const int tau = 16 * Tb + l16, i0 = 16 * I + g4;
+                        float w4[4];
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) w4[rr] = (i0 + rr <= 2 * tau + 1) ? a[rr] : 0.f;
+                        store_p(tau, i0, w4[0], w4[1], w4[2], w4[3]);
+                    }
+                    if (++r == count(I)) {
+                        r = 0;
+                        ++I;
+                    }
                 }
             }
         } else {
