@@ -32,10 +32,11 @@
 //   Kl = Diag(b') lam o e^{G - r},  Kr = kap o e^{r - G},  Ql = q o e^{G - r},
 // so A = strict_lower(Kl Kr^T) and P = causal(Ql Kr^T) only see factors
 // within e^{+-|G_C|/2}; the exports carry the scale e^r of each key channel
-// (lam o e^G = Kl e^r / b', Khat = Kr e^r, q o e^G = Ql e^r).  A chunk in
-// which some channel decays by more than e^-120 (only possible below the
-// safe gate's floor alpha = e^-5) forms A and P element-wise from
-// e^{G_j - G_i} and uses unsplit operands (r = 0).
+// (lam o e^G = Kl e^r / b', Khat = Kr e^r, q o e^G = Ql e^r).  The split
+// operands stay within e^{+-75} (inside the bf16 and fp32 ranges, with room
+// for the sums of products that reach e^{75}); a chunk in which some channel
+// decays by more than e^-150 forms A and P element-wise from e^{G_j - G_i}
+// and uses unsplit operands (r = 0).
 //
 // Rounding: every matrix-core operand is bf16; products accumulate in fp32.
 // Each exported factor is rounded once, from fp32 accumulators: beta and e^r
@@ -68,8 +69,8 @@
 namespace eda {
 namespace b16 {
 
-// wide-chunk threshold on a chunk's log2-decay (e^-120 = 2^-173)
-constexpr float WIDE_G2 = 173.f;
+// wide-chunk threshold on a chunk's log2-decay (e^-150 = 2^-216.4)
+constexpr float WIDE_G2 = 216.4f;
 
 __host__ __device__ constexpr int imax(int a, int b) { return a > b ? a : b; }
 __host__ __device__ constexpr int imin(int a, int b) { return a < b ? a : b; }

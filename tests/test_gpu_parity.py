@@ -247,15 +247,16 @@ def test_stress_decay_extremes(kind, chunk):
     check(to64(o), to64(S), ro, rS, "bf16", f"stress {kind} chunk={chunk}")
 
 
+@pytest.mark.parametrize("decay", [100.0, 145.0])
 @pytest.mark.parametrize("chunk", [16, 32, 64])
-def test_strong_decay_inside_split_range(chunk):
-    """Half of the key channels decay by e^-100 over each chunk: still inside
-    the split-exponent range (the element-wise path starts past e^-120), where
-    the split operands reach e^{50} and a product of two of them would leave
-    the fp32 range; the other half barely decays."""
-    say(f"strong decay inside the split range chunk={chunk}")
+def test_strong_decay_inside_split_range(chunk, decay):
+    """Half of the key channels decay by e^-100 or e^-145 over each chunk:
+    still inside the split-exponent range (the element-wise path starts past
+    e^-150), where the split operands reach e^{72} and a product of two of
+    them would leave the fp32 range; the other half barely decays."""
+    say(f"strong decay inside the split range chunk={chunk} decay={decay}")
     x = make_inputs(2, 3 * chunk + 9, 2, 128, 128, "bf16", seed=41, s0_std=0.5)
-    x["alpha"][..., ::2] = math.exp(-100.0 / chunk)
+    x["alpha"][..., ::2] = math.exp(-decay / chunk)
     x["alpha"][..., 1::2] = 0.999
     ro, rS = full_oracle(x)
     o, S = run_chunked(dev(x), chunk=chunk)
