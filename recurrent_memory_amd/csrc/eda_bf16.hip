@@ -1328,14 +1328,16 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
 // Prefix over segments, fp32: S_in(s + 1) = M_s S_in(s) + N_s for s = 0 .. P-2,
 // with S_in(0) = S0 (zero when S0 is NULL).  One workgroup per (head, 16-column
 // slice of the value dimension); thread (row, half) holds 8 columns of one
-// state row.  Per step, S_in(s) and M_s (in two halves of its columns, loaded
-// row-contiguous) are staged in LDS.  maps: [BH][P-1][d_k][d_k + d_v]; starts
-// (written): [BH][P-1][d_k][d_v] for segments 1 .. P-1.
-constexpr int COMB_T = 256, COMB_KH = 64;
+// state row.  Per step, the whole of M_s and the thread's N_s entries are
+// fetched at once (one memory latency per step, the next step's fetch issued
+// before this step's products), then M_s passes through LDS in two halves of
+// its columns.  maps: [BH][P-1][d_k][d_k + d_v]; starts (written):
+// [BH][P-1][d_k][d_v] for segments 1 .. P-1.
+constexpr int COMB_T = 256, COMB_KH = 64, COMB_NM = 128 * 128 / COMB_T;
 __global__ void __launch_bounds__(COMB_T)
 eda_bf16_combine(const float *S0, const float *__restrict__ maps, float *__restrict__ starts, int BH, int dk,
                  int dv, int P) {
-    __shared__ float Xs[128][16];
+    __shared__ __attribute__((aligned(16))) float Xs[128][16];
     __shared__ float Ms[128][COMB_KH + 1];   // (+1: rows of one wave fall in distinct banks)
     const int nsl = (dv + 15) / 16;
     const int bh = blockIdx.x / nsl, c0 = 16 * (blockIdx.x % nsl);
@@ -1347,29 +1349,49 @@ eda_bf16_combine(const float *S0, const float *__restrict__ maps, float *__restr
         const int col = c0 + cq + j;
         x[j] = (live && col < dv && S0) ? S0[((long)bh * dk + row) * dv + col] : 0.f;
     }
-    for (int s = 0; s + 1 < P; ++s) {
+    // element idx = tid + COMB_T i of M_s: row idx / 128, column idx % 128
+    float mr[COMB_NM], nr[8];
+    auto fetch = [&](int s) __attribute__((always_inline)) {
         const float *m = maps + ((long)bh * (P - 1) + s) * dk * (dk + dv);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) Xs[row][cq + j] = x[j];
-        float y[8];
+        for (int i = 0; i < COMB_NM; ++i) {
+            const int idx = tid + COMB_T * i, r = idx >> 7, k = idx & 127;
+            mr[i] = (r < dk && k < dk) ? m[(long)r * (dk + dv) + k] : 0.f;
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int col = c0 + cq + j;
-            y[j] = (live && col < dv) ? m[(long)row * (dk + dv) + dk + col] : 0.f;   // N_s
+            nr[j] = (live && col < dv) ? m[(long)row * (dk + dv) + dk + col] : 0.f;   // N_s
         }
-        for (int k0 = 0; k0 < dk; k0 += COMB_KH) {
-            __syncthreads();
-            // M_s[:, k0 .. k0 + 63]: consecutive threads read consecutive columns
-            for (int idx = tid; idx < 128 * COMB_KH; idx += COMB_T) {
-                const int r = idx / COMB_KH, k = idx % COMB_KH;
-                Ms[r][k] = (r < dk && k0 + k < dk) ? m[(long)r * (dk + dv) + k0 + k] : 0.f;
-            }
-            __syncthreads();
-            const int kn = min(COMB_KH, dk - k0);
-            for (int k = 0; k < kn; ++k) {
-                const float mk = Ms[row][k];
+    };
+    if (P > 1) fetch(0);
+    for (int s = 0; s + 1 < P; ++s) {
+        float y[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) y[j] = fmaf(mk, Xs[k0 + k][cq + j], y[j]);
+        for (int j = 0; j < 8; ++j) {
+            Xs[row][cq + j] = x[j];
+            y[j] = nr[j];
+        }
+#pragma unroll
+        for (int h = 0; h < 128 / COMB_KH; ++h) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < COMB_NM; ++i) {
+                const int idx = tid + COMB_T * i, r = idx >> 7, k = idx & 127;
+                if (k / COMB_KH == h) Ms[r][k % COMB_KH] = mr[i];
+            }
+            if (h == 128 / COMB_KH - 1 && s + 2 < P) fetch(s + 1);   // the next map, in flight
+            __syncthreads();
+            // (rows of Xs and columns of M_s beyond d_k hold zeros)
+#pragma unroll 16
+            for (int k = 0; k < COMB_KH; ++k) {
+                const float mk = Ms[row][k];
+                const f32x4 xa = *(const f32x4 *)&Xs[COMB_KH * h + k][cq], xb = *(const f32x4 *)&Xs[COMB_KH * h + k][cq + 4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    y[j] = fmaf(mk, xa[j], y[j]);
+                    y[4 + j] = fmaf(mk, xb[j], y[4 + j]);
+                }
             }
         }
         __syncthreads();

@@ -23,6 +23,8 @@ steps, state in place).  `summarize` scales each kernel's
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same counter reported
 for the calibration kernel and writes profiles/traffic_<kernel>_<workload>.txt,
 tagged with the SHA-1 of the kernel source so that stale figures are not used.
+Figures are per forward step: the state side of a step is every dispatch of
+its kernels (with few heads, the segment maps, their prefix and the pass).
 """
 from __future__ import annotations
 
@@ -40,6 +42,11 @@ CALIB_BYTES = 256 << 20
 NCALIB = 3
 KERNELS = {"eda_bf16_factors": "eda_bf16.hip", "eda_bf16_state": "eda_bf16.hip",
            "eda_decode_kernel": "eda_decode.hip"}
+# the dispatches that make up each family in one forward step
+FAMILY = {"eda_bf16_factors": ("eda_bf16_factors",),
+          "eda_bf16_state": ("eda_bf16_state", "eda_bf16_combine"),
+          "eda_decode_kernel": ("eda_decode_kernel",)}
+NSTEPS = 3
 
 
 def run(workload: str) -> None:
@@ -101,9 +108,9 @@ def summarize(fetch_dir: str, write_dir: str, workload: str, algorithmic: dict) 
         calib_kib = sum(r[2] for r in calib) / len(calib)
         scale = CALIB_BYTES / (calib_kib * 1024.0)
         for kern in KERNELS:
-            vals = [r[2] for r in rows if kern in r[1]]
+            vals = [r[2] for r in rows if any(n in r[1] for n in FAMILY[kern])]
             if vals:
-                out.setdefault(kern, {})[counter] = (sum(vals) / len(vals), calib_kib, scale)
+                out.setdefault(kern, {})[counter] = (sum(vals) / NSTEPS, calib_kib, scale)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for kern, src in KERNELS.items():
         if kern not in out or len(out[kern]) != 2:
@@ -114,7 +121,8 @@ def summarize(fetch_dir: str, write_dir: str, workload: str, algorithmic: dict) 
         total = fk * 1024 * fs + wk * 1024 * wsc
         path = os.path.join(ROOT, "profiles", f"traffic_{kern}_{workload}.txt")
         with open(path, "w") as f:
-            f.write(f"# HBM traffic per launch of {kern} on the {workload} workload, from rocprofv3\n"
+            f.write(f"# HBM traffic per forward step of {kern} on the {workload} workload (summed over\n"
+                    f"# the step's dispatches of {', '.join(FAMILY[kern])}), from rocprofv3\n"
                     "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over instances), each\n"
                     f"# scaled by the same counter on a calibration kernel that reads and writes\n"
                     f"# {CALIB_BYTES} bytes.  Commands (repo at REPO):\n"
@@ -140,7 +148,7 @@ N_XCC, N_SIMD = 8, 1024   # MI355X: 8 XCDs, 256 compute units x 4 SIMDs
 
 
 def summarize_mfma(directory: str, workload: str, canonical: dict) -> None:
-    """Per launch of each chunked kernel: the bf16 matrix operations issued
+    """Per forward step of each chunked kernel family: the bf16 matrix operations issued
     (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts add and multiply operations / 512),
     the matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES summed over the
     SIMDs, over the kernel's GRBM_GUI_ACTIVE cycles -- summed over the XCDs in
@@ -158,12 +166,13 @@ def summarize_mfma(directory: str, workload: str, canonical: dict) -> None:
         names[d] = row["Kernel_Name"]
     for d, c in per.items():
         for kern in ("eda_bf16_factors", "eda_bf16_state"):
-            if kern in names[d]:
+            if any(n in names[d] for n in FAMILY[kern]):
                 for k, v in c.items():
                     vals[kern][k].append(v)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for kern, c in vals.items():
-        avg = {k: sum(v) / len(v) for k, v in c.items()}
+        # per forward step: the sum over the step's dispatches of the family
+        avg = {k: sum(v) / NSTEPS for k, v in c.items()}
         cycles = avg["GRBM_GUI_ACTIVE"] / N_XCC
         issued = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
         busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMD)
@@ -173,15 +182,16 @@ def summarize_mfma(directory: str, workload: str, canonical: dict) -> None:
         sha = hashlib.sha1(open(os.path.join(HERE, "csrc", KERNELS[kern]), "rb").read()).hexdigest()
         path = os.path.join(ROOT, "profiles", f"mfma_{kern}_{workload}.txt")
         with open(path, "w") as f:
-            f.write(f"# Matrix-core use per launch of {kern} on the {workload} workload, from rocprofv3\n"
-                    "# counters (averages over the launches).  Commands (repo at REPO):\n"
+            f.write(f"# Matrix-core use per forward step of {kern} on the {workload} workload (summed\n"
+                    f"# over the step's dispatches of {', '.join(FAMILY[kern])}), from rocprofv3 counters.\n"
+                    "# Commands (repo at REPO):\n"
                     "#   cd /tmp && export TMPDIR=/tmp\n"
                     "#   rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES "
                     f"GRBM_GUI_ACTIVE --output-format csv -d M -o t -- python3 REPO/recurrent_memory_amd/traffic.py "
                     f"run --workload {workload}\n"
                     f"#   python3 REPO/recurrent_memory_amd/traffic.py summarize-mfma M --workload {workload}\n")
             f.write(f"kernel = {kern}\nworkload = {workload}\nsource = {KERNELS[kern]}\nsource_sha1 = {sha}\n")
-            f.write(f"launches = {len(c['GRBM_GUI_ACTIVE'])}\n")
+            f.write(f"dispatches = {len(c['GRBM_GUI_ACTIVE'])} over {NSTEPS} forward steps\n")
             for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
                       "GRBM_GUI_ACTIVE"):
                 f.write(f"{k} = {avg[k]:.0f}\n")
