@@ -796,12 +796,16 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             const auto [lane, g4, l16, gq] = lane_ids(tid);
             const int cbs[2] = {c0, c1};
             int nb[NCH], tb[NCH], Jtop[NCH], pr[NCH];
+            char *ex[NCH];   // this lane's Psi or Phat entries of fragment column l16, step 0
             f32x4 acc[NCH][NB];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const int cb = cbs[c];
                 nb[c] = cb;
                 tb[c] = cb - NBD;
+                // token t = 8 K + 2 gq (+1) sits in k-step t / 32 = K / 4, lane slot
+                // 16 ((t & 31) / 8) + l16 = 16 (K & 3) + l16, bytes 2 (t & 7) = 4 gq
+                ex[c] = wsb + (KY[c] ? F::oPsi + nb[c] * KSC * 1024 : F::oPh + tb[c] * KSC * 1024) + l16 * 16 + 4 * gq;
                 Jtop[c] = KY[c] ? NB - 1 : imin(NB - 1, 2 * tb[c] + 1);   // Z: P is zero below 32 tb + 32
                 pr[c] = KY[c] ? 0 : G::poff(tb[c]) + l16 * G::pld(tb[c]); // P row of token 16 tb + l16
                 // right-looking: every row block's bracket starts as R_J; once X_K is solved
@@ -830,13 +834,24 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     }
                 }
             }
+            // each step's diagonal-inverse block and off-diagonal blocks are read one
+            // step ahead (they are fixed by now), so the step's chain never waits on LDS
+            s16x4 mt_n = *(const s16x4 *)(MT + (16 * (NB - 1) + l16) * MTW + g4);
+            s16x4 ak_n[NB];
+#pragma unroll
+            for (int J = NB - 2; J >= 0; --J) ak_n[J] = frag_col4(MI + 16 * J * LDL + 16 * (NB - 1), LDL, lane);
 #pragma unroll
             for (int K = NB - 1; K >= 0; --K) {
                 // X_K = M_KK^T acc[K], acc[K] as a bf16 pair
-                const s16x4 mt = *(const s16x4 *)(MT + (16 * K + l16) * MTW + g4);
+                const s16x4 mt = mt_n;
                 s16x4 ak[NB];
 #pragma unroll
-                for (int J = K - 1; J >= 0; --J) ak[J] = frag_col4(MI + 16 * J * LDL + 16 * K, LDL, lane);
+                for (int J = K - 1; J >= 0; --J) ak[J] = ak_n[J];
+                if (K > 0) {
+                    mt_n = *(const s16x4 *)(MT + (16 * (K - 1) + l16) * MTW + g4);
+#pragma unroll
+                    for (int J = K - 2; J >= 0; --J) ak_n[J] = frag_col4(MI + 16 * J * LDL + 16 * (K - 1), LDL, lane);
+                }
                 uint32_t x01[NCH], x23[NCH];
                 f32x4 x[NCH];
 #pragma unroll
@@ -862,25 +877,22 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                         acc[c][J] = mma16(ak[J], __builtin_bit_cast(s16x4, make_uint2(x01[c] ^ 0x80008000u,
                                                                                       x23[c] ^ 0x80008000u)),
                                           acc[c][J]);
-                // lane: X[16 K + g4 + i][column l16 of the block]; delta rows j = 16 K + g4 + 1, + 3
-                const int t0 = 8 * K + 2 * gq;
-                const float2 bt = *(const float2 *)(sb + t0);
+                // lane: X[16 K + g4 + i][column l16 of the block]; delta rows j = 16 K + g4 + 1, + 3,
+                // tokens 8 K + 2 gq and + 1
+                const float2 bt = *(const float2 *)(sb + 8 * K + 2 * gq);
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
                     const uint32_t ev = pack_bf16(x[c][1] * bt.x, x[c][3] * bt.y);
+                    // Psi[n][t], n = 16 nb + l16, or Phat[t'][t], t' = 16 tb + l16
+                    *(uint32_t *)(ex[c] + (K >> 2) * 1024 + (K & 3) * 256) = ev;
                     if (KY[c]) {
-                        // Psi[n][t], n = 16 nb + l16
-                        *(uint32_t *)(wsb + F::oPsi + ((nb[c] * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
-                                      2 * (t0 & 7)) = ev;
                         T *yk = Kr + (16 * K + g4) * LDA + 16 * nb[c] + l16;
                         yk[0] = (T)(x01[c] & 0xffffu);
                         yk[LDA] = (T)(x01[c] >> 16);
                         yk[2 * LDA] = (T)(x23[c] & 0xffffu);
                         yk[3 * LDA] = (T)(x23[c] >> 16);
                     } else {
-                        // Phat[t][t'], t = 16 tb + l16; Z[t][16 K + g4 ..]
-                        *(uint32_t *)(wsb + F::oPh + ((tb[c] * KSC + t0 / 32) * 64 + 16 * ((t0 & 31) >> 3) + l16) * 16 +
-                                      2 * (t0 & 7)) = ev;
+                        // Z[t'][16 K + g4 ..]
                         T *zd = K <= Jtop[c] ? Zs + pr[c] + 16 * K + g4 : (T *)AdT + 4 * lane;
                         *(uint2 *)zd = make_uint2(x01[c], x23[c]);
                     }
