@@ -127,6 +127,27 @@ __device__ __forceinline__ LaneIds lane_ids(int tid) {
     return {x, 4 * (x >> 4), x & 15, x >> 4};
 }
 
+// LDS byte address of a per-lane base, opaque to the compiler: the fixed
+// offsets added to it stay in the instructions' immediate fields instead of
+// being folded into the base (one register per offset, spilled under
+// pressure).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+    asm volatile("" : "+v"(a));
+    return a;
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 lds_ld2(uint32_t a) { return *(const __attribute__((address_space(3))) u32x2 *)(uintptr_t)a; }
+__device__ __forceinline__ f32x2 lds_ldf2(uint32_t a) { return *(const __attribute__((address_space(3))) f32x2 *)(uintptr_t)a; }
+__device__ __forceinline__ void lds_st2(uint32_t a, uint32_t x, uint32_t y) {
+    *(__attribute__((address_space(3))) u32x2 *)(uintptr_t)a = u32x2{x, y};
+}
+__device__ __forceinline__ void lds_st16(uint32_t a, uint16_t x) { *(__attribute__((address_space(3))) uint16_t *)(uintptr_t)a = x; }
+__device__ __forceinline__ s16x4 lds_ld_tr4(uint32_t a) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
+}
+
 __device__ __forceinline__ bf16x8 ld_frag(const char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 __device__ __forceinline__ void st_frag(char *p, bf16x8 x) { *reinterpret_cast<bf16x8 *>(p) = x; }
 
@@ -141,6 +162,21 @@ __device__ __forceinline__ float safe_gate_log2(float a, float Ap, float b) {
     const float x = a + b;
     const float sp = fmaxf(x, 0.f) + LN2 * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * L2E));
     return -GATE_FLOOR * L2E * (__builtin_amdgcn_exp2f(-Ap * sp) - 1.f);
+}
+
+// Exchanges between the four 16-lane rows of a wave (gfx950 lane permutes),
+// for x holding x0 .. x3 in rows 0 .. 3:
+//   row_swap16(x) = {[x0 x0 x2 x2], [x1 x1 x3 x3]},
+//   row_swap32(x) = {[x0 x1 x0 x1], [x2 x3 x2 x3]}.
+__device__ __forceinline__ float2 row_swap16(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return make_float2(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+}
+__device__ __forceinline__ float2 row_swap32(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return make_float2(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
 }
 
 // Value of lane S of each group of four lanes (DPP quad permutation).
@@ -189,6 +225,9 @@ struct K1G {
     static constexpr int NI = imax(1, TPW / TI);       // token rows per lane
     static constexpr int RA = imin(TI, TPW);           // row groups of a wave holding tokens
     static_assert(TPW % TI == 0 || TPW < TI, "token split");
+    // four 16-lane token rows per wave instruction, all holding tokens: the scan
+    // moves between rows by lane permutes
+    static constexpr bool ROWS4 = NO == 16 && RA == 4 && NW % 4 == 0;
     static_assert(NB <= NW, "one diagonal block per wave");
     static_assert(C <= 64, "beta/gamma staging by the first wave");
     // P (and later Z = P M) is stored packed: the rows of token block tb hold
@@ -214,8 +253,13 @@ struct K1G {
     static_assert(LDS <= (NW == 8 ? 160 : 80) * 1024, "LDS budget");
     // phase 4/5 work lists
     static constexpr int NZT = NBC * (NBC + 1);         // Z tiles (tb, J <= 2 tb + 1)
-    static constexpr int BM = 2, BN = imin(4, NBD);     // Phi register block (tiles)
+    // 8 waves and 128 channels: Phi as four 4 x 4-tile blocks on waves 0..3, Qhat
+    // on waves 4..7 in pairs of column blocks sharing their Z fragments (fewer
+    // LDS reads per product than one 2 x 4 block per wave and Qhat by column)
+    static constexpr bool PQSPLIT = NW == 8 && NBD == 8;
+    static constexpr int BM = PQSPLIT ? 4 : 2, BN = imin(4, NBD);   // Phi register block (tiles)
     static constexpr int NPB = (NBD / BM) * (NBD / BN); // Phi blocks
+    static_assert(!PQSPLIT || NPB == 4, "Phi blocks on waves 0..3");
 };
 
 // VEC: d_k == D and 16-byte aligned q, k, e and decay input (each thread's
@@ -250,6 +294,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     constexpr bool LAYER = MODE == MODE_LAYER, DPLR = MODE == MODE_DPLR;
     constexpr int L = G::L, NB = G::NB, NT = G::NT, NW = G::NW, LDA = G::LDA, LDL = G::LDL;
     constexpr int ADS = G::ADS, MTW = G::MTW, NO = G::NO, TI = G::TI, NI = G::NI, RA = G::RA;
+    constexpr bool ROWS4 = G::ROWS4;
     constexpr int NBD = F::NBD, NBC = F::NBC, KSD = F::KSD, KSC = F::KSC;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Kl = (T *)(smem + G::oKl);            // Diag(b') Kl              [L][LDA]
@@ -500,13 +545,23 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     } else {
                         x = __builtin_amdgcn_logf(xa[i][j >> 2][j & 3]);
                     }
+                    if constexpr (ROWS4) {
+                        // rows 2 k + 1 add row 2 k; rows 2, 3 add the pair total of rows 0, 1
+                        const float2 a = row_swap16(x);
+                        const float pt = a.x + a.y;
+                        const float sx = (r & 1) ? pt : x;
+                        const float2 b = row_swap32(pt);
+                        g[i][j] = carry[j] + ((r & 2) ? sx + b.x : sx);
+                        carry[j] += b.x + b.y;
+                    } else {
 #pragma unroll
-                    for (int sh = 1; sh < RA; sh <<= 1) {
-                        const float y = __shfl_up(x, sh * NO, 64);
-                        if (r >= sh) x += y;
+                        for (int sh = 1; sh < RA; sh <<= 1) {
+                            const float y = __shfl_up(x, sh * NO, 64);
+                            if (r >= sh) x += y;
+                        }
+                        g[i][j] = carry[j] + x;
+                        carry[j] += __shfl(x, (RA - 1) * NO + o, 64);
                     }
-                    g[i][j] = carry[j] + x;
-                    carry[j] += __shfl(x, (RA - 1) * NO + o, 64);
                 }
             // the decay input is consumed: the next item's is fetched now
             if constexpr (VEC) prefetch_at(next_item(it), std::integral_constant<int, 1>{});
@@ -518,21 +573,25 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         __syncthreads();
         bool wide_here = false;
         {
+            // running sums over the waves in order: the wave's prefix is the sum
+            // before its own term, and the total (the same in every wave) the last
             float pre[8], tot[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) pre[j] = tot[j] = 0.f;
+            f32x4 wt[NW][2];
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                const f32x4 a = *(const f32x4 *)(wtot + w * D + c0), b = *(const f32x4 *)(wtot + w * D + c0 + 4);
+                wt[w][0] = *(const f32x4 *)(wtot + w * D + c0);
+                wt[w][1] = *(const f32x4 *)(wtot + w * D + c0 + 4);
+            }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    tot[j] += a[j];
-                    tot[4 + j] += b[j];
-                    if (w < wave) {
-                        pre[j] += a[j];
-                        pre[4 + j] += b[j];
-                    }
+            for (int w = 0; w < NW; ++w) {
+                if (w == wave) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) pre[j] = tot[j];
                 }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) tot[j] += wt[w][j >> 2][j & 3];
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -795,8 +854,13 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             constexpr bool KY[2] = {(KIND & 1) == 0, (KIND & 2) == 0};
             const auto [lane, g4, l16, gq] = lane_ids(tid);
             const int cbs[2] = {c0, c1};
-            int nb[NCH], tb[NCH], Jtop[NCH], pr[NCH];
+            int nb[NCH], tb[NCH], Jtop[NCH];
             char *ex[NCH];   // this lane's Psi or Phat entries of fragment column l16, step 0
+            // per-lane LDS bases; every block's address is a fixed offset from one
+            uint32_t kca[NCH], kya[NCH], pha[NCH], pla[NCH];
+            const int ltr = 4 * gq + (l16 >> 2), ctr = 4 * (l16 & 3);   // transposed-read lane part
+            const uint32_t mia = lds_addr(MI + ltr * LDL + ctr), mta = lds_addr(MT + l16 * MTW + g4);
+            const uint32_t sba = lds_addr(sb + 2 * gq), dum = lds_addr(AdT + 4 * lane);
             f32x4 acc[NCH][NB];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
@@ -807,7 +871,14 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 // 16 ((t & 31) / 8) + l16 = 16 (K & 3) + l16, bytes 2 (t & 7) = 4 gq
                 ex[c] = wsb + (KY[c] ? F::oPsi + nb[c] * KSC * 1024 : F::oPh + tb[c] * KSC * 1024) + l16 * 16 + 4 * gq;
                 Jtop[c] = KY[c] ? NB - 1 : imin(NB - 1, 2 * tb[c] + 1);   // Z: P is zero below 32 tb + 32
-                pr[c] = KY[c] ? 0 : G::poff(tb[c]) + l16 * G::pld(tb[c]); // P row of token 16 tb + l16
+                if (KY[c]) {
+                    kca[c] = lds_addr(Kr + ltr * LDA + 16 * nb[c] + ctr);
+                    kya[c] = lds_addr(Kr + g4 * LDA + 16 * nb[c] + l16);
+                } else {
+                    const int pr = G::poff(tb[c]) + l16 * G::pld(tb[c]);  // P row of token 16 tb + l16
+                    pha[c] = lds_addr(Ph + pr + g4);                      // (Z overwrites P's high part)
+                    pla[c] = lds_addr(Pl + pr + g4);
+                }
                 // right-looking: every row block's bracket starts as R_J; once X_K is solved
                 // it updates all the brackets above it at once (independent products), so
                 // the chain from one solved block to the next is one update, the pair split
@@ -816,7 +887,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     const float scale = ers[16 * nb[c] + l16];   // Khat = Kr e^r, column n
 #pragma unroll
                     for (int J = 0; J < NB; ++J) {
-                        const s16x4 r = frag_col4(Kr + 16 * J * LDA + 16 * nb[c], LDA, lane);   // rows 16 J + g4 + i
+                        const s16x4 r = lds_ld_tr4(kca[c] + 2 * 16 * J * LDA);   // rows 16 J + g4 + i
                         const uint2 u = __builtin_bit_cast(uint2, r);
                         acc[c][J] = f32x4{lo_bf16(u.x), hi_bf16(u.x), lo_bf16(u.y), hi_bf16(u.y)} * scale;
                     }
@@ -825,9 +896,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     for (int J = 0; J < NB; ++J) {
                         // (rows beyond the stored part read as zero)
                         const bool in = J <= Jtop[c];
-                        const int off = in ? pr[c] + 16 * J + g4 : pr[c];
-                        const uint2 h = *(const uint2 *)(Ph + off);
-                        const uint2 l = *(const uint2 *)(Pl + off);
+                        const u32x2 h = lds_ld2(in ? pha[c] + 2 * 16 * J : pha[c]);
+                        const u32x2 l = lds_ld2(in ? pla[c] + 2 * 16 * J : pla[c]);
                         const f32x4 v = f32x4{lo_bf16(h.x) + lo_bf16(l.x), hi_bf16(h.x) + hi_bf16(l.x),
                                               lo_bf16(h.y) + lo_bf16(l.y), hi_bf16(h.y) + hi_bf16(l.y)};
                         acc[c][J] = in ? v : zero4();
@@ -835,11 +905,13 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 }
             }
             // each step's diagonal-inverse block and off-diagonal blocks are read one
-            // step ahead (they are fixed by now), so the step's chain never waits on LDS
-            s16x4 mt_n = *(const s16x4 *)(MT + (16 * (NB - 1) + l16) * MTW + g4);
+            // step ahead (they are fixed by now), so the step's chain never waits on LDS;
+            // A_KJ is stored at block (J, K)
+            auto a_blk = [&](int J, int K) __attribute__((always_inline)) { return lds_ld_tr4(mia + 2 * (16 * J * LDL + 16 * K)); };
+            s16x4 mt_n = __builtin_bit_cast(s16x4, lds_ld2(mta + 2 * 16 * (NB - 1) * MTW));
             s16x4 ak_n[NB];
 #pragma unroll
-            for (int J = NB - 2; J >= 0; --J) ak_n[J] = frag_col4(MI + 16 * J * LDL + 16 * (NB - 1), LDL, lane);
+            for (int J = NB - 2; J >= 0; --J) ak_n[J] = a_blk(J, NB - 1);
 #pragma unroll
             for (int K = NB - 1; K >= 0; --K) {
                 // X_K = M_KK^T acc[K], acc[K] as a bf16 pair
@@ -848,9 +920,9 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 #pragma unroll
                 for (int J = K - 1; J >= 0; --J) ak[J] = ak_n[J];
                 if (K > 0) {
-                    mt_n = *(const s16x4 *)(MT + (16 * (K - 1) + l16) * MTW + g4);
+                    mt_n = __builtin_bit_cast(s16x4, lds_ld2(mta + 2 * 16 * (K - 1) * MTW));
 #pragma unroll
-                    for (int J = K - 2; J >= 0; --J) ak_n[J] = frag_col4(MI + 16 * J * LDL + 16 * (K - 1), LDL, lane);
+                    for (int J = K - 2; J >= 0; --J) ak_n[J] = a_blk(J, K - 1);
                 }
                 uint32_t x01[NCH], x23[NCH];
                 f32x4 x[NCH];
@@ -868,8 +940,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     x01[c] = pack_bf16(x[c][0], x[c][1]);
                     x23[c] = pack_bf16(x[c][2], x[c][3]);
                 }
-                // acc[J] -= A_KJ^T X_K for every J < K (A_KJ stored at block (J, K)); the
-                // bracket solved next (J = K - 1) is updated first
+                // acc[J] -= A_KJ^T X_K for every J < K; the bracket solved next (J = K - 1)
+                // is updated first
 #pragma unroll
                 for (int J = K - 1; J >= 0; --J)
 #pragma unroll
@@ -879,22 +951,23 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                                           acc[c][J]);
                 // lane: X[16 K + g4 + i][column l16 of the block]; delta rows j = 16 K + g4 + 1, + 3,
                 // tokens 8 K + 2 gq and + 1
-                const float2 bt = *(const float2 *)(sb + 8 * K + 2 * gq);
+                // (taken as floats: this compiler's bit-cast of a vector element reads element 0)
+                const f32x2 bt = lds_ldf2(sba + 4 * 8 * K);
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
-                    const uint32_t ev = pack_bf16(x[c][1] * bt.x, x[c][3] * bt.y);
+                    const uint32_t ev = pack_bf16(x[c][1] * bt[0], x[c][3] * bt[1]);
                     // Psi[n][t], n = 16 nb + l16, or Phat[t'][t], t' = 16 tb + l16
                     *(uint32_t *)(ex[c] + (K >> 2) * 1024 + (K & 3) * 256) = ev;
                     if (KY[c]) {
-                        T *yk = Kr + (16 * K + g4) * LDA + 16 * nb[c] + l16;
-                        yk[0] = (T)(x01[c] & 0xffffu);
-                        yk[LDA] = (T)(x01[c] >> 16);
-                        yk[2 * LDA] = (T)(x23[c] & 0xffffu);
-                        yk[3 * LDA] = (T)(x23[c] >> 16);
+                        // Yhat rows 16 K + g4 + i, column 16 nb + l16, over Kr
+                        const uint32_t ya = kya[c] + 2 * 16 * K * LDA;
+                        lds_st16(ya, (uint16_t)(x01[c] & 0xffffu));
+                        lds_st16(ya + 2 * LDA, (uint16_t)(x01[c] >> 16));
+                        lds_st16(ya + 4 * LDA, (uint16_t)(x23[c] & 0xffffu));
+                        lds_st16(ya + 6 * LDA, (uint16_t)(x23[c] >> 16));
                     } else {
                         // Z[t'][16 K + g4 ..]
-                        T *zd = K <= Jtop[c] ? Zs + pr[c] + 16 * K + g4 : (T *)AdT + 4 * lane;
-                        *(uint2 *)zd = make_uint2(x01[c], x23[c]);
+                        lds_st2(K <= Jtop[c] ? pha[c] + 2 * 16 * K : dum, x01[c], x23[c]);
                     }
                 }
             }
@@ -969,6 +1042,40 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             }
         }
         // ---- Qhat = (Ql - Z Kl) e^r as transposed tiles -------------------------------
+        if constexpr (G::PQSPLIT) {
+            if (wave >= 4) {
+                const auto [lane, g4, l16, gq] = lane_ids(tid);
+                const int mb0 = 2 * (wave - 4);
+                f32x4 erm[2];
+#pragma unroll
+                for (int a = 0; a < 2; ++a) erm[a] = *(const f32x4 *)(ers + 16 * (mb0 + a) + g4);
+#pragma unroll 1
+                for (int tb = 0; tb < NBC; ++tb) {
+                    const int pr = G::poff(tb) + l16 * G::pld(tb);
+                    f32x4 acc[2];
+#pragma unroll
+                    for (int a = 0; a < 2; ++a) {
+                        const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * (mb0 + a) + g4);
+                        acc[a] = f32x4{-lo_bf16(q0.x), -hi_bf16(q0.x), -lo_bf16(q0.y), -hi_bf16(q0.y)};
+                    }
+#pragma unroll
+                    for (int s = 0; s < tb + 1; ++s) {
+                        const bf16x8 z = *(const bf16x8 *)(Zs + pr + 32 * s + 8 * gq);
+#pragma unroll
+                        for (int a = 0; a < 2; ++a)
+                            acc[a] = mma32(frag_col(Kl + 32 * s * LDA + 16 * (mb0 + a), LDA, lane), z, acc[a]);
+                    }
+#pragma unroll
+                    for (int a = 0; a < 2; ++a) {
+                        const int mb = mb0 + a;
+                        *(uint2 *)(wsb + F::oQh + ((tb * KSD + mb / 2) * 64 + 16 * (2 * (mb & 1) + (gq >> 1)) + l16) * 16 +
+                                   8 * (gq & 1)) =
+                            make_uint2(pack_bf16(-acc[a][0] * erm[a][0], -acc[a][1] * erm[a][1]),
+                                       pack_bf16(-acc[a][2] * erm[a][2], -acc[a][3] * erm[a][3]));
+                    }
+                }
+            }
+        } else
         for (int mb = wave; mb < NBD; mb += NW) {
             const auto [lane, g4, l16, gq] = lane_ids(tid);
             const f32x4 erm = *(const f32x4 *)(ers + 16 * mb + g4);
