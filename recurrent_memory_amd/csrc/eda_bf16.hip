@@ -578,20 +578,18 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             float pre[8], tot[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) pre[j] = tot[j] = 0.f;
-            f32x4 wt[NW][2];
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                wt[w][0] = *(const f32x4 *)(wtot + w * D + c0);
-                wt[w][1] = *(const f32x4 *)(wtot + w * D + c0 + 4);
-            }
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
+                const f32x4 a = *(const f32x4 *)(wtot + w * D + c0), b = *(const f32x4 *)(wtot + w * D + c0 + 4);
                 if (w == wave) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) pre[j] = tot[j];
                 }
 #pragma unroll
-                for (int j = 0; j < 8; ++j) tot[j] += wt[w][j >> 2][j & 3];
+                for (int j = 0; j < 4; ++j) {
+                    tot[j] += a[j];
+                    tot[4 + j] += b[j];
+                }
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
