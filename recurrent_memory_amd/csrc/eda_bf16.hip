@@ -137,6 +137,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return a;
 }
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// The bf16 pairs (-1, 0) and (0, -1), in scalar registers the compiler cannot
+// see into: folded, this compiler encodes (-1, 0) as the inline constant -1.0,
+// which the bf16 dot product reads as the 32-bit pattern 0xbf800000, i.e. (0, -1).
+struct NegSel {
+    uint32_t lo, hi;
+};
+__device__ __forceinline__ NegSel neg_sel() {
+    NegSel m{0x0000bf80u, 0xbf800000u};
+    asm volatile("" : "+s"(m.lo));
+    asm volatile("" : "+s"(m.hi));
+    return m;
+}
+// x - (element 0 or 1 of the bf16 pair h, by m = neg_sel's lo or hi), in one
+// instruction (a bf16 dot product with an fp32 addend: the product is exact, so
+// the only rounding is the sum's, and none when h is x rounded to bf16)
+__device__ __forceinline__ float minus_bf16(uint32_t h, uint32_t m, float x) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, h), __builtin_bit_cast(bf16x2v, m), x, false);
+}
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 lds_ld2(uint32_t a) { return *(const __attribute__((address_space(3))) u32x2 *)(uintptr_t)a; }
 __device__ __forceinline__ f32x2 lds_ldf2(uint32_t a) { return *(const __attribute__((address_space(3))) f32x2 *)(uintptr_t)a; }
@@ -468,7 +487,9 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[i] -= a[i] * xp;
         }
-        const uint32_t x01 = pack_bf16(x[0], x[1]), x23 = pack_bf16(x[2], x[3]);
+        // stored negated: the substitution then yields -X, which the bracket
+        // updates take as they are (the consumers of -X absorb its sign)
+        const uint32_t x01 = pack_bf16(-x[0], -x[1]), x23 = pack_bf16(-x[2], -x[3]);
         *(uint2 *)(MT + (16 * J + col) * MTW + s4) = make_uint2(x01, x23);
     };
 
@@ -830,9 +851,11 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         //      one 16-column block of R per wave, with no barrier:
         //          X_K = M_KK^T (R_K - sum_{J > K} A_JK^T X_J),   K = NB-1 .. 0.
         //      The solved blocks feed the later steps as bf16; the bracket enters the
-        //      diagonal-inverse product as a bf16 pair.  Y overwrites Kr and Z overwrites
-        //      P's high part, in place (each column block belongs to one wave, and each
-        //      row block of it is read before it is written).  From the fp32 results:
+        //      diagonal-inverse product as a bf16 pair.  The diagonal inverses are stored
+        //      negated, so each step yields -X_K, which the bracket updates add as it is;
+        //      -Y overwrites Kr and -Z overwrites P's high part, in place (each column
+        //      block belongs to one wave, and each row block of it is read before it is
+        //      written).  From the fp32 results:
         //      Psi = Yhat[delta rows]^T Diag(beta), Phat = Z[:, delta cols] Diag(beta).
         //      Every product here is the 16x16x16 instruction.  (Yhat = Y Diag(e^r) =
         //      M^T Khat is kept, bounded by |M|: Y^T Kl would otherwise reach e^{|G_C|},
@@ -906,13 +929,14 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             // step ahead (they are fixed by now), so the step's chain never waits on LDS;
             // A_KJ is stored at block (J, K)
             auto a_blk = [&](int J, int K) __attribute__((always_inline)) { return lds_ld_tr4(mia + 2 * (16 * J * LDL + 16 * K)); };
+            const NegSel ns = neg_sel();
             s16x4 mt_n = __builtin_bit_cast(s16x4, lds_ld2(mta + 2 * 16 * (NB - 1) * MTW));
             s16x4 ak_n[NB];
 #pragma unroll
             for (int J = NB - 2; J >= 0; --J) ak_n[J] = a_blk(J, NB - 1);
 #pragma unroll
             for (int K = NB - 1; K >= 0; --K) {
-                // X_K = M_KK^T acc[K], acc[K] as a bf16 pair
+                // x = -X_K = (-M_KK)^T acc[K], acc[K] as a bf16 pair
                 const s16x4 mt = mt_n;
                 s16x4 ak[NB];
 #pragma unroll
@@ -928,8 +952,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 for (int c = 0; c < NCH; ++c) {
                     const f32x4 a = acc[c][K];
                     const uint32_t h01 = pack_bf16(a[0], a[1]), h23 = pack_bf16(a[2], a[3]);
-                    const uint32_t l01 = pack_bf16(a[0] - lo_bf16(h01), a[1] - hi_bf16(h01));
-                    const uint32_t l23 = pack_bf16(a[2] - lo_bf16(h23), a[3] - hi_bf16(h23));
+                    const uint32_t l01 = pack_bf16(minus_bf16(h01, ns.lo, a[0]), minus_bf16(h01, ns.hi, a[1]));
+                    const uint32_t l23 = pack_bf16(minus_bf16(h23, ns.lo, a[2]), minus_bf16(h23, ns.hi, a[3]));
                     x[c] = mma16(mt, __builtin_bit_cast(s16x4, make_uint2(h01, h23)), zero4());
                     x[c] = mma16(mt, __builtin_bit_cast(s16x4, make_uint2(l01, l23)), x[c]);
                 }
@@ -938,33 +962,31 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     x01[c] = pack_bf16(x[c][0], x[c][1]);
                     x23[c] = pack_bf16(x[c][2], x[c][3]);
                 }
-                // acc[J] -= A_KJ^T X_K for every J < K; the bracket solved next (J = K - 1)
-                // is updated first
+                // acc[J] -= A_KJ^T X_K (+= A_KJ^T x) for every J < K; the bracket solved
+                // next (J = K - 1) is updated first
 #pragma unroll
                 for (int J = K - 1; J >= 0; --J)
 #pragma unroll
                     for (int c = 0; c < NCH; ++c)
-                        acc[c][J] = mma16(ak[J], __builtin_bit_cast(s16x4, make_uint2(x01[c] ^ 0x80008000u,
-                                                                                      x23[c] ^ 0x80008000u)),
-                                          acc[c][J]);
+                        acc[c][J] = mma16(ak[J], __builtin_bit_cast(s16x4, make_uint2(x01[c], x23[c])), acc[c][J]);
                 // lane: X[16 K + g4 + i][column l16 of the block]; delta rows j = 16 K + g4 + 1, + 3,
                 // tokens 8 K + 2 gq and + 1
                 // (taken as floats: this compiler's bit-cast of a vector element reads element 0)
                 const f32x2 bt = lds_ldf2(sba + 4 * 8 * K);
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
-                    const uint32_t ev = pack_bf16(x[c][1] * bt[0], x[c][3] * bt[1]);
+                    const uint32_t ev = pack_bf16(x[c][1] * -bt[0], x[c][3] * -bt[1]);
                     // Psi[n][t], n = 16 nb + l16, or Phat[t'][t], t' = 16 tb + l16
                     *(uint32_t *)(ex[c] + (K >> 2) * 1024 + (K & 3) * 256) = ev;
                     if (KY[c]) {
-                        // Yhat rows 16 K + g4 + i, column 16 nb + l16, over Kr
+                        // -Yhat rows 16 K + g4 + i, column 16 nb + l16, over Kr
                         const uint32_t ya = kya[c] + 2 * 16 * K * LDA;
                         lds_st16(ya, (uint16_t)(x01[c] & 0xffffu));
                         lds_st16(ya + 2 * LDA, (uint16_t)(x01[c] >> 16));
                         lds_st16(ya + 4 * LDA, (uint16_t)(x23[c] & 0xffffu));
                         lds_st16(ya + 6 * LDA, (uint16_t)(x23[c] >> 16));
                     } else {
-                        // Z[t'][16 K + g4 ..]
+                        // -Z[t'][16 K + g4 ..]
                         lds_st2(K <= Jtop[c] ? pha[c] + 2 * 16 * K : dum, x01[c], x23[c]);
                     }
                 }
@@ -999,7 +1021,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         __syncthreads();
 
-        // ---- Phi = -(Yhat^T Kl) e^r as transposed tiles, BM x BN tiles per block ---
+        // ---- Phi = -(Yhat^T Kl) e^r (Kr holds -Yhat) as transposed tiles, BM x BN tiles per block
         //      (this and the Qhat loop are kept rolled: unrolled, their fragments
         //      are hoisted beside the next item's inputs and the kernel spills)
         for (int pb = wave; pb < G::NPB; pb += NW) {
@@ -1035,11 +1057,11 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     const f32x4 v = acc[a][b];
                     *(uint2 *)(wsb + F::oPhi + ((nb * KSD + mb / 2) * 64 + 16 * (2 * (mb & 1) + (gq >> 1)) + l16) * 16 +
                                8 * (gq & 1)) =
-                        make_uint2(pack_bf16(-v[0] * erm[0], -v[1] * erm[1]), pack_bf16(-v[2] * erm[2], -v[3] * erm[3]));
+                        make_uint2(pack_bf16(v[0] * erm[0], v[1] * erm[1]), pack_bf16(v[2] * erm[2], v[3] * erm[3]));
                 }
             }
         }
-        // ---- Qhat = (Ql - Z Kl) e^r as transposed tiles -------------------------------
+        // ---- Qhat = (Ql - Z Kl) e^r (P's high part holds -Z) as transposed tiles ----------
         if constexpr (G::PQSPLIT) {
             if (wave >= 4) {
                 const auto [lane, g4, l16, gq] = lane_ids(tid);
@@ -1054,7 +1076,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
 #pragma unroll
                     for (int a = 0; a < 2; ++a) {
                         const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * (mb0 + a) + g4);
-                        acc[a] = f32x4{-lo_bf16(q0.x), -hi_bf16(q0.x), -lo_bf16(q0.y), -hi_bf16(q0.y)};
+                        acc[a] = f32x4{lo_bf16(q0.x), hi_bf16(q0.x), lo_bf16(q0.y), hi_bf16(q0.y)};
                     }
 #pragma unroll
                     for (int s = 0; s < tb + 1; ++s) {
@@ -1068,8 +1090,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                         const int mb = mb0 + a;
                         *(uint2 *)(wsb + F::oQh + ((tb * KSD + mb / 2) * 64 + 16 * (2 * (mb & 1) + (gq >> 1)) + l16) * 16 +
                                    8 * (gq & 1)) =
-                            make_uint2(pack_bf16(-acc[a][0] * erm[a][0], -acc[a][1] * erm[a][1]),
-                                       pack_bf16(-acc[a][2] * erm[a][2], -acc[a][3] * erm[a][3]));
+                            make_uint2(pack_bf16(acc[a][0] * erm[a][0], acc[a][1] * erm[a][1]),
+                                       pack_bf16(acc[a][2] * erm[a][2], acc[a][3] * erm[a][3]));
                     }
                 }
             }
@@ -1082,15 +1104,15 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 const int pr = G::poff(tb) + l16 * G::pld(tb);
 
                 const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * mb + g4);
-                f32x4 acc = {-lo_bf16(q0.x), -hi_bf16(q0.x), -lo_bf16(q0.y), -hi_bf16(q0.y)};
+                f32x4 acc = {lo_bf16(q0.x), hi_bf16(q0.x), lo_bf16(q0.y), hi_bf16(q0.y)};
 #pragma unroll
                 for (int s = 0; s < tb + 1; ++s)
                     acc = mma32(frag_col(Kl + 32 * s * LDA + 16 * mb, LDA, lane),
                                 *(const bf16x8 *)(Zs + pr + 32 * s + 8 * gq), acc);
-                // lane: -Qhat[t = 16 tb + l16][m = 16 mb + g4 + i] / e^r
+                // lane: Qhat[t = 16 tb + l16][m = 16 mb + g4 + i] / e^r
                 *(uint2 *)(wsb + F::oQh + ((tb * KSD + mb / 2) * 64 + 16 * (2 * (mb & 1) + (gq >> 1)) + l16) * 16 +
                            8 * (gq & 1)) =
-                    make_uint2(pack_bf16(-acc[0] * erm[0], -acc[1] * erm[1]), pack_bf16(-acc[2] * erm[2], -acc[3] * erm[3]));
+                    make_uint2(pack_bf16(acc[0] * erm[0], acc[1] * erm[1]), pack_bf16(acc[2] * erm[2], acc[3] * erm[3]));
             }
         }
         // No barrier here: the next item writes LDS before its first barrier only
