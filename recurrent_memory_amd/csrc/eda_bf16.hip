@@ -683,8 +683,9 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 float f[8], fi[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    f[j] = exp2f_(g[i][j] - rr[j]);
-                    fi[j] = wide ? exp2f_(glq[j] - g[i][j]) : exp2f_(rr[j] - g[i][j]);
+                    const float d = g[i][j] - rr[j];   // (rr - g = -d exactly)
+                    f[j] = exp2f_(d);
+                    fi[j] = wide ? exp2f_(glq[j] - g[i][j]) : exp2f_(-d);
                 }
                 store8(Kl + (2 * tau) * LDA + c0, ev, gmt, f);
                 // (DPLR: the delta sub-step reads along a, held in ev; its erase sub-step has no key)
@@ -882,6 +883,11 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             const int ltr = 4 * gq + (l16 >> 2), ctr = 4 * (l16 & 3);   // transposed-read lane part
             const uint32_t mia = lds_addr(MI + ltr * LDL + ctr), mta = lds_addr(MT + l16 * MTW + g4);
             const uint32_t sba = lds_addr(sb + 2 * gq), dum = lds_addr(AdT + 4 * lane);
+            const NegSel ns = neg_sel();
+            // the identity as the row-by-k operand: lane (gq, l16) holds row l16, k = 4 gq .. + 3
+            const s16x4 eye = __builtin_bit_cast(
+                s16x4, make_uint2((4 * gq == l16 ? 0x3f80u : 0u) | (4 * gq + 1 == l16 ? 0x3f800000u : 0u),
+                                  (4 * gq + 2 == l16 ? 0x3f80u : 0u) | (4 * gq + 3 == l16 ? 0x3f800000u : 0u)));
             f32x4 acc[NCH][NB];
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
@@ -893,7 +899,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 ex[c] = wsb + (KY[c] ? F::oPsi + nb[c] * KSC * 1024 : F::oPh + tb[c] * KSC * 1024) + l16 * 16 + 4 * gq;
                 Jtop[c] = KY[c] ? NB - 1 : imin(NB - 1, 2 * tb[c] + 1);   // Z: P is zero below 32 tb + 32
                 if (KY[c]) {
-                    kca[c] = lds_addr(Kr + ltr * LDA + 16 * nb[c] + ctr);
+                    kca[c] = lds_addr(Kr + l16 * LDA + 16 * nb[c] + 4 * gq);
                     kya[c] = lds_addr(Kr + g4 * LDA + 16 * nb[c] + l16);
                 } else {
                     const int pr = G::poff(tb[c]) + l16 * G::pld(tb[c]);  // P row of token 16 tb + l16
@@ -904,24 +910,41 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 // it updates all the brackets above it at once (independent products), so
                 // the chain from one solved block to the next is one update, the pair split
                 // and the two diagonal-inverse products
+                // the brackets start on the matrix cores: Khat's block as Kr's block times
+                // Diag(e^r) (e^r as a bf16 pair, the two products exact in fp32), P^T's
+                // block as the identity times P^T (its high and low parts)
                 if (KY[c]) {
                     const float scale = ers[16 * nb[c] + l16];   // Khat = Kr e^r, column n
+                    const uint32_t shi = pack_bf16(scale, 0.f), slo = pack_bf16(minus_bf16(shi, ns.lo, scale), 0.f);
+                    // Diag(s) as the k-by-column operand: lane (gq, l16) holds rows 4 gq + i of column l16
+                    uint32_t d[2][2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t sv = h ? slo : shi;   // the value in the low half
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int k0 = 4 * gq + 2 * q;
+                            d[h][q] = (k0 == l16 ? sv : 0u) | (k0 + 1 == l16 ? sv << 16 : 0u);
+                        }
+                    }
+                    const s16x4 dhi = __builtin_bit_cast(s16x4, make_uint2(d[0][0], d[0][1]));
+                    const s16x4 dlo = __builtin_bit_cast(s16x4, make_uint2(d[1][0], d[1][1]));
 #pragma unroll
                     for (int J = 0; J < NB; ++J) {
-                        const s16x4 r = lds_ld_tr4(kca[c] + 2 * 16 * J * LDA);   // rows 16 J + g4 + i
-                        const uint2 u = __builtin_bit_cast(uint2, r);
-                        acc[c][J] = f32x4{lo_bf16(u.x), hi_bf16(u.x), lo_bf16(u.y), hi_bf16(u.y)} * scale;
+                        // Kr rows 16 J + l16, channels 16 nb + 4 gq .. + 3 (row-by-k operand)
+                        const s16x4 kb = __builtin_bit_cast(s16x4, lds_ld2(kca[c] + 2 * 16 * J * LDA));
+                        acc[c][J] = mma16(kb, dlo, mma16(kb, dhi, zero4()));
                     }
                 } else {
 #pragma unroll
                     for (int J = 0; J < NB; ++J) {
-                        // (rows beyond the stored part read as zero)
+                        // (rows beyond the stored part enter as zero)
                         const bool in = J <= Jtop[c];
                         const u32x2 h = lds_ld2(in ? pha[c] + 2 * 16 * J : pha[c]);
                         const u32x2 l = lds_ld2(in ? pla[c] + 2 * 16 * J : pla[c]);
-                        const f32x4 v = f32x4{lo_bf16(h.x) + lo_bf16(l.x), hi_bf16(h.x) + hi_bf16(l.x),
-                                              lo_bf16(h.y) + lo_bf16(l.y), hi_bf16(h.y) + hi_bf16(l.y)};
-                        acc[c][J] = in ? v : zero4();
+                        const s16x4 hv = __builtin_bit_cast(s16x4, make_uint2(in ? h.x : 0u, in ? h.y : 0u));
+                        const s16x4 lv = __builtin_bit_cast(s16x4, make_uint2(in ? l.x : 0u, in ? l.y : 0u));
+                        acc[c][J] = mma16(eye, lv, mma16(eye, hv, zero4()));
                     }
                 }
             }
@@ -929,7 +952,6 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             // step ahead (they are fixed by now), so the step's chain never waits on LDS;
             // A_KJ is stored at block (J, K)
             auto a_blk = [&](int J, int K) __attribute__((always_inline)) { return lds_ld_tr4(mia + 2 * (16 * J * LDL + 16 * K)); };
-            const NegSel ns = neg_sel();
             s16x4 mt_n = __builtin_bit_cast(s16x4, lds_ld2(mta + 2 * 16 * (NB - 1) * MTW));
             s16x4 ak_n[NB];
 #pragma unroll
