@@ -758,8 +758,13 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 const auto [lane, g4, l16, gq] = lane_ids(tid);
                 constexpr int NKS = D / 32;
                 constexpr int PER = (NOD + NPV + NW - 1) / NW;
+                // with 8 waves, waves w and w + 4 share a SIMD and the later ones issue
+                // second (and also fetch the next item's inputs right after): the first
+                // half takes one tile more, the second half one fewer
+                constexpr int SK = (NW == 8 && PER > 1) ? 1 : 0;
                 auto count = [](int I) { return NB - 1 - I + NBC - I / 2; };
-                const int tbeg = wave * PER, tend = imin(NOD + NPV, tbeg + PER);
+                const int tbeg = wave < NW / 2 ? wave * (PER + SK) : (NW / 2) * (PER + SK) + (wave - NW / 2) * (PER - SK);
+                const int tend = imin(NOD + NPV, tbeg + (wave < NW / 2 ? PER + SK : PER - SK));
                 int I = 0, r = tbeg;
                 while (I < NB && r >= count(I)) { r -= count(I); ++I; }
                 bf16x8 kr[NKS];
@@ -1088,34 +1093,41 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             if (wave >= 4) {
                 const auto [lane, g4, l16, gq] = lane_ids(tid);
                 const int mb0 = 2 * (wave - 4);
-                f32x4 erm[2];
+                // all token blocks at once, k-step outer: each Kl fragment is read once per
+                // k-step, each Z fragment once, and the 2 x NBC accumulations interleave
+                f32x4 acc[2][NBC];
 #pragma unroll
-                for (int a = 0; a < 2; ++a) erm[a] = *(const f32x4 *)(ers + 16 * (mb0 + a) + g4);
-#pragma unroll 1
-                for (int tb = 0; tb < NBC; ++tb) {
-                    const int pr = G::poff(tb) + l16 * G::pld(tb);
-                    f32x4 acc[2];
+                for (int tb = 0; tb < NBC; ++tb)
 #pragma unroll
                     for (int a = 0; a < 2; ++a) {
                         const uint2 q0 = *(const uint2 *)(Ql + (16 * tb + l16) * LDA + 16 * (mb0 + a) + g4);
-                        acc[a] = f32x4{lo_bf16(q0.x), hi_bf16(q0.x), lo_bf16(q0.y), hi_bf16(q0.y)};
+                        acc[a][tb] = f32x4{lo_bf16(q0.x), hi_bf16(q0.x), lo_bf16(q0.y), hi_bf16(q0.y)};
                     }
 #pragma unroll
-                    for (int s = 0; s < tb + 1; ++s) {
-                        const bf16x8 z = *(const bf16x8 *)(Zs + pr + 32 * s + 8 * gq);
+                for (int s = 0; s < NBC; ++s) {   // sub-steps 32 s .. 32 s + 31 reach token blocks tb >= s
+                    bf16x8 kf[2];
 #pragma unroll
-                        for (int a = 0; a < 2; ++a)
-                            acc[a] = mma32(frag_col(Kl + 32 * s * LDA + 16 * (mb0 + a), LDA, lane), z, acc[a]);
+                    for (int a = 0; a < 2; ++a) kf[a] = frag_col(Kl + 32 * s * LDA + 16 * (mb0 + a), LDA, lane);
+#pragma unroll
+                    for (int tb = s; tb < NBC; ++tb) {
+                        const bf16x8 z = *(const bf16x8 *)(Zs + G::poff(tb) + l16 * G::pld(tb) + 32 * s + 8 * gq);
+#pragma unroll
+                        for (int a = 0; a < 2; ++a) acc[a][tb] = mma32(kf[a], z, acc[a][tb]);
                     }
+                }
+                f32x4 erm[2];
+#pragma unroll
+                for (int a = 0; a < 2; ++a) erm[a] = *(const f32x4 *)(ers + 16 * (mb0 + a) + g4);
+#pragma unroll
+                for (int tb = 0; tb < NBC; ++tb)
 #pragma unroll
                     for (int a = 0; a < 2; ++a) {
                         const int mb = mb0 + a;
                         *(uint2 *)(wsb + F::oQh + ((tb * KSD + mb / 2) * 64 + 16 * (2 * (mb & 1) + (gq >> 1)) + l16) * 16 +
                                    8 * (gq & 1)) =
-                            make_uint2(pack_bf16(acc[a][0] * erm[a][0], acc[a][1] * erm[a][1]),
-                                       pack_bf16(acc[a][2] * erm[a][2], acc[a][3] * erm[a][3]));
+                            make_uint2(pack_bf16(acc[a][tb][0] * erm[a][0], acc[a][tb][1] * erm[a][1]),
+                                       pack_bf16(acc[a][tb][2] * erm[a][2], acc[a][tb][3] * erm[a][3]));
                     }
-                }
             }
         } else
         for (int mb = wave; mb < NBD; mb += NW) {
