@@ -528,6 +528,11 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                          "v"(xB[0][3]), "v"(xB[1][0]), "v"(xB[1][1]), "v"(xB[1][2]), "v"(xB[1][3]));
     }
     for (; it < items; it += gridDim.x) {
+        // Waves w and w + NW/2 share a SIMD and the arbiter favours the older one.
+        // In the Phi/Qhat phase the second half carries the paired Qhat blocks, so
+        // it runs at raised issue priority there; every other phase runs level
+        // (raising either half in the scan or in the substitution did not pay).
+        if constexpr (NW == 8) __builtin_amdgcn_s_setprio(0);
         const int bh = head_of(it), cidx = chunk_of(it);
         if (!is_fast(cidx)) fetch_slow(it);
         // (nothing read after this item's last barrier uses bp, sb or sg)
@@ -1048,6 +1053,9 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         }
         __syncthreads();
 
+        if constexpr (NW == 8) {
+            if (wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
+        }
         // ---- Phi = -(Yhat^T Kl) e^r (Kr holds -Yhat) as transposed tiles, BM x BN tiles per block
         //      (this and the Qhat loop are kept rolled: unrolled, their fragments
         //      are hoisted beside the next item's inputs and the kernel spills)
@@ -1213,8 +1221,11 @@ struct FragSet {
 // of every (R NBC)-th 128-byte line of chunk c + WARM_AHEAD's block, so the R
 // slices of a head (same XCD, one L2) together bring that block into L2
 // before its fragments are fetched.  The words are consumed, unused, when the
-// chunk's set is.
-constexpr int WARM_AHEAD = 4;
+// chunk's set is.  Two chunks ahead: at four, the warmed lines of the XCD's
+// units (eight per XCD at 16 heads) were often evicted before their fetch,
+// and the pass read its blocks 1.7 times over.  The segment maps run without
+// it (they read Phi and Psi alone, and their blocks met in L2 anyway).
+constexpr int WARM_AHEAD = 2;
 constexpr size_t WARM_MIN_BYTES = (size_t)256 << 20;   // MI355X MALL capacity
 
 // VV: every value slice is whole (d_v a multiple of BV) and v is 16-byte
@@ -1678,7 +1689,7 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
         auto ks = vv ? eda_bf16_state<C, D, BV, true, KIND_SUMMARY> : eda_bf16_state<C, D, BV, false, KIND_SUMMARY>;
         hipLaunchKernelGGL(ks, dim3((unsigned)gridS), dim3(G2::NT), G2::LDS, stream, (const bf16 *)v, S0,
                            S_final, (bf16 *)o, (const char *)ws, maps, Tlen, H, BH, dk, dv, NC, RX + R, RX,
-                           sp.P - 1, sp.NCS, warm);
+                           sp.P - 1, sp.NCS, 0);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL(eda_bf16_combine, dim3((unsigned)(BH * ((dv + 15) / 16))), dim3(COMB_T), 0, stream,
                            S0, (const float *)maps, starts, BH, dk, dv, sp.P);
