@@ -746,7 +746,18 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             if (wave < NB) {
                 const int J = wave;
                 const auto [lane, g4, l16, gq] = lane_ids(tid);
-                const f32x4 a = tile_nt<T, D>(Kl + 16 * J * LDA, LDA, Kr + 16 * J * LDA, LDA, zero4(), lane);
+                // both operands read as one group before the products
+                constexpr int NKS = D / 32;
+                bf16x8 xl[NKS], xr[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    xl[ks] = *(const bf16x8 *)(Kl + (16 * J + l16) * LDA + 32 * ks + 8 * gq);
+                    xr[ks] = *(const bf16x8 *)(Kr + (16 * J + l16) * LDA + 32 * ks + 8 * gq);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 a = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) a = mma32(xl[ks], xr[ks], a);
                 // lane holds A[g4 + rr][l16]: one column run of the transposed block
                 *(f32x4 *)(AdT + (J * 16 + l16) * ADS + g4) =
                     f32x4{g4 > l16 ? a[0] : 0.f, g4 + 1 > l16 ? a[1] : 0.f, g4 + 2 > l16 ? a[2] : 0.f,
@@ -782,11 +793,17 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     }
                     const int na = NB - 1 - I;
                     f32x4 a = zero4();
+                    // the tile's other operand is read as one group before its
+                    // products (left to the scheduler, each read sinks to its
+                    // product and the tile pays one LDS round trip per k-step)
+                    bf16x8 ot[NKS];
                     if (r < na) {
                         const int J = I + 1 + r;
 #pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks)
-                            a = mma32(*(const bf16x8 *)(Kl + (16 * J + l16) * LDA + 32 * ks + 8 * gq), kr[ks], a);
+                        for (int ks = 0; ks < NKS; ++ks) ot[ks] = *(const bf16x8 *)(Kl + (16 * J + l16) * LDA + 32 * ks + 8 * gq);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) a = mma32(ot[ks], kr[ks], a);
                         // A[16 J + g4 + rr][16 I + l16] -> mirrored block (I, J) of M's storage
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr)
@@ -795,8 +812,10 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                         // P^T tile: rows = sub-steps i, cols = tokens; kept for i <= 2 tau + 1
                         const int Tb = I / 2 + (r - na);
 #pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks)
-                            a = mma32(kr[ks], *(const bf16x8 *)(Ql + (16 * Tb + l16) * LDA + 32 * ks + 8 * gq), a);
+                        for (int ks = 0; ks < NKS; ++ks) ot[ks] = *(const bf16x8 *)(Ql + (16 * Tb + l16) * LDA + 32 * ks + 8 * gq);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) a = mma32(kr[ks], ot[ks], a);
                         const int tau = 16 * Tb + l16, i0 = 16 * I + g4;
                         float w4[4];
 #pragma unroll
@@ -946,14 +965,21 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                         acc[c][J] = mma16(kb, dlo, mma16(kb, dhi, zero4()));
                     }
                 } else {
+                    // (rows beyond the stored part enter as zero; all the reads are
+                    // issued before the first product, or each waits for its own)
+                    u32x2 h[NB], l[NB];
 #pragma unroll
                     for (int J = 0; J < NB; ++J) {
-                        // (rows beyond the stored part enter as zero)
+                        const uint32_t off = J <= Jtop[c] ? 2 * 16 * J : 0;
+                        h[J] = lds_ld2(pha[c] + off);
+                        l[J] = lds_ld2(pla[c] + off);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int J = 0; J < NB; ++J) {
                         const bool in = J <= Jtop[c];
-                        const u32x2 h = lds_ld2(in ? pha[c] + 2 * 16 * J : pha[c]);
-                        const u32x2 l = lds_ld2(in ? pla[c] + 2 * 16 * J : pla[c]);
-                        const s16x4 hv = __builtin_bit_cast(s16x4, make_uint2(in ? h.x : 0u, in ? h.y : 0u));
-                        const s16x4 lv = __builtin_bit_cast(s16x4, make_uint2(in ? l.x : 0u, in ? l.y : 0u));
+                        const s16x4 hv = __builtin_bit_cast(s16x4, make_uint2(in ? h[J].x : 0u, in ? h[J].y : 0u));
+                        const s16x4 lv = __builtin_bit_cast(s16x4, make_uint2(in ? l[J].x : 0u, in ? l[J].y : 0u));
                         acc[c][J] = mma16(eye, lv, mma16(eye, hv, zero4()));
                     }
                 }
