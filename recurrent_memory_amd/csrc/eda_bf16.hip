@@ -478,9 +478,18 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         f32x4 x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = (s4 + i == col) ? 1.f : 0.f;
+        // the block's columns (A[s4 + i][p]) are read RD steps ahead of the
+        // serial steps that use them
+        constexpr int RD = 6;
+        f32x4 ac[15];
+        auto acol = [&](int p) __attribute__((always_inline)) { return *(const f32x4 *)(AdT + (J * 16 + p) * ADS + s4); };
+#pragma unroll
+        for (int p = 0; p < RD; ++p) ac[p] = acol(p);
 #pragma unroll
         for (int p = 0; p < 15; ++p) {
-            const f32x4 a = *(const f32x4 *)(AdT + (J * 16 + p) * ADS + s4);   // A[s4 + i][p]
+            if (p + RD < 15) ac[p + RD] = acol(p + RD);
+            __builtin_amdgcn_sched_barrier(0);
+            const f32x4 a = ac[p];
             const float xs = x[p & 3];
             const float xp = (p >> 2) == 0 ? quad_bcast<0>(xs) : (p >> 2) == 1 ? quad_bcast<1>(xs)
                            : (p >> 2) == 2 ? quad_bcast<2>(xs) : quad_bcast<3>(xs);
