@@ -1637,10 +1637,12 @@ static int pad_dim(int dk, int dv) {
 // still leaves at most one workgroup per compute unit (256 on MI355X).
 // Fewer heads than fill the chip even with 16-column slices, and a long
 // sequence: 64-column slices and P segments, the largest power of two that
-// keeps at least 128 chunks per segment and at most 256 workgroups in the
-// pass (segment maps double the factor reads of the state side, so shorter
-// segments cost more than they gain; measured on MI355X at d = 128).  NCS
-// chunks per segment; P is recounted from NCS so that no segment is empty.
+// keeps at least 64 chunks per segment and at most 256 workgroups both in the
+// pass and in the segment maps, which walk whole-width slices (one for M's
+// columns, one for the values; segment maps double the factor reads of the
+// state side, so shorter segments cost more than they gain; measured on MI355X
+// at d = 128).  NCS chunks per segment; P is recounted from NCS so that no
+// segment is empty.
 struct SegPlan {
     int BV, P, NCS;
 };
@@ -1649,8 +1651,10 @@ static SegPlan seg_plan(int BH, int NC, int D, int dv) {
     while (sp.BV < 32 && sp.BV < D && (long)BH * (D / sp.BV) > 256) sp.BV *= 2;
     if (D >= 64 && (long)BH * (D / 16) < 256 && NC >= 256) {
         sp.BV = 64;
-        const long units = (long)BH * ((dv + 63) / 64);
-        while (sp.P < 64 && NC >= 128 * 2 * sp.P && units * 2 * sp.P <= 256) sp.P *= 2;
+        const long units = (long)BH * ((dv + 63) / 64);        // pass workgroups per segment
+        const long mapw = (long)BH * (1 + (dv + D - 1) / D);   // map workgroups per segment
+        while (sp.P < 64 && NC >= 64 * 2 * sp.P && units * 2 * sp.P <= 256 && mapw * (2 * sp.P - 1) <= 256)
+            sp.P *= 2;
     }
     sp.NCS = (NC + sp.P - 1) / sp.P;
     sp.P = (NC + sp.NCS - 1) / sp.NCS;
@@ -1716,14 +1720,20 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     const int warm = fac_bytes<C, D>(B, Tlen, H) > WARM_MIN_BYTES;
     float *maps = nullptr, *starts = nullptr;
     if (sp.P > 1) {
-        // segment maps, their prefix, then the segments' passes
+        // segment maps (whole-width slices: one for M's d_k columns, one for the
+        // values), their prefix, then the segments' passes
+        using G2S = K2G<C, D, D>;
         maps = (float *)((char *)ws + fac_bytes<C, D>(B, Tlen, H));
         starts = maps + (size_t)BH * (sp.P - 1) * dk * (dk + dv);
-        const int RX = (dk + BV - 1) / BV;
-        const int gridS = 8 * ((BH * (sp.P - 1) + 7) / 8) * (RX + R);
-        auto ks = vv ? eda_bf16_state<C, D, BV, true, KIND_SUMMARY> : eda_bf16_state<C, D, BV, false, KIND_SUMMARY>;
-        hipLaunchKernelGGL(ks, dim3((unsigned)gridS), dim3(G2::NT), G2::LDS, stream, (const bf16 *)v, S0,
-                           S_final, (bf16 *)o, (const char *)ws, maps, Tlen, H, BH, dk, dv, NC, RX + R, RX,
+        const int RX = (dk + D - 1) / D, RS = (dv + D - 1) / D;
+        const bool vvs = (dv % D == 0) && ((uintptr_t)v % 16 == 0);
+        const int gridS = 8 * ((BH * (sp.P - 1) + 7) / 8) * (RX + RS);
+        auto ks = vvs ? eda_bf16_state<C, D, D, true, KIND_SUMMARY> : eda_bf16_state<C, D, D, false, KIND_SUMMARY>;
+        if ((err = hipFuncSetAttribute((const void *)ks, hipFuncAttributeMaxDynamicSharedMemorySize, G2S::LDS)) !=
+            hipSuccess)
+            return err;
+        hipLaunchKernelGGL(ks, dim3((unsigned)gridS), dim3(G2S::NT), G2S::LDS, stream, (const bf16 *)v, S0,
+                           S_final, (bf16 *)o, (const char *)ws, maps, Tlen, H, BH, dk, dv, NC, RX + RS, RX,
                            sp.P - 1, sp.NCS, 0);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL(eda_bf16_combine, dim3((unsigned)(BH * ((dv + 15) / 16))), dim3(COMB_T), 0, stream,

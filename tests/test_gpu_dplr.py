@@ -54,7 +54,7 @@ def ref_dplr(y):
     ("bf16", 2, 200, 2, 128, 128, 64, True),
     ("bf16", 1, 190, 3, 64, 64, 64, False),
     ("bf16", 1, 140, 2, 100, 80, 64, True),
-    ("bf16", 1, 32 * 520 + 9, 2, 128, 128, 32, True),  # the state pass in 4 segments
+    ("bf16", 1, 32 * 520 + 9, 2, 128, 128, 32, True),  # the state pass in 8 segments
 ])
 def test_dplr_chunked(dtype, B, T, H, dk, dv, chunk, qed):
     say(f"dplr chunked {dtype} B={B} T={T} H={H} dk={dk} dv={dv} chunk={chunk} qed={qed}")

@@ -48,7 +48,7 @@ CASES = [
     ("bf16", 2, 200, 2, 4, 128, 128, 64),
     ("bf16", 1, 129, 1, 2, 64, 64, 64),
     ("bf16", 1, 140, 1, 3, 100, 80, 64),
-    ("bf16", 1, 64 * 260 + 3, 1, 2, 128, 128, 64),  # the state pass in 2 segments
+    ("bf16", 1, 64 * 260 + 3, 1, 2, 128, 128, 64),  # the state pass in 4 segments
 ]
 
 

@@ -124,10 +124,11 @@ def segment_count(B, T, H, dk, dv, chunk):
 
 # Few heads and long sequences: the state pass cuts each head's chunks into
 # segments walked at the same time (B, T, H, d_k, d_v, chunk, segments)
-SEGMENTED = [(1, 64 * 260 + 17, 2, 128, 128, 64, 2),     # ragged last chunk and segment
-             (1, 16 * 520, 2, 128, 128, 16, 4),
-             (2, 32 * 300 + 5, 1, 64, 40, 32, 2),        # d_k != d_v, partial value slice
-             (1, 16 * 1100, 1, 128, 100, 16, 8)]
+SEGMENTED = [(1, 64 * 260 + 17, 2, 128, 128, 64, 4),     # ragged last chunk and segment
+             (1, 16 * 520, 2, 128, 128, 16, 8),
+             (2, 32 * 300 + 5, 1, 64, 40, 32, 4),        # d_k != d_v, partial value slice
+             (1, 16 * 1100, 1, 128, 100, 16, 16),
+             (1, 64 * 512, 1, 128, 128, 64, 8)]          # 64-chunk segments, as at 16 heads and T = 32768
 
 
 @pytest.mark.parametrize("B,T,H,dk,dv,chunk,P", SEGMENTED)
@@ -146,7 +147,7 @@ def test_segmented_strong_decay_and_no_decay():
     """Segments where the chunk maps contract to nearly zero (alpha ~ e^-5 per
     token) and where they do not contract at all (alpha = 1), with S0."""
     B, T, H, d, chunk = 1, 64 * 300, 1, 128, 64
-    assert segment_count(B, T, H, d, d, chunk) == 2
+    assert segment_count(B, T, H, d, d, chunk) == 4
     for kind in ("floor", "one"):
         say(f"segmented decay {kind}")
         x = make_inputs(B, T, H, d, d, "bf16", seed=41, s0_std=0.05)
