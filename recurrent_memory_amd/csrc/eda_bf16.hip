@@ -1545,81 +1545,73 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
 }
 
 // Prefix over segments, fp32: S_in(s + 1) = M_s S_in(s) + N_s for s = 0 .. P-2,
-// with S_in(0) = S0 (zero when S0 is NULL).  One workgroup per (head, 16-column
-// slice of the value dimension); thread (row, half) holds 8 columns of one
-// state row.  Per step, the whole of M_s and the thread's N_s entries are
-// fetched at once (one memory latency per step, the next step's fetch issued
-// before this step's products), then M_s passes through LDS in two halves of
-// its columns.  maps: [BH][P-1][d_k][d_k + d_v]; starts (written):
-// [BH][P-1][d_k][d_v] for segments 1 .. P-1.
-constexpr int COMB_T = 256, COMB_KH = 64, COMB_NM = 128 * 128 / COMB_T;
+// with S_in(0) = S0 (zero when S0 is NULL), on the fp32 matrix cores (16x16x4:
+// products exact in fp32, fp32 sums).  One workgroup per (head, 16-column slice
+// of the value dimension); wave w owns rows 16 w .. 16 w + 15 of the slice.
+// The A operands (rows of M_s) come straight from memory into registers, one
+// step ahead; S_in(s) sits transposed in LDS as the B operand.  K-step (j, i)
+// takes k = 16 j + 4 g + i in lane group g, so a lane's four consecutive k of a
+// row of M_s arrive as one 16-byte piece (V4: d_k and d_k + d_v multiples of
+// 4).  The slices of a head get workgroup ids congruent mod 8 (one XCD, one L2
+// for the maps they all read).  maps: [BH][P-1][d_k][d_k + d_v]; starts
+// (written): [BH][P-1][d_k][d_v] for segments 1 .. P-1.
+constexpr int COMB_W = 8, COMB_T = 64 * COMB_W, COMB_LD = 128 + 4;
+template <bool V4>
 __global__ void __launch_bounds__(COMB_T)
 eda_bf16_combine(const float *S0, const float *__restrict__ maps, float *__restrict__ starts, int BH, int dk,
                  int dv, int P) {
-    __shared__ __attribute__((aligned(16))) float Xs[128][16];
-    __shared__ float Ms[128][COMB_KH + 1];   // (+1: rows of one wave fall in distinct banks)
-    const int nsl = (dv + 15) / 16;
-    const int bh = blockIdx.x / nsl, c0 = 16 * (blockIdx.x % nsl);
-    const int tid = threadIdx.x, row = tid >> 1, cq = 8 * (tid & 1);
-    const bool live = row < dk;
-    float x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int col = c0 + cq + j;
-        x[j] = (live && col < dv && S0) ? S0[((long)bh * dk + row) * dv + col] : 0.f;
+    __shared__ __attribute__((aligned(16))) float XT[16][COMB_LD];   // S_in^T: column, row (zero beyond d_k)
+    const int nsl = (dv + 15) / 16, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int bh = (slot / nsl) * 8 + xcd, c0 = 16 * (slot % nsl);
+    if (bh >= BH) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, gq = lane >> 4;
+    const int col = c0 + l16;                 // the lane's column (B operand, output)
+    const int arow = 16 * wave + l16;         // the lane's row of M_s (A operand)
+    const int orow = 16 * wave + 4 * gq;      // the lane's first output row
+    const long ld = (long)dk + dv;
+    for (int idx = tid; idx < 16 * 128; idx += COMB_T) {
+        const int c = idx >> 7, k = idx & 127;
+        XT[c][k] = (S0 && k < dk && c0 + c < dv) ? S0[((long)bh * dk + k) * dv + c0 + c] : 0.f;
     }
-    // element idx = tid + COMB_T i of M_s: row idx / 128, column idx % 128
-    float mr[COMB_NM], nr[8];
-    auto fetch = [&](int s) __attribute__((always_inline)) {
-        const float *m = maps + ((long)bh * (P - 1) + s) * dk * (dk + dv);
-#pragma unroll
-        for (int i = 0; i < COMB_NM; ++i) {
-            const int idx = tid + COMB_T * i, r = idx >> 7, k = idx & 127;
-            mr[i] = (r < dk && k < dk) ? m[(long)r * (dk + dv) + k] : 0.f;
-        }
+    auto mbase = [&](int s) __attribute__((always_inline)) { return maps + ((long)bh * (P - 1) + s) * dk * ld; };
+    auto fetch = [&](f32x4 (&a)[8], int s) __attribute__((always_inline)) {
+        const float *m = mbase(s) + (arow < dk ? arow : 0) * ld;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int col = c0 + cq + j;
-            nr[j] = (live && col < dv) ? m[(long)row * (dk + dv) + dk + col] : 0.f;   // N_s
+            const int k = 16 * j + 4 * gq;
+            if constexpr (V4) {
+                a[j] = (arow < dk && k < dk) ? *(const f32x4 *)(m + k) : zero4();
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[j][i] = (arow < dk && k + i < dk) ? m[k + i] : 0.f;
+            }
         }
     };
-    if (P > 1) fetch(0);
-    for (int s = 0; s + 1 < P; ++s) {
-        float y[8];
+    auto step = [&](const f32x4 (&a)[8], f32x4 (&an)[8], int s) __attribute__((always_inline)) {
+        if (s + 2 < P) fetch(an, s + 1);   // the next map, in flight during this step
+        f32x4 y;                           // N_s: rows orow + i, column col
+        const float *nb = mbase(s) + dk + (col < dv ? col : 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = (orow + i < dk && col < dv) ? nb[(orow + i) * ld] : 0.f;
+        __syncthreads();   // XT holds S_in(s)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            Xs[row][cq + j] = x[j];
-            y[j] = nr[j];
+            const f32x4 b = *(const f32x4 *)&XT[l16][16 * j + 4 * gq];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j][i], b[i], y, 0, 0, 0);
         }
+        __syncthreads();   // every wave has read S_in(s)
+        *(f32x4 *)&XT[l16][orow] = y;
 #pragma unroll
-        for (int h = 0; h < 128 / COMB_KH; ++h) {
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < COMB_NM; ++i) {
-                const int idx = tid + COMB_T * i, r = idx >> 7, k = idx & 127;
-                if (k / COMB_KH == h) Ms[r][k % COMB_KH] = mr[i];
-            }
-            if (h == 128 / COMB_KH - 1 && s + 2 < P) fetch(s + 1);   // the next map, in flight
-            __syncthreads();
-            // (rows of Xs and columns of M_s beyond d_k hold zeros)
-#pragma unroll 16
-            for (int k = 0; k < COMB_KH; ++k) {
-                const float mk = Ms[row][k];
-                const f32x4 xa = *(const f32x4 *)&Xs[COMB_KH * h + k][cq], xb = *(const f32x4 *)&Xs[COMB_KH * h + k][cq + 4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    y[j] = fmaf(mk, xa[j], y[j]);
-                    y[4 + j] = fmaf(mk, xb[j], y[4 + j]);
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            x[j] = y[j];
-            const int col = c0 + cq + j;
-            if (live && col < dv) starts[(((long)bh * (P - 1) + s) * dk + row) * dv + col] = y[j];
-        }
+        for (int i = 0; i < 4; ++i)
+            if (orow + i < dk && col < dv) starts[(((long)bh * (P - 1) + s) * dk + orow + i) * dv + col] = y[i];
+    };
+    f32x4 a0[8], a1[8];
+    if (P > 1) fetch(a0, 0);
+    for (int s = 0; s + 1 < P; s += 2) {
+        step(a0, a1, s);
+        if (s + 2 < P) step(a1, a0, s + 1);
     }
 }
 
@@ -1736,7 +1728,8 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
                            S_final, (bf16 *)o, (const char *)ws, maps, Tlen, H, BH, dk, dv, NC, RX + RS, RX,
                            sp.P - 1, sp.NCS, 0);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(eda_bf16_combine, dim3((unsigned)(BH * ((dv + 15) / 16))), dim3(COMB_T), 0, stream,
+        auto kc = (dk % 4 == 0 && (dk + dv) % 4 == 0) ? eda_bf16_combine<true> : eda_bf16_combine<false>;
+        hipLaunchKernelGGL(kc, dim3((unsigned)(8 * ((BH + 7) / 8) * ((dv + 15) / 16))), dim3(COMB_T), 0, stream,
                            S0, (const float *)maps, starts, BH, dk, dv, sp.P);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }

@@ -128,7 +128,8 @@ SEGMENTED = [(1, 64 * 260 + 17, 2, 128, 128, 64, 4),     # ragged last chunk and
              (1, 16 * 520, 2, 128, 128, 16, 8),
              (2, 32 * 300 + 5, 1, 64, 40, 32, 4),        # d_k != d_v, partial value slice
              (1, 16 * 1100, 1, 128, 100, 16, 16),
-             (1, 64 * 512, 1, 128, 128, 64, 8)]          # 64-chunk segments, as at 16 heads and T = 32768
+             (1, 64 * 512, 1, 128, 128, 64, 8),          # 64-chunk segments, as at 16 heads and T = 32768
+             (1, 16 * 520, 1, 128, 30, 16, 8)]           # d_k + d_v not a multiple of 4: element-wise prefix reads
 
 
 @pytest.mark.parametrize("B,T,H,dk,dv,chunk,P", SEGMENTED)
