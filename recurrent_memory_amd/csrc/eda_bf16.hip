@@ -332,7 +332,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
     float *wtot = (float *)(smem + G::oMI);  // per-wave decay totals of the scan [NW][D]
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = H / Hk;                  // value heads per key head
     const float *alpha = (const float *)decay;
     const bf16 *agate = (const bf16 *)decay;
@@ -542,6 +542,10 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
         // it runs at raised issue priority there; every other phase runs level
         // (raising either half in the scan or in the substitution did not pay).
         if constexpr (NW == 8) __builtin_amdgcn_s_setprio(0);
+        // (layer form: the wave index made opaque again, so that nothing derived
+        // from it is hoisted out of the item loop into spilled scalar registers;
+        // in the other modes the hoisted values pay)
+        if constexpr (LAYER) asm volatile("" : "+s"(wave));
         const int bh = head_of(it), cidx = chunk_of(it);
         if (!is_fast(cidx)) fetch_slow(it);
         // (nothing read after this item's last barrier uses bp, sb or sg)
@@ -611,12 +615,14 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             // running sums over the waves in order: the wave's prefix is the sum
             // before its own term, and the total (the same in every wave) the last
             float pre[8], tot[8];
+            int wv = wave;   // (opaque: the eight comparisons below stay in the item)
+            asm volatile("" : "+s"(wv));
 #pragma unroll
             for (int j = 0; j < 8; ++j) pre[j] = tot[j] = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 const f32x4 a = *(const f32x4 *)(wtot + w * D + c0), b = *(const f32x4 *)(wtot + w * D + c0 + 4);
-                if (w == wave) {
+                if (w == wv) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) pre[j] = tot[j];
                 }
