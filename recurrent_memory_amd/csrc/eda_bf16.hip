@@ -572,7 +572,8 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             }
             float carry[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) carry[j] = 0.f;
+            for (int j = 0; j < 8; ++j) carry[j] = -0.f;   // (x + -0 is x exactly: the first add folds away)
+            const float rb1 = (r & 1) ? 1.f : 0.f, rb2 = (r & 2) ? 1.f : 0.f;
 #pragma unroll
             for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -586,11 +587,14 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                     }
                     if constexpr (ROWS4) {
                         // rows 2 k + 1 add row 2 k; rows 2, 3 add the pair total of rows 0, 1
+                        // (a = (row 2 k, row 2 k + 1) of the lane's pair, so a.x is x itself
+                        // in an even row; the selections are products with the lane's 0/1
+                        // row bits, exact, so no select and no copy of x is needed)
                         const float2 a = row_swap16(x);
                         const float pt = a.x + a.y;
-                        const float sx = (r & 1) ? pt : x;
+                        const float sx = __builtin_fmaf(rb1, a.y, a.x);
                         const float2 b = row_swap32(pt);
-                        g[i][j] = carry[j] + ((r & 2) ? sx + b.x : sx);
+                        g[i][j] = carry[j] + __builtin_fmaf(rb2, b.x, sx);
                         carry[j] += b.x + b.y;
                     } else {
 #pragma unroll
@@ -618,7 +622,7 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
             int wv = wave;   // (opaque: the eight comparisons below stay in the item)
             asm volatile("" : "+s"(wv));
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pre[j] = tot[j] = 0.f;
+            for (int j = 0; j < 8; ++j) pre[j] = tot[j] = -0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 const f32x4 a = *(const f32x4 *)(wtot + w * D + c0), b = *(const f32x4 *)(wtot + w * D + c0 + 4);
