@@ -1263,14 +1263,15 @@ struct FragSet {
 
 // L2 warm-up of the state pass (when the workspace exceeds the MALL): while
 // fetching chunk c's operands, output wave w of slice j also reads one word
-// of every (R NBC)-th 128-byte line of chunk c + WARM_AHEAD's block, so the R
-// slices of a head (same XCD, one L2) together bring that block into L2
-// before its fragments are fetched.  The words are consumed, unused, when the
-// chunk's set is.  Two chunks ahead: at four, the warmed lines of the XCD's
-// units (eight per XCD at 16 heads) were often evicted before their fetch,
-// and the pass read its blocks 1.7 times over.  The segment maps run without
-// it (they read Phi and Psi alone, and their blocks met in L2 anyway).
-constexpr int WARM_AHEAD = 2;
+// of every (R NBC)-th 128-byte line of chunk c + warm's block, so the R slices
+// of a head (same XCD, one L2) together bring that block into L2 before its
+// fragments are fetched.  The words are consumed, unused, when the chunk's
+// set is.  The distance `warm` (0: no warm-up) is two chunks without
+// segments and one with them (eight segments' units per XCD keep more lines
+// in flight); at four, the warmed lines were often evicted before their
+// fetch and the pass read its blocks 1.7 times over.  The segment maps run
+// without it (they read Phi and Psi alone, and their blocks met in L2 anyway).
+constexpr int WARM_PLAIN = 2, WARM_SEGMENTS = 1;
 constexpr size_t WARM_MIN_BYTES = (size_t)256 << 20;   // MI355X MALL capacity
 
 // VV: every value slice is whole (d_v a multiple of BV) and v is 16-byte
@@ -1373,7 +1374,7 @@ eda_bf16_state(const bf16 *__restrict__ v, const float *S0, float *S_final, bf16
                 }
                 s.pf[0] = s.pf[1] = 0u;
                 if (warm) {
-                    const int cw = c + WARM_AHEAD < NC ? c + WARM_AHEAD : NC - 1;
+                    const int cw = c + warm < NC ? c + warm : NC - 1;
                     const char *wb = wsh + (long)cw * F::bytes;
                     const int stride = R * G::NBC;
 #pragma unroll
@@ -1719,7 +1720,7 @@ hipError_t launch_t(const void *q, const void *k, const void *e, const void *v, 
     if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
     const SegPlan sp = seg_plan(BH, NC, D, dv);
     const int R = (dv + BV - 1) / BV;
-    const int warm = fac_bytes<C, D>(B, Tlen, H) > WARM_MIN_BYTES;
+    const int warm = fac_bytes<C, D>(B, Tlen, H) <= WARM_MIN_BYTES ? 0 : sp.P > 1 ? WARM_SEGMENTS : WARM_PLAIN;
     float *maps = nullptr, *starts = nullptr;
     if (sp.P > 1) {
         // segment maps (whole-width slices: one for M's d_k columns, one for the
