@@ -76,6 +76,38 @@ def test_workspace_size():
     assert ws(0, 2048, 16, 128, 128, 0, 32) == 0
 
 
+def _bf16_segments(B, T, H, dk, dv, chunk=64):
+    """Segments per head of the bf16 state pass, read back from the workspace
+    size (the chunk factors plus, with P > 1, B H (P - 1) d_k (d_k + 2 d_v) fp32)."""
+    ws = eda.load_library().eda_fwd_chunked_workspace_size
+    D = 32 if max(dk, dv) <= 32 else 64 if max(dk, dv) <= 64 else 128
+    frag = (D // 16) * (D // 32) + (D // 16) * -(-chunk // 32) + (chunk // 16) * (D // 32) + (chunk // 16) * -(-chunk // 32)
+    blk = -(-(frag * 1024 + 4 * D) // 256) * 256
+    extra = ws(B, T, H, dk, dv, 1, chunk) - B * H * -(-T // chunk) * blk
+    per = B * H * dk * (dk + 2 * dv) * 4
+    assert extra >= 0 and extra % per == 0
+    return 1 + extra // per
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,P", [
+    (4, 2048, 16, 128, 128, 1),       # the training shape: many heads, 32 chunks
+    (1, 32768, 32, 128, 128, 1),      # 32 heads fill the chip with 16-column slices
+    (1, 32768, 16, 128, 128, 8),      # 16 heads at T = 32768: 8 segments of 64 chunks
+    (1, 131072, 16, 128, 128, 8),     # 16 would need 512 pass workgroups
+    (1, 64 * 255, 1, 128, 128, 1),    # fewer than 256 chunks
+    (1, 64 * 256, 1, 128, 128, 4),    # at least 64 chunks per segment
+    (2, 32768, 4, 128, 128, 8),
+    (1, 65536, 8, 128, 128, 16),      # 256 pass and 240 map workgroups
+    (1, 32768, 16, 64, 64, 8),        # d = 64: whole-width slices of 64 columns
+])
+def test_segment_plan(B, T, H, dk, dv, P):
+    """The state pass's segment count at chunk 64: the largest power of two that
+    keeps at least 64 chunks per segment and at most 256 workgroups both in the
+    pass (64-column slices) and in the segment maps (two whole-width slices per
+    head and segment), for few heads (B H d / 16 < 256) and at least 256 chunks."""
+    assert _bf16_segments(B, T, H, dk, dv) == P
+
+
 # Fake device addresses: distinct, 256-byte aligned, far apart, never dereferenced.
 BASE = 1 << 40
 
