@@ -793,10 +793,11 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                 const auto [lane, g4, l16, gq] = lane_ids(tid);
                 constexpr int NKS = D / 32;
                 constexpr int PER = (NOD + NPV + NW - 1) / NW;
-                // with 8 waves, waves w and w + 4 share a SIMD and the later ones issue
-                // second (and also fetch the next item's inputs right after): the first
-                // half takes one tile more, the second half one fewer
-                constexpr int SK = (NW == 8 && PER > 1) ? 1 : 0;
+                // with 8 waves, waves w and w + 4 share a SIMD; the first half, which
+                // carries the paired substitution chains and Phi after this phase,
+                // takes two tiles fewer and the second half two more (measured: even
+                // shares, or one more tile on the first half, were 1-2 % slower)
+                constexpr int SK = (NW == 8 && PER > 2) ? -2 : 0;
                 auto count = [](int I) { return NB - 1 - I + NBC - I / 2; };
                 const int tbeg = wave < NW / 2 ? wave * (PER + SK) : (NW / 2) * (PER + SK) + (wave - NW / 2) * (PER - SK);
                 const int tend = imin(NOD + NPV, tbeg + (wave < NW / 2 ? PER + SK : PER - SK));
