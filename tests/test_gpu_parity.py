@@ -342,9 +342,10 @@ def test_timed_entry_point_matches_plain_call():
 @pytest.mark.slow
 def test_large_workspace_ragged_slices():
     """A workspace beyond 256 MB (the state pass then warms L2 ahead of its
-    factor fetches) with a ragged tail, d_v = 100 (seven 16-column slices per
-    head, the last one partial) and an initial state; sampled heads against
-    the oracle."""
+    factor fetches) with a ragged tail, d_v = 100 (at 8 heads the pass runs 8
+    segments on two 64-column slices per head, the second one partial, and
+    the segment maps on whole-width slices) and an initial state; sampled
+    heads against the oracle."""
     B, T, H, dk, dv = 1, 32768 + 17, 8, 128, 100
     need = eda.workspace_size(B, T, H, dk, dv, torch.bfloat16)
     assert need > 256 << 20
