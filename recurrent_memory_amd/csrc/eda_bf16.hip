@@ -823,11 +823,12 @@ eda_bf16_factors(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const b
                         for (int ks = 0; ks < NKS; ++ks) ot[ks] = *(const bf16x8 *)(Kl + (16 * J + l16) * LDA + 32 * ks + 8 * gq);
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks) a = mma32(ot[ks], kr[ks], a);
-                        // A[16 J + g4 + rr][16 I + l16] -> mirrored block (I, J) of M's storage
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr)
-                            MI[(16 * I + g4 + rr) * LDL + 16 * J + l16] = from_f32<T>(a[rr]);
+                        for (int ks = 0; ks < NKS; ++ks) a = mma32(kr[ks], ot[ks], a);
+                        // the tile transposed: lane holds A[16 J + l16][16 I + g4 + rr], which
+                        // block (I, J) of M's storage keeps at row l16, columns g4 + rr (one
+                        // 8-byte store)
+                        *(uint2 *)(MI + (16 * I + l16) * LDL + 16 * J + g4) =
+                            make_uint2(pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]));
                     } else {
                         // P^T tile: rows = sub-steps i, cols = tokens; kept for i <= 2 tau + 1
                         const int Tb = I / 2 + (r - na);
