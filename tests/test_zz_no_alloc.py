@@ -2,8 +2,11 @@
 array) against eda_fwd_chunked (caller workspace) on the same inputs.
 
 Both run the same kernels, so the outputs must agree to the parity bar, and
-in fact bit for bit.  Two calls in a row, the second smaller, show that the
-contents left in the shared array by one call do not leak into the next.
+in fact bit for bit.  Three calls in a row, each smaller than the one
+before, show that the contents left in the shared array by one call do not
+leak into the next.  The first has one head and 300 chunks, so the bf16
+state pass runs in segments (4 at chunk 64, 8 at chunk 32), with the segment
+maps and their prefix in the array as well.
 """
 import pytest
 import torch
@@ -32,8 +35,8 @@ def both(x, chunk):
     return o, S, o_ref, S_ref
 
 
-# (B, T, H, d_k, d_v): a larger call, then a smaller one with a ragged tail
-SHAPES = [(2, 1000, 8, 128, 128), (1, 77, 3, 64, 40)]
+# (B, T, H, d_k, d_v): a segmented call, a smaller one, then one with a ragged tail
+SHAPES = [(1, 64 * 300, 1, 128, 128), (2, 1000, 8, 128, 128), (1, 77, 3, 64, 40)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
